@@ -1,0 +1,133 @@
+/*
+ * gemmf32 -- FP32 GEMM C = A.B for AMD MI355X (gfx950), tiled over LDS with a
+ * single-buffered and a double-buffered (two-slot, one barrier per K step) K-loop.
+ *
+ * Operation (all entry points that launch):
+ *     C[i][j] = sum_{k=0}^{K-1} A[i][k] * B[k][j]      0 <= i < M, 0 <= j < N
+ * with row-major A (M x K, row stride lda), B (K x N, row stride ldb) and C (M x N, row
+ * stride ldc), all FP32, products and sums in FP32 on the matrix cores.  C is overwritten
+ * and never read (no alpha/beta); there are no transposed modes.  The K-loop walks tiles
+ * of A and B through on-chip shared memory ("Double Buffering", opening paragraph and code
+ * figure; "Case Study: The Double-Buffered GEMM", code figure).
+ *
+ * Memory and ownership: A, B and C are caller-owned DEVICE pointers (for instance the
+ * data pointers of GPU tensors).  Each must be 4-byte aligned; any leading dimension is
+ * accepted (misaligned rows take a scalar-load path).  The library allocates nothing,
+ * keeps no per-call state and only borrows `stream` (a hipStream_t; NULL = the legacy
+ * default stream).  C must not overlap A or B.
+ *
+ * Asynchrony: a launching call only enqueues one kernel on `stream` and returns; the
+ * caller synchronizes.  Calls are re-entrant: the only shared state is a constant table.
+ *
+ * Errors: every entry point returns GEMMF32_OK (0) or a negative GEMMF32_ERR_* code.
+ * Arguments are validated before any HIP call, so a rejected call launches nothing and
+ * touches no memory.  GEMMF32_ERR_HIP means the launch itself failed; the HIP error code
+ * is then available from gemm_f32_last_hip_error() (per thread).
+ *
+ * Degenerate shapes: M == 0 or N == 0 is a no-op that returns 0 (pointers may be NULL);
+ * K == 0 writes zeros to the M x N block of C (A and B may be NULL).
+ */
+#ifndef GEMMF32_H
+#define GEMMF32_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    GEMMF32_OK = 0,
+    GEMMF32_ERR_NEGATIVE_DIM = -1,  /* M, N or K < 0                                    */
+    GEMMF32_ERR_BAD_LD = -2,        /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
+    GEMMF32_ERR_NULL_PTR = -3,      /* NULL pointer for a non-empty operand              */
+    GEMMF32_ERR_MISALIGNED = -4,    /* A, B or C not 4-byte aligned                      */
+    GEMMF32_ERR_ALIAS = -5,         /* the byte range of C overlaps that of A or B       */
+    GEMMF32_ERR_TOO_LARGE = -6,     /* M, N, K or a leading dimension beyond 2^31 - 1,
+                                       or the grid does not fit one launch              */
+    GEMMF32_ERR_BAD_CONFIG = -7,    /* unknown variant or tile configuration id          */
+    GEMMF32_ERR_HIP = -8            /* the HIP launch failed                             */
+};
+
+/* Variants of the K-loop. */
+enum {
+    GEMMF32_VARIANT_AUTO = 0,  /* per-shape choice from the measured dispatch table      */
+    GEMMF32_VARIANT_SB = 1,    /* one LDS slot: load -> barrier -> compute -> barrier,
+                                  two barriers per K step ("Case Study: The
+                                  Double-Buffered GEMM", second paragraph: the sibling) */
+    GEMMF32_VARIANT_DB = 2     /* two LDS slots: prologue loads tile 0 into slot 0; each
+                                  K step has one barrier, prefetches tile l+1 into the
+                                  idle slot and computes on the current one ("Double
+                                  Buffering", code figure; "Case Study", code figure)   */
+};
+
+/* C = A.B with the variant and tile configuration chosen per shape by the dispatch
+ * table (GEMMF32_VARIANT environment variable "sb" or "db" forces the variant, for
+ * measurement).  The pages' lesson that the faster variant depends on the shape is the
+ * reason for the table ("Double Buffering", last two paragraphs). */
+int gemm_f32(int64_t M, int64_t N, int64_t K,
+             const float *A, int64_t lda,
+             const float *B, int64_t ldb,
+             float *C, int64_t ldc,
+             void *stream);
+
+/* C = A.B with the single-buffered K-loop (two barriers per K step); tile configuration
+ * from the dispatch table's single-buffered column for this shape. */
+int gemm_f32_sb(int64_t M, int64_t N, int64_t K,
+                const float *A, int64_t lda,
+                const float *B, int64_t ldb,
+                float *C, int64_t ldc,
+                void *stream);
+
+/* C = A.B with the double-buffered K-loop (one barrier per K step); tile configuration
+ * from the dispatch table's double-buffered column for this shape. */
+int gemm_f32_db(int64_t M, int64_t N, int64_t K,
+                const float *A, int64_t lda,
+                const float *B, int64_t ldb,
+                float *C, int64_t ldc,
+                void *stream);
+
+/* C = A.B with an explicit variant (GEMMF32_VARIANT_SB or _DB; _AUTO = dispatch table)
+ * and tile configuration id (0 .. gemm_f32_num_configs()-1; -1 = dispatch table).  For
+ * measurement and tests: every (variant, configuration) pair computes the same product. */
+int gemm_f32_ex(int64_t M, int64_t N, int64_t K,
+                const float *A, int64_t lda,
+                const float *B, int64_t ldb,
+                float *C, int64_t ldc,
+                int variant, int cfg_id,
+                void *stream);
+
+/* The dispatch decision for a shape, without launching: *variant receives
+ * GEMMF32_VARIANT_SB or _DB and *cfg_id the tile configuration id.  Either output pointer
+ * may be NULL.  Pure host code (no GPU needed).  Returns GEMMF32_ERR_NEGATIVE_DIM for
+ * negative sizes. */
+int gemm_f32_select(int64_t M, int64_t N, int64_t K, int *variant, int *cfg_id);
+
+/* Tile configuration id for an explicit variant (SB or DB) and shape, as used by
+ * gemm_f32_sb / gemm_f32_db.  Returns the id (>= 0) or a negative error code. */
+int gemm_f32_select_cfg(int64_t M, int64_t N, int64_t K, int variant);
+
+/* Number of compiled tile configurations. */
+int gemm_f32_num_configs(void);
+
+/* Describe tile configuration cfg_id: output tile BM x BN, K tile BK, threads per
+ * workgroup, and the LDS bytes one workgroup uses with one slot (single-buffered) and
+ * with two slots (double-buffered).  Output pointers may be NULL.  Returns 0 or
+ * GEMMF32_ERR_BAD_CONFIG. */
+int gemm_f32_config_info(int cfg_id, int *BM, int *BN, int *BK, int *threads,
+                         int *lds_bytes_sb, int *lds_bytes_db);
+
+/* The HIP error code of this thread's last failed launch (0 if none). */
+int gemm_f32_last_hip_error(void);
+
+/* Static description of an error code (never NULL). */
+const char *gemm_f32_strerror(int code);
+
+/* Library version string, e.g. "gemmf32 0.1.0 gfx950". */
+const char *gemm_f32_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMMF32_H */

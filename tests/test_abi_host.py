@@ -1,0 +1,162 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header declares, and
+rejects bad arguments before any HIP call (so these run without a GPU).
+
+No call here passes validation with made-up pointers: a call that passed would launch a
+kernel on them.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_double_buffered_amd as tdb
+from tiled_double_buffered_amd import build
+
+HEADER = os.path.join(build.INCLUDE, "gemmf32.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_f32\w*)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = tdb.load()
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in gemmf32.h but not exported"
+    assert set(names) == set(tdb.SIGNATURES), "binding and header disagree"
+
+
+def test_exported_symbols_are_c_linkage():
+    out = os.popen(f"nm -D --defined-only {tdb._binding.LIB_PATH}").read()
+    for n in _declared_functions():
+        assert re.search(rf"\bT {n}$", out, re.M), n
+
+
+def test_version_and_strerror():
+    assert tdb.gemm_f32_version().startswith("gemmf32")
+    assert "gfx950" in tdb.gemm_f32_version()
+    codes = [tdb.OK, tdb.ERR_NEGATIVE_DIM, tdb.ERR_BAD_LD, tdb.ERR_NULL_PTR,
+             tdb.ERR_MISALIGNED, tdb.ERR_ALIAS, tdb.ERR_TOO_LARGE, tdb.ERR_BAD_CONFIG,
+             tdb.ERR_HIP]
+    msgs = [tdb.gemm_f32_strerror(c) for c in codes]
+    assert len(set(msgs)) == len(codes)
+    assert tdb.gemm_f32_strerror(-999) == "unknown error code"
+
+
+# Fake, 256-byte aligned, far-apart addresses.  Only ever used with arguments that fail
+# validation or with M == 0 / N == 0.
+PA, PB, PC = 0x7F0000000000, 0x7F1000000000, 0x7F2000000000
+
+
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f32_sb", "gemm_f32_db"])
+def test_validation_errors(fn):
+    f = getattr(tdb, fn)
+    assert f(-1, 4, 4, PA, 4, PB, 4, PC, 4) == tdb.ERR_NEGATIVE_DIM
+    assert f(4, -1, 4, PA, 4, PB, 4, PC, 4) == tdb.ERR_NEGATIVE_DIM
+    assert f(4, 4, -1, PA, 4, PB, 4, PC, 4) == tdb.ERR_NEGATIVE_DIM
+    assert f(4, 4, 8, PA, 7, PB, 4, PC, 4) == tdb.ERR_BAD_LD      # lda < K
+    assert f(4, 8, 4, PA, 4, PB, 7, PC, 8) == tdb.ERR_BAD_LD      # ldb < N
+    assert f(4, 8, 4, PA, 4, PB, 8, PC, 7) == tdb.ERR_BAD_LD      # ldc < N
+    assert f(4, 4, 0, 0, 0, 0, 4, PC, 4) == tdb.ERR_BAD_LD        # lda < 1
+    assert f(4, 4, 4, 0, 4, PB, 4, PC, 4) == tdb.ERR_NULL_PTR
+    assert f(4, 4, 4, PA, 4, 0, 4, PC, 4) == tdb.ERR_NULL_PTR
+    assert f(4, 4, 4, PA, 4, PB, 4, 0, 4) == tdb.ERR_NULL_PTR
+    assert f(4, 4, 4, PA + 2, 4, PB, 4, PC, 4) == tdb.ERR_MISALIGNED
+    assert f(4, 4, 4, PA, 4, PB + 1, 4, PC, 4) == tdb.ERR_MISALIGNED
+    assert f(4, 4, 4, PA, 4, PB, 4, PC + 3, 4) == tdb.ERR_MISALIGNED
+    assert f(1 << 31, 4, 4, PA, 4, PB, 4, PC, 4) == tdb.ERR_TOO_LARGE
+    assert f(4, 4, 1 << 31, PA, 1 << 31, PB, 4, PC, 4) == tdb.ERR_TOO_LARGE
+
+
+def test_alias_detection():
+    f = tdb.gemm_f32
+    M, N, K = 16, 16, 16
+    # C starts inside A's extent
+    assert f(M, N, K, PA, K, PB, N, PA + 4 * (M * K - 1), N) == tdb.ERR_ALIAS
+    # C ends inside B's extent
+    assert f(M, N, K, PA, K, PB, N, PB - 4 * (M * N - 1), N) == tdb.ERR_ALIAS
+    # C identical to A
+    assert f(M, N, K, PA, K, PB, N, PA, N) == tdb.ERR_ALIAS
+    # C inside the padding of a strided A still counts: the extent spans the padding
+    assert f(2, 4, 4, PA, 1000, PB, 4, PA + 4 * 500, 4) == tdb.ERR_ALIAS
+
+
+def test_degenerate_shapes_are_noops_without_launch():
+    # M == 0 or N == 0: success, nothing launched, pointers may be NULL
+    assert tdb.gemm_f32(0, 4, 4, 0, 4, 0, 4, 0, 4) == tdb.OK
+    assert tdb.gemm_f32(4, 0, 4, 0, 4, 0, 1, 0, 1) == tdb.OK
+    assert tdb.gemm_f32_sb(0, 0, 0, 0, 1, 0, 1, 0, 1) == tdb.OK
+    assert tdb.gemm_f32_db(0, 7, 3, 0, 3, 0, 7, 0, 7) == tdb.OK
+
+
+def test_ex_rejects_bad_variant_and_config():
+    n = tdb.gemm_f32_num_configs()
+    assert tdb.gemm_f32_ex(4, 4, 4, PA, 4, PB, 4, PC, 4, 3, -1) == tdb.ERR_BAD_CONFIG
+    assert tdb.gemm_f32_ex(4, 4, 4, PA, 4, PB, 4, PC, 4, 1, n) == tdb.ERR_BAD_CONFIG
+    assert tdb.gemm_f32_ex(4, 4, 4, PA, 4, PB, 4, PC, 4, 2, -2) == tdb.ERR_BAD_CONFIG
+
+
+def test_config_table():
+    n = tdb.gemm_f32_num_configs()
+    assert n >= 4
+    for c in range(n):
+        rc, info = tdb.gemm_f32_config_info(c)
+        assert rc == tdb.OK
+        assert info["BM"] % 32 == 0 and info["BN"] % 32 == 0 and info["BK"] % 8 == 0
+        assert info["threads"] % 64 == 0
+        assert info["lds_bytes_db"] == 2 * info["lds_bytes_sb"]
+        assert info["lds_bytes_db"] <= 160 * 1024
+        # one slot holds at least the A and B tiles: 4 * BK * (BM + BN) bytes
+        assert info["lds_bytes_sb"] >= 4 * info["BK"] * (info["BM"] + info["BN"])
+    assert tdb.gemm_f32_config_info(n)[0] == tdb.ERR_BAD_CONFIG
+    assert tdb.gemm_f32_config_info(-1)[0] == tdb.ERR_BAD_CONFIG
+
+
+@pytest.mark.parametrize("shape", [(128, 128, 128), (127, 193, 61), (513, 257, 129),
+                                   (1024, 1024, 1024), (256, 1024, 128), (1024, 128, 256),
+                                   (4096, 4096, 4096), (8192, 8192, 8192), (1, 1, 1),
+                                   (3, 100000, 5), (0, 0, 0), (77, 0, 9)])
+def test_select(shape):
+    n = tdb.gemm_f32_num_configs()
+    rc, v, c = tdb.gemm_f32_select(*shape)
+    assert rc == tdb.OK
+    assert v in (tdb.VARIANT_SB, tdb.VARIANT_DB)
+    assert 0 <= c < n
+    for var in (tdb.VARIANT_SB, tdb.VARIANT_DB):
+        cid = tdb.gemm_f32_select_cfg(*shape, var)
+        assert 0 <= cid < n
+    assert tdb.gemm_f32_select_cfg(*shape, 0) == tdb.ERR_BAD_CONFIG
+    assert tdb.gemm_f32_select(-1, 2, 3)[0] == tdb.ERR_NEGATIVE_DIM
+
+
+def test_select_matches_the_table_on_its_rows():
+    rows = _dispatch_rows()
+    assert rows, "dispatch table has no rows"
+    for (m, n, k, v, c, sb, db) in rows:
+        assert tdb.gemm_f32_select(m, n, k) == (tdb.OK, v, c)
+        assert tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_SB) == sb
+        assert tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_DB) == db
+        assert (v, c) in ((tdb.VARIANT_SB, sb), (tdb.VARIANT_DB, db))
+
+
+def _dispatch_rows():
+    text = open(os.path.join(build.CSRC, "dispatch_table.h")).read()
+    body = text[text.index("kDispatch[] = {"):]
+    body = body[:body.index("};")]
+    return [tuple(int(x) for x in m.groups())
+            for m in re.finditer(r"\{\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),"
+                                 r"\s*(\d+)\s*\}", body)]
+
+
+def test_tensor_wrapper_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    a = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        tdb.matmul(a, a)
+    with pytest.raises(TypeError):
+        tdb.matmul(a.double(), a.double())

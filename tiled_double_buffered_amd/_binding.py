@@ -1,0 +1,169 @@
+"""ctypes binding of libgemmf32.so: the C-ABI entry points under the same names, plus a
+tensor-level `matmul` that only marshals arguments (device pointers, leading dimensions,
+the current stream) -- every step of the product runs in the library's HIP kernels.
+
+There is no fallback: if the library is missing or cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgemmf32.so")
+
+OK = 0
+ERR_NEGATIVE_DIM = -1
+ERR_BAD_LD = -2
+ERR_NULL_PTR = -3
+ERR_MISALIGNED = -4
+ERR_ALIAS = -5
+ERR_TOO_LARGE = -6
+ERR_BAD_CONFIG = -7
+ERR_HIP = -8
+
+VARIANT_AUTO = 0
+VARIANT_SB = 1
+VARIANT_DB = 2
+_VARIANTS = {"auto": VARIANT_AUTO, "sb": VARIANT_SB, "db": VARIANT_DB}
+
+# Every exported symbol and its C signature (kept in step with include/gemmf32.h).
+_i64, _int, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+_GEMM_ARGS = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
+SIGNATURES = {
+    "gemm_f32": (_int, _GEMM_ARGS + [_vp]),
+    "gemm_f32_sb": (_int, _GEMM_ARGS + [_vp]),
+    "gemm_f32_db": (_int, _GEMM_ARGS + [_vp]),
+    "gemm_f32_ex": (_int, _GEMM_ARGS + [_int, _int, _vp]),
+    "gemm_f32_select": (_int, [_i64, _i64, _i64, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
+    "gemm_f32_select_cfg": (_int, [_i64, _i64, _i64, _int]),
+    "gemm_f32_num_configs": (_int, []),
+    "gemm_f32_config_info": (_int, [_int] + [ctypes.POINTER(_int)] * 6),
+    "gemm_f32_last_hip_error": (_int, []),
+    "gemm_f32_strerror": (ctypes.c_char_p, [_int]),
+    "gemm_f32_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class GemmError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        msg = strerror(code)
+        if code == ERR_HIP:
+            msg += f" (HIP error {gemm_f32_last_hip_error()})"
+        super().__init__(f"{what}: {msg} [{code}]" if what else f"{msg} [{code}]")
+
+
+def load(path: str = LIB_PATH):
+    """Load the library (once).  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m tiled_double_buffered_amd.build`"
+                           " (the GEMM has no fallback path)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------------------------- raw C ABI
+def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return load().gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_sb(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return load().gemm_f32_sb(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_db(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return load().gemm_f32_db(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, variant, cfg_id, stream=None) -> int:
+    return load().gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, variant, cfg_id, stream)
+
+
+def gemm_f32_select(M, N, K):
+    """Returns (rc, variant, cfg_id)."""
+    v, c = _int(0), _int(0)
+    rc = load().gemm_f32_select(M, N, K, ctypes.byref(v), ctypes.byref(c))
+    return rc, v.value, c.value
+
+
+def gemm_f32_select_cfg(M, N, K, variant) -> int:
+    return load().gemm_f32_select_cfg(M, N, K, variant)
+
+
+def gemm_f32_num_configs() -> int:
+    return load().gemm_f32_num_configs()
+
+
+def gemm_f32_config_info(cfg_id):
+    """Returns (rc, dict) with BM, BN, BK, threads, lds_bytes_sb, lds_bytes_db."""
+    vals = [_int(0) for _ in range(6)]
+    rc = load().gemm_f32_config_info(cfg_id, *[ctypes.byref(v) for v in vals])
+    keys = ("BM", "BN", "BK", "threads", "lds_bytes_sb", "lds_bytes_db")
+    return rc, dict(zip(keys, (v.value for v in vals)))
+
+
+def gemm_f32_last_hip_error() -> int:
+    return load().gemm_f32_last_hip_error()
+
+
+def gemm_f32_strerror(code) -> str:
+    return load().gemm_f32_strerror(code).decode()
+
+
+def gemm_f32_version() -> str:
+    return load().gemm_f32_version().decode()
+
+
+strerror = gemm_f32_strerror
+
+
+# ----------------------------------------------------------------------------- tensors
+def _operand(t, name):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D float32 tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU (the library takes device pointers)")
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride (row-major)")
+    ld = t.stride(0) if rows > 1 else max(cols, 1)
+    return t.data_ptr(), max(ld, cols, 1)
+
+
+def matmul(A, B, out=None, variant: str = "auto", cfg_id: int = -1, stream=None):
+    """out = A @ B for row-major float32 GPU tensors through the C ABI.
+
+    A is M x K, B is K x N, out (allocated when None) is M x N; any row stride >= the row
+    length is passed as the leading dimension.  The launch goes on `stream` (a
+    torch.cuda.Stream; default: the current stream) and is asynchronous."""
+    import torch
+    if variant not in _VARIANTS:
+        raise ValueError(f"variant must be one of {sorted(_VARIANTS)}")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {tuple(A.shape)} @ {tuple(B.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    elif tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong shape")
+    pa, lda = _operand(A, "A")
+    pb, ldb = _operand(B, "B")
+    pc, ldc = _operand(out, "out")
+    s = (stream if stream is not None else torch.cuda.current_stream(A.device)).cuda_stream
+    rc = gemm_f32_ex(M, N, K, pa, lda, pb, ldb, pc, ldc, _VARIANTS[variant], cfg_id, s)
+    if rc != OK:
+        raise GemmError(rc, "gemm_f32")
+    return out

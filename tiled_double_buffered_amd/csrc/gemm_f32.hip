@@ -1,0 +1,525 @@
+// gemmf32: FP32 GEMM C = A.B for gfx950 (MI355X), tiled through LDS, with a
+// single-buffered and a double-buffered K-loop, an FP32 matrix-core micro-kernel,
+// a guarded path for ragged or misaligned operands, and a per-shape dispatcher.
+//
+// What the K-loop does comes from two pages on the technique:
+//   "Double Buffering" (metalworking glossary), code figure: two staging buffers per
+//     operand; each iteration opens with one barrier, loads tile l+1 into the idle
+//     buffer when there is one, computes on the current buffer and swaps.
+//   "Case Study: The Double-Buffered GEMM", code figure: a prologue loads tile 0 into
+//     buffer 0 before the loop; its second paragraph: the sibling (single-buffered)
+//     kernel has one buffer set and two barriers per iteration.
+//   Same case study, paragraph after the figure: the one barrier serves both as "the
+//     prefetch has landed" and as "every wave is done reading the buffer about to be
+//     overwritten", because the buffers alternate.
+// The pages' own kernels target Apple GPUs; everything below is written for CDNA4:
+// 64-lane waves, v_mfma_f32_32x32x2_f32 on the matrix cores, LDS with padded rows,
+// 16-byte global loads, and an XCD-aware ordering of workgroups.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "gemmf32.h"
+
+namespace gemmf32 {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------------------------------
+// Tile configuration.
+//   BM x BN : output tile of one workgroup        BK : K depth of one LDS tile
+//   WAVES_M x WAVES_N waves per workgroup; each wave owns a TM x TN sub-tile made of
+//   FM x FN blocks of 32 x 32, one 16-register accumulator per block.
+// LDS layout of one slot (FP32):
+//   As[BM][AS]  A tile with k contiguous, row stride AS = BK + 4 (the pad of 4 words
+//               makes the 16-byte reads of 8 or 16 consecutive rows hit distinct banks)
+//   Bs[BK][BS]  B tile with n contiguous, row stride BS = BN + 8 (so the two half-waves,
+//               which read rows 4 apart, land on opposite halves of the 64 banks)
+// ------------------------------------------------------------------------------------
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int NT = WAVES_M * WAVES_N * 64;
+  static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int AS = BK + 4;
+  static constexpr int BS = BN + 8;
+  static constexpr int A_SLOT = BM * AS;
+  static constexpr int B_SLOT = BK * BS;
+  static constexpr int SLOT = A_SLOT + B_SLOT;  // floats per LDS slot
+  // Global -> LDS copy: 16-byte groups of 4 consecutive floats along a row.
+  static constexpr int A_GROUPS_PER_ROW = BK / 4;
+  static constexpr int B_GROUPS_PER_ROW = BN / 4;
+  static constexpr int A_PER_T = BM * BK / 4 / NT;  // groups per thread per tile
+  static constexpr int B_PER_T = BK * BN / 4 / NT;
+  static constexpr int A_ROWS_PER_PASS = NT / A_GROUPS_PER_ROW;
+  static constexpr int B_ROWS_PER_PASS = NT / B_GROUPS_PER_ROW;
+
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+  static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+  static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "copy must divide");
+  static_assert(NT % A_GROUPS_PER_ROW == 0 && NT % B_GROUPS_PER_ROW == 0, "copy rows");
+  static_assert(A_PER_T >= 1 && B_PER_T >= 1, "copy work per thread");
+};
+
+// Flags passed to the kernel.
+enum : int {
+  kVecA = 1,  // A 16-byte aligned and lda % 4 == 0: rows can be read 16 bytes at a time
+  kVecB = 2,  // same for B
+};
+
+// ------------------------------------------------------------------------------------
+// Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin; renumber
+// them so that consecutive ids run on one XCD (which has its own L2), then walk the
+// tiles in column-major groups of GROUP_M tile rows so that workgroups close in id
+// share panels of A and B.
+// ------------------------------------------------------------------------------------
+__device__ inline void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  constexpr int kXcds = 8;
+  constexpr int kGroupM = 8;
+  const int nwg = gridDim.x;
+  int bid = blockIdx.x;
+  if (nwg % kXcds == 0) bid = (bid % kXcds) * (nwg / kXcds) + bid / kXcds;
+  const int per_group = kGroupM * tiles_n;
+  const int group = bid / per_group;
+  const int first_m = group * kGroupM;
+  const int rows = min(tiles_m - first_m, kGroupM);
+  const int in_group = bid - group * per_group;
+  tm = first_m + in_group % rows;
+  tn = in_group / rows;
+}
+
+// ------------------------------------------------------------------------------------
+// The workgroup's copy of one K tile: global memory -> registers -> LDS.
+// Thread t moves groups g = t + p * NT (p = 0 .. PER_T-1); group g of A is row
+// g / (BK/4), columns 4 * (g % (BK/4)) .. +3 of the tile; likewise for B with BN/4.
+// ------------------------------------------------------------------------------------
+template <class C>
+struct TileCopy {
+  floatx4 ra[C::A_PER_T];
+  floatx4 rb[C::B_PER_T];
+
+  // Per-thread coordinates inside the tile.
+  int a_row, a_col, b_row, b_col;
+
+  __device__ inline void init(int tid) {
+    a_row = tid / C::A_GROUPS_PER_ROW;
+    a_col = 4 * (tid % C::A_GROUPS_PER_ROW);
+    b_row = tid / C::B_GROUPS_PER_ROW;
+    b_col = 4 * (tid % C::B_GROUPS_PER_ROW);
+  }
+
+  // Fast path: the whole tile lies inside the matrices and rows are 16-byte aligned.
+  __device__ inline void load_a_fast(const float* __restrict__ A, int64_t lda, int m0,
+                                     int k0) {
+    const float* p = A + (int64_t)(m0 + a_row) * lda + (k0 + a_col);
+#pragma unroll
+    for (int i = 0; i < C::A_PER_T; ++i)
+      ra[i] = *reinterpret_cast<const floatx4*>(p + (int64_t)(i * C::A_ROWS_PER_PASS) * lda);
+  }
+  __device__ inline void load_b_fast(const float* __restrict__ B, int64_t ldb, int n0,
+                                     int k0) {
+    const float* p = B + (int64_t)(k0 + b_row) * ldb + (n0 + b_col);
+#pragma unroll
+    for (int i = 0; i < C::B_PER_T; ++i)
+      rb[i] = *reinterpret_cast<const floatx4*>(p + (int64_t)(i * C::B_ROWS_PER_PASS) * ldb);
+  }
+
+  // Guarded path: element by element; anything outside M x K (A) or K x N (B) reads as
+  // +0, so a partial K tile adds exact zeros and edge rows/columns stay finite.
+  __device__ inline void load_a_guarded(const float* __restrict__ A, int64_t lda, int M,
+                                        int K, int m0, int k0) {
+#pragma unroll
+    for (int i = 0; i < C::A_PER_T; ++i) {
+      const int r = m0 + a_row + i * C::A_ROWS_PER_PASS;
+      const int c = k0 + a_col;
+      const float* p = A + (int64_t)r * lda + c;
+      floatx4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (r < M && c + e < K) ? p[e] : 0.0f;
+      ra[i] = v;
+    }
+  }
+  __device__ inline void load_b_guarded(const float* __restrict__ B, int64_t ldb, int N,
+                                        int K, int n0, int k0) {
+#pragma unroll
+    for (int i = 0; i < C::B_PER_T; ++i) {
+      const int r = k0 + b_row + i * C::B_ROWS_PER_PASS;
+      const int c = n0 + b_col;
+      const float* p = B + (int64_t)r * ldb + c;
+      floatx4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (r < K && c + e < N) ? p[e] : 0.0f;
+      rb[i] = v;
+    }
+  }
+
+  __device__ inline void store(float* slot) {
+    float* As = slot;
+    float* Bs = slot + C::A_SLOT;
+#pragma unroll
+    for (int i = 0; i < C::A_PER_T; ++i)
+      *reinterpret_cast<floatx4*>(As + (a_row + i * C::A_ROWS_PER_PASS) * C::AS + a_col) = ra[i];
+#pragma unroll
+    for (int i = 0; i < C::B_PER_T; ++i)
+      *reinterpret_cast<floatx4*>(Bs + (b_row + i * C::B_ROWS_PER_PASS) * C::BS + b_col) = rb[i];
+  }
+};
+
+// ------------------------------------------------------------------------------------
+// Matrix-core micro-kernel on one LDS slot.
+// v_mfma_f32_32x32x2_f32: lane L supplies A[L%32][L/32] and B[L/32][L%32] of a
+// 32x2 by 2x32 step and accumulates a 32x32 block, of which lane L holds column L%32,
+// rows 8*(r/4) + 4*(L/32) + r%4 in accumulator register r (r = 0..15).
+// Eight k values are consumed per round: lane L reads A[row][kk+4h .. kk+4h+3]
+// (h = L/32) with one 16-byte LDS read, and B[kk+4h+t][col] for t = 0..3; the MFMA for
+// t then sums k = kk+t and kk+4+t.  The four MFMAs of a round cover kk .. kk+7 once
+// each, so the product is unchanged; only the order of the k sum differs.
+// ------------------------------------------------------------------------------------
+template <class C>
+__device__ inline void mma_slot(const float* slot, floatx16 (&acc)[C::FM][C::FN], int wm,
+                                int wn, int lane) {
+  const float* As = slot;
+  const float* Bs = slot + C::A_SLOT;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+  const float* a_ptr = As + (wm * C::TM + l32) * C::AS + 4 * h;
+  const float* b_ptr = Bs + (4 * h) * C::BS + wn * C::TN + l32;
+#pragma unroll
+  for (int kk = 0; kk < C::BK; kk += 8) {
+    floatx4 a[C::FM];
+    float b[C::FN][4];
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+      a[fm] = *reinterpret_cast<const floatx4*>(a_ptr + fm * 32 * C::AS + kk);
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) b[fn][t] = b_ptr[(kk + t) * C::BS + fn * 32];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+          acc[fm][fn] =
+              __builtin_amdgcn_mfma_f32_32x32x2f32(a[fm][t], b[fn][t], acc[fm][fn], 0, 0, 0);
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// The kernel.  DB = true: two LDS slots, one barrier per K step.  DB = false: one slot,
+// two barriers per K step (load; barrier; compute; barrier).
+// ------------------------------------------------------------------------------------
+template <class C, bool DB>
+__global__ void __launch_bounds__(C::NT)
+gemm_f32_tile_kernel(int M, int N, int K, const float* __restrict__ A, int64_t lda,
+                     const float* __restrict__ B, int64_t ldb, float* __restrict__ Cmat,
+                     int64_t ldc, int flags) {
+  __shared__ __attribute__((aligned(16))) float smem[(DB ? 2 : 1) * C::SLOT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WAVES_N;
+  const int wn = wave % C::WAVES_N;
+
+  const int tiles_m = (M + C::BM - 1) / C::BM;
+  const int tiles_n = (N + C::BN - 1) / C::BN;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * C::BM;
+  const int n0 = tn * C::BN;
+  const bool m_full = m0 + C::BM <= M;
+  const bool n_full = n0 + C::BN <= N;
+  const bool vec_a = (flags & kVecA) && m_full;
+  const bool vec_b = (flags & kVecB) && n_full;
+
+  floatx16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
+
+  TileCopy<C> cp;
+  cp.init(tid);
+  auto load = [&](int kt) {
+    const int k0 = kt * C::BK;
+    const bool k_full = k0 + C::BK <= K;
+    if (vec_a && k_full)
+      cp.load_a_fast(A, lda, m0, k0);
+    else
+      cp.load_a_guarded(A, lda, M, K, m0, k0);
+    if (vec_b && k_full)
+      cp.load_b_fast(B, ldb, n0, k0);
+    else
+      cp.load_b_guarded(B, ldb, N, K, n0, k0);
+  };
+
+  const int k_tiles = (K + C::BK - 1) / C::BK;
+  if constexpr (DB) {
+    if (k_tiles > 0) {
+      // Prologue: tile 0 into slot 0.
+      load(0);
+      cp.store(smem);
+      int cur = 0;
+      for (int l = 0; l < k_tiles; ++l) {
+        // One barrier: slot `cur` is complete (its writes came before this point in
+        // every wave) and slot `cur ^ 1` is no longer read (its last reads were in the
+        // previous iteration's compute, also before this point in every wave).
+        __syncthreads();
+        const bool more = l + 1 < k_tiles;
+        if (more) load(l + 1);  // global loads in flight while the MFMAs below run
+        mma_slot<C>(smem + cur * C::SLOT, acc, wm, wn, lane);
+        if (more) cp.store(smem + (cur ^ 1) * C::SLOT);
+        cur ^= 1;
+      }
+    }
+  } else {
+    for (int l = 0; l < k_tiles; ++l) {
+      load(l);
+      cp.store(smem);
+      __syncthreads();  // tile l is in LDS
+      mma_slot<C>(smem, acc, wm, wn, lane);
+      __syncthreads();  // every wave is done reading before the next tile overwrites it
+    }
+  }
+
+  // Epilogue: C is written once, never read.  Lanes 0-31 of a store cover 32 consecutive
+  // columns of one row and lanes 32-63 the same columns four rows further down.
+  const int row0 = m0 + wm * C::TM + 4 * (lane >> 5);
+  const int col0 = n0 + wn * C::TN + (lane & 31);
+  if (m_full && n_full) {
+    float* cbase = Cmat + (int64_t)row0 * ldc + col0;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          cbase[(int64_t)(fm * 32 + 8 * (r >> 2) + (r & 3)) * ldc + fn * 32] = acc[fm][fn][r];
+  } else {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + fm * 32 + 8 * (r >> 2) + (r & 3);
+          const int col = col0 + fn * 32;
+          if (row < M && col < N) Cmat[(int64_t)row * ldc + col] = acc[fm][fn][r];
+        }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Configuration table.  Ids are part of the ABI (gemm_f32_ex, gemm_f32_config_info).
+// ------------------------------------------------------------------------------------
+using Cfg0 = TileCfg<256, 256, 16, 2, 2>;  // wave 128x128 (16 blocks)
+using Cfg1 = TileCfg<256, 256, 32, 2, 2>;  // wave 128x128, deeper K tile
+using Cfg2 = TileCfg<256, 128, 16, 2, 2>;  // wave 128x64
+using Cfg3 = TileCfg<128, 128, 16, 2, 2>;  // wave 64x64
+using Cfg4 = TileCfg<128, 128, 32, 2, 2>;  // wave 64x64, deeper K tile
+using Cfg5 = TileCfg<128, 64, 32, 2, 2>;   // wave 64x32
+using Cfg6 = TileCfg<64, 64, 32, 2, 2>;    // wave 32x32
+using Cfg7 = TileCfg<64, 64, 64, 2, 2>;    // wave 32x32, deeper K tile
+
+typedef void (*KernelFn)(int, int, int, const float*, int64_t, const float*, int64_t, float*,
+                         int64_t, int);
+
+struct CfgEntry {
+  int bm, bn, bk, nt;
+  int lds_sb, lds_db;
+  KernelFn sb, db;
+};
+
+template <class C>
+constexpr CfgEntry make_entry() {
+  return CfgEntry{C::BM,
+                  C::BN,
+                  C::BK,
+                  C::NT,
+                  (int)(C::SLOT * sizeof(float)),
+                  (int)(2 * C::SLOT * sizeof(float)),
+                  &gemm_f32_tile_kernel<C, false>,
+                  &gemm_f32_tile_kernel<C, true>};
+}
+
+static const CfgEntry kConfigs[] = {
+    make_entry<Cfg0>(), make_entry<Cfg1>(), make_entry<Cfg2>(), make_entry<Cfg3>(),
+    make_entry<Cfg4>(), make_entry<Cfg5>(), make_entry<Cfg6>(), make_entry<Cfg7>(),
+};
+constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+
+}  // namespace gemmf32
+
+#include "dispatch_table.h"
+
+namespace gemmf32 {
+
+// ------------------------------------------------------------------------------------
+// Host side: validation, dispatch, launch.
+// ------------------------------------------------------------------------------------
+static thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxDim = 2147483647LL - 1024;  // keeps tile-end arithmetic in int32
+
+static int validate(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                    const float* B, int64_t ldb, const float* C, int64_t ldc) {
+  if (M < 0 || N < 0 || K < 0) return GEMMF32_ERR_NEGATIVE_DIM;
+  const int64_t min_lda = K > 1 ? K : 1;
+  const int64_t min_ldb = N > 1 ? N : 1;
+  if (lda < min_lda || ldb < min_ldb || ldc < min_ldb) return GEMMF32_ERR_BAD_LD;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMMF32_ERR_TOO_LARGE;
+  if (lda > kMaxDim * 64 || ldb > kMaxDim * 64 || ldc > kMaxDim * 64)
+    return GEMMF32_ERR_TOO_LARGE;
+  if (M == 0 || N == 0) return GEMMF32_OK;
+  if (C == nullptr) return GEMMF32_ERR_NULL_PTR;
+  if (K > 0 && (A == nullptr || B == nullptr)) return GEMMF32_ERR_NULL_PTR;
+  if (((uintptr_t)C & 3u) != 0) return GEMMF32_ERR_MISALIGNED;
+  if (K > 0 && ((((uintptr_t)A) & 3u) != 0 || (((uintptr_t)B) & 3u) != 0))
+    return GEMMF32_ERR_MISALIGNED;
+  // Byte extents [begin, end) of the three operands; C must be disjoint from A and B.
+  const uintptr_t c0 = (uintptr_t)C;
+  const uintptr_t c1 = c0 + (uintptr_t)(((M - 1) * ldc + N) * 4);
+  if (K > 0) {
+    const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)(((M - 1) * lda + K) * 4);
+    const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)(((K - 1) * ldb + N) * 4);
+    if (c0 < a1 && a0 < c1) return GEMMF32_ERR_ALIAS;
+    if (c0 < b1 && b0 < c1) return GEMMF32_ERR_ALIAS;
+  }
+  return GEMMF32_OK;
+}
+
+static int launch(int variant, int cfg_id, int64_t M, int64_t N, int64_t K, const float* A,
+                  int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
+                  void* stream) {
+  const CfgEntry& e = kConfigs[cfg_id];
+  const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
+  if (tiles * e.nt > 0xFFFFFFFFLL) return GEMMF32_ERR_TOO_LARGE;
+  int flags = 0;
+  if (K > 0 && (((uintptr_t)A) & 15u) == 0 && (lda & 3) == 0) flags |= kVecA;
+  if (K > 0 && (((uintptr_t)B) & 15u) == 0 && (ldb & 3) == 0) flags |= kVecB;
+  int m = (int)M, n = (int)N, k = (int)K;
+  void* args[] = {&m, &n, &k, (void*)&A, &lda, (void*)&B, &ldb, &C, &ldc, &flags};
+  KernelFn fn = variant == GEMMF32_VARIANT_SB ? e.sb : e.db;
+  hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)tiles), dim3(e.nt), args, 0,
+                                   (hipStream_t)stream);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return GEMMF32_ERR_HIP;
+  }
+  return GEMMF32_OK;
+}
+
+static int env_variant() {
+  const char* v = std::getenv("GEMMF32_VARIANT");
+  if (v == nullptr) return GEMMF32_VARIANT_AUTO;
+  if (std::strcmp(v, "sb") == 0) return GEMMF32_VARIANT_SB;
+  if (std::strcmp(v, "db") == 0) return GEMMF32_VARIANT_DB;
+  return GEMMF32_VARIANT_AUTO;
+}
+
+static int run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
+               int64_t ldb, float* C, int64_t ldc, int variant, int cfg_id, void* stream) {
+  if (variant != GEMMF32_VARIANT_AUTO && variant != GEMMF32_VARIANT_SB &&
+      variant != GEMMF32_VARIANT_DB)
+    return GEMMF32_ERR_BAD_CONFIG;
+  if (cfg_id < -1 || cfg_id >= kNumConfigs) return GEMMF32_ERR_BAD_CONFIG;
+  int rc = validate(M, N, K, A, lda, B, ldb, C, ldc);
+  if (rc != GEMMF32_OK) return rc;
+  if (M == 0 || N == 0) return GEMMF32_OK;
+  if (variant == GEMMF32_VARIANT_AUTO) {
+    int v = 0, c = 0;
+    select_shape(M, N, K, &v, &c);
+    variant = v;
+    if (cfg_id < 0) cfg_id = c;
+  } else if (cfg_id < 0) {
+    cfg_id = select_for_variant(M, N, K, variant);
+  }
+  return launch(variant, cfg_id, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+}  // namespace gemmf32
+
+using namespace gemmf32;
+
+extern "C" {
+
+int gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
+             int64_t ldb, float* C, int64_t ldc, void* stream) {
+  return run(M, N, K, A, lda, B, ldb, C, ldc, env_variant(), -1, stream);
+}
+
+int gemm_f32_sb(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
+                int64_t ldb, float* C, int64_t ldc, void* stream) {
+  return run(M, N, K, A, lda, B, ldb, C, ldc, GEMMF32_VARIANT_SB, -1, stream);
+}
+
+int gemm_f32_db(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
+                int64_t ldb, float* C, int64_t ldc, void* stream) {
+  return run(M, N, K, A, lda, B, ldb, C, ldc, GEMMF32_VARIANT_DB, -1, stream);
+}
+
+int gemm_f32_ex(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
+                int64_t ldb, float* C, int64_t ldc, int variant, int cfg_id, void* stream) {
+  return run(M, N, K, A, lda, B, ldb, C, ldc, variant, cfg_id, stream);
+}
+
+int gemm_f32_select(int64_t M, int64_t N, int64_t K, int* variant, int* cfg_id) {
+  if (M < 0 || N < 0 || K < 0) return GEMMF32_ERR_NEGATIVE_DIM;
+  int v = 0, c = 0;
+  select_shape(M, N, K, &v, &c);
+  if (variant) *variant = v;
+  if (cfg_id) *cfg_id = c;
+  return GEMMF32_OK;
+}
+
+int gemm_f32_select_cfg(int64_t M, int64_t N, int64_t K, int variant) {
+  if (M < 0 || N < 0 || K < 0) return GEMMF32_ERR_NEGATIVE_DIM;
+  if (variant != GEMMF32_VARIANT_SB && variant != GEMMF32_VARIANT_DB)
+    return GEMMF32_ERR_BAD_CONFIG;
+  return select_for_variant(M, N, K, variant);
+}
+
+int gemm_f32_num_configs(void) { return kNumConfigs; }
+
+int gemm_f32_config_info(int cfg_id, int* BM, int* BN, int* BK, int* threads, int* lds_sb,
+                         int* lds_db) {
+  if (cfg_id < 0 || cfg_id >= kNumConfigs) return GEMMF32_ERR_BAD_CONFIG;
+  const CfgEntry& e = kConfigs[cfg_id];
+  if (BM) *BM = e.bm;
+  if (BN) *BN = e.bn;
+  if (BK) *BK = e.bk;
+  if (threads) *threads = e.nt;
+  if (lds_sb) *lds_sb = e.lds_sb;
+  if (lds_db) *lds_db = e.lds_db;
+  return GEMMF32_OK;
+}
+
+int gemm_f32_last_hip_error(void) { return g_last_hip_error; }
+
+const char* gemm_f32_strerror(int code) {
+  switch (code) {
+    case GEMMF32_OK: return "success";
+    case GEMMF32_ERR_NEGATIVE_DIM: return "negative matrix dimension";
+    case GEMMF32_ERR_BAD_LD: return "leading dimension smaller than the row length";
+    case GEMMF32_ERR_NULL_PTR: return "null pointer for a non-empty operand";
+    case GEMMF32_ERR_MISALIGNED: return "operand pointer not 4-byte aligned";
+    case GEMMF32_ERR_ALIAS: return "C overlaps A or B";
+    case GEMMF32_ERR_TOO_LARGE: return "dimension or grid too large for one launch";
+    case GEMMF32_ERR_BAD_CONFIG: return "unknown variant or tile configuration";
+    case GEMMF32_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+const char* gemm_f32_version(void) { return "gemmf32 0.1.0 gfx950"; }
+
+}  // extern "C"
