@@ -1,0 +1,358 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP32 GEMM C = A.B on one MI355X.
+
+One step = one 8192 x 8192 x 8192 product through the dispatched C-ABI entry point
+(gemm_f32): dispatcher -> tiled kernel (global -> LDS copy, LDS ping-pong or single slot,
+FP32 MFMA micro-kernel, guarded epilogue).  Inputs are the seeded uniform grid values of
+tdb_inputs, resident in HBM before timing starts; C is preallocated.
+
+Prints ONE JSON line:
+  value         whole-job TFLOP/s = 2*M*N*K / (host-wall time per step), K timed steps
+                bracketed by torch.cuda.synchronize()
+  roofline      FP32 MFMA bound: algorithmic FLOP per launch / average launch duration
+                from HIP events on the launch stream, against the 157.3 TFLOP/s peak;
+                `traffic` = HBM bytes per launch from the committed rocprofv3 counter
+                summary (null if the kernel source changed since it was taken)
+  cpu_baseline  the CPU oracle timed on a bounded row sample of the same product
+  per_shape     single- vs double-buffered vs dispatched time for every workload shape
+  parity        the 8192^3 result checked on 4096 seeded positions against the oracle
+
+Also:
+  python bench.py --summarize-trace DIR      per-(kernel, grid) average durations from a
+                                             rocprofv3 kernel trace (kernel_trace.csv)
+  python bench.py --summarize-counters DIR   per-(kernel, grid) average counter values
+                                             from rocprofv3 --pmc runs (counter_collection.csv)
+  --copy-calibration MIB                     also run one plain device-to-device copy of
+                                             MIB MiB, whose FETCH_SIZE / WRITE_SIZE readings
+                                             calibrate the GEMM's HBM byte counts
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_MFMA_TFLOPS = 157.3          # MI355X dense FP32 matrix peak (AMD specification)
+METRIC = "FP32 GEMM TFLOP/s and % of MFMA FP32 peak at 1024³/4096³/8192³, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_8192.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "tiled_double_buffered_amd", "csrc", f)
+                  for f in ("gemm_f32.hip", "dispatch_table.h")]
+HEADLINE = "square_8192"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def summarize_trace(d: str) -> int:
+    """Average kernel duration per (kernel name, grid size) from rocprofv3's CSV trace."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        print(f"no kernel_trace.csv under {d}", file=sys.stderr)
+        return 1
+    groups = {}
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                name = row.get("Kernel_Name", "")
+                grid = row.get("Grid_Size", row.get("Grid_Size_X", ""))
+                dur = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+                groups.setdefault((name, grid), []).append(dur)
+    print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}  grid  kernel")
+    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{len(v):6d} {statistics.mean(v)/1e3:10.2f} {min(v)/1e3:10.2f} "
+              f"{max(v)/1e3:10.2f}  {grid}  {name[:150]}")
+    return 0
+
+
+def summarize_counters(d: str) -> int:
+    """Average counter value per (kernel name, grid size, counter) from rocprofv3 --pmc."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        print(f"no counter_collection.csv under {d}", file=sys.stderr)
+        return 1
+    groups = {}
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                key = (row.get("Kernel_Name", ""), row.get("Grid_Size", ""),
+                       row.get("Counter_Name", ""))
+                groups.setdefault(key, {}).setdefault(row.get("Dispatch_Id", ""), 0.0)
+                groups[key][row.get("Dispatch_Id", "")] += float(row["Counter_Value"])
+    print(f"{'dispatches':>10} {'avg_value':>16}  counter  grid  kernel")
+    for (name, grid, ctr), per in sorted(groups.items()):
+        vals = list(per.values())
+        print(f"{len(vals):10d} {statistics.mean(vals):16.4f}  {ctr}  {grid}  {name[:140]}")
+    return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--per-shape", choices=("all", "metric", "none"), default="all",
+                    help="which workload shapes get the SB/DB/dispatch comparison")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-counters", metavar="DIR")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    args = ap.parse_args()
+
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import tdb_inputs as ti
+    import tiled_double_buffered_amd as tdb
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    lib_version = tdb.gemm_f32_version()
+
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads and writes exactly MIB MiB each
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.copy_calibration} MiB done")
+        del src, dst
+
+    # ------------------------------------------------------------------ headline
+    M, N, K, seed = ti.WORKLOADS[HEADLINE]
+    log(f"[bench] generating {M}x{N}x{K} inputs (seed {seed}) ...")
+    A_h, B_h = ti.workload_inputs(M, N, K, seed)
+    A = torch.from_numpy(A_h).to(dev)
+    B = torch.from_numpy(B_h).to(dev)
+    C = torch.zeros((M, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    s_ptr = stream.cuda_stream
+    flop = 2.0 * M * N * K
+    _, variant, cfg = tdb.gemm_f32_select(M, N, K)
+
+    def step():
+        rc = tdb.gemm_f32(M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N, s_ptr)
+        if rc != tdb.OK:
+            raise tdb.GemmError(rc, "gemm_f32")
+
+    log(f"[bench] warmup {args.warmup} steps (variant {variant}, cfg {cfg}) ...")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = e0.elapsed_time(e1) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (kernel_ms * 1e-3) / 1e12
+    log(f"[bench] {HEADLINE}: {ms_per_step:.3f} ms/step wall, {kernel_ms:.3f} ms/launch "
+        f"(events) -> {value:.2f} TFLOP/s")
+
+    # parity of the timed output on the workload's seeded positions
+    parity = None
+    try:
+        import oracle
+        ri, rj = ti.sample_positions(seed, M, N, 4096)
+        c64, bnd = oracle.gemm_f64_sampled(A_h, B_h, ri, rj)
+        got = C[torch.from_numpy(ri).to(dev), torch.from_numpy(rj).to(dev)].cpu().numpy()
+        r = oracle.tolerance_ratio(got, c64, bnd)
+        parity = {"positions": 4096, "max_err_over_bound": r, "pass": bool(r <= 1.0)}
+        log(f"[bench] parity on 4096 positions: max |C-C64|/(1e-5*Bnd+1e-6) = {r:.3g}")
+    except Exception as exc:  # the oracle is test infrastructure; report, do not fail
+        parity = {"error": repr(exc)}
+
+    # traffic from the committed counter summary, if it describes this kernel source
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha256") == kernel_source_hash() and \
+                tr.get("workload") == HEADLINE:
+            traffic = tr["hbm_bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        traffic = None
+
+    roofline = {"bound": "mfma", "achieved": round(achieved, 3),
+                "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": traffic,
+                "kernel": f"{'db' if variant == tdb.VARIANT_DB else 'sb'} cfg{cfg}",
+                "launch_ms": round(kernel_ms, 4)}
+
+    # ------------------------------------------------------------------ per shape
+    def time_call(fn, target_ms=25.0, batches=5):
+        fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        one = max(time.perf_counter() - t, 1e-6)
+        reps = int(min(5000, max(3, target_ms * 1e-3 / one)))
+        for _ in range(min(reps, 10)):
+            fn()
+        res = []
+        for _ in range(batches):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            h0 = time.perf_counter()
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            h1 = time.perf_counter()
+            res.append((a.elapsed_time(b) * 1e3 / reps, (h1 - h0) * 1e6 / reps))
+        ev = statistics.median(x[0] for x in res)
+        wall_us = statistics.median(x[1] for x in res)
+        return ev, wall_us
+
+    per_shape = {}
+    names = {"all": list(ti.WORKLOADS), "none": [],
+             "metric": ["square_1024", "square_4096", "square_8192"]}[args.per_shape]
+    rounds = 2
+    for name in names:
+        m, n, k, s = ti.WORKLOADS[name]
+        if name == HEADLINE:
+            Ad, Bd, Cd = A, B, C
+        else:
+            a_h, b_h = ti.workload_inputs(m, n, k, s)
+            Ad, Bd = torch.from_numpy(a_h).to(dev), torch.from_numpy(b_h).to(dev)
+            Cd = torch.zeros((m, n), dtype=torch.float32, device=dev)
+        pa, pb, pc = Ad.data_ptr(), Bd.data_ptr(), Cd.data_ptr()
+        fns = {
+            "sb": lambda: tdb.gemm_f32_sb(m, n, k, pa, k, pb, n, pc, n, s_ptr),
+            "db": lambda: tdb.gemm_f32_db(m, n, k, pa, k, pb, n, pc, n, s_ptr),
+            "dispatch": lambda: tdb.gemm_f32(m, n, k, pa, k, pb, n, pc, n, s_ptr),
+        }
+        order = list(fns)
+        samples = {v: [] for v in fns}
+        for r in range(rounds):  # rotate the variant order between rounds
+            for v in order[r % 3:] + order[:r % 3]:
+                samples[v].append(time_call(fns[v]))
+        f = 2.0 * m * n * k
+        entry = {"M": m, "N": n, "K": k}
+        for v, xs in samples.items():
+            ev = statistics.median(x[0] for x in xs)
+            wl = statistics.median(x[1] for x in xs)
+            entry[v] = {"us": round(ev, 2), "host_wall_us": round(wl, 2),
+                        "tflops": round(f / (ev * 1e-6) / 1e12, 2),
+                        "frac_peak": round(f / (ev * 1e-6) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)}
+        entry["sb_cfg"] = tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_SB)
+        entry["db_cfg"] = tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_DB)
+        _, dv, dc = tdb.gemm_f32_select(m, n, k)
+        entry["dispatch_choice"] = f"{'db' if dv == tdb.VARIANT_DB else 'sb'} cfg{dc}"
+        entry["db_over_sb_speedup"] = round(entry["sb"]["us"] / entry["db"]["us"], 3)
+        per_shape[name] = entry
+        log(f"[bench] {name}: sb {entry['sb']['us']} us, db {entry['db']['us']} us, "
+            f"dispatch {entry['dispatch']['us']} us ({entry['dispatch']['tflops']} TFLOP/s)")
+        if name != HEADLINE:
+            del Ad, Bd, Cd
+
+    # ------------------------------------------------------------------ CPU baseline
+    cpu_baseline = None
+    if args.cpu_seconds > 0:
+        try:
+            import oracle
+            threads = oracle.max_threads()
+            rows = threads
+            t = time.perf_counter()
+            oracle.gemm_f64(A_h[:rows], B_h)
+            dt = time.perf_counter() - t
+            rows = int(min(M, max(threads, threads * round(args.cpu_seconds / dt))))
+            t = time.perf_counter()
+            oracle.gemm_f64(A_h[:rows], B_h)
+            dt = time.perf_counter() - t
+            cpu_tflops = 2.0 * rows * N * K / dt / 1e12
+            cpu_baseline = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s",
+                            "cores": threads, "kind": "oracle",
+                            "sample": f"first {rows} rows of the {M}x{N}x{K} product "
+                                      f"(C64 and Bnd in FP64, {dt:.1f} s); full product "
+                                      f"extrapolates to {flop / (cpu_tflops * 1e12):.0f} s",
+                            "cpu": _cpu_model()}
+            log(f"[bench] CPU oracle: {rows} rows in {dt:.1f} s on {threads} threads")
+        except Exception as exc:
+            cpu_baseline = {"error": repr(exc)}
+
+    metric_shapes = {}
+    for name in ("square_1024", "square_4096", "square_8192"):
+        if name in per_shape:
+            d = per_shape[name]["dispatch"]
+            metric_shapes[name] = {"tflops": d["tflops"], "frac_peak": d["frac_peak"]}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": HEADLINE, "M": M, "N": N, "K": K, "seed": seed,
+                   "inputs": "uniform grid values in [-1, 1) (SplitMix64)",
+                   "dispatch": roofline["kernel"], "library": lib_version},
+        "frac_peak": round(value / PEAK_FP32_MFMA_TFLOPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu_baseline,
+        "metric_shapes": metric_shapes,
+        "per_shape": per_shape,
+        "parity": parity,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    sys.exit(main())

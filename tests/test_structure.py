@@ -34,30 +34,50 @@ def kernels():
     return out
 
 
-def _loops(body: str):
-    """(start, end) character spans of the loops: a label followed later by a branch back
-    to it."""
-    labels = {m.group(1): m.start() for m in re.finditer(r"^(\.LBB\w+):", body, re.M)}
-    spans = []
-    for m in re.finditer(r"^\s*s_(?:cbranch_\w+|branch)\s+(\.LBB\w+)", body, re.M):
-        tgt = m.group(1)
-        if tgt in labels and labels[tgt] < m.start():
-            spans.append((labels[tgt], m.end()))
-    return spans
+def _loop_blocks(body: str):
+    """Loops of a kernel, from the compiler's own block annotations: header id -> list of
+    the instruction lines of every basic block in that loop (nested loops included)."""
+    loops, cur = {}, None
+    for line in body.split("\n"):
+        m = re.match(r"^\.LBB(\w+):(.*)", line)
+        if m:
+            hdr = None
+            if "Loop Header" in m.group(2):
+                hdr = m.group(1)
+            mm = re.search(r"Header=BB(\w+)", m.group(2))
+            if mm:
+                hdr = mm.group(1)
+            cur = loops.setdefault(hdr, []) if hdr else None
+            continue
+        t = line.strip()
+        if cur is not None and t and not t.startswith((";", ".")):
+            cur.append(t)
+    return loops
+
+
+def _count_barriers(lines):
+    return sum(1 for t in lines if re.match(r"s_barrier\b", t.strip()))
 
 
 def test_barriers_per_k_step(kernels):
+    """Per K-loop iteration: 1 barrier (double-buffered) or 2 (single-buffered).  The
+    double-buffered kernel adds one prologue barrier per loop (tile 0 -> slot 0), so a
+    product issues k_tiles barriers in total, against 2 * k_tiles single-buffered."""
     facts = json.load(open(GOLDEN))["barriers_per_k_step"]
     for name, k in kernels.items():
-        body = k["body"]
-        barriers = [m.start() for m in re.finditer(r"\bs_barrier\b", body)]
+        total = _count_barriers(k["body"].split("\n"))
+        loops = {h: ls for h, ls in _loop_blocks(k["body"]).items() if _count_barriers(ls)}
+        assert loops, f"no K-loop with a barrier in {k['cfg']}"
         expected = facts["double_buffered"] if k["db"] else facts["single_buffered"]
-        assert len(barriers) == expected, (k["cfg"], k["db"], len(barriers))
-        loops = _loops(body)
-        assert loops, f"no K-loop found in {k['cfg']}"
-        # every barrier sits inside one loop, and that loop holds all of them
-        inside = [lp for lp in loops if all(lp[0] <= b <= lp[1] for b in barriers)]
-        assert inside, (k["cfg"], k["db"], "barrier outside the K-loop")
+        inside = 0
+        for h, ls in loops.items():
+            assert _count_barriers(ls) == expected, (k["cfg"], k["db"], h)
+            inside += expected
+        outside = total - inside
+        if k["db"]:
+            assert outside == len(loops), (k["cfg"], "one prologue barrier per loop")
+        else:
+            assert outside == 0, (k["cfg"], "single-buffered barriers all in the loop")
 
 
 def test_no_scratch_and_lds_fits(kernels):
@@ -77,10 +97,12 @@ def test_fp32_matrix_instruction_only(kernels):
 
 
 def test_mfma_count_matches_tile(kernels):
-    """Unrolled K tile: (BM/32) * (BN/32) * BK/2 MFMAs per workgroup = per wave
-    FM * FN * BK / 2 (each MFMA consumes a k pair)."""
+    """One K tile is FM * FN * BK / 2 MFMAs per wave (each MFMA consumes a k pair).  The
+    kernel holds whole copies of that tile body: single-buffered one per loop (unguarded
+    and guarded), double-buffered two per loop (steady state and the peeled last tile)."""
     for name, k in kernels.items():
         bm, bn, bk, wm, wn = k["cfg"]
         fm, fn = bm // wm // 32, bn // wn // 32
+        per_tile = fm * fn * bk // 2
         n = len(re.findall(r"\bv_mfma_f32_32x32x2_f32\b", k["body"]))
-        assert n == fm * fn * bk // 2, (k["cfg"], n)
+        assert n == per_tile * (4 if k["db"] else 2), (k["cfg"], k["db"], n, per_tile)

@@ -21,17 +21,16 @@ struct DispatchRow {
   int variant, cfg, sb_cfg, db_cfg;
 };
 
-// Initial rows (heuristic, before measurement): big tiles where they fill the 256 CUs,
-// small tiles otherwise; double buffering everywhere.
+// Interim rows from a first sweep (one run per configuration, not yet counterbalanced).
 static const DispatchRow kDispatch[] = {
-    {128, 128, 128, 2, 6, 6, 6},
-    {127, 193, 61, 2, 6, 6, 6},
-    {513, 257, 129, 2, 6, 6, 6},
-    {1024, 1024, 1024, 2, 6, 6, 6},
-    {256, 1024, 128, 2, 6, 6, 6},
-    {1024, 128, 256, 2, 6, 6, 6},
-    {4096, 4096, 4096, 2, 0, 0, 0},
-    {8192, 8192, 8192, 2, 0, 0, 0},
+    {128, 128, 128, 2, 7, 7, 7},
+    {127, 193, 61, 2, 7, 7, 7},
+    {513, 257, 129, 2, 7, 7, 7},
+    {1024, 1024, 1024, 2, 7, 7, 7},
+    {256, 1024, 128, 2, 7, 7, 7},
+    {1024, 128, 256, 2, 7, 7, 7},
+    {4096, 4096, 4096, 1, 3, 3, 1},
+    {8192, 8192, 8192, 2, 2, 3, 2},
 };
 
 static inline double dispatch_log2(int64_t x) { return x > 0 ? std::log2((double)x) : -1.0; }

@@ -171,55 +171,247 @@ struct TileCopy {
 };
 
 // ------------------------------------------------------------------------------------
-// Matrix-core micro-kernel on one LDS slot.
+// Matrix-core micro-kernel.
 // v_mfma_f32_32x32x2_f32: lane L supplies A[L%32][L/32] and B[L/32][L%32] of a
 // 32x2 by 2x32 step and accumulates a 32x32 block, of which lane L holds column L%32,
 // rows 8*(r/4) + 4*(L/32) + r%4 in accumulator register r (r = 0..15).
-// Eight k values are consumed per round: lane L reads A[row][kk+4h .. kk+4h+3]
-// (h = L/32) with one 16-byte LDS read, and B[kk+4h+t][col] for t = 0..3; the MFMA for
-// t then sums k = kk+t and kk+4+t.  The four MFMAs of a round cover kk .. kk+7 once
-// each, so the product is unchanged; only the order of the k sum differs.
+// A K tile is consumed in BK/8 rounds of eight k values.  In round q lane L reads
+// A[row][8q+4h .. 8q+4h+3] (h = L/32) with one 16-byte LDS read and B[8q+4h+t][col] for
+// t = 0..3; the MFMA for t then sums k = 8q+t and 8q+4+t.  The four MFMAs of a round
+// cover its eight k values once each, so the product is unchanged; only the order of the
+// k sum differs from the textbook loop.
 // ------------------------------------------------------------------------------------
 template <class C>
-__device__ inline void mma_slot(const float* slot, floatx16 (&acc)[C::FM][C::FN], int wm,
-                                int wn, int lane) {
-  const float* As = slot;
-  const float* Bs = slot + C::A_SLOT;
-  const int h = lane >> 5;
-  const int l32 = lane & 31;
-  const float* a_ptr = As + (wm * C::TM + l32) * C::AS + 4 * h;
-  const float* b_ptr = Bs + (4 * h) * C::BS + wn * C::TN + l32;
+struct Frag {
+  floatx4 a[C::FM];
+  float b[C::FN][4];
+};
+
+// This lane's fragment offsets (in floats) inside an LDS slot.
+template <class C>
+struct LaneView {
+  int a_off, b_off;
+  __device__ inline void init(int wm, int wn, int lane) {
+    const int h = lane >> 5, l32 = lane & 31;
+    a_off = (wm * C::TM + l32) * C::AS + 4 * h;
+    b_off = C::A_SLOT + (4 * h) * C::BS + wn * C::TN + l32;
+  }
+};
+
+template <class C>
+__device__ inline void read_frag(const float* slot, const LaneView<C>& lv, int q, Frag<C>& f) {
+  const float* a_ptr = slot + lv.a_off + 8 * q;
+  const float* b_ptr = slot + lv.b_off + 8 * q * C::BS;
 #pragma unroll
-  for (int kk = 0; kk < C::BK; kk += 8) {
-    floatx4 a[C::FM];
-    float b[C::FN][4];
+  for (int fm = 0; fm < C::FM; ++fm)
+    f.a[fm] = *reinterpret_cast<const floatx4*>(a_ptr + fm * 32 * C::AS);
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) f.b[fn][t] = b_ptr[t * C::BS + fn * 32];
+}
+
+// The MFMAs of one round; PART 0 = all four k pairs, 1 = the first two, 2 = the last two.
+template <class C, int PART>
+__device__ inline void mfma_round(const Frag<C>& f, floatx16 (&acc)[C::FM][C::FN]) {
+  constexpr int t0 = PART == 2 ? 2 : 0;
+  constexpr int t1 = PART == 1 ? 2 : 4;
+#pragma unroll
+  for (int t = t0; t < t1; ++t)
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
-      a[fm] = *reinterpret_cast<const floatx4*>(a_ptr + fm * 32 * C::AS + kk);
 #pragma unroll
-    for (int fn = 0; fn < C::FN; ++fn)
+      for (int fn = 0; fn < C::FN; ++fn)
+        acc[fm][fn] =
+            __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[fm][t], f.b[fn][t], acc[fm][fn], 0, 0, 0);
+}
+
+// ------------------------------------------------------------------------------------
+// Instruction interleaving for the unguarded loops.  The compiler's scheduler, left
+// alone, sinks the global prefetch loads to just before their LDS stores, which exposes
+// their whole latency.  These hints (sched_group_barrier, applied to the scheduling
+// region they close) ask for each other memory instruction to be followed by a share of
+// the MFMAs, so that the matrix pipe keeps issuing while loads and stores are in flight.
+// ------------------------------------------------------------------------------------
+enum : int { kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100,
+             kSchedDsWrite = 0x200 };
+
+template <int MASK, int SIZE>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (SIZE > 0) __builtin_amdgcn_sched_group_barrier(MASK, SIZE, 0);
+}
+
+// NOTHER instructions of class OMASK spread evenly over NMFMA MFMAs.
+template <int OMASK, int NOTHER, int NMFMA, int I = 0>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (NOTHER == 0) {
+    sched_group<kSchedMfma, NMFMA>();
+  } else if constexpr (I < NOTHER) {
+    constexpr int lo = I * NMFMA / NOTHER, hi = (I + 1) * NMFMA / NOTHER;
+    sched_group<OMASK, 1>();
+    sched_group<kSchedMfma, hi - lo>();
+    sched_interleave<OMASK, NOTHER, NMFMA, I + 1>();
+  }
+}
+
+template <class C>
+struct Sched {
+  static constexpr int R = C::BK / 8;                  // rounds per K tile
+  static constexpr int MQ = 4 * C::FM * C::FN;         // MFMAs per round
+  static constexpr int G = C::A_PER_T + C::B_PER_T;    // 16-byte global loads per tile
+  static constexpr int W = C::A_PER_T + C::B_PER_T;    // 16-byte LDS stores per tile
+  static constexpr int D = C::FM + 2 * C::FN;          // LDS read instructions per round
+
+  // Double-buffered, from the top of an iteration up to the barrier: round 0 carries the
+  // global loads of tile l+1 and the LDS reads of round 1; middle rounds carry the reads
+  // of the next round; the first half of the last round carries the LDS stores of tile
+  // l+1 into the idle slot.
+  template <int Q = 0>
+  static __device__ __forceinline__ void db_before_barrier() {
+    if constexpr (Q == 0) {
+      sched_interleave<kSchedVmemRead, G, MQ / 2>();
+      if constexpr (R > 1) sched_interleave<kSchedDsRead, D, MQ - MQ / 2>();
+      else sched_group<kSchedMfma, MQ - MQ / 2>();
+      db_before_barrier<1>();
+    } else if constexpr (Q < R - 1) {
+      sched_interleave<kSchedDsRead, D, MQ>();
+      db_before_barrier<Q + 1>();
+    } else {
+      sched_interleave<kSchedDsWrite, W, MQ / 2>();
+    }
+  }
+  // After the barrier: the first reads of tile l+1, then the rest of tile l's last round.
+  static __device__ __forceinline__ void db_after_barrier() {
+    sched_group<kSchedDsRead, D>();
+    sched_group<kSchedMfma, MQ - MQ / 2>();
+  }
+  // Rounds whose MFMAs each carry the LDS reads of the following round.
+  template <int Q = 0>
+  static __device__ __forceinline__ void rounds_with_reads() {
+    if constexpr (Q < R - 1) {
+      sched_interleave<kSchedDsRead, D, MQ>();
+      rounds_with_reads<Q + 1>();
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------
+// The K-loop.  GUARD = false is taken by workgroups whose whole tile lies inside the
+// matrices, with 16-byte-aligned rows and K a multiple of BK: every copy is unguarded.
+// GUARD = true picks per K tile between the unguarded and the element-guarded copy.
+// ------------------------------------------------------------------------------------
+template <class C>
+struct LoopArgs {
+  const float* A;
+  const float* B;
+  int64_t lda, ldb;
+  int M, N, K, m0, n0;
+  bool vec_a, vec_b;
+};
+
+template <class C, bool GUARD>
+__device__ inline void load_tile(TileCopy<C>& cp, const LoopArgs<C>& g, int kt) {
+  const int k0 = kt * C::BK;
+  if constexpr (!GUARD) {
+    cp.load_a_fast(g.A, g.lda, g.m0, k0);
+    cp.load_b_fast(g.B, g.ldb, g.n0, k0);
+  } else {
+    const bool k_full = k0 + C::BK <= g.K;
+    if (g.vec_a && k_full)
+      cp.load_a_fast(g.A, g.lda, g.m0, k0);
+    else
+      cp.load_a_guarded(g.A, g.lda, g.M, g.K, g.m0, k0);
+    if (g.vec_b && k_full)
+      cp.load_b_fast(g.B, g.ldb, g.n0, k0);
+    else
+      cp.load_b_guarded(g.B, g.ldb, g.N, g.K, g.n0, k0);
+  }
+}
+
+// Double-buffered: two LDS slots, tile l+1 copied into the idle slot while tile l is
+// multiplied, ONE barrier per K tile.  The loop is rotated so that the barrier sits at
+// the hand-off between slots: after this wave has written tile l+1 into the idle slot and
+// before anybody reads it.  That single barrier is at once "tile l+1 has landed" and
+// "nobody still reads the slot that tile l+2 will overwrite" (all reads of tile l are
+// already in registers by then).  LDS fragments are read one round ahead of the MFMAs,
+// and the second half of tile l's last round runs after the barrier, covering the
+// latency of the first reads of tile l+1.  Barriers per product: 1 (prologue) +
+// (k_tiles - 1) = k_tiles, the same count as a barrier at the top of every iteration.
+template <class C, bool GUARD>
+__device__ inline void k_loop_db(float* smem, TileCopy<C>& cp, const LaneView<C>& lv,
+                                 const LoopArgs<C>& g, int k_tiles,
+                                 floatx16 (&acc)[C::FM][C::FN]) {
+  constexpr int R = C::BK / 8;
+  Frag<C> f[2];
+  load_tile<C, GUARD>(cp, g, 0);  // prologue: tile 0 into slot 0
+  cp.store(smem);
+  __syncthreads();
+  read_frag(smem, lv, 0, f[0]);
+  for (int l = 0; l + 1 < k_tiles; ++l) {
+    const float* cur = smem + (l & 1) * C::SLOT;
+    float* nxt = smem + ((l + 1) & 1) * C::SLOT;
+    load_tile<C, GUARD>(cp, g, l + 1);  // in flight during the MFMAs below
 #pragma unroll
-      for (int t = 0; t < 4; ++t) b[fn][t] = b_ptr[(kk + t) * C::BS + fn * 32];
+    for (int q = 0; q + 1 < R; ++q) {
+      read_frag(cur, lv, q + 1, f[(q + 1) & 1]);
+      mfma_round<C, 0>(f[q & 1], acc);
+    }
+    mfma_round<C, 1>(f[1], acc);
+    cp.store(nxt);
+    if constexpr (!GUARD) Sched<C>::template db_before_barrier<0>();
+    __syncthreads();
+    read_frag(nxt, lv, 0, f[0]);
+    mfma_round<C, 2>(f[1], acc);
+    if constexpr (!GUARD) Sched<C>::db_after_barrier();
+  }
+  // Last tile: nothing left to prefetch.
+  const float* cur = smem + ((k_tiles - 1) & 1) * C::SLOT;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+  for (int q = 0; q + 1 < R; ++q) {
+    read_frag(cur, lv, q + 1, f[(q + 1) & 1]);
+    mfma_round<C, 0>(f[q & 1], acc);
+  }
+  mfma_round<C, 0>(f[1], acc);
+}
+
+// Single-buffered: one LDS slot; per K tile: copy -> barrier -> multiply -> barrier.
+// The second barrier comes as soon as this wave's last LDS read of the tile has returned
+// (the last round's MFMAs run after it on registers).
+template <class C, bool GUARD>
+__device__ inline void k_loop_sb(float* smem, TileCopy<C>& cp, const LaneView<C>& lv,
+                                 const LoopArgs<C>& g, int k_tiles,
+                                 floatx16 (&acc)[C::FM][C::FN]) {
+  constexpr int R = C::BK / 8;
+  Frag<C> f[2];
+  for (int l = 0; l < k_tiles; ++l) {
+    load_tile<C, GUARD>(cp, g, l);
+    cp.store(smem);
+    __syncthreads();  // tile l is in LDS
+    read_frag(smem, lv, 0, f[0]);
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-          acc[fm][fn] =
-              __builtin_amdgcn_mfma_f32_32x32x2f32(a[fm][t], b[fn][t], acc[fm][fn], 0, 0, 0);
+    for (int q = 0; q + 1 < R; ++q) {
+      read_frag(smem, lv, q + 1, f[(q + 1) & 1]);
+      mfma_round<C, 0>(f[q & 1], acc);
+    }
+    if constexpr (!GUARD) {
+      sched_group<kSchedDsRead, Sched<C>::D>();
+      Sched<C>::template rounds_with_reads<0>();
+    }
+    __syncthreads();  // every wave has read tile l: the slot may be overwritten
+    mfma_round<C, 0>(f[1], acc);
   }
 }
 
 // ------------------------------------------------------------------------------------
-// The kernel.  DB = true: two LDS slots, one barrier per K step.  DB = false: one slot,
-// two barriers per K step (load; barrier; compute; barrier).
+// The kernel.  DB = true: two LDS slots, one barrier per K tile.  DB = false: one slot,
+// two barriers per K tile.
 // ------------------------------------------------------------------------------------
 template <class C, bool DB>
 __global__ void __launch_bounds__(C::NT)
 gemm_f32_tile_kernel(int M, int N, int K, const float* __restrict__ A, int64_t lda,
                      const float* __restrict__ B, int64_t ldb, float* __restrict__ Cmat,
                      int64_t ldc, int flags) {
+  static_assert((C::BK / 8) % 2 == 0, "BK/8 rounds must be even for the fragment ping-pong");
   __shared__ __attribute__((aligned(16))) float smem[(DB ? 2 : 1) * C::SLOT];
 
   const int tid = threadIdx.x;
@@ -232,12 +424,20 @@ gemm_f32_tile_kernel(int M, int N, int K, const float* __restrict__ A, int64_t l
   const int tiles_n = (N + C::BN - 1) / C::BN;
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * C::BM;
-  const int n0 = tn * C::BN;
-  const bool m_full = m0 + C::BM <= M;
-  const bool n_full = n0 + C::BN <= N;
-  const bool vec_a = (flags & kVecA) && m_full;
-  const bool vec_b = (flags & kVecB) && n_full;
+  LoopArgs<C> g;
+  g.A = A;
+  g.B = B;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.m0 = tm * C::BM;
+  g.n0 = tn * C::BN;
+  const bool m_full = g.m0 + C::BM <= M;
+  const bool n_full = g.n0 + C::BN <= N;
+  g.vec_a = (flags & kVecA) && m_full;
+  g.vec_b = (flags & kVecB) && n_full;
 
   floatx16 acc[C::FM][C::FN];
 #pragma unroll
@@ -249,52 +449,28 @@ gemm_f32_tile_kernel(int M, int N, int K, const float* __restrict__ A, int64_t l
 
   TileCopy<C> cp;
   cp.init(tid);
-  auto load = [&](int kt) {
-    const int k0 = kt * C::BK;
-    const bool k_full = k0 + C::BK <= K;
-    if (vec_a && k_full)
-      cp.load_a_fast(A, lda, m0, k0);
-    else
-      cp.load_a_guarded(A, lda, M, K, m0, k0);
-    if (vec_b && k_full)
-      cp.load_b_fast(B, ldb, n0, k0);
-    else
-      cp.load_b_guarded(B, ldb, N, K, n0, k0);
-  };
-
+  LaneView<C> lv;
+  lv.init(wm, wn, lane);
   const int k_tiles = (K + C::BK - 1) / C::BK;
-  if constexpr (DB) {
-    if (k_tiles > 0) {
-      // Prologue: tile 0 into slot 0.
-      load(0);
-      cp.store(smem);
-      int cur = 0;
-      for (int l = 0; l < k_tiles; ++l) {
-        // One barrier: slot `cur` is complete (its writes came before this point in
-        // every wave) and slot `cur ^ 1` is no longer read (its last reads were in the
-        // previous iteration's compute, also before this point in every wave).
-        __syncthreads();
-        const bool more = l + 1 < k_tiles;
-        if (more) load(l + 1);  // global loads in flight while the MFMAs below run
-        mma_slot<C>(smem + cur * C::SLOT, acc, wm, wn, lane);
-        if (more) cp.store(smem + (cur ^ 1) * C::SLOT);
-        cur ^= 1;
-      }
-    }
-  } else {
-    for (int l = 0; l < k_tiles; ++l) {
-      load(l);
-      cp.store(smem);
-      __syncthreads();  // tile l is in LDS
-      mma_slot<C>(smem, acc, wm, wn, lane);
-      __syncthreads();  // every wave is done reading before the next tile overwrites it
+  if (k_tiles > 0) {
+    const bool unguarded = g.vec_a && g.vec_b && (K % C::BK) == 0;
+    if constexpr (DB) {
+      if (unguarded)
+        k_loop_db<C, false>(smem, cp, lv, g, k_tiles, acc);
+      else
+        k_loop_db<C, true>(smem, cp, lv, g, k_tiles, acc);
+    } else {
+      if (unguarded)
+        k_loop_sb<C, false>(smem, cp, lv, g, k_tiles, acc);
+      else
+        k_loop_sb<C, true>(smem, cp, lv, g, k_tiles, acc);
     }
   }
 
   // Epilogue: C is written once, never read.  Lanes 0-31 of a store cover 32 consecutive
   // columns of one row and lanes 32-63 the same columns four rows further down.
-  const int row0 = m0 + wm * C::TM + 4 * (lane >> 5);
-  const int col0 = n0 + wn * C::TN + (lane & 31);
+  const int row0 = g.m0 + wm * C::TM + 4 * (lane >> 5);
+  const int col0 = g.n0 + wn * C::TN + (lane & 31);
   if (m_full && n_full) {
     float* cbase = Cmat + (int64_t)row0 * ldc + col0;
 #pragma unroll
