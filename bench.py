@@ -22,9 +22,20 @@ Also:
                                              rocprofv3 kernel trace (kernel_trace.csv)
   python bench.py --summarize-counters DIR   per-(kernel, grid) average counter values
                                              from rocprofv3 --pmc runs (counter_collection.csv)
-  --copy-calibration MIB                     also run one plain device-to-device copy of
-                                             MIB MiB, whose FETCH_SIZE / WRITE_SIZE readings
-                                             calibrate the GEMM's HBM byte counts
+  --copy-calibration MIB                     first run one streaming elementwise kernel
+                                             (negate) that reads MIB MiB and writes MIB MiB;
+                                             its FETCH_SIZE / WRITE_SIZE readings calibrate
+                                             the GEMM's HBM byte counts
+  python bench.py --counter-run              a few single- and double-buffered launches per
+                                             metric shape (1024^3, 4096^3, 8192^3) plus the
+                                             calibration kernel: the program that the
+                                             rocprofv3 --pmc passes profile
+  python bench.py --write-traffic FETCH_DIR WRITE_DIR
+                                             HBM bytes per launch of the headline kernel from
+                                             a FETCH_SIZE pass and a WRITE_SIZE pass of
+                                             --counter-run, scaled by the calibration
+                                             kernel's readings; writes
+                                             profiles/traffic_square_8192.json
 """
 from __future__ import annotations
 
@@ -99,6 +110,122 @@ def summarize_counters(d: str) -> int:
     return 0
 
 
+def _counter_rows(d: str):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _per_dispatch(rows, counter, match):
+    """Average over dispatches of one counter (summed over its instances) for the
+    dispatches whose (kernel name, grid size) satisfy `match`."""
+    per = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter or not match(r.get("Kernel_Name", ""),
+                                                         r.get("Grid_Size", "")):
+            continue
+        per[r.get("Dispatch_Id")] = per.get(r.get("Dispatch_Id"), 0.0) + float(r["Counter_Value"])
+    return (statistics.mean(per.values()), len(per)) if per else (None, 0)
+
+
+def write_traffic(fetch_dir: str, write_dir: str, calib_mib: int = 512) -> int:
+    import tdb_inputs as ti
+    import tiled_double_buffered_amd as tdb
+
+    M, N, K, _ = ti.WORKLOADS[HEADLINE]
+    _, variant, cfg = tdb.gemm_f32_select(M, N, K)
+    _, info = tdb.gemm_f32_config_info(cfg)
+    grid = str(((M + info["BM"] - 1) // info["BM"]) * ((N + info["BN"] - 1) // info["BN"])
+               * info["threads"])
+    flag = "true" if variant == tdb.VARIANT_DB else "false"
+    tag = f"TileCfg<{info['BM']}, {info['BN']}, {info['BK']},"
+
+    def is_gemm(name, g):
+        return "gemm_f32_tile_kernel" in name and tag in name and f", {flag}>" in name \
+            and g == grid
+
+    def is_calib(name, g):
+        return "neg" in name.lower() and "gemm" not in name
+
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    g_fetch, nf = _per_dispatch(fr, "FETCH_SIZE", is_gemm)
+    g_write, nw = _per_dispatch(wr, "WRITE_SIZE", is_gemm)
+    c_fetch, _ = _per_dispatch(fr, "FETCH_SIZE", is_calib)
+    c_write, _ = _per_dispatch(wr, "WRITE_SIZE", is_calib)
+    if None in (g_fetch, g_write, c_fetch, c_write):
+        print("missing counter rows (gemm fetch/write, calibration fetch/write): "
+              f"{g_fetch} {g_write} {c_fetch} {c_write}", file=sys.stderr)
+        return 1
+    kib = calib_mib * 1024.0
+    sf, sw = kib / c_fetch, kib / c_write
+    fetch_b = g_fetch * sf * 1024.0
+    write_b = g_write * sw * 1024.0
+    algo = 4.0 * (M * K + K * N + M * N)
+    out = {
+        "workload": HEADLINE,
+        "kernel": f"{'db' if variant == tdb.VARIANT_DB else 'sb'} cfg{cfg} "
+                  f"{info['BM']}x{info['BN']}x{info['BK']}",
+        "kernel_source_sha256": kernel_source_hash(),
+        "fetch_kib_per_launch_raw": g_fetch, "write_kib_per_launch_raw": g_write,
+        "dispatches": [nf, nw],
+        "calibration": {"kernel": "torch negate, reads and writes %d MiB" % calib_mib,
+                        "fetch_kib_raw": c_fetch, "write_kib_raw": c_write,
+                        "fetch_scale": sf, "write_scale": sw},
+        "hbm_fetch_bytes_per_launch": fetch_b,
+        "hbm_write_bytes_per_launch": write_b,
+        "hbm_bytes_per_launch": fetch_b + write_b,
+        "algorithmic_bytes_per_launch": algo,
+        "traffic_over_algorithmic": (fetch_b + write_b) / algo,
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE -f csv -d <FETCH_DIR> -o run -- "
+            "python3 bench.py --counter-run --copy-calibration %d" % calib_mib,
+            "rocprofv3 --pmc WRITE_SIZE -f csv -d <WRITE_DIR> -o run -- "
+            "python3 bench.py --counter-run --copy-calibration %d" % calib_mib,
+            "python3 bench.py --write-traffic <FETCH_DIR> <WRITE_DIR>"],
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
+
+
+def counter_run(calib_mib: int) -> int:
+    """A short program for counter passes: a few launches of both variants (dispatch-table
+    configurations) at the three metric shapes."""
+    import torch
+
+    import tdb_inputs as ti
+    import tiled_double_buffered_amd as tdb
+
+    dev = torch.device("cuda:0")
+    if calib_mib > 0:
+        n = calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    s_ptr = torch.cuda.current_stream(dev).cuda_stream
+    for name in ("square_1024", "square_4096", "square_8192"):
+        M, N, K, seed = ti.WORKLOADS[name]
+        a, b = ti.workload_inputs(M, N, K, seed)
+        A, B = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+        C = torch.empty((M, N), device=dev)
+        for fn in (tdb.gemm_f32_sb, tdb.gemm_f32_db):
+            for _ in range(3):
+                rc = fn(M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N, s_ptr)
+                if rc != tdb.OK:
+                    raise tdb.GemmError(rc, fn.__name__)
+        torch.cuda.synchronize()
+        print(f"[counter-run] {name} done", file=sys.stderr, flush=True)
+        del A, B, C
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,7 +238,14 @@ def main() -> int:
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", metavar="DIR")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
+    ap.add_argument("--counter-run", action="store_true")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+
+    if args.write_traffic:
+        return write_traffic(*args.write_traffic)
+    if args.counter_run:
+        return counter_run(args.copy_calibration)
 
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace)
@@ -142,7 +276,7 @@ def main() -> int:
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)  # reads and writes exactly MIB MiB each
+        torch.neg(src, out=dst)  # reads and writes exactly MIB MiB each
         torch.cuda.synchronize()
         log(f"[bench] calibration copy of {args.copy_calibration} MiB done")
         del src, dst

@@ -1,0 +1,226 @@
+"""Measure every (variant, tile configuration) per shape on the GPU and regenerate the
+dispatch table csrc/dispatch_table.h from the measurements.
+
+    python -m tiled_double_buffered_amd.tune [--out results.json] [--write-header]
+
+Protocol (after the repeated, counterbalanced timing of the LuisaCompute note "Dependence-
+aware group synchronization on M1 Max", section "Controlled implementation comparison"):
+for each shape, `rounds` rounds visit every (variant, configuration) pair in an order that
+rotates from round to round; each visit times `batches` batches of back-to-back launches
+(each batch at least `batch_ms` of GPU time) with HIP events on the launch stream; a pair's
+time is the median over rounds of the per-round median batch.  The fastest single-buffered
+and double-buffered configurations and the overall winner go into the table.
+
+Timing does not depend on the values multiplied, so inputs are seeded uniform values.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+from . import _binding as tdb
+from .build import CSRC
+
+SHAPES = [
+    # the workloads
+    (128, 128, 128), (127, 193, 61), (513, 257, 129), (1024, 1024, 1024),
+    (256, 1024, 128), (1024, 128, 256), (4096, 4096, 4096), (8192, 8192, 8192),
+    # more points for the nearest-shape rule
+    (256, 256, 256), (512, 512, 512), (2048, 2048, 2048), (6144, 6144, 6144),
+    (64, 4096, 4096), (4096, 4096, 512), (2048, 8192, 2048),
+]
+
+HEADER_TEMPLATE = """// Per-shape dispatch table: (M, N, K) -> variant and tile configuration.
+//
+// The pages' central measured lesson is that double buffering wins at some sizes and
+// loses or ties at others, so a library has to pick a variant per shape ("Double
+// Buffering", last two paragraphs; "Case Study: The Double-Buffered GEMM", paragraph on
+// the three regimes).  The rows below were measured on {device} by
+// tiled_double_buffered_amd/tune.py ({rounds} rotated rounds x {batches} batches of >= {batch_ms} ms
+// per pair), which rewrites this file; a shape that is not in the table takes the row
+// nearest to it in (log2 M, log2 N, log2 K).
+//
+// Columns: M, N, K, best variant (1 = single-buffered, 2 = double-buffered), its tile
+// configuration, best single-buffered configuration, best double-buffered configuration.
+// Trailing comments: measured microseconds of the best single- and double-buffered runs.
+#pragma once
+
+#include <cmath>
+#include <cstdint>
+
+namespace gemmf32 {{
+
+struct DispatchRow {{
+  int64_t m, n, k;
+  int variant, cfg, sb_cfg, db_cfg;
+}};
+
+static const DispatchRow kDispatch[] = {{
+{rows}
+}};
+
+static inline double dispatch_log2(int64_t x) {{ return x > 0 ? std::log2((double)x) : -1.0; }}
+
+static inline const DispatchRow& dispatch_nearest(int64_t M, int64_t N, int64_t K) {{
+  const double lm = dispatch_log2(M), ln = dispatch_log2(N), lk = dispatch_log2(K);
+  int best = 0;
+  double best_d = 1e300;
+  for (int i = 0; i < (int)(sizeof(kDispatch) / sizeof(kDispatch[0])); ++i) {{
+    const DispatchRow& r = kDispatch[i];
+    const double dm = lm - dispatch_log2(r.m), dn = ln - dispatch_log2(r.n),
+                 dk = lk - dispatch_log2(r.k);
+    const double d = dm * dm + dn * dn + dk * dk;
+    if (d < best_d) {{
+      best_d = d;
+      best = i;
+    }}
+  }}
+  return kDispatch[best];
+}}
+
+static inline void select_shape(int64_t M, int64_t N, int64_t K, int* variant, int* cfg) {{
+  const DispatchRow& r = dispatch_nearest(M, N, K);
+  *variant = r.variant;
+  *cfg = r.cfg;
+}}
+
+static inline int select_for_variant(int64_t M, int64_t N, int64_t K, int variant) {{
+  const DispatchRow& r = dispatch_nearest(M, N, K);
+  return variant == 1 ? r.sb_cfg : r.db_cfg;
+}}
+
+}}  // namespace gemmf32
+"""
+
+
+def measure(shapes, rounds=2, batches=5, batch_ms=20.0, log=print):
+    import torch
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    s_ptr = stream.cuda_stream
+    ncfg = tdb.gemm_f32_num_configs()
+    pairs = [(v, c) for c in range(ncfg) for v in (tdb.VARIANT_SB, tdb.VARIANT_DB)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    results = []
+    for (M, N, K) in shapes:
+        A = torch.rand((M, K), device=dev, generator=gen) * 2 - 1
+        B = torch.rand((K, N), device=dev, generator=gen) * 2 - 1
+        C = torch.empty((M, N), device=dev)
+        pa, pb, pc = A.data_ptr(), B.data_ptr(), C.data_ptr()
+
+        def call(v, c):
+            rc = tdb.gemm_f32_ex(M, N, K, pa, K, pb, N, pc, N, v, c, s_ptr)
+            if rc != tdb.OK:
+                raise tdb.GemmError(rc, "gemm_f32_ex")
+
+        reps = {}
+        for (v, c) in pairs:  # calibrate launches per batch
+            call(v, c)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(3):
+                call(v, c)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            one = e0.elapsed_time(e1) / 3
+            reps[(v, c)] = int(min(20000, max(2, batch_ms / max(one, 1e-4))))
+        per_round = {p: [] for p in pairs}
+        for r in range(rounds):
+            shift = (r * len(pairs)) // max(rounds, 1)
+            order = pairs[shift:] + pairs[:shift]
+            if r % 2:
+                order = order[::-1]
+            for p in order:
+                n = reps[p]
+                for _ in range(2):
+                    call(*p)
+                ts = []
+                for _ in range(batches):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for _ in range(n):
+                        call(*p)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1) * 1e3 / n)
+                per_round[p].append(statistics.median(ts))
+        row = {"M": M, "N": N, "K": K, "us": {}}
+        for (v, c), xs in per_round.items():
+            row["us"][f"{'sb' if v == tdb.VARIANT_SB else 'db'}{c}"] = statistics.median(xs)
+        results.append(row)
+        best = min(row["us"].items(), key=lambda kv: kv[1])
+        log(f"{M}x{N}x{K}: best {best[0]} {best[1]:.2f} us "
+            f"({2.0 * M * N * K / best[1] / 1e6:.2f} TFLOP/s)")
+        del A, B, C
+    return results
+
+
+def table_rows(results):
+    rows = []
+    for r in results:
+        sb = min(((k, v) for k, v in r["us"].items() if k.startswith("sb")), key=lambda kv: kv[1])
+        db = min(((k, v) for k, v in r["us"].items() if k.startswith("db")), key=lambda kv: kv[1])
+        sb_cfg, db_cfg = int(sb[0][2:]), int(db[0][2:])
+        variant, cfg = (1, sb_cfg) if sb[1] < db[1] else (2, db_cfg)
+        rows.append((r["M"], r["N"], r["K"], variant, cfg, sb_cfg, db_cfg, sb[1], db[1]))
+    return rows
+
+
+def write_header(results, device, rounds, batches, batch_ms, path=None):
+    path = path or os.path.join(CSRC, "dispatch_table.h")
+    lines = []
+    for (m, n, k, v, c, s, d, sb_us, db_us) in table_rows(results):
+        lines.append(f"    {{{m}, {n}, {k}, {v}, {c}, {s}, {d}}},  // sb {sb_us:.2f} us, "
+                     f"db {db_us:.2f} us")
+    text = HEADER_TEMPLATE.format(device=device, rounds=rounds, batches=batches,
+                                  batch_ms=int(batch_ms), rows="\n".join(lines))
+    with open(path, "w") as f:
+        f.write(text)
+    return path
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--out", default=None, help="write the raw measurements (JSON)")
+    ap.add_argument("--write-header", action="store_true",
+                    help="regenerate csrc/dispatch_table.h from the measurements")
+    ap.add_argument("--from-json", default=None,
+                    help="regenerate the header from an earlier --out file, no GPU")
+    ap.add_argument("--rounds", type=int, default=2)
+    ap.add_argument("--batches", type=int, default=5)
+    ap.add_argument("--batch-ms", type=float, default=20.0)
+    args = ap.parse_args(argv)
+    if args.from_json:
+        with open(args.from_json) as f:
+            data = json.load(f)
+        print(write_header(data["results"], data["device"], data["rounds"], data["batches"],
+                           data["batch_ms"]))
+        return 0
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    device = f"{props.name} ({getattr(props, 'gcnArchName', '?')})"
+    t0 = time.time()
+    results = measure(SHAPES, args.rounds, args.batches, args.batch_ms,
+                      log=lambda *a: print(*a, flush=True))
+    data = {"device": device, "rounds": args.rounds, "batches": args.batches,
+            "batch_ms": args.batch_ms, "library": tdb.gemm_f32_version(),
+            "seconds": time.time() - t0, "results": results}
+    if args.out:
+        with open(args.out, "w") as f:
+            json.dump(data, f, indent=1)
+    if args.write_header:
+        print(write_header(results, device, args.rounds, args.batches, args.batch_ms))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
