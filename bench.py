@@ -14,7 +14,8 @@ Prints ONE JSON line:
                 `traffic` = HBM bytes per launch from the committed rocprofv3 counter
                 summary (null if the kernel source changed since it was taken)
   cpu_baseline  the CPU oracle timed on a bounded row sample of the same product
-  per_shape     single- vs double-buffered vs dispatched time for every workload shape
+  per_shape     single-buffered, double-buffered, multi-stage and dispatched time for
+                every workload shape
   parity        the 8192^3 result checked on 4096 seeded positions against the oracle
 
 Also:
@@ -26,7 +27,7 @@ Also:
                                              (negate) that reads MIB MiB and writes MIB MiB;
                                              its FETCH_SIZE / WRITE_SIZE readings calibrate
                                              the GEMM's HBM byte counts
-  python bench.py --counter-run              a few single- and double-buffered launches per
+  python bench.py --counter-run              a few SB, DB and MS launches per
                                              metric shape (1024^3, 4096^3, 8192^3) plus the
                                              calibration kernel: the program that the
                                              rocprofv3 --pmc passes profile
@@ -58,6 +59,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_8192.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_double_buffered_amd", "csrc", f)
                   for f in ("gemm_f32.hip", "dispatch_table.h")]
 HEADLINE = "square_8192"
+VARIANT_NAMES = {1: "sb", 2: "db", 3: "ms"}
 
 
 def kernel_source_hash() -> str:
@@ -140,12 +142,14 @@ def write_traffic(fetch_dir: str, write_dir: str, calib_mib: int = 512) -> int:
     _, info = tdb.gemm_f32_config_info(cfg)
     grid = str(((M + info["BM"] - 1) // info["BM"]) * ((N + info["BN"] - 1) // info["BN"])
                * info["threads"])
-    flag = "true" if variant == tdb.VARIANT_DB else "false"
     tag = f"TileCfg<{info['BM']}, {info['BN']}, {info['BK']},"
+    if variant == tdb.VARIANT_MS:
+        kname, flag = "gemm_f32_ms_kernel", ">, %d>" % tdb.gemm_f32_config_ms(cfg)[1]["stages"]
+    else:
+        kname, flag = "gemm_f32_tile_kernel", ", true>" if variant == tdb.VARIANT_DB else ", false>"
 
     def is_gemm(name, g):
-        return "gemm_f32_tile_kernel" in name and tag in name and f", {flag}>" in name \
-            and g == grid
+        return kname in name and tag in name and flag in name and g == grid
 
     def is_calib(name, g):
         return "neg" in name.lower() and "gemm" not in name
@@ -166,7 +170,7 @@ def write_traffic(fetch_dir: str, write_dir: str, calib_mib: int = 512) -> int:
     algo = 4.0 * (M * K + K * N + M * N)
     out = {
         "workload": HEADLINE,
-        "kernel": f"{'db' if variant == tdb.VARIANT_DB else 'sb'} cfg{cfg} "
+        "kernel": f"{VARIANT_NAMES[variant]} cfg{cfg} "
                   f"{info['BM']}x{info['BN']}x{info['BK']}",
         "kernel_source_sha256": kernel_source_hash(),
         "fetch_kib_per_launch_raw": g_fetch, "write_kib_per_launch_raw": g_write,
@@ -194,7 +198,7 @@ def write_traffic(fetch_dir: str, write_dir: str, calib_mib: int = 512) -> int:
 
 
 def counter_run(calib_mib: int) -> int:
-    """A short program for counter passes: a few launches of both variants (dispatch-table
+    """A short program for counter passes: a few launches of each variant (dispatch-table
     configurations) at the three metric shapes."""
     import torch
 
@@ -215,7 +219,7 @@ def counter_run(calib_mib: int) -> int:
         a, b = ti.workload_inputs(M, N, K, seed)
         A, B = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
         C = torch.empty((M, N), device=dev)
-        for fn in (tdb.gemm_f32_sb, tdb.gemm_f32_db):
+        for fn in (tdb.gemm_f32_sb, tdb.gemm_f32_db, tdb.gemm_f32_ms):
             for _ in range(3):
                 rc = fn(M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N, s_ptr)
                 if rc != tdb.OK:
@@ -346,7 +350,7 @@ def main() -> int:
     roofline = {"bound": "mfma", "achieved": round(achieved, 3),
                 "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": traffic,
-                "kernel": f"{'db' if variant == tdb.VARIANT_DB else 'sb'} cfg{cfg}",
+                "kernel": f"{VARIANT_NAMES[variant]} cfg{cfg}",
                 "launch_ms": round(kernel_ms, 4)}
 
     # ------------------------------------------------------------------ per shape
@@ -393,12 +397,14 @@ def main() -> int:
         fns = {
             "sb": lambda: tdb.gemm_f32_sb(m, n, k, pa, k, pb, n, pc, n, s_ptr),
             "db": lambda: tdb.gemm_f32_db(m, n, k, pa, k, pb, n, pc, n, s_ptr),
+            "ms": lambda: tdb.gemm_f32_ms(m, n, k, pa, k, pb, n, pc, n, s_ptr),
             "dispatch": lambda: tdb.gemm_f32(m, n, k, pa, k, pb, n, pc, n, s_ptr),
         }
         order = list(fns)
         samples = {v: [] for v in fns}
         for r in range(rounds):  # rotate the variant order between rounds
-            for v in order[r % 3:] + order[:r % 3]:
+            rot = r % len(order)
+            for v in order[rot:] + order[:rot]:
                 samples[v].append(time_call(fns[v]))
         f = 2.0 * m * n * k
         entry = {"M": m, "N": n, "K": k}
@@ -410,12 +416,15 @@ def main() -> int:
                         "frac_peak": round(f / (ev * 1e-6) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)}
         entry["sb_cfg"] = tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_SB)
         entry["db_cfg"] = tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_DB)
+        entry["ms_cfg"] = tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_MS)
         _, dv, dc = tdb.gemm_f32_select(m, n, k)
-        entry["dispatch_choice"] = f"{'db' if dv == tdb.VARIANT_DB else 'sb'} cfg{dc}"
+        entry["dispatch_choice"] = f"{VARIANT_NAMES[dv]} cfg{dc}"
         entry["db_over_sb_speedup"] = round(entry["sb"]["us"] / entry["db"]["us"], 3)
+        entry["ms_over_db_speedup"] = round(entry["db"]["us"] / entry["ms"]["us"], 3)
         per_shape[name] = entry
         log(f"[bench] {name}: sb {entry['sb']['us']} us, db {entry['db']['us']} us, "
-            f"dispatch {entry['dispatch']['us']} us ({entry['dispatch']['tflops']} TFLOP/s)")
+            f"ms {entry['ms']['us']} us, dispatch {entry['dispatch']['us']} us "
+            f"({entry['dispatch']['tflops']} TFLOP/s)")
         if name != HEADLINE:
             del Ad, Bd, Cd
 

@@ -55,14 +55,19 @@ enum {
     GEMMF32_VARIANT_SB = 1,    /* one LDS slot: load -> barrier -> compute -> barrier,
                                   two barriers per K step ("Case Study: The
                                   Double-Buffered GEMM", second paragraph: the sibling) */
-    GEMMF32_VARIANT_DB = 2     /* two LDS slots: prologue loads tile 0 into slot 0; each
+    GEMMF32_VARIANT_DB = 2,    /* two LDS slots: prologue loads tile 0 into slot 0; each
                                   K step has one barrier, prefetches tile l+1 into the
                                   idle slot and computes on the current one ("Double
                                   Buffering", code figure; "Case Study", code figure)   */
+    GEMMF32_VARIANT_MS = 3     /* S >= 2 LDS stages filled by asynchronous direct-to-LDS
+                                  copies, tiles l+1 .. l+S-1 in flight, one barrier per
+                                  K step: the multi-stage asynchronous-copy pipeline the
+                                  glossary page names as the CUDA analogue ("Double
+                                  Buffering", second paragraph)                         */
 };
 
 /* C = A.B with the variant and tile configuration chosen per shape by the dispatch
- * table (GEMMF32_VARIANT environment variable "sb" or "db" forces the variant, for
+ * table (GEMMF32_VARIANT environment variable "sb", "db" or "ms" forces the variant, for
  * measurement).  The pages' lesson that the faster variant depends on the shape is the
  * reason for the table ("Double Buffering", last two paragraphs). */
 int gemm_f32(int64_t M, int64_t N, int64_t K,
@@ -87,7 +92,16 @@ int gemm_f32_db(int64_t M, int64_t N, int64_t K,
                 float *C, int64_t ldc,
                 void *stream);
 
-/* C = A.B with an explicit variant (GEMMF32_VARIANT_SB or _DB; _AUTO = dispatch table)
+/* C = A.B with the multi-stage direct-to-LDS K-loop; tile configuration from the
+ * dispatch table's multi-stage column for this shape.  Edge, misaligned and K-ragged
+ * tiles of the launch run the guarded double-buffered loop instead. */
+int gemm_f32_ms(int64_t M, int64_t N, int64_t K,
+                const float *A, int64_t lda,
+                const float *B, int64_t ldb,
+                float *C, int64_t ldc,
+                void *stream);
+
+/* C = A.B with an explicit variant (GEMMF32_VARIANT_SB, _DB or _MS; _AUTO = dispatch table)
  * and tile configuration id (0 .. gemm_f32_num_configs()-1; -1 = dispatch table).  For
  * measurement and tests: every (variant, configuration) pair computes the same product. */
 int gemm_f32_ex(int64_t M, int64_t N, int64_t K,
@@ -98,13 +112,14 @@ int gemm_f32_ex(int64_t M, int64_t N, int64_t K,
                 void *stream);
 
 /* The dispatch decision for a shape, without launching: *variant receives
- * GEMMF32_VARIANT_SB or _DB and *cfg_id the tile configuration id.  Either output pointer
+ * GEMMF32_VARIANT_SB, _DB or _MS and *cfg_id the tile configuration id.  Either output pointer
  * may be NULL.  Pure host code (no GPU needed).  Returns GEMMF32_ERR_NEGATIVE_DIM for
  * negative sizes. */
 int gemm_f32_select(int64_t M, int64_t N, int64_t K, int *variant, int *cfg_id);
 
-/* Tile configuration id for an explicit variant (SB or DB) and shape, as used by
- * gemm_f32_sb / gemm_f32_db.  Returns the id (>= 0) or a negative error code. */
+/* Tile configuration id for an explicit variant (SB, DB or MS) and shape, as used by
+ * gemm_f32_sb / gemm_f32_db / gemm_f32_ms.  Returns the id (>= 0) or a negative error
+ * code. */
 int gemm_f32_select_cfg(int64_t M, int64_t N, int64_t K, int variant);
 
 /* Number of compiled tile configurations. */
@@ -116,6 +131,11 @@ int gemm_f32_num_configs(void);
  * GEMMF32_ERR_BAD_CONFIG. */
 int gemm_f32_config_info(int cfg_id, int *BM, int *BN, int *BK, int *threads,
                          int *lds_bytes_sb, int *lds_bytes_db);
+
+/* Multi-stage figures of tile configuration cfg_id: number of LDS stages and LDS bytes per
+ * workgroup of the multi-stage kernel.  Output pointers may be NULL.  Returns 0 or
+ * GEMMF32_ERR_BAD_CONFIG. */
+int gemm_f32_config_ms(int cfg_id, int *stages, int *lds_bytes);
 
 /* The HIP error code of this thread's last failed launch (0 if none). */
 int gemm_f32_last_hip_error(void);

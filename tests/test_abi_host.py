@@ -53,7 +53,7 @@ def test_version_and_strerror():
 PA, PB, PC = 0x7F0000000000, 0x7F1000000000, 0x7F2000000000
 
 
-@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f32_sb", "gemm_f32_db"])
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f32_sb", "gemm_f32_db", "gemm_f32_ms"])
 def test_validation_errors(fn):
     f = getattr(tdb, fn)
     assert f(-1, 4, 4, PA, 4, PB, 4, PC, 4) == tdb.ERR_NEGATIVE_DIM
@@ -96,7 +96,7 @@ def test_degenerate_shapes_are_noops_without_launch():
 
 def test_ex_rejects_bad_variant_and_config():
     n = tdb.gemm_f32_num_configs()
-    assert tdb.gemm_f32_ex(4, 4, 4, PA, 4, PB, 4, PC, 4, 3, -1) == tdb.ERR_BAD_CONFIG
+    assert tdb.gemm_f32_ex(4, 4, 4, PA, 4, PB, 4, PC, 4, 4, -1) == tdb.ERR_BAD_CONFIG
     assert tdb.gemm_f32_ex(4, 4, 4, PA, 4, PB, 4, PC, 4, 1, n) == tdb.ERR_BAD_CONFIG
     assert tdb.gemm_f32_ex(4, 4, 4, PA, 4, PB, 4, PC, 4, 2, -2) == tdb.ERR_BAD_CONFIG
 
@@ -115,6 +115,14 @@ def test_config_table():
         assert info["lds_bytes_sb"] >= 4 * info["BK"] * (info["BM"] + info["BN"])
     assert tdb.gemm_f32_config_info(n)[0] == tdb.ERR_BAD_CONFIG
     assert tdb.gemm_f32_config_info(-1)[0] == tdb.ERR_BAD_CONFIG
+    for c in range(n):
+        rc, ms = tdb.gemm_f32_config_ms(c)
+        _, info = tdb.gemm_f32_config_info(c)
+        assert rc == tdb.OK and 2 <= ms["stages"] <= 4
+        stage = 4 * info["BK"] * (info["BM"] + info["BN"])
+        assert ms["lds_bytes"] == max(ms["stages"] * stage, info["lds_bytes_db"])
+        assert ms["lds_bytes"] <= 160 * 1024
+    assert tdb.gemm_f32_config_ms(n)[0] == tdb.ERR_BAD_CONFIG
 
 
 @pytest.mark.parametrize("shape", [(128, 128, 128), (127, 193, 61), (513, 257, 129),
@@ -125,9 +133,9 @@ def test_select(shape):
     n = tdb.gemm_f32_num_configs()
     rc, v, c = tdb.gemm_f32_select(*shape)
     assert rc == tdb.OK
-    assert v in (tdb.VARIANT_SB, tdb.VARIANT_DB)
+    assert v in (tdb.VARIANT_SB, tdb.VARIANT_DB, tdb.VARIANT_MS)
     assert 0 <= c < n
-    for var in (tdb.VARIANT_SB, tdb.VARIANT_DB):
+    for var in (tdb.VARIANT_SB, tdb.VARIANT_DB, tdb.VARIANT_MS):
         cid = tdb.gemm_f32_select_cfg(*shape, var)
         assert 0 <= cid < n
     assert tdb.gemm_f32_select_cfg(*shape, 0) == tdb.ERR_BAD_CONFIG
@@ -137,11 +145,12 @@ def test_select(shape):
 def test_select_matches_the_table_on_its_rows():
     rows = _dispatch_rows()
     assert rows, "dispatch table has no rows"
-    for (m, n, k, v, c, sb, db) in rows:
+    for (m, n, k, v, c, sb, db, ms) in rows:
         assert tdb.gemm_f32_select(m, n, k) == (tdb.OK, v, c)
         assert tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_SB) == sb
         assert tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_DB) == db
-        assert (v, c) in ((tdb.VARIANT_SB, sb), (tdb.VARIANT_DB, db))
+        assert tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_MS) == ms
+        assert (v, c) in ((tdb.VARIANT_SB, sb), (tdb.VARIANT_DB, db), (tdb.VARIANT_MS, ms))
 
 
 def _dispatch_rows():
@@ -150,7 +159,7 @@ def _dispatch_rows():
     body = body[:body.index("};")]
     return [tuple(int(x) for x in m.groups())
             for m in re.finditer(r"\{\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),\s*(\d+),"
-                                 r"\s*(\d+)\s*\}", body)]
+                                 r"\s*(\d+),\s*(\d+)\s*\}", body)]
 
 
 def test_tensor_wrapper_rejects_host_tensors():

@@ -61,7 +61,7 @@ SMALL = ["square_128", "ragged_127x193x61", "ragged_513x257x129", "square_1024",
          "rect_256x1024x128", "rect_1024x128x256"]
 
 
-@pytest.mark.parametrize("variant", ["auto", "sb", "db"])
+@pytest.mark.parametrize("variant", ["auto", "sb", "db", "ms"])
 @pytest.mark.parametrize("name", SMALL)
 def test_workload_parity(name, variant):
     _say(f"[parity] {name} {variant}")
@@ -77,17 +77,21 @@ def test_workload_parity(name, variant):
 @pytest.mark.parametrize("cfg", range(NCFG))
 def test_every_config_sb_equals_db_and_matches_oracle(cfg):
     """Each tile configuration, on a ragged shape spanning several tiles in M, N and K and
-    on an aligned one: both variants pass, and agree bit for bit."""
-    for (M, N, K, seed) in [(300, 333, 97, 11), (512, 512, 256, 12)]:
+    on aligned ones (one with many K tiles, so the multi-stage ring wraps several times):
+    all three variants pass, and agree bit for bit (same MFMA sequence per accumulator)."""
+    for (M, N, K, seed) in [(300, 333, 97, 11), (512, 512, 256, 12), (768, 512, 1024, 13)]:
         _say(f"[config] cfg={cfg} {M}x{N}x{K}")
         A, B = ti.workload_inputs(M, N, K, seed)
         C64, Bnd = oracle.gemm_f64(A, B)
         Ad, Bd = _dev(A), _dev(B)
-        Csb = _run(Ad, Bd, "sb", cfg)
-        Cdb = _run(Ad, Bd, "db", cfg)
+        Csb = _run(Ad, Bd, "sb", cfg).clone()
+        Cdb = _run(Ad, Bd, "db", cfg).clone()
+        Cms = _run(Ad, Bd, "ms", cfg).clone()
         assert _ratio(Csb, C64, Bnd) <= 1.0
         assert _ratio(Cdb, C64, Bnd) <= 1.0
+        assert _ratio(Cms, C64, Bnd) <= 1.0
         assert torch.equal(Csb, Cdb), "single- and double-buffered results differ"
+        assert torch.equal(Cms, Cdb), "multi-stage and double-buffered results differ"
 
 
 def _edge_shapes():
@@ -106,7 +110,7 @@ def test_edge_residues(cfg):
         A, B = ti.workload_inputs(M, N, K, 7000 + M + N + K)
         C64, Bnd = oracle.gemm_f64(A, B)
         Ad, Bd = _dev(A), _dev(B)
-        for v in ("sb", "db"):
+        for v in ("sb", "db", "ms"):
             C = torch.full((M, N), float("nan"), device=DEV)
             _run(Ad, Bd, v, cfg, out=C)
             r = _ratio(C, C64, Bnd)
@@ -133,7 +137,7 @@ def test_leading_dimensions_padding_and_misalignment(cfg):
         A = Ad[off:].view(M, lda)[:, :K]
         B = Bd[off:].view(K, ldb)[:, :N]
         C = Cd[off:].view(M, ldc)[:, :N]
-        for v in ("sb", "db"):
+        for v in ("sb", "db", "ms"):
             _run(A, B, v, cfg, out=C)
             assert _ratio(C, C64, Bnd) <= 1.0, (cfg, v, lda, ldb, ldc, off)
             Cfull = Cd[off:].view(M, ldc).cpu().numpy()
@@ -143,7 +147,7 @@ def test_leading_dimensions_padding_and_misalignment(cfg):
 
 
 def test_k_zero_writes_zeros_and_empty_is_noop():
-    for v in ("auto", "sb", "db"):
+    for v in ("auto", "sb", "db", "ms"):
         C = torch.full((37, 41), float("nan"), device=DEV)
         A = torch.empty((37, 0), device=DEV)
         B = torch.empty((0, 41), device=DEV)
@@ -161,7 +165,7 @@ def test_closed_forms_on_gpu():
     n = 257
     B = ti.grid_matrix(91, 2, n, n)
     I = _dev(np.eye(n, dtype=np.float32))
-    for v in ("sb", "db"):
+    for v in ("sb", "db", "ms"):
         C = _run(I, _dev(B), v)
         assert torch.equal(C.cpu(), torch.from_numpy(B)), "identity"
         ones = torch.ones((130, 1000), device=DEV)
@@ -212,13 +216,15 @@ def test_square_4096_full():
     r = _ratio(Cauto, C64, Bnd)
     _say(f"[parity] square_4096 auto ratio={r:.3g}")
     assert r <= 1.0
-    for v in ("sb", "db"):
-        cfg = tdb.gemm_f32_select_cfg(4096, 4096, 4096, tdb.VARIANT_SB if v == "sb"
-                                      else tdb.VARIANT_DB)
-        C = _run(Ad, Bd, v)
+    ids = {"sb": tdb.VARIANT_SB, "db": tdb.VARIANT_DB, "ms": tdb.VARIANT_MS}
+    for v in ("sb", "db", "ms"):
+        cfg = tdb.gemm_f32_select_cfg(4096, 4096, 4096, ids[v])
+        C = _run(Ad, Bd, v).clone()
         assert _ratio(C, C64, Bnd) <= 1.0, v
-        other = _run(Ad, Bd, "db" if v == "sb" else "sb", cfg)
-        assert torch.equal(C, other), f"{v} cfg {cfg}: SB and DB differ"
+        for other_v in ("sb", "db", "ms"):
+            if other_v != v:
+                other = _run(Ad, Bd, other_v, cfg)
+                assert torch.equal(C, other), f"{v} cfg {cfg}: {v} and {other_v} differ"
 
 
 @pytest.mark.slow
@@ -233,7 +239,7 @@ def test_square_8192_sampled():
     Ad, Bd = _dev(A), _dev(B)
     del A, B
     ii, jj = torch.from_numpy(ri).to(DEV), torch.from_numpy(rj).to(DEV)
-    for v in ("auto", "sb", "db"):
+    for v in ("auto", "sb", "db", "ms"):
         C = _run(Ad, Bd, v)
         got = C[ii, jj].cpu().numpy()
         r = oracle.tolerance_ratio(got, c64, bnd)

@@ -27,10 +27,14 @@ def kernels():
     assert funcs and set(funcs) == set(meta)
     out = {}
     for name, body in funcs.items():
-        m = re.search(r"TileCfgILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEELb([01])E", name)
+        m = re.search(r"TileCfgILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEE(?:Lb([01])|Li(\d+))E",
+                      name)
         assert m, name
-        bm, bn, bk, wm, wn, db = (int(x) for x in m.groups())
-        out[name] = dict(cfg=(bm, bn, bk, wm, wn), db=bool(db), body=body, meta=meta[name])
+        bm, bn, bk, wm, wn = (int(x) for x in m.groups()[:5])
+        ms = "gemm_f32_ms_kernel" in name
+        out[name] = dict(cfg=(bm, bn, bk, wm, wn), db=ms or m.group(6) == "1", ms=ms,
+                         stages=int(m.group(7)) if ms else (2 if m.group(6) == "1" else 1),
+                         body=body, meta=meta[name])
     return out
 
 
@@ -60,9 +64,10 @@ def _count_barriers(lines):
 
 
 def test_barriers_per_k_step(kernels):
-    """Per K-loop iteration: 1 barrier (double-buffered) or 2 (single-buffered).  The
-    double-buffered kernel adds one prologue barrier per loop (tile 0 -> slot 0), so a
-    product issues k_tiles barriers in total, against 2 * k_tiles single-buffered."""
+    """Per K-loop iteration: 1 barrier (double-buffered and multi-stage) or 2
+    (single-buffered).  The double-buffered and multi-stage loops add one prologue barrier
+    each (tile 0 in LDS), so a product issues k_tiles barriers in total, against
+    2 * k_tiles single-buffered."""
     facts = json.load(open(GOLDEN))["barriers_per_k_step"]
     for name, k in kernels.items():
         total = _count_barriers(k["body"].split("\n"))
@@ -99,10 +104,36 @@ def test_fp32_matrix_instruction_only(kernels):
 def test_mfma_count_matches_tile(kernels):
     """One K tile is FM * FN * BK / 2 MFMAs per wave (each MFMA consumes a k pair).  The
     kernel holds whole copies of that tile body: single-buffered one per loop (unguarded
-    and guarded), double-buffered two per loop (steady state and the peeled last tile)."""
+    and guarded), double-buffered two per loop (steady state and the peeled last tile),
+    multi-stage one for its own loop plus two for the guarded double-buffered fallback."""
     for name, k in kernels.items():
         bm, bn, bk, wm, wn = k["cfg"]
         fm, fn = bm // wm // 32, bn // wn // 32
         per_tile = fm * fn * bk // 2
         n = len(re.findall(r"\bv_mfma_f32_32x32x2_f32\b", k["body"]))
-        assert n == per_tile * (4 if k["db"] else 2), (k["cfg"], k["db"], n, per_tile)
+        copies = 3 if k["ms"] else (4 if k["db"] else 2)
+        assert n == per_tile * copies, (k["cfg"], k["db"], k["ms"], n, per_tile)
+
+
+def test_multistage_copies_and_m0(kernels):
+    """The multi-stage kernels copy with global_load_lds_dwordx4 only, each copy right
+    after the s_mov_b32 that sets its LDS destination in M0, and nothing else touches M0.
+    The per-tile copy count is (BM*BK + BK*BN) * 4 bytes / 1 KiB / waves, issued S-1 times
+    in the prologue and once in the loop."""
+    seen = 0
+    for name, k in kernels.items():
+        lines = [t.strip() for t in k["body"].split("\n")]
+        m0_lines = [i for i, t in enumerate(lines) if re.search(r"\bm0\b", t)]
+        if not k["ms"]:
+            assert "global_load_lds" not in k["body"], k["cfg"]
+            continue
+        seen += 1
+        for i in m0_lines:
+            assert lines[i].startswith("s_mov_b32 m0,"), (k["cfg"], lines[i])
+            assert lines[i + 1].startswith("global_load_lds_dwordx4"), (k["cfg"], lines[i + 1])
+        bm, bn, bk, wm, wn = k["cfg"]
+        per_wave = (bm * bk + bk * bn) * 4 // 1024 // (wm * wn)
+        n = len(re.findall(r"\bglobal_load_lds_dwordx4\b", k["body"]))
+        assert n == per_wave * k["stages"], (k["cfg"], n, per_wave, k["stages"])
+        assert len(m0_lines) == n
+    assert seen >= 1

@@ -25,7 +25,8 @@ ERR_HIP = -8
 VARIANT_AUTO = 0
 VARIANT_SB = 1
 VARIANT_DB = 2
-_VARIANTS = {"auto": VARIANT_AUTO, "sb": VARIANT_SB, "db": VARIANT_DB}
+VARIANT_MS = 3
+_VARIANTS = {"auto": VARIANT_AUTO, "sb": VARIANT_SB, "db": VARIANT_DB, "ms": VARIANT_MS}
 
 # Every exported symbol and its C signature (kept in step with include/gemmf32.h).
 _i64, _int, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
@@ -34,11 +35,13 @@ SIGNATURES = {
     "gemm_f32": (_int, _GEMM_ARGS + [_vp]),
     "gemm_f32_sb": (_int, _GEMM_ARGS + [_vp]),
     "gemm_f32_db": (_int, _GEMM_ARGS + [_vp]),
+    "gemm_f32_ms": (_int, _GEMM_ARGS + [_vp]),
     "gemm_f32_ex": (_int, _GEMM_ARGS + [_int, _int, _vp]),
     "gemm_f32_select": (_int, [_i64, _i64, _i64, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
     "gemm_f32_select_cfg": (_int, [_i64, _i64, _i64, _int]),
     "gemm_f32_num_configs": (_int, []),
     "gemm_f32_config_info": (_int, [_int] + [ctypes.POINTER(_int)] * 6),
+    "gemm_f32_config_ms": (_int, [_int, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
     "gemm_f32_last_hip_error": (_int, []),
     "gemm_f32_strerror": (ctypes.c_char_p, [_int]),
     "gemm_f32_version": (ctypes.c_char_p, []),
@@ -86,6 +89,10 @@ def gemm_f32_db(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
     return load().gemm_f32_db(M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
+def gemm_f32_ms(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    return load().gemm_f32_ms(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
 def gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, variant, cfg_id, stream=None) -> int:
     return load().gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, variant, cfg_id, stream)
 
@@ -111,6 +118,13 @@ def gemm_f32_config_info(cfg_id):
     rc = load().gemm_f32_config_info(cfg_id, *[ctypes.byref(v) for v in vals])
     keys = ("BM", "BN", "BK", "threads", "lds_bytes_sb", "lds_bytes_db")
     return rc, dict(zip(keys, (v.value for v in vals)))
+
+
+def gemm_f32_config_ms(cfg_id):
+    """Returns (rc, dict) with the multi-stage kernel's stages and lds_bytes."""
+    st, lds = _int(0), _int(0)
+    rc = load().gemm_f32_config_ms(cfg_id, ctypes.byref(st), ctypes.byref(lds))
+    return rc, {"stages": st.value, "lds_bytes": lds.value}
 
 
 def gemm_f32_last_hip_error() -> int:

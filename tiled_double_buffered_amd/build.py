@@ -62,7 +62,7 @@ def device_asm() -> str:
 def kernel_functions(asm: str) -> dict:
     """Map mangled kernel name -> its assembly body (from the label to .Lfunc_end)."""
     out = {}
-    for m in re.finditer(r"^(_Z\S*gemm_f32_tile_kernel\S*):[ \t]*(?:;.*)?$", asm, re.M):
+    for m in re.finditer(r"^(_Z\S*gemm_f32_(?:tile|ms)_kernel\S*):[ \t]*(?:;.*)?$", asm, re.M):
         name = m.group(1)
         end = asm.find(f".Lfunc_end", m.end())
         out[name] = asm[m.end():end]

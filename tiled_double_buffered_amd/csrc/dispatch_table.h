@@ -8,9 +8,9 @@
 // per pair), which rewrites this file; a shape that is not in the table takes the row
 // nearest to it in (log2 M, log2 N, log2 K).
 //
-// Columns: M, N, K, best variant (1 = single-buffered, 2 = double-buffered), its tile
-// configuration, best single-buffered configuration, best double-buffered configuration.
-// Trailing comments: measured microseconds of the best single- and double-buffered runs.
+// Columns: M, N, K, best variant (1 = single-buffered, 2 = double-buffered, 3 = multi-stage
+// direct-to-LDS), its tile configuration, and the best configuration of each variant.
+// Trailing comments: measured microseconds of the best run of each variant.
 #pragma once
 
 #include <cmath>
@@ -20,25 +20,25 @@ namespace gemmf32 {
 
 struct DispatchRow {
   int64_t m, n, k;
-  int variant, cfg, sb_cfg, db_cfg;
+  int variant, cfg, sb_cfg, db_cfg, ms_cfg;
 };
 
 static const DispatchRow kDispatch[] = {
-    {128, 128, 128, 1, 7, 7, 7},  // sb 4.57 us, db 4.58 us
-    {127, 193, 61, 2, 6, 6, 6},  // sb 5.35 us, db 5.25 us
-    {513, 257, 129, 2, 6, 6, 6},  // sb 9.09 us, db 8.57 us
-    {1024, 1024, 1024, 2, 6, 7, 6},  // sb 24.15 us, db 22.56 us
-    {256, 1024, 128, 1, 7, 7, 7},  // sb 4.91 us, db 4.93 us
-    {1024, 128, 256, 2, 6, 7, 6},  // sb 7.30 us, db 7.24 us
-    {4096, 4096, 4096, 2, 1, 3, 1},  // sb 1022.90 us, db 948.27 us
-    {8192, 8192, 8192, 2, 1, 3, 1},  // sb 8203.52 us, db 7496.10 us
-    {256, 256, 256, 2, 6, 7, 6},  // sb 7.28 us, db 7.21 us
-    {512, 512, 512, 2, 6, 7, 6},  // sb 12.38 us, db 12.12 us
-    {2048, 2048, 2048, 2, 4, 7, 4},  // sb 140.76 us, db 130.70 us
-    {6144, 6144, 6144, 2, 4, 4, 4},  // sb 3483.24 us, db 3319.05 us
-    {64, 4096, 4096, 2, 6, 7, 6},  // sb 96.10 us, db 80.34 us
-    {4096, 4096, 512, 2, 2, 3, 2},  // sb 135.36 us, db 129.20 us
-    {2048, 8192, 2048, 2, 1, 3, 1},  // sb 514.65 us, db 479.69 us
+    {128, 128, 128, 1, 7, 7, 7, 6},  // sb 4.63 us, db 4.63 us, ms 4.79 us
+    {127, 193, 61, 2, 6, 6, 6, 6},  // sb 5.31 us, db 5.22 us, ms 5.25 us
+    {513, 257, 129, 3, 6, 6, 6, 6},  // sb 9.09 us, db 8.49 us, ms 8.46 us
+    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.96 us, db 22.42 us, ms 21.54 us
+    {256, 1024, 128, 1, 7, 7, 7, 6},  // sb 4.87 us, db 4.87 us, ms 5.02 us
+    {1024, 128, 256, 2, 6, 7, 6, 6},  // sb 7.29 us, db 7.21 us, ms 7.22 us
+    {4096, 4096, 4096, 2, 1, 3, 1, 0},  // sb 1011.75 us, db 940.94 us, ms 978.54 us
+    {8192, 8192, 8192, 2, 1, 3, 1, 0},  // sb 8142.95 us, db 7414.98 us, ms 7736.04 us
+    {256, 256, 256, 2, 6, 7, 6, 6},  // sb 7.26 us, db 7.18 us, ms 7.20 us
+    {512, 512, 512, 3, 6, 7, 6, 6},  // sb 12.36 us, db 12.08 us, ms 11.80 us
+    {2048, 2048, 2048, 2, 4, 7, 4, 3},  // sb 140.55 us, db 129.64 us, ms 135.12 us
+    {6144, 6144, 6144, 2, 4, 4, 4, 3},  // sb 3471.42 us, db 3318.59 us, ms 3340.08 us
+    {64, 4096, 4096, 3, 6, 7, 6, 6},  // sb 96.02 us, db 80.36 us, ms 75.74 us
+    {4096, 4096, 512, 2, 2, 3, 2, 0},  // sb 134.82 us, db 129.02 us, ms 134.30 us
+    {2048, 8192, 2048, 2, 1, 3, 1, 0},  // sb 511.14 us, db 477.13 us, ms 497.06 us
 };
 
 static inline double dispatch_log2(int64_t x) { return x > 0 ? std::log2((double)x) : -1.0; }
@@ -68,7 +68,7 @@ static inline void select_shape(int64_t M, int64_t N, int64_t K, int* variant, i
 
 static inline int select_for_variant(int64_t M, int64_t N, int64_t K, int variant) {
   const DispatchRow& r = dispatch_nearest(M, N, K);
-  return variant == 1 ? r.sb_cfg : r.db_cfg;
+  return variant == 1 ? r.sb_cfg : variant == 3 ? r.ms_cfg : r.db_cfg;
 }
 
 }  // namespace gemmf32

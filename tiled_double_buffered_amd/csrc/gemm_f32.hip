@@ -495,6 +495,297 @@ gemm_f32_tile_kernel(int M, int N, int K, const float* __restrict__ A, int64_t l
 }
 
 // ------------------------------------------------------------------------------------
+// Multi-stage variant (MS): S LDS stages filled by gfx950 direct-to-LDS loads.
+//
+// The glossary page ("Double Buffering", second paragraph and the figure caption) notes
+// that its platform lost its asynchronous copy engine, so its double buffering overlaps
+// copies and math only through instruction-level parallelism, and it names the CUDA
+// analogue: a multi-stage asynchronous-copy pipeline.  gfx950 has the asynchronous copy:
+// global_load_lds_dwordx4 moves 16 bytes per lane from global memory straight into LDS
+// (lane L's bytes land at M0 + 16*L), with no registers in between and completion
+// tracked by vmcnt.  Tiles l+1 .. l+S-1 are in flight while tile l is multiplied.
+//
+// LDS layout of a stage (no padding; XOR swizzle at 16-byte-chunk granularity):
+//   A part: BM rows of BK floats;  chunk c of row r is stored at chunk c ^ swz_a(r)
+//   B part: BK rows of BN floats;  chunk c of row k is stored at chunk c ^ swz_b(k)
+// A wave's copy instruction always fills 1 KiB of consecutive LDS; each lane chooses the
+// global chunk that belongs at its position, so the swizzle costs nothing on the copy
+// side and makes the fragment reads conflict-free: the 16 lanes of a 16-byte read (16
+// consecutive rows, one logical chunk) hit 16 distinct bank groups, and the two
+// half-waves of a B read (rows k and k+4) fall on opposite halves of the 64 banks.
+//
+// The compiler's own wait insertion cannot tell one stage from another and would wait
+// for every outstanding copy before any LDS read, so the copies are issued from inline
+// assembly and their completion is waited for explicitly, per tile.
+// ------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) float lds_float;
+
+template <class C, int S>
+struct MsCfg {
+  static constexpr int STAGES = S;
+  static constexpr int A_FLOATS = C::BM * C::BK;
+  static constexpr int B_FLOATS = C::BK * C::BN;
+  static constexpr int STAGE = A_FLOATS + B_FLOATS;  // floats per stage
+  static constexpr int A_CHUNKS = A_FLOATS / 256;    // 1 KiB copy instructions, A part
+  static constexpr int B_CHUNKS = B_FLOATS / 256;
+  static constexpr int WAVES = C::NT / 64;
+  static constexpr int D = (A_CHUNKS + B_CHUNKS) / WAVES;  // copies per wave per tile
+  static constexpr int CPR_A = C::BK / 4;            // 16-byte chunks per A row
+  static constexpr int RPC_A = 256 / C::BK;          // A rows per 1 KiB
+  static constexpr int CPR_B = C::BN / 4;
+  static constexpr int RPC_B = 256 / C::BN;
+  // LDS floats: the stages, or the two padded slots of the guarded fallback loop.
+  static constexpr int LDS_FLOATS = S * STAGE > 2 * C::SLOT ? S * STAGE : 2 * C::SLOT;
+  static_assert(S >= 2, "at least two stages");
+  static_assert(C::BK == 16 || C::BK == 32 || C::BK == 64, "swizzle period");
+  static_assert(C::BN % 64 == 0, "B swizzle flips chunk bit 3 inside 16-chunk groups");
+  static_assert(A_FLOATS % 256 == 0 && B_FLOATS % 256 == 0, "whole 1 KiB copies");
+  static_assert((A_CHUNKS + B_CHUNKS) % WAVES == 0, "copies divide among waves");
+  static_assert(D * (S - 2) <= 63, "vmcnt range");
+  static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS of one CU");
+};
+
+template <class C>
+__device__ __forceinline__ int swz_a(int row) {
+  return (row / (64 / C::BK)) % (C::BK / 4);
+}
+__device__ __forceinline__ int swz_b(int k) { return ((k >> 2) & 1) << 3; }
+
+template <class C, int S>
+struct MsCopy {
+  using MC = MsCfg<C, S>;
+  const float* ptr[MC::D];  // this lane's source for tile 0
+  int64_t step[MC::D];      // floats between consecutive K tiles
+  uint32_t lds_off[MC::D];  // byte offset of the wave's 1 KiB inside a stage
+  uint32_t lds_base;        // LDS byte address of stage 0
+
+  __device__ inline void init(const float* smem, int wave, int lane, const float* A,
+                              int64_t lda, const float* B, int64_t ldb, int m0, int n0) {
+    lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_float*)smem);
+#pragma unroll
+    for (int i = 0; i < MC::D; ++i) {
+      const int j = wave + i * MC::WAVES;  // which 1 KiB of the stage this copy fills
+      if (j < MC::A_CHUNKS) {
+        const int row = j * MC::RPC_A + lane / MC::CPR_A;
+        const int c = (lane % MC::CPR_A) ^ swz_a<C>(row);
+        ptr[i] = A + (int64_t)(m0 + row) * lda + 4 * c;
+        step[i] = C::BK;
+        lds_off[i] = (uint32_t)j * 1024u;
+      } else {
+        const int jb = j - MC::A_CHUNKS;
+        const int k = jb * MC::RPC_B + lane / MC::CPR_B;
+        const int c = (lane % MC::CPR_B) ^ swz_b(k);
+        ptr[i] = B + (int64_t)k * ldb + n0 + 4 * c;
+        step[i] = (int64_t)C::BK * ldb;
+        lds_off[i] = (uint32_t)(MC::A_FLOATS * 4 + jb * 1024);
+      }
+    }
+  }
+
+  // Start the copy of K tile kt into stage st (asynchronous; counted by vmcnt).
+  __device__ inline void issue(int kt, int st) const {
+    const uint32_t stage_base = lds_base + (uint32_t)st * (uint32_t)(MC::STAGE * 4);
+#pragma unroll
+    for (int i = 0; i < MC::D; ++i) {
+      const float* src = ptr[i] + (int64_t)kt * step[i];
+      const uint32_t m0v = __builtin_amdgcn_readfirstlane(stage_base + lds_off[i]);
+      // M0 is reserved by the compiler, which warns about clobbering it.  Nothing else in
+      // these kernels uses M0 (a structural test checks that every M0 write is one of these
+      // copies, immediately followed by its load), so the clobber is safe here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(src), "s"(m0v)
+                   : "memory", "m0");
+#pragma clang diagnostic pop
+    }
+  }
+};
+
+// Wait until at most N copies of this wave are outstanding and this wave's LDS reads have
+// returned.
+template <int N>
+__device__ __forceinline__ void ms_wait() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" : : "n"(N) : "memory");
+}
+
+// Tile `next` must have landed in every wave before anybody reads it: wait for this
+// wave's copies of it (`after` later tiles, 0 .. S-2, may stay in flight), then barrier.
+template <class C, int S>
+__device__ __forceinline__ void ms_wait_tile_barrier(int after) {
+  constexpr int D = MsCfg<C, S>::D;
+  if (S >= 4 && after >= 2)
+    ms_wait<(S >= 4 ? 2 * D : 0)>();
+  else if (S >= 3 && after >= 1)
+    ms_wait<(S >= 3 ? D : 0)>();
+  else
+    ms_wait<0>();
+  asm volatile("s_barrier" : : : "memory");
+}
+
+template <class C, int S>
+struct LaneViewMs {
+  int a_off;          // float offset of this lane's A row (fm = 0) inside a stage
+  int a_x;            // h ^ swz_a(row): logical chunk 2q+h of the row is at (2q) ^ a_x
+  int b_off[C::FN];   // float offset of B[4h][col(fn)] inside a stage (swizzled)
+
+  __device__ inline void init(int wm, int wn, int lane) {
+    const int h = lane >> 5, l32 = lane & 31;
+    const int row = wm * C::TM + l32;
+    a_off = row * C::BK;
+    a_x = h ^ swz_a<C>(row);
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int col = wn * C::TN + fn * 32 + l32;
+      const int k = 4 * h;
+      b_off[fn] = MsCfg<C, S>::A_FLOATS + k * C::BN + 4 * ((col >> 2) ^ swz_b(k)) + (col & 3);
+    }
+  }
+};
+
+template <class C, int S>
+__device__ inline void read_frag_ms(const float* stage, const LaneViewMs<C, S>& lv, int q,
+                                    Frag<C>& f) {
+  const float* a_ptr = stage + lv.a_off + 4 * ((2 * q) ^ lv.a_x);
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+    f.a[fm] = *reinterpret_cast<const floatx4*>(a_ptr + fm * 32 * C::BK);
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) f.b[fn][t] = stage[lv.b_off[fn] + (8 * q + t) * C::BN];
+}
+
+// The MS K-loop.  Per iteration l: start the copy of tile l+S-1 into the stage that tile
+// l-1 used, multiply tile l, and -- at the hand-off, before the second half of tile l's
+// last round -- wait for tile l+1 and pass ONE barrier.  That barrier makes tile l+1
+// visible to every wave and certifies that every wave has finished reading tile l, whose
+// stage the copy issued in the next iteration overwrites.
+template <class C, int S>
+__device__ inline void k_loop_ms(float* smem, const MsCopy<C, S>& cp,
+                                 const LaneViewMs<C, S>& lv, int k_tiles,
+                                 floatx16 (&acc)[C::FM][C::FN]) {
+  using MC = MsCfg<C, S>;
+  constexpr int R = C::BK / 8;
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t)
+    if (t < k_tiles) cp.issue(t, t);
+  ms_wait_tile_barrier<C, S>(min(S - 2, k_tiles - 1));
+  Frag<C> f[2];
+  read_frag_ms(smem, lv, 0, f[0]);
+  int st = 0;                 // stage of tile l
+  int st_issue = S - 1;       // stage for tile l+S-1
+  for (int l = 0; l < k_tiles; ++l) {
+    if (l + S - 1 < k_tiles) cp.issue(l + S - 1, st_issue);
+    const float* cur = smem + st * MC::STAGE;
+#pragma unroll
+    for (int q = 0; q + 1 < R; ++q) {
+      read_frag_ms(cur, lv, q + 1, f[(q + 1) & 1]);
+      mfma_round<C, 0>(f[q & 1], acc);
+    }
+    mfma_round<C, 1>(f[1], acc);
+    st = st + 1 == S ? 0 : st + 1;
+    st_issue = st_issue + 1 == S ? 0 : st_issue + 1;
+    if (l + 1 < k_tiles) {
+      ms_wait_tile_barrier<C, S>(min(S - 2, k_tiles - 2 - l));
+      read_frag_ms(smem + st * MC::STAGE, lv, 0, f[0]);
+    }
+    mfma_round<C, 2>(f[1], acc);
+  }
+}
+
+template <class C, int S>
+__global__ void __launch_bounds__(C::NT)
+gemm_f32_ms_kernel(int M, int N, int K, const float* __restrict__ A, int64_t lda,
+                   const float* __restrict__ B, int64_t ldb, float* __restrict__ Cmat,
+                   int64_t ldc, int flags) {
+  using MC = MsCfg<C, S>;
+  __shared__ __attribute__((aligned(1024))) float smem[MC::LDS_FLOATS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / C::WAVES_N;
+  const int wn = wave % C::WAVES_N;
+  const int tiles_m = (M + C::BM - 1) / C::BM;
+  const int tiles_n = (N + C::BN - 1) / C::BN;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  LoopArgs<C> g;
+  g.A = A;
+  g.B = B;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.m0 = tm * C::BM;
+  g.n0 = tn * C::BN;
+  const bool m_full = g.m0 + C::BM <= M;
+  const bool n_full = g.n0 + C::BN <= N;
+  g.vec_a = (flags & kVecA) && m_full;
+  g.vec_b = (flags & kVecB) && n_full;
+
+  floatx16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
+
+  const int k_tiles = (K + C::BK - 1) / C::BK;
+  if (k_tiles > 0) {
+    if (g.vec_a && g.vec_b && (K % C::BK) == 0) {
+      MsCopy<C, S> cp;
+      cp.init(smem, wave, lane, A, lda, B, ldb, g.m0, g.n0);
+      LaneViewMs<C, S> lv;
+      lv.init(wm, wn, lane);
+      k_loop_ms<C, S>(smem, cp, lv, k_tiles, acc);
+    } else {
+      // Edge, misaligned or K-ragged tiles: the guarded double-buffered loop.
+      TileCopy<C> cp;
+      cp.init(tid);
+      LaneView<C> lv;
+      lv.init(wm, wn, lane);
+      k_loop_db<C, true>(smem, cp, lv, g, k_tiles, acc);
+    }
+  }
+
+  const int row0 = g.m0 + wm * C::TM + 4 * (lane >> 5);
+  const int col0 = g.n0 + wn * C::TN + (lane & 31);
+  if (m_full && n_full) {
+    float* cbase = Cmat + (int64_t)row0 * ldc + col0;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          cbase[(int64_t)(fm * 32 + 8 * (r >> 2) + (r & 3)) * ldc + fn * 32] = acc[fm][fn][r];
+  } else {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + fm * 32 + 8 * (r >> 2) + (r & 3);
+          const int col = col0 + fn * 32;
+          if (row < M && col < N) Cmat[(int64_t)row * ldc + col] = acc[fm][fn][r];
+        }
+  }
+}
+
+// Stage count per configuration: as many as fit (at most 4) in the 160 KiB of a CU.
+template <class C>
+constexpr int ms_stages() {
+  constexpr int stage_bytes = 4 * (C::BM * C::BK + C::BK * C::BN);
+  return (160 * 1024) / stage_bytes >= 4 ? 4 : (160 * 1024) / stage_bytes;
+}
+
+// ------------------------------------------------------------------------------------
 // Configuration table.  Ids are part of the ABI (gemm_f32_ex, gemm_f32_config_info).
 // ------------------------------------------------------------------------------------
 using Cfg0 = TileCfg<256, 256, 16, 2, 2>;  // wave 128x128 (16 blocks)
@@ -512,19 +803,24 @@ typedef void (*KernelFn)(int, int, int, const float*, int64_t, const float*, int
 struct CfgEntry {
   int bm, bn, bk, nt;
   int lds_sb, lds_db;
-  KernelFn sb, db;
+  int ms_stages, lds_ms;
+  KernelFn sb, db, ms;
 };
 
 template <class C>
 constexpr CfgEntry make_entry() {
+  constexpr int S = ms_stages<C>();
   return CfgEntry{C::BM,
                   C::BN,
                   C::BK,
                   C::NT,
                   (int)(C::SLOT * sizeof(float)),
                   (int)(2 * C::SLOT * sizeof(float)),
+                  S,
+                  (int)(MsCfg<C, S>::LDS_FLOATS * sizeof(float)),
                   &gemm_f32_tile_kernel<C, false>,
-                  &gemm_f32_tile_kernel<C, true>};
+                  &gemm_f32_tile_kernel<C, true>,
+                  &gemm_f32_ms_kernel<C, S>};
 }
 
 static const CfgEntry kConfigs[] = {
@@ -584,7 +880,7 @@ static int launch(int variant, int cfg_id, int64_t M, int64_t N, int64_t K, cons
   if (K > 0 && (((uintptr_t)B) & 15u) == 0 && (ldb & 3) == 0) flags |= kVecB;
   int m = (int)M, n = (int)N, k = (int)K;
   void* args[] = {&m, &n, &k, (void*)&A, &lda, (void*)&B, &ldb, &C, &ldc, &flags};
-  KernelFn fn = variant == GEMMF32_VARIANT_SB ? e.sb : e.db;
+  KernelFn fn = variant == GEMMF32_VARIANT_SB ? e.sb : variant == GEMMF32_VARIANT_MS ? e.ms : e.db;
   hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)tiles), dim3(e.nt), args, 0,
                                    (hipStream_t)stream);
   if (err != hipSuccess) {
@@ -599,13 +895,14 @@ static int env_variant() {
   if (v == nullptr) return GEMMF32_VARIANT_AUTO;
   if (std::strcmp(v, "sb") == 0) return GEMMF32_VARIANT_SB;
   if (std::strcmp(v, "db") == 0) return GEMMF32_VARIANT_DB;
+  if (std::strcmp(v, "ms") == 0) return GEMMF32_VARIANT_MS;
   return GEMMF32_VARIANT_AUTO;
 }
 
 static int run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
                int64_t ldb, float* C, int64_t ldc, int variant, int cfg_id, void* stream) {
   if (variant != GEMMF32_VARIANT_AUTO && variant != GEMMF32_VARIANT_SB &&
-      variant != GEMMF32_VARIANT_DB)
+      variant != GEMMF32_VARIANT_DB && variant != GEMMF32_VARIANT_MS)
     return GEMMF32_ERR_BAD_CONFIG;
   if (cfg_id < -1 || cfg_id >= kNumConfigs) return GEMMF32_ERR_BAD_CONFIG;
   int rc = validate(M, N, K, A, lda, B, ldb, C, ldc);
@@ -643,6 +940,11 @@ int gemm_f32_db(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, co
   return run(M, N, K, A, lda, B, ldb, C, ldc, GEMMF32_VARIANT_DB, -1, stream);
 }
 
+int gemm_f32_ms(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
+                int64_t ldb, float* C, int64_t ldc, void* stream) {
+  return run(M, N, K, A, lda, B, ldb, C, ldc, GEMMF32_VARIANT_MS, -1, stream);
+}
+
 int gemm_f32_ex(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
                 int64_t ldb, float* C, int64_t ldc, int variant, int cfg_id, void* stream) {
   return run(M, N, K, A, lda, B, ldb, C, ldc, variant, cfg_id, stream);
@@ -659,7 +961,8 @@ int gemm_f32_select(int64_t M, int64_t N, int64_t K, int* variant, int* cfg_id) 
 
 int gemm_f32_select_cfg(int64_t M, int64_t N, int64_t K, int variant) {
   if (M < 0 || N < 0 || K < 0) return GEMMF32_ERR_NEGATIVE_DIM;
-  if (variant != GEMMF32_VARIANT_SB && variant != GEMMF32_VARIANT_DB)
+  if (variant != GEMMF32_VARIANT_SB && variant != GEMMF32_VARIANT_DB &&
+      variant != GEMMF32_VARIANT_MS)
     return GEMMF32_ERR_BAD_CONFIG;
   return select_for_variant(M, N, K, variant);
 }
@@ -676,6 +979,14 @@ int gemm_f32_config_info(int cfg_id, int* BM, int* BN, int* BK, int* threads, in
   if (threads) *threads = e.nt;
   if (lds_sb) *lds_sb = e.lds_sb;
   if (lds_db) *lds_db = e.lds_db;
+  return GEMMF32_OK;
+}
+
+int gemm_f32_config_ms(int cfg_id, int* stages, int* lds_bytes) {
+  if (cfg_id < 0 || cfg_id >= kNumConfigs) return GEMMF32_ERR_BAD_CONFIG;
+  const CfgEntry& e = kConfigs[cfg_id];
+  if (stages) *stages = e.ms_stages;
+  if (lds_bytes) *lds_bytes = e.lds_ms;
   return GEMMF32_OK;
 }
 

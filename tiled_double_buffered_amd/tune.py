@@ -25,6 +25,9 @@ import time
 from . import _binding as tdb
 from .build import CSRC
 
+VARIANTS = (tdb.VARIANT_SB, tdb.VARIANT_DB, tdb.VARIANT_MS)
+NAMES = {tdb.VARIANT_SB: "sb", tdb.VARIANT_DB: "db", tdb.VARIANT_MS: "ms"}
+
 SHAPES = [
     # the workloads
     (128, 128, 128), (127, 193, 61), (513, 257, 129), (1024, 1024, 1024),
@@ -44,9 +47,9 @@ HEADER_TEMPLATE = """// Per-shape dispatch table: (M, N, K) -> variant and tile 
 // per pair), which rewrites this file; a shape that is not in the table takes the row
 // nearest to it in (log2 M, log2 N, log2 K).
 //
-// Columns: M, N, K, best variant (1 = single-buffered, 2 = double-buffered), its tile
-// configuration, best single-buffered configuration, best double-buffered configuration.
-// Trailing comments: measured microseconds of the best single- and double-buffered runs.
+// Columns: M, N, K, best variant (1 = single-buffered, 2 = double-buffered, 3 = multi-stage
+// direct-to-LDS), its tile configuration, and the best configuration of each variant.
+// Trailing comments: measured microseconds of the best run of each variant.
 #pragma once
 
 #include <cmath>
@@ -56,7 +59,7 @@ namespace gemmf32 {{
 
 struct DispatchRow {{
   int64_t m, n, k;
-  int variant, cfg, sb_cfg, db_cfg;
+  int variant, cfg, sb_cfg, db_cfg, ms_cfg;
 }};
 
 static const DispatchRow kDispatch[] = {{
@@ -90,7 +93,7 @@ static inline void select_shape(int64_t M, int64_t N, int64_t K, int* variant, i
 
 static inline int select_for_variant(int64_t M, int64_t N, int64_t K, int variant) {{
   const DispatchRow& r = dispatch_nearest(M, N, K);
-  return variant == 1 ? r.sb_cfg : r.db_cfg;
+  return variant == 1 ? r.sb_cfg : variant == 3 ? r.ms_cfg : r.db_cfg;
 }}
 
 }}  // namespace gemmf32
@@ -104,7 +107,7 @@ def measure(shapes, rounds=2, batches=5, batch_ms=20.0, log=print):
     stream = torch.cuda.current_stream(dev)
     s_ptr = stream.cuda_stream
     ncfg = tdb.gemm_f32_num_configs()
-    pairs = [(v, c) for c in range(ncfg) for v in (tdb.VARIANT_SB, tdb.VARIANT_DB)]
+    pairs = [(v, c) for c in range(ncfg) for v in VARIANTS]
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
     results = []
@@ -154,7 +157,7 @@ def measure(shapes, rounds=2, batches=5, batch_ms=20.0, log=print):
                 per_round[p].append(statistics.median(ts))
         row = {"M": M, "N": N, "K": K, "us": {}}
         for (v, c), xs in per_round.items():
-            row["us"][f"{'sb' if v == tdb.VARIANT_SB else 'db'}{c}"] = statistics.median(xs)
+            row["us"][f"{NAMES[v]}{c}"] = statistics.median(xs)
         results.append(row)
         best = min(row["us"].items(), key=lambda kv: kv[1])
         log(f"{M}x{N}x{K}: best {best[0]} {best[1]:.2f} us "
@@ -166,20 +169,26 @@ def measure(shapes, rounds=2, batches=5, batch_ms=20.0, log=print):
 def table_rows(results):
     rows = []
     for r in results:
-        sb = min(((k, v) for k, v in r["us"].items() if k.startswith("sb")), key=lambda kv: kv[1])
-        db = min(((k, v) for k, v in r["us"].items() if k.startswith("db")), key=lambda kv: kv[1])
-        sb_cfg, db_cfg = int(sb[0][2:]), int(db[0][2:])
-        variant, cfg = (1, sb_cfg) if sb[1] < db[1] else (2, db_cfg)
-        rows.append((r["M"], r["N"], r["K"], variant, cfg, sb_cfg, db_cfg, sb[1], db[1]))
+        best = {}
+        for name in ("sb", "db", "ms"):
+            cands = [(k, v) for k, v in r["us"].items() if k[:2] == name]
+            if cands:
+                k, v = min(cands, key=lambda kv: kv[1])
+                best[name] = (int(k[2:]), v)
+        win = min(best, key=lambda n: best[n][1])
+        vid = {"sb": 1, "db": 2, "ms": 3}[win]
+        ms = best.get("ms", best["db"])
+        rows.append((r["M"], r["N"], r["K"], vid, best[win][0], best["sb"][0], best["db"][0],
+                     ms[0], best["sb"][1], best["db"][1], ms[1]))
     return rows
 
 
 def write_header(results, device, rounds, batches, batch_ms, path=None):
     path = path or os.path.join(CSRC, "dispatch_table.h")
     lines = []
-    for (m, n, k, v, c, s, d, sb_us, db_us) in table_rows(results):
-        lines.append(f"    {{{m}, {n}, {k}, {v}, {c}, {s}, {d}}},  // sb {sb_us:.2f} us, "
-                     f"db {db_us:.2f} us")
+    for (m, n, k, v, c, s, d, ms, sb_us, db_us, ms_us) in table_rows(results):
+        lines.append(f"    {{{m}, {n}, {k}, {v}, {c}, {s}, {d}, {ms}}},  // sb {sb_us:.2f} us, "
+                     f"db {db_us:.2f} us, ms {ms_us:.2f} us")
     text = HEADER_TEMPLATE.format(device=device, rounds=rounds, batches=batches,
                                   batch_ms=int(batch_ms), rows="\n".join(lines))
     with open(path, "w") as f:
