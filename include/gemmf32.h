@@ -59,16 +59,25 @@ enum {
                                   K step has one barrier, prefetches tile l+1 into the
                                   idle slot and computes on the current one ("Double
                                   Buffering", code figure; "Case Study", code figure)   */
-    GEMMF32_VARIANT_MS = 3     /* S >= 2 LDS stages filled by asynchronous direct-to-LDS
+    GEMMF32_VARIANT_MS = 3,    /* S >= 2 LDS stages filled by asynchronous direct-to-LDS
                                   copies, tiles l+1 .. l+S-1 in flight, one barrier per
                                   K step: the multi-stage asynchronous-copy pipeline the
                                   glossary page names as the CUDA analogue ("Double
                                   Buffering", second paragraph)                         */
+    GEMMF32_VARIANT_SB3 = 4    /* measurement baseline: single-buffered with the A and B
+                                  copies published by separate barriers, copy A ->
+                                  barrier -> copy B -> barrier -> compute -> barrier,
+                                  three barriers per K step (the pre-coalescing fence
+                                  placement of "Dependence-aware group synchronization on
+                                  M1 Max", section "Transformation and safety boundary");
+                                  only through gemm_f32_ex, never dispatched; its tile
+                                  configuration defaults to the single-buffered column  */
 };
 
 /* C = A.B with the variant and tile configuration chosen per shape by the dispatch
  * table (GEMMF32_VARIANT environment variable "sb", "db" or "ms" forces the variant, for
- * measurement).  The pages' lesson that the faster variant depends on the shape is the
+ * measurement; GEMMF32_RASTER=<group_m>[,noxcd] changes the order in which workgroups walk
+ * the output tiles, for every launching entry point, also for measurement only).  The pages' lesson that the faster variant depends on the shape is the
  * reason for the table ("Double Buffering", last two paragraphs). */
 int gemm_f32(int64_t M, int64_t N, int64_t K,
              const float *A, int64_t lda,
@@ -101,7 +110,8 @@ int gemm_f32_ms(int64_t M, int64_t N, int64_t K,
                 float *C, int64_t ldc,
                 void *stream);
 
-/* C = A.B with an explicit variant (GEMMF32_VARIANT_SB, _DB or _MS; _AUTO = dispatch table)
+/* C = A.B with an explicit variant (GEMMF32_VARIANT_SB, _DB, _MS or _SB3; _AUTO = dispatch
+ * table)
  * and tile configuration id (0 .. gemm_f32_num_configs()-1; -1 = dispatch table).  For
  * measurement and tests: every (variant, configuration) pair computes the same product. */
 int gemm_f32_ex(int64_t M, int64_t N, int64_t K,

@@ -49,7 +49,8 @@ def test_version_and_strerror():
 
 
 # Fake, 256-byte aligned, far-apart addresses.  Only ever used with arguments that fail
-# validation or with M == 0 / N == 0.
+# validation or with M == 0 / N == 0: a call that passed validation would launch a kernel
+# on them.  Invalid variant or configuration ids are values no future id can take.
 PA, PB, PC = 0x7F0000000000, 0x7F1000000000, 0x7F2000000000
 
 
@@ -96,7 +97,9 @@ def test_degenerate_shapes_are_noops_without_launch():
 
 def test_ex_rejects_bad_variant_and_config():
     n = tdb.gemm_f32_num_configs()
-    assert tdb.gemm_f32_ex(4, 4, 4, PA, 4, PB, 4, PC, 4, 4, -1) == tdb.ERR_BAD_CONFIG
+    # variant ids that can never be valid (the check runs before validation and launch)
+    assert tdb.gemm_f32_ex(4, 4, 4, PA, 4, PB, 4, PC, 4, 99, -1) == tdb.ERR_BAD_CONFIG
+    assert tdb.gemm_f32_ex(4, 4, 4, PA, 4, PB, 4, PC, 4, -5, -1) == tdb.ERR_BAD_CONFIG
     assert tdb.gemm_f32_ex(4, 4, 4, PA, 4, PB, 4, PC, 4, 1, n) == tdb.ERR_BAD_CONFIG
     assert tdb.gemm_f32_ex(4, 4, 4, PA, 4, PB, 4, PC, 4, 2, -2) == tdb.ERR_BAD_CONFIG
 

@@ -61,7 +61,7 @@ SMALL = ["square_128", "ragged_127x193x61", "ragged_513x257x129", "square_1024",
          "rect_256x1024x128", "rect_1024x128x256"]
 
 
-@pytest.mark.parametrize("variant", ["auto", "sb", "db", "ms"])
+@pytest.mark.parametrize("variant", ["auto", "sb", "db", "ms", "sb3"])
 @pytest.mark.parametrize("name", SMALL)
 def test_workload_parity(name, variant):
     _say(f"[parity] {name} {variant}")
@@ -87,11 +87,13 @@ def test_every_config_sb_equals_db_and_matches_oracle(cfg):
         Csb = _run(Ad, Bd, "sb", cfg).clone()
         Cdb = _run(Ad, Bd, "db", cfg).clone()
         Cms = _run(Ad, Bd, "ms", cfg).clone()
+        Csb3 = _run(Ad, Bd, "sb3", cfg).clone()
         assert _ratio(Csb, C64, Bnd) <= 1.0
         assert _ratio(Cdb, C64, Bnd) <= 1.0
         assert _ratio(Cms, C64, Bnd) <= 1.0
         assert torch.equal(Csb, Cdb), "single- and double-buffered results differ"
         assert torch.equal(Cms, Cdb), "multi-stage and double-buffered results differ"
+        assert torch.equal(Csb3, Csb), "split-barrier and single-buffered results differ"
 
 
 def _edge_shapes():
@@ -110,7 +112,7 @@ def test_edge_residues(cfg):
         A, B = ti.workload_inputs(M, N, K, 7000 + M + N + K)
         C64, Bnd = oracle.gemm_f64(A, B)
         Ad, Bd = _dev(A), _dev(B)
-        for v in ("sb", "db", "ms"):
+        for v in ("sb", "db", "ms", "sb3"):
             C = torch.full((M, N), float("nan"), device=DEV)
             _run(Ad, Bd, v, cfg, out=C)
             r = _ratio(C, C64, Bnd)

@@ -32,8 +32,10 @@ def kernels():
         assert m, name
         bm, bn, bk, wm, wn = (int(x) for x in m.groups()[:5])
         ms = "gemm_f32_ms_kernel" in name
-        out[name] = dict(cfg=(bm, bn, bk, wm, wn), db=ms or m.group(6) == "1", ms=ms,
-                         stages=int(m.group(7)) if ms else (2 if m.group(6) == "1" else 1),
+        loop = int(m.group(7))
+        kind = "ms" if ms else {1: "sb", 2: "db", 4: "sb3"}[loop]
+        out[name] = dict(cfg=(bm, bn, bk, wm, wn), kind=kind, db=kind in ("db", "ms"),
+                         ms=ms, stages=loop if ms else (2 if kind == "db" else 1),
                          body=body, meta=meta[name])
     return out
 
@@ -64,8 +66,8 @@ def _count_barriers(lines):
 
 
 def test_barriers_per_k_step(kernels):
-    """Per K-loop iteration: 1 barrier (double-buffered and multi-stage) or 2
-    (single-buffered).  The double-buffered and multi-stage loops add one prologue barrier
+    """Per K-loop iteration: 1 barrier (double-buffered and multi-stage), 2
+    (single-buffered) or 3 (single-buffered with split copy barriers).  The double-buffered and multi-stage loops add one prologue barrier
     each (tile 0 in LDS), so a product issues k_tiles barriers in total, against
     2 * k_tiles single-buffered."""
     facts = json.load(open(GOLDEN))["barriers_per_k_step"]
@@ -73,7 +75,9 @@ def test_barriers_per_k_step(kernels):
         total = _count_barriers(k["body"].split("\n"))
         loops = {h: ls for h, ls in _loop_blocks(k["body"]).items() if _count_barriers(ls)}
         assert loops, f"no K-loop with a barrier in {k['cfg']}"
-        expected = facts["double_buffered"] if k["db"] else facts["single_buffered"]
+        expected = {"db": facts["double_buffered"], "ms": facts["double_buffered"],
+                    "sb": facts["single_buffered"],
+                    "sb3": facts["single_buffered_split_copies"]}[k["kind"]]
         inside = 0
         for h, ls in loops.items():
             assert _count_barriers(ls) == expected, (k["cfg"], k["db"], h)
@@ -111,7 +115,7 @@ def test_mfma_count_matches_tile(kernels):
         fm, fn = bm // wm // 32, bn // wn // 32
         per_tile = fm * fn * bk // 2
         n = len(re.findall(r"\bv_mfma_f32_32x32x2_f32\b", k["body"]))
-        copies = 3 if k["ms"] else (4 if k["db"] else 2)
+        copies = {"ms": 3, "db": 4, "sb": 2, "sb3": 2}[k["kind"]]
         assert n == per_tile * copies, (k["cfg"], k["db"], k["ms"], n, per_tile)
 
 

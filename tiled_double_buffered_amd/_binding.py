@@ -26,7 +26,9 @@ VARIANT_AUTO = 0
 VARIANT_SB = 1
 VARIANT_DB = 2
 VARIANT_MS = 3
-_VARIANTS = {"auto": VARIANT_AUTO, "sb": VARIANT_SB, "db": VARIANT_DB, "ms": VARIANT_MS}
+VARIANT_SB3 = 4
+_VARIANTS = {"auto": VARIANT_AUTO, "sb": VARIANT_SB, "db": VARIANT_DB, "ms": VARIANT_MS,
+             "sb3": VARIANT_SB3}
 
 # Every exported symbol and its C signature (kept in step with include/gemmf32.h).
 _i64, _int, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p

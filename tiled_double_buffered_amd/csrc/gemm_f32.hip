@@ -75,19 +75,24 @@ enum : int {
 // ------------------------------------------------------------------------------------
 // Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin; renumber
 // them so that consecutive ids run on one XCD (which has its own L2), then walk the
-// tiles in column-major groups of GROUP_M tile rows so that workgroups close in id
-// share panels of A and B.
+// tiles in column-major groups of `group_m` tile rows so that workgroups close in id
+// share panels of A and B.  Both choices can be changed per launch for measurement (flags
+// bits 8..15: group_m, 0 = the default 8; bit 16: keep the hardware order of ids).
 // ------------------------------------------------------------------------------------
-__device__ inline void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+enum : int { kRasterGroupShift = 8, kRasterNoXcdRemap = 1 << 16 };
+
+__device__ inline void tile_coords(int tiles_m, int tiles_n, int flags, int& tm, int& tn) {
   constexpr int kXcds = 8;
-  constexpr int kGroupM = 8;
+  const int gm_flag = (flags >> kRasterGroupShift) & 0xff;
+  const int group_m = gm_flag ? gm_flag : 8;
   const int nwg = gridDim.x;
   int bid = blockIdx.x;
-  if (nwg % kXcds == 0) bid = (bid % kXcds) * (nwg / kXcds) + bid / kXcds;
-  const int per_group = kGroupM * tiles_n;
+  if (!(flags & kRasterNoXcdRemap) && nwg % kXcds == 0)
+    bid = (bid % kXcds) * (nwg / kXcds) + bid / kXcds;
+  const int per_group = group_m * tiles_n;
   const int group = bid / per_group;
-  const int first_m = group * kGroupM;
-  const int rows = min(tiles_m - first_m, kGroupM);
+  const int first_m = group * group_m;
+  const int rows = min(tiles_m - first_m, group_m);
   const int in_group = bid - group * per_group;
   tm = first_m + in_group % rows;
   tn = in_group / rows;
@@ -158,15 +163,21 @@ struct TileCopy {
     }
   }
 
-  __device__ inline void store(float* slot) {
+  __device__ inline void store_a(float* slot) {
     float* As = slot;
-    float* Bs = slot + C::A_SLOT;
 #pragma unroll
     for (int i = 0; i < C::A_PER_T; ++i)
       *reinterpret_cast<floatx4*>(As + (a_row + i * C::A_ROWS_PER_PASS) * C::AS + a_col) = ra[i];
+  }
+  __device__ inline void store_b(float* slot) {
+    float* Bs = slot + C::A_SLOT;
 #pragma unroll
     for (int i = 0; i < C::B_PER_T; ++i)
       *reinterpret_cast<floatx4*>(Bs + (b_row + i * C::B_ROWS_PER_PASS) * C::BS + b_col) = rb[i];
+  }
+  __device__ inline void store(float* slot) {
+    store_a(slot);
+    store_b(slot);
   }
 };
 
@@ -310,22 +321,27 @@ struct LoopArgs {
 };
 
 template <class C, bool GUARD>
-__device__ inline void load_tile(TileCopy<C>& cp, const LoopArgs<C>& g, int kt) {
+__device__ inline void load_tile_a(TileCopy<C>& cp, const LoopArgs<C>& g, int kt) {
   const int k0 = kt * C::BK;
-  if constexpr (!GUARD) {
+  if (!GUARD || (g.vec_a && k0 + C::BK <= g.K))
     cp.load_a_fast(g.A, g.lda, g.m0, k0);
+  else
+    cp.load_a_guarded(g.A, g.lda, g.M, g.K, g.m0, k0);
+}
+
+template <class C, bool GUARD>
+__device__ inline void load_tile_b(TileCopy<C>& cp, const LoopArgs<C>& g, int kt) {
+  const int k0 = kt * C::BK;
+  if (!GUARD || (g.vec_b && k0 + C::BK <= g.K))
     cp.load_b_fast(g.B, g.ldb, g.n0, k0);
-  } else {
-    const bool k_full = k0 + C::BK <= g.K;
-    if (g.vec_a && k_full)
-      cp.load_a_fast(g.A, g.lda, g.m0, k0);
-    else
-      cp.load_a_guarded(g.A, g.lda, g.M, g.K, g.m0, k0);
-    if (g.vec_b && k_full)
-      cp.load_b_fast(g.B, g.ldb, g.n0, k0);
-    else
-      cp.load_b_guarded(g.B, g.ldb, g.N, g.K, g.n0, k0);
-  }
+  else
+    cp.load_b_guarded(g.B, g.ldb, g.N, g.K, g.n0, k0);
+}
+
+template <class C, bool GUARD>
+__device__ inline void load_tile(TileCopy<C>& cp, const LoopArgs<C>& g, int kt) {
+  load_tile_a<C, GUARD>(cp, g, kt);
+  load_tile_b<C, GUARD>(cp, g, kt);
 }
 
 // Double-buffered: two LDS slots, tile l+1 copied into the idle slot while tile l is
@@ -377,15 +393,28 @@ __device__ inline void k_loop_db(float* smem, TileCopy<C>& cp, const LaneView<C>
 // Single-buffered: one LDS slot; per K tile: copy -> barrier -> multiply -> barrier.
 // The second barrier comes as soon as this wave's last LDS read of the tile has returned
 // (the last round's MFMAs run after it on registers).
-template <class C, bool GUARD>
+// SPLIT = true is the same loop with the A and B copies published by separate barriers,
+// copy A -> barrier -> copy B -> barrier -> multiply -> barrier: three barriers per K tile,
+// the arrangement the LuisaCompute note measured before it coalesced the two copy fences
+// ("Dependence-aware group synchronization on M1 Max", section "Transformation and safety
+// boundary").  It exists to measure what one barrier per K tile costs on this hardware.
+template <class C, bool GUARD, bool SPLIT = false>
 __device__ inline void k_loop_sb(float* smem, TileCopy<C>& cp, const LaneView<C>& lv,
                                  const LoopArgs<C>& g, int k_tiles,
                                  floatx16 (&acc)[C::FM][C::FN]) {
   constexpr int R = C::BK / 8;
   Frag<C> f[2];
   for (int l = 0; l < k_tiles; ++l) {
-    load_tile<C, GUARD>(cp, g, l);
-    cp.store(smem);
+    if constexpr (SPLIT) {
+      load_tile_a<C, GUARD>(cp, g, l);
+      cp.store_a(smem);
+      __syncthreads();  // the A tile is in LDS
+      load_tile_b<C, GUARD>(cp, g, l);
+      cp.store_b(smem);
+    } else {
+      load_tile<C, GUARD>(cp, g, l);
+      cp.store(smem);
+    }
     __syncthreads();  // tile l is in LDS
     read_frag(smem, lv, 0, f[0]);
 #pragma unroll
@@ -403,15 +432,22 @@ __device__ inline void k_loop_sb(float* smem, TileCopy<C>& cp, const LaneView<C>
 }
 
 // ------------------------------------------------------------------------------------
-// The kernel.  DB = true: two LDS slots, one barrier per K tile.  DB = false: one slot,
-// two barriers per K tile.
+// The kernel with register-staged copies.  LOOP (the variant id of the C ABI):
+//   1 single-buffered: one slot, two barriers per K tile
+//   2 double-buffered: two slots, one barrier per K tile
+//   4 single-buffered with split copy barriers: one slot, three barriers per K tile
 // ------------------------------------------------------------------------------------
-template <class C, bool DB>
+enum : int { kLoopSB = 1, kLoopDB = 2, kLoopSB3 = 4 };
+
+template <class C, int LOOP>
 __global__ void __launch_bounds__(C::NT)
 gemm_f32_tile_kernel(int M, int N, int K, const float* __restrict__ A, int64_t lda,
                      const float* __restrict__ B, int64_t ldb, float* __restrict__ Cmat,
                      int64_t ldc, int flags) {
   static_assert((C::BK / 8) % 2 == 0, "BK/8 rounds must be even for the fragment ping-pong");
+  static_assert(LOOP == kLoopSB || LOOP == kLoopDB || LOOP == kLoopSB3, "loop kind");
+  constexpr bool DB = LOOP == kLoopDB;
+  constexpr bool SPLIT = LOOP == kLoopSB3;
   __shared__ __attribute__((aligned(16))) float smem[(DB ? 2 : 1) * C::SLOT];
 
   const int tid = threadIdx.x;
@@ -423,7 +459,7 @@ gemm_f32_tile_kernel(int M, int N, int K, const float* __restrict__ A, int64_t l
   const int tiles_m = (M + C::BM - 1) / C::BM;
   const int tiles_n = (N + C::BN - 1) / C::BN;
   int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  tile_coords(tiles_m, tiles_n, flags, tm, tn);
   LoopArgs<C> g;
   g.A = A;
   g.B = B;
@@ -461,9 +497,9 @@ gemm_f32_tile_kernel(int M, int N, int K, const float* __restrict__ A, int64_t l
         k_loop_db<C, true>(smem, cp, lv, g, k_tiles, acc);
     } else {
       if (unguarded)
-        k_loop_sb<C, false>(smem, cp, lv, g, k_tiles, acc);
+        k_loop_sb<C, false, SPLIT>(smem, cp, lv, g, k_tiles, acc);
       else
-        k_loop_sb<C, true>(smem, cp, lv, g, k_tiles, acc);
+        k_loop_sb<C, true, SPLIT>(smem, cp, lv, g, k_tiles, acc);
     }
   }
 
@@ -711,7 +747,7 @@ gemm_f32_ms_kernel(int M, int N, int K, const float* __restrict__ A, int64_t lda
   const int tiles_m = (M + C::BM - 1) / C::BM;
   const int tiles_n = (N + C::BN - 1) / C::BN;
   int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  tile_coords(tiles_m, tiles_n, flags, tm, tn);
   LoopArgs<C> g;
   g.A = A;
   g.B = B;
@@ -804,7 +840,7 @@ struct CfgEntry {
   int bm, bn, bk, nt;
   int lds_sb, lds_db;
   int ms_stages, lds_ms;
-  KernelFn sb, db, ms;
+  KernelFn sb, db, ms, sb3;
 };
 
 template <class C>
@@ -818,9 +854,10 @@ constexpr CfgEntry make_entry() {
                   (int)(2 * C::SLOT * sizeof(float)),
                   S,
                   (int)(MsCfg<C, S>::LDS_FLOATS * sizeof(float)),
-                  &gemm_f32_tile_kernel<C, false>,
-                  &gemm_f32_tile_kernel<C, true>,
-                  &gemm_f32_ms_kernel<C, S>};
+                  &gemm_f32_tile_kernel<C, kLoopSB>,
+                  &gemm_f32_tile_kernel<C, kLoopDB>,
+                  &gemm_f32_ms_kernel<C, S>,
+                  &gemm_f32_tile_kernel<C, kLoopSB3>};
 }
 
 static const CfgEntry kConfigs[] = {
@@ -869,6 +906,19 @@ static int validate(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda
   return GEMMF32_OK;
 }
 
+// GEMMF32_RASTER=<group_m>[,noxcd] changes the workgroup order of every launch (for
+// measurement); group_m in 1..255.
+static int env_raster_flags() {
+  const char* v = std::getenv("GEMMF32_RASTER");
+  if (v == nullptr || *v == 0) return 0;
+  char* end = nullptr;
+  long gm = std::strtol(v, &end, 10);
+  int flags = 0;
+  if (gm >= 1 && gm <= 255) flags |= (int)gm << kRasterGroupShift;
+  if (end && std::strstr(end, "noxcd")) flags |= kRasterNoXcdRemap;
+  return flags;
+}
+
 static int launch(int variant, int cfg_id, int64_t M, int64_t N, int64_t K, const float* A,
                   int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
                   void* stream) {
@@ -878,9 +928,13 @@ static int launch(int variant, int cfg_id, int64_t M, int64_t N, int64_t K, cons
   int flags = 0;
   if (K > 0 && (((uintptr_t)A) & 15u) == 0 && (lda & 3) == 0) flags |= kVecA;
   if (K > 0 && (((uintptr_t)B) & 15u) == 0 && (ldb & 3) == 0) flags |= kVecB;
+  flags |= env_raster_flags();
   int m = (int)M, n = (int)N, k = (int)K;
   void* args[] = {&m, &n, &k, (void*)&A, &lda, (void*)&B, &ldb, &C, &ldc, &flags};
-  KernelFn fn = variant == GEMMF32_VARIANT_SB ? e.sb : variant == GEMMF32_VARIANT_MS ? e.ms : e.db;
+  KernelFn fn = variant == GEMMF32_VARIANT_SB    ? e.sb
+                : variant == GEMMF32_VARIANT_MS  ? e.ms
+                : variant == GEMMF32_VARIANT_SB3 ? e.sb3
+                                                 : e.db;
   hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)tiles), dim3(e.nt), args, 0,
                                    (hipStream_t)stream);
   if (err != hipSuccess) {
@@ -902,7 +956,8 @@ static int env_variant() {
 static int run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
                int64_t ldb, float* C, int64_t ldc, int variant, int cfg_id, void* stream) {
   if (variant != GEMMF32_VARIANT_AUTO && variant != GEMMF32_VARIANT_SB &&
-      variant != GEMMF32_VARIANT_DB && variant != GEMMF32_VARIANT_MS)
+      variant != GEMMF32_VARIANT_DB && variant != GEMMF32_VARIANT_MS &&
+      variant != GEMMF32_VARIANT_SB3)
     return GEMMF32_ERR_BAD_CONFIG;
   if (cfg_id < -1 || cfg_id >= kNumConfigs) return GEMMF32_ERR_BAD_CONFIG;
   int rc = validate(M, N, K, A, lda, B, ldb, C, ldc);
@@ -914,7 +969,8 @@ static int run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, con
     variant = v;
     if (cfg_id < 0) cfg_id = c;
   } else if (cfg_id < 0) {
-    cfg_id = select_for_variant(M, N, K, variant);
+    cfg_id = select_for_variant(M, N, K, variant == GEMMF32_VARIANT_SB3 ? GEMMF32_VARIANT_SB
+                                                                        : variant);
   }
   return launch(variant, cfg_id, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }

@@ -166,6 +166,138 @@ def measure(shapes, rounds=2, batches=5, batch_ms=20.0, log=print):
     return results
 
 
+def time_calls(calls, rounds=2, batches=5, batch_ms=20.0):
+    """Median-of-round-medians microseconds per launch for each named callable, with the
+    visiting order rotated (and reversed on odd rounds) from round to round."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    names = list(calls)
+    reps = {}
+    for n in names:
+        calls[n]()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            calls[n]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        reps[n] = int(min(20000, max(2, batch_ms / max(e0.elapsed_time(e1) / 3, 1e-4))))
+    per_round = {n: [] for n in names}
+    for r in range(rounds):
+        shift = (r * len(names)) // max(rounds, 1)
+        order = names[shift:] + names[:shift]
+        if r % 2:
+            order = order[::-1]
+        for n in order:
+            for _ in range(2):
+                calls[n]()
+            ts = []
+            for _ in range(batches):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps[n]):
+                    calls[n]()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3 / reps[n])
+            per_round[n].append(statistics.median(ts))
+    return {n: statistics.median(v) for n, v in per_round.items()}
+
+
+def _operands(M, N, K, seed=99):
+    import torch
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    A = torch.rand((M, K), device=dev, generator=gen) * 2 - 1
+    B = torch.rand((K, N), device=dev, generator=gen) * 2 - 1
+    C = torch.empty((M, N), device=dev)
+    return A, B, C
+
+
+def _caller(M, N, K, A, B, C, variant, cfg):
+    import torch
+
+    s_ptr = torch.cuda.current_stream().cuda_stream
+    pa, pb, pc = A.data_ptr(), B.data_ptr(), C.data_ptr()
+
+    def call():
+        rc = tdb.gemm_f32_ex(M, N, K, pa, K, pb, N, pc, N, variant, cfg, s_ptr)
+        if rc != tdb.OK:
+            raise tdb.GemmError(rc, "gemm_f32_ex")
+    return call
+
+
+BARRIER_SHAPES = [(1024, 1024, 1024), (2048, 2048, 2048), (4096, 4096, 4096),
+                  (8192, 8192, 8192), (513, 257, 129)]
+
+
+def barrier_study(shapes=BARRIER_SHAPES, rounds=2, batches=5, batch_ms=20.0, log=print):
+    """Single-buffered with 3 barriers per K tile (copy A | copy B | multiply), with 2
+    (copies coalesced) and double-buffered with 1, all at the same tile configuration
+    (the single- and the double-buffered column of the table for the shape)."""
+    out = []
+    for (M, N, K) in shapes:
+        A, B, C = _operands(M, N, K)
+        cfgs = sorted({tdb.gemm_f32_select_cfg(M, N, K, tdb.VARIANT_SB),
+                       tdb.gemm_f32_select_cfg(M, N, K, tdb.VARIANT_DB)})
+        for cfg in cfgs:
+            _, info = tdb.gemm_f32_config_info(cfg)
+            calls = {n: _caller(M, N, K, A, B, C, v, cfg)
+                     for n, v in (("sb3", tdb.VARIANT_SB3), ("sb", tdb.VARIANT_SB),
+                                  ("db", tdb.VARIANT_DB))}
+            us = time_calls(calls, rounds, batches, batch_ms)
+            k_tiles = -(-K // info["BK"])
+            row = {"M": M, "N": N, "K": K, "cfg": cfg,
+                   "tile": f"{info['BM']}x{info['BN']}x{info['BK']}", "k_tiles": k_tiles,
+                   "us": us,
+                   "barriers": {"sb3": 3 * k_tiles, "sb": 2 * k_tiles, "db": k_tiles},
+                   "us_per_removed_barrier_sb3_to_sb": (us["sb3"] - us["sb"]) / k_tiles,
+                   "sb_over_db": us["sb"] / us["db"]}
+            out.append(row)
+            log(f"{M}x{N}x{K} cfg{cfg} {row['tile']}: sb3 {us['sb3']:.2f} us, "
+                f"sb {us['sb']:.2f} us, db {us['db']:.2f} us; "
+                f"{row['us_per_removed_barrier_sb3_to_sb'] * 1e3:.1f} ns per removed barrier")
+        del A, B, C
+    return out
+
+
+RASTER_SHAPES = [(4096, 4096, 4096), (8192, 8192, 8192), (6144, 6144, 6144)]
+RASTER_SETTINGS = ["", "1", "2", "3", "4", "16", "32", "8,noxcd", "1,noxcd"]
+
+
+def raster_study(shapes=RASTER_SHAPES, settings=RASTER_SETTINGS, rounds=2, batches=5,
+                 batch_ms=20.0, log=print):
+    """The dispatched kernel of each shape under different workgroup orders
+    (GEMMF32_RASTER; "" is the built-in default: group 8 with XCD renumbering)."""
+    out = []
+    for (M, N, K) in shapes:
+        A, B, C = _operands(M, N, K)
+        _, v, cfg = tdb.gemm_f32_select(M, N, K)
+        base = _caller(M, N, K, A, B, C, v, cfg)
+
+        def with_raster(setting):
+            def call():
+                os.environ["GEMMF32_RASTER"] = setting
+                base()
+            return call
+        calls = {st or "default": with_raster(st) for st in settings}
+        try:
+            us = time_calls(calls, rounds, batches, batch_ms)
+        finally:
+            os.environ.pop("GEMMF32_RASTER", None)
+        out.append({"M": M, "N": N, "K": K, "variant": v, "cfg": cfg, "us": us})
+        best = min(us, key=us.get)
+        log(f"{M}x{N}x{K} v{v} cfg{cfg}: " + ", ".join(f"{k} {t:.1f}" for k, t in us.items())
+            + f" -> best {best}")
+        del A, B, C
+    return out
+
+
 def table_rows(results):
     rows = []
     for r in results:
@@ -206,7 +338,30 @@ def main(argv=None) -> int:
     ap.add_argument("--rounds", type=int, default=2)
     ap.add_argument("--batches", type=int, default=5)
     ap.add_argument("--batch-ms", type=float, default=20.0)
+    ap.add_argument("--barrier-study", action="store_true",
+                    help="time 3-, 2- and 1-barrier loops at equal tile configurations")
+    ap.add_argument("--raster-study", action="store_true",
+                    help="time the dispatched kernels under different workgroup orders")
     args = ap.parse_args(argv)
+    if args.barrier_study or args.raster_study:
+        import torch
+
+        props = torch.cuda.get_device_properties(0)
+        res = {"device": f"{props.name} ({getattr(props, 'gcnArchName', '?')})",
+               "library": tdb.gemm_f32_version(), "rounds": args.rounds,
+               "batches": args.batches, "batch_ms": args.batch_ms}
+        if args.barrier_study:
+            res["barrier_study"] = barrier_study(rounds=args.rounds, batches=args.batches,
+                                                 batch_ms=args.batch_ms,
+                                                 log=lambda *a: print(*a, flush=True))
+        if args.raster_study:
+            res["raster_study"] = raster_study(rounds=args.rounds, batches=args.batches,
+                                               batch_ms=args.batch_ms,
+                                               log=lambda *a: print(*a, flush=True))
+        if args.out:
+            with open(args.out, "w") as f:
+                json.dump(res, f, indent=1)
+        return 0
     if args.from_json:
         with open(args.from_json) as f:
             data = json.load(f)
