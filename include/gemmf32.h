@@ -121,6 +121,29 @@ int gemm_f32_ex(int64_t M, int64_t N, int64_t K,
                 int variant, int cfg_id,
                 void *stream);
 
+/* C = A.B with the K range split into `splits` chunks (whole multiples of 64, so at most
+ * `splits` are used; 1 .. 64) for shapes whose M x N tiles cannot fill the GPU, such as
+ * the skinny decode-like regime the case study mentions ("Case Study: The Double-Buffered
+ * GEMM", paragraph on the three regimes).  Each chunk's partial product goes into the
+ * caller's `workspace` (device memory, >= gemm_f32_splitk_workspace(M, N, K, splits)
+ * floats, 4-byte aligned, overlapping none of A, B, C); a second kernel then sums the
+ * partials into C in a fixed order, so the result is deterministic (it differs in
+ * rounding, within the accuracy of one product, from the unsplit one).  The workspace is
+ * owned by the caller and overwritten; it may be NULL when fewer than two chunks result.
+ * Both kernels go on `stream`.  Errors as for gemm_f32, plus GEMMF32_ERR_BAD_CONFIG for
+ * `splits` outside 1 .. 64, GEMMF32_ERR_BAD_LD for a workspace that is too small,
+ * GEMMF32_ERR_NULL_PTR / _MISALIGNED / _ALIAS for a bad workspace pointer. */
+int gemm_f32_splitk(int64_t M, int64_t N, int64_t K,
+                    const float *A, int64_t lda,
+                    const float *B, int64_t ldb,
+                    float *C, int64_t ldc,
+                    int splits, float *workspace, int64_t workspace_floats,
+                    void *stream);
+
+/* Workspace floats gemm_f32_splitk needs for this shape and split count (0 when it will
+ * not split), or a negative error code. */
+int64_t gemm_f32_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits);
+
 /* The dispatch decision for a shape, without launching: *variant receives
  * GEMMF32_VARIANT_SB, _DB or _MS and *cfg_id the tile configuration id.  Either output pointer
  * may be NULL.  Pure host code (no GPU needed).  Returns GEMMF32_ERR_NEGATIVE_DIM for

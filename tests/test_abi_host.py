@@ -172,3 +172,32 @@ def test_tensor_wrapper_rejects_host_tensors():
         tdb.matmul(a, a)
     with pytest.raises(TypeError):
         tdb.matmul(a.double(), a.double())
+
+
+def test_splitk_workspace_sizes():
+    ws = tdb.gemm_f32_splitk_workspace
+    assert ws(64, 4096, 4096, 4) == 4 * 64 * 4096      # 4 chunks of 1024
+    assert ws(64, 4096, 4096, 3) == 3 * 64 * 4096      # chunks of 1408 (a multiple of 64)
+    assert ws(10, 20, 100, 4) == 2 * 10 * 20            # chunks of 64: only 2 used
+    assert ws(10, 20, 64, 4) == 0                       # one chunk: no split, no workspace
+    assert ws(10, 20, 0, 4) == 0 and ws(0, 20, 100, 4) == 0
+    assert ws(10, 20, 100, 0) == tdb.ERR_BAD_CONFIG
+    assert ws(10, 20, 100, 65) == tdb.ERR_BAD_CONFIG
+    assert ws(-1, 20, 100, 2) == tdb.ERR_NEGATIVE_DIM
+
+
+def test_splitk_validation_before_launch():
+    """Every call here fails validation (so nothing launches on the fake pointers)."""
+    f = tdb.gemm_f32_splitk
+    M, N, K = 64, 256, 4096
+    need = tdb.gemm_f32_splitk_workspace(M, N, K, 4)
+    PW = 0x7F3000000000
+    assert f(M, N, K, PA, K, PB, N, PC, N, 0, PW, need) == tdb.ERR_BAD_CONFIG
+    assert f(M, N, K, PA, K, PB, N, PC, N, 65, PW, need) == tdb.ERR_BAD_CONFIG
+    assert f(M, N, K, PA, K, PB, N, PC, N, 4, 0, need) == tdb.ERR_NULL_PTR
+    assert f(M, N, K, PA, K, PB, N, PC, N, 4, PW + 2, need) == tdb.ERR_MISALIGNED
+    assert f(M, N, K, PA, K, PB, N, PC, N, 4, PW, need - 1) == tdb.ERR_BAD_LD
+    assert f(M, N, K, PA, K, PB, N, PC, N, 4, PA + 64, need) == tdb.ERR_ALIAS   # overlaps A
+    assert f(M, N, K, PA, K, PB, N, PC, N, 4, PC - 4 * 100, need) == tdb.ERR_ALIAS  # C
+    assert f(M, N, K, PA, K - 1, PB, N, PC, N, 4, PW, need) == tdb.ERR_BAD_LD   # lda < K
+    assert f(0, N, K, 0, K, 0, N, 0, N, 4, 0, 0) == tdb.OK                    # empty: no-op

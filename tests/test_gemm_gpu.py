@@ -249,3 +249,46 @@ def test_square_8192_sampled():
         assert r <= 1.0, v
         assert torch.isfinite(C).all()
         del C
+
+
+@pytest.mark.parametrize("shape,splits", [((16, 4096, 4096), 4), ((64, 2048, 8192), 8),
+                                          ((33, 257, 1000), 3), ((300, 200, 777), 2),
+                                          ((128, 128, 4096), 16), ((7, 9, 130), 5)])
+def test_splitk_parity(shape, splits):
+    """Split-K: each K chunk's partial product in the workspace, a fixed-order sum into C.
+    Within the bound; deterministic; the workspace size the library asks for suffices."""
+    M, N, K = shape
+    _say(f"[splitk] {M}x{N}x{K} splits={splits}")
+    A, B = ti.workload_inputs(M, N, K, 8000 + M + K)
+    C64, Bnd = oracle.gemm_f64(A, B)
+    Ad, Bd = _dev(A), _dev(B)
+    need = tdb.gemm_f32_splitk_workspace(M, N, K, splits)
+    ws = torch.full((max(need, 1),), float("nan"), device=DEV)
+    C = torch.full((M, N), float("nan"), device=DEV)
+    tdb.matmul_splitk(Ad, Bd, splits, out=C, workspace=ws)
+    torch.cuda.synchronize()
+    r = _ratio(C, C64, Bnd)
+    _say(f"[splitk] ratio={r:.3g}")
+    assert r <= 1.0
+    C2 = tdb.matmul_splitk(Ad, Bd, splits, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(C, C2), "split-K is not deterministic"
+
+
+def test_splitk_one_split_equals_plain_and_errors():
+    A, B, C64, Bnd = _workload("square_128")
+    Ad, Bd = _dev(A), _dev(B)
+    C1 = tdb.matmul_splitk(Ad, Bd, 1)
+    C0 = _run(Ad, Bd)
+    assert torch.equal(C1, C0)
+    # too small a workspace is rejected before anything is launched
+    M, N, K = 64, 512, 4096
+    Ad = torch.ones((M, K), device=DEV)
+    Bd = torch.ones((K, N), device=DEV)
+    need = tdb.gemm_f32_splitk_workspace(M, N, K, 4)
+    with pytest.raises(tdb.GemmError) as e:
+        tdb.matmul_splitk(Ad, Bd, 4, workspace=torch.empty(need - 1, device=DEV))
+    assert e.value.code == tdb.ERR_BAD_LD
+    C = tdb.matmul_splitk(Ad, Bd, 4)
+    torch.cuda.synchronize()
+    assert torch.all(C == float(K))

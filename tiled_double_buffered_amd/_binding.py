@@ -39,6 +39,8 @@ SIGNATURES = {
     "gemm_f32_db": (_int, _GEMM_ARGS + [_vp]),
     "gemm_f32_ms": (_int, _GEMM_ARGS + [_vp]),
     "gemm_f32_ex": (_int, _GEMM_ARGS + [_int, _int, _vp]),
+    "gemm_f32_splitk": (_int, _GEMM_ARGS + [_int, _vp, _i64, _vp]),
+    "gemm_f32_splitk_workspace": (_i64, [_i64, _i64, _i64, _int]),
     "gemm_f32_select": (_int, [_i64, _i64, _i64, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
     "gemm_f32_select_cfg": (_int, [_i64, _i64, _i64, _int]),
     "gemm_f32_num_configs": (_int, []),
@@ -97,6 +99,16 @@ def gemm_f32_ms(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
 
 def gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, variant, cfg_id, stream=None) -> int:
     return load().gemm_f32_ex(M, N, K, A, lda, B, ldb, C, ldc, variant, cfg_id, stream)
+
+
+def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, splits, workspace, workspace_floats,
+                    stream=None) -> int:
+    return load().gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, splits, workspace,
+                                  workspace_floats, stream)
+
+
+def gemm_f32_splitk_workspace(M, N, K, splits) -> int:
+    return load().gemm_f32_splitk_workspace(M, N, K, splits)
 
 
 def gemm_f32_select(M, N, K):
@@ -182,4 +194,36 @@ def matmul(A, B, out=None, variant: str = "auto", cfg_id: int = -1, stream=None)
     rc = gemm_f32_ex(M, N, K, pa, lda, pb, ldb, pc, ldc, _VARIANTS[variant], cfg_id, s)
     if rc != OK:
         raise GemmError(rc, "gemm_f32")
+    return out
+
+
+def matmul_splitk(A, B, splits, out=None, workspace=None, stream=None):
+    """out = A @ B through gemm_f32_splitk.  `workspace` is a float32 GPU tensor of at least
+    gemm_f32_splitk_workspace(M, N, K, splits) elements; when None, one is allocated here
+    with torch (the library itself never allocates)."""
+    import torch
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {tuple(A.shape)} @ {tuple(B.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    elif tuple(out.shape) != (M, N):
+        raise ValueError("out has the wrong shape")
+    need = gemm_f32_splitk_workspace(M, N, K, splits)
+    if need < 0:
+        raise GemmError(int(need), "gemm_f32_splitk_workspace")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.float32, device=A.device)
+    if workspace.dtype != torch.float32 or not workspace.is_cuda or \
+            not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous float32 GPU tensor")
+    pa, lda = _operand(A, "A")
+    pb, ldb = _operand(B, "B")
+    pc, ldc = _operand(out, "out")
+    s = (stream if stream is not None else torch.cuda.current_stream(A.device)).cuda_stream
+    rc = gemm_f32_splitk(M, N, K, pa, lda, pb, ldb, pc, ldc, splits, workspace.data_ptr(),
+                         workspace.numel(), s)
+    if rc != OK:
+        raise GemmError(rc, "gemm_f32_splitk")
     return out

@@ -443,7 +443,16 @@ template <class C, int LOOP>
 __global__ void __launch_bounds__(C::NT)
 gemm_f32_tile_kernel(int M, int N, int K, const float* __restrict__ A, int64_t lda,
                      const float* __restrict__ B, int64_t ldb, float* __restrict__ Cmat,
-                     int64_t ldc, int flags) {
+                     int64_t ldc, int flags, int k_chunk, int64_t c_split_stride) {
+  // Split-K: workgroup row y of the grid multiplies K range [y*k_chunk, y*k_chunk + k_chunk)
+  // into its own M x N partial product at Cmat + y*c_split_stride.
+  if (gridDim.y > 1) {
+    const int kb = blockIdx.y * k_chunk;
+    K = min(K - kb, k_chunk);
+    A += kb;
+    B += (int64_t)kb * ldb;
+    Cmat += (int64_t)blockIdx.y * c_split_stride;
+  }
   static_assert((C::BK / 8) % 2 == 0, "BK/8 rounds must be even for the fragment ping-pong");
   static_assert(LOOP == kLoopSB || LOOP == kLoopDB || LOOP == kLoopSB3, "loop kind");
   constexpr bool DB = LOOP == kLoopDB;
@@ -735,7 +744,16 @@ template <class C, int S>
 __global__ void __launch_bounds__(C::NT)
 gemm_f32_ms_kernel(int M, int N, int K, const float* __restrict__ A, int64_t lda,
                    const float* __restrict__ B, int64_t ldb, float* __restrict__ Cmat,
-                   int64_t ldc, int flags) {
+                   int64_t ldc, int flags, int k_chunk, int64_t c_split_stride) {
+  // Split-K: workgroup row y of the grid multiplies K range [y*k_chunk, y*k_chunk + k_chunk)
+  // into its own M x N partial product at Cmat + y*c_split_stride.
+  if (gridDim.y > 1) {
+    const int kb = blockIdx.y * k_chunk;
+    K = min(K - kb, k_chunk);
+    A += kb;
+    B += (int64_t)kb * ldb;
+    Cmat += (int64_t)blockIdx.y * c_split_stride;
+  }
   using MC = MsCfg<C, S>;
   __shared__ __attribute__((aligned(1024))) float smem[MC::LDS_FLOATS];
 
@@ -822,6 +840,41 @@ constexpr int ms_stages() {
 }
 
 // ------------------------------------------------------------------------------------
+// Split-K reduction: C[i][j] = P[0][i][j] + P[1][i][j] + ... + P[S-1][i][j], summed in
+// that fixed order, so a split product is deterministic.  P holds S partial products of
+// M x N floats each, rows of N.  A streaming kernel bounded by HBM bandwidth:
+// (S + 1) * 4 * M * N bytes per launch.  VEC: rows of P and C are 16-byte aligned and
+// N % 4 == 0, so each thread moves 4 consecutive columns.
+// ------------------------------------------------------------------------------------
+template <bool VEC>
+__global__ void __launch_bounds__(256)
+gemm_f32_splitk_reduce(int M, int N, int S, const float* __restrict__ P,
+                       float* __restrict__ C, int64_t ldc) {
+  const int64_t mn = (int64_t)M * N;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  if constexpr (VEC) {
+    const int n4 = N / 4;
+    const int64_t total = (int64_t)M * n4;
+    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += stride) {
+      const int64_t i = t / n4;
+      const int64_t j = 4 * (t - i * n4);
+      const int64_t e = i * N + j;
+      floatx4 acc = *reinterpret_cast<const floatx4*>(P + e);
+      for (int sp = 1; sp < S; ++sp) acc += *reinterpret_cast<const floatx4*>(P + sp * mn + e);
+      *reinterpret_cast<floatx4*>(C + i * ldc + j) = acc;
+    }
+  } else {
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < mn; e += stride) {
+      const int64_t i = e / N;
+      const int64_t j = e - i * N;
+      float acc = P[e];
+      for (int sp = 1; sp < S; ++sp) acc += P[sp * mn + e];
+      C[i * ldc + j] = acc;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // Configuration table.  Ids are part of the ABI (gemm_f32_ex, gemm_f32_config_info).
 // ------------------------------------------------------------------------------------
 using Cfg0 = TileCfg<256, 256, 16, 2, 2>;  // wave 128x128 (16 blocks)
@@ -832,9 +885,12 @@ using Cfg4 = TileCfg<128, 128, 32, 2, 2>;  // wave 64x64, deeper K tile
 using Cfg5 = TileCfg<128, 64, 32, 2, 2>;   // wave 64x32
 using Cfg6 = TileCfg<64, 64, 32, 2, 2>;    // wave 32x32
 using Cfg7 = TileCfg<64, 64, 64, 2, 2>;    // wave 32x32, deeper K tile
+using Cfg8 = TileCfg<256, 256, 32, 2, 4>;  // 8 waves of 128x64: two waves per SIMD
+using Cfg9 = TileCfg<128, 256, 32, 2, 4>;  // 8 waves of 64x64
+using Cfg10 = TileCfg<32, 128, 32, 1, 4>;  // 4 waves of 32x32 side by side: skinny M
 
 typedef void (*KernelFn)(int, int, int, const float*, int64_t, const float*, int64_t, float*,
-                         int64_t, int);
+                         int64_t, int, int, int64_t);
 
 struct CfgEntry {
   int bm, bn, bk, nt;
@@ -863,6 +919,7 @@ constexpr CfgEntry make_entry() {
 static const CfgEntry kConfigs[] = {
     make_entry<Cfg0>(), make_entry<Cfg1>(), make_entry<Cfg2>(), make_entry<Cfg3>(),
     make_entry<Cfg4>(), make_entry<Cfg5>(), make_entry<Cfg6>(), make_entry<Cfg7>(),
+    make_entry<Cfg8>(), make_entry<Cfg9>(), make_entry<Cfg10>(),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -919,9 +976,11 @@ static int env_raster_flags() {
   return flags;
 }
 
+// One launch of a GEMM kernel.  splits > 1: grid rows y = 0..splits-1 each multiply the
+// K range [y*k_chunk, ...) into C + y*c_split_stride (the split-K partial products).
 static int launch(int variant, int cfg_id, int64_t M, int64_t N, int64_t K, const float* A,
                   int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
-                  void* stream) {
+                  void* stream, int splits = 1, int k_chunk = 0, int64_t c_split_stride = 0) {
   const CfgEntry& e = kConfigs[cfg_id];
   const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
   if (tiles * e.nt > 0xFFFFFFFFLL) return GEMMF32_ERR_TOO_LARGE;
@@ -930,13 +989,15 @@ static int launch(int variant, int cfg_id, int64_t M, int64_t N, int64_t K, cons
   if (K > 0 && (((uintptr_t)B) & 15u) == 0 && (ldb & 3) == 0) flags |= kVecB;
   flags |= env_raster_flags();
   int m = (int)M, n = (int)N, k = (int)K;
-  void* args[] = {&m, &n, &k, (void*)&A, &lda, (void*)&B, &ldb, &C, &ldc, &flags};
+  int kc = splits > 1 ? k_chunk : k;
+  void* args[] = {&m,   &n,     &k,  (void*)&A, &lda, (void*)&B,
+                  &ldb, &C,     &ldc, &flags,   &kc,  &c_split_stride};
   KernelFn fn = variant == GEMMF32_VARIANT_SB    ? e.sb
                 : variant == GEMMF32_VARIANT_MS  ? e.ms
                 : variant == GEMMF32_VARIANT_SB3 ? e.sb3
                                                  : e.db;
-  hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)tiles), dim3(e.nt), args, 0,
-                                   (hipStream_t)stream);
+  hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)tiles, (unsigned)splits),
+                                   dim3(e.nt), args, 0, (hipStream_t)stream);
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
     return GEMMF32_ERR_HIP;
@@ -975,6 +1036,62 @@ static int run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, con
   return launch(variant, cfg_id, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
+constexpr int kMaxSplits = 64;
+constexpr int kSplitGranule = 64;  // K chunks are whole K tiles of every configuration
+
+// K chunk of one split and the number of splits actually used.
+static void splitk_plan(int64_t K, int splits, int64_t* k_chunk, int* used) {
+  int64_t kc = (K + splits - 1) / splits;
+  kc = (kc + kSplitGranule - 1) / kSplitGranule * kSplitGranule;
+  if (kc < kSplitGranule) kc = kSplitGranule;
+  *k_chunk = kc;
+  *used = (int)((K + kc - 1) / kc);
+}
+
+static int run_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                      const float* B, int64_t ldb, float* C, int64_t ldc, int splits,
+                      float* ws, int64_t ws_floats, void* stream) {
+  if (splits < 1 || splits > kMaxSplits) return GEMMF32_ERR_BAD_CONFIG;
+  int rc = validate(M, N, K, A, lda, B, ldb, C, ldc);
+  if (rc != GEMMF32_OK) return rc;
+  if (M == 0 || N == 0) return GEMMF32_OK;
+  int64_t kc = 0;
+  int used = 1;
+  if (K > 0) splitk_plan(K, splits, &kc, &used);
+  if (used <= 1) return run(M, N, K, A, lda, B, ldb, C, ldc, GEMMF32_VARIANT_AUTO, -1, stream);
+  const int64_t need = (int64_t)used * M * N;
+  if (ws == nullptr) return GEMMF32_ERR_NULL_PTR;
+  if (((uintptr_t)ws & 3u) != 0) return GEMMF32_ERR_MISALIGNED;
+  if (ws_floats < need) return GEMMF32_ERR_BAD_LD;
+  // The workspace must not overlap A, B or C.
+  const uintptr_t w0 = (uintptr_t)ws, w1 = w0 + (uintptr_t)(need * 4);
+  const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)(((M - 1) * lda + K) * 4);
+  const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)(((K - 1) * ldb + N) * 4);
+  const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)(((M - 1) * ldc + N) * 4);
+  if ((w0 < a1 && a0 < w1) || (w0 < b1 && b0 < w1) || (w0 < c1 && c0 < w1))
+    return GEMMF32_ERR_ALIAS;
+  int v = 0, cfg = 0;
+  select_shape(M, N, kc, &v, &cfg);
+  rc = launch(v, cfg, M, N, K, A, lda, B, ldb, ws, N, stream, used, (int)kc, M * N);
+  if (rc != GEMMF32_OK) return rc;
+  const bool vec = (N % 4) == 0 && (ldc % 4) == 0 && ((uintptr_t)ws & 15u) == 0 &&
+                   ((uintptr_t)C & 15u) == 0;
+  const int64_t items = vec ? M * (N / 4) : M * N;
+  const int64_t blocks64 = (items + 255) / 256;
+  const unsigned blocks = (unsigned)(blocks64 < 4096 ? blocks64 : 4096);
+  int m = (int)M, n = (int)N;
+  const float* p = ws;
+  void* args[] = {&m, &n, &used, (void*)&p, &C, &ldc};
+  const void* fn = vec ? (const void*)&gemm_f32_splitk_reduce<true>
+                       : (const void*)&gemm_f32_splitk_reduce<false>;
+  hipError_t err = hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, (hipStream_t)stream);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return GEMMF32_ERR_HIP;
+  }
+  return GEMMF32_OK;
+}
+
 }  // namespace gemmf32
 
 using namespace gemmf32;
@@ -1004,6 +1121,23 @@ int gemm_f32_ms(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, co
 int gemm_f32_ex(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
                 int64_t ldb, float* C, int64_t ldc, int variant, int cfg_id, void* stream) {
   return run(M, N, K, A, lda, B, ldb, C, ldc, variant, cfg_id, stream);
+}
+
+int gemm_f32_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                    const float* B, int64_t ldb, float* C, int64_t ldc, int splits,
+                    float* workspace, int64_t workspace_floats, void* stream) {
+  return run_splitk(M, N, K, A, lda, B, ldb, C, ldc, splits, workspace, workspace_floats,
+                    stream);
+}
+
+int64_t gemm_f32_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits) {
+  if (M < 0 || N < 0 || K < 0) return GEMMF32_ERR_NEGATIVE_DIM;
+  if (splits < 1 || splits > kMaxSplits) return GEMMF32_ERR_BAD_CONFIG;
+  if (M == 0 || N == 0 || K == 0) return 0;
+  int64_t kc = 0;
+  int used = 1;
+  splitk_plan(K, splits, &kc, &used);
+  return used <= 1 ? 0 : (int64_t)used * M * N;
 }
 
 int gemm_f32_select(int64_t M, int64_t N, int64_t K, int* variant, int* cfg_id) {
