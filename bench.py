@@ -146,7 +146,7 @@ def write_traffic(fetch_dir: str, write_dir: str, calib_mib: int = 512) -> int:
     if variant == tdb.VARIANT_MS:
         kname, flag = "gemm_f32_ms_kernel", ">, %d>" % tdb.gemm_f32_config_ms(cfg)[1]["stages"]
     else:
-        kname, flag = "gemm_f32_tile_kernel", ", true>" if variant == tdb.VARIANT_DB else ", false>"
+        kname, flag = "gemm_f32_tile_kernel", ", %d>" % variant  # loop kind = variant id
 
     def is_gemm(name, g):
         return kname in name and tag in name and flag in name and g == grid

@@ -130,9 +130,10 @@ int gemm_f32_ex(int64_t M, int64_t N, int64_t K,
  * partials into C in a fixed order, so the result is deterministic (it differs in
  * rounding, within the accuracy of one product, from the unsplit one).  The workspace is
  * owned by the caller and overwritten; it may be NULL when fewer than two chunks result.
- * Both kernels go on `stream`.  Errors as for gemm_f32, plus GEMMF32_ERR_BAD_CONFIG for
- * `splits` outside 1 .. 64, GEMMF32_ERR_BAD_LD for a workspace that is too small,
- * GEMMF32_ERR_NULL_PTR / _MISALIGNED / _ALIAS for a bad workspace pointer. */
+ * `splits` = 0 takes the measured choice of gemm_f32_splitk_select.  Both kernels go on
+ * `stream`.  Errors as for gemm_f32, plus GEMMF32_ERR_BAD_CONFIG for `splits` outside
+ * 0 .. 64, GEMMF32_ERR_BAD_LD for a workspace that is too small, GEMMF32_ERR_NULL_PTR /
+ * _MISALIGNED / _ALIAS for a bad workspace pointer. */
 int gemm_f32_splitk(int64_t M, int64_t N, int64_t K,
                     const float *A, int64_t lda,
                     const float *B, int64_t ldb,
@@ -140,9 +141,13 @@ int gemm_f32_splitk(int64_t M, int64_t N, int64_t K,
                     int splits, float *workspace, int64_t workspace_floats,
                     void *stream);
 
-/* Workspace floats gemm_f32_splitk needs for this shape and split count (0 when it will
- * not split), or a negative error code. */
+/* Workspace floats gemm_f32_splitk needs for this shape and split count (0 = the measured
+ * choice; the result is 0 when it will not split), or a negative error code. */
 int64_t gemm_f32_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits);
+
+/* The measured best split count for a shape (1 = do not split), from the split table of
+ * the dispatch table; host code only.  Negative sizes give GEMMF32_ERR_NEGATIVE_DIM. */
+int gemm_f32_splitk_select(int64_t M, int64_t N, int64_t K);
 
 /* The dispatch decision for a shape, without launching: *variant receives
  * GEMMF32_VARIANT_SB, _DB or _MS and *cfg_id the tile configuration id.  Either output pointer

@@ -181,9 +181,14 @@ def test_splitk_workspace_sizes():
     assert ws(10, 20, 100, 4) == 2 * 10 * 20            # chunks of 64: only 2 used
     assert ws(10, 20, 64, 4) == 0                       # one chunk: no split, no workspace
     assert ws(10, 20, 0, 4) == 0 and ws(0, 20, 100, 4) == 0
-    assert ws(10, 20, 100, 0) == tdb.ERR_BAD_CONFIG
+    assert ws(10, 20, 100, -1) == tdb.ERR_BAD_CONFIG
     assert ws(10, 20, 100, 65) == tdb.ERR_BAD_CONFIG
     assert ws(-1, 20, 100, 2) == tdb.ERR_NEGATIVE_DIM
+    for shape in [(16, 4096, 4096), (4096, 4096, 4096), (1, 1, 1)]:
+        sp = tdb.gemm_f32_splitk_select(*shape)
+        assert 1 <= sp <= 64
+        assert ws(*shape, 0) == ws(*shape, sp)
+    assert tdb.gemm_f32_splitk_select(-1, 2, 3) == tdb.ERR_NEGATIVE_DIM
 
 
 def test_splitk_validation_before_launch():
@@ -192,7 +197,7 @@ def test_splitk_validation_before_launch():
     M, N, K = 64, 256, 4096
     need = tdb.gemm_f32_splitk_workspace(M, N, K, 4)
     PW = 0x7F3000000000
-    assert f(M, N, K, PA, K, PB, N, PC, N, 0, PW, need) == tdb.ERR_BAD_CONFIG
+    assert f(M, N, K, PA, K, PB, N, PC, N, -1, PW, need) == tdb.ERR_BAD_CONFIG
     assert f(M, N, K, PA, K, PB, N, PC, N, 65, PW, need) == tdb.ERR_BAD_CONFIG
     assert f(M, N, K, PA, K, PB, N, PC, N, 4, 0, need) == tdb.ERR_NULL_PTR
     assert f(M, N, K, PA, K, PB, N, PC, N, 4, PW + 2, need) == tdb.ERR_MISALIGNED

@@ -41,6 +41,7 @@ SIGNATURES = {
     "gemm_f32_ex": (_int, _GEMM_ARGS + [_int, _int, _vp]),
     "gemm_f32_splitk": (_int, _GEMM_ARGS + [_int, _vp, _i64, _vp]),
     "gemm_f32_splitk_workspace": (_i64, [_i64, _i64, _i64, _int]),
+    "gemm_f32_splitk_select": (_int, [_i64, _i64, _i64]),
     "gemm_f32_select": (_int, [_i64, _i64, _i64, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
     "gemm_f32_select_cfg": (_int, [_i64, _i64, _i64, _int]),
     "gemm_f32_num_configs": (_int, []),
@@ -109,6 +110,10 @@ def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, splits, workspace, workspac
 
 def gemm_f32_splitk_workspace(M, N, K, splits) -> int:
     return load().gemm_f32_splitk_workspace(M, N, K, splits)
+
+
+def gemm_f32_splitk_select(M, N, K) -> int:
+    return load().gemm_f32_splitk_select(M, N, K)
 
 
 def gemm_f32_select(M, N, K):
@@ -197,7 +202,7 @@ def matmul(A, B, out=None, variant: str = "auto", cfg_id: int = -1, stream=None)
     return out
 
 
-def matmul_splitk(A, B, splits, out=None, workspace=None, stream=None):
+def matmul_splitk(A, B, splits=0, out=None, workspace=None, stream=None):
     """out = A @ B through gemm_f32_splitk.  `workspace` is a float32 GPU tensor of at least
     gemm_f32_splitk_workspace(M, N, K, splits) elements; when None, one is allocated here
     with torch (the library itself never allocates)."""

@@ -1051,6 +1051,7 @@ static void splitk_plan(int64_t K, int splits, int64_t* k_chunk, int* used) {
 static int run_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                       const float* B, int64_t ldb, float* C, int64_t ldc, int splits,
                       float* ws, int64_t ws_floats, void* stream) {
+  if (splits == 0 && M >= 0 && N >= 0 && K >= 0) splits = select_splits(M, N, K);
   if (splits < 1 || splits > kMaxSplits) return GEMMF32_ERR_BAD_CONFIG;
   int rc = validate(M, N, K, A, lda, B, ldb, C, ldc);
   if (rc != GEMMF32_OK) return rc;
@@ -1130,8 +1131,14 @@ int gemm_f32_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda
                     stream);
 }
 
+int gemm_f32_splitk_select(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return GEMMF32_ERR_NEGATIVE_DIM;
+  return select_splits(M, N, K);
+}
+
 int64_t gemm_f32_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits) {
   if (M < 0 || N < 0 || K < 0) return GEMMF32_ERR_NEGATIVE_DIM;
+  if (splits == 0) splits = select_splits(M, N, K);
   if (splits < 1 || splits > kMaxSplits) return GEMMF32_ERR_BAD_CONFIG;
   if (M == 0 || N == 0 || K == 0) return 0;
   int64_t kc = 0;

@@ -35,7 +35,15 @@ SHAPES = [
     # more points for the nearest-shape rule
     (256, 256, 256), (512, 512, 512), (2048, 2048, 2048), (6144, 6144, 6144),
     (64, 4096, 4096), (4096, 4096, 512), (2048, 8192, 2048),
+    # skinny shapes (a small batch of rows against a wide layer)
+    (16, 4096, 4096), (32, 4096, 4096), (128, 4096, 4096), (32, 8192, 8192),
 ]
+
+# Shapes for the split-count table: skinny, tall-K and square.
+SPLIT_SHAPES = [(16, 4096, 4096), (32, 4096, 4096), (64, 4096, 4096), (128, 4096, 4096),
+                (32, 8192, 8192), (64, 8192, 8192), (256, 256, 8192), (512, 512, 8192),
+                (1024, 1024, 1024), (2048, 2048, 2048), (4096, 4096, 4096)]
+SPLIT_CHOICES = (1, 2, 4, 8, 16)
 
 HEADER_TEMPLATE = """// Per-shape dispatch table: (M, N, K) -> variant and tile configuration.
 //
@@ -94,6 +102,34 @@ static inline void select_shape(int64_t M, int64_t N, int64_t K, int* variant, i
 static inline int select_for_variant(int64_t M, int64_t N, int64_t K, int variant) {{
   const DispatchRow& r = dispatch_nearest(M, N, K);
   return variant == 1 ? r.sb_cfg : variant == 3 ? r.ms_cfg : r.db_cfg;
+}}
+
+// Split-K: measured best number of K chunks per shape (1 = do not split), nearest row in
+// (log2 M, log2 N, log2 K).  Trailing comments: microseconds of each measured choice.
+struct SplitRow {{
+  int64_t m, n, k;
+  int splits;
+}};
+
+static const SplitRow kSplitK[] = {{
+{split_rows}
+}};
+
+static inline int select_splits(int64_t M, int64_t N, int64_t K) {{
+  const double lm = dispatch_log2(M), ln = dispatch_log2(N), lk = dispatch_log2(K);
+  int best = 0;
+  double best_d = 1e300;
+  for (int i = 0; i < (int)(sizeof(kSplitK) / sizeof(kSplitK[0])); ++i) {{
+    const SplitRow& r = kSplitK[i];
+    const double dm = lm - dispatch_log2(r.m), dn = ln - dispatch_log2(r.n),
+                 dk = lk - dispatch_log2(r.k);
+    const double d = dm * dm + dn * dn + dk * dk;
+    if (d < best_d) {{
+      best_d = d;
+      best = i;
+    }}
+  }}
+  return kSplitK[best].splits;
 }}
 
 }}  // namespace gemmf32
@@ -266,6 +302,34 @@ def barrier_study(shapes=BARRIER_SHAPES, rounds=2, batches=5, batch_ms=20.0, log
     return out
 
 
+def split_study(shapes=SPLIT_SHAPES, choices=SPLIT_CHOICES, rounds=2, batches=5,
+                batch_ms=20.0, log=print):
+    """Time gemm_f32_splitk for each split count (1 = the plain dispatched product)."""
+    import torch
+
+    out = []
+    for (M, N, K) in shapes:
+        A, B, C = _operands(M, N, K)
+        s_ptr = torch.cuda.current_stream().cuda_stream
+        need = max(tdb.gemm_f32_splitk_workspace(M, N, K, sp) for sp in choices)
+        ws = torch.empty(max(need, 1), device=A.device)
+
+        def caller(sp):
+            def call():
+                rc = tdb.gemm_f32_splitk(M, N, K, A.data_ptr(), K, B.data_ptr(), N,
+                                         C.data_ptr(), N, sp, ws.data_ptr(), ws.numel(), s_ptr)
+                if rc != tdb.OK:
+                    raise tdb.GemmError(rc, "gemm_f32_splitk")
+            return call
+        us = time_calls({str(sp): caller(sp) for sp in choices}, rounds, batches, batch_ms)
+        out.append({"M": M, "N": N, "K": K, "us": us})
+        best = min(us, key=us.get)
+        log(f"{M}x{N}x{K}: " + ", ".join(f"s{k} {v:.1f}" for k, v in us.items())
+            + f" -> splits {best}")
+        del A, B, C, ws
+    return out
+
+
 RASTER_SHAPES = [(4096, 4096, 4096), (8192, 8192, 8192), (6144, 6144, 6144)]
 RASTER_SETTINGS = ["", "1", "2", "3", "4", "16", "32", "8,noxcd", "1,noxcd"]
 
@@ -315,14 +379,25 @@ def table_rows(results):
     return rows
 
 
-def write_header(results, device, rounds, batches, batch_ms, path=None):
+def split_rows(split_results):
+    lines = []
+    for r in split_results:
+        best = min(r["us"], key=lambda k: r["us"][k])
+        times = ", ".join(f"{k}: {v:.1f}" for k, v in r["us"].items())
+        lines.append(f"    {{{r['M']}, {r['N']}, {r['K']}, {int(best)}}},  // {times}")
+    return lines
+
+
+def write_header(results, device, rounds, batches, batch_ms, path=None, split_results=None):
     path = path or os.path.join(CSRC, "dispatch_table.h")
     lines = []
     for (m, n, k, v, c, s, d, ms, sb_us, db_us, ms_us) in table_rows(results):
         lines.append(f"    {{{m}, {n}, {k}, {v}, {c}, {s}, {d}, {ms}}},  // sb {sb_us:.2f} us, "
                      f"db {db_us:.2f} us, ms {ms_us:.2f} us")
+    srows = split_rows(split_results) if split_results else ["    {1024, 1024, 1024, 1},"]
     text = HEADER_TEMPLATE.format(device=device, rounds=rounds, batches=batches,
-                                  batch_ms=int(batch_ms), rows="\n".join(lines))
+                                  batch_ms=int(batch_ms), rows="\n".join(lines),
+                                  split_rows="\n".join(srows))
     with open(path, "w") as f:
         f.write(text)
     return path
@@ -366,7 +441,7 @@ def main(argv=None) -> int:
         with open(args.from_json) as f:
             data = json.load(f)
         print(write_header(data["results"], data["device"], data["rounds"], data["batches"],
-                           data["batch_ms"]))
+                           data["batch_ms"], split_results=data.get("splits")))
         return 0
     import torch
 
@@ -375,14 +450,17 @@ def main(argv=None) -> int:
     t0 = time.time()
     results = measure(SHAPES, args.rounds, args.batches, args.batch_ms,
                       log=lambda *a: print(*a, flush=True))
+    splits = split_study(rounds=args.rounds, batches=args.batches, batch_ms=args.batch_ms,
+                         log=lambda *a: print(*a, flush=True))
     data = {"device": device, "rounds": args.rounds, "batches": args.batches,
             "batch_ms": args.batch_ms, "library": tdb.gemm_f32_version(),
-            "seconds": time.time() - t0, "results": results}
+            "seconds": time.time() - t0, "results": results, "splits": splits}
     if args.out:
         with open(args.out, "w") as f:
             json.dump(data, f, indent=1)
     if args.write_header:
-        print(write_header(results, device, args.rounds, args.batches, args.batch_ms))
+        print(write_header(results, device, args.rounds, args.batches, args.batch_ms,
+                           split_results=splits))
     return 0
 
 
