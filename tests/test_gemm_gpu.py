@@ -292,3 +292,69 @@ def test_splitk_one_split_equals_plain_and_errors():
     C = tdb.matmul_splitk(Ad, Bd, 4)
     torch.cuda.synchronize()
     assert torch.all(C == float(K))
+
+
+def test_offsets_beyond_2gib():
+    """32768 x 32768 x 32: C is 4 GiB, so row offsets pass 2^31 bytes (64-bit addressing in
+    the copies and the epilogue).  Checked at 4096 seeded positions plus the last row and
+    the last column."""
+    M = N = 32768
+    K = 32
+    _say("[big] 32768x32768x32 generating ...")
+    A, B = ti.workload_inputs(M, N, K, 9001)
+    Ad, Bd = _dev(A), _dev(B)
+    C = torch.empty((M, N), device=DEV)
+    ri, rj = ti.sample_positions(9001, M, N, 4096)
+    ri = np.concatenate([ri, np.full(64, M - 1), np.arange(M - 64, M)])
+    rj = np.concatenate([rj, np.arange(N - 64, N), np.full(64, N - 1)])
+    c64, bnd = oracle.gemm_f64_sampled(A, B, ri, rj)
+    ii, jj = torch.from_numpy(ri).to(DEV), torch.from_numpy(rj).to(DEV)
+    for v in ("auto", "db", "ms"):
+        _say(f"[big] {v}")
+        _run(Ad, Bd, v, out=C)
+        got = C[ii, jj].cpu().numpy()
+        assert oracle.tolerance_ratio(got, c64, bnd) <= 1.0, v
+    del C
+
+
+def test_wide_dynamic_range():
+    """Rows of A and columns of B scaled by powers of two from 2^-30 to 2^30: every product
+    stays a normal FP32 number and the bound is relative, so nothing may lose accuracy."""
+    M, N, K = 200, 150, 700
+    rng = np.random.default_rng(55)
+    A, B = ti.workload_inputs(M, N, K, 9100)
+    A = (A * np.ldexp(1.0, rng.integers(-30, 31, (M, 1)))).astype(np.float32)
+    B = (B * np.ldexp(1.0, rng.integers(-30, 31, (1, N)))).astype(np.float32)
+    C64, Bnd = oracle.gemm_f64(A, B)
+    Ad, Bd = _dev(A), _dev(B)
+    for v in ("sb", "db", "ms"):
+        assert _ratio(_run(Ad, Bd, v), C64, Bnd) <= 1.0, v
+
+
+def test_long_k_full_output():
+    """K = 16384 (twice the largest workload's K), full output checked."""
+    M, N, K = 96, 80, 16384
+    A, B = ti.workload_inputs(M, N, K, 9200)
+    C64, Bnd = oracle.gemm_f64(A, B)
+    Ad, Bd = _dev(A), _dev(B)
+    for v in ("auto", "sb", "db", "ms"):
+        r = _ratio(_run(Ad, Bd, v), C64, Bnd)
+        _say(f"[longk] {v} ratio={r:.3g}")
+        assert r <= 1.0, v
+
+
+def test_raster_order_does_not_change_results(monkeypatch):
+    """GEMMF32_RASTER only changes which workgroup computes which tile: bitwise equal."""
+    A, B, C64, Bnd = _workload("ragged_513x257x129")
+    Ad, Bd = _dev(A), _dev(B)
+    M2, N2, K2 = 1100, 900, 300
+    A2, B2 = ti.workload_inputs(M2, N2, K2, 9300)
+    A2d, B2d = _dev(A2), _dev(B2)
+    ref = [_run(Ad, Bd, v).clone() for v in ("db", "ms")]
+    ref2 = [_run(A2d, B2d, v, 3).clone() for v in ("sb", "db")]
+    for setting in ("1", "3", "16,noxcd", "255"):
+        monkeypatch.setenv("GEMMF32_RASTER", setting)
+        for r, v in zip(ref, ("db", "ms")):
+            assert torch.equal(_run(Ad, Bd, v), r), (setting, v)
+        for r, v in zip(ref2, ("sb", "db")):
+            assert torch.equal(_run(A2d, B2d, v, 3), r), (setting, v)
