@@ -58,6 +58,11 @@ struct TileCfg {
   static constexpr int B_PER_T = BK * BN / 4 / NT;
   static constexpr int A_ROWS_PER_PASS = NT / A_GROUPS_PER_ROW;
   static constexpr int B_ROWS_PER_PASS = NT / B_GROUPS_PER_ROW;
+  // Unroll the double-buffered loop by two (fixed slot addresses) unless the wave's
+  // register budget is too tight for it: with eight waves per workgroup a wave has 256
+  // registers, and a 128-accumulator wave tile plus two tiles' worth of copy and fragment
+  // registers would spill.
+  static constexpr bool DB_UNROLL = NT <= 256 || FM * FN * 16 <= 64;
 
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(BK % 8 == 0, "BK must be a multiple of 8");
@@ -353,35 +358,64 @@ __device__ inline void load_tile(TileCopy<C>& cp, const LoopArgs<C>& g, int kt) 
 // and the second half of tile l's last round runs after the barrier, covering the
 // latency of the first reads of tile l+1.  Barriers per product: 1 (prologue) +
 // (k_tiles - 1) = k_tiles, the same count as a barrier at the top of every iteration.
+// One steady-state step of the double-buffered loop: copy tile l+1 towards the idle slot
+// `nxt` while multiplying the tile in `cur`, one barrier at the hand-off.  On entry f[0]
+// holds round 0 of the current tile; on exit it holds round 0 of tile l+1.
+template <class C, bool GUARD>
+__device__ __forceinline__ void db_step(const float* cur, float* nxt, TileCopy<C>& cp,
+                                        const LaneView<C>& lv, const LoopArgs<C>& g, int l,
+                                        Frag<C> (&f)[2], floatx16 (&acc)[C::FM][C::FN]) {
+  constexpr int R = C::BK / 8;
+  load_tile<C, GUARD>(cp, g, l + 1);  // in flight during the MFMAs below
+#pragma unroll
+  for (int q = 0; q + 1 < R; ++q) {
+    read_frag(cur, lv, q + 1, f[(q + 1) & 1]);
+    mfma_round<C, 0>(f[q & 1], acc);
+  }
+  mfma_round<C, 1>(f[1], acc);
+  cp.store(nxt);
+  if constexpr (!GUARD) Sched<C>::template db_before_barrier<0>();
+  __syncthreads();
+  read_frag(nxt, lv, 0, f[0]);
+  mfma_round<C, 2>(f[1], acc);
+  if constexpr (!GUARD) Sched<C>::db_after_barrier();
+}
+
+// Double-buffered: two LDS slots, tile l+1 copied into the idle slot while tile l is
+// multiplied, ONE barrier per K tile.  The loop is rotated so that the barrier sits at
+// the hand-off between slots: after this wave has written tile l+1 into the idle slot and
+// before anybody reads it.  That single barrier is at once "tile l+1 has landed" and
+// "nobody still reads the slot that tile l+2 will overwrite" (all reads of tile l are
+// already in registers by then).  LDS fragments are read one round ahead of the MFMAs,
+// and the second half of tile l's last round runs after the barrier, covering the
+// latency of the first reads of tile l+1.  Barriers per product: 1 (prologue) +
+// (k_tiles - 1) = k_tiles, the same count as a barrier at the top of every iteration.
+// Where registers allow (DB_UNROLL) the loop body holds two steps (slot 0 -> 1, then slot
+// 1 -> 0), so both slot addresses are fixed in each step instead of being recomputed from
+// the tile parity.
 template <class C, bool GUARD>
 __device__ inline void k_loop_db(float* smem, TileCopy<C>& cp, const LaneView<C>& lv,
                                  const LoopArgs<C>& g, int k_tiles,
                                  floatx16 (&acc)[C::FM][C::FN]) {
   constexpr int R = C::BK / 8;
   Frag<C> f[2];
+  float* const s0 = smem;
+  float* const s1 = smem + C::SLOT;
   load_tile<C, GUARD>(cp, g, 0);  // prologue: tile 0 into slot 0
-  cp.store(smem);
+  cp.store(s0);
   __syncthreads();
-  read_frag(smem, lv, 0, f[0]);
-  for (int l = 0; l + 1 < k_tiles; ++l) {
-    const float* cur = smem + (l & 1) * C::SLOT;
-    float* nxt = smem + ((l + 1) & 1) * C::SLOT;
-    load_tile<C, GUARD>(cp, g, l + 1);  // in flight during the MFMAs below
-#pragma unroll
-    for (int q = 0; q + 1 < R; ++q) {
-      read_frag(cur, lv, q + 1, f[(q + 1) & 1]);
-      mfma_round<C, 0>(f[q & 1], acc);
+  read_frag(s0, lv, 0, f[0]);
+  int l = 0;
+  if constexpr (C::DB_UNROLL) {
+    for (; l + 2 < k_tiles; l += 2) {
+      db_step<C, GUARD>(s0, s1, cp, lv, g, l, f, acc);
+      db_step<C, GUARD>(s1, s0, cp, lv, g, l + 1, f, acc);
     }
-    mfma_round<C, 1>(f[1], acc);
-    cp.store(nxt);
-    if constexpr (!GUARD) Sched<C>::template db_before_barrier<0>();
-    __syncthreads();
-    read_frag(nxt, lv, 0, f[0]);
-    mfma_round<C, 2>(f[1], acc);
-    if constexpr (!GUARD) Sched<C>::db_after_barrier();
   }
-  // Last tile: nothing left to prefetch.
-  const float* cur = smem + ((k_tiles - 1) & 1) * C::SLOT;
+  for (; l + 1 < k_tiles; ++l)
+    db_step<C, GUARD>((l & 1) ? s1 : s0, (l & 1) ? s0 : s1, cp, lv, g, l, f, acc);
+  // Last tile (l == k_tiles - 1): nothing left to prefetch.
+  const float* cur = (l & 1) ? s1 : s0;
 #pragma unroll
   for (int q = 0; q + 1 < R; ++q) {
     read_frag(cur, lv, q + 1, f[(q + 1) & 1]);
@@ -655,17 +689,11 @@ __device__ __forceinline__ void ms_wait() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" : : "n"(N) : "memory");
 }
 
-// Tile `next` must have landed in every wave before anybody reads it: wait for this
-// wave's copies of it (`after` later tiles, 0 .. S-2, may stay in flight), then barrier.
+// Wait until tile l+1 has landed in this wave's copies (the S-2 tiles issued after it may
+// stay in flight) and this wave's LDS reads have returned, then barrier.
 template <class C, int S>
-__device__ __forceinline__ void ms_wait_tile_barrier(int after) {
-  constexpr int D = MsCfg<C, S>::D;
-  if (S >= 4 && after >= 2)
-    ms_wait<(S >= 4 ? 2 * D : 0)>();
-  else if (S >= 3 && after >= 1)
-    ms_wait<(S >= 3 ? D : 0)>();
-  else
-    ms_wait<0>();
+__device__ __forceinline__ void ms_wait_tile_barrier() {
+  ms_wait<MsCfg<C, S>::D * (S - 2)>();
   asm volatile("s_barrier" : : : "memory");
 }
 
@@ -702,11 +730,39 @@ __device__ inline void read_frag_ms(const float* stage, const LaneViewMs<C, S>& 
     for (int t = 0; t < 4; ++t) f.b[fn][t] = stage[lv.b_off[fn] + (8 * q + t) * C::BN];
 }
 
-// The MS K-loop.  Per iteration l: start the copy of tile l+S-1 into the stage that tile
-// l-1 used, multiply tile l, and -- at the hand-off, before the second half of tile l's
-// last round -- wait for tile l+1 and pass ONE barrier.  That barrier makes tile l+1
-// visible to every wave and certifies that every wave has finished reading tile l, whose
-// stage the copy issued in the next iteration overwrites.
+// One steady-state step of the MS loop for tile l held in stage `st`: start the copy of
+// tile l+S-1 into the stage that tile l-1 used, multiply tile l, and -- at the hand-off,
+// before the second half of tile l's last round -- wait for tile l+1 and pass ONE
+// barrier.  That barrier makes tile l+1 visible to every wave and certifies that every
+// wave has finished reading tile l, whose stage the copy issued in the next step
+// overwrites.  Near the end the copy index is clamped to the last tile (a harmless
+// duplicate into a stage no later tile uses), so every wait keeps S-2 tiles in flight.
+template <class C, int S>
+__device__ __forceinline__ void ms_step(const float* smem, const MsCopy<C, S>& cp,
+                                        const LaneViewMs<C, S>& lv, int l, int k_tiles,
+                                        int st, Frag<C> (&f)[2],
+                                        floatx16 (&acc)[C::FM][C::FN]) {
+  using MC = MsCfg<C, S>;
+  constexpr int R = C::BK / 8;
+  cp.issue(min(l + S - 1, k_tiles - 1), st == 0 ? S - 1 : st - 1);
+  const float* cur = smem + st * MC::STAGE;
+#pragma unroll
+  for (int q = 0; q + 1 < R; ++q) {
+    read_frag_ms(cur, lv, q + 1, f[(q + 1) & 1]);
+    mfma_round<C, 0>(f[q & 1], acc);
+  }
+  mfma_round<C, 1>(f[1], acc);
+  Sched<C>::template rounds_with_reads<0>();
+  sched_group<kSchedMfma, Sched<C>::MQ / 2>();
+  ms_wait_tile_barrier<C, S>();
+  read_frag_ms(smem + (st + 1 == S ? 0 : st + 1) * MC::STAGE, lv, 0, f[0]);
+  mfma_round<C, 2>(f[1], acc);
+  Sched<C>::db_after_barrier();
+}
+
+// The MS K-loop: prologue (tiles 0 .. S-2 in flight, tile 0 landed), steps unrolled S at a
+// time so that every stage address is fixed, the remaining steps one by one, and the
+// last tile (nothing left to copy) peeled off.
 template <class C, int S>
 __device__ inline void k_loop_ms(float* smem, const MsCopy<C, S>& cp,
                                  const LaneViewMs<C, S>& lv, int k_tiles,
@@ -714,30 +770,23 @@ __device__ inline void k_loop_ms(float* smem, const MsCopy<C, S>& cp,
   using MC = MsCfg<C, S>;
   constexpr int R = C::BK / 8;
 #pragma unroll
-  for (int t = 0; t < S - 1; ++t)
-    if (t < k_tiles) cp.issue(t, t);
-  ms_wait_tile_barrier<C, S>(min(S - 2, k_tiles - 1));
+  for (int t = 0; t < S - 1; ++t) cp.issue(min(t, k_tiles - 1), t);
+  ms_wait_tile_barrier<C, S>();
   Frag<C> f[2];
   read_frag_ms(smem, lv, 0, f[0]);
-  int st = 0;                 // stage of tile l
-  int st_issue = S - 1;       // stage for tile l+S-1
-  for (int l = 0; l < k_tiles; ++l) {
-    if (l + S - 1 < k_tiles) cp.issue(l + S - 1, st_issue);
-    const float* cur = smem + st * MC::STAGE;
+  int l = 0;
+  for (; l + S < k_tiles; l += S) {
 #pragma unroll
-    for (int q = 0; q + 1 < R; ++q) {
-      read_frag_ms(cur, lv, q + 1, f[(q + 1) & 1]);
-      mfma_round<C, 0>(f[q & 1], acc);
-    }
-    mfma_round<C, 1>(f[1], acc);
-    st = st + 1 == S ? 0 : st + 1;
-    st_issue = st_issue + 1 == S ? 0 : st_issue + 1;
-    if (l + 1 < k_tiles) {
-      ms_wait_tile_barrier<C, S>(min(S - 2, k_tiles - 2 - l));
-      read_frag_ms(smem + st * MC::STAGE, lv, 0, f[0]);
-    }
-    mfma_round<C, 2>(f[1], acc);
+    for (int u = 0; u < S; ++u) ms_step<C, S>(smem, cp, lv, l + u, k_tiles, u, f, acc);
   }
+  for (; l + 1 < k_tiles; ++l) ms_step<C, S>(smem, cp, lv, l, k_tiles, l % S, f, acc);
+  const float* cur = smem + (l % S) * MC::STAGE;  // last tile: nothing left to copy
+#pragma unroll
+  for (int q = 0; q + 1 < R; ++q) {
+    read_frag_ms(cur, lv, q + 1, f[(q + 1) & 1]);
+    mfma_round<C, 0>(f[q & 1], acc);
+  }
+  mfma_round<C, 0>(f[1], acc);
 }
 
 template <class C, int S>
