@@ -24,25 +24,25 @@ struct DispatchRow {
 };
 
 static const DispatchRow kDispatch[] = {
-    {128, 128, 128, 2, 7, 7, 7, 10},  // sb 4.36 us, db 4.35 us, ms 4.58 us
-    {127, 193, 61, 2, 6, 6, 6, 6},  // sb 5.15 us, db 5.07 us, ms 5.14 us
-    {513, 257, 129, 2, 6, 6, 6, 6},  // sb 8.86 us, db 8.20 us, ms 8.31 us
-    {1024, 1024, 1024, 3, 7, 7, 6, 7},  // sb 23.80 us, db 22.27 us, ms 21.49 us
-    {256, 1024, 128, 2, 7, 7, 7, 10},  // sb 4.65 us, db 4.65 us, ms 4.83 us
-    {1024, 128, 256, 2, 6, 7, 6, 10},  // sb 7.11 us, db 6.99 us, ms 7.09 us
-    {4096, 4096, 4096, 2, 1, 9, 1, 8},  // sb 994.83 us, db 937.29 us, ms 952.47 us
-    {8192, 8192, 8192, 2, 1, 9, 1, 8},  // sb 8095.20 us, db 7433.89 us, ms 7586.61 us
-    {256, 256, 256, 2, 6, 7, 6, 10},  // sb 7.06 us, db 6.94 us, ms 7.03 us
-    {512, 512, 512, 3, 10, 7, 6, 10},  // sb 12.21 us, db 11.90 us, ms 11.73 us
-    {2048, 2048, 2048, 2, 4, 7, 4, 3},  // sb 139.42 us, db 129.64 us, ms 135.79 us
-    {6144, 6144, 6144, 2, 4, 4, 4, 3},  // sb 3459.10 us, db 3308.22 us, ms 3352.21 us
-    {64, 4096, 4096, 3, 7, 7, 6, 7},  // sb 96.51 us, db 80.12 us, ms 76.17 us
-    {4096, 4096, 512, 2, 2, 9, 2, 8},  // sb 133.53 us, db 128.64 us, ms 131.04 us
-    {2048, 8192, 2048, 2, 1, 9, 1, 8},  // sb 501.87 us, db 476.36 us, ms 482.86 us
-    {16, 4096, 4096, 2, 7, 7, 7, 7},  // sb 120.42 us, db 106.55 us, ms 106.64 us
-    {32, 4096, 4096, 3, 10, 7, 10, 10},  // sb 123.20 us, db 80.86 us, ms 76.44 us
-    {128, 4096, 4096, 3, 7, 7, 6, 7},  // sb 96.70 us, db 80.27 us, ms 76.33 us
-    {32, 8192, 8192, 3, 10, 7, 10, 10},  // sb 248.04 us, db 165.12 us, ms 151.43 us
+    {128, 128, 128, 2, 6, 7, 6, 6},  // sb 4.43 us, db 4.43 us, ms 4.50 us
+    {127, 193, 61, 2, 6, 6, 6, 6},  // sb 5.13 us, db 5.01 us, ms 5.07 us
+    {513, 257, 129, 2, 6, 6, 6, 6},  // sb 8.86 us, db 7.92 us, ms 8.02 us
+    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.75 us, db 20.48 us, ms 19.31 us
+    {256, 1024, 128, 1, 7, 7, 6, 6},  // sb 4.68 us, db 4.70 us, ms 4.73 us
+    {1024, 128, 256, 3, 6, 7, 6, 6},  // sb 7.08 us, db 6.75 us, ms 6.61 us
+    {4096, 4096, 4096, 2, 1, 9, 1, 9},  // sb 989.81 us, db 924.86 us, ms 934.96 us
+    {8192, 8192, 8192, 2, 1, 9, 1, 9},  // sb 8065.19 us, db 7316.10 us, ms 7395.04 us
+    {256, 256, 256, 3, 6, 7, 6, 6},  // sb 7.07 us, db 6.73 us, ms 6.60 us
+    {512, 512, 512, 3, 6, 7, 6, 6},  // sb 12.20 us, db 11.16 us, ms 10.60 us
+    {2048, 2048, 2048, 2, 4, 7, 4, 3},  // sb 139.36 us, db 123.99 us, ms 125.80 us
+    {6144, 6144, 6144, 2, 4, 4, 4, 4},  // sb 3452.80 us, db 3192.19 us, ms 3260.80 us
+    {64, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.78 us, db 72.37 us, ms 66.00 us
+    {4096, 4096, 512, 2, 2, 9, 2, 9},  // sb 133.30 us, db 126.83 us, ms 127.96 us
+    {2048, 8192, 2048, 2, 1, 9, 1, 9},  // sb 501.66 us, db 469.61 us, ms 474.87 us
+    {16, 4096, 4096, 2, 7, 7, 7, 10},  // sb 120.72 us, db 101.40 us, ms 101.75 us
+    {32, 4096, 4096, 3, 10, 7, 10, 10},  // sb 123.07 us, db 76.51 us, ms 67.45 us
+    {128, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.83 us, db 72.66 us, ms 66.34 us
+    {32, 8192, 8192, 3, 10, 7, 10, 10},  // sb 246.72 us, db 157.68 us, ms 132.25 us
 };
 
 static inline double dispatch_log2(int64_t x) { return x > 0 ? std::log2((double)x) : -1.0; }
@@ -83,17 +83,17 @@ struct SplitRow {
 };
 
 static const SplitRow kSplitK[] = {
-    {16, 4096, 4096, 8},  // 1: 119.6, 2: 63.5, 4: 35.2, 8: 30.2, 16: 33.6
-    {32, 4096, 4096, 8},  // 1: 119.6, 2: 63.8, 4: 35.7, 8: 30.5, 16: 33.1
-    {64, 4096, 4096, 4},  // 1: 77.3, 2: 43.0, 4: 26.2, 8: 27.3, 16: 31.3
-    {128, 4096, 4096, 4},  // 1: 77.3, 2: 43.9, 4: 42.0, 8: 43.7, 16: 47.8
-    {32, 8192, 8192, 4},  // 1: 237.3, 2: 124.7, 4: 96.6, 8: 99.3, 16: 105.4
-    {64, 8192, 8192, 4},  // 1: 152.2, 2: 82.1, 4: 79.2, 8: 84.3, 16: 92.3
-    {256, 256, 8192, 16},  // 1: 151.0, 2: 79.0, 4: 42.5, 8: 25.5, 16: 18.6
-    {512, 512, 8192, 8},  // 1: 151.6, 2: 79.9, 4: 43.9, 8: 42.4, 16: 46.1
-    {1024, 1024, 1024, 1},  // 1: 21.7, 2: 26.3, 4: 27.4, 8: 31.3, 16: 39.1
-    {2048, 2048, 2048, 1},  // 1: 129.3, 2: 137.9, 4: 143.3, 8: 157.9, 16: 194.1
-    {4096, 4096, 4096, 1},  // 1: 938.9, 2: 981.0, 4: 1033.1, 8: 1121.1, 16: 1308.6
+    {16, 4096, 4096, 8},  // 1: 101.3, 2: 54.1, 4: 30.6, 8: 27.5, 16: 30.9
+    {32, 4096, 4096, 8},  // 1: 67.6, 2: 37.4, 4: 22.4, 8: 19.4, 16: 32.9
+    {64, 4096, 4096, 4},  // 1: 67.6, 2: 38.3, 4: 24.4, 8: 29.7, 16: 29.9
+    {128, 4096, 4096, 2},  // 1: 68.0, 2: 39.6, 4: 42.8, 8: 43.2, 16: 48.9
+    {32, 8192, 8192, 4},  // 1: 132.9, 2: 71.0, 4: 46.2, 8: 50.6, 16: 56.7
+    {64, 8192, 8192, 2},  // 1: 133.6, 2: 74.9, 4: 78.6, 8: 89.5, 16: 104.5
+    {256, 256, 8192, 16},  // 1: 130.9, 2: 69.9, 4: 38.1, 8: 23.3, 16: 18.2
+    {512, 512, 8192, 4},  // 1: 132.2, 2: 70.6, 4: 40.6, 8: 41.2, 16: 45.1
+    {1024, 1024, 1024, 1},  // 1: 20.1, 2: 26.8, 4: 27.5, 8: 34.0, 16: 44.8
+    {2048, 2048, 2048, 1},  // 1: 123.9, 2: 134.6, 4: 141.4, 8: 156.5, 16: 193.1
+    {4096, 4096, 4096, 1},  // 1: 931.4, 2: 973.2, 4: 1022.9, 8: 1112.9, 16: 1296.4
 };
 
 static inline int select_splits(int64_t M, int64_t N, int64_t K) {
