@@ -57,7 +57,8 @@ PEAK_FP32_MFMA_TFLOPS = 157.3          # MI355X dense FP32 matrix peak (AMD spec
 METRIC = "FP32 GEMM TFLOP/s and % of MFMA FP32 peak at 1024³/4096³/8192³, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_8192.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_double_buffered_amd", "csrc", f)
-                  for f in ("gemm_f32.hip", "dispatch_table.h")]
+                  for f in ("gemm_f32.hip", "gemm_common.h", "kernels_sb_db.h",
+                            "kernels_ms.h", "splitk_reduce.h", "dispatch_table.h")]
 HEADLINE = "square_8192"
 VARIANT_NAMES = {1: "sb", 2: "db", 3: "ms"}
 

@@ -15,7 +15,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 SOURCES = [os.path.join(CSRC, "gemm_f32.hip")]
-DEPS = SOURCES + [os.path.join(CSRC, "dispatch_table.h"), os.path.join(INCLUDE, "gemmf32.h")]
+HEADERS = [os.path.join(CSRC, f) for f in ("gemm_common.h", "kernels_sb_db.h", "kernels_ms.h",
+                                            "splitk_reduce.h", "dispatch_table.h")]
+DEPS = SOURCES + HEADERS + [os.path.join(INCLUDE, "gemmf32.h")]
 LIB = os.path.join(PKG, "libgemmf32.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 

@@ -1,0 +1,440 @@
+// Shared device code of the gemmf32 kernels: tile configurations, the workgroup-to-tile
+// order, the register-staged global -> LDS copy, the FP32 matrix-core micro-kernel, the
+// instruction-interleaving hints, per-workgroup setup and the guarded epilogue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace gemmf32 {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------------------------------
+// Tile configuration.
+//   BM x BN : output tile of one workgroup        BK : K depth of one LDS tile
+//   WAVES_M x WAVES_N waves per workgroup; each wave owns a TM x TN sub-tile made of
+//   FM x FN blocks of 32 x 32, one 16-register accumulator per block.
+// LDS layout of one slot (FP32):
+//   As[BM][AS]  A tile with k contiguous, row stride AS = BK + 4 (the pad of 4 words
+//               makes the 16-byte reads of 8 or 16 consecutive rows hit distinct banks)
+//   Bs[BK][BS]  B tile with n contiguous, row stride BS = BN + 8 (so the two half-waves,
+//               which read rows 4 apart, land on opposite halves of the 64 banks)
+// ------------------------------------------------------------------------------------
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int NT = WAVES_M * WAVES_N * 64;
+  static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
+  static constexpr int FM = TM / 32, FN = TN / 32;
+  static constexpr int AS = BK + 4;
+  static constexpr int BS = BN + 8;
+  static constexpr int A_SLOT = BM * AS;
+  static constexpr int B_SLOT = BK * BS;
+  static constexpr int SLOT = A_SLOT + B_SLOT;  // floats per LDS slot
+  // Global -> LDS copy: 16-byte groups of 4 consecutive floats along a row.
+  static constexpr int A_GROUPS_PER_ROW = BK / 4;
+  static constexpr int B_GROUPS_PER_ROW = BN / 4;
+  static constexpr int A_PER_T = BM * BK / 4 / NT;  // groups per thread per tile
+  static constexpr int B_PER_T = BK * BN / 4 / NT;
+  static constexpr int A_ROWS_PER_PASS = NT / A_GROUPS_PER_ROW;
+  static constexpr int B_ROWS_PER_PASS = NT / B_GROUPS_PER_ROW;
+  // Unroll the double-buffered loop by two (fixed slot addresses) unless the wave's
+  // register budget is too tight for it: with eight waves per workgroup a wave has 256
+  // registers, and a 128-accumulator wave tile plus two tiles' worth of copy and fragment
+  // registers would spill.
+  static constexpr bool DB_UNROLL = NT <= 256 || FM * FN * 16 <= 64;
+
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+  static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+  static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "copy must divide");
+  static_assert(NT % A_GROUPS_PER_ROW == 0 && NT % B_GROUPS_PER_ROW == 0, "copy rows");
+  static_assert(A_PER_T >= 1 && B_PER_T >= 1, "copy work per thread");
+};
+
+// Flags passed to the kernel.
+enum : int {
+  kVecA = 1,  // A 16-byte aligned and lda % 4 == 0: rows can be read 16 bytes at a time
+  kVecB = 2,  // same for B
+};
+
+// ------------------------------------------------------------------------------------
+// Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin; renumber
+// them so that consecutive ids run on one XCD (which has its own L2), then walk the
+// tiles in column-major groups of `group_m` tile rows so that workgroups close in id
+// share panels of A and B.  Both choices can be changed per launch for measurement (flags
+// bits 8..15: group_m, 0 = the default 8; bit 16: keep the hardware order of ids).
+// ------------------------------------------------------------------------------------
+enum : int { kRasterGroupShift = 8, kRasterNoXcdRemap = 1 << 16 };
+
+__device__ inline void tile_coords(int tiles_m, int tiles_n, int flags, int& tm, int& tn) {
+  constexpr int kXcds = 8;
+  const int gm_flag = (flags >> kRasterGroupShift) & 0xff;
+  const int group_m = gm_flag ? gm_flag : 8;
+  const int nwg = gridDim.x;
+  int bid = blockIdx.x;
+  if (!(flags & kRasterNoXcdRemap) && nwg % kXcds == 0)
+    bid = (bid % kXcds) * (nwg / kXcds) + bid / kXcds;
+  const int per_group = group_m * tiles_n;
+  const int group = bid / per_group;
+  const int first_m = group * group_m;
+  const int rows = min(tiles_m - first_m, group_m);
+  const int in_group = bid - group * per_group;
+  tm = first_m + in_group % rows;
+  tn = in_group / rows;
+}
+
+// ------------------------------------------------------------------------------------
+// The workgroup's copy of one K tile: global memory -> registers -> LDS.
+// Thread t moves groups g = t + p * NT (p = 0 .. PER_T-1); group g of A is row
+// g / (BK/4), columns 4 * (g % (BK/4)) .. +3 of the tile; likewise for B with BN/4.
+// ------------------------------------------------------------------------------------
+template <class C>
+struct TileCopy {
+  floatx4 ra[C::A_PER_T];
+  floatx4 rb[C::B_PER_T];
+
+  // Per-thread coordinates inside the tile.
+  int a_row, a_col, b_row, b_col;
+
+  __device__ inline void init(int tid) {
+    a_row = tid / C::A_GROUPS_PER_ROW;
+    a_col = 4 * (tid % C::A_GROUPS_PER_ROW);
+    b_row = tid / C::B_GROUPS_PER_ROW;
+    b_col = 4 * (tid % C::B_GROUPS_PER_ROW);
+  }
+
+  // Fast path: the whole tile lies inside the matrices and rows are 16-byte aligned.
+  __device__ inline void load_a_fast(const float* __restrict__ A, int64_t lda, int m0,
+                                     int k0) {
+    const float* p = A + (int64_t)(m0 + a_row) * lda + (k0 + a_col);
+#pragma unroll
+    for (int i = 0; i < C::A_PER_T; ++i)
+      ra[i] = *reinterpret_cast<const floatx4*>(p + (int64_t)(i * C::A_ROWS_PER_PASS) * lda);
+  }
+  __device__ inline void load_b_fast(const float* __restrict__ B, int64_t ldb, int n0,
+                                     int k0) {
+    const float* p = B + (int64_t)(k0 + b_row) * ldb + (n0 + b_col);
+#pragma unroll
+    for (int i = 0; i < C::B_PER_T; ++i)
+      rb[i] = *reinterpret_cast<const floatx4*>(p + (int64_t)(i * C::B_ROWS_PER_PASS) * ldb);
+  }
+
+  // Guarded path: element by element; anything outside M x K (A) or K x N (B) reads as
+  // +0, so a partial K tile adds exact zeros and edge rows/columns stay finite.
+  __device__ inline void load_a_guarded(const float* __restrict__ A, int64_t lda, int M,
+                                        int K, int m0, int k0) {
+#pragma unroll
+    for (int i = 0; i < C::A_PER_T; ++i) {
+      const int r = m0 + a_row + i * C::A_ROWS_PER_PASS;
+      const int c = k0 + a_col;
+      const float* p = A + (int64_t)r * lda + c;
+      floatx4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (r < M && c + e < K) ? p[e] : 0.0f;
+      ra[i] = v;
+    }
+  }
+  __device__ inline void load_b_guarded(const float* __restrict__ B, int64_t ldb, int N,
+                                        int K, int n0, int k0) {
+#pragma unroll
+    for (int i = 0; i < C::B_PER_T; ++i) {
+      const int r = k0 + b_row + i * C::B_ROWS_PER_PASS;
+      const int c = n0 + b_col;
+      const float* p = B + (int64_t)r * ldb + c;
+      floatx4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (r < K && c + e < N) ? p[e] : 0.0f;
+      rb[i] = v;
+    }
+  }
+
+  __device__ inline void store_a(float* slot) {
+    float* As = slot;
+#pragma unroll
+    for (int i = 0; i < C::A_PER_T; ++i)
+      *reinterpret_cast<floatx4*>(As + (a_row + i * C::A_ROWS_PER_PASS) * C::AS + a_col) = ra[i];
+  }
+  __device__ inline void store_b(float* slot) {
+    float* Bs = slot + C::A_SLOT;
+#pragma unroll
+    for (int i = 0; i < C::B_PER_T; ++i)
+      *reinterpret_cast<floatx4*>(Bs + (b_row + i * C::B_ROWS_PER_PASS) * C::BS + b_col) = rb[i];
+  }
+  __device__ inline void store(float* slot) {
+    store_a(slot);
+    store_b(slot);
+  }
+};
+
+// ------------------------------------------------------------------------------------
+// Matrix-core micro-kernel.
+// v_mfma_f32_32x32x2_f32: lane L supplies A[L%32][L/32] and B[L/32][L%32] of a
+// 32x2 by 2x32 step and accumulates a 32x32 block, of which lane L holds column L%32,
+// rows 8*(r/4) + 4*(L/32) + r%4 in accumulator register r (r = 0..15).
+// A K tile is consumed in BK/8 rounds of eight k values.  In round q lane L reads
+// A[row][8q+4h .. 8q+4h+3] (h = L/32) with one 16-byte LDS read and B[8q+4h+t][col] for
+// t = 0..3; the MFMA for t then sums k = 8q+t and 8q+4+t.  The four MFMAs of a round
+// cover its eight k values once each, so the product is unchanged; only the order of the
+// k sum differs from the textbook loop.
+// ------------------------------------------------------------------------------------
+template <class C>
+struct Frag {
+  floatx4 a[C::FM];
+  float b[C::FN][4];
+};
+
+// This lane's fragment offsets (in floats) inside an LDS slot.
+template <class C>
+struct LaneView {
+  int a_off, b_off;
+  __device__ inline void init(int wm, int wn, int lane) {
+    const int h = lane >> 5, l32 = lane & 31;
+    a_off = (wm * C::TM + l32) * C::AS + 4 * h;
+    b_off = C::A_SLOT + (4 * h) * C::BS + wn * C::TN + l32;
+  }
+};
+
+template <class C>
+__device__ inline void read_frag(const float* slot, const LaneView<C>& lv, int q, Frag<C>& f) {
+  const float* a_ptr = slot + lv.a_off + 8 * q;
+  const float* b_ptr = slot + lv.b_off + 8 * q * C::BS;
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+    f.a[fm] = *reinterpret_cast<const floatx4*>(a_ptr + fm * 32 * C::AS);
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) f.b[fn][t] = b_ptr[t * C::BS + fn * 32];
+}
+
+// The MFMAs of one round; PART 0 = all four k pairs, 1 = the first two, 2 = the last two.
+template <class C, int PART>
+__device__ inline void mfma_round(const Frag<C>& f, floatx16 (&acc)[C::FM][C::FN]) {
+  constexpr int t0 = PART == 2 ? 2 : 0;
+  constexpr int t1 = PART == 1 ? 2 : 4;
+#pragma unroll
+  for (int t = t0; t < t1; ++t)
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+        acc[fm][fn] =
+            __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[fm][t], f.b[fn][t], acc[fm][fn], 0, 0, 0);
+}
+
+// ------------------------------------------------------------------------------------
+// Instruction interleaving for the unguarded loops.  The compiler's scheduler, left
+// alone, sinks the global prefetch loads to just before their LDS stores, which exposes
+// their whole latency.  These hints (sched_group_barrier, applied to the scheduling
+// region they close) ask for each other memory instruction to be followed by a share of
+// the MFMAs, so that the matrix pipe keeps issuing while loads and stores are in flight.
+// ------------------------------------------------------------------------------------
+enum : int { kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100,
+             kSchedDsWrite = 0x200 };
+
+template <int MASK, int SIZE>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (SIZE > 0) __builtin_amdgcn_sched_group_barrier(MASK, SIZE, 0);
+}
+
+// NOTHER instructions of class OMASK spread evenly over NMFMA MFMAs.
+template <int OMASK, int NOTHER, int NMFMA, int I = 0>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (NOTHER == 0) {
+    sched_group<kSchedMfma, NMFMA>();
+  } else if constexpr (I < NOTHER) {
+    constexpr int lo = I * NMFMA / NOTHER, hi = (I + 1) * NMFMA / NOTHER;
+    sched_group<OMASK, 1>();
+    sched_group<kSchedMfma, hi - lo>();
+    sched_interleave<OMASK, NOTHER, NMFMA, I + 1>();
+  }
+}
+
+template <class C>
+struct Sched {
+  static constexpr int R = C::BK / 8;                  // rounds per K tile
+  static constexpr int MQ = 4 * C::FM * C::FN;         // MFMAs per round
+  static constexpr int G = C::A_PER_T + C::B_PER_T;    // 16-byte global loads per tile
+  static constexpr int W = C::A_PER_T + C::B_PER_T;    // 16-byte LDS stores per tile
+  static constexpr int D = C::FM + 2 * C::FN;          // LDS read instructions per round
+
+  // Double-buffered, from the top of an iteration up to the barrier: round 0 carries the
+  // global loads of tile l+1 and the LDS reads of round 1; middle rounds carry the reads
+  // of the next round; the first half of the last round carries the LDS stores of tile
+  // l+1 into the idle slot.
+  template <int Q = 0>
+  static __device__ __forceinline__ void db_before_barrier() {
+    if constexpr (Q == 0) {
+      sched_interleave<kSchedVmemRead, G, MQ / 2>();
+      if constexpr (R > 1) sched_interleave<kSchedDsRead, D, MQ - MQ / 2>();
+      else sched_group<kSchedMfma, MQ - MQ / 2>();
+      db_before_barrier<1>();
+    } else if constexpr (Q < R - 1) {
+      sched_interleave<kSchedDsRead, D, MQ>();
+      db_before_barrier<Q + 1>();
+    } else {
+      sched_interleave<kSchedDsWrite, W, MQ / 2>();
+    }
+  }
+  // After the barrier: the first reads of tile l+1, then the rest of tile l's last round.
+  static __device__ __forceinline__ void db_after_barrier() {
+    sched_group<kSchedDsRead, D>();
+    sched_group<kSchedMfma, MQ - MQ / 2>();
+  }
+  // Rounds whose MFMAs each carry the LDS reads of the following round.
+  template <int Q = 0>
+  static __device__ __forceinline__ void rounds_with_reads() {
+    if constexpr (Q < R - 1) {
+      sched_interleave<kSchedDsRead, D, MQ>();
+      rounds_with_reads<Q + 1>();
+    }
+  }
+};
+
+// ------------------------------------------------------------------------------------
+// The K-loop.  GUARD = false is taken by workgroups whose whole tile lies inside the
+// matrices, with 16-byte-aligned rows and K a multiple of BK: every copy is unguarded.
+// GUARD = true picks per K tile between the unguarded and the element-guarded copy.
+// ------------------------------------------------------------------------------------
+template <class C>
+struct LoopArgs {
+  const float* A;
+  const float* B;
+  int64_t lda, ldb;
+  int M, N, K, m0, n0;
+  bool vec_a, vec_b;
+};
+
+template <class C, bool GUARD>
+__device__ inline void load_tile_a(TileCopy<C>& cp, const LoopArgs<C>& g, int kt) {
+  const int k0 = kt * C::BK;
+  if (!GUARD || (g.vec_a && k0 + C::BK <= g.K))
+    cp.load_a_fast(g.A, g.lda, g.m0, k0);
+  else
+    cp.load_a_guarded(g.A, g.lda, g.M, g.K, g.m0, k0);
+}
+
+template <class C, bool GUARD>
+__device__ inline void load_tile_b(TileCopy<C>& cp, const LoopArgs<C>& g, int kt) {
+  const int k0 = kt * C::BK;
+  if (!GUARD || (g.vec_b && k0 + C::BK <= g.K))
+    cp.load_b_fast(g.B, g.ldb, g.n0, k0);
+  else
+    cp.load_b_guarded(g.B, g.ldb, g.N, g.K, g.n0, k0);
+}
+
+template <class C, bool GUARD>
+__device__ inline void load_tile(TileCopy<C>& cp, const LoopArgs<C>& g, int kt) {
+  load_tile_a<C, GUARD>(cp, g, kt);
+  load_tile_b<C, GUARD>(cp, g, kt);
+}
+
+// Double-buffered: two LDS slots, tile l+1 copied into the idle slot while tile l is
+// multiplied, ONE barrier per K tile.  The loop is rotated so that the barrier sits at
+// the hand-off between slots: after this wave has written tile l+1 into the idle slot and
+// before anybody reads it.  That single barrier is at once "tile l+1 has landed" and
+// "nobody still reads the slot that tile l+2 will overwrite" (all reads of tile l are
+// already in registers by then).  LDS fragments are read one round ahead of the MFMAs,
+// and the second half of tile l's last round runs after the barrier, covering the
+// latency of the first reads of tile l+1.  Barriers per product: 1 (prologue) +
+// (k_tiles - 1) = k_tiles, the same count as a barrier at the top of every iteration.
+
+// ------------------------------------------------------------------------------------
+// Per-workgroup setup shared by every kernel.
+// ------------------------------------------------------------------------------------
+// Split-K: grid row y multiplies the K range [y*k_chunk, y*k_chunk + k_chunk) into its own
+// M x N partial product at Cmat + y*c_split_stride.  A one-row grid is left untouched.
+template <class PA, class PB, class PC>
+__device__ __forceinline__ void split_k_range(int& K, PA& A, PB& B, int64_t ldb, PC& Cmat,
+                                              int k_chunk, int64_t c_split_stride) {
+  if (gridDim.y > 1) {
+    const int kb = blockIdx.y * k_chunk;
+    K = min(K - kb, k_chunk);
+    A += kb;
+    B += (int64_t)kb * ldb;
+    Cmat += (int64_t)blockIdx.y * c_split_stride;
+  }
+}
+
+// Where this workgroup, wave and lane sit, and the copy arguments of the K-loop.
+template <class C>
+struct TilePos {
+  int tid, lane, wave, wm, wn;
+  bool m_full, n_full;  // the tile lies inside M (rows) / N (columns)
+  LoopArgs<C> g;
+
+  __device__ inline void init(int M, int N, int K, const float* A, int64_t lda,
+                              const float* B, int64_t ldb, int flags) {
+    tid = threadIdx.x;
+    lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    wm = wave / C::WAVES_N;
+    wn = wave % C::WAVES_N;
+    int tm, tn;
+    tile_coords((M + C::BM - 1) / C::BM, (N + C::BN - 1) / C::BN, flags, tm, tn);
+    g.A = A;
+    g.B = B;
+    g.lda = lda;
+    g.ldb = ldb;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.m0 = tm * C::BM;
+    g.n0 = tn * C::BN;
+    m_full = g.m0 + C::BM <= M;
+    n_full = g.n0 + C::BN <= N;
+    g.vec_a = (flags & kVecA) && m_full;
+    g.vec_b = (flags & kVecB) && n_full;
+  }
+  // Every K tile of this workgroup can be copied unguarded, 16 bytes at a time.
+  __device__ inline bool unguarded() const {
+    return g.vec_a && g.vec_b && (g.K % C::BK) == 0;
+  }
+};
+
+template <class C>
+__device__ inline void zero_acc(floatx16 (&acc)[C::FM][C::FN]) {
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
+}
+
+// Epilogue: C is written once, never read.  Lanes 0-31 of a store cover 32 consecutive
+// columns of one row and lanes 32-63 the same columns four rows further down; tiles that
+// stick out of M x N store only their inside part.
+template <class C>
+__device__ inline void store_c(const floatx16 (&acc)[C::FM][C::FN], float* Cmat, int64_t ldc,
+                               const TilePos<C>& t) {
+  const int row0 = t.g.m0 + t.wm * C::TM + 4 * (t.lane >> 5);
+  const int col0 = t.g.n0 + t.wn * C::TN + (t.lane & 31);
+  if (t.m_full && t.n_full) {
+    float* cbase = Cmat + (int64_t)row0 * ldc + col0;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          cbase[(int64_t)(fm * 32 + 8 * (r >> 2) + (r & 3)) * ldc + fn * 32] = acc[fm][fn][r];
+  } else {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + fm * 32 + 8 * (r >> 2) + (r & 3);
+          const int col = col0 + fn * 32;
+          if (row < t.g.M && col < t.g.N) Cmat[(int64_t)row * ldc + col] = acc[fm][fn][r];
+        }
+  }
+}
+
+}  // namespace gemmf32

@@ -1,0 +1,266 @@
+// The multi-stage (MS) K-loop of gemmf32 and its kernel: S LDS stages filled by gfx950
+// direct-to-LDS copies.
+#pragma once
+
+#include "gemm_common.h"
+#include "kernels_sb_db.h"
+
+namespace gemmf32 {
+
+// ------------------------------------------------------------------------------------
+// Multi-stage variant (MS): S LDS stages filled by gfx950 direct-to-LDS loads.
+//
+// The glossary page ("Double Buffering", second paragraph and the figure caption) notes
+// that its platform lost its asynchronous copy engine, so its double buffering overlaps
+// copies and math only through instruction-level parallelism, and it names the CUDA
+// analogue: a multi-stage asynchronous-copy pipeline.  gfx950 has the asynchronous copy:
+// global_load_lds_dwordx4 moves 16 bytes per lane from global memory straight into LDS
+// (lane L's bytes land at M0 + 16*L), with no registers in between and completion
+// tracked by vmcnt.  Tiles l+1 .. l+S-1 are in flight while tile l is multiplied.
+//
+// LDS layout of a stage (no padding; XOR swizzle at 16-byte-chunk granularity):
+//   A part: BM rows of BK floats;  chunk c of row r is stored at chunk c ^ swz_a(r)
+//   B part: BK rows of BN floats;  chunk c of row k is stored at chunk c ^ swz_b(k)
+// A wave's copy instruction always fills 1 KiB of consecutive LDS; each lane chooses the
+// global chunk that belongs at its position, so the swizzle costs nothing on the copy
+// side and makes the fragment reads conflict-free: the 16 lanes of a 16-byte read (16
+// consecutive rows, one logical chunk) hit 16 distinct bank groups, and the two
+// half-waves of a B read (rows k and k+4) fall on opposite halves of the 64 banks.
+//
+// The compiler's own wait insertion cannot tell one stage from another and would wait
+// for every outstanding copy before any LDS read, so the copies are issued from inline
+// assembly and their completion is waited for explicitly, per tile.
+// ------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) float lds_float;
+
+template <class C, int S>
+struct MsCfg {
+  static constexpr int STAGES = S;
+  static constexpr int A_FLOATS = C::BM * C::BK;
+  static constexpr int B_FLOATS = C::BK * C::BN;
+  static constexpr int STAGE = A_FLOATS + B_FLOATS;  // floats per stage
+  static constexpr int A_CHUNKS = A_FLOATS / 256;    // 1 KiB copy instructions, A part
+  static constexpr int B_CHUNKS = B_FLOATS / 256;
+  static constexpr int WAVES = C::NT / 64;
+  static constexpr int D = (A_CHUNKS + B_CHUNKS) / WAVES;  // copies per wave per tile
+  static constexpr int CPR_A = C::BK / 4;            // 16-byte chunks per A row
+  static constexpr int RPC_A = 256 / C::BK;          // A rows per 1 KiB
+  static constexpr int CPR_B = C::BN / 4;
+  static constexpr int RPC_B = 256 / C::BN;
+  // LDS floats: the stages, or the two padded slots of the guarded fallback loop.
+  static constexpr int LDS_FLOATS = S * STAGE > 2 * C::SLOT ? S * STAGE : 2 * C::SLOT;
+  static_assert(S >= 2, "at least two stages");
+  static_assert(C::BK == 16 || C::BK == 32 || C::BK == 64, "swizzle period");
+  static_assert(C::BN % 64 == 0, "B swizzle flips chunk bit 3 inside 16-chunk groups");
+  static_assert(A_FLOATS % 256 == 0 && B_FLOATS % 256 == 0, "whole 1 KiB copies");
+  static_assert((A_CHUNKS + B_CHUNKS) % WAVES == 0, "copies divide among waves");
+  static_assert(D * (S - 2) <= 63, "vmcnt range");
+  static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS of one CU");
+};
+
+template <class C>
+__device__ __forceinline__ int swz_a(int row) {
+  return (row / (64 / C::BK)) % (C::BK / 4);
+}
+__device__ __forceinline__ int swz_b(int k) { return ((k >> 2) & 1) << 3; }
+
+template <class C, int S>
+struct MsCopy {
+  using MC = MsCfg<C, S>;
+  const float* ptr[MC::D];  // this lane's source for tile 0
+  int64_t step[MC::D];      // floats between consecutive K tiles
+  uint32_t lds_off[MC::D];  // byte offset of the wave's 1 KiB inside a stage
+  uint32_t lds_base;        // LDS byte address of stage 0
+
+  __device__ inline void init(const float* smem, int wave, int lane, const float* A,
+                              int64_t lda, const float* B, int64_t ldb, int m0, int n0) {
+    lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_float*)smem);
+#pragma unroll
+    for (int i = 0; i < MC::D; ++i) {
+      const int j = wave + i * MC::WAVES;  // which 1 KiB of the stage this copy fills
+      if (j < MC::A_CHUNKS) {
+        const int row = j * MC::RPC_A + lane / MC::CPR_A;
+        const int c = (lane % MC::CPR_A) ^ swz_a<C>(row);
+        ptr[i] = A + (int64_t)(m0 + row) * lda + 4 * c;
+        step[i] = C::BK;
+        lds_off[i] = (uint32_t)j * 1024u;
+      } else {
+        const int jb = j - MC::A_CHUNKS;
+        const int k = jb * MC::RPC_B + lane / MC::CPR_B;
+        const int c = (lane % MC::CPR_B) ^ swz_b(k);
+        ptr[i] = B + (int64_t)k * ldb + n0 + 4 * c;
+        step[i] = (int64_t)C::BK * ldb;
+        lds_off[i] = (uint32_t)(MC::A_FLOATS * 4 + jb * 1024);
+      }
+    }
+  }
+
+  // Start the copy of K tile kt into stage st (asynchronous; counted by vmcnt).
+  __device__ inline void issue(int kt, int st) const {
+    const uint32_t stage_base = lds_base + (uint32_t)st * (uint32_t)(MC::STAGE * 4);
+#pragma unroll
+    for (int i = 0; i < MC::D; ++i) {
+      const float* src = ptr[i] + (int64_t)kt * step[i];
+      const uint32_t m0v = __builtin_amdgcn_readfirstlane(stage_base + lds_off[i]);
+      // M0 is reserved by the compiler, which warns about clobbering it.  Nothing else in
+      // these kernels uses M0 (a structural test checks that every M0 write is one of these
+      // copies, immediately followed by its load), so the clobber is safe here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(src), "s"(m0v)
+                   : "memory", "m0");
+#pragma clang diagnostic pop
+    }
+  }
+};
+
+// Wait until at most N copies of this wave are outstanding and this wave's LDS reads have
+// returned.
+template <int N>
+__device__ __forceinline__ void ms_wait() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" : : "n"(N) : "memory");
+}
+
+// Wait until tile l+1 has landed in this wave's copies (the S-2 tiles issued after it may
+// stay in flight) and this wave's LDS reads have returned, then barrier.
+template <class C, int S>
+__device__ __forceinline__ void ms_wait_tile_barrier() {
+  ms_wait<MsCfg<C, S>::D * (S - 2)>();
+  asm volatile("s_barrier" : : : "memory");
+}
+
+template <class C, int S>
+struct LaneViewMs {
+  int a_off;          // float offset of this lane's A row (fm = 0) inside a stage
+  int a_x;            // h ^ swz_a(row): logical chunk 2q+h of the row is at (2q) ^ a_x
+  int b_off[C::FN];   // float offset of B[4h][col(fn)] inside a stage (swizzled)
+
+  __device__ inline void init(int wm, int wn, int lane) {
+    const int h = lane >> 5, l32 = lane & 31;
+    const int row = wm * C::TM + l32;
+    a_off = row * C::BK;
+    a_x = h ^ swz_a<C>(row);
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) {
+      const int col = wn * C::TN + fn * 32 + l32;
+      const int k = 4 * h;
+      b_off[fn] = MsCfg<C, S>::A_FLOATS + k * C::BN + 4 * ((col >> 2) ^ swz_b(k)) + (col & 3);
+    }
+  }
+};
+
+template <class C, int S>
+__device__ inline void read_frag_ms(const float* stage, const LaneViewMs<C, S>& lv, int q,
+                                    Frag<C>& f) {
+  const float* a_ptr = stage + lv.a_off + 4 * ((2 * q) ^ lv.a_x);
+#pragma unroll
+  for (int fm = 0; fm < C::FM; ++fm)
+    f.a[fm] = *reinterpret_cast<const floatx4*>(a_ptr + fm * 32 * C::BK);
+#pragma unroll
+  for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) f.b[fn][t] = stage[lv.b_off[fn] + (8 * q + t) * C::BN];
+}
+
+// One steady-state step of the MS loop for tile l held in stage `st`: start the copy of
+// tile l+S-1 into the stage that tile l-1 used, multiply tile l, and -- at the hand-off,
+// before the second half of tile l's last round -- wait for tile l+1 and pass ONE
+// barrier.  That barrier makes tile l+1 visible to every wave and certifies that every
+// wave has finished reading tile l, whose stage the copy issued in the next step
+// overwrites.  Near the end the copy index is clamped to the last tile (a harmless
+// duplicate into a stage no later tile uses), so every wait keeps S-2 tiles in flight.
+template <class C, int S>
+__device__ __forceinline__ void ms_step(const float* smem, const MsCopy<C, S>& cp,
+                                        const LaneViewMs<C, S>& lv, int l, int k_tiles,
+                                        int st, Frag<C> (&f)[2],
+                                        floatx16 (&acc)[C::FM][C::FN]) {
+  using MC = MsCfg<C, S>;
+  constexpr int R = C::BK / 8;
+  cp.issue(min(l + S - 1, k_tiles - 1), st == 0 ? S - 1 : st - 1);
+  const float* cur = smem + st * MC::STAGE;
+#pragma unroll
+  for (int q = 0; q + 1 < R; ++q) {
+    read_frag_ms(cur, lv, q + 1, f[(q + 1) & 1]);
+    mfma_round<C, 0>(f[q & 1], acc);
+  }
+  mfma_round<C, 1>(f[1], acc);
+  Sched<C>::template rounds_with_reads<0>();
+  sched_group<kSchedMfma, Sched<C>::MQ / 2>();
+  ms_wait_tile_barrier<C, S>();
+  read_frag_ms(smem + (st + 1 == S ? 0 : st + 1) * MC::STAGE, lv, 0, f[0]);
+  mfma_round<C, 2>(f[1], acc);
+  Sched<C>::db_after_barrier();
+}
+
+// The MS K-loop: prologue (tiles 0 .. S-2 in flight, tile 0 landed), steps unrolled S at a
+// time so that every stage address is fixed, the remaining steps one by one, and the
+// last tile (nothing left to copy) peeled off.
+template <class C, int S>
+__device__ inline void k_loop_ms(float* smem, const MsCopy<C, S>& cp,
+                                 const LaneViewMs<C, S>& lv, int k_tiles,
+                                 floatx16 (&acc)[C::FM][C::FN]) {
+  using MC = MsCfg<C, S>;
+  constexpr int R = C::BK / 8;
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t) cp.issue(min(t, k_tiles - 1), t);
+  ms_wait_tile_barrier<C, S>();
+  Frag<C> f[2];
+  read_frag_ms(smem, lv, 0, f[0]);
+  int l = 0;
+  for (; l + S < k_tiles; l += S) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) ms_step<C, S>(smem, cp, lv, l + u, k_tiles, u, f, acc);
+  }
+  for (; l + 1 < k_tiles; ++l) ms_step<C, S>(smem, cp, lv, l, k_tiles, l % S, f, acc);
+  const float* cur = smem + (l % S) * MC::STAGE;  // last tile: nothing left to copy
+#pragma unroll
+  for (int q = 0; q + 1 < R; ++q) {
+    read_frag_ms(cur, lv, q + 1, f[(q + 1) & 1]);
+    mfma_round<C, 0>(f[q & 1], acc);
+  }
+  mfma_round<C, 0>(f[1], acc);
+}
+
+template <class C, int S>
+__global__ void __launch_bounds__(C::NT)
+gemm_f32_ms_kernel(int M, int N, int K, const float* __restrict__ A, int64_t lda,
+                   const float* __restrict__ B, int64_t ldb, float* __restrict__ Cmat,
+                   int64_t ldc, int flags, int k_chunk, int64_t c_split_stride) {
+  using MC = MsCfg<C, S>;
+  __shared__ __attribute__((aligned(1024))) float smem[MC::LDS_FLOATS];
+
+  split_k_range(K, A, B, ldb, Cmat, k_chunk, c_split_stride);
+  TilePos<C> t;
+  t.init(M, N, K, A, lda, B, ldb, flags);
+  floatx16 acc[C::FM][C::FN];
+  zero_acc<C>(acc);
+  const int k_tiles = (K + C::BK - 1) / C::BK;
+  if (k_tiles > 0) {
+    if (t.unguarded()) {
+      MsCopy<C, S> cp;
+      cp.init(smem, t.wave, t.lane, A, lda, B, ldb, t.g.m0, t.g.n0);
+      LaneViewMs<C, S> lv;
+      lv.init(t.wm, t.wn, t.lane);
+      k_loop_ms<C, S>(smem, cp, lv, k_tiles, acc);
+    } else {
+      // Edge, misaligned or K-ragged tiles: the guarded double-buffered loop.
+      TileCopy<C> cp;
+      cp.init(t.tid);
+      LaneView<C> lv;
+      lv.init(t.wm, t.wn, t.lane);
+      k_loop_db<C, true>(smem, cp, lv, t.g, k_tiles, acc);
+    }
+  }
+  store_c<C>(acc, Cmat, ldc, t);
+}
+
+// Stage count per configuration: as many as fit (at most 4) in the 160 KiB of a CU.
+template <class C>
+constexpr int ms_stages() {
+  constexpr int stage_bytes = 4 * (C::BM * C::BK + C::BK * C::BN);
+  return (160 * 1024) / stage_bytes >= 4 ? 4 : (160 * 1024) / stage_bytes;
+}
+
+}  // namespace gemmf32

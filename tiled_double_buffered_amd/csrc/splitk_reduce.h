@@ -1,0 +1,43 @@
+// The split-K reduction kernel of gemmf32.
+#pragma once
+
+#include "gemm_common.h"
+
+namespace gemmf32 {
+
+// ------------------------------------------------------------------------------------
+// Split-K reduction: C[i][j] = P[0][i][j] + P[1][i][j] + ... + P[S-1][i][j], summed in
+// that fixed order, so a split product is deterministic.  P holds S partial products of
+// M x N floats each, rows of N.  A streaming kernel bounded by HBM bandwidth:
+// (S + 1) * 4 * M * N bytes per launch.  VEC: rows of P and C are 16-byte aligned and
+// N % 4 == 0, so each thread moves 4 consecutive columns.
+// ------------------------------------------------------------------------------------
+template <bool VEC>
+__global__ void __launch_bounds__(256)
+gemm_f32_splitk_reduce(int M, int N, int S, const float* __restrict__ P,
+                       float* __restrict__ C, int64_t ldc) {
+  const int64_t mn = (int64_t)M * N;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  if constexpr (VEC) {
+    const int n4 = N / 4;
+    const int64_t total = (int64_t)M * n4;
+    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += stride) {
+      const int64_t i = t / n4;
+      const int64_t j = 4 * (t - i * n4);
+      const int64_t e = i * N + j;
+      floatx4 acc = *reinterpret_cast<const floatx4*>(P + e);
+      for (int sp = 1; sp < S; ++sp) acc += *reinterpret_cast<const floatx4*>(P + sp * mn + e);
+      *reinterpret_cast<floatx4*>(C + i * ldc + j) = acc;
+    }
+  } else {
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < mn; e += stride) {
+      const int64_t i = e / N;
+      const int64_t j = e - i * N;
+      float acc = P[e];
+      for (int sp = 1; sp < S; ++sp) acc += P[sp * mn + e];
+      C[i * ldc + j] = acc;
+    }
+  }
+}
+
+}  // namespace gemmf32
