@@ -14,11 +14,15 @@ Prints ONE JSON line:
                 `traffic` = HBM bytes per launch from the committed rocprofv3 counter
                 summary (null if the kernel source changed since it was taken)
   cpu_baseline  the CPU oracle timed on a bounded row sample of the same product
+  mfma_ceiling  the matrix-core ceiling at the clock the device sustains (a kernel of
+                nothing but FP32 MFMAs) and the headline's fraction of it
   per_shape     single-buffered, double-buffered, multi-stage and dispatched time for
-                every workload shape
+                every workload shape, with torch.matmul (FP32, black box) as context
   parity        the 8192^3 result checked on 4096 seeded positions against the oracle
 
 Also:
+  python bench.py --oracle-table             the CPU oracle's time per workload on all host
+                                             threads and on one (no GPU needed)
   python bench.py --summarize-trace DIR      per-(kernel, grid) average durations from a
                                              rocprofv3 kernel trace (kernel_trace.csv)
   python bench.py --summarize-counters DIR   per-(kernel, grid) average counter values
@@ -245,7 +249,11 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--counter-run", action="store_true")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--oracle-table", action="store_true")
     args = ap.parse_args()
+
+    if args.oracle_table:
+        return oracle_table()
 
     if args.write_traffic:
         return write_traffic(*args.write_traffic)
@@ -272,6 +280,7 @@ def main() -> int:
         return 2
     dev = torch.device("cuda:0")
     lib_version = tdb.gemm_f32_version()
+    torch.backends.cuda.matmul.allow_tf32 = False  # the torch.matmul context stays FP32
 
     def log(*a):
         print(*a, file=sys.stderr, flush=True)
@@ -354,6 +363,17 @@ def main() -> int:
                 "kernel": f"{VARIANT_NAMES[variant]} cfg{cfg}",
                 "launch_ms": round(kernel_ms, 4)}
 
+    # the matrix-core ceiling at the clock this device sustains, measured right after the
+    # headline so that both run warm
+    try:
+        from tiled_double_buffered_amd import peak
+        ceiling = peak.mfma_ceiling(stream=stream)
+        ceiling["headline_frac"] = round(achieved / ceiling["value"], 4)
+        log(f"[bench] matrix-core ceiling {ceiling['value']} TFLOP/s at "
+            f"{ceiling['clock_ghz']} GHz; headline at {ceiling['headline_frac']:.3f} of it")
+    except Exception as exc:
+        ceiling = {"error": repr(exc)}
+
     # ------------------------------------------------------------------ per shape
     def time_call(fn, target_ms=25.0, batches=5):
         fn()
@@ -400,6 +420,8 @@ def main() -> int:
             "db": lambda: tdb.gemm_f32_db(m, n, k, pa, k, pb, n, pc, n, s_ptr),
             "ms": lambda: tdb.gemm_f32_ms(m, n, k, pa, k, pb, n, pc, n, s_ptr),
             "dispatch": lambda: tdb.gemm_f32(m, n, k, pa, k, pb, n, pc, n, s_ptr),
+            # context only: the vendor library through torch, timed as a black box
+            "torch": lambda: torch.matmul(Ad, Bd, out=Cd),
         }
         order = list(fns)
         samples = {v: [] for v in fns}
@@ -422,10 +444,12 @@ def main() -> int:
         entry["dispatch_choice"] = f"{VARIANT_NAMES[dv]} cfg{dc}"
         entry["db_over_sb_speedup"] = round(entry["sb"]["us"] / entry["db"]["us"], 3)
         entry["ms_over_db_speedup"] = round(entry["db"]["us"] / entry["ms"]["us"], 3)
+        entry["dispatch_over_torch_speedup"] = round(entry["torch"]["us"] /
+                                                     entry["dispatch"]["us"], 3)
         per_shape[name] = entry
         log(f"[bench] {name}: sb {entry['sb']['us']} us, db {entry['db']['us']} us, "
             f"ms {entry['ms']['us']} us, dispatch {entry['dispatch']['us']} us "
-            f"({entry['dispatch']['tflops']} TFLOP/s)")
+            f"({entry['dispatch']['tflops']} TFLOP/s), torch.matmul {entry['torch']['us']} us")
         if name != HEADLINE:
             del Ad, Bd, Cd
 
@@ -478,12 +502,42 @@ def main() -> int:
                    "dispatch": roofline["kernel"], "library": lib_version},
         "frac_peak": round(value / PEAK_FP32_MFMA_TFLOPS, 4),
         "roofline": roofline,
+        "mfma_ceiling": ceiling,
         "cpu_baseline": cpu_baseline,
         "metric_shapes": metric_shapes,
         "per_shape": per_shape,
         "parity": parity,
     }
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def oracle_table() -> int:
+    """Time the CPU oracle (C64 and Bnd in FP64) on every workload, in full up to 4096^3
+    and on the 4096 seeded positions at 8192^3, on all host threads and on one thread.
+    Prints one JSON object; needs no GPU."""
+    import oracle
+    import tdb_inputs as ti
+    threads = oracle.max_threads()
+    rows = []
+    for name, (m, n, k, seed) in ti.WORKLOADS.items():
+        a, b = ti.workload_inputs(m, n, k, seed)
+        full = m * n * k <= 4096 ** 3
+        row = {"workload": name, "M": m, "N": n, "K": k,
+               "what": "full product" if full else "4096 seeded positions"}
+        for t in (threads, 1):
+            oracle.set_threads(t)
+            t0 = time.perf_counter()
+            if full:
+                oracle.gemm_f64(a, b)
+            else:
+                ri, rj = ti.sample_positions(seed, m, n, 4096)
+                oracle.gemm_f64_sampled(a, b, ri, rj)
+            row[f"seconds_{t}_threads"] = round(time.perf_counter() - t0, 4)
+        rows.append(row)
+        print(f"[oracle] {row}", file=sys.stderr, flush=True)
+    oracle.set_threads(threads)
+    print(json.dumps({"cpu": _cpu_model(), "threads": threads, "rows": rows}), flush=True)
     return 0
 
 

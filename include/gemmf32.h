@@ -184,6 +184,24 @@ const char *gemm_f32_strerror(int code);
 /* Library version string, e.g. "gemmf32 0.1.0 gfx950". */
 const char *gemm_f32_version(void);
 
+/* Measurement aid, not a GEMM: the FP32 matrix-core ceiling at the clock the device runs
+ * at.  The pages price their kernels against nothing but time; this call gives the
+ * attainable matrix-instruction rate of this device, against which a GEMM's TFLOP/s can
+ * be read besides the 2.4 GHz specification peak.
+ *
+ * Enqueues one kernel on `stream`: `blocks` workgroups of 4 waves (256 lanes), each wave
+ * issuing 16 * iters v_mfma_f32_32x32x2_f32 instructions (4096 FLOP each) on register
+ * operands and nothing else in its loop.  FLOP per launch = blocks * 4 * 16 * iters * 4096.
+ *   out  device buffer of blocks * 256 floats (one per lane, written; keeps the work live)
+ *   rec  device buffer of blocks * 8 uint64 (written): for wave w = 4 * block + wave-in-
+ *        block, rec[2w] = shader-clock cycles of its loop (s_memtime) and rec[2w+1] =
+ *        100 MHz wall-clock ticks of the same interval (s_memrealtime); their ratio
+ *        times 0.1 GHz is the shader clock.
+ * Errors: GEMMF32_ERR_TOO_LARGE if blocks is outside 1..65536 or iters outside 0..2^20;
+ * GEMMF32_ERR_NULL_PTR / GEMMF32_ERR_MISALIGNED for out (4-byte) or rec (8-byte);
+ * GEMMF32_ERR_HIP if the launch fails.  Validation precedes any HIP call. */
+int gemm_f32_peak_probe(int blocks, int iters, float *out, uint64_t *rec, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

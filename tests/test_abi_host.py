@@ -206,3 +206,17 @@ def test_splitk_validation_before_launch():
     assert f(M, N, K, PA, K, PB, N, PC, N, 4, PC - 4 * 100, need) == tdb.ERR_ALIAS  # C
     assert f(M, N, K, PA, K - 1, PB, N, PC, N, 4, PW, need) == tdb.ERR_BAD_LD   # lda < K
     assert f(0, N, K, 0, K, 0, N, 0, N, 4, 0, 0) == tdb.OK                    # empty: no-op
+
+
+def test_peak_probe_validation_before_launch():
+    """The matrix-core ceiling probe rejects bad arguments without launching."""
+    f = tdb.gemm_f32_peak_probe
+    PR = 0x7F4000000000
+    assert f(0, 16, PA, PR) == tdb.ERR_TOO_LARGE
+    assert f(65537, 16, PA, PR) == tdb.ERR_TOO_LARGE
+    assert f(4, -1, PA, PR) == tdb.ERR_TOO_LARGE
+    assert f(4, (1 << 20) + 1, PA, PR) == tdb.ERR_TOO_LARGE
+    assert f(4, 16, 0, PR) == tdb.ERR_NULL_PTR
+    assert f(4, 16, PA, 0) == tdb.ERR_NULL_PTR
+    assert f(4, 16, PA + 2, PR) == tdb.ERR_MISALIGNED
+    assert f(4, 16, PA, PR + 4) == tdb.ERR_MISALIGNED

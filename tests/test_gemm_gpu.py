@@ -358,3 +358,27 @@ def test_raster_order_does_not_change_results(monkeypatch):
             assert torch.equal(_run(Ad, Bd, v), r), (setting, v)
         for r, v in zip(ref2, ("sb", "db")):
             assert torch.equal(_run(A2d, B2d, v, 3), r), (setting, v)
+
+
+def test_peak_probe_measures_the_matrix_pipe():
+    """The ceiling probe runs, reports a plausible shader clock and per-wave cycle counts
+    of at least one v_mfma_f32_32x32x2_f32 per 64 clocks (256 workgroups: one to three
+    waves per SIMD, depending on how the dispatcher places them), and the attained rate
+    stays below what 64 clocks per instruction allow at the measured clock."""
+    import torch
+    blocks, iters = 256, 64
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    rec = torch.zeros(blocks * 8, dtype=torch.int64, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    assert tdb.gemm_f32_peak_probe(blocks, iters, out.data_ptr(), rec.data_ptr(), s) == tdb.OK
+    torch.cuda.synchronize()
+    r = rec.view(-1, 2).cpu().numpy().astype(np.float64)
+    assert (r > 0).all()
+    ghz = r[:, 0].sum() / r[:, 1].sum() * 0.1
+    assert 0.5 < ghz < 3.5, ghz
+    per_mfma = r[:, 0] / (16 * iters)
+    assert per_mfma.min() > 60.0 and per_mfma.max() < 64.0 * 3 * 1.2, per_mfma
+    assert torch.isfinite(out).all()
+    from tiled_double_buffered_amd import peak
+    c = peak.mfma_ceiling(warm_s=0.05, launches=3)
+    assert 0.5 * c["at_clock_tflops"] < c["value"] <= 1.02 * c["at_clock_tflops"], c

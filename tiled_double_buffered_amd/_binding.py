@@ -50,6 +50,7 @@ SIGNATURES = {
     "gemm_f32_last_hip_error": (_int, []),
     "gemm_f32_strerror": (ctypes.c_char_p, [_int]),
     "gemm_f32_version": (ctypes.c_char_p, []),
+    "gemm_f32_peak_probe": (_int, [_int, _int, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -156,6 +157,10 @@ def gemm_f32_strerror(code) -> str:
 
 def gemm_f32_version() -> str:
     return load().gemm_f32_version().decode()
+
+
+def gemm_f32_peak_probe(blocks, iters, out, rec, stream=None) -> int:
+    return load().gemm_f32_peak_probe(blocks, iters, out, rec, stream)
 
 
 strerror = gemm_f32_strerror

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 SOURCES = [os.path.join(CSRC, "gemm_f32.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("gemm_common.h", "kernels_sb_db.h", "kernels_ms.h",
-                                            "splitk_reduce.h", "dispatch_table.h")]
+                                            "splitk_reduce.h", "dispatch_table.h",
+                                            "mfma_peak.h")]
 DEPS = SOURCES + HEADERS + [os.path.join(INCLUDE, "gemmf32.h")]
 LIB = os.path.join(PKG, "libgemmf32.so")
 BUILD_DIR = os.path.join(ROOT, "_build")

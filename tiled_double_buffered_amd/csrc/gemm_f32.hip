@@ -31,6 +31,7 @@
 #include "gemm_common.h"
 #include "kernels_ms.h"
 #include "kernels_sb_db.h"
+#include "mfma_peak.h"
 #include "splitk_reduce.h"
 
 namespace gemmf32 {
@@ -366,5 +367,20 @@ const char* gemm_f32_strerror(int code) {
 }
 
 const char* gemm_f32_version(void) { return "gemmf32 0.1.0 gfx950"; }
+
+int gemm_f32_peak_probe(int blocks, int iters, float* out, uint64_t* rec, void* stream) {
+  if (blocks < 1 || blocks > kPeakMaxBlocks || iters < 0 || iters > kPeakMaxIters)
+    return GEMMF32_ERR_TOO_LARGE;
+  if (out == nullptr || rec == nullptr) return GEMMF32_ERR_NULL_PTR;
+  if (((uintptr_t)out & 3u) != 0 || ((uintptr_t)rec & 7u) != 0) return GEMMF32_ERR_MISALIGNED;
+  void* args[] = {&iters, &out, &rec};
+  hipError_t err = hipLaunchKernel((const void*)&gemm_f32_peak_kernel, dim3(blocks),
+                                   dim3(kPeakThreads), args, 0, (hipStream_t)stream);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return GEMMF32_ERR_HIP;
+  }
+  return GEMMF32_OK;
+}
 
 }  // extern "C"
