@@ -262,10 +262,15 @@ struct Sched {
   static constexpr int W = C::A_PER_T + C::B_PER_T;    // 16-byte LDS stores per tile
   static constexpr int D = C::FM + 2 * C::FN;          // LDS read instructions per round
 
+  // MFMAs kept between the last LDS store of a tile and the barrier that publishes it,
+  // where a round has enough of them: the wait for the stores before the barrier then
+  // finds them complete instead of stalling the matrix pipe for their latency.
+  static constexpr int TAIL = MQ / 2 >= 16 ? 4 : 0;
+
   // Double-buffered, from the top of an iteration up to the barrier: round 0 carries the
   // global loads of tile l+1 and the LDS reads of round 1; middle rounds carry the reads
   // of the next round; the first half of the last round carries the LDS stores of tile
-  // l+1 into the idle slot.
+  // l+1 into the idle slot, then TAIL MFMAs.
   template <int Q = 0>
   static __device__ __forceinline__ void db_before_barrier() {
     if constexpr (Q == 0) {
@@ -277,13 +282,16 @@ struct Sched {
       sched_interleave<kSchedDsRead, D, MQ>();
       db_before_barrier<Q + 1>();
     } else {
-      sched_interleave<kSchedDsWrite, W, MQ / 2>();
+      sched_interleave<kSchedDsWrite, W, MQ / 2 - TAIL>();
+      sched_group<kSchedMfma, TAIL>();
     }
   }
-  // After the barrier: the first reads of tile l+1, then the rest of tile l's last round.
+  // After the barrier: the rest of tile l's last round with the first reads of tile l+1
+  // spread over it, an MFMA first so that the matrix pipe restarts at once (its operands
+  // are already in registers).
   static __device__ __forceinline__ void db_after_barrier() {
-    sched_group<kSchedDsRead, D>();
-    sched_group<kSchedMfma, MQ - MQ / 2>();
+    sched_group<kSchedMfma, 1>();
+    sched_interleave<kSchedDsRead, D, MQ - MQ / 2 - 1>();
   }
   // Rounds whose MFMAs each carry the LDS reads of the following round.
   template <int Q = 0>

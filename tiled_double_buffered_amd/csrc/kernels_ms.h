@@ -188,7 +188,13 @@ __device__ __forceinline__ void ms_step(const float* smem, const MsCopy<C, S>& c
   mfma_round<C, 1>(f[1], acc);
   Sched<C>::template rounds_with_reads<0>();
   sched_group<kSchedMfma, Sched<C>::MQ / 2>();
+  // With few MFMAs per round (small wave tiles) the two sides of the barrier are kept
+  // apart, as in the double-buffered step; with many, the compiler's own placement
+  // measured faster.
+  constexpr bool kFence = Sched<C>::MQ <= 8;
+  if constexpr (kFence) __builtin_amdgcn_sched_barrier(0);
   ms_wait_tile_barrier<C, S>();
+  if constexpr (kFence) __builtin_amdgcn_sched_barrier(0);
   read_frag_ms(smem + (st + 1 == S ? 0 : st + 1) * MC::STAGE, lv, 0, f[0]);
   mfma_round<C, 2>(f[1], acc);
   Sched<C>::db_after_barrier();

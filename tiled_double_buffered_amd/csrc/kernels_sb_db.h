@@ -23,8 +23,15 @@ __device__ __forceinline__ void db_step(const float* cur, float* nxt, TileCopy<C
   }
   mfma_round<C, 1>(f[1], acc);
   cp.store(nxt);
-  if constexpr (!GUARD) Sched<C>::template db_before_barrier<0>();
+  // The scheduling hints describe the two sides of the barrier separately; the fences
+  // (sched_barrier) keep the compiler from moving register-only MFMAs across it, which
+  // would undo the tail of MFMAs placed after the LDS stores.
+  if constexpr (!GUARD) {
+    Sched<C>::template db_before_barrier<0>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
   __syncthreads();
+  if constexpr (!GUARD) __builtin_amdgcn_sched_barrier(0);
   read_frag(nxt, lv, 0, f[0]);
   mfma_round<C, 2>(f[1], acc);
   if constexpr (!GUARD) Sched<C>::db_after_barrier();
