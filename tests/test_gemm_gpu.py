@@ -317,6 +317,38 @@ def test_offsets_beyond_2gib():
     del C
 
 
+@pytest.mark.parametrize("which", ["A", "B"])
+def test_row_stride_beyond_32bit_tile_offsets(which):
+    """A row stride so large that the byte offsets inside one tile pass 2^32 (more than
+    4 GiB between a tile's first and last row): the 16-byte copies address a tile with a
+    32-bit offset from its first element, so such operands must take the element-wise
+    path, and the result must still be exact to the bound.  Each case allocates about
+    4.2 GiB on the device."""
+    M, N, K = 64, 256, 64
+    A, B = ti.workload_inputs(M, N, K, 9200)
+    C64, Bnd = oracle.gemm_f64(A, B)
+    if which == "A":
+        ld = (1 << 24) + 4                       # 64 rows x ld x 4 B > 2^32
+        big = torch.empty((M - 1) * ld + K, device=DEV)
+        Ad = big.as_strided((M, K), (ld, 1))
+        Ad.copy_(torch.from_numpy(A))
+        Bd = _dev(B)
+    else:
+        K = 32                                   # one K tile of 32 rows x ld x 4 B > 2^32
+        A, B = ti.workload_inputs(M, N, K, 9201)
+        C64, Bnd = oracle.gemm_f64(A, B)
+        ld = (1 << 25) + 4
+        big = torch.empty((K - 1) * ld + N, device=DEV)
+        Bd = big.as_strided((K, N), (ld, 1))
+        Bd.copy_(torch.from_numpy(B))
+        Ad = _dev(A)
+    for v, cfg in (("auto", -1), ("sb", 6), ("db", 6), ("ms", 6), ("db", 1)):
+        _say(f"[ld32] {which} ld={ld} {v} cfg={cfg}")
+        assert _ratio(_run(Ad, Bd, v, cfg), C64, Bnd) <= 1.0, (which, v, cfg)
+    del big
+    torch.cuda.empty_cache()
+
+
 def test_wide_dynamic_range():
     """Rows of A and columns of B scaled by powers of two from 2^-30 to 2^30: every product
     stays a normal FP32 number and the bound is relative, so nothing may lose accuracy."""

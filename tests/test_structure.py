@@ -154,3 +154,23 @@ def test_every_kernel_has_no_scratch():
     assert any("splitk_reduce" in n for n in meta)
     for name, m in meta.items():
         assert m["private_segment_fixed_size"] == 0, name
+
+
+def test_unguarded_copies_are_buffer_loads_without_vector_address_math(kernels):
+    """The register-staged kernels' unguarded K-loop (the one with no element-wise
+    guarded loads) copies with buffer loads from a scalar base plus fixed per-thread
+    offsets: no 64-bit vector address additions are left in it."""
+    seen = 0
+    for name, k in kernels.items():
+        if k["ms"]:
+            continue
+        fast = [ins for ins in _loop_blocks(k["body"]).values()
+                if _count_barriers(ins) and
+                not any(re.match(r"global_load_dword\b", t) for t in ins)]
+        assert fast, k["cfg"]
+        for ins in fast:
+            assert any(t.startswith("buffer_load_dwordx4") for t in ins), (k["cfg"], k["kind"])
+            assert not any(t.startswith("global_load_dwordx4") for t in ins), k["cfg"]
+            assert not any(t.startswith("v_lshl_add_u64") for t in ins), (k["cfg"], k["kind"])
+        seen += 1
+    assert seen >= 3

@@ -87,6 +87,12 @@ __device__ inline void tile_coords(int tiles_m, int tiles_n, int flags, int& tm,
   tn = in_group / rows;
 }
 
+// Buffer descriptor of the fast copies: a raw byte buffer (stride 0) whose range check
+// admits every 32-bit offset below kBufferRange; word 3 selects 32-bit data, the
+// untyped-load setting of this GPU family.
+constexpr uint32_t kBufferRange = 0xFFFFFFF0u;
+constexpr int kBufferFlags = 0x00020000;
+
 // ------------------------------------------------------------------------------------
 // The workgroup's copy of one K tile: global memory -> registers -> LDS.
 // Thread t moves groups g = t + p * NT (p = 0 .. PER_T-1); group g of A is row
@@ -99,28 +105,47 @@ struct TileCopy {
 
   // Per-thread coordinates inside the tile.
   int a_row, a_col, b_row, b_col;
+  // Byte offsets of this thread's 16-byte groups from the tile's first element; they are
+  // the same for every K tile (see the fast path below).
+  uint32_t a_off[C::A_PER_T], b_off[C::B_PER_T];
 
-  __device__ inline void init(int tid) {
+  __device__ inline void init(int tid, int64_t lda, int64_t ldb) {
     a_row = tid / C::A_GROUPS_PER_ROW;
     a_col = 4 * (tid % C::A_GROUPS_PER_ROW);
     b_row = tid / C::B_GROUPS_PER_ROW;
     b_col = 4 * (tid % C::B_GROUPS_PER_ROW);
+#pragma unroll
+    for (int i = 0; i < C::A_PER_T; ++i)
+      a_off[i] = (uint32_t)(((int64_t)(a_row + i * C::A_ROWS_PER_PASS) * lda + a_col) * 4);
+#pragma unroll
+    for (int i = 0; i < C::B_PER_T; ++i)
+      b_off[i] = (uint32_t)(((int64_t)(b_row + i * C::B_ROWS_PER_PASS) * ldb + b_col) * 4);
   }
 
   // Fast path: the whole tile lies inside the matrices and rows are 16-byte aligned.
+  // The copies are buffer loads: the tile's first element is a workgroup-uniform base (a
+  // buffer descriptor in scalar registers, advanced by scalar arithmetic per K tile) and
+  // each thread adds its fixed 32-bit offset.  Plain global loads would need a 64-bit
+  // vector address add per load and per tile, and that vector arithmetic measurably slows
+  // the matrix instructions it is interleaved with.  The host takes this path only when
+  // every offset inside a tile fits in 32 bits.
+  static __device__ inline floatx4 buffer_load16(const float* base, uint32_t off) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(base), (short)0, (int)kBufferRange, kBufferFlags);
+    return __builtin_bit_cast(floatx4,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  }
   __device__ inline void load_a_fast(const float* __restrict__ A, int64_t lda, int m0,
                                      int k0) {
-    const float* p = A + (int64_t)(m0 + a_row) * lda + (k0 + a_col);
+    const float* base = A + (int64_t)m0 * lda + k0;
 #pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i)
-      ra[i] = *reinterpret_cast<const floatx4*>(p + (int64_t)(i * C::A_ROWS_PER_PASS) * lda);
+    for (int i = 0; i < C::A_PER_T; ++i) ra[i] = buffer_load16(base, a_off[i]);
   }
   __device__ inline void load_b_fast(const float* __restrict__ B, int64_t ldb, int n0,
                                      int k0) {
-    const float* p = B + (int64_t)(k0 + b_row) * ldb + (n0 + b_col);
+    const float* base = B + (int64_t)k0 * ldb + n0;
 #pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i)
-      rb[i] = *reinterpret_cast<const floatx4*>(p + (int64_t)(i * C::B_ROWS_PER_PASS) * ldb);
+    for (int i = 0; i < C::B_PER_T; ++i) rb[i] = buffer_load16(base, b_off[i]);
   }
 
   // Guarded path: element by element; anything outside M x K (A) or K x N (B) reads as

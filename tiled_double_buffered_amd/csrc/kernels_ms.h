@@ -253,7 +253,7 @@ gemm_f32_ms_kernel(int M, int N, int K, const float* __restrict__ A, int64_t lda
     } else {
       // Edge, misaligned or K-ragged tiles: the guarded double-buffered loop.
       TileCopy<C> cp;
-      cp.init(t.tid);
+      cp.init(t.tid, lda, ldb);
       LaneView<C> lv;
       lv.init(t.wm, t.wn, t.lane);
       k_loop_db<C, true>(smem, cp, lv, t.g, k_tiles, acc);

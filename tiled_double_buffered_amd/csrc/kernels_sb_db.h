@@ -146,7 +146,7 @@ gemm_f32_tile_kernel(int M, int N, int K, const float* __restrict__ A, int64_t l
   floatx16 acc[C::FM][C::FN];
   zero_acc<C>(acc);
   TileCopy<C> cp;
-  cp.init(t.tid);
+  cp.init(t.tid, lda, ldb);
   LaneView<C> lv;
   lv.init(t.wm, t.wn, t.lane);
   const int k_tiles = (K + C::BK - 1) / C::BK;
