@@ -124,7 +124,7 @@ def test_mfma_count_matches_tile(kernels):
 
 
 def test_multistage_copies_and_m0(kernels):
-    """The multi-stage kernels copy with global_load_lds_dwordx4 only, each copy right
+    """The multi-stage kernels copy with buffer_load_dwordx4 ... lds only, each copy right
     after the s_mov_b32 that sets its LDS destination in M0, and nothing else touches M0.
     The per-tile copy count is (BM*BK + BK*BN) * 4 bytes / 1 KiB / waves, issued S-1 times
     in the prologue, S times in the unrolled steps and once in the remainder step."""
@@ -132,16 +132,18 @@ def test_multistage_copies_and_m0(kernels):
     for name, k in kernels.items():
         lines = [t.strip() for t in k["body"].split("\n")]
         m0_lines = [i for i, t in enumerate(lines) if re.search(r"\bm0\b", t)]
+        dma = [t for t in lines if re.match(r"buffer_load_dwordx4\b.*\blds$", t)]
         if not k["ms"]:
-            assert "global_load_lds" not in k["body"], k["cfg"]
+            assert not dma and "global_load_lds" not in k["body"], k["cfg"]
             continue
         seen += 1
         for i in m0_lines:
             assert lines[i].startswith("s_mov_b32 m0,"), (k["cfg"], lines[i])
-            assert lines[i + 1].startswith("global_load_lds_dwordx4"), (k["cfg"], lines[i + 1])
+            assert re.match(r"buffer_load_dwordx4\b.*\blds$", lines[i + 1]), \
+                (k["cfg"], lines[i + 1])
         bm, bn, bk, wm, wn = k["cfg"]
         per_wave = (bm * bk + bk * bn) * 4 // 1024 // (wm * wn)
-        n = len(re.findall(r"\bglobal_load_lds_dwordx4\b", k["body"]))
+        n = len(dma)
         # issue sites: S-1 in the prologue, S in the unrolled steps, 1 in the remainder step
         assert n == per_wave * 2 * k["stages"], (k["cfg"], n, per_wave, k["stages"])
         assert len(m0_lines) == n

@@ -24,25 +24,25 @@ struct DispatchRow {
 };
 
 static const DispatchRow kDispatch[] = {
-    {128, 128, 128, 2, 6, 7, 6, 6},  // sb 4.45 us, db 4.42 us, ms 4.51 us
-    {127, 193, 61, 2, 6, 6, 6, 6},  // sb 5.23 us, db 5.03 us, ms 5.10 us
-    {513, 257, 129, 2, 6, 6, 6, 6},  // sb 8.86 us, db 7.93 us, ms 8.04 us
-    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.76 us, db 19.71 us, ms 18.91 us
-    {256, 1024, 128, 2, 6, 7, 6, 6},  // sb 4.72 us, db 4.68 us, ms 4.76 us
-    {1024, 128, 256, 3, 6, 7, 6, 6},  // sb 7.10 us, db 6.65 us, ms 6.60 us
-    {4096, 4096, 4096, 2, 1, 9, 1, 8},  // sb 991.23 us, db 916.88 us, ms 934.18 us
-    {8192, 8192, 8192, 2, 1, 9, 1, 8},  // sb 8092.22 us, db 7260.77 us, ms 7386.64 us
-    {256, 256, 256, 3, 6, 7, 6, 6},  // sb 7.07 us, db 6.61 us, ms 6.57 us
-    {512, 512, 512, 3, 6, 7, 6, 6},  // sb 12.22 us, db 10.83 us, ms 10.50 us
-    {2048, 2048, 2048, 2, 4, 7, 4, 3},  // sb 139.70 us, db 121.76 us, ms 125.62 us
-    {6144, 6144, 6144, 2, 4, 4, 4, 3},  // sb 3456.96 us, db 3189.65 us, ms 3238.56 us
-    {64, 4096, 4096, 3, 6, 7, 6, 6},  // sb 96.27 us, db 69.05 us, ms 64.65 us
-    {4096, 4096, 512, 2, 0, 9, 0, 9},  // sb 133.19 us, db 125.99 us, ms 128.76 us
-    {2048, 8192, 2048, 2, 0, 9, 0, 8},  // sb 502.22 us, db 466.38 us, ms 474.34 us
-    {16, 4096, 4096, 2, 7, 7, 7, 7},  // sb 120.90 us, db 101.65 us, ms 102.15 us
-    {32, 4096, 4096, 3, 10, 7, 10, 10},  // sb 123.10 us, db 73.21 us, ms 65.14 us
-    {128, 4096, 4096, 3, 6, 7, 6, 6},  // sb 96.44 us, db 69.26 us, ms 64.88 us
-    {32, 8192, 8192, 3, 10, 7, 10, 10},  // sb 247.14 us, db 150.22 us, ms 127.74 us
+    {128, 128, 128, 2, 6, 7, 6, 6},  // sb 4.65 us, db 4.28 us, ms 4.48 us
+    {127, 193, 61, 2, 6, 6, 6, 6},  // sb 5.24 us, db 5.04 us, ms 5.05 us
+    {513, 257, 129, 3, 6, 6, 6, 6},  // sb 8.96 us, db 7.80 us, ms 7.79 us
+    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.49 us, db 18.24 us, ms 17.93 us
+    {256, 1024, 128, 2, 6, 7, 6, 6},  // sb 4.85 us, db 4.47 us, ms 4.70 us
+    {1024, 128, 256, 2, 6, 7, 6, 6},  // sb 7.16 us, db 6.27 us, ms 6.45 us
+    {4096, 4096, 4096, 2, 1, 7, 1, 3},  // sb 953.50 us, db 903.45 us, ms 914.58 us
+    {8192, 8192, 8192, 2, 2, 3, 2, 3},  // sb 7407.52 us, db 7166.92 us, ms 7202.52 us
+    {256, 256, 256, 2, 6, 7, 6, 6},  // sb 7.13 us, db 6.25 us, ms 6.41 us
+    {512, 512, 512, 2, 6, 7, 6, 6},  // sb 12.23 us, db 10.03 us, ms 10.05 us
+    {2048, 2048, 2048, 2, 3, 6, 3, 6},  // sb 124.48 us, db 117.82 us, ms 120.52 us
+    {6144, 6144, 6144, 2, 4, 4, 4, 3},  // sb 3171.01 us, db 3051.21 us, ms 3057.85 us
+    {64, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.21 us, db 64.88 us, ms 61.00 us
+    {4096, 4096, 512, 2, 2, 9, 2, 3},  // sb 128.32 us, db 122.37 us, ms 124.91 us
+    {2048, 8192, 2048, 2, 2, 7, 2, 3},  // sb 484.53 us, db 457.29 us, ms 462.59 us
+    {16, 4096, 4096, 2, 10, 7, 10, 10},  // sb 115.59 us, db 98.35 us, ms 99.30 us
+    {32, 4096, 4096, 3, 10, 10, 10, 10},  // sb 120.45 us, db 69.07 us, ms 63.05 us
+    {128, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.45 us, db 64.80 us, ms 61.20 us
+    {32, 8192, 8192, 3, 10, 7, 10, 10},  // sb 242.10 us, db 143.74 us, ms 123.84 us
 };
 
 static inline double dispatch_log2(int64_t x) { return x > 0 ? std::log2((double)x) : -1.0; }
@@ -83,17 +83,17 @@ struct SplitRow {
 };
 
 static const SplitRow kSplitK[] = {
-    {16, 4096, 4096, 8},  // 1: 101.4, 2: 54.6, 4: 31.4, 8: 28.9, 16: 33.7
-    {32, 4096, 4096, 8},  // 1: 65.3, 2: 36.7, 4: 23.0, 8: 19.8, 16: 32.8
-    {64, 4096, 4096, 4},  // 1: 64.8, 2: 37.0, 4: 23.5, 8: 26.7, 16: 31.3
-    {128, 4096, 4096, 2},  // 1: 64.9, 2: 38.4, 4: 40.6, 8: 43.7, 16: 47.7
-    {32, 8192, 8192, 4},  // 1: 127.7, 2: 68.4, 4: 46.2, 8: 50.3, 16: 56.3
-    {64, 8192, 8192, 2},  // 1: 128.2, 2: 72.7, 4: 76.5, 8: 81.7, 16: 88.5
-    {256, 256, 8192, 16},  // 1: 126.2, 2: 66.9, 4: 36.6, 8: 22.7, 16: 17.6
-    {512, 512, 8192, 4},  // 1: 127.0, 2: 67.6, 4: 39.1, 8: 40.9, 16: 45.6
-    {1024, 1024, 1024, 1},  // 1: 18.9, 2: 25.7, 4: 26.9, 8: 31.3, 16: 38.7
-    {2048, 2048, 2048, 1},  // 1: 122.1, 2: 134.1, 4: 140.7, 8: 157.1, 16: 190.4
-    {4096, 4096, 4096, 1},  // 1: 924.3, 2: 966.0, 4: 1018.1, 8: 1104.9, 16: 1292.7
+    {16, 4096, 4096, 8},  // 1: 99.6, 2: 53.7, 4: 30.6, 8: 27.5, 16: 30.9
+    {32, 4096, 4096, 8},  // 1: 62.9, 2: 35.4, 4: 22.1, 8: 19.3, 16: 29.8
+    {64, 4096, 4096, 4},  // 1: 60.7, 2: 34.7, 4: 21.7, 8: 24.4, 16: 26.9
+    {128, 4096, 4096, 2},  // 1: 60.9, 2: 35.5, 4: 36.6, 8: 38.4, 16: 46.5
+    {32, 8192, 8192, 4},  // 1: 123.8, 2: 66.5, 4: 46.3, 8: 48.2, 16: 54.8
+    {64, 8192, 8192, 2},  // 1: 124.0, 2: 66.0, 4: 68.8, 8: 74.7, 16: 82.5
+    {256, 256, 8192, 16},  // 1: 118.2, 2: 62.7, 4: 34.6, 8: 21.7, 16: 16.9
+    {512, 512, 8192, 4},  // 1: 118.8, 2: 63.6, 4: 35.9, 8: 37.8, 16: 43.1
+    {1024, 1024, 1024, 1},  // 1: 18.0, 2: 24.7, 4: 26.1, 8: 31.1, 16: 38.5
+    {2048, 2048, 2048, 1},  // 1: 117.9, 2: 128.6, 4: 138.1, 8: 157.5, 16: 199.8
+    {4096, 4096, 4096, 1},  // 1: 903.9, 2: 946.6, 4: 988.7, 8: 1096.1, 16: 1284.7
 };
 
 static inline int select_splits(int64_t M, int64_t N, int64_t K) {

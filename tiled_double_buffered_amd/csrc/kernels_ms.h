@@ -14,9 +14,9 @@ namespace gemmf32 {
 // that its platform lost its asynchronous copy engine, so its double buffering overlaps
 // copies and math only through instruction-level parallelism, and it names the CUDA
 // analogue: a multi-stage asynchronous-copy pipeline.  gfx950 has the asynchronous copy:
-// global_load_lds_dwordx4 moves 16 bytes per lane from global memory straight into LDS
-// (lane L's bytes land at M0 + 16*L), with no registers in between and completion
-// tracked by vmcnt.  Tiles l+1 .. l+S-1 are in flight while tile l is multiplied.
+// buffer_load_dwordx4 with the lds flag moves 16 bytes per lane from global memory
+// straight into LDS (lane L's bytes land at M0 + 16*L), with no registers in between and
+// completion tracked by vmcnt.  Tiles l+1 .. l+S-1 are in flight while tile l is multiplied.
 //
 // LDS layout of a stage (no padding; XOR swizzle at 16-byte-chunk granularity):
 //   A part: BM rows of BK floats;  chunk c of row r is stored at chunk c ^ swz_a(r)
@@ -64,52 +64,76 @@ __device__ __forceinline__ int swz_a(int row) {
 }
 __device__ __forceinline__ int swz_b(int k) { return ((k >> 2) & 1) << 3; }
 
+// The four descriptor words of a raw buffer starting at `base` (range and flags as for the
+// register-staged copies), for the inline-assembly copies below.
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int32x4 buffer_words(const float* base) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  int32x4 r;
+  r[0] = (int)(uint32_t)b;
+  r[1] = (int)(uint32_t)(b >> 32);
+  r[2] = (int)kBufferRange;
+  r[3] = kBufferFlags;
+  return r;
+}
+
 template <class C, int S>
 struct MsCopy {
   using MC = MsCfg<C, S>;
-  const float* ptr[MC::D];  // this lane's source for tile 0
-  int64_t step[MC::D];      // floats between consecutive K tiles
+  uint32_t off[MC::D];      // this lane's byte offset from its operand's tile origin
+  bool from_a[MC::D];       // copy i fills part of the A tile (uniform per wave)
   uint32_t lds_off[MC::D];  // byte offset of the wave's 1 KiB inside a stage
   uint32_t lds_base;        // LDS byte address of stage 0
+  const float* a_org;       // A + m0 * lda
+  const float* b_org;       // B + n0
+  int64_t ldb;
 
   __device__ inline void init(const float* smem, int wave, int lane, const float* A,
-                              int64_t lda, const float* B, int64_t ldb, int m0, int n0) {
+                              int64_t lda, const float* B, int64_t ldb_, int m0, int n0) {
     lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_float*)smem);
+    a_org = A + (int64_t)m0 * lda;
+    b_org = B + n0;
+    ldb = ldb_;
 #pragma unroll
     for (int i = 0; i < MC::D; ++i) {
       const int j = wave + i * MC::WAVES;  // which 1 KiB of the stage this copy fills
+      from_a[i] = j < MC::A_CHUNKS;
       if (j < MC::A_CHUNKS) {
         const int row = j * MC::RPC_A + lane / MC::CPR_A;
         const int c = (lane % MC::CPR_A) ^ swz_a<C>(row);
-        ptr[i] = A + (int64_t)(m0 + row) * lda + 4 * c;
-        step[i] = C::BK;
+        off[i] = (uint32_t)(((int64_t)row * lda + 4 * c) * 4);
         lds_off[i] = (uint32_t)j * 1024u;
       } else {
         const int jb = j - MC::A_CHUNKS;
         const int k = jb * MC::RPC_B + lane / MC::CPR_B;
         const int c = (lane % MC::CPR_B) ^ swz_b(k);
-        ptr[i] = B + (int64_t)k * ldb + n0 + 4 * c;
-        step[i] = (int64_t)C::BK * ldb;
+        off[i] = (uint32_t)(((int64_t)k * ldb + 4 * c) * 4);
         lds_off[i] = (uint32_t)(MC::A_FLOATS * 4 + jb * 1024);
       }
     }
   }
 
-  // Start the copy of K tile kt into stage st (asynchronous; counted by vmcnt).
+  // Start the copy of K tile kt into stage st (asynchronous; counted by vmcnt).  The
+  // sources are buffer loads: a descriptor per operand and K tile, built from the tile's
+  // origin in scalar registers, plus this lane's fixed 32-bit offset, so no vector address
+  // arithmetic runs per copy.  (The host takes this path only when every offset inside a
+  // tile fits in 32 bits.)
   __device__ inline void issue(int kt, int st) const {
     const uint32_t stage_base = lds_base + (uint32_t)st * (uint32_t)(MC::STAGE * 4);
+    const int32x4 ra = buffer_words(a_org + (int64_t)kt * C::BK);
+    const int32x4 rb = buffer_words(b_org + (int64_t)kt * C::BK * ldb);
 #pragma unroll
     for (int i = 0; i < MC::D; ++i) {
-      const float* src = ptr[i] + (int64_t)kt * step[i];
+      const int32x4 r = from_a[i] ? ra : rb;
       const uint32_t m0v = __builtin_amdgcn_readfirstlane(stage_base + lds_off[i]);
       // M0 is reserved by the compiler, which warns about clobbering it.  Nothing else in
       // these kernels uses M0 (a structural test checks that every M0 write is one of these
       // copies, immediately followed by its load), so the clobber is safe here.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+      asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                    :
-                   : "v"(src), "s"(m0v)
+                   : "v"(off[i]), "s"(r), "s"(m0v)
                    : "memory", "m0");
 #pragma clang diagnostic pop
     }
