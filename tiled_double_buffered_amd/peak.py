@@ -23,14 +23,15 @@ CUS = 256                        # MI355X compute units, 4 SIMDs each
 FLOP_PER_CLOCK = CUS * 4 * MFMA_FLOP // 64   # each SIMD retires one such MFMA per 64 clocks
 
 
-def mfma_ceiling(blocks: int = 768, iters: int = 1536, warm_s: float = 0.3,
-                 launches: int = 10, stream=None) -> dict:
+def mfma_ceiling(blocks: int = 768, iters: int = 6144, warm_s: float = 0.3,
+                 launches: int = 5, stream=None) -> dict:
     """Time `launches` probe launches after `warm_s` seconds of warm-up on `stream`
     (default: torch's current stream) and return the attained rate, the shader clock and
     the rate that one instruction per SIMD per 64 clocks gives at that clock.
 
     The default of 768 workgroups is three waves per SIMD, all resident at once (the probe
-    needs 132 registers per lane, so a SIMD holds three of its waves)."""
+    needs 132 registers per lane, so a SIMD holds three of its waves); 6144 iterations
+    make one launch about 8 ms, so that launch and ramp overheads stay near 0.3%."""
     import torch
     dev = torch.device("cuda", torch.cuda.current_device())
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
