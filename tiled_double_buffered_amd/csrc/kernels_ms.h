@@ -90,6 +90,9 @@ struct MsCopy {
 
   __device__ inline void init(const float* smem, int wave, int lane, const float* A,
                               int64_t lda, const float* B, int64_t ldb_, int m0, int n0) {
+    // The wave index is below WAVES; saying so lets the compiler resolve at compile time
+    // which operand each copy reads wherever the split of A and B chunks allows.
+    __builtin_assume(wave >= 0 && wave < MC::WAVES);
     lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_float*)smem);
     a_org = A + (int64_t)m0 * lda;
     b_org = B + n0;
