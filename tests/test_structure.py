@@ -124,8 +124,8 @@ def test_mfma_count_matches_tile(kernels):
 
 
 def test_multistage_copies_and_m0(kernels):
-    """The multi-stage kernels copy with buffer_load_dwordx4 ... lds only, each copy right
-    after the s_mov_b32 that sets its LDS destination in M0, and nothing else touches M0.
+    """The multi-stage kernels copy with buffer_load_dwordx4 ... lds only, each copy one wait
+    state after the s_mov_b32 that sets its LDS destination in M0, and nothing else touches M0.
     The per-tile copy count is (BM*BK + BK*BN) * 4 bytes / 1 KiB / waves, issued S-1 times
     in the prologue, S times in the unrolled steps and once in the remainder step."""
     seen = 0
@@ -138,9 +138,12 @@ def test_multistage_copies_and_m0(kernels):
             continue
         seen += 1
         for i in m0_lines:
+            # the M0 write, one wait state (the hazard between a scalar M0 write and a
+            # direct-to-LDS load), then the load
             assert lines[i].startswith("s_mov_b32 m0,"), (k["cfg"], lines[i])
-            assert re.match(r"buffer_load_dwordx4\b.*\blds$", lines[i + 1]), \
-                (k["cfg"], lines[i + 1])
+            assert lines[i + 1] == "s_nop 0", (k["cfg"], lines[i + 1])
+            assert re.match(r"buffer_load_dwordx4\b.*\blds$", lines[i + 2]), \
+                (k["cfg"], lines[i + 2])
         bm, bn, bk, wm, wn = k["cfg"]
         per_wave = (bm * bk + bk * bn) * 4 // 1024 // (wm * wn)
         n = len(dma)

@@ -131,10 +131,12 @@ struct MsCopy {
       const uint32_t m0v = __builtin_amdgcn_readfirstlane(stage_base + lds_off[i]);
       // M0 is reserved by the compiler, which warns about clobbering it.  Nothing else in
       // these kernels uses M0 (a structural test checks that every M0 write is one of these
-      // copies, immediately followed by its load), so the clobber is safe here.
+      // copies, followed by its load), so the clobber is safe here.  A scalar write of M0
+      // needs one wait state before a direct-to-LDS load reads it; the compiler inserts that
+      // for its own code but cannot see inside this statement, hence the s_nop.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-      asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+      asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                    :
                    : "v"(off[i]), "s"(r), "s"(m0v)
                    : "memory", "m0");
