@@ -253,7 +253,7 @@ __device__ inline void mfma_round(const Frag<C>& f, floatx16 (&acc)[C::FM][C::FN
 
 // ------------------------------------------------------------------------------------
 // Instruction interleaving for the unguarded loops.  The compiler's scheduler, left
-// alone, sinks the global prefetch loads to just before their LDS stores, which exposes
+// alone, sinks the prefetch loads to just before their LDS stores, which exposes
 // their whole latency.  These hints (sched_group_barrier, applied to the scheduling
 // region they close) ask for each other memory instruction to be followed by a share of
 // the MFMAs, so that the matrix pipe keeps issuing while loads and stores are in flight.
@@ -283,7 +283,7 @@ template <class C>
 struct Sched {
   static constexpr int R = C::BK / 8;                  // rounds per K tile
   static constexpr int MQ = 4 * C::FM * C::FN;         // MFMAs per round
-  static constexpr int G = C::A_PER_T + C::B_PER_T;    // 16-byte global loads per tile
+  static constexpr int G = C::A_PER_T + C::B_PER_T;    // 16-byte buffer loads per tile
   static constexpr int W = C::A_PER_T + C::B_PER_T;    // 16-byte LDS stores per tile
   static constexpr int D = C::FM + 2 * C::FN;          // LDS read instructions per round
 

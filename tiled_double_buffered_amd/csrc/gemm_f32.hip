@@ -14,7 +14,8 @@
 //     overwritten", because the buffers alternate.
 // The pages' own kernels target Apple GPUs; everything here is written for CDNA4:
 // 64-lane waves, v_mfma_f32_32x32x2_f32 on the matrix cores, LDS with padded rows,
-// 16-byte global loads, and an XCD-aware ordering of workgroups.
+// 16-byte buffer loads from scalar tile bases (and direct-to-LDS copies in the
+// multi-stage loop), and an XCD-aware ordering of workgroups.
 //
 // Files: gemm_common.h (tile configurations, copy, micro-kernel, epilogue),
 // kernels_sb_db.h (single- and double-buffered loops), kernels_ms.h (multi-stage
