@@ -119,6 +119,48 @@ def test_edge_residues(cfg):
             assert r <= 1.0, (cfg, v, M, N, K, r)
 
 
+def _random_cases(n=60, seed=31337):
+    """Seeded random products: sizes log-uniform in 1..700, leading dimensions padded by
+    0..7, base pointers offset by 0 or 1 float, any variant and configuration."""
+    rng = np.random.default_rng(seed)
+    variants = ["auto", "sb", "db", "ms", "sb3"]
+    cases = []
+    for i in range(n):
+        M, N, K = (int(np.exp(rng.uniform(0.0, np.log(700.0)))) for _ in range(3))
+        v = variants[int(rng.integers(len(variants)))]
+        cfg = -1 if v == "auto" else int(rng.integers(NCFG))
+        pads = [int(x) for x in rng.integers(0, 8, 3)]
+        offs = [int(x) for x in rng.integers(0, 2, 3)]
+        cases.append((i, M, N, K, v, cfg, pads, offs))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"r{c[0]}")
+def test_random_shapes_strides_and_offsets(case):
+    """Elementwise parity on random sizes, strides and alignments, with NaN in every pad
+    (it must not leak into C) and C's own pad left untouched."""
+    i, M, N, K, v, cfg, (pa, pb, pc), (oa, ob, oc) = case
+    lda, ldb, ldc = K + pa, N + pb, N + pc
+    _say(f"[random] #{i} {M}x{N}x{K} {v} cfg={cfg} ld=({lda},{ldb},{ldc}) off=({oa},{ob},{oc})")
+    Ab = ti.grid_matrix(9300 + i, 1, M, K, ld=lda)
+    Bb = ti.grid_matrix(9300 + i, 2, K, N, ld=ldb)
+    C64, Bnd = oracle.gemm_f64(Ab[:, :K], Bb[:, :N])
+    Ad = torch.full((M * lda + oa,), float("nan"), device=DEV)
+    Bd = torch.full((K * ldb + ob,), float("nan"), device=DEV)
+    Cd = torch.full((M * ldc + oc,), float("nan"), device=DEV)
+    Ad[oa:].view(M, lda).copy_(torch.from_numpy(Ab))
+    Bd[ob:].view(K, ldb).copy_(torch.from_numpy(Bb))
+    A = Ad[oa:].view(M, lda)[:, :K]
+    B = Bd[ob:].view(K, ldb)[:, :N]
+    C = Cd[oc:].view(M, ldc)[:, :N]
+    _run(A, B, v, cfg, out=C)
+    assert _ratio(C, C64, Bnd) <= 1.0, case
+    Cfull = Cd[oc:].view(M, ldc).cpu().numpy()
+    assert np.all(np.isnan(Cfull[:, N:])), "C padding was written"
+    if oc:
+        assert torch.isnan(Cd[:oc]).all()
+
+
 @pytest.mark.parametrize("cfg", [-1] + list(range(NCFG)))
 def test_leading_dimensions_padding_and_misalignment(cfg):
     """Row strides larger than the rows, odd strides (rows not 16-byte aligned), base

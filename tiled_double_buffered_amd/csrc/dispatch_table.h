@@ -24,25 +24,30 @@ struct DispatchRow {
 };
 
 static const DispatchRow kDispatch[] = {
-    {128, 128, 128, 2, 6, 7, 6, 6},  // sb 4.65 us, db 4.28 us, ms 4.48 us
-    {127, 193, 61, 2, 6, 6, 6, 6},  // sb 5.24 us, db 5.04 us, ms 5.05 us
-    {513, 257, 129, 3, 6, 6, 6, 6},  // sb 8.96 us, db 7.80 us, ms 7.79 us
-    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.49 us, db 18.24 us, ms 17.93 us
-    {256, 1024, 128, 2, 6, 7, 6, 6},  // sb 4.85 us, db 4.47 us, ms 4.70 us
-    {1024, 128, 256, 2, 6, 7, 6, 6},  // sb 7.16 us, db 6.27 us, ms 6.45 us
-    {4096, 4096, 4096, 2, 1, 7, 1, 3},  // sb 953.50 us, db 903.45 us, ms 914.58 us
-    {8192, 8192, 8192, 2, 2, 3, 2, 3},  // sb 7407.52 us, db 7166.92 us, ms 7202.52 us
-    {256, 256, 256, 2, 6, 7, 6, 6},  // sb 7.13 us, db 6.25 us, ms 6.41 us
-    {512, 512, 512, 2, 6, 7, 6, 6},  // sb 12.23 us, db 10.03 us, ms 10.05 us
-    {2048, 2048, 2048, 2, 3, 6, 3, 6},  // sb 124.48 us, db 117.82 us, ms 120.52 us
-    {6144, 6144, 6144, 2, 4, 4, 4, 3},  // sb 3171.01 us, db 3051.21 us, ms 3057.85 us
-    {64, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.21 us, db 64.88 us, ms 61.00 us
-    {4096, 4096, 512, 2, 2, 9, 2, 3},  // sb 128.32 us, db 122.37 us, ms 124.91 us
-    {2048, 8192, 2048, 2, 2, 7, 2, 3},  // sb 484.53 us, db 457.29 us, ms 462.59 us
-    {16, 4096, 4096, 2, 10, 7, 10, 10},  // sb 115.59 us, db 98.35 us, ms 99.30 us
-    {32, 4096, 4096, 3, 10, 10, 10, 10},  // sb 120.45 us, db 69.07 us, ms 63.05 us
-    {128, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.45 us, db 64.80 us, ms 61.20 us
-    {32, 8192, 8192, 3, 10, 7, 10, 10},  // sb 242.10 us, db 143.74 us, ms 123.84 us
+    {128, 128, 128, 2, 6, 7, 6, 6},  // sb 4.58 us, db 4.39 us, ms 4.46 us
+    {127, 193, 61, 3, 6, 6, 6, 6},  // sb 5.23 us, db 5.11 us, ms 5.11 us
+    {513, 257, 129, 3, 6, 6, 6, 6},  // sb 8.95 us, db 7.78 us, ms 7.77 us
+    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.52 us, db 18.27 us, ms 17.91 us
+    {256, 1024, 128, 2, 6, 7, 6, 6},  // sb 4.74 us, db 4.46 us, ms 4.66 us
+    {1024, 128, 256, 2, 6, 7, 6, 6},  // sb 7.14 us, db 6.25 us, ms 6.39 us
+    {4096, 4096, 4096, 2, 1, 9, 1, 3},  // sb 960.86 us, db 901.85 us, ms 914.64 us
+    {8192, 8192, 8192, 2, 0, 9, 0, 3},  // sb 7434.30 us, db 7155.08 us, ms 7238.40 us
+    {256, 256, 256, 2, 6, 7, 6, 6},  // sb 7.12 us, db 6.27 us, ms 6.38 us
+    {512, 512, 512, 2, 6, 7, 6, 6},  // sb 12.28 us, db 10.04 us, ms 10.05 us
+    {768, 768, 768, 3, 6, 7, 6, 6},  // sb 17.74 us, db 14.21 us, ms 13.91 us
+    {1536, 1536, 1536, 2, 6, 7, 6, 6},  // sb 77.41 us, db 68.47 us, ms 68.93 us
+    {2048, 2048, 2048, 2, 3, 6, 3, 3},  // sb 127.27 us, db 117.95 us, ms 121.40 us
+    {3072, 3072, 3072, 3, 6, 7, 6, 6},  // sb 422.96 us, db 417.88 us, ms 406.66 us
+    {6144, 6144, 6144, 2, 4, 4, 4, 3},  // sb 3189.78 us, db 3060.80 us, ms 3063.22 us
+    {64, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.11 us, db 64.82 us, ms 60.75 us
+    {4096, 4096, 512, 2, 2, 4, 2, 3},  // sb 128.00 us, db 122.20 us, ms 124.03 us
+    {2048, 8192, 2048, 2, 2, 4, 2, 3},  // sb 486.43 us, db 457.18 us, ms 463.14 us
+    {4096, 1024, 1024, 2, 3, 7, 3, 3},  // sb 67.09 us, db 61.64 us, ms 63.67 us
+    {1024, 1024, 8192, 3, 6, 7, 6, 6},  // sb 190.59 us, db 127.87 us, ms 122.01 us
+    {16, 4096, 4096, 2, 10, 7, 10, 10},  // sb 116.15 us, db 98.37 us, ms 99.12 us
+    {32, 4096, 4096, 3, 10, 10, 10, 10},  // sb 120.25 us, db 69.00 us, ms 63.14 us
+    {128, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.11 us, db 64.81 us, ms 60.82 us
+    {32, 8192, 8192, 3, 10, 7, 10, 10},  // sb 241.83 us, db 143.57 us, ms 124.43 us
 };
 
 static inline double dispatch_log2(int64_t x) { return x > 0 ? std::log2((double)x) : -1.0; }
@@ -83,17 +88,17 @@ struct SplitRow {
 };
 
 static const SplitRow kSplitK[] = {
-    {16, 4096, 4096, 8},  // 1: 99.6, 2: 53.7, 4: 30.6, 8: 27.5, 16: 30.9
-    {32, 4096, 4096, 8},  // 1: 62.9, 2: 35.4, 4: 22.1, 8: 19.3, 16: 29.8
-    {64, 4096, 4096, 4},  // 1: 60.7, 2: 34.7, 4: 21.7, 8: 24.4, 16: 26.9
-    {128, 4096, 4096, 2},  // 1: 60.9, 2: 35.5, 4: 36.6, 8: 38.4, 16: 46.5
-    {32, 8192, 8192, 4},  // 1: 123.8, 2: 66.5, 4: 46.3, 8: 48.2, 16: 54.8
-    {64, 8192, 8192, 2},  // 1: 124.0, 2: 66.0, 4: 68.8, 8: 74.7, 16: 82.5
-    {256, 256, 8192, 16},  // 1: 118.2, 2: 62.7, 4: 34.6, 8: 21.7, 16: 16.9
-    {512, 512, 8192, 4},  // 1: 118.8, 2: 63.6, 4: 35.9, 8: 37.8, 16: 43.1
-    {1024, 1024, 1024, 1},  // 1: 18.0, 2: 24.7, 4: 26.1, 8: 31.1, 16: 38.5
-    {2048, 2048, 2048, 1},  // 1: 117.9, 2: 128.6, 4: 138.1, 8: 157.5, 16: 199.8
-    {4096, 4096, 4096, 1},  // 1: 903.9, 2: 946.6, 4: 988.7, 8: 1096.1, 16: 1284.7
+    {16, 4096, 4096, 8},  // 1: 98.2, 2: 53.2, 4: 30.8, 8: 22.5, 16: 22.7
+    {32, 4096, 4096, 8},  // 1: 63.4, 2: 35.6, 4: 22.0, 8: 19.0, 16: 29.8
+    {64, 4096, 4096, 4},  // 1: 60.8, 2: 34.7, 4: 21.7, 8: 24.4, 16: 27.0
+    {128, 4096, 4096, 2},  // 1: 61.0, 2: 35.7, 4: 37.2, 8: 39.6, 16: 46.8
+    {32, 8192, 8192, 4},  // 1: 124.0, 2: 67.0, 4: 46.3, 8: 48.4, 16: 55.1
+    {64, 8192, 8192, 2},  // 1: 125.2, 2: 68.7, 4: 71.8, 8: 77.6, 16: 85.4
+    {256, 256, 8192, 16},  // 1: 117.6, 2: 67.2, 4: 37.1, 8: 23.2, 16: 17.4
+    {512, 512, 8192, 4},  // 1: 118.9, 2: 63.7, 4: 37.0, 8: 39.1, 16: 41.1
+    {1024, 1024, 1024, 1},  // 1: 17.9, 2: 24.6, 4: 25.3, 8: 31.2, 16: 39.5
+    {2048, 2048, 2048, 1},  // 1: 118.4, 2: 128.5, 4: 137.0, 8: 151.7, 16: 191.3
+    {4096, 4096, 4096, 1},  // 1: 910.2, 2: 951.8, 4: 983.6, 8: 1085.1, 16: 1260.3
 };
 
 static inline int select_splits(int64_t M, int64_t N, int64_t K) {

@@ -32,9 +32,12 @@ SHAPES = [
     # the workloads
     (128, 128, 128), (127, 193, 61), (513, 257, 129), (1024, 1024, 1024),
     (256, 1024, 128), (1024, 128, 256), (4096, 4096, 4096), (8192, 8192, 8192),
-    # more points for the nearest-shape rule
-    (256, 256, 256), (512, 512, 512), (2048, 2048, 2048), (6144, 6144, 6144),
-    (64, 4096, 4096), (4096, 4096, 512), (2048, 8192, 2048),
+    # more points for the nearest-shape rule; the squares also trace the SB / DB regimes
+    # from 256 to 8192
+    (256, 256, 256), (512, 512, 512), (768, 768, 768), (1536, 1536, 1536),
+    (2048, 2048, 2048), (3072, 3072, 3072), (6144, 6144, 6144),
+    (64, 4096, 4096), (4096, 4096, 512), (2048, 8192, 2048), (4096, 1024, 1024),
+    (1024, 1024, 8192),
     # skinny shapes (a small batch of rows against a wide layer)
     (16, 4096, 4096), (32, 4096, 4096), (128, 4096, 4096), (32, 8192, 8192),
 ]
