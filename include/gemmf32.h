@@ -12,9 +12,10 @@
  *
  * Memory and ownership: A, B and C are caller-owned DEVICE pointers (for instance the
  * data pointers of GPU tensors).  Each must be 4-byte aligned; any leading dimension is
- * accepted (misaligned rows take a scalar-load path).  The library allocates nothing,
- * keeps no per-call state and only borrows `stream` (a hipStream_t; NULL = the legacy
- * default stream).  C must not overlap A or B.
+ * accepted (rows that are not 16-byte aligned, and row strides so large that one tile of
+ * A or B spans 4 GiB or more, take an element-wise copy path).  The library allocates
+ * nothing, keeps no per-call state and only borrows `stream` (a hipStream_t; NULL = the
+ * legacy default stream).  C must not overlap A or B.
  *
  * Asynchrony: a launching call only enqueues one kernel on `stream` and returns; the
  * caller synchronizes.  Calls are re-entrant: the only shared state is a constant table.
@@ -77,8 +78,9 @@ enum {
 /* C = A.B with the variant and tile configuration chosen per shape by the dispatch
  * table (GEMMF32_VARIANT environment variable "sb", "db" or "ms" forces the variant, for
  * measurement; GEMMF32_RASTER=<group_m>[,noxcd] changes the order in which workgroups walk
- * the output tiles, for every launching entry point, also for measurement only).  The pages' lesson that the faster variant depends on the shape is the
- * reason for the table ("Double Buffering", last two paragraphs). */
+ * the output tiles, for every launching entry point, also for measurement only).  The
+ * pages' lesson that the faster variant depends on the shape is the reason for the table
+ * ("Double Buffering", last two paragraphs). */
 int gemm_f32(int64_t M, int64_t N, int64_t K,
              const float *A, int64_t lda,
              const float *B, int64_t ldb,
@@ -111,9 +113,9 @@ int gemm_f32_ms(int64_t M, int64_t N, int64_t K,
                 void *stream);
 
 /* C = A.B with an explicit variant (GEMMF32_VARIANT_SB, _DB, _MS or _SB3; _AUTO = dispatch
- * table)
- * and tile configuration id (0 .. gemm_f32_num_configs()-1; -1 = dispatch table).  For
- * measurement and tests: every (variant, configuration) pair computes the same product. */
+ * table) and tile configuration id (0 .. gemm_f32_num_configs()-1; -1 = dispatch table).
+ * For measurement and tests: every (variant, configuration) pair computes the same
+ * product. */
 int gemm_f32_ex(int64_t M, int64_t N, int64_t K,
                 const float *A, int64_t lda,
                 const float *B, int64_t ldb,

@@ -49,17 +49,30 @@ static const DispatchRow kDispatch[] = {
     {128, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.11 us, db 64.81 us, ms 60.82 us
     {32, 8192, 8192, 3, 10, 7, 10, 10},  // sb 241.83 us, db 143.57 us, ms 124.43 us
 };
+constexpr int kDispatchRows = (int)(sizeof(kDispatch) / sizeof(kDispatch[0]));
 
 static inline double dispatch_log2(int64_t x) { return x > 0 ? std::log2((double)x) : -1.0; }
 
+// (log2 M, log2 N, log2 K) of every row, computed once (thread-safe static initialization),
+// so that a lookup costs three logarithms instead of three per row.
+struct DispatchLogs {
+  double v[kDispatchRows][3];
+  DispatchLogs() {
+    for (int i = 0; i < kDispatchRows; ++i) {
+      v[i][0] = dispatch_log2(kDispatch[i].m);
+      v[i][1] = dispatch_log2(kDispatch[i].n);
+      v[i][2] = dispatch_log2(kDispatch[i].k);
+    }
+  }
+};
+
 static inline const DispatchRow& dispatch_nearest(int64_t M, int64_t N, int64_t K) {
+  static const DispatchLogs logs;
   const double lm = dispatch_log2(M), ln = dispatch_log2(N), lk = dispatch_log2(K);
   int best = 0;
   double best_d = 1e300;
-  for (int i = 0; i < (int)(sizeof(kDispatch) / sizeof(kDispatch[0])); ++i) {
-    const DispatchRow& r = kDispatch[i];
-    const double dm = lm - dispatch_log2(r.m), dn = ln - dispatch_log2(r.n),
-                 dk = lk - dispatch_log2(r.k);
+  for (int i = 0; i < kDispatchRows; ++i) {
+    const double dm = lm - logs.v[i][0], dn = ln - logs.v[i][1], dk = lk - logs.v[i][2];
     const double d = dm * dm + dn * dn + dk * dk;
     if (d < best_d) {
       best_d = d;

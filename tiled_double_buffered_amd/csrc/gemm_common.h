@@ -366,16 +366,6 @@ __device__ inline void load_tile(TileCopy<C>& cp, const LoopArgs<C>& g, int kt) 
   load_tile_b<C, GUARD>(cp, g, kt);
 }
 
-// Double-buffered: two LDS slots, tile l+1 copied into the idle slot while tile l is
-// multiplied, ONE barrier per K tile.  The loop is rotated so that the barrier sits at
-// the hand-off between slots: after this wave has written tile l+1 into the idle slot and
-// before anybody reads it.  That single barrier is at once "tile l+1 has landed" and
-// "nobody still reads the slot that tile l+2 will overwrite" (all reads of tile l are
-// already in registers by then).  LDS fragments are read one round ahead of the MFMAs,
-// and the second half of tile l's last round runs after the barrier, covering the
-// latency of the first reads of tile l+1.  Barriers per product: 1 (prologue) +
-// (k_tiles - 1) = k_tiles, the same count as a barrier at the top of every iteration.
-
 // ------------------------------------------------------------------------------------
 // Per-workgroup setup shared by every kernel.
 // ------------------------------------------------------------------------------------
