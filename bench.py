@@ -243,6 +243,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--per-shape", choices=("all", "metric", "none"), default="all",
                     help="which workload shapes get the SB/DB/dispatch comparison")
+    ap.add_argument("--rounds", type=int, default=2,
+                    help="per-shape timing: rounds, each visiting the variants in rotated order")
+    ap.add_argument("--batches", type=int, default=5, help="per-shape timing: batches per round")
+    ap.add_argument("--batch-ms", type=float, default=25.0,
+                    help="per-shape timing: minimum milliseconds of launches per batch")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--summarize-trace", metavar="DIR")
@@ -375,8 +380,12 @@ def main() -> int:
     except Exception as exc:
         ceiling = {"error": repr(exc)}
 
+    # power, clocks and temperatures while the headline kernel runs (amd-smi, sampled once)
+    telemetry = telemetry_under_load(step, torch)
+    log(f"[bench] telemetry under load: {telemetry}")
+
     # ------------------------------------------------------------------ per shape
-    def time_call(fn, target_ms=25.0, batches=5):
+    def time_call(fn, target_ms=args.batch_ms, batches=args.batches):
         fn()
         torch.cuda.synchronize()
         t = time.perf_counter()
@@ -401,20 +410,36 @@ def main() -> int:
             res.append((a.elapsed_time(b) * 1e3 / reps, (h1 - h0) * 1e6 / reps))
         ev = statistics.median(x[0] for x in res)
         wall_us = statistics.median(x[1] for x in res)
-        return ev, wall_us
+        return ev, wall_us, min(x[0] for x in res), max(x[0] for x in res)
+
+    # the oracle for each per-shape workload, to check every timed variant once per round
+    def shape_checker(name, m, n, k, s, a_h, b_h):
+        try:
+            import oracle
+        except Exception as exc:  # the oracle is test infrastructure; report, do not fail
+            return lambda C: {"error": repr(exc)}
+        if m * n * k <= 4096 ** 3:
+            c64, bnd = oracle.gemm_f64(a_h, b_h)
+            return lambda C: oracle.tolerance_ratio(C.cpu().numpy(), c64, bnd)
+        ri, rj = ti.sample_positions(s, m, n, 4096)
+        c64, bnd = oracle.gemm_f64_sampled(a_h, b_h, ri, rj)
+        ii, jj = torch.from_numpy(ri).to(dev), torch.from_numpy(rj).to(dev)
+        return lambda C: oracle.tolerance_ratio(C[ii, jj].cpu().numpy(), c64, bnd)
 
     per_shape = {}
     names = {"all": list(ti.WORKLOADS), "none": [],
              "metric": ["square_1024", "square_4096", "square_8192"]}[args.per_shape]
-    rounds = 2
+    rounds = args.rounds
     for name in names:
         m, n, k, s = ti.WORKLOADS[name]
         if name == HEADLINE:
             Ad, Bd, Cd = A, B, C
+            a_h, b_h = A_h, B_h
         else:
             a_h, b_h = ti.workload_inputs(m, n, k, s)
             Ad, Bd = torch.from_numpy(a_h).to(dev), torch.from_numpy(b_h).to(dev)
             Cd = torch.zeros((m, n), dtype=torch.float32, device=dev)
+        check = shape_checker(name, m, n, k, s, a_h, b_h)
         pa, pb, pc = Ad.data_ptr(), Bd.data_ptr(), Cd.data_ptr()
         fns = {
             "sb": lambda: tdb.gemm_f32_sb(m, n, k, pa, k, pb, n, pc, n, s_ptr),
@@ -426,18 +451,30 @@ def main() -> int:
         }
         order = list(fns)
         samples = {v: [] for v in fns}
+        checks = {v: [] for v in fns if v != "torch"}
         for r in range(rounds):  # rotate the variant order between rounds
             rot = r % len(order)
             for v in order[rot:] + order[:rot]:
                 samples[v].append(time_call(fns[v]))
+            for v in checks:  # every timed variant of the library, once per round
+                Cd.fill_(float("nan"))
+                fns[v]()
+                torch.cuda.synchronize()
+                checks[v].append(check(Cd))
         f = 2.0 * m * n * k
         entry = {"M": m, "N": n, "K": k}
         for v, xs in samples.items():
-            ev = statistics.median(x[0] for x in xs)
+            ev = statistics.median(x[0] for x in xs)  # median of the per-round medians
             wl = statistics.median(x[1] for x in xs)
             entry[v] = {"us": round(ev, 2), "host_wall_us": round(wl, 2),
+                        "us_range": [round(min(x[2] for x in xs), 2),
+                                     round(max(x[3] for x in xs), 2)],
                         "tflops": round(f / (ev * 1e-6) / 1e12, 2),
                         "frac_peak": round(f / (ev * 1e-6) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4)}
+            if v in checks:
+                cs = checks[v]
+                entry[v]["max_err_over_bound"] = (max(cs) if all(isinstance(c, float)
+                                                                   for c in cs) else cs[0])
         entry["sb_cfg"] = tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_SB)
         entry["db_cfg"] = tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_DB)
         entry["ms_cfg"] = tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_MS)
@@ -453,6 +490,7 @@ def main() -> int:
             f"({entry['dispatch']['tflops']} TFLOP/s), torch.matmul {entry['torch']['us']} us")
         if name != HEADLINE:
             del Ad, Bd, Cd
+        del check
 
     # ------------------------------------------------------------------ CPU baseline
     cpu_baseline = None
@@ -504,6 +542,7 @@ def main() -> int:
         "frac_peak": round(value / PEAK_FP32_MFMA_TFLOPS, 4),
         "roofline": roofline,
         "mfma_ceiling": ceiling,
+        "telemetry": telemetry,
         "cpu_baseline": cpu_baseline,
         "metric_shapes": metric_shapes,
         "per_shape": per_shape,
@@ -540,6 +579,45 @@ def oracle_table() -> int:
     oracle.set_threads(threads)
     print(json.dumps({"cpu": _cpu_model(), "threads": threads, "rows": rows}), flush=True)
     return 0
+
+
+def telemetry_under_load(step, torch, timeout_s: float = 20.0) -> dict:
+    """One amd-smi sample of socket power, shader clocks (per XCD) and temperatures, taken
+    while `step` keeps the GPU busy.  amd-smi runs as a child process; nothing is timed
+    meanwhile.  Returns {"error": ...} when amd-smi is missing or fails."""
+    import shutil
+    import subprocess
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return {"error": "amd-smi not found"}
+    try:
+        proc = subprocess.Popen([exe, "metric", "-g", "0", "-p", "-c", "-t", "--json"],
+                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL)
+    except OSError as exc:
+        return {"error": repr(exc)}
+    t0 = time.perf_counter()
+    while proc.poll() is None and time.perf_counter() - t0 < timeout_s:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    try:
+        out, _ = proc.communicate(timeout=5)
+    except subprocess.TimeoutExpired:
+        proc.kill()
+        proc.communicate()
+        return {"error": "amd-smi timed out"}
+    try:
+        d = json.loads(out)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clocks = [v["clk"]["value"] for k, v in sorted(g["clock"].items())
+                  if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+        temps = {k: v["value"] for k, v in g.get("temperature", {}).items()
+                 if isinstance(v, dict) and "value" in v}
+        return {"socket_power_w": g["power"]["socket_power"]["value"],
+                "gfx_clock_mhz_per_xcd": clocks, "temperature_c": temps,
+                "source": "amd-smi metric -g 0 -p -c -t, sampled during headline launches"}
+    except (ValueError, KeyError, IndexError, TypeError) as exc:
+        return {"error": "unparsed amd-smi output: " + repr(exc)}
 
 
 def _cpu_model() -> str:
