@@ -1,7 +1,9 @@
 """Build the gfx950 library libgemmf32.so in-tree with hipcc, and expose its device
 assembly and per-kernel resource usage for the structural tests.
 
-    python -m tiled_double_buffered_amd.build          # builds the library
+    python -m tiled_double_buffered_amd.build              # builds the library
+    python -m tiled_double_buffered_amd.build --resources  # per-kernel registers, LDS,
+                                                           # scratch, barriers per loop
 """
 from __future__ import annotations
 
@@ -87,7 +89,56 @@ def kernel_metadata(asm: str) -> dict:
     return meta
 
 
+def _loops(body: str) -> dict:
+    """Loop header id -> instruction lines of the loop's blocks (from the compiler's own
+    block annotations)."""
+    loops, cur = {}, None
+    for line in body.split("\n"):
+        m = re.match(r"^\.LBB(\w+):(.*)", line)
+        if m:
+            hdr = m.group(1) if "Loop Header" in m.group(2) else None
+            mm = re.search(r"Header=BB(\w+)", m.group(2))
+            if mm:
+                hdr = mm.group(1)
+            cur = loops.setdefault(hdr, []) if hdr else None
+            continue
+        t = line.strip()
+        if cur is not None and t and not t.startswith((";", ".")):
+            cur.append(t)
+    return loops
+
+
+def resources_table(asm: str) -> str:
+    """One line per kernel: tile, loop kind, registers, LDS, scratch, and the barriers and
+    MFMAs of each barrier-carrying loop (barriers per MFMA-tile of that loop)."""
+    meta = kernel_metadata(asm)
+    rows = ["kernel                         vgpr agpr sgpr  lds_B scratch  loops: barriers/MFMAs"]
+    for name, body in sorted(kernel_functions(asm).items()):
+        m = re.search(r"TileCfgILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEELi(\d+)E", name)
+        kind = "ms%s" % m.group(6) if "_ms_kernel" in name else \
+            {"1": "sb", "2": "db", "4": "sb3"}[m.group(6)]
+        tile = "%sx%sx%s/%sx%s" % m.groups()[:5]
+        d = meta[name]
+        # unified register file: architected VGPRs first, AGPRs from accum_offset on
+        arch = min(d.get("accum_offset", d["next_free_vgpr"]), d["next_free_vgpr"])
+        agpr = max(0, d["next_free_vgpr"] - d.get("accum_offset", d["next_free_vgpr"]))
+        loops = []
+        for ins in _loops(body).values():
+            nb = sum(1 for t in ins if re.match(r"s_barrier\b", t))
+            if nb:
+                nm = sum(1 for t in ins if t.startswith("v_mfma"))
+                loops.append(f"{nb}/{nm}")
+        rows.append(f"{kind:>4} {tile:<24} {arch:>4} {agpr:>4} {d['next_free_sgpr']:>4} "
+                    f"{d['group_segment_fixed_size']:>6} {d['private_segment_fixed_size']:>7}  "
+                    + " ".join(loops))
+    return "\n".join(rows)
+
+
 def main(argv=None) -> int:
+    argv = list(argv or [])
+    if "--resources" in argv:
+        print(resources_table(device_asm()))
+        return 0
     path = build_library()
     print(path)
     return 0
