@@ -75,8 +75,9 @@ def test_barriers_per_k_step(kernels):
     (single-buffered) or 3 (single-buffered with split copy barriers).  A loop body may
     hold several K tiles (the double-buffered loop is unrolled by two); the tiles per
     iteration are its MFMA count over one tile's.  Outside the loops the single-buffered
-    kernels have no barrier; the others have their prologue barriers and the barrier of a
-    left-over unrolled step."""
+    kernels have exactly the barriers of one peeled last tile per loop (that tile's A
+    columns past K are zeroed); the others have their prologue barriers and the barriers
+    of the peeled step that copies the last tile."""
     facts = json.load(open(GOLDEN))["barriers_per_k_step"]
     for name, k in kernels.items():
         expected = {"db": facts["double_buffered"], "ms": facts["double_buffered"],
@@ -93,9 +94,9 @@ def test_barriers_per_k_step(kernels):
         outside = _count_barriers(k["body"].split("\n")) - sum(
             _count_barriers(ls) for ls in loops.values())
         if k["kind"] in ("sb", "sb3"):
-            assert outside == 0, (k["cfg"], "single-buffered barriers all in the loop")
+            assert outside == expected * len(loops), (k["cfg"], k["kind"], outside)
         else:
-            assert 1 <= outside <= 2 * len(loops), (k["cfg"], k["kind"], outside)
+            assert 1 <= outside <= 3 * len(loops), (k["cfg"], k["kind"], outside)
 
 
 def test_no_scratch_and_lds_fits(kernels):
@@ -127,7 +128,8 @@ def test_multistage_copies_and_m0(kernels):
     """The multi-stage kernels copy with buffer_load_dwordx4 ... lds only, each copy one wait
     state after the s_mov_b32 that sets its LDS destination in M0, and nothing else touches M0.
     The per-tile copy count is (BM*BK + BK*BN) * 4 bytes / 1 KiB / waves, issued S-1 times
-    in the prologue, S times in the unrolled steps and once in the remainder step."""
+    in the prologue, S times in the unrolled steps and once in the remainder step, in the
+    loop for interior tiles and in the one for edge tiles."""
     seen = 0
     for name, k in kernels.items():
         lines = [t.strip() for t in k["body"].split("\n")]
@@ -147,8 +149,9 @@ def test_multistage_copies_and_m0(kernels):
         bm, bn, bk, wm, wn = k["cfg"]
         per_wave = (bm * bk + bk * bn) * 4 // 1024 // (wm * wn)
         n = len(dma)
-        # issue sites: S-1 in the prologue, S in the unrolled steps, 1 in the remainder step
-        assert n == per_wave * 2 * k["stages"], (k["cfg"], n, per_wave, k["stages"])
+        # issue sites: S-1 in the prologue, S in the unrolled steps, 1 in the remainder step,
+        # in each of the two copies of the loop (interior tiles, edge tiles)
+        assert n == 2 * per_wave * 2 * k["stages"], (k["cfg"], n, per_wave, k["stages"])
         assert len(m0_lines) == n
     assert seen >= 1
 

@@ -57,7 +57,7 @@ struct TileCfg {
 
 // Flags passed to the kernel.
 enum : int {
-  kVecA = 1,  // A 16-byte aligned and lda % 4 == 0: rows can be read 16 bytes at a time
+  kVecA = 1,  // every 16-byte copy offset inside a tile of A fits the 32-bit buffer range
   kVecB = 2,  // same for B
 };
 
@@ -122,30 +122,65 @@ struct TileCopy {
       b_off[i] = (uint32_t)(((int64_t)(b_row + i * C::B_ROWS_PER_PASS) * ldb + b_col) * 4);
   }
 
-  // Fast path: the whole tile lies inside the matrices and rows are 16-byte aligned.
-  // The copies are buffer loads: the tile's first element is a workgroup-uniform base (a
-  // buffer descriptor in scalar registers, advanced by scalar arithmetic per K tile) and
-  // each thread adds its fixed 32-bit offset.  Plain global loads would need a 64-bit
-  // vector address add per load and per tile, and that vector arithmetic measurably slows
-  // the matrix instructions it is interleaved with.  The host takes this path only when
-  // every offset inside a tile fits in 32 bits.
-  static __device__ inline floatx4 buffer_load16(const float* base, uint32_t off) {
+  // Fast path: 16-byte buffer loads.  The tile's first element is a workgroup-uniform
+  // base (a buffer descriptor in scalar registers, rebuilt by scalar arithmetic per K
+  // tile) and each thread adds its fixed 32-bit offset.  Plain global loads would need a
+  // 64-bit vector address add per load and per tile, and that vector arithmetic measurably
+  // slows the matrix instructions it is interleaved with.
+  //
+  // The descriptor's range ends where the operand ends (`bytes` = the byte extent of A or
+  // B from its origin), and a buffer load returns 0 for every 4-byte word past the range.
+  // That makes the same copy serve edge tiles and any leading dimension:
+  //   * A rows at or past M and B rows at or past K lie past the range and read 0;
+  //   * B columns at or past N read the start of the next row (or 0 past the range), and A
+  //     rows inside the matrix read their padding or the next row past column K-1: such
+  //     values reach only C rows >= M or columns >= N, which the epilogue never stores,
+  //     except A's columns >= K, which would meet B's zero rows: a K-tail tile therefore
+  //     zeroes them (load_a_fast_masked);
+  //   * rows need only 4-byte alignment (16-byte loads from 4-byte-aligned addresses are
+  //     served in the unaligned access mode of this GPU).
+  // The host takes this path only when every offset inside a tile fits in 32 bits.
+  static __device__ inline floatx4 buffer_load16(const float* base, uint32_t range,
+                                                 uint32_t off) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(base), (short)0, (int)kBufferRange, kBufferFlags);
+        const_cast<float*>(base), (short)0, (int)range, kBufferFlags);
     return __builtin_bit_cast(floatx4,
                               __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
   }
-  __device__ inline void load_a_fast(const float* __restrict__ A, int64_t lda, int m0,
-                                     int k0) {
-    const float* base = A + (int64_t)m0 * lda + k0;
-#pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) ra[i] = buffer_load16(base, a_off[i]);
+  // Bytes of the operand left from element offset `first` on, clamped to the range a
+  // descriptor can hold.
+  static __device__ inline uint32_t range_from(int64_t bytes, int64_t first) {
+    const int64_t left = bytes - first * 4;
+    return left <= 0 ? 0u : left >= (int64_t)kBufferRange ? kBufferRange : (uint32_t)left;
   }
-  __device__ inline void load_b_fast(const float* __restrict__ B, int64_t ldb, int n0,
-                                     int k0) {
-    const float* base = B + (int64_t)k0 * ldb + n0;
+  // EXACT: the range ends where A ends (edge tiles, the last tile); otherwise the tile
+  // lies inside A and the widest range saves the scalar arithmetic.
+  template <bool EXACT>
+  __device__ inline void load_a_fast(const float* __restrict__ A, int64_t lda, int m0,
+                                     int k0, int64_t a_bytes) {
+    const int64_t first = (int64_t)m0 * lda + k0;
+    const uint32_t range = EXACT ? range_from(a_bytes, first) : kBufferRange;
 #pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) rb[i] = buffer_load16(base, b_off[i]);
+    for (int i = 0; i < C::A_PER_T; ++i) ra[i] = buffer_load16(A + first, range, a_off[i]);
+  }
+  // The same for the tile that holds column K-1 when K is not a multiple of BK: columns
+  // >= K are zeroed, so they add exact zeros against B's zero rows.
+  __device__ inline void load_a_fast_masked(const float* __restrict__ A, int64_t lda, int m0,
+                                            int k0, int64_t a_bytes, int K) {
+    load_a_fast<true>(A, lda, m0, k0, a_bytes);
+    const int c = k0 + a_col;
+#pragma unroll
+    for (int i = 0; i < C::A_PER_T; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ra[i][e] = c + e < K ? ra[i][e] : 0.0f;
+  }
+  template <bool EXACT>
+  __device__ inline void load_b_fast(const float* __restrict__ B, int64_t ldb, int n0,
+                                     int k0, int64_t b_bytes) {
+    const int64_t first = (int64_t)k0 * ldb + n0;
+    const uint32_t range = EXACT ? range_from(b_bytes, first) : kBufferRange;
+#pragma unroll
+    for (int i = 0; i < C::B_PER_T; ++i) rb[i] = buffer_load16(B + first, range, b_off[i]);
   }
 
   // Guarded path: element by element; anything outside M x K (A) or K x N (B) reads as
@@ -338,32 +373,43 @@ struct LoopArgs {
   const float* A;
   const float* B;
   int64_t lda, ldb;
+  int64_t a_bytes, b_bytes;  // byte extents of A (M x K) and B (K x N) from A and B
   int M, N, K, m0, n0;
   bool vec_a, vec_b;
 };
 
-template <class C, bool GUARD>
+// MASKED: this tile may hold column K-1 of a K that is not a multiple of BK (the last
+// tile of the loop); its A columns >= K are zeroed, and its copies use exact ranges.
+// EDGE: the workgroup's tile sticks out of M or N (exact ranges for every K tile).  The
+// guarded loop always uses exact ranges for the tiles it copies 16 bytes at a time.
+template <class C, bool GUARD, bool MASKED = false, bool EDGE = true>
 __device__ inline void load_tile_a(TileCopy<C>& cp, const LoopArgs<C>& g, int kt) {
+  constexpr bool EXACT = GUARD || MASKED || EDGE;
   const int k0 = kt * C::BK;
-  if (!GUARD || (g.vec_a && k0 + C::BK <= g.K))
-    cp.load_a_fast(g.A, g.lda, g.m0, k0);
-  else
+  if (!GUARD || (g.vec_a && k0 + C::BK <= g.K)) {
+    if constexpr (MASKED)
+      cp.load_a_fast_masked(g.A, g.lda, g.m0, k0, g.a_bytes, g.K);
+    else
+      cp.template load_a_fast<EXACT>(g.A, g.lda, g.m0, k0, g.a_bytes);
+  } else {
     cp.load_a_guarded(g.A, g.lda, g.M, g.K, g.m0, k0);
+  }
 }
 
-template <class C, bool GUARD>
+template <class C, bool GUARD, bool MASKED = false, bool EDGE = true>
 __device__ inline void load_tile_b(TileCopy<C>& cp, const LoopArgs<C>& g, int kt) {
+  constexpr bool EXACT = GUARD || MASKED || EDGE;
   const int k0 = kt * C::BK;
   if (!GUARD || (g.vec_b && k0 + C::BK <= g.K))
-    cp.load_b_fast(g.B, g.ldb, g.n0, k0);
+    cp.template load_b_fast<EXACT>(g.B, g.ldb, g.n0, k0, g.b_bytes);
   else
     cp.load_b_guarded(g.B, g.ldb, g.N, g.K, g.n0, k0);
 }
 
-template <class C, bool GUARD>
+template <class C, bool GUARD, bool MASKED = false, bool EDGE = true>
 __device__ inline void load_tile(TileCopy<C>& cp, const LoopArgs<C>& g, int kt) {
-  load_tile_a<C, GUARD>(cp, g, kt);
-  load_tile_b<C, GUARD>(cp, g, kt);
+  load_tile_a<C, GUARD, MASKED, EDGE>(cp, g, kt);
+  load_tile_b<C, GUARD, MASKED, EDGE>(cp, g, kt);
 }
 
 // ------------------------------------------------------------------------------------
@@ -408,15 +454,16 @@ struct TilePos {
     g.K = K;
     g.m0 = tm * C::BM;
     g.n0 = tn * C::BN;
+    g.a_bytes = ((int64_t)(M - 1) * lda + K) * 4;
+    g.b_bytes = ((int64_t)(K - 1) * ldb + N) * 4;
     m_full = g.m0 + C::BM <= M;
     n_full = g.n0 + C::BN <= N;
-    g.vec_a = (flags & kVecA) && m_full;
-    g.vec_b = (flags & kVecB) && n_full;
+    g.vec_a = (flags & kVecA) != 0;
+    g.vec_b = (flags & kVecB) != 0;
   }
-  // Every K tile of this workgroup can be copied unguarded, 16 bytes at a time.
-  __device__ inline bool unguarded() const {
-    return g.vec_a && g.vec_b && (g.K % C::BK) == 0;
-  }
+  // Every K tile of this workgroup can be copied 16 bytes at a time (edge tiles and a K
+  // tail included, see the fast path of TileCopy).
+  __device__ inline bool unguarded() const { return g.vec_a && g.vec_b; }
 };
 
 template <class C>

@@ -148,14 +148,11 @@ static int launch(int variant, int cfg_id, int64_t M, int64_t N, int64_t K, cons
   const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
   if (tiles * e.nt > 0xFFFFFFFFLL) return GEMMF32_ERR_TOO_LARGE;
   int flags = 0;
-  // 16-byte copies need 16-byte-aligned rows, and their per-thread byte offsets inside a
-  // tile (rows x leading dimension) must stay below the buffer range.
-  if (K > 0 && (((uintptr_t)A) & 15u) == 0 && (lda & 3) == 0 &&
-      (int64_t)e.bm * lda * 4 <= (int64_t)kBufferRange)
-    flags |= kVecA;
-  if (K > 0 && (((uintptr_t)B) & 15u) == 0 && (ldb & 3) == 0 &&
-      (int64_t)e.bk * ldb * 4 <= (int64_t)kBufferRange)
-    flags |= kVecB;
+  // 16-byte copies address a tile with 32-bit per-thread byte offsets (rows x leading
+  // dimension), which must stay below the buffer range; rows need only the 4-byte
+  // alignment that validation already demands.
+  if (K > 0 && (int64_t)e.bm * lda * 4 <= (int64_t)kBufferRange) flags |= kVecA;
+  if (K > 0 && (int64_t)e.bk * ldb * 4 <= (int64_t)kBufferRange) flags |= kVecB;
   flags |= env_raster_flags();
   int m = (int)M, n = (int)N, k = (int)K;
   int kc = splits > 1 ? k_chunk : k;

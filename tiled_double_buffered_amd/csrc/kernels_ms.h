@@ -64,15 +64,15 @@ __device__ __forceinline__ int swz_a(int row) {
 }
 __device__ __forceinline__ int swz_b(int k) { return ((k >> 2) & 1) << 3; }
 
-// The four descriptor words of a raw buffer starting at `base` (range and flags as for the
-// register-staged copies), for the inline-assembly copies below.
+// The four descriptor words of a raw buffer starting at `base` and `range` bytes long
+// (flags as for the register-staged copies), for the inline-assembly copies below.
 typedef int int32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ int32x4 buffer_words(const float* base) {
+__device__ __forceinline__ int32x4 buffer_words(const float* base, uint32_t range) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
   int32x4 r;
   r[0] = (int)(uint32_t)b;
   r[1] = (int)(uint32_t)(b >> 32);
-  r[2] = (int)kBufferRange;
+  r[2] = (int)range;
   r[3] = kBufferFlags;
   return r;
 }
@@ -87,9 +87,11 @@ struct MsCopy {
   const float* a_org;       // A + m0 * lda
   const float* b_org;       // B + n0
   int64_t ldb;
+  int64_t a_bytes, b_bytes;  // byte extents of A and B left from a_org and b_org
 
   __device__ inline void init(const float* smem, int wave, int lane, const float* A,
-                              int64_t lda, const float* B, int64_t ldb_, int m0, int n0) {
+                              int64_t lda, const float* B, int64_t ldb_, int m0, int n0,
+                              int64_t a_bytes_, int64_t b_bytes_) {
     // The wave index is below WAVES; saying so lets the compiler resolve at compile time
     // which operand each copy reads wherever the split of A and B chunks allows.
     __builtin_assume(wave >= 0 && wave < MC::WAVES);
@@ -97,6 +99,8 @@ struct MsCopy {
     a_org = A + (int64_t)m0 * lda;
     b_org = B + n0;
     ldb = ldb_;
+    a_bytes = a_bytes_ - (int64_t)m0 * lda * 4;
+    b_bytes = b_bytes_ - (int64_t)n0 * 4;
 #pragma unroll
     for (int i = 0; i < MC::D; ++i) {
       const int j = wave + i * MC::WAVES;  // which 1 KiB of the stage this copy fills
@@ -121,10 +125,19 @@ struct MsCopy {
   // origin in scalar registers, plus this lane's fixed 32-bit offset, so no vector address
   // arithmetic runs per copy.  (The host takes this path only when every offset inside a
   // tile fits in 32 bits.)
+  template <bool EXACT>
   __device__ inline void issue(int kt, int st) const {
     const uint32_t stage_base = lds_base + (uint32_t)st * (uint32_t)(MC::STAGE * 4);
-    const int32x4 ra = buffer_words(a_org + (int64_t)kt * C::BK);
-    const int32x4 rb = buffer_words(b_org + (int64_t)kt * C::BK * ldb);
+    // Ranges end where A and B end: rows of A past M read as 0, and columns of B past N
+    // read the next row or 0, which reach only C elements the epilogue does not store.
+    // (EXACT: edge tiles; interior tiles lie inside A and B, and the widest range saves
+    // the scalar arithmetic.)
+    const int32x4 ra = buffer_words(
+        a_org + (int64_t)kt * C::BK,
+        EXACT ? TileCopy<C>::range_from(a_bytes, (int64_t)kt * C::BK) : kBufferRange);
+    const int32x4 rb = buffer_words(
+        b_org + (int64_t)kt * C::BK * ldb,
+        EXACT ? TileCopy<C>::range_from(b_bytes, (int64_t)kt * C::BK * ldb) : kBufferRange);
 #pragma unroll
     for (int i = 0; i < MC::D; ++i) {
       const int32x4 r = from_a[i] ? ra : rb;
@@ -200,14 +213,14 @@ __device__ inline void read_frag_ms(const float* stage, const LaneViewMs<C, S>& 
 // wave has finished reading tile l, whose stage the copy issued in the next step
 // overwrites.  Near the end the copy index is clamped to the last tile (a harmless
 // duplicate into a stage no later tile uses), so every wait keeps S-2 tiles in flight.
-template <class C, int S>
+template <class C, int S, bool EDGE>
 __device__ __forceinline__ void ms_step(const float* smem, const MsCopy<C, S>& cp,
                                         const LaneViewMs<C, S>& lv, int l, int k_tiles,
                                         int st, Frag<C> (&f)[2],
                                         floatx16 (&acc)[C::FM][C::FN]) {
   using MC = MsCfg<C, S>;
   constexpr int R = C::BK / 8;
-  cp.issue(min(l + S - 1, k_tiles - 1), st == 0 ? S - 1 : st - 1);
+  cp.template issue<EDGE>(min(l + S - 1, k_tiles - 1), st == 0 ? S - 1 : st - 1);
   const float* cur = smem + st * MC::STAGE;
 #pragma unroll
   for (int q = 0; q + 1 < R; ++q) {
@@ -232,23 +245,23 @@ __device__ __forceinline__ void ms_step(const float* smem, const MsCopy<C, S>& c
 // The MS K-loop: prologue (tiles 0 .. S-2 in flight, tile 0 landed), steps unrolled S at a
 // time so that every stage address is fixed, the remaining steps one by one, and the
 // last tile (nothing left to copy) peeled off.
-template <class C, int S>
+template <class C, int S, bool EDGE>
 __device__ inline void k_loop_ms(float* smem, const MsCopy<C, S>& cp,
                                  const LaneViewMs<C, S>& lv, int k_tiles,
                                  floatx16 (&acc)[C::FM][C::FN]) {
   using MC = MsCfg<C, S>;
   constexpr int R = C::BK / 8;
 #pragma unroll
-  for (int t = 0; t < S - 1; ++t) cp.issue(min(t, k_tiles - 1), t);
+  for (int t = 0; t < S - 1; ++t) cp.template issue<EDGE>(min(t, k_tiles - 1), t);
   ms_wait_tile_barrier<C, S>();
   Frag<C> f[2];
   read_frag_ms(smem, lv, 0, f[0]);
   int l = 0;
   for (; l + S < k_tiles; l += S) {
 #pragma unroll
-    for (int u = 0; u < S; ++u) ms_step<C, S>(smem, cp, lv, l + u, k_tiles, u, f, acc);
+    for (int u = 0; u < S; ++u) ms_step<C, S, EDGE>(smem, cp, lv, l + u, k_tiles, u, f, acc);
   }
-  for (; l + 1 < k_tiles; ++l) ms_step<C, S>(smem, cp, lv, l, k_tiles, l % S, f, acc);
+  for (; l + 1 < k_tiles; ++l) ms_step<C, S, EDGE>(smem, cp, lv, l, k_tiles, l % S, f, acc);
   const float* cur = smem + (l % S) * MC::STAGE;  // last tile: nothing left to copy
 #pragma unroll
   for (int q = 0; q + 1 < R; ++q) {
@@ -273,19 +286,27 @@ gemm_f32_ms_kernel(int M, int N, int K, const float* __restrict__ A, int64_t lda
   zero_acc<C>(acc);
   const int k_tiles = (K + C::BK - 1) / C::BK;
   if (k_tiles > 0) {
-    if (t.unguarded()) {
+    if (t.unguarded() && K % C::BK == 0) {
       MsCopy<C, S> cp;
-      cp.init(smem, t.wave, t.lane, A, lda, B, ldb, t.g.m0, t.g.n0);
+      cp.init(smem, t.wave, t.lane, A, lda, B, ldb, t.g.m0, t.g.n0, t.g.a_bytes, t.g.b_bytes);
       LaneViewMs<C, S> lv;
       lv.init(t.wm, t.wn, t.lane);
-      k_loop_ms<C, S>(smem, cp, lv, k_tiles, acc);
+      if (t.m_full && t.n_full)
+        k_loop_ms<C, S, false>(smem, cp, lv, k_tiles, acc);
+      else
+        k_loop_ms<C, S, true>(smem, cp, lv, k_tiles, acc);
     } else {
-      // Edge, misaligned or K-ragged tiles: the guarded double-buffered loop.
+      // A K tail (its A columns past K must be zeroed, which a direct-to-LDS copy cannot
+      // do) or offsets beyond the 32-bit range: the double-buffered loop, with 16-byte
+      // copies and a masked last tile, or element-guarded copies.
       TileCopy<C> cp;
       cp.init(t.tid, lda, ldb);
       LaneView<C> lv;
       lv.init(t.wm, t.wn, t.lane);
-      k_loop_db<C, true>(smem, cp, lv, t.g, k_tiles, acc);
+      if (t.unguarded())
+        k_loop_db<C, false, true>(smem, cp, lv, t.g, k_tiles, acc);
+      else
+        k_loop_db<C, true>(smem, cp, lv, t.g, k_tiles, acc);
     }
   }
   store_c<C>(acc, Cmat, ldc, t);
