@@ -391,6 +391,34 @@ def test_row_stride_beyond_32bit_tile_offsets(which):
     torch.cuda.empty_cache()
 
 
+def test_large_odd_shapes():
+    """Odd sizes large enough for every tile kind at once (interior, right and bottom edges,
+    the K tail) with leading dimensions that are not multiples of 4: 1537x2049x1027 in full
+    and 4095x4097x4093 on 4096 seeded positions plus its last row and column."""
+    M, N, K = 1537, 2049, 1027
+    A, B = ti.workload_inputs(M, N, K, 9400)
+    C64, Bnd = oracle.gemm_f64(A, B)
+    Ad, Bd = _dev(A), _dev(B)
+    for v in ("auto", "sb", "db", "ms"):
+        r = _ratio(_run(Ad, Bd, v), C64, Bnd)
+        _say(f"[odd] {M}x{N}x{K} {v} ratio={r:.3g}")
+        assert r <= 1.0, v
+    del Ad, Bd
+    M, N, K = 4095, 4097, 4093
+    A, B = ti.workload_inputs(M, N, K, 9401)
+    ri, rj = ti.sample_positions(9401, M, N, 4096)
+    ri = np.concatenate([ri, np.full(64, M - 1), np.arange(M - 64, M)])
+    rj = np.concatenate([rj, np.arange(N - 64, N), np.full(64, N - 1)])
+    c64, bnd = oracle.gemm_f64_sampled(A, B, ri, rj)
+    Ad, Bd = _dev(A), _dev(B)
+    ii, jj = torch.from_numpy(ri).to(DEV), torch.from_numpy(rj).to(DEV)
+    for v in ("auto", "sb", "db", "ms"):
+        C = _run(Ad, Bd, v)
+        r = oracle.tolerance_ratio(C[ii, jj].cpu().numpy(), c64, bnd)
+        _say(f"[odd] {M}x{N}x{K} {v} sampled ratio={r:.3g}")
+        assert r <= 1.0, v
+
+
 def test_wide_dynamic_range():
     """Rows of A and columns of B scaled by powers of two from 2^-30 to 2^30: every product
     stays a normal FP32 number and the bound is relative, so nothing may lose accuracy."""

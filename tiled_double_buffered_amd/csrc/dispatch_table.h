@@ -24,30 +24,32 @@ struct DispatchRow {
 };
 
 static const DispatchRow kDispatch[] = {
-    {128, 128, 128, 2, 6, 7, 6, 6},  // sb 4.58 us, db 4.39 us, ms 4.46 us
-    {127, 193, 61, 3, 6, 6, 6, 6},  // sb 5.23 us, db 5.11 us, ms 5.11 us
-    {513, 257, 129, 3, 6, 6, 6, 6},  // sb 8.95 us, db 7.78 us, ms 7.77 us
-    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.52 us, db 18.27 us, ms 17.91 us
-    {256, 1024, 128, 2, 6, 7, 6, 6},  // sb 4.74 us, db 4.46 us, ms 4.66 us
-    {1024, 128, 256, 2, 6, 7, 6, 6},  // sb 7.14 us, db 6.25 us, ms 6.39 us
-    {4096, 4096, 4096, 2, 1, 9, 1, 3},  // sb 960.86 us, db 901.85 us, ms 914.64 us
-    {8192, 8192, 8192, 2, 0, 9, 0, 3},  // sb 7434.30 us, db 7155.08 us, ms 7238.40 us
-    {256, 256, 256, 2, 6, 7, 6, 6},  // sb 7.12 us, db 6.27 us, ms 6.38 us
-    {512, 512, 512, 2, 6, 7, 6, 6},  // sb 12.28 us, db 10.04 us, ms 10.05 us
-    {768, 768, 768, 3, 6, 7, 6, 6},  // sb 17.74 us, db 14.21 us, ms 13.91 us
-    {1536, 1536, 1536, 2, 6, 7, 6, 6},  // sb 77.41 us, db 68.47 us, ms 68.93 us
-    {2048, 2048, 2048, 2, 3, 6, 3, 3},  // sb 127.27 us, db 117.95 us, ms 121.40 us
-    {3072, 3072, 3072, 3, 6, 7, 6, 6},  // sb 422.96 us, db 417.88 us, ms 406.66 us
-    {6144, 6144, 6144, 2, 4, 4, 4, 3},  // sb 3189.78 us, db 3060.80 us, ms 3063.22 us
-    {64, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.11 us, db 64.82 us, ms 60.75 us
-    {4096, 4096, 512, 2, 2, 4, 2, 3},  // sb 128.00 us, db 122.20 us, ms 124.03 us
-    {2048, 8192, 2048, 2, 2, 4, 2, 3},  // sb 486.43 us, db 457.18 us, ms 463.14 us
-    {4096, 1024, 1024, 2, 3, 7, 3, 3},  // sb 67.09 us, db 61.64 us, ms 63.67 us
-    {1024, 1024, 8192, 3, 6, 7, 6, 6},  // sb 190.59 us, db 127.87 us, ms 122.01 us
-    {16, 4096, 4096, 2, 10, 7, 10, 10},  // sb 116.15 us, db 98.37 us, ms 99.12 us
-    {32, 4096, 4096, 3, 10, 10, 10, 10},  // sb 120.25 us, db 69.00 us, ms 63.14 us
-    {128, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.11 us, db 64.81 us, ms 60.82 us
-    {32, 8192, 8192, 3, 10, 7, 10, 10},  // sb 241.83 us, db 143.57 us, ms 124.43 us
+    {128, 128, 128, 2, 6, 7, 6, 6},  // sb 4.79 us, db 4.47 us, ms 4.52 us
+    {127, 193, 61, 2, 7, 7, 7, 6},  // sb 4.31 us, db 4.28 us, ms 4.32 us
+    {513, 257, 129, 2, 6, 6, 6, 6},  // sb 6.46 us, db 5.90 us, ms 5.97 us
+    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.74 us, db 18.52 us, ms 17.96 us
+    {256, 1024, 128, 2, 6, 7, 6, 6},  // sb 5.02 us, db 4.71 us, ms 4.74 us
+    {1024, 128, 256, 3, 6, 7, 6, 6},  // sb 7.44 us, db 6.49 us, ms 6.47 us
+    {4096, 4096, 4096, 2, 0, 5, 0, 3},  // sb 960.21 us, db 902.68 us, ms 911.33 us
+    {8192, 8192, 8192, 2, 0, 9, 0, 3},  // sb 7443.01 us, db 7150.15 us, ms 7197.94 us
+    {256, 256, 256, 3, 6, 7, 6, 6},  // sb 7.40 us, db 6.47 us, ms 6.45 us
+    {512, 512, 512, 3, 6, 7, 6, 6},  // sb 12.55 us, db 10.29 us, ms 10.10 us
+    {768, 768, 768, 3, 6, 7, 6, 6},  // sb 18.03 us, db 14.48 us, ms 14.04 us
+    {1536, 1536, 1536, 2, 6, 7, 6, 6},  // sb 77.24 us, db 68.51 us, ms 68.80 us
+    {2048, 2048, 2048, 2, 3, 6, 3, 3},  // sb 127.19 us, db 117.92 us, ms 121.26 us
+    {3072, 3072, 3072, 3, 6, 7, 6, 6},  // sb 421.76 us, db 417.91 us, ms 403.43 us
+    {6144, 6144, 6144, 3, 3, 4, 4, 3},  // sb 3176.84 us, db 3052.01 us, ms 3051.46 us
+    {64, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.86 us, db 65.11 us, ms 60.84 us
+    {4096, 4096, 512, 2, 2, 9, 2, 3},  // sb 127.30 us, db 122.49 us, ms 124.06 us
+    {2048, 8192, 2048, 2, 0, 9, 0, 3},  // sb 486.63 us, db 457.56 us, ms 462.29 us
+    {4096, 1024, 1024, 2, 3, 7, 3, 6},  // sb 66.35 us, db 61.92 us, ms 63.67 us
+    {1024, 1024, 8192, 3, 6, 7, 6, 6},  // sb 190.93 us, db 127.86 us, ms 121.35 us
+    {1023, 1023, 1023, 2, 6, 7, 6, 6},  // sb 25.26 us, db 20.74 us, ms 20.74 us
+    {4095, 4095, 4095, 2, 9, 9, 9, 0},  // sb 1003.51 us, db 913.94 us, ms 917.32 us
+    {16, 4096, 4096, 3, 6, 7, 6, 6},  // sb 97.49 us, db 70.28 us, ms 69.57 us
+    {32, 4096, 4096, 3, 10, 7, 10, 10},  // sb 98.10 us, db 69.43 us, ms 63.57 us
+    {128, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.96 us, db 65.33 us, ms 61.26 us
+    {32, 8192, 8192, 3, 10, 7, 10, 10},  // sb 197.49 us, db 143.35 us, ms 124.26 us
 };
 constexpr int kDispatchRows = (int)(sizeof(kDispatch) / sizeof(kDispatch[0]));
 
@@ -101,17 +103,17 @@ struct SplitRow {
 };
 
 static const SplitRow kSplitK[] = {
-    {16, 4096, 4096, 8},  // 1: 98.2, 2: 53.2, 4: 30.8, 8: 22.5, 16: 22.7
-    {32, 4096, 4096, 8},  // 1: 63.4, 2: 35.6, 4: 22.0, 8: 19.0, 16: 29.8
-    {64, 4096, 4096, 4},  // 1: 60.8, 2: 34.7, 4: 21.7, 8: 24.4, 16: 27.0
-    {128, 4096, 4096, 2},  // 1: 61.0, 2: 35.7, 4: 37.2, 8: 39.6, 16: 46.8
-    {32, 8192, 8192, 4},  // 1: 124.0, 2: 67.0, 4: 46.3, 8: 48.4, 16: 55.1
-    {64, 8192, 8192, 2},  // 1: 125.2, 2: 68.7, 4: 71.8, 8: 77.6, 16: 85.4
-    {256, 256, 8192, 16},  // 1: 117.6, 2: 67.2, 4: 37.1, 8: 23.2, 16: 17.4
-    {512, 512, 8192, 4},  // 1: 118.9, 2: 63.7, 4: 37.0, 8: 39.1, 16: 41.1
-    {1024, 1024, 1024, 1},  // 1: 17.9, 2: 24.6, 4: 25.3, 8: 31.2, 16: 39.5
-    {2048, 2048, 2048, 1},  // 1: 118.4, 2: 128.5, 4: 137.0, 8: 151.7, 16: 191.3
-    {4096, 4096, 4096, 1},  // 1: 910.2, 2: 951.8, 4: 983.6, 8: 1085.1, 16: 1260.3
+    {16, 4096, 4096, 8},  // 1: 75.6, 2: 42.2, 4: 26.2, 8: 21.4, 16: 22.6
+    {32, 4096, 4096, 8},  // 1: 63.5, 2: 35.9, 4: 22.8, 8: 19.6, 16: 28.8
+    {64, 4096, 4096, 4},  // 1: 60.9, 2: 35.2, 4: 22.5, 8: 25.8, 16: 29.8
+    {128, 4096, 4096, 2},  // 1: 61.2, 2: 36.1, 4: 38.2, 8: 39.8, 16: 45.8
+    {32, 8192, 8192, 4},  // 1: 124.3, 2: 67.0, 4: 46.1, 8: 48.7, 16: 55.1
+    {64, 8192, 8192, 2},  // 1: 125.1, 2: 73.1, 4: 74.9, 8: 78.5, 16: 86.5
+    {256, 256, 8192, 16},  // 1: 117.9, 2: 62.8, 4: 37.3, 8: 23.4, 16: 17.7
+    {512, 512, 8192, 4},  // 1: 118.7, 2: 63.8, 4: 36.3, 8: 38.9, 16: 41.0
+    {1024, 1024, 1024, 1},  // 1: 17.9, 2: 24.6, 4: 26.2, 8: 30.8, 16: 39.8
+    {2048, 2048, 2048, 1},  // 1: 117.9, 2: 145.7, 4: 136.7, 8: 151.4, 16: 191.9
+    {4096, 4096, 4096, 1},  // 1: 902.9, 2: 1003.1, 4: 981.3, 8: 1076.1, 16: 1262.5
 };
 
 static inline int select_splits(int64_t M, int64_t N, int64_t K) {
