@@ -498,14 +498,19 @@ def main() -> int:
         try:
             import oracle
             threads = oracle.max_threads()
-            rows = threads
+            # successive row blocks of the product until the time budget is spent; the
+            # block size comes from a pilot block so that the last one overshoots little
             t = time.perf_counter()
-            oracle.gemm_f64(A_h[:rows], B_h)
-            dt = time.perf_counter() - t
-            rows = int(min(M, max(threads, threads * round(args.cpu_seconds / dt))))
-            t = time.perf_counter()
-            oracle.gemm_f64(A_h[:rows], B_h)
-            dt = time.perf_counter() - t
+            oracle.gemm_f64(A_h[:threads], B_h)
+            pilot = time.perf_counter() - t
+            block = int(min(M, max(threads, threads * round(args.cpu_seconds / 8 / pilot))))
+            rows, dt = 0, 0.0
+            while rows < M and dt < args.cpu_seconds:
+                r1 = min(M, rows + block)
+                t = time.perf_counter()
+                oracle.gemm_f64(A_h[rows:r1], B_h)
+                dt += time.perf_counter() - t
+                rows = r1
             cpu_tflops = 2.0 * rows * N * K / dt / 1e12
             cpu_baseline = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s",
                             "cores": threads, "kind": "oracle",
