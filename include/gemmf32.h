@@ -75,8 +75,10 @@ enum {
                                   configuration defaults to the single-buffered column  */
 };
 
-/* C = A.B with the variant and tile configuration chosen per shape by the dispatch
- * table (GEMMF32_VARIANT environment variable "sb", "db" or "ms" forces the variant, for
+/* C = A.B with the variant and tile configuration chosen per shape: the measured pick
+ * for a shape in the dispatch table, otherwise the pick of the table's cost model, which
+ * weighs each pair's fixed cost against its time per K tile and round of workgroups over
+ * the 256 compute units (GEMMF32_VARIANT environment variable "sb", "db" or "ms" forces the variant, for
  * measurement; GEMMF32_RASTER=<group_m>[,noxcd] changes the order in which workgroups walk
  * the output tiles, for every launching entry point, also for measurement only).  The
  * pages' lesson that the faster variant depends on the shape is the reason for the table
@@ -88,7 +90,8 @@ int gemm_f32(int64_t M, int64_t N, int64_t K,
              void *stream);
 
 /* C = A.B with the single-buffered K-loop (two barriers per K step); tile configuration
- * from the dispatch table's single-buffered column for this shape. */
+ * from the dispatch table's single-buffered column for this shape (the cost model's best
+ * single-buffered configuration for a shape not in the table). */
 int gemm_f32_sb(int64_t M, int64_t N, int64_t K,
                 const float *A, int64_t lda,
                 const float *B, int64_t ldb,
@@ -96,7 +99,8 @@ int gemm_f32_sb(int64_t M, int64_t N, int64_t K,
                 void *stream);
 
 /* C = A.B with the double-buffered K-loop (one barrier per K step); tile configuration
- * from the dispatch table's double-buffered column for this shape. */
+ * from the dispatch table's double-buffered column for this shape (the cost model's best
+ * double-buffered configuration for a shape not in the table). */
 int gemm_f32_db(int64_t M, int64_t N, int64_t K,
                 const float *A, int64_t lda,
                 const float *B, int64_t ldb,
@@ -104,7 +108,8 @@ int gemm_f32_db(int64_t M, int64_t N, int64_t K,
                 void *stream);
 
 /* C = A.B with the multi-stage direct-to-LDS K-loop; tile configuration from the
- * dispatch table's multi-stage column for this shape.  Edge, misaligned and K-ragged
+ * dispatch table's multi-stage column for this shape (the cost model's pick for a shape
+ * not in the table).  Edge, misaligned and K-ragged
  * tiles of the launch run the guarded double-buffered loop instead. */
 int gemm_f32_ms(int64_t M, int64_t N, int64_t K,
                 const float *A, int64_t lda,
@@ -148,7 +153,7 @@ int gemm_f32_splitk(int64_t M, int64_t N, int64_t K,
 int64_t gemm_f32_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits);
 
 /* The measured best split count for a shape (1 = do not split), from the split table of
- * the dispatch table; host code only.  Negative sizes give GEMMF32_ERR_NEGATIVE_DIM. */
+ * the dispatch table (the nearest row in log2 M, log2 N, log2 K); host code only.  Negative sizes give GEMMF32_ERR_NEGATIVE_DIM. */
 int gemm_f32_splitk_select(int64_t M, int64_t N, int64_t K);
 
 /* The dispatch decision for a shape, without launching: *variant receives

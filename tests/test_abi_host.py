@@ -156,6 +156,81 @@ def test_select_matches_the_table_on_its_rows():
         assert (v, c) in ((tdb.VARIANT_SB, sb), (tdb.VARIANT_DB, db), (tdb.VARIANT_MS, ms))
 
 
+def _model_rows():
+    text = open(os.path.join(build.CSRC, "dispatch_table.h")).read()
+    body = text[text.index("kModel[] = {"):]
+    body = body[:body.index("};")]
+    return [(int(m.group(1)), int(m.group(2)), float(m.group(3)), float(m.group(4)))
+            for m in re.finditer(r"\{\s*(\d+),\s*(\d+),\s*([0-9.eE+-]+),\s*([0-9.eE+-]+)\s*\}",
+                                 body)]
+
+
+def _model_pick(M, N, K, rows, dims, variant=0):
+    """The cost-model rule, read independently of the C++: least a + g * rounds * k_tiles,
+    rounds = ceil(tiles / 256), first row on ties."""
+    best = None
+    for (v, c, a, g) in rows:
+        if variant and v != variant:
+            continue
+        bm, bn, bk = dims[c]
+        tiles = -(-M // bm) * -(-N // bn)
+        t = a + g * float(-(-tiles // 256)) * float(-(-K // bk))
+        if best is None or t < best[0]:
+            best = (t, v, c)
+    return best[1], best[2]
+
+
+def test_cost_model_has_a_row_per_pair():
+    rows = _model_rows()
+    n = tdb.gemm_f32_num_configs()
+    assert sorted((v, c) for v, c, _, _ in rows) == sorted(
+        (v, c) for v in (tdb.VARIANT_SB, tdb.VARIANT_DB, tdb.VARIANT_MS) for c in range(n))
+    assert all(a >= 0 and g >= 0 for _, _, a, g in rows)
+
+
+# Off-table shapes, among them grids that a 256x256 or 128x128 tile leaves mostly empty.
+OFF_TABLE = [(793, 5620, 654), (6682, 178, 1587), (4385, 311, 1702), (1976, 2199, 279),
+             (3000, 3000, 3000), (8191, 8191, 8191), (1, 1, 1), (5, 70000, 3), (64, 64, 0),
+             (100, 100, 100000), (12288, 12288, 64), (2000, 40, 9000)]
+
+
+@pytest.mark.parametrize("shape", OFF_TABLE)
+def test_select_off_table_follows_the_cost_model(shape):
+    table = {(m, n, k) for (m, n, k, *_rest) in _dispatch_rows()}
+    assert shape not in table
+    rows = _model_rows()
+    dims = {c: (i["BM"], i["BN"], i["BK"]) for c in range(tdb.gemm_f32_num_configs())
+            for i in [tdb.gemm_f32_config_info(c)[1]]}
+    assert tdb.gemm_f32_select(*shape) == (tdb.OK, *_model_pick(*shape, rows, dims))
+    for var in (tdb.VARIANT_SB, tdb.VARIANT_DB, tdb.VARIANT_MS):
+        assert tdb.gemm_f32_select_cfg(*shape, var) == _model_pick(*shape, rows, dims, var)[1]
+
+
+def test_under_filled_grids_get_small_tiles():
+    """793 x 5620 x 654 makes 88 workgroups of 256 x 256 for 256 compute units (and 6682 x
+    178 x 1587 makes 106 of 128 x 128); the model must pick a tile that keeps at least half
+    of the compute units busy."""
+    for shape in [(793, 5620, 654), (6682, 178, 1587)]:
+        _, _, c = tdb.gemm_f32_select(*shape)
+        _, info = tdb.gemm_f32_config_info(c)
+        tiles = -(-shape[0] // info["BM"]) * -(-shape[1] // info["BN"])
+        assert tiles >= 128, (shape, c, tiles)
+
+
+def test_model_fit_recovers_known_costs():
+    from tiled_double_buffered_amd import tune
+    xs = [1, 3, 10, 40, 200, 1000]
+    a, g = tune._fit_pair(xs, [4.0 + 0.5 * x for x in xs])
+    assert abs(a - 4.0) < 1e-9 and abs(g - 0.5) < 1e-12
+    # a negative intercept is clamped to zero
+    xs = [10, 40, 200, 1000]
+    a, g = tune._fit_pair(xs, [-2.0 + 0.5 * x for x in xs])
+    assert a == 0.0 and g > 0
+    assert tune.model_features(793, 5620, 654, (256, 256, 16)) == 1 * 41
+    assert tune.model_features(793, 5620, 654, (64, 64, 32)) == 5 * 21
+    assert tune.model_features(793, 5620, 654, (64, 64, 32), wg_factor=4) == 18 * 21
+
+
 def _dispatch_rows():
     text = open(os.path.join(build.CSRC, "dispatch_table.h")).read()
     body = text[text.index("kDispatch[] = {"):]

@@ -237,9 +237,11 @@ static int run_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t l
   const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)(((M - 1) * ldc + N) * 4);
   if ((w0 < a1 && a0 < w1) || (w0 < b1 && b0 < w1) || (w0 < c1 && c0 < w1))
     return GEMMF32_ERR_ALIAS;
-  int v = 0, cfg = 0;
-  select_shape(M, N, kc, &v, &cfg);
-  rc = launch(v, cfg, M, N, K, A, lda, B, ldb, ws, N, stream, used, (int)kc, M * N);
+  // The chunks run side by side in one grid, so the tile is chosen for `used` times the
+  // workgroups of one chunk's product.
+  const ModelRow& pick = model_pick(M, N, kc, 0, used);
+  rc = launch(pick.variant, pick.cfg, M, N, K, A, lda, B, ldb, ws, N, stream, used, (int)kc,
+              M * N);
   if (rc != GEMMF32_OK) return rc;
   const bool vec = (N % 4) == 0 && (ldc % 4) == 0 && ((uintptr_t)ws & 15u) == 0 &&
                    ((uintptr_t)C & 15u) == 0;

@@ -8,8 +8,13 @@ aware group synchronization on M1 Max", section "Controlled implementation compa
 for each shape, `rounds` rounds visit every (variant, configuration) pair in an order that
 rotates from round to round; each visit times `batches` batches of back-to-back launches
 (each batch at least `batch_ms` of GPU time) with HIP events on the launch stream; a pair's
-time is the median over rounds of the per-round median batch.  The fastest single-buffered
-and double-buffered configurations and the overall winner go into the table.
+time is the median over rounds of the per-round median batch.  The fastest configuration
+of each variant and the overall winner go into the table (within 0.5% of the fastest, the
+larger tile, then the smaller LDS footprint).  The same measurements, plus those of seeded
+shapes outside the table, fit the cost model that picks for every other shape.
+
+    python -m tiled_double_buffered_amd.tune --holdout 40   # dispatcher regret on 40 seeded
+                                                            # shapes outside the table
 
 Timing does not depend on the values multiplied, so inputs are seeded uniform values.
 """
@@ -32,8 +37,8 @@ SHAPES = [
     # the workloads
     (128, 128, 128), (127, 193, 61), (513, 257, 129), (1024, 1024, 1024),
     (256, 1024, 128), (1024, 128, 256), (4096, 4096, 4096), (8192, 8192, 8192),
-    # more points for the nearest-shape rule; the squares also trace the SB / DB regimes
-    # from 256 to 8192
+    # more measured points, also fitted by the cost model; the squares trace the SB / DB
+    # regimes from 256 to 8192
     (256, 256, 256), (512, 512, 512), (768, 768, 768), (1536, 1536, 1536),
     (2048, 2048, 2048), (3072, 3072, 3072), (6144, 6144, 6144),
     (64, 4096, 4096), (4096, 4096, 512), (2048, 8192, 2048), (4096, 1024, 1024),
@@ -57,8 +62,8 @@ HEADER_TEMPLATE = """// Per-shape dispatch table: (M, N, K) -> variant and tile 
 // Buffering", last two paragraphs; "Case Study: The Double-Buffered GEMM", paragraph on
 // the three regimes).  The rows below were measured on {device} by
 // tiled_double_buffered_amd/tune.py ({rounds} rotated rounds x {batches} batches of >= {batch_ms} ms
-// per pair), which rewrites this file; a shape that is not in the table takes the row
-// nearest to it in (log2 M, log2 N, log2 K).
+// per pair), which rewrites this file.  A shape in the table takes its measured pick; any
+// other shape takes the pick of the cost model further down, fitted to the same runs.
 //
 // Columns: M, N, K, best variant (1 = single-buffered, 2 = double-buffered, 3 = multi-stage
 // direct-to-LDS), its tile configuration, and the best configuration of each variant.
@@ -82,44 +87,76 @@ constexpr int kDispatchRows = (int)(sizeof(kDispatch) / sizeof(kDispatch[0]));
 
 static inline double dispatch_log2(int64_t x) {{ return x > 0 ? std::log2((double)x) : -1.0; }}
 
-// (log2 M, log2 N, log2 K) of every row, computed once (thread-safe static initialization),
-// so that a lookup costs three logarithms instead of three per row.
-struct DispatchLogs {{
-  double v[kDispatchRows][3];
-  DispatchLogs() {{
-    for (int i = 0; i < kDispatchRows; ++i) {{
-      v[i][0] = dispatch_log2(kDispatch[i].m);
-      v[i][1] = dispatch_log2(kDispatch[i].n);
-      v[i][2] = dispatch_log2(kDispatch[i].k);
-    }}
-  }}
+static inline const DispatchRow* dispatch_exact(int64_t M, int64_t N, int64_t K) {{
+  for (int i = 0; i < kDispatchRows; ++i)
+    if (kDispatch[i].m == M && kDispatch[i].n == N && kDispatch[i].k == K) return &kDispatch[i];
+  return nullptr;
+}}
+
+// Cost model of every (variant, configuration) for shapes outside the table.  The features
+// are the two the regimes turn on: how many tiles the busiest compute unit multiplies,
+// rounds = ceil(workgroups / 256), and the K tiles per tile, k_tiles = ceil(K / BK).  A
+// launch is modelled as
+//     a + g * rounds * k_tiles   microseconds,
+// a being the fixed cost (launch, first copy, epilogue) and g the time of one K tile of one
+// round.  a and g were fitted per pair by least squares on relative error, both kept
+// >= 0, to the {nfit} shapes measured for this file (the table's {ntable} and {ntrain} seeded
+// shapes outside it).
+struct ModelRow {{
+  int variant, cfg;
+  double a_us, g_us;
 }};
 
-static inline const DispatchRow& dispatch_nearest(int64_t M, int64_t N, int64_t K) {{
-  static const DispatchLogs logs;
-  const double lm = dispatch_log2(M), ln = dispatch_log2(N), lk = dispatch_log2(K);
+static const ModelRow kModel[] = {{
+{model_rows}
+}};
+constexpr int kModelRows = (int)(sizeof(kModel) / sizeof(kModel[0]));
+constexpr int64_t kModelCUs = 256;
+
+// Modelled microseconds of one launch; wg_factor multiplies the workgroup count (the K
+// chunks of a split-K launch run side by side in one grid).
+static inline double model_us(const ModelRow& r, int64_t M, int64_t N, int64_t K,
+                              int64_t wg_factor) {{
+  const CfgEntry& e = kConfigs[r.cfg];
+  const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn) * wg_factor;
+  const int64_t rounds = (tiles + kModelCUs - 1) / kModelCUs;
+  const int64_t k_tiles = (K + e.bk - 1) / e.bk;
+  return r.a_us + r.g_us * (double)rounds * (double)k_tiles;
+}}
+
+// The row with the least modelled time (variant 0: any variant), first row on ties.
+static inline const ModelRow& model_pick(int64_t M, int64_t N, int64_t K, int variant,
+                                         int64_t wg_factor) {{
   int best = 0;
-  double best_d = 1e300;
-  for (int i = 0; i < kDispatchRows; ++i) {{
-    const double dm = lm - logs.v[i][0], dn = ln - logs.v[i][1], dk = lk - logs.v[i][2];
-    const double d = dm * dm + dn * dn + dk * dk;
-    if (d < best_d) {{
-      best_d = d;
+  double best_t = 0.0;
+  bool found = false;
+  for (int i = 0; i < kModelRows; ++i) {{
+    if (variant != 0 && kModel[i].variant != variant) continue;
+    const double t = model_us(kModel[i], M, N, K, wg_factor);
+    if (!found || t < best_t) {{
       best = i;
+      best_t = t;
+      found = true;
     }}
   }}
-  return kDispatch[best];
+  return kModel[best];
 }}
 
 static inline void select_shape(int64_t M, int64_t N, int64_t K, int* variant, int* cfg) {{
-  const DispatchRow& r = dispatch_nearest(M, N, K);
-  *variant = r.variant;
-  *cfg = r.cfg;
+  if (const DispatchRow* r = dispatch_exact(M, N, K)) {{
+    *variant = r->variant;
+    *cfg = r->cfg;
+    return;
+  }}
+  const ModelRow& m = model_pick(M, N, K, 0, 1);
+  *variant = m.variant;
+  *cfg = m.cfg;
 }}
 
 static inline int select_for_variant(int64_t M, int64_t N, int64_t K, int variant) {{
-  const DispatchRow& r = dispatch_nearest(M, N, K);
-  return variant == 1 ? r.sb_cfg : variant == 3 ? r.ms_cfg : r.db_cfg;
+  if (const DispatchRow* r = dispatch_exact(M, N, K))
+    return variant == 1 ? r->sb_cfg : variant == 3 ? r->ms_cfg : r->db_cfg;
+  return model_pick(M, N, K, variant, 1).cfg;
 }}
 
 // Split-K: measured best number of K chunks per shape (1 = do not split), nearest row in
@@ -380,16 +417,143 @@ def raster_study(shapes=RASTER_SHAPES, settings=RASTER_SETTINGS, rounds=2, batch
     return out
 
 
-def table_rows(results):
+def holdout_shapes(n, seed=2024, lo=5.0, hi=13.0, max_flop=2.0 * 4096 ** 3, exclude=()):
+    """n shapes drawn with each of M, N, K log-uniform in [2**lo, 2**hi] (so sizes are
+    mostly not multiples of any tile), redrawn while 2MNK exceeds max_flop.  Seeded; none
+    of them is a row of the table or in `exclude`."""
+    import random
+
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        m, n_, k = (int(round(2.0 ** rng.uniform(lo, hi))) for _ in range(3))
+        if (2.0 * m * n_ * k <= max_flop and (m, n_, k) not in SHAPES
+                and (m, n_, k) not in exclude and (m, n_, k) not in out):
+            out.append((m, n_, k))
+    return out
+
+
+def train_shapes():
+    """The seeded shapes outside the table that the cost model is also fitted to."""
+    return holdout_shapes(TRAIN_COUNT, TRAIN_SEED)
+
+
+def holdout_study(n=40, seed=2024, rounds=2, batches=5, batch_ms=20.0, log=print):
+    """How far the dispatcher's pick is from the best measured (variant, configuration) on
+    shapes it was not tuned on: per shape, the time of the dispatched pair over the time of
+    the fastest pair (1.0 = the dispatcher found the best)."""
+    shapes = holdout_shapes(n, seed, exclude=set(train_shapes()))
+    results = measure(shapes, rounds, batches, batch_ms, log=log)
+    out = []
+    for r in results:
+        M, N, K = r["M"], r["N"], r["K"]
+        _, v, cfg = tdb.gemm_f32_select(M, N, K)
+        pick = f"{NAMES[v]}{cfg}"
+        best = min(r["us"], key=r["us"].get)
+        regret = r["us"][pick] / r["us"][best]
+        out.append({"M": M, "N": N, "K": K, "pick": pick, "pick_us": r["us"][pick],
+                    "best": best, "best_us": r["us"][best], "regret": regret,
+                    "us": r["us"]})
+        log(f"{M}x{N}x{K}: dispatched {pick} {r['us'][pick]:.2f} us, best {best} "
+            f"{r['us'][best]:.2f} us, regret {regret:.3f}")
+    regrets = sorted(o["regret"] for o in out)
+    summary = {"shapes": len(out), "median": statistics.median(regrets),
+               "p90": regrets[int(0.9 * (len(regrets) - 1))], "max": regrets[-1],
+               "within_5pct": sum(1 for x in regrets if x <= 1.05) / len(regrets)}
+    log("dispatcher regret on held-out shapes: " + json.dumps(summary))
+    return {"summary": summary, "rows": out}
+
+
+# Shapes measured only to fit the cost model (never table rows).
+TRAIN_SEED = 1
+TRAIN_COUNT = 48
+
+
+def model_features(M, N, K, cfg_dims, wg_factor=1, cus=256):
+    """rounds * k_tiles of the cost model for a configuration of tile BM x BN x BK."""
+    bm, bn, bk = cfg_dims
+    tiles = -(-M // bm) * -(-N // bn) * wg_factor
+    return -(-tiles // cus) * -(-K // bk)
+
+
+def _fit_pair(xs, ys):
+    """a, g >= 0 minimising sum(((a + g*x) / y - 1)**2)."""
+    p = [1.0 / y for y in ys]
+    q = [x / y for x, y in zip(xs, ys)]
+    spp = sum(v * v for v in p)
+    sqq = sum(v * v for v in q)
+    spq = sum(u * v for u, v in zip(p, q))
+    sp, sq = sum(p), sum(q)
+    cands = []
+    det = spp * sqq - spq * spq
+    if det > 1e-12 * spp * max(sqq, 1e-300):
+        a = (sp * sqq - sq * spq) / det
+        g = (spp * sq - spq * sp) / det
+        if a >= 0 and g >= 0:
+            cands.append((a, g))
+    if sqq > 0:
+        cands.append((0.0, sq / sqq))
+    cands.append((sp / spp, 0.0))
+
+    def obj(ag):
+        return sum(((ag[0] + ag[1] * x) / y - 1.0) ** 2 for x, y in zip(xs, ys))
+    return min(cands, key=obj)
+
+
+def fit_model(rows, cfg_dims):
+    """Per (variant, configuration): (variant id, cfg, a_us, g_us, median |relative error|)
+    of the cost model a + g * rounds * k_tiles over the measured rows."""
+    out = []
+    ids = {"sb": tdb.VARIANT_SB, "db": tdb.VARIANT_DB, "ms": tdb.VARIANT_MS}
+    keys = sorted(rows[0]["us"], key=lambda k: (ids[k[:2]], int(k[2:])))
+    for key in keys:
+        cfg = int(key[2:])
+        xs = [model_features(r["M"], r["N"], r["K"], cfg_dims[cfg][:3]) for r in rows]
+        ys = [r["us"][key] for r in rows]
+        a, g = _fit_pair(xs, ys)
+        err = statistics.median(abs((a + g * x) / y - 1.0) for x, y in zip(xs, ys))
+        out.append((ids[key[:2]], cfg, a, g, err))
+    return out
+
+
+def config_dims():
+    """cfg -> (BM, BN, BK, LDS bytes of the double-buffered loop)."""
+    dims = {}
+    for c in range(tdb.gemm_f32_num_configs()):
+        _, info = tdb.gemm_f32_config_info(c)
+        dims[c] = (info["BM"], info["BN"], info["BK"], info["lds_bytes_db"])
+    return dims
+
+
+# Pairs whose times differ by less than this are within run-to-run noise (two tunes on two
+# boxes ordered the 256x256 and 256x128 tiles at 8192^3 both ways, 0.2% apart).
+TIE_TOLERANCE = 0.005
+
+
+def _pick(cands, dims):
+    """Fastest (name, us) of cands, except that among those within TIE_TOLERANCE of it the
+    largest tile wins (fewest bytes fetched per FLOP), then the smallest LDS footprint, then
+    the faster: a choice that noise between runs does not flip."""
+    fastest = min(v for _, v in cands)
+    close = [(k, v) for k, v in cands if v <= fastest * (1.0 + TIE_TOLERANCE)]
+
+    def key(kv):
+        bm, bn, _bk, lds = dims[int(kv[0][2:])]
+        return (-bm * bn, lds, kv[1])
+    return min(close, key=key)
+
+
+def table_rows(results, dims=None):
+    dims = dims or config_dims()
     rows = []
     for r in results:
         best = {}
         for name in ("sb", "db", "ms"):
             cands = [(k, v) for k, v in r["us"].items() if k[:2] == name]
             if cands:
-                k, v = min(cands, key=lambda kv: kv[1])
+                k, v = _pick(cands, dims)
                 best[name] = (int(k[2:]), v)
-        win = min(best, key=lambda n: best[n][1])
+        win = _pick([(n + str(c), v) for n, (c, v) in best.items()], dims)[0][:2]
         vid = {"sb": 1, "db": 2, "ms": 3}[win]
         ms = best.get("ms", best["db"])
         rows.append((r["M"], r["N"], r["K"], vid, best[win][0], best["sb"][0], best["db"][0],
@@ -406,16 +570,22 @@ def split_rows(split_results):
     return lines
 
 
-def write_header(results, device, rounds, batches, batch_ms, path=None, split_results=None):
+def write_header(results, device, rounds, batches, batch_ms, path=None, split_results=None,
+                 train=None):
     path = path or os.path.join(CSRC, "dispatch_table.h")
     lines = []
     for (m, n, k, v, c, s, d, ms, sb_us, db_us, ms_us) in table_rows(results):
         lines.append(f"    {{{m}, {n}, {k}, {v}, {c}, {s}, {d}, {ms}}},  // sb {sb_us:.2f} us, "
                      f"db {db_us:.2f} us, ms {ms_us:.2f} us")
     srows = split_rows(split_results) if split_results else ["    {1024, 1024, 1024, 1},"]
+    fit_rows = list(results) + list(train or [])
+    mrows = [f"    {{{v}, {c}, {a:.4f}, {g:.5f}}},  // median |error| {100 * e:.1f}%"
+             for (v, c, a, g, e) in fit_model(fit_rows, config_dims())]
     text = HEADER_TEMPLATE.format(device=device, rounds=rounds, batches=batches,
                                   batch_ms=int(batch_ms), rows="\n".join(lines),
-                                  split_rows="\n".join(srows))
+                                  split_rows="\n".join(srows), model_rows="\n".join(mrows),
+                                  nfit=len(fit_rows), ntable=len(results),
+                                  ntrain=len(fit_rows) - len(results))
     with open(path, "w") as f:
         f.write(text)
     return path
@@ -435,8 +605,12 @@ def main(argv=None) -> int:
                     help="time 3-, 2- and 1-barrier loops at equal tile configurations")
     ap.add_argument("--raster-study", action="store_true",
                     help="time the dispatched kernels under different workgroup orders")
+    ap.add_argument("--holdout", type=int, default=0, metavar="N",
+                    help="time every pair on N seeded shapes outside the table and report "
+                         "how far the dispatcher's pick is from the fastest")
+    ap.add_argument("--holdout-seed", type=int, default=2024)
     args = ap.parse_args(argv)
-    if args.barrier_study or args.raster_study:
+    if args.barrier_study or args.raster_study or args.holdout:
         import torch
 
         props = torch.cuda.get_device_properties(0)
@@ -451,6 +625,10 @@ def main(argv=None) -> int:
             res["raster_study"] = raster_study(rounds=args.rounds, batches=args.batches,
                                                batch_ms=args.batch_ms,
                                                log=lambda *a: print(*a, flush=True))
+        if args.holdout:
+            res["holdout"] = holdout_study(args.holdout, args.holdout_seed, args.rounds,
+                                           args.batches, args.batch_ms,
+                                           log=lambda *a: print(*a, flush=True))
         if args.out:
             with open(args.out, "w") as f:
                 json.dump(res, f, indent=1)
@@ -459,7 +637,8 @@ def main(argv=None) -> int:
         with open(args.from_json) as f:
             data = json.load(f)
         print(write_header(data["results"], data["device"], data["rounds"], data["batches"],
-                           data["batch_ms"], split_results=data.get("splits")))
+                           data["batch_ms"], split_results=data.get("splits"),
+                           train=data.get("train")))
         return 0
     import torch
 
@@ -468,17 +647,20 @@ def main(argv=None) -> int:
     t0 = time.time()
     results = measure(SHAPES, args.rounds, args.batches, args.batch_ms,
                       log=lambda *a: print(*a, flush=True))
+    train = measure(train_shapes(), args.rounds, args.batches, args.batch_ms,
+                    log=lambda *a: print(*a, flush=True))
     splits = split_study(rounds=args.rounds, batches=args.batches, batch_ms=args.batch_ms,
                          log=lambda *a: print(*a, flush=True))
     data = {"device": device, "rounds": args.rounds, "batches": args.batches,
             "batch_ms": args.batch_ms, "library": tdb.gemm_f32_version(),
-            "seconds": time.time() - t0, "results": results, "splits": splits}
+            "seconds": time.time() - t0, "results": results, "train": train,
+            "splits": splits}
     if args.out:
         with open(args.out, "w") as f:
             json.dump(data, f, indent=1)
     if args.write_header:
         print(write_header(results, device, args.rounds, args.batches, args.batch_ms,
-                           split_results=splits))
+                           split_results=splits, train=train))
     return 0
 
 
