@@ -52,7 +52,7 @@ enum {
 
 /* Variants of the K-loop. */
 enum {
-    GEMMF32_VARIANT_AUTO = 0,  /* per-shape choice from the measured dispatch table      */
+    GEMMF32_VARIANT_AUTO = 0,  /* per-shape choice: dispatch table, else its cost model */
     GEMMF32_VARIANT_SB = 1,    /* one LDS slot: load -> barrier -> compute -> barrier,
                                   two barriers per K step ("Case Study: The
                                   Double-Buffered GEMM", second paragraph: the sibling) */
@@ -137,7 +137,7 @@ int gemm_f32_ex(int64_t M, int64_t N, int64_t K,
  * partials into C in a fixed order, so the result is deterministic (it differs in
  * rounding, within the accuracy of one product, from the unsplit one).  The workspace is
  * owned by the caller and overwritten; it may be NULL when fewer than two chunks result.
- * `splits` = 0 takes the measured choice of gemm_f32_splitk_select.  Both kernels go on
+ * `splits` = 0 takes the modelled choice of gemm_f32_splitk_select.  Both kernels go on
  * `stream`.  Errors as for gemm_f32, plus GEMMF32_ERR_BAD_CONFIG for `splits` outside
  * 0 .. 64, GEMMF32_ERR_BAD_LD for a workspace that is too small, GEMMF32_ERR_NULL_PTR /
  * _MISALIGNED / _ALIAS for a bad workspace pointer. */
@@ -148,12 +148,14 @@ int gemm_f32_splitk(int64_t M, int64_t N, int64_t K,
                     int splits, float *workspace, int64_t workspace_floats,
                     void *stream);
 
-/* Workspace floats gemm_f32_splitk needs for this shape and split count (0 = the measured
+/* Workspace floats gemm_f32_splitk needs for this shape and split count (0 = the modelled
  * choice; the result is 0 when it will not split), or a negative error code. */
 int64_t gemm_f32_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits);
 
-/* The measured best split count for a shape (1 = do not split), from the split table of
- * the dispatch table (the nearest row in log2 M, log2 N, log2 K); host code only.  Negative sizes give GEMMF32_ERR_NEGATIVE_DIM. */
+/* The split count for a shape (1 = do not split) with the least modelled time among 1, 2,
+ * 4, 8 and 16: the dispatch table's cost model of the chunks' GEMM in one grid plus the
+ * split overhead fitted to the measured split study; host code only.  Negative sizes give
+ * GEMMF32_ERR_NEGATIVE_DIM. */
 int gemm_f32_splitk_select(int64_t M, int64_t N, int64_t K);
 
 /* The dispatch decision for a shape, without launching: *variant receives

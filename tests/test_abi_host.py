@@ -266,6 +266,82 @@ def test_splitk_workspace_sizes():
     assert tdb.gemm_f32_splitk_select(-1, 2, 3) == tdb.ERR_NEGATIVE_DIM
 
 
+def _header_text():
+    return open(os.path.join(build.CSRC, "dispatch_table.h")).read()
+
+
+def _split_model_constants():
+    text = _header_text()
+    consts = [float(re.search(name + r" = ([0-9.eE+-]+);", text).group(1))
+              for name in ("kSplitFixedUs", "kSplitUsPerMB", "kSplitUsPerRound")]
+    choices = [int(x) for x in
+               re.search(r"kSplitChoices\[\] = \{([^}]*)\}", text).group(1).split(",")]
+    return consts, choices
+
+
+def _split_pick(M, N, K, rows, dims, consts, choices):
+    """The split-count rule, read independently of the C++: least modelled time, where a
+    split launch costs the model's best GEMM of its chunks in one grid, plus a fixed cost,
+    a cost per MB of (2 * chunks + 1) * M * N * 4 bytes and a cost per round of workgroups
+    of that grid; first count on ties."""
+    r0, per_mb, per_round = consts
+
+    def gemm(m, n, k, wg):
+        best = None
+        for (v, c, a, g) in rows:
+            bm, bn, bk = dims[c]
+            tiles = -(-m // bm) * -(-n // bn) * wg
+            t = a + g * float(-(-tiles // 256)) * float(-(-k // bk))
+            if best is None or t < best[0]:
+                best = (t, tiles)
+        return best
+    best = None
+    for sp in choices:
+        kc = max(64, -(-(-(-K // sp)) // 64) * 64)
+        used = -(-K // kc) if K > 0 else 1
+        if used <= 1:
+            t = gemm(M, N, K, 1)[0]
+        else:
+            g, tiles = gemm(M, N, kc, used)
+            t = (g + r0 + per_mb * ((2 * used + 1) * M * N * 4.0 / 1e6)
+                 + per_round * float(-(-tiles // 256)))
+        if best is None or t < best[0]:
+            best = (t, sp)
+    return best[1]
+
+
+@pytest.mark.parametrize("shape", [(16, 4096, 4096), (120, 2401, 3849), (10, 3657, 15587),
+                                   (766, 2342, 13171), (256, 256, 8192), (4096, 4096, 4096),
+                                   (1, 1, 1), (7, 9, 0), (1, 50000, 64)])
+def test_split_count_follows_the_split_model(shape):
+    consts, choices = _split_model_constants()
+    assert min(consts) >= 0 and 1 in choices
+    dims = {c: (i["BM"], i["BN"], i["BK"]) for c in range(tdb.gemm_f32_num_configs())
+            for i in [tdb.gemm_f32_config_info(c)[1]]}
+    assert tdb.gemm_f32_splitk_select(*shape) == _split_pick(*shape, _model_rows(), dims,
+                                                             consts, choices)
+
+
+def test_split_model_agrees_with_the_split_study():
+    """Over the shapes of the split study (the rows' trailing comments hold the measured
+    times of every count), the modelled count's time over the fastest count's: median at
+    most 1.02, at least 80% of the shapes within 5%, none beyond 1.25."""
+    text = _header_text()
+    body = text[text.index("kSplitK[] = {"):]
+    body = body[:body.index("};")]
+    rows = re.findall(r"\{(\d+), (\d+), (\d+), (\d+)\},\s*//\s*(.*)", body)
+    assert len(rows) >= 10
+    regrets = []
+    for (m, n, k, _best, times) in rows:
+        us = {int(a): float(b) for a, b in re.findall(r"(\d+): ([0-9.]+)", times)}
+        pick = tdb.gemm_f32_splitk_select(int(m), int(n), int(k))
+        regrets.append(us[pick] / min(us.values()))
+    regrets.sort()
+    assert regrets[len(regrets) // 2] <= 1.02, regrets
+    assert sum(r <= 1.05 for r in regrets) >= 0.8 * len(regrets), regrets
+    assert regrets[-1] <= 1.25, regrets
+
+
 def test_splitk_validation_before_launch():
     """Every call here fails validation (so nothing launches on the fake pointers)."""
     f = tdb.gemm_f32_splitk

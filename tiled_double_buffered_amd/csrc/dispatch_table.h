@@ -24,32 +24,32 @@ struct DispatchRow {
 };
 
 static const DispatchRow kDispatch[] = {
-    {128, 128, 128, 2, 6, 7, 6, 6},  // sb 4.81 us, db 4.69 us, ms 4.76 us
-    {127, 193, 61, 1, 7, 7, 6, 7},  // sb 4.55 us, db 4.58 us, ms 4.60 us
-    {513, 257, 129, 2, 6, 6, 6, 6},  // sb 6.49 us, db 5.93 us, ms 6.03 us
-    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.76 us, db 18.54 us, ms 17.98 us
-    {256, 1024, 128, 2, 6, 7, 6, 6},  // sb 5.02 us, db 4.72 us, ms 4.76 us
-    {1024, 128, 256, 3, 6, 7, 6, 6},  // sb 7.44 us, db 6.52 us, ms 6.49 us
-    {4096, 4096, 4096, 2, 0, 9, 0, 8},  // sb 962.85 us, db 909.98 us, ms 919.79 us
-    {8192, 8192, 8192, 2, 0, 9, 0, 3},  // sb 7459.57 us, db 7198.21 us, ms 7239.15 us
-    {256, 256, 256, 3, 6, 7, 6, 6},  // sb 7.43 us, db 6.45 us, ms 6.42 us
-    {512, 512, 512, 3, 6, 7, 6, 6},  // sb 12.58 us, db 10.31 us, ms 10.12 us
-    {768, 768, 768, 3, 6, 7, 6, 6},  // sb 18.06 us, db 14.49 us, ms 14.05 us
-    {1536, 1536, 1536, 2, 6, 7, 6, 6},  // sb 77.21 us, db 68.59 us, ms 68.78 us
-    {2048, 2048, 2048, 2, 3, 6, 3, 3},  // sb 127.85 us, db 118.23 us, ms 121.70 us
-    {3072, 3072, 3072, 3, 6, 7, 6, 6},  // sb 426.68 us, db 422.58 us, ms 407.06 us
-    {6144, 6144, 6144, 3, 3, 4, 4, 3},  // sb 3188.94 us, db 3061.77 us, ms 3060.85 us
-    {64, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.64 us, db 65.18 us, ms 61.10 us
-    {4096, 4096, 512, 2, 2, 9, 2, 3},  // sb 128.09 us, db 123.19 us, ms 124.79 us
-    {2048, 8192, 2048, 2, 2, 9, 2, 8},  // sb 487.98 us, db 458.02 us, ms 466.23 us
-    {4096, 1024, 1024, 2, 3, 7, 3, 3},  // sb 66.70 us, db 61.99 us, ms 63.79 us
-    {1024, 1024, 8192, 3, 6, 7, 6, 6},  // sb 190.92 us, db 128.79 us, ms 122.49 us
-    {1023, 1023, 1023, 3, 6, 7, 6, 6},  // sb 25.30 us, db 21.03 us, ms 20.79 us
-    {4095, 4095, 4095, 2, 9, 9, 9, 0},  // sb 999.12 us, db 916.25 us, ms 924.16 us
-    {16, 4096, 4096, 3, 6, 7, 6, 6},  // sb 97.43 us, db 70.26 us, ms 69.49 us
-    {32, 4096, 4096, 3, 10, 7, 10, 10},  // sb 97.83 us, db 69.37 us, ms 63.40 us
-    {128, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.72 us, db 65.15 us, ms 61.12 us
-    {32, 8192, 8192, 3, 10, 7, 10, 10},  // sb 198.26 us, db 144.27 us, ms 124.57 us
+    {128, 128, 128, 3, 6, 7, 6, 6},  // sb 4.77 us, db 4.55 us, ms 4.52 us
+    {127, 193, 61, 3, 10, 10, 10, 10},  // sb 4.23 us, db 4.21 us, ms 4.16 us
+    {513, 257, 129, 2, 6, 6, 6, 6},  // sb 6.44 us, db 5.87 us, ms 5.94 us
+    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.73 us, db 18.53 us, ms 17.97 us
+    {256, 1024, 128, 2, 6, 7, 6, 6},  // sb 4.98 us, db 4.67 us, ms 4.70 us
+    {1024, 128, 256, 3, 6, 7, 6, 6},  // sb 7.42 us, db 6.49 us, ms 6.48 us
+    {4096, 4096, 4096, 2, 0, 9, 0, 8},  // sb 963.16 us, db 907.44 us, ms 920.75 us
+    {8192, 8192, 8192, 2, 0, 9, 0, 3},  // sb 7443.92 us, db 7172.62 us, ms 7219.22 us
+    {256, 256, 256, 3, 6, 7, 6, 6},  // sb 7.41 us, db 6.47 us, ms 6.45 us
+    {512, 512, 512, 3, 6, 7, 6, 6},  // sb 12.51 us, db 10.28 us, ms 10.09 us
+    {768, 768, 768, 3, 6, 7, 6, 6},  // sb 18.06 us, db 14.49 us, ms 14.07 us
+    {1536, 1536, 1536, 2, 6, 7, 6, 6},  // sb 77.09 us, db 68.68 us, ms 68.99 us
+    {2048, 2048, 2048, 2, 3, 6, 3, 3},  // sb 128.24 us, db 118.28 us, ms 121.97 us
+    {3072, 3072, 3072, 3, 6, 7, 6, 6},  // sb 424.33 us, db 422.11 us, ms 406.21 us
+    {6144, 6144, 6144, 3, 3, 4, 4, 3},  // sb 3190.50 us, db 3049.85 us, ms 3050.87 us
+    {64, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.86 us, db 64.97 us, ms 60.78 us
+    {4096, 4096, 512, 2, 2, 9, 2, 3},  // sb 127.95 us, db 122.90 us, ms 124.53 us
+    {2048, 8192, 2048, 2, 0, 9, 0, 3},  // sb 488.20 us, db 461.13 us, ms 464.31 us
+    {4096, 1024, 1024, 2, 3, 7, 3, 3},  // sb 66.77 us, db 61.88 us, ms 63.77 us
+    {1024, 1024, 8192, 3, 6, 7, 6, 6},  // sb 190.63 us, db 128.54 us, ms 121.95 us
+    {1023, 1023, 1023, 3, 6, 7, 6, 6},  // sb 25.19 us, db 20.94 us, ms 20.70 us
+    {4095, 4095, 4095, 2, 0, 9, 0, 0},  // sb 1003.19 us, db 919.44 us, ms 921.98 us
+    {16, 4096, 4096, 3, 6, 7, 6, 6},  // sb 97.52 us, db 70.24 us, ms 69.55 us
+    {32, 4096, 4096, 3, 10, 7, 10, 10},  // sb 97.74 us, db 69.27 us, ms 63.33 us
+    {128, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.93 us, db 65.19 us, ms 61.15 us
+    {32, 8192, 8192, 3, 10, 7, 10, 10},  // sb 197.78 us, db 143.76 us, ms 124.18 us
 };
 constexpr int kDispatchRows = (int)(sizeof(kDispatch) / sizeof(kDispatch[0]));
 
@@ -76,39 +76,39 @@ struct ModelRow {
 };
 
 static const ModelRow kModel[] = {
-    {1, 0, 9.5674, 4.10572},  // median |error| 3.4%
-    {1, 1, 9.4552, 7.82883},  // median |error| 2.2%
-    {1, 2, 6.0537, 2.21105},  // median |error| 4.4%
-    {1, 3, 3.8813, 1.20448},  // median |error| 7.6%
-    {1, 4, 4.1597, 2.21729},  // median |error| 5.0%
-    {1, 5, 3.4672, 1.19244},  // median |error| 7.1%
-    {1, 6, 3.3127, 0.63058},  // median |error| 10.0%
-    {1, 7, 3.2708, 1.17486},  // median |error| 7.6%
-    {1, 8, 6.2370, 7.69616},  // median |error| 2.0%
-    {1, 9, 4.4140, 4.04300},  // median |error| 2.1%
-    {1, 10, 3.3128, 0.65921},  // median |error| 10.2%
-    {2, 0, 10.2762, 3.47966},  // median |error| 1.3%
-    {2, 1, 10.6630, 6.96635},  // median |error| 1.3%
-    {2, 2, 6.5401, 1.76496},  // median |error| 1.3%
-    {2, 3, 4.3756, 0.91607},  // median |error| 1.7%
-    {2, 4, 4.5750, 1.78336},  // median |error| 1.2%
-    {2, 5, 4.0593, 0.93737},  // median |error| 1.8%
-    {2, 6, 3.3433, 0.50129},  // median |error| 4.1%
-    {2, 7, 3.4119, 1.04691},  // median |error| 3.6%
-    {2, 8, 7.0341, 7.09064},  // median |error| 1.0%
-    {2, 9, 5.1901, 3.51445},  // median |error| 1.1%
-    {2, 10, 3.3231, 0.53594},  // median |error| 4.5%
-    {3, 0, 10.4842, 3.55750},  // median |error| 2.2%
-    {3, 1, 10.3217, 7.13801},  // median |error| 2.3%
-    {3, 2, 6.7027, 1.80775},  // median |error| 2.1%
-    {3, 3, 4.6181, 0.91260},  // median |error| 1.8%
-    {3, 4, 4.5367, 1.84703},  // median |error| 2.0%
-    {3, 5, 4.1379, 0.96627},  // median |error| 1.8%
-    {3, 6, 3.4314, 0.49893},  // median |error| 4.6%
-    {3, 7, 3.3658, 1.09070},  // median |error| 4.2%
-    {3, 8, 7.6671, 7.08704},  // median |error| 1.1%
-    {3, 9, 5.0893, 3.55513},  // median |error| 1.3%
-    {3, 10, 3.3973, 0.52273},  // median |error| 5.3%
+    {1, 0, 9.6025, 4.10568},  // median |error| 3.3%
+    {1, 1, 9.4886, 7.82862},  // median |error| 2.0%
+    {1, 2, 6.0496, 2.21215},  // median |error| 4.3%
+    {1, 3, 3.8712, 1.20347},  // median |error| 7.6%
+    {1, 4, 4.1555, 2.21474},  // median |error| 5.0%
+    {1, 5, 3.4583, 1.19254},  // median |error| 7.2%
+    {1, 6, 3.1208, 0.63470},  // median |error| 10.0%
+    {1, 7, 3.0794, 1.18107},  // median |error| 7.4%
+    {1, 8, 6.2696, 7.69579},  // median |error| 2.1%
+    {1, 9, 4.4221, 4.04198},  // median |error| 2.1%
+    {1, 10, 3.1323, 0.66385},  // median |error| 10.2%
+    {2, 0, 10.3141, 3.47871},  // median |error| 1.3%
+    {2, 1, 10.7009, 6.96492},  // median |error| 1.4%
+    {2, 2, 6.5465, 1.76328},  // median |error| 1.1%
+    {2, 3, 4.3633, 0.91470},  // median |error| 2.0%
+    {2, 4, 4.5710, 1.78125},  // median |error| 1.1%
+    {2, 5, 4.0455, 0.93638},  // median |error| 1.6%
+    {2, 6, 3.1691, 0.50436},  // median |error| 3.5%
+    {2, 7, 3.2308, 1.05355},  // median |error| 2.9%
+    {2, 8, 7.0628, 7.08961},  // median |error| 0.8%
+    {2, 9, 5.1976, 3.51237},  // median |error| 0.9%
+    {2, 10, 3.1690, 0.53871},  // median |error| 3.9%
+    {3, 0, 10.5231, 3.55626},  // median |error| 2.3%
+    {3, 1, 10.3626, 7.13541},  // median |error| 2.3%
+    {3, 2, 6.7082, 1.80632},  // median |error| 2.0%
+    {3, 3, 4.6086, 0.91163},  // median |error| 1.8%
+    {3, 4, 4.5355, 1.84429},  // median |error| 1.9%
+    {3, 5, 4.1289, 0.96506},  // median |error| 1.8%
+    {3, 6, 3.2594, 0.50167},  // median |error| 3.3%
+    {3, 7, 3.1774, 1.09819},  // median |error| 2.8%
+    {3, 8, 7.6960, 7.08562},  // median |error| 1.1%
+    {3, 9, 5.0972, 3.55414},  // median |error| 1.2%
+    {3, 10, 3.2235, 0.52565},  // median |error| 5.4%
 };
 constexpr int kModelRows = (int)(sizeof(kModel) / sizeof(kModel[0]));
 constexpr int64_t kModelCUs = 256;
@@ -159,42 +159,93 @@ static inline int select_for_variant(int64_t M, int64_t N, int64_t K, int varian
   return model_pick(M, N, K, variant, 1).cfg;
 }
 
-// Split-K: measured best number of K chunks per shape (1 = do not split), nearest row in
-// (log2 M, log2 N, log2 K).  Trailing comments: microseconds of each measured choice.
+// Split-K: the number of K chunks (1 = do not split) with the least modelled time among
+// the counts the split study measured.  A split launch costs the GEMM of its chunks, all in
+// one grid (the model above, with the workgroups multiplied by the chunks), plus
+//     2.5816 us (the reduction's launch)
+//   + 0.16456 us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
+//     written once and read once by the reduction, and C)
+//   + 0.9034 us per round of workgroups of the split grid (each workgroup's
+//     first copy and partial-tile store, which short chunks no longer hide),
+// the constants fitted (>= 0, least squares) to the 35 shapes of the split study below.
+constexpr double kSplitFixedUs = 2.5816;
+constexpr double kSplitUsPerMB = 0.16456;
+constexpr double kSplitUsPerRound = 0.9034;
+constexpr int kSplitChoices[] = {1, 2, 4, 8, 16};
+
+// The split study: trailing comments hold the measured microseconds of each count.
 struct SplitRow {
   int64_t m, n, k;
   int splits;
 };
 
 static const SplitRow kSplitK[] = {
-    {16, 4096, 4096, 8},  // 1: 69.5, 2: 38.6, 4: 22.8, 8: 19.9, 16: 21.9
-    {32, 4096, 4096, 8},  // 1: 63.4, 2: 39.0, 4: 23.4, 8: 19.1, 16: 22.1
-    {64, 4096, 4096, 4},  // 1: 60.8, 2: 34.8, 4: 21.8, 8: 24.3, 16: 29.6
-    {128, 4096, 4096, 2},  // 1: 61.0, 2: 35.8, 4: 37.8, 8: 39.6, 16: 43.7
-    {32, 8192, 8192, 4},  // 1: 124.2, 2: 73.0, 4: 46.5, 8: 48.6, 16: 55.2
-    {64, 8192, 8192, 2},  // 1: 119.4, 2: 72.3, 4: 74.6, 8: 78.4, 16: 86.8
-    {256, 256, 8192, 16},  // 1: 118.1, 2: 62.9, 4: 34.8, 8: 21.8, 16: 17.1
-    {512, 512, 8192, 4},  // 1: 119.1, 2: 63.5, 4: 36.9, 8: 39.0, 16: 40.7
-    {1024, 1024, 1024, 1},  // 1: 18.0, 2: 24.6, 4: 25.4, 8: 30.2, 16: 39.6
-    {2048, 2048, 2048, 1},  // 1: 118.2, 2: 130.6, 4: 140.1, 8: 158.4, 16: 206.3
-    {4096, 4096, 4096, 1},  // 1: 907.6, 2: 949.6, 4: 992.8, 8: 1101.4, 16: 1295.1
+    {16, 4096, 4096, 8},  // 1: 69.4, 2: 38.7, 4: 24.1, 8: 20.4, 16: 23.5
+    {32, 4096, 4096, 8},  // 1: 63.4, 2: 39.2, 4: 24.5, 8: 19.6, 16: 23.8
+    {64, 4096, 4096, 4},  // 1: 60.9, 2: 35.0, 4: 23.8, 8: 24.6, 16: 29.8
+    {128, 4096, 4096, 2},  // 1: 61.3, 2: 36.2, 4: 38.3, 8: 40.0, 16: 44.9
+    {32, 8192, 8192, 4},  // 1: 124.4, 2: 73.2, 4: 46.5, 8: 48.7, 16: 55.2
+    {64, 8192, 8192, 2},  // 1: 119.3, 2: 71.4, 4: 74.8, 8: 78.9, 16: 86.8
+    {256, 256, 8192, 16},  // 1: 117.8, 2: 62.9, 4: 34.8, 8: 23.4, 16: 17.7
+    {512, 512, 8192, 4},  // 1: 119.1, 2: 64.0, 4: 38.1, 8: 38.9, 16: 40.7
+    {1024, 1024, 1024, 1},  // 1: 18.0, 2: 22.9, 4: 25.4, 8: 30.1, 16: 39.6
+    {2048, 2048, 2048, 1},  // 1: 118.2, 2: 130.6, 4: 140.2, 8: 158.9, 16: 206.0
+    {4096, 4096, 4096, 1},  // 1: 908.4, 2: 949.6, 4: 992.6, 8: 1100.8, 16: 1292.0
+    {39, 432, 6224, 16},  // 1: 105.2, 2: 56.3, 4: 31.9, 8: 20.8, 16: 16.3
+    {11, 1640, 2822, 16},  // 1: 49.8, 2: 29.2, 4: 18.5, 8: 13.4, 16: 12.3
+    {11, 1486, 1136, 16},  // 1: 21.7, 2: 14.4, 4: 10.9, 8: 9.6, 16: 9.5
+    {66, 326, 1317, 8},  // 1: 25.0, 2: 17.2, 4: 12.1, 8: 9.8, 16: 9.8
+    {63, 4495, 1443, 8},  // 1: 29.1, 2: 19.8, 4: 18.0, 8: 17.5, 16: 20.2
+    {24, 2252, 14173, 8},  // 1: 236.2, 2: 122.4, 4: 64.7, 8: 38.7, 16: 45.3
+    {132, 1012, 15340, 8},  // 1: 256.0, 2: 132.2, 4: 70.0, 8: 65.9, 16: 67.2
+    {10, 5016, 2286, 4},  // 1: 41.2, 2: 24.8, 4: 16.8, 8: 19.7, 16: 17.2
+    {16, 385, 2409, 16},  // 1: 42.6, 2: 25.0, 4: 15.9, 8: 11.7, 16: 11.0
+    {420, 479, 5136, 4},  // 1: 88.5, 2: 48.3, 4: 28.7, 8: 30.3, 16: 33.8
+    {178, 931, 4676, 4},  // 1: 86.9, 2: 47.9, 4: 26.8, 8: 28.1, 16: 27.0
+    {11, 315, 1813, 16},  // 1: 32.8, 2: 20.6, 4: 13.8, 8: 10.5, 16: 10.2
+    {217, 1127, 2447, 4},  // 1: 43.9, 2: 26.8, 4: 21.6, 8: 23.5, 16: 23.8
+    {137, 1231, 2351, 4},  // 1: 47.0, 2: 27.2, 4: 18.7, 8: 19.2, 16: 23.6
+    {378, 2886, 2015, 4},  // 1: 64.6, 2: 54.2, 4: 53.0, 8: 61.0, 16: 71.8
+    {130, 1580, 11590, 16},  // 1: 205.2, 2: 109.3, 4: 94.1, 8: 76.0, 16: 73.9
+    {276, 694, 15508, 8},  // 1: 276.3, 2: 145.3, 4: 81.9, 8: 76.8, 16: 81.8
+    {14, 1090, 8356, 16},  // 1: 140.4, 2: 73.7, 4: 39.8, 8: 25.1, 16: 18.4
+    {17, 1394, 1142, 16},  // 1: 21.7, 2: 14.5, 4: 10.9, 8: 9.5, 16: 9.4
+    {205, 3623, 5015, 4},  // 1: 100.3, 2: 84.0, 4: 83.0, 8: 86.2, 16: 106.2
+    {560, 759, 7039, 4},  // 1: 121.3, 2: 66.5, 4: 62.2, 8: 63.4, 16: 65.2
+    {143, 1910, 3628, 8},  // 1: 67.3, 2: 38.7, 4: 36.4, 8: 35.5, 16: 40.6
+    {471, 6763, 3812, 2},  // 1: 221.7, 2: 219.3, 4: 240.3, 8: 228.2, 16: 282.2
+    {201, 316, 7161, 8},  // 1: 128.5, 2: 68.3, 4: 37.9, 8: 23.4, 16: 24.6
 };
 
+static inline double model_best_us(int64_t M, int64_t N, int64_t K, int64_t wg_factor) {
+  return model_us(model_pick(M, N, K, 0, wg_factor), M, N, K, wg_factor);
+}
+
+static inline double split_model_us(int64_t M, int64_t N, int64_t K, int splits) {
+  int64_t kc = K;
+  int used = 1;
+  if (K > 0) splitk_plan(K, splits, &kc, &used);
+  if (used <= 1) return model_best_us(M, N, K, 1);
+  const ModelRow& r = model_pick(M, N, kc, 0, used);
+  const CfgEntry& e = kConfigs[r.cfg];
+  const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn) * used;
+  const double rounds = (double)((tiles + kModelCUs - 1) / kModelCUs);
+  const double mb = (double)(2 * used + 1) * (double)M * (double)N * 4.0 / 1e6;
+  return model_us(r, M, N, kc, used) + kSplitFixedUs + kSplitUsPerMB * mb +
+         kSplitUsPerRound * rounds;
+}
+
 static inline int select_splits(int64_t M, int64_t N, int64_t K) {
-  const double lm = dispatch_log2(M), ln = dispatch_log2(N), lk = dispatch_log2(K);
-  int best = 0;
-  double best_d = 1e300;
-  for (int i = 0; i < (int)(sizeof(kSplitK) / sizeof(kSplitK[0])); ++i) {
-    const SplitRow& r = kSplitK[i];
-    const double dm = lm - dispatch_log2(r.m), dn = ln - dispatch_log2(r.n),
-                 dk = lk - dispatch_log2(r.k);
-    const double d = dm * dm + dn * dn + dk * dk;
-    if (d < best_d) {
-      best_d = d;
-      best = i;
+  int best = 1;
+  double best_t = 0.0;
+  for (int i = 0; i < (int)(sizeof(kSplitChoices) / sizeof(kSplitChoices[0])); ++i) {
+    const double t = split_model_us(M, N, K, kSplitChoices[i]);
+    if (i == 0 || t < best_t) {
+      best = kSplitChoices[i];
+      best_t = t;
     }
   }
-  return kSplitK[best].splits;
+  return best;
 }
 
 }  // namespace gemmf32

@@ -86,6 +86,18 @@ static const CfgEntry kConfigs[] = {
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
+constexpr int kMaxSplits = 64;
+constexpr int kSplitGranule = 64;  // K chunks are whole K tiles of every configuration
+
+// K chunk of one split and the number of splits actually used.
+static inline void splitk_plan(int64_t K, int splits, int64_t* k_chunk, int* used) {
+  int64_t kc = (K + splits - 1) / splits;
+  kc = (kc + kSplitGranule - 1) / kSplitGranule * kSplitGranule;
+  if (kc < kSplitGranule) kc = kSplitGranule;
+  *k_chunk = kc;
+  *used = (int)((K + kc - 1) / kc);
+}
+
 }  // namespace gemmf32
 
 #include "dispatch_table.h"
@@ -202,17 +214,6 @@ static int run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, con
   return launch(variant, cfg_id, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
-constexpr int kMaxSplits = 64;
-constexpr int kSplitGranule = 64;  // K chunks are whole K tiles of every configuration
-
-// K chunk of one split and the number of splits actually used.
-static void splitk_plan(int64_t K, int splits, int64_t* k_chunk, int* used) {
-  int64_t kc = (K + splits - 1) / splits;
-  kc = (kc + kSplitGranule - 1) / kSplitGranule * kSplitGranule;
-  if (kc < kSplitGranule) kc = kSplitGranule;
-  *k_chunk = kc;
-  *used = (int)((K + kc - 1) / kc);
-}
 
 static int run_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                       const float* B, int64_t ldb, float* C, int64_t ldc, int splits,

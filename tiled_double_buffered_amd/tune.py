@@ -54,6 +54,9 @@ SPLIT_SHAPES = [(16, 4096, 4096), (32, 4096, 4096), (64, 4096, 4096), (128, 4096
                 (32, 8192, 8192), (64, 8192, 8192), (256, 256, 8192), (512, 512, 8192),
                 (1024, 1024, 1024), (2048, 2048, 2048), (4096, 4096, 4096)]
 SPLIT_CHOICES = (1, 2, 4, 8, 16)
+# Skinny shapes measured only to fit the split model.
+SPLIT_TRAIN_SEED = 7
+SPLIT_TRAIN_COUNT = 24
 
 HEADER_TEMPLATE = """// Per-shape dispatch table: (M, N, K) -> variant and tile configuration.
 //
@@ -159,8 +162,21 @@ static inline int select_for_variant(int64_t M, int64_t N, int64_t K, int varian
   return model_pick(M, N, K, variant, 1).cfg;
 }}
 
-// Split-K: measured best number of K chunks per shape (1 = do not split), nearest row in
-// (log2 M, log2 N, log2 K).  Trailing comments: microseconds of each measured choice.
+// Split-K: the number of K chunks (1 = do not split) with the least modelled time among
+// the counts the split study measured.  A split launch costs the GEMM of its chunks, all in
+// one grid (the model above, with the workgroups multiplied by the chunks), plus
+//     {split_fixed:.4f} us (the reduction's launch)
+//   + {split_us_per_mb:.5f} us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
+//     written once and read once by the reduction, and C)
+//   + {split_us_per_round:.4f} us per round of workgroups of the split grid (each workgroup's
+//     first copy and partial-tile store, which short chunks no longer hide),
+// the constants fitted (>= 0, least squares) to the {nsplit} shapes of the split study below.
+constexpr double kSplitFixedUs = {split_fixed:.4f};
+constexpr double kSplitUsPerMB = {split_us_per_mb:.5f};
+constexpr double kSplitUsPerRound = {split_us_per_round:.4f};
+constexpr int kSplitChoices[] = {{{split_choices}}};
+
+// The split study: trailing comments hold the measured microseconds of each count.
 struct SplitRow {{
   int64_t m, n, k;
   int splits;
@@ -170,21 +186,35 @@ static const SplitRow kSplitK[] = {{
 {split_rows}
 }};
 
+static inline double model_best_us(int64_t M, int64_t N, int64_t K, int64_t wg_factor) {{
+  return model_us(model_pick(M, N, K, 0, wg_factor), M, N, K, wg_factor);
+}}
+
+static inline double split_model_us(int64_t M, int64_t N, int64_t K, int splits) {{
+  int64_t kc = K;
+  int used = 1;
+  if (K > 0) splitk_plan(K, splits, &kc, &used);
+  if (used <= 1) return model_best_us(M, N, K, 1);
+  const ModelRow& r = model_pick(M, N, kc, 0, used);
+  const CfgEntry& e = kConfigs[r.cfg];
+  const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn) * used;
+  const double rounds = (double)((tiles + kModelCUs - 1) / kModelCUs);
+  const double mb = (double)(2 * used + 1) * (double)M * (double)N * 4.0 / 1e6;
+  return model_us(r, M, N, kc, used) + kSplitFixedUs + kSplitUsPerMB * mb +
+         kSplitUsPerRound * rounds;
+}}
+
 static inline int select_splits(int64_t M, int64_t N, int64_t K) {{
-  const double lm = dispatch_log2(M), ln = dispatch_log2(N), lk = dispatch_log2(K);
-  int best = 0;
-  double best_d = 1e300;
-  for (int i = 0; i < (int)(sizeof(kSplitK) / sizeof(kSplitK[0])); ++i) {{
-    const SplitRow& r = kSplitK[i];
-    const double dm = lm - dispatch_log2(r.m), dn = ln - dispatch_log2(r.n),
-                 dk = lk - dispatch_log2(r.k);
-    const double d = dm * dm + dn * dn + dk * dk;
-    if (d < best_d) {{
-      best_d = d;
-      best = i;
+  int best = 1;
+  double best_t = 0.0;
+  for (int i = 0; i < (int)(sizeof(kSplitChoices) / sizeof(kSplitChoices[0])); ++i) {{
+    const double t = split_model_us(M, N, K, kSplitChoices[i]);
+    if (i == 0 || t < best_t) {{
+      best = kSplitChoices[i];
+      best_t = t;
     }}
   }}
-  return kSplitK[best].splits;
+  return best;
 }}
 
 }}  // namespace gemmf32
@@ -516,6 +546,56 @@ def fit_model(rows, cfg_dims):
     return out
 
 
+def _model_pick_py(M, N, K, model, dims, wg_factor=1):
+    """Least modelled (us, variant, cfg) over the fitted rows, as the header computes it."""
+    best = None
+    for (v, c, a, g, _e) in model:
+        t = a + g * model_features(M, N, K, dims[c][:3], wg_factor)
+        if best is None or t < best[0]:
+            best = (t, v, c)
+    return best
+
+
+def split_plan(K, splits, granule=64):
+    """(K chunk, chunks used) of a split launch, as the library plans it."""
+    kc = -(-K // splits)
+    kc = max(granule, -(-kc // granule) * granule)
+    return kc, -(-K // kc)
+
+
+def split_extra_mb(M, N, used):
+    return (2 * used + 1) * M * N * 4 / 1e6
+
+
+def split_features(M, N, K, splits, model, dims):
+    """(chunks used, modelled GEMM us of the chunks in one grid, [1, extra MB, rounds]) of a
+    split launch; the overhead model is the dot product of fitted constants with the list."""
+    kc, used = split_plan(K, splits)
+    t, _v, c = _model_pick_py(M, N, kc, model, dims, used)
+    bm, bn = dims[c][0], dims[c][1]
+    rounds = -(-(-(-M // bm) * -(-N // bn) * used) // 256)
+    return used, t, [1.0, split_extra_mb(M, N, used), float(rounds)]
+
+
+def fit_split_model(split_results, model, dims):
+    """(fixed us, us per extra MB, us per round of workgroups) >= 0 of the split overhead:
+    least squares of what the measured split launches took beyond the modelled GEMM of their
+    chunks."""
+    import numpy as np
+    from scipy.optimize import nnls
+
+    X, y = [], []
+    for r in split_results:
+        M, N, K = r["M"], r["N"], r["K"]
+        for sp, us in r["us"].items():
+            used, gemm, f = split_features(M, N, K, int(sp), model, dims)
+            if used > 1:
+                X.append(f)
+                y.append(us - gemm)
+    coef, _ = nnls(np.array(X), np.array(y))
+    return tuple(float(c) for c in coef)
+
+
 def config_dims():
     """cfg -> (BM, BN, BK, LDS bytes of the double-buffered loop)."""
     dims = {}
@@ -541,6 +621,70 @@ def _pick(cands, dims):
         bm, bn, _bk, lds = dims[int(kv[0][2:])]
         return (-bm * bn, lds, kv[1])
     return min(close, key=key)
+
+
+def skinny_shapes(n, seed=2025, max_flop=2.0 * 2048 * 4096 * 4096, exclude=()):
+    """n seeded shapes of the split-K regime: few rows against long K (M log-uniform in
+    [8, 1024], N in [256, 8192], K in [1024, 16384])."""
+    import random
+
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        m = int(round(2.0 ** rng.uniform(3, 10)))
+        n_ = int(round(2.0 ** rng.uniform(8, 13)))
+        k = int(round(2.0 ** rng.uniform(10, 14)))
+        if 2.0 * m * n_ * k <= max_flop and (m, n_, k) not in SPLIT_SHAPES \
+                and (m, n_, k) not in out and (m, n_, k) not in exclude:
+            out.append((m, n_, k))
+    return out
+
+
+def _nearest_split_row(M, N, K, split_results):
+    """The split count of the nearest measured row in (log2 M, log2 N, log2 K): the rule the
+    split model replaced, kept here to measure against."""
+    import math
+
+    def d(r):
+        return sum((math.log2(a) - math.log2(b)) ** 2
+                   for a, b in ((M, r["M"]), (N, r["N"]), (K, r["K"])))
+    r = min(split_results, key=d)
+    return int(min(r["us"], key=r["us"].get))
+
+
+def holdout_splitk_study(n=24, seed=2025, rounds=2, batches=5, batch_ms=20.0, log=print,
+                         split_results=None):
+    """Every split count on n seeded skinny shapes: the time of gemm_f32_splitk_select's
+    count over the fastest count (and, given the split study, the same for the nearest-row
+    rule)."""
+    shapes = skinny_shapes(n, seed, exclude=set(skinny_shapes(SPLIT_TRAIN_COUNT,
+                                                              SPLIT_TRAIN_SEED)))
+    meas = split_study(shapes, rounds=rounds, batches=batches, batch_ms=batch_ms, log=log)
+    rows = []
+    for r in meas:
+        M, N, K = r["M"], r["N"], r["K"]
+        best = min(r["us"], key=r["us"].get)
+        pick = str(tdb.gemm_f32_splitk_select(M, N, K))
+        row = {"M": M, "N": N, "K": K, "pick": int(pick), "best": int(best),
+               "regret": r["us"][pick] / r["us"][best], "us": r["us"]}
+        if split_results:
+            old = str(_nearest_split_row(M, N, K, split_results))
+            row["nearest_row_pick"] = int(old)
+            row["nearest_row_regret"] = r["us"][old] / r["us"][best]
+        rows.append(row)
+        log(f"{M}x{N}x{K}: model picks {pick} ({row['regret']:.3f} of best {best})"
+            + (f", nearest row picks {row['nearest_row_pick']} "
+               f"({row['nearest_row_regret']:.3f})" if split_results else ""))
+
+    def summ(key):
+        xs = sorted(x[key] for x in rows)
+        return {"median": statistics.median(xs), "p90": xs[int(0.9 * (len(xs) - 1))],
+                "max": xs[-1], "within_5pct": sum(1 for x in xs if x <= 1.05) / len(xs)}
+    summary = {"shapes": len(rows), "model": summ("regret")}
+    if split_results:
+        summary["nearest_row"] = summ("nearest_row_regret")
+    log("split-count regret on held-out skinny shapes: " + json.dumps(summary))
+    return {"summary": summary, "rows": rows}
 
 
 def table_rows(results, dims=None):
@@ -579,13 +723,23 @@ def write_header(results, device, rounds, batches, batch_ms, path=None, split_re
                      f"db {db_us:.2f} us, ms {ms_us:.2f} us")
     srows = split_rows(split_results) if split_results else ["    {1024, 1024, 1024, 1},"]
     fit_rows = list(results) + list(train or [])
+    dims = config_dims()
+    model = fit_model(fit_rows, dims)
+    # round as written, so that the split fit sees the model the library will use
+    model = [(v, c, round(a, 4), round(g, 5), e) for (v, c, a, g, e) in model]
     mrows = [f"    {{{v}, {c}, {a:.4f}, {g:.5f}}},  // median |error| {100 * e:.1f}%"
-             for (v, c, a, g, e) in fit_model(fit_rows, config_dims())]
+             for (v, c, a, g, e) in model]
+    r0, per_mb, per_round = (fit_split_model(split_results, model, dims) if split_results
+                             else (3.0, 0.3, 1.0))
+    choices = sorted({int(k) for r in (split_results or []) for k in r["us"]}) or [1]
     text = HEADER_TEMPLATE.format(device=device, rounds=rounds, batches=batches,
                                   batch_ms=int(batch_ms), rows="\n".join(lines),
                                   split_rows="\n".join(srows), model_rows="\n".join(mrows),
                                   nfit=len(fit_rows), ntable=len(results),
-                                  ntrain=len(fit_rows) - len(results))
+                                  ntrain=len(fit_rows) - len(results), split_fixed=r0,
+                                  split_us_per_mb=per_mb, split_us_per_round=per_round,
+                                  nsplit=len(split_results or []),
+                                  split_choices=", ".join(str(c) for c in choices))
     with open(path, "w") as f:
         f.write(text)
     return path
@@ -609,8 +763,14 @@ def main(argv=None) -> int:
                     help="time every pair on N seeded shapes outside the table and report "
                          "how far the dispatcher's pick is from the fastest")
     ap.add_argument("--holdout-seed", type=int, default=2024)
+    ap.add_argument("--holdout-splitk", type=int, default=0, metavar="N",
+                    help="time every split count on N seeded skinny shapes and report how "
+                         "far gemm_f32_splitk_select is from the fastest")
+    ap.add_argument("--split-json", default=None,
+                    help="an earlier --out file whose split study the nearest-row rule of "
+                         "--holdout-splitk is measured against")
     args = ap.parse_args(argv)
-    if args.barrier_study or args.raster_study or args.holdout:
+    if args.barrier_study or args.raster_study or args.holdout or args.holdout_splitk:
         import torch
 
         props = torch.cuda.get_device_properties(0)
@@ -629,6 +789,15 @@ def main(argv=None) -> int:
             res["holdout"] = holdout_study(args.holdout, args.holdout_seed, args.rounds,
                                            args.batches, args.batch_ms,
                                            log=lambda *a: print(*a, flush=True))
+        if args.holdout_splitk:
+            prior = None
+            if args.split_json:
+                with open(args.split_json) as f:
+                    prior = json.load(f).get("splits")
+            res["holdout_splitk"] = holdout_splitk_study(
+                args.holdout_splitk, rounds=args.rounds, batches=args.batches,
+                batch_ms=args.batch_ms, log=lambda *a: print(*a, flush=True),
+                split_results=prior)
         if args.out:
             with open(args.out, "w") as f:
                 json.dump(res, f, indent=1)
@@ -649,7 +818,8 @@ def main(argv=None) -> int:
                       log=lambda *a: print(*a, flush=True))
     train = measure(train_shapes(), args.rounds, args.batches, args.batch_ms,
                     log=lambda *a: print(*a, flush=True))
-    splits = split_study(rounds=args.rounds, batches=args.batches, batch_ms=args.batch_ms,
+    splits = split_study(SPLIT_SHAPES + skinny_shapes(SPLIT_TRAIN_COUNT, SPLIT_TRAIN_SEED),
+                         rounds=args.rounds, batches=args.batches, batch_ms=args.batch_ms,
                          log=lambda *a: print(*a, flush=True))
     data = {"device": device, "rounds": args.rounds, "batches": args.batches,
             "batch_ms": args.batch_ms, "library": tdb.gemm_f32_version(),
