@@ -98,7 +98,8 @@ def test_every_config_sb_equals_db_and_matches_oracle(cfg):
 
 def _edge_shapes():
     rng = np.random.default_rng(2024)
-    dims_mn = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+    dims_mn = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257,
+               383, 384, 385]
     dims_k = [1, 2, 3, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100]
     shapes = {(int(rng.choice(dims_mn)), int(rng.choice(dims_mn)), int(rng.choice(dims_k)))
               for _ in range(40)}
@@ -269,6 +270,27 @@ def test_square_4096_full():
             if other_v != v:
                 other = _run(Ad, Bd, other_v, cfg)
                 assert torch.equal(C, other), f"{v} cfg {cfg}: {v} and {other_v} differ"
+
+
+def test_square_3072_full_on_192_tiles():
+    """3072^3 is 16 x 16 tiles of 192 x 192, one per compute unit: the dispatched product
+    and both 192-wide configurations in every variant, checked on the full output, with
+    the variants bit for bit equal per configuration."""
+    M = N = K = 3072
+    _say("[parity] 3072^3 oracle (full output) ...")
+    A, B = ti.workload_inputs(M, N, K, 3072)
+    C64, Bnd = oracle.gemm_f64(A, B)
+    Ad, Bd = _dev(A), _dev(B)
+    assert _ratio(_run(Ad, Bd, "auto"), C64, Bnd) <= 1.0
+    wide = [c for c in range(NCFG)
+            if tdb.gemm_f32_config_info(c)[1]["BM"] == 192 == tdb.gemm_f32_config_info(c)[1]["BN"]]
+    assert wide
+    for cfg in wide:
+        _say(f"[parity] 3072^3 cfg={cfg}")
+        Cdb = _run(Ad, Bd, "db", cfg).clone()
+        assert _ratio(Cdb, C64, Bnd) <= 1.0, cfg
+        for v in ("sb", "ms", "sb3"):
+            assert torch.equal(_run(Ad, Bd, v, cfg), Cdb), (cfg, v)
 
 
 @pytest.mark.slow

@@ -24,32 +24,32 @@ struct DispatchRow {
 };
 
 static const DispatchRow kDispatch[] = {
-    {128, 128, 128, 3, 6, 7, 6, 6},  // sb 4.77 us, db 4.55 us, ms 4.52 us
-    {127, 193, 61, 3, 10, 10, 10, 10},  // sb 4.23 us, db 4.21 us, ms 4.16 us
-    {513, 257, 129, 2, 6, 6, 6, 6},  // sb 6.44 us, db 5.87 us, ms 5.94 us
-    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.73 us, db 18.53 us, ms 17.97 us
-    {256, 1024, 128, 2, 6, 7, 6, 6},  // sb 4.98 us, db 4.67 us, ms 4.70 us
-    {1024, 128, 256, 3, 6, 7, 6, 6},  // sb 7.42 us, db 6.49 us, ms 6.48 us
-    {4096, 4096, 4096, 2, 0, 9, 0, 8},  // sb 963.16 us, db 907.44 us, ms 920.75 us
-    {8192, 8192, 8192, 2, 0, 9, 0, 3},  // sb 7443.92 us, db 7172.62 us, ms 7219.22 us
-    {256, 256, 256, 3, 6, 7, 6, 6},  // sb 7.41 us, db 6.47 us, ms 6.45 us
-    {512, 512, 512, 3, 6, 7, 6, 6},  // sb 12.51 us, db 10.28 us, ms 10.09 us
-    {768, 768, 768, 3, 6, 7, 6, 6},  // sb 18.06 us, db 14.49 us, ms 14.07 us
-    {1536, 1536, 1536, 2, 6, 7, 6, 6},  // sb 77.09 us, db 68.68 us, ms 68.99 us
-    {2048, 2048, 2048, 2, 3, 6, 3, 3},  // sb 128.24 us, db 118.28 us, ms 121.97 us
-    {3072, 3072, 3072, 3, 6, 7, 6, 6},  // sb 424.33 us, db 422.11 us, ms 406.21 us
-    {6144, 6144, 6144, 3, 3, 4, 4, 3},  // sb 3190.50 us, db 3049.85 us, ms 3050.87 us
-    {64, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.86 us, db 64.97 us, ms 60.78 us
-    {4096, 4096, 512, 2, 2, 9, 2, 3},  // sb 127.95 us, db 122.90 us, ms 124.53 us
-    {2048, 8192, 2048, 2, 0, 9, 0, 3},  // sb 488.20 us, db 461.13 us, ms 464.31 us
-    {4096, 1024, 1024, 2, 3, 7, 3, 3},  // sb 66.77 us, db 61.88 us, ms 63.77 us
-    {1024, 1024, 8192, 3, 6, 7, 6, 6},  // sb 190.63 us, db 128.54 us, ms 121.95 us
-    {1023, 1023, 1023, 3, 6, 7, 6, 6},  // sb 25.19 us, db 20.94 us, ms 20.70 us
-    {4095, 4095, 4095, 2, 0, 9, 0, 0},  // sb 1003.19 us, db 919.44 us, ms 921.98 us
-    {16, 4096, 4096, 3, 6, 7, 6, 6},  // sb 97.52 us, db 70.24 us, ms 69.55 us
-    {32, 4096, 4096, 3, 10, 7, 10, 10},  // sb 97.74 us, db 69.27 us, ms 63.33 us
-    {128, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.93 us, db 65.19 us, ms 61.15 us
-    {32, 8192, 8192, 3, 10, 7, 10, 10},  // sb 197.78 us, db 143.76 us, ms 124.18 us
+    {128, 128, 128, 2, 6, 7, 6, 6},  // sb 4.79 us, db 4.48 us, ms 4.51 us
+    {127, 193, 61, 2, 7, 7, 7, 7},  // sb 4.19 us, db 4.15 us, ms 4.18 us
+    {513, 257, 129, 2, 6, 6, 6, 6},  // sb 6.45 us, db 5.92 us, ms 5.98 us
+    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.72 us, db 18.55 us, ms 17.97 us
+    {256, 1024, 128, 2, 6, 7, 6, 6},  // sb 4.98 us, db 4.69 us, ms 4.72 us
+    {1024, 128, 256, 3, 6, 7, 6, 6},  // sb 7.41 us, db 6.46 us, ms 6.44 us
+    {4096, 4096, 4096, 2, 0, 9, 0, 3},  // sb 967.15 us, db 907.21 us, ms 918.32 us
+    {8192, 8192, 8192, 2, 0, 9, 0, 3},  // sb 7435.37 us, db 7169.95 us, ms 7243.42 us
+    {256, 256, 256, 3, 6, 7, 6, 6},  // sb 7.38 us, db 6.46 us, ms 6.44 us
+    {512, 512, 512, 3, 6, 7, 6, 6},  // sb 12.55 us, db 10.29 us, ms 10.09 us
+    {768, 768, 768, 3, 6, 7, 6, 6},  // sb 18.10 us, db 14.51 us, ms 14.07 us
+    {1536, 1536, 1536, 2, 6, 7, 6, 6},  // sb 77.22 us, db 69.00 us, ms 69.01 us
+    {2048, 2048, 2048, 2, 3, 6, 3, 3},  // sb 127.95 us, db 118.15 us, ms 121.56 us
+    {3072, 3072, 3072, 2, 11, 7, 11, 11},  // sb 426.36 us, db 386.39 us, ms 401.51 us
+    {6144, 6144, 6144, 2, 11, 4, 11, 3},  // sb 3195.06 us, db 3050.72 us, ms 3066.50 us
+    {64, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.32 us, db 65.15 us, ms 60.91 us
+    {4096, 4096, 512, 2, 2, 9, 2, 3},  // sb 127.49 us, db 123.14 us, ms 124.68 us
+    {2048, 8192, 2048, 2, 0, 9, 0, 3},  // sb 487.67 us, db 459.34 us, ms 463.65 us
+    {4096, 1024, 1024, 2, 3, 7, 3, 3},  // sb 66.75 us, db 61.97 us, ms 63.78 us
+    {1024, 1024, 8192, 3, 6, 7, 6, 6},  // sb 191.05 us, db 128.71 us, ms 122.64 us
+    {1023, 1023, 1023, 3, 6, 7, 6, 6},  // sb 25.16 us, db 21.10 us, ms 20.74 us
+    {4095, 4095, 4095, 2, 0, 9, 0, 0},  // sb 1005.94 us, db 919.57 us, ms 920.66 us
+    {16, 4096, 4096, 3, 6, 7, 6, 6},  // sb 97.70 us, db 70.21 us, ms 69.54 us
+    {32, 4096, 4096, 3, 10, 7, 10, 10},  // sb 98.09 us, db 69.60 us, ms 63.57 us
+    {128, 4096, 4096, 3, 6, 7, 6, 6},  // sb 95.54 us, db 65.13 us, ms 61.14 us
+    {32, 8192, 8192, 3, 10, 7, 7, 10},  // sb 196.96 us, db 143.04 us, ms 124.04 us
 };
 constexpr int kDispatchRows = (int)(sizeof(kDispatch) / sizeof(kDispatch[0]));
 
@@ -76,39 +76,45 @@ struct ModelRow {
 };
 
 static const ModelRow kModel[] = {
-    {1, 0, 9.6025, 4.10568},  // median |error| 3.3%
-    {1, 1, 9.4886, 7.82862},  // median |error| 2.0%
-    {1, 2, 6.0496, 2.21215},  // median |error| 4.3%
-    {1, 3, 3.8712, 1.20347},  // median |error| 7.6%
-    {1, 4, 4.1555, 2.21474},  // median |error| 5.0%
-    {1, 5, 3.4583, 1.19254},  // median |error| 7.2%
-    {1, 6, 3.1208, 0.63470},  // median |error| 10.0%
-    {1, 7, 3.0794, 1.18107},  // median |error| 7.4%
-    {1, 8, 6.2696, 7.69579},  // median |error| 2.1%
-    {1, 9, 4.4221, 4.04198},  // median |error| 2.1%
-    {1, 10, 3.1323, 0.66385},  // median |error| 10.2%
-    {2, 0, 10.3141, 3.47871},  // median |error| 1.3%
-    {2, 1, 10.7009, 6.96492},  // median |error| 1.4%
-    {2, 2, 6.5465, 1.76328},  // median |error| 1.1%
-    {2, 3, 4.3633, 0.91470},  // median |error| 2.0%
-    {2, 4, 4.5710, 1.78125},  // median |error| 1.1%
-    {2, 5, 4.0455, 0.93638},  // median |error| 1.6%
-    {2, 6, 3.1691, 0.50436},  // median |error| 3.5%
-    {2, 7, 3.2308, 1.05355},  // median |error| 2.9%
-    {2, 8, 7.0628, 7.08961},  // median |error| 0.8%
-    {2, 9, 5.1976, 3.51237},  // median |error| 0.9%
-    {2, 10, 3.1690, 0.53871},  // median |error| 3.9%
-    {3, 0, 10.5231, 3.55626},  // median |error| 2.3%
-    {3, 1, 10.3626, 7.13541},  // median |error| 2.3%
-    {3, 2, 6.7082, 1.80632},  // median |error| 2.0%
-    {3, 3, 4.6086, 0.91163},  // median |error| 1.8%
-    {3, 4, 4.5355, 1.84429},  // median |error| 1.9%
-    {3, 5, 4.1289, 0.96506},  // median |error| 1.8%
-    {3, 6, 3.2594, 0.50167},  // median |error| 3.3%
-    {3, 7, 3.1774, 1.09819},  // median |error| 2.8%
-    {3, 8, 7.6960, 7.08562},  // median |error| 1.1%
-    {3, 9, 5.0972, 3.55414},  // median |error| 1.2%
-    {3, 10, 3.2235, 0.52565},  // median |error| 5.4%
+    {1, 0, 9.5762, 4.10180},  // median |error| 3.3%
+    {1, 1, 9.4564, 7.82131},  // median |error| 2.3%
+    {1, 2, 6.0338, 2.20983},  // median |error| 4.3%
+    {1, 3, 3.8545, 1.20407},  // median |error| 7.5%
+    {1, 4, 4.1413, 2.21554},  // median |error| 5.1%
+    {1, 5, 3.4404, 1.19323},  // median |error| 7.2%
+    {1, 6, 3.0823, 0.63464},  // median |error| 10.3%
+    {1, 7, 3.0535, 1.18353},  // median |error| 7.6%
+    {1, 8, 6.2496, 7.68663},  // median |error| 2.0%
+    {1, 9, 4.4084, 4.04096},  // median |error| 2.2%
+    {1, 10, 3.1288, 0.66092},  // median |error| 10.6%
+    {1, 11, 6.0678, 2.52124},  // median |error| 4.2%
+    {1, 12, 6.5667, 4.68467},  // median |error| 2.9%
+    {2, 0, 10.2937, 3.47376},  // median |error| 1.1%
+    {2, 1, 10.6765, 6.95484},  // median |error| 1.2%
+    {2, 2, 6.5270, 1.76279},  // median |error| 1.2%
+    {2, 3, 4.3504, 0.91518},  // median |error| 1.9%
+    {2, 4, 4.5535, 1.78263},  // median |error| 1.0%
+    {2, 5, 4.0253, 0.93750},  // median |error| 1.8%
+    {2, 6, 3.1323, 0.50612},  // median |error| 3.2%
+    {2, 7, 3.1419, 1.05879},  // median |error| 2.7%
+    {2, 8, 7.0478, 7.08027},  // median |error| 0.9%
+    {2, 9, 5.1862, 3.51099},  // median |error| 1.1%
+    {2, 10, 3.1392, 0.54142},  // median |error| 4.1%
+    {2, 11, 6.8706, 1.99730},  // median |error| 0.9%
+    {2, 12, 7.4940, 3.95635},  // median |error| 0.9%
+    {3, 0, 10.4925, 3.55269},  // median |error| 2.3%
+    {3, 1, 10.3382, 7.12597},  // median |error| 2.3%
+    {3, 2, 6.6884, 1.80543},  // median |error| 2.0%
+    {3, 3, 4.5946, 0.91211},  // median |error| 1.7%
+    {3, 4, 4.5204, 1.84514},  // median |error| 2.0%
+    {3, 5, 4.1040, 0.96609},  // median |error| 1.8%
+    {3, 6, 3.2114, 0.50393},  // median |error| 3.2%
+    {3, 7, 3.1263, 1.10119},  // median |error| 2.8%
+    {3, 8, 7.6829, 7.07705},  // median |error| 1.0%
+    {3, 9, 5.0848, 3.55197},  // median |error| 1.3%
+    {3, 10, 3.1867, 0.52778},  // median |error| 5.3%
+    {3, 11, 7.2231, 2.04638},  // median |error| 2.4%
+    {3, 12, 7.5777, 4.07320},  // median |error| 2.8%
 };
 constexpr int kModelRows = (int)(sizeof(kModel) / sizeof(kModel[0]));
 constexpr int64_t kModelCUs = 256;
@@ -162,15 +168,15 @@ static inline int select_for_variant(int64_t M, int64_t N, int64_t K, int varian
 // Split-K: the number of K chunks (1 = do not split) with the least modelled time among
 // the counts the split study measured.  A split launch costs the GEMM of its chunks, all in
 // one grid (the model above, with the workgroups multiplied by the chunks), plus
-//     2.5816 us (the reduction's launch)
-//   + 0.16456 us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
+//     2.4096 us (the reduction's launch)
+//   + 0.16505 us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
 //     written once and read once by the reduction, and C)
-//   + 0.9034 us per round of workgroups of the split grid (each workgroup's
+//   + 0.9253 us per round of workgroups of the split grid (each workgroup's
 //     first copy and partial-tile store, which short chunks no longer hide),
 // the constants fitted (>= 0, least squares) to the 35 shapes of the split study below.
-constexpr double kSplitFixedUs = 2.5816;
-constexpr double kSplitUsPerMB = 0.16456;
-constexpr double kSplitUsPerRound = 0.9034;
+constexpr double kSplitFixedUs = 2.4096;
+constexpr double kSplitUsPerMB = 0.16505;
+constexpr double kSplitUsPerRound = 0.9253;
 constexpr int kSplitChoices[] = {1, 2, 4, 8, 16};
 
 // The split study: trailing comments hold the measured microseconds of each count.
@@ -180,41 +186,41 @@ struct SplitRow {
 };
 
 static const SplitRow kSplitK[] = {
-    {16, 4096, 4096, 8},  // 1: 69.4, 2: 38.7, 4: 24.1, 8: 20.4, 16: 23.5
-    {32, 4096, 4096, 8},  // 1: 63.4, 2: 39.2, 4: 24.5, 8: 19.6, 16: 23.8
-    {64, 4096, 4096, 4},  // 1: 60.9, 2: 35.0, 4: 23.8, 8: 24.6, 16: 29.8
-    {128, 4096, 4096, 2},  // 1: 61.3, 2: 36.2, 4: 38.3, 8: 40.0, 16: 44.9
-    {32, 8192, 8192, 4},  // 1: 124.4, 2: 73.2, 4: 46.5, 8: 48.7, 16: 55.2
-    {64, 8192, 8192, 2},  // 1: 119.3, 2: 71.4, 4: 74.8, 8: 78.9, 16: 86.8
-    {256, 256, 8192, 16},  // 1: 117.8, 2: 62.9, 4: 34.8, 8: 23.4, 16: 17.7
-    {512, 512, 8192, 4},  // 1: 119.1, 2: 64.0, 4: 38.1, 8: 38.9, 16: 40.7
+    {16, 4096, 4096, 8},  // 1: 69.5, 2: 38.6, 4: 24.0, 8: 19.9, 16: 21.8
+    {32, 4096, 4096, 8},  // 1: 63.2, 2: 39.1, 4: 24.5, 8: 19.1, 16: 22.1
+    {64, 4096, 4096, 4},  // 1: 60.8, 2: 34.7, 4: 23.6, 8: 24.0, 16: 26.6
+    {128, 4096, 4096, 2},  // 1: 61.2, 2: 35.8, 4: 38.0, 8: 39.5, 16: 43.7
+    {32, 8192, 8192, 4},  // 1: 124.1, 2: 73.3, 4: 46.2, 8: 48.6, 16: 55.1
+    {64, 8192, 8192, 2},  // 1: 119.2, 2: 69.1, 4: 73.2, 8: 77.9, 16: 88.4
+    {256, 256, 8192, 16},  // 1: 117.8, 2: 62.8, 4: 34.8, 8: 23.4, 16: 17.7
+    {512, 512, 8192, 4},  // 1: 118.7, 2: 63.5, 4: 37.6, 8: 39.0, 16: 40.8
     {1024, 1024, 1024, 1},  // 1: 18.0, 2: 22.9, 4: 25.4, 8: 30.1, 16: 39.6
-    {2048, 2048, 2048, 1},  // 1: 118.2, 2: 130.6, 4: 140.2, 8: 158.9, 16: 206.0
-    {4096, 4096, 4096, 1},  // 1: 908.4, 2: 949.6, 4: 992.6, 8: 1100.8, 16: 1292.0
-    {39, 432, 6224, 16},  // 1: 105.2, 2: 56.3, 4: 31.9, 8: 20.8, 16: 16.3
-    {11, 1640, 2822, 16},  // 1: 49.8, 2: 29.2, 4: 18.5, 8: 13.4, 16: 12.3
-    {11, 1486, 1136, 16},  // 1: 21.7, 2: 14.4, 4: 10.9, 8: 9.6, 16: 9.5
-    {66, 326, 1317, 8},  // 1: 25.0, 2: 17.2, 4: 12.1, 8: 9.8, 16: 9.8
-    {63, 4495, 1443, 8},  // 1: 29.1, 2: 19.8, 4: 18.0, 8: 17.5, 16: 20.2
-    {24, 2252, 14173, 8},  // 1: 236.2, 2: 122.4, 4: 64.7, 8: 38.7, 16: 45.3
-    {132, 1012, 15340, 8},  // 1: 256.0, 2: 132.2, 4: 70.0, 8: 65.9, 16: 67.2
-    {10, 5016, 2286, 4},  // 1: 41.2, 2: 24.8, 4: 16.8, 8: 19.7, 16: 17.2
-    {16, 385, 2409, 16},  // 1: 42.6, 2: 25.0, 4: 15.9, 8: 11.7, 16: 11.0
-    {420, 479, 5136, 4},  // 1: 88.5, 2: 48.3, 4: 28.7, 8: 30.3, 16: 33.8
-    {178, 931, 4676, 4},  // 1: 86.9, 2: 47.9, 4: 26.8, 8: 28.1, 16: 27.0
-    {11, 315, 1813, 16},  // 1: 32.8, 2: 20.6, 4: 13.8, 8: 10.5, 16: 10.2
-    {217, 1127, 2447, 4},  // 1: 43.9, 2: 26.8, 4: 21.6, 8: 23.5, 16: 23.8
+    {2048, 2048, 2048, 1},  // 1: 118.3, 2: 130.4, 4: 139.7, 8: 158.4, 16: 206.1
+    {4096, 4096, 4096, 1},  // 1: 906.6, 2: 947.0, 4: 991.4, 8: 1099.7, 16: 1292.3
+    {39, 432, 6224, 16},  // 1: 105.3, 2: 56.3, 4: 31.8, 8: 20.7, 16: 16.0
+    {11, 1640, 2822, 16},  // 1: 49.8, 2: 29.1, 4: 18.4, 8: 13.2, 16: 12.3
+    {11, 1486, 1136, 16},  // 1: 21.8, 2: 14.5, 4: 10.9, 8: 9.6, 16: 9.5
+    {66, 326, 1317, 8},  // 1: 24.9, 2: 17.1, 4: 11.9, 8: 9.6, 16: 9.6
+    {63, 4495, 1443, 8},  // 1: 29.1, 2: 19.8, 4: 17.9, 8: 17.5, 16: 20.2
+    {24, 2252, 14173, 8},  // 1: 236.1, 2: 122.3, 4: 64.5, 8: 39.0, 16: 45.5
+    {132, 1012, 15340, 8},  // 1: 256.2, 2: 132.4, 4: 70.0, 8: 66.1, 16: 67.5
+    {10, 5016, 2286, 4},  // 1: 41.3, 2: 24.9, 4: 16.8, 8: 19.8, 16: 17.1
+    {16, 385, 2409, 16},  // 1: 42.6, 2: 25.0, 4: 15.9, 8: 11.8, 16: 11.0
+    {420, 479, 5136, 4},  // 1: 88.8, 2: 48.4, 4: 28.8, 8: 30.4, 16: 33.7
+    {178, 931, 4676, 4},  // 1: 87.1, 2: 47.8, 4: 26.8, 8: 28.1, 16: 27.0
+    {11, 315, 1813, 16},  // 1: 32.7, 2: 20.5, 4: 13.8, 8: 10.5, 16: 10.1
+    {217, 1127, 2447, 4},  // 1: 43.9, 2: 26.9, 4: 21.6, 8: 23.6, 16: 23.8
     {137, 1231, 2351, 4},  // 1: 47.0, 2: 27.2, 4: 18.7, 8: 19.2, 16: 23.6
-    {378, 2886, 2015, 4},  // 1: 64.6, 2: 54.2, 4: 53.0, 8: 61.0, 16: 71.8
-    {130, 1580, 11590, 16},  // 1: 205.2, 2: 109.3, 4: 94.1, 8: 76.0, 16: 73.9
-    {276, 694, 15508, 8},  // 1: 276.3, 2: 145.3, 4: 81.9, 8: 76.8, 16: 81.8
-    {14, 1090, 8356, 16},  // 1: 140.4, 2: 73.7, 4: 39.8, 8: 25.1, 16: 18.4
-    {17, 1394, 1142, 16},  // 1: 21.7, 2: 14.5, 4: 10.9, 8: 9.5, 16: 9.4
-    {205, 3623, 5015, 4},  // 1: 100.3, 2: 84.0, 4: 83.0, 8: 86.2, 16: 106.2
-    {560, 759, 7039, 4},  // 1: 121.3, 2: 66.5, 4: 62.2, 8: 63.4, 16: 65.2
-    {143, 1910, 3628, 8},  // 1: 67.3, 2: 38.7, 4: 36.4, 8: 35.5, 16: 40.6
-    {471, 6763, 3812, 2},  // 1: 221.7, 2: 219.3, 4: 240.3, 8: 228.2, 16: 282.2
-    {201, 316, 7161, 8},  // 1: 128.5, 2: 68.3, 4: 37.9, 8: 23.4, 16: 24.6
+    {378, 2886, 2015, 4},  // 1: 64.9, 2: 54.3, 4: 52.6, 8: 61.0, 16: 71.9
+    {130, 1580, 11590, 16},  // 1: 205.7, 2: 109.6, 4: 94.6, 8: 76.0, 16: 74.2
+    {276, 694, 15508, 8},  // 1: 277.1, 2: 145.4, 4: 81.8, 8: 77.1, 16: 81.7
+    {14, 1090, 8356, 16},  // 1: 140.5, 2: 73.9, 4: 39.9, 8: 24.5, 16: 18.4
+    {17, 1394, 1142, 16},  // 1: 21.9, 2: 14.5, 4: 10.9, 8: 9.5, 16: 9.3
+    {205, 3623, 5015, 4},  // 1: 100.3, 2: 84.1, 4: 83.1, 8: 86.4, 16: 106.5
+    {560, 759, 7039, 4},  // 1: 121.5, 2: 66.7, 4: 62.5, 8: 63.4, 16: 65.0
+    {143, 1910, 3628, 8},  // 1: 67.5, 2: 38.7, 4: 36.5, 8: 35.5, 16: 40.6
+    {471, 6763, 3812, 2},  // 1: 221.2, 2: 220.5, 4: 240.8, 8: 229.2, 16: 282.6
+    {201, 316, 7161, 8},  // 1: 128.4, 2: 68.4, 4: 37.9, 8: 23.5, 16: 24.6
 };
 
 static inline double model_best_us(int64_t M, int64_t N, int64_t K, int64_t wg_factor) {

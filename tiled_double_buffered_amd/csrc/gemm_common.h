@@ -51,7 +51,10 @@ struct TileCfg {
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(BK % 8 == 0, "BK must be a multiple of 8");
   static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "copy must divide");
-  static_assert(NT % A_GROUPS_PER_ROW == 0 && NT % B_GROUPS_PER_ROW == 0, "copy rows");
+  static_assert(NT % A_GROUPS_PER_ROW == 0, "copy rows of A");
+  // NT a multiple of the B groups per row: every pass of the B copy starts at the same
+  // column, one row stride further (otherwise, as for 192-wide tiles, per pass)
+  static constexpr bool B_EVEN = NT % B_GROUPS_PER_ROW == 0;
   static_assert(A_PER_T >= 1 && B_PER_T >= 1, "copy work per thread");
 };
 
@@ -97,14 +100,37 @@ constexpr int kBufferFlags = 0x00020000;
 // The workgroup's copy of one K tile: global memory -> registers -> LDS.
 // Thread t moves groups g = t + p * NT (p = 0 .. PER_T-1); group g of A is row
 // g / (BK/4), columns 4 * (g % (BK/4)) .. +3 of the tile; likewise for B with BN/4.
+// When NT is a multiple of the groups per row, pass p is pass 0 moved down by
+// p * NT / (groups per row) rows; otherwise (B of a 192-wide tile) each pass has its own
+// row and column.
 // ------------------------------------------------------------------------------------
+// Row and column of a thread's B group in each pass, kept only where passes differ in
+// column (empty otherwise).
+template <int N>
+struct BPassCoords {
+  int rows[N], cols[N];
+};
+template <>
+struct BPassCoords<0> {};
+
 template <class C>
 struct TileCopy {
   floatx4 ra[C::A_PER_T];
   floatx4 rb[C::B_PER_T];
 
-  // Per-thread coordinates inside the tile.
+  // Per-thread coordinates inside the tile (B: of pass 0, or of every pass when the
+  // passes do not share a column).
   int a_row, a_col, b_row, b_col;
+  [[no_unique_address]] BPassCoords<C::B_EVEN ? 0 : C::B_PER_T> bp;
+
+  __device__ inline int brow(int i) const {
+    if constexpr (C::B_EVEN) return b_row + i * C::B_ROWS_PER_PASS;
+    else return bp.rows[i];
+  }
+  __device__ inline int bcol(int i) const {
+    if constexpr (C::B_EVEN) return b_col;
+    else return bp.cols[i];
+  }
   // Byte offsets of this thread's 16-byte groups from the tile's first element; they are
   // the same for every K tile (see the fast path below).
   uint32_t a_off[C::A_PER_T], b_off[C::B_PER_T];
@@ -114,12 +140,19 @@ struct TileCopy {
     a_col = 4 * (tid % C::A_GROUPS_PER_ROW);
     b_row = tid / C::B_GROUPS_PER_ROW;
     b_col = 4 * (tid % C::B_GROUPS_PER_ROW);
+    if constexpr (!C::B_EVEN) {
+#pragma unroll
+      for (int i = 0; i < C::B_PER_T; ++i) {
+        bp.rows[i] = (tid + i * C::NT) / C::B_GROUPS_PER_ROW;
+        bp.cols[i] = 4 * ((tid + i * C::NT) % C::B_GROUPS_PER_ROW);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < C::A_PER_T; ++i)
       a_off[i] = (uint32_t)(((int64_t)(a_row + i * C::A_ROWS_PER_PASS) * lda + a_col) * 4);
 #pragma unroll
     for (int i = 0; i < C::B_PER_T; ++i)
-      b_off[i] = (uint32_t)(((int64_t)(b_row + i * C::B_ROWS_PER_PASS) * ldb + b_col) * 4);
+      b_off[i] = (uint32_t)(((int64_t)brow(i) * ldb + bcol(i)) * 4);
   }
 
   // Fast path: 16-byte buffer loads.  The tile's first element is a workgroup-uniform
@@ -202,8 +235,8 @@ struct TileCopy {
                                         int K, int n0, int k0) {
 #pragma unroll
     for (int i = 0; i < C::B_PER_T; ++i) {
-      const int r = k0 + b_row + i * C::B_ROWS_PER_PASS;
-      const int c = n0 + b_col;
+      const int r = k0 + brow(i);
+      const int c = n0 + bcol(i);
       const float* p = B + (int64_t)r * ldb + c;
       floatx4 v;
 #pragma unroll
@@ -222,7 +255,7 @@ struct TileCopy {
     float* Bs = slot + C::A_SLOT;
 #pragma unroll
     for (int i = 0; i < C::B_PER_T; ++i)
-      *reinterpret_cast<floatx4*>(Bs + (b_row + i * C::B_ROWS_PER_PASS) * C::BS + b_col) = rb[i];
+      *reinterpret_cast<floatx4*>(Bs + brow(i) * C::BS + bcol(i)) = rb[i];
   }
   __device__ inline void store(float* slot) {
     store_a(slot);

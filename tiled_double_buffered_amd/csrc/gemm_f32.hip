@@ -51,6 +51,8 @@ using Cfg7 = TileCfg<64, 64, 64, 2, 2>;    // wave 32x32, deeper K tile
 using Cfg8 = TileCfg<256, 256, 32, 2, 4>;  // 8 waves of 128x64: two waves per SIMD
 using Cfg9 = TileCfg<128, 256, 32, 2, 4>;  // 8 waves of 64x64
 using Cfg10 = TileCfg<32, 128, 32, 1, 4>;  // 4 waves of 32x32 side by side: skinny M
+using Cfg11 = TileCfg<192, 192, 16, 2, 2>;  // wave 96x96: 16x16 tiles for 3072-wide C
+using Cfg12 = TileCfg<192, 192, 32, 2, 2>;  // wave 96x96, deeper K tile
 
 typedef void (*KernelFn)(int, int, int, const float*, int64_t, const float*, int64_t, float*,
                          int64_t, int, int, int64_t);
@@ -82,7 +84,8 @@ constexpr CfgEntry make_entry() {
 static const CfgEntry kConfigs[] = {
     make_entry<Cfg0>(), make_entry<Cfg1>(), make_entry<Cfg2>(), make_entry<Cfg3>(),
     make_entry<Cfg4>(), make_entry<Cfg5>(), make_entry<Cfg6>(), make_entry<Cfg7>(),
-    make_entry<Cfg8>(), make_entry<Cfg9>(), make_entry<Cfg10>(),
+    make_entry<Cfg8>(), make_entry<Cfg9>(), make_entry<Cfg10>(), make_entry<Cfg11>(),
+    make_entry<Cfg12>(),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 

@@ -46,7 +46,7 @@ struct MsCfg {
   static constexpr int CPR_A = C::BK / 4;            // 16-byte chunks per A row
   static constexpr int RPC_A = 256 / C::BK;          // A rows per 1 KiB
   static constexpr int CPR_B = C::BN / 4;
-  static constexpr int RPC_B = 256 / C::BN;
+  static constexpr int RPC_B = 256 / C::BN;          // (when whole rows fit in 1 KiB)
   // LDS floats: the stages, or the two padded slots of the guarded fallback loop.
   static constexpr int LDS_FLOATS = S * STAGE > 2 * C::SLOT ? S * STAGE : 2 * C::SLOT;
   static_assert(S >= 2, "at least two stages");
@@ -112,8 +112,15 @@ struct MsCopy {
         lds_off[i] = (uint32_t)j * 1024u;
       } else {
         const int jb = j - MC::A_CHUNKS;
-        const int k = jb * MC::RPC_B + lane / MC::CPR_B;
-        const int c = (lane % MC::CPR_B) ^ swz_b(k);
+        int k, c;
+        if constexpr (256 % C::BN == 0) {  // whole B rows per 1 KiB
+          k = jb * MC::RPC_B + lane / MC::CPR_B;
+          c = (lane % MC::CPR_B) ^ swz_b(k);
+        } else {  // a 1 KiB copy spans row boundaries (192-wide tiles)
+          const int p = jb * 256 + 4 * lane;  // float index in the stage's B part
+          k = p / C::BN;
+          c = ((p % C::BN) / 4) ^ swz_b(k);
+        }
         off[i] = (uint32_t)(((int64_t)k * ldb + 4 * c) * 4);
         lds_off[i] = (uint32_t)(MC::A_FLOATS * 4 + jb * 1024);
       }
