@@ -128,18 +128,26 @@ int gemm_f32_ex(int64_t M, int64_t N, int64_t K,
                 int variant, int cfg_id,
                 void *stream);
 
-/* C = A.B with the K range split into `splits` chunks (whole multiples of 64, so at most
- * `splits` are used; 1 .. 64) for shapes whose M x N tiles cannot fill the GPU, such as
+/* C = A.B with the K range split into chunks (whole multiples of 64, so at most the
+ * requested number are used), for shapes whose M x N tiles cannot fill the GPU, such as
  * the skinny decode-like regime the case study mentions ("Case Study: The Double-Buffered
- * GEMM", paragraph on the three regimes).  Each chunk's partial product goes into the
- * caller's `workspace` (device memory, >= gemm_f32_splitk_workspace(M, N, K, splits)
- * floats, 4-byte aligned, overlapping none of A, B, C); a second kernel then sums the
- * partials into C in a fixed order, so the result is deterministic (it differs in
- * rounding, within the accuracy of one product, from the unsplit one).  The workspace is
- * owned by the caller and overwritten; it may be NULL when fewer than two chunks result.
- * `splits` = 0 takes the modelled choice of gemm_f32_splitk_select.  Both kernels go on
- * `stream`.  Errors as for gemm_f32, plus GEMMF32_ERR_BAD_CONFIG for `splits` outside
- * 0 .. 64, GEMMF32_ERR_BAD_LD for a workspace that is too small, GEMMF32_ERR_NULL_PTR /
+ * GEMM", paragraph on the three regimes), or leave the last round of workgroups partly
+ * empty.
+ *   splits = s in 1 .. 64: every tile is split into s chunks; chunk y's partial product
+ *            is an M x N plane (rows of N floats) at workspace + y * M * N.
+ *   splits = -s, s in 2 .. 64 (tail split): the tiles that fill whole rounds of
+ *            workgroups run over the whole K range into C; only the tiles of the last,
+ *            partly filled round are split, their chunks packed as tile-sized blocks of
+ *            the workspace.  A product with no full round of tiles splits every tile.
+ *   splits = 0: the modelled choice of gemm_f32_splitk_select.
+ * A second kernel then sums each element's partials into C in the fixed chunk order, so
+ * the result is deterministic (it differs in rounding, within the accuracy of one
+ * product, from the unsplit one).  The `workspace` is device memory of at least
+ * gemm_f32_splitk_workspace(M, N, K, splits) floats, 4-byte aligned, overlapping none of
+ * A, B, C; it is owned by the caller and overwritten, and it may be NULL when fewer than
+ * two chunks result.  Both kernels go on `stream`.  Errors as for gemm_f32, plus
+ * GEMMF32_ERR_BAD_CONFIG for `splits` outside -64 .. 64 or equal to -1,
+ * GEMMF32_ERR_BAD_LD for a workspace that is too small, GEMMF32_ERR_NULL_PTR /
  * _MISALIGNED / _ALIAS for a bad workspace pointer. */
 int gemm_f32_splitk(int64_t M, int64_t N, int64_t K,
                     const float *A, int64_t lda,
@@ -152,10 +160,10 @@ int gemm_f32_splitk(int64_t M, int64_t N, int64_t K,
  * choice; the result is 0 when it will not split), or a negative error code. */
 int64_t gemm_f32_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits);
 
-/* The split count for a shape (1 = do not split) with the least modelled time among 1, 2,
- * 4, 8 and 16: the dispatch table's cost model of the chunks' GEMM in one grid plus the
- * split overhead fitted to the measured split study; host code only.  Negative sizes give
- * GEMMF32_ERR_NEGATIVE_DIM. */
+/* The split count for a shape with the least modelled time among 1 (do not split), the
+ * full splits 2, 4, 8, 16 and the tail splits -2, -4, -8, -16: the dispatch table's cost
+ * model of the GEMM part plus the split overhead fitted to the measured split study; host
+ * code only.  Negative sizes give GEMMF32_ERR_NEGATIVE_DIM. */
 int gemm_f32_splitk_select(int64_t M, int64_t N, int64_t K);
 
 /* The dispatch decision for a shape, without launching: *variant receives

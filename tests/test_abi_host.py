@@ -261,7 +261,7 @@ def test_splitk_workspace_sizes():
     assert ws(-1, 20, 100, 2) == tdb.ERR_NEGATIVE_DIM
     for shape in [(16, 4096, 4096), (4096, 4096, 4096), (1, 1, 1)]:
         sp = tdb.gemm_f32_splitk_select(*shape)
-        assert 1 <= sp <= 64
+        assert 1 <= abs(sp) <= 64
         assert ws(*shape, 0) == ws(*shape, sp)
     assert tdb.gemm_f32_splitk_select(-1, 2, 3) == tdb.ERR_NEGATIVE_DIM
 
@@ -281,10 +281,15 @@ def _split_model_constants():
 
 def _split_pick(M, N, K, rows, dims, consts, choices):
     """The split-count rule, read independently of the C++: least modelled time, where a
-    split launch costs the model's best GEMM of its chunks in one grid, plus a fixed cost,
-    a cost per MB of (2 * chunks + 1) * M * N * 4 bytes and a cost per round of workgroups
-    of that grid; first count on ties."""
+    full split costs the model's best GEMM of its chunks in one grid, plus a fixed cost, a
+    cost per MB of (2 * chunks + 1) * M * N * 4 bytes and a cost per round of workgroups of
+    that grid; a tail split (returned as -s) runs the full rounds whole and prices only the
+    tail tiles' chunks and bytes; first candidate on ties, full splits before tail ones."""
     r0, per_mb, per_round = consts
+
+    def plan(sp):
+        kc = max(64, -(-(-(-K // sp)) // 64) * 64)
+        return kc, (-(-K // kc) if K > 0 else 1)
 
     def gemm(m, n, k, wg):
         best = None
@@ -295,10 +300,26 @@ def _split_pick(M, N, K, rows, dims, consts, choices):
             if best is None or t < best[0]:
                 best = (t, tiles)
         return best
+
+    def tail(kc, used):
+        best = None
+        for (v, c, a, g) in rows:
+            bm, bn, bk = dims[c]
+            tiles = -(-M // bm) * -(-N // bn)
+            full = tiles // 256 * 256
+            rest = tiles - full
+            if full == 0 or rest == 0:
+                continue
+            tr = float(-(-(rest * used) // 256))
+            t = (a + g * (float(full // 256) * float(-(-K // bk)) + tr * float(-(-kc // bk)))
+                 + r0 + per_mb * ((2 * used + 1) * rest * bm * bn * 4.0 / 1e6) + per_round * tr)
+            if best is None or t < best:
+                best = t
+        return best
+
     best = None
     for sp in choices:
-        kc = max(64, -(-(-(-K // sp)) // 64) * 64)
-        used = -(-K // kc) if K > 0 else 1
+        kc, used = plan(sp)
         if used <= 1:
             t = gemm(M, N, K, 1)[0]
         else:
@@ -307,12 +328,22 @@ def _split_pick(M, N, K, rows, dims, consts, choices):
                  + per_round * float(-(-tiles // 256)))
         if best is None or t < best[0]:
             best = (t, sp)
+    for sp in choices:
+        if sp < 2 or K <= 0:
+            continue
+        kc, used = plan(sp)
+        if used <= 1:
+            continue
+        t = tail(kc, used)
+        if t is not None and t < best[0]:
+            best = (t, -sp)
     return best[1]
 
 
 @pytest.mark.parametrize("shape", [(16, 4096, 4096), (120, 2401, 3849), (10, 3657, 15587),
                                    (766, 2342, 13171), (256, 256, 8192), (4096, 4096, 4096),
-                                   (1, 1, 1), (7, 9, 0), (1, 50000, 64)])
+                                   (1, 1, 1), (7, 9, 0), (1, 50000, 64), (1536, 1536, 1536),
+                                   (2560, 2560, 2560), (5000, 5000, 1000), (1100, 1100, 300)])
 def test_split_count_follows_the_split_model(shape):
     consts, choices = _split_model_constants()
     assert min(consts) >= 0 and 1 in choices
@@ -324,22 +355,40 @@ def test_split_count_follows_the_split_model(shape):
 
 def test_split_model_agrees_with_the_split_study():
     """Over the shapes of the split study (the rows' trailing comments hold the measured
-    times of every count), the modelled count's time over the fastest count's: median at
-    most 1.02, at least 80% of the shapes within 5%, none beyond 1.25."""
+    times of every count, tail splits as negative counts), the modelled count's time over
+    the fastest count's: median at most 1.02, at least 80% of the shapes within 5%, none
+    beyond 1.25."""
     text = _header_text()
     body = text[text.index("kSplitK[] = {"):]
     body = body[:body.index("};")]
-    rows = re.findall(r"\{(\d+), (\d+), (\d+), (\d+)\},\s*//\s*(.*)", body)
+    rows = re.findall(r"\{(\d+), (\d+), (\d+), (-?\d+)\},\s*//\s*(.*)", body)
     assert len(rows) >= 10
     regrets = []
     for (m, n, k, _best, times) in rows:
-        us = {int(a): float(b) for a, b in re.findall(r"(\d+): ([0-9.]+)", times)}
+        us = {int(a): float(b) for a, b in re.findall(r"(-?\d+): ([0-9.]+)", times)}
         pick = tdb.gemm_f32_splitk_select(int(m), int(n), int(k))
         regrets.append(us[pick] / min(us.values()))
     regrets.sort()
     assert regrets[len(regrets) // 2] <= 1.02, regrets
     assert sum(r <= 1.05 for r in regrets) >= 0.8 * len(regrets), regrets
     assert regrets[-1] <= 1.25, regrets
+
+
+def test_tail_split_workspace_is_packed_tiles():
+    """A tail split needs only the split tiles' packed blocks; with no full round of tiles
+    (too few tiles) it splits every tile and needs the M x N planes."""
+    ws = tdb.gemm_f32_splitk_workspace
+    M = N = K = 1536
+    need = ws(M, N, K, -8)
+    assert 0 < need < 8 * M * N
+    # 1536 / 64 = 24: 576 tiles of 64 x 64 at most, 512 of them in full rounds
+    assert need % (64 * 64) == 0 or need % (128 * 128) == 0
+    assert ws(300, 200, 777, -2) == 2 * 300 * 200
+    assert ws(M, N, K, -65) == tdb.ERR_BAD_CONFIG
+    assert ws(M, N, 0, -4) == 0
+    sp = tdb.gemm_f32_splitk_select(M, N, K)
+    assert -64 <= sp <= 64 and sp != 0
+    assert ws(M, N, K, 0) == ws(M, N, K, sp)
 
 
 def test_splitk_validation_before_launch():

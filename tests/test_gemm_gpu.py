@@ -339,6 +339,34 @@ def test_splitk_parity(shape, splits):
     assert torch.equal(C, C2), "split-K is not deterministic"
 
 
+@pytest.mark.parametrize("shape,splits", [((1100, 1100, 300), -4), ((1536, 1536, 1536), -8),
+                                          ((1000, 1300, 257), -3), ((1536, 1536, 700), 0),
+                                          ((300, 200, 777), -2)])
+def test_splitk_tail_parity(shape, splits):
+    """Tail split (negative split counts, or the automatic choice): the tiles of the full
+    rounds of workgroups run whole into C, only the last round's tiles are split into
+    packed blocks of the workspace and summed into C.  Within the bound; deterministic;
+    the workspace the library asks for suffices (NaN-filled, so a block that is read but
+    never written would show).  A product with no full round splits every tile."""
+    M, N, K = shape
+    _say(f"[splitk-tail] {M}x{N}x{K} splits={splits} "
+         f"(chosen {tdb.gemm_f32_splitk_select(M, N, K) if splits == 0 else splits})")
+    A, B = ti.workload_inputs(M, N, K, 8100 + M + K)
+    C64, Bnd = oracle.gemm_f64(A, B)
+    Ad, Bd = _dev(A), _dev(B)
+    need = tdb.gemm_f32_splitk_workspace(M, N, K, splits)
+    ws = torch.full((max(need, 1),), float("nan"), device=DEV)
+    C = torch.full((M, N), float("nan"), device=DEV)
+    tdb.matmul_splitk(Ad, Bd, splits, out=C, workspace=ws)
+    torch.cuda.synchronize()
+    r = _ratio(C, C64, Bnd)
+    _say(f"[splitk-tail] ratio={r:.3g}")
+    assert r <= 1.0
+    C2 = tdb.matmul_splitk(Ad, Bd, splits, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(C, C2), "tail split is not deterministic"
+
+
 def test_splitk_one_split_equals_plain_and_errors():
     A, B, C64, Bnd = _workload("square_128")
     Ad, Bd = _dev(A), _dev(B)

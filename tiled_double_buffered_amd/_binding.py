@@ -208,7 +208,9 @@ def matmul(A, B, out=None, variant: str = "auto", cfg_id: int = -1, stream=None)
 
 
 def matmul_splitk(A, B, splits=0, out=None, workspace=None, stream=None):
-    """out = A @ B through gemm_f32_splitk.  `workspace` is a float32 GPU tensor of at least
+    """out = A @ B through gemm_f32_splitk (`splits`: s > 0 splits every tile into s K
+    chunks, -s only the tiles of the last partly filled round of workgroups, 0 the modelled
+    choice).  `workspace` is a float32 GPU tensor of at least
     gemm_f32_splitk_workspace(M, N, K, splits) elements; when None, one is allocated here
     with torch (the library itself never allocates)."""
     import torch

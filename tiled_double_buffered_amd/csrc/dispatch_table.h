@@ -168,15 +168,15 @@ static inline int select_for_variant(int64_t M, int64_t N, int64_t K, int varian
 // Split-K: the number of K chunks (1 = do not split) with the least modelled time among
 // the counts the split study measured.  A split launch costs the GEMM of its chunks, all in
 // one grid (the model above, with the workgroups multiplied by the chunks), plus
-//     2.4096 us (the reduction's launch)
-//   + 0.16505 us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
+//     0.0000 us (the reduction's launch)
+//   + 0.20133 us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
 //     written once and read once by the reduction, and C)
-//   + 0.9253 us per round of workgroups of the split grid (each workgroup's
+//   + 0.2828 us per round of workgroups of the split grid (each workgroup's
 //     first copy and partial-tile store, which short chunks no longer hide),
-// the constants fitted (>= 0, least squares) to the 35 shapes of the split study below.
-constexpr double kSplitFixedUs = 2.4096;
-constexpr double kSplitUsPerMB = 0.16505;
-constexpr double kSplitUsPerRound = 0.9253;
+// the constants fitted (>= 0, least squares) to the 41 shapes of the split study below.
+constexpr double kSplitFixedUs = 0.0000;
+constexpr double kSplitUsPerMB = 0.20133;
+constexpr double kSplitUsPerRound = 0.2828;
 constexpr int kSplitChoices[] = {1, 2, 4, 8, 16};
 
 // The split study: trailing comments hold the measured microseconds of each count.
@@ -186,41 +186,47 @@ struct SplitRow {
 };
 
 static const SplitRow kSplitK[] = {
-    {16, 4096, 4096, 8},  // 1: 69.5, 2: 38.6, 4: 24.0, 8: 19.9, 16: 21.8
-    {32, 4096, 4096, 8},  // 1: 63.2, 2: 39.1, 4: 24.5, 8: 19.1, 16: 22.1
-    {64, 4096, 4096, 4},  // 1: 60.8, 2: 34.7, 4: 23.6, 8: 24.0, 16: 26.6
-    {128, 4096, 4096, 2},  // 1: 61.2, 2: 35.8, 4: 38.0, 8: 39.5, 16: 43.7
-    {32, 8192, 8192, 4},  // 1: 124.1, 2: 73.3, 4: 46.2, 8: 48.6, 16: 55.1
-    {64, 8192, 8192, 2},  // 1: 119.2, 2: 69.1, 4: 73.2, 8: 77.9, 16: 88.4
-    {256, 256, 8192, 16},  // 1: 117.8, 2: 62.8, 4: 34.8, 8: 23.4, 16: 17.7
-    {512, 512, 8192, 4},  // 1: 118.7, 2: 63.5, 4: 37.6, 8: 39.0, 16: 40.8
-    {1024, 1024, 1024, 1},  // 1: 18.0, 2: 22.9, 4: 25.4, 8: 30.1, 16: 39.6
-    {2048, 2048, 2048, 1},  // 1: 118.3, 2: 130.4, 4: 139.7, 8: 158.4, 16: 206.1
-    {4096, 4096, 4096, 1},  // 1: 906.6, 2: 947.0, 4: 991.4, 8: 1099.7, 16: 1292.3
-    {39, 432, 6224, 16},  // 1: 105.3, 2: 56.3, 4: 31.8, 8: 20.7, 16: 16.0
-    {11, 1640, 2822, 16},  // 1: 49.8, 2: 29.1, 4: 18.4, 8: 13.2, 16: 12.3
-    {11, 1486, 1136, 16},  // 1: 21.8, 2: 14.5, 4: 10.9, 8: 9.6, 16: 9.5
-    {66, 326, 1317, 8},  // 1: 24.9, 2: 17.1, 4: 11.9, 8: 9.6, 16: 9.6
-    {63, 4495, 1443, 8},  // 1: 29.1, 2: 19.8, 4: 17.9, 8: 17.5, 16: 20.2
-    {24, 2252, 14173, 8},  // 1: 236.1, 2: 122.3, 4: 64.5, 8: 39.0, 16: 45.5
-    {132, 1012, 15340, 8},  // 1: 256.2, 2: 132.4, 4: 70.0, 8: 66.1, 16: 67.5
-    {10, 5016, 2286, 4},  // 1: 41.3, 2: 24.9, 4: 16.8, 8: 19.8, 16: 17.1
-    {16, 385, 2409, 16},  // 1: 42.6, 2: 25.0, 4: 15.9, 8: 11.8, 16: 11.0
-    {420, 479, 5136, 4},  // 1: 88.8, 2: 48.4, 4: 28.8, 8: 30.4, 16: 33.7
-    {178, 931, 4676, 4},  // 1: 87.1, 2: 47.8, 4: 26.8, 8: 28.1, 16: 27.0
-    {11, 315, 1813, 16},  // 1: 32.7, 2: 20.5, 4: 13.8, 8: 10.5, 16: 10.1
-    {217, 1127, 2447, 4},  // 1: 43.9, 2: 26.9, 4: 21.6, 8: 23.6, 16: 23.8
-    {137, 1231, 2351, 4},  // 1: 47.0, 2: 27.2, 4: 18.7, 8: 19.2, 16: 23.6
-    {378, 2886, 2015, 4},  // 1: 64.9, 2: 54.3, 4: 52.6, 8: 61.0, 16: 71.9
-    {130, 1580, 11590, 16},  // 1: 205.7, 2: 109.6, 4: 94.6, 8: 76.0, 16: 74.2
-    {276, 694, 15508, 8},  // 1: 277.1, 2: 145.4, 4: 81.8, 8: 77.1, 16: 81.7
-    {14, 1090, 8356, 16},  // 1: 140.5, 2: 73.9, 4: 39.9, 8: 24.5, 16: 18.4
-    {17, 1394, 1142, 16},  // 1: 21.9, 2: 14.5, 4: 10.9, 8: 9.5, 16: 9.3
-    {205, 3623, 5015, 4},  // 1: 100.3, 2: 84.1, 4: 83.1, 8: 86.4, 16: 106.5
-    {560, 759, 7039, 4},  // 1: 121.5, 2: 66.7, 4: 62.5, 8: 63.4, 16: 65.0
-    {143, 1910, 3628, 8},  // 1: 67.5, 2: 38.7, 4: 36.5, 8: 35.5, 16: 40.6
-    {471, 6763, 3812, 2},  // 1: 221.2, 2: 220.5, 4: 240.8, 8: 229.2, 16: 282.6
-    {201, 316, 7161, 8},  // 1: 128.4, 2: 68.4, 4: 37.9, 8: 23.5, 16: 24.6
+    {16, 4096, 4096, 8},  // 1: 69.2, 2: 38.7, 4: 23.3, 8: 17.5, 16: 21.5
+    {32, 4096, 4096, 8},  // 1: 63.1, 2: 39.2, 4: 23.6, 8: 17.3, 16: 21.7
+    {64, 4096, 4096, 8},  // 1: 60.5, 2: 34.8, 4: 23.0, 8: 23.0, 16: 26.1
+    {128, 4096, 4096, 2},  // 1: 61.2, 2: 35.7, 4: 37.1, 8: 39.2, 16: 43.3
+    {32, 8192, 8192, 4},  // 1: 124.1, 2: 73.5, 4: 45.7, 8: 46.6, 16: 52.0
+    {64, 8192, 8192, 2},  // 1: 119.3, 2: 68.2, 4: 70.9, 8: 75.4, 16: 87.1
+    {256, 256, 8192, 16},  // 1: 117.9, 2: 62.7, 4: 34.7, 8: 22.5, 16: 17.2
+    {512, 512, 8192, 4},  // 1: 118.9, 2: 63.8, 4: 35.5, 8: 37.4, 16: 40.2
+    {1024, 1024, 1024, 1},  // 1: 18.0, 2: 24.9, 4: 29.2, 8: 35.0, 16: 38.7
+    {2048, 2048, 2048, 1},  // 1: 117.9, 2: 130.0, 4: 139.3, 8: 157.8, 16: 203.2
+    {4096, 4096, 4096, 1},  // 1: 903.4, 2: 945.2, 4: 996.1, 8: 1113.6, 16: 1278.0, -2: 1068.4, -4: 1079.3, -8: 1122.3, -16: 1166.7
+    {1536, 1536, 1536, -4},  // 1: 68.2, 2: 66.5, 4: 64.8, 8: 76.6, 16: 88.2, -2: 61.4, -4: 57.1, -8: 57.9, -16: 63.8
+    {1536, 1536, 4096, -8},  // 1: 174.1, 2: 154.5, 4: 143.5, 8: 154.9, 16: 176.1, -2: 149.2, -4: 138.5, -8: 136.8, -16: 139.3
+    {2560, 2560, 2560, -8},  // 1: 255.7, 2: 263.2, 4: 272.2, 8: 292.0, 16: 366.3, -2: 244.1, -4: 240.5, -8: 234.3, -16: 240.4
+    {1280, 1280, 2048, -4},  // 1: 62.0, 2: 66.0, 4: 66.0, 8: 71.4, 16: 82.1, -2: 66.6, -4: 61.1, -8: 62.0, -16: 66.2
+    {5000, 5000, 1000, -8},  // 1: 393.7, 2: 442.1, 4: 532.5, 8: 742.7, 16: 1145.0, -2: 402.9, -4: 403.2, -8: 382.7, -16: 386.2
+    {1536, 3072, 4096, -8},  // 1: 289.7, 2: 270.2, 4: 280.8, 8: 302.0, 16: 369.9, -2: 272.5, -4: 266.6, -8: 266.3, -16: 270.2
+    {39, 432, 6224, 16},  // 1: 104.9, 2: 56.0, 4: 31.8, 8: 20.5, 16: 16.1
+    {11, 1640, 2822, 16},  // 1: 49.5, 2: 29.2, 4: 18.4, 8: 13.1, 16: 12.3
+    {11, 1486, 1136, 16},  // 1: 21.7, 2: 14.5, 4: 10.9, 8: 9.7, 16: 9.5
+    {66, 326, 1317, 8},  // 1: 24.8, 2: 17.1, 4: 12.0, 8: 9.7, 16: 9.7
+    {63, 4495, 1443, 8},  // 1: 29.0, 2: 20.0, 4: 19.0, 8: 18.9, 16: 19.7
+    {24, 2252, 14173, 8},  // 1: 235.2, 2: 121.7, 4: 64.5, 8: 38.1, 16: 40.1
+    {132, 1012, 15340, 16},  // 1: 254.9, 2: 131.3, 4: 69.3, 8: 65.6, 16: 55.4
+    {10, 5016, 2286, 4},  // 1: 41.1, 2: 24.9, 4: 16.7, 8: 19.6, 16: 16.9
+    {16, 385, 2409, 16},  // 1: 42.5, 2: 24.9, 4: 15.9, 8: 11.8, 16: 11.0
+    {420, 479, 5136, 4},  // 1: 88.2, 2: 48.1, 4: 28.6, 8: 31.3, 16: 34.0
+    {178, 931, 4676, 4},  // 1: 86.7, 2: 44.9, 4: 26.3, 8: 28.9, 16: 27.3
+    {11, 315, 1813, 16},  // 1: 32.7, 2: 20.6, 4: 13.8, 8: 10.6, 16: 10.3
+    {217, 1127, 2447, 4},  // 1: 43.5, 2: 26.6, 4: 18.3, 8: 21.4, 16: 23.9
+    {137, 1231, 2351, 4},  // 1: 46.8, 2: 25.4, 4: 17.6, 8: 19.7, 16: 24.6
+    {378, 2886, 2015, -8},  // 1: 64.7, 2: 55.9, 4: 52.2, 8: 52.2, 16: 68.1, -2: 55.5, -4: 48.0, -8: 45.7, -16: 47.4
+    {130, 1580, 11590, 8},  // 1: 204.2, 2: 102.7, 4: 94.2, 8: 73.9, 16: 75.6
+    {276, 694, 15508, 8},  // 1: 275.3, 2: 134.7, 4: 69.9, 8: 67.9, 16: 73.0
+    {14, 1090, 8356, 16},  // 1: 139.7, 2: 73.4, 4: 39.8, 8: 24.7, 16: 18.6
+    {17, 1394, 1142, 16},  // 1: 21.7, 2: 14.5, 4: 10.9, 8: 9.6, 16: 9.4
+    {205, 3623, 5015, 4},  // 1: 99.4, 2: 83.7, 4: 83.1, 8: 85.3, 16: 89.7
+    {560, 759, 7039, 8},  // 1: 120.6, 2: 64.6, 4: 61.6, 8: 61.4, 16: 62.1
+    {143, 1910, 3628, 2},  // 1: 67.0, 2: 36.3, 4: 36.5, 8: 40.4, 16: 44.1
+    {471, 6763, 3812, -2},  // 1: 219.9, 2: 215.2, 4: 214.9, 8: 237.4, 16: 280.2, -2: 206.8, -4: 253.6, -8: 253.8, -16: 257.8
+    {201, 316, 7161, 8},  // 1: 128.1, 2: 65.5, 4: 35.5, 8: 22.4, 16: 25.0
 };
 
 static inline double model_best_us(int64_t M, int64_t N, int64_t K, int64_t wg_factor) {
@@ -241,6 +247,38 @@ static inline double split_model_us(int64_t M, int64_t N, int64_t K, int splits)
          kSplitUsPerRound * rounds;
 }
 
+// Tail split: only the tiles of the last, partly filled round of workgroups are split (the
+// full rounds run whole), priced like a split launch whose overhead covers just those
+// tiles.  The pick with the least modelled time among the configurations whose tiles make
+// at least one full round and a partly filled one; found = false when there is none.
+struct TailPick {
+  bool found;
+  int variant, cfg;
+  int64_t split_from;
+  double us;
+};
+
+static inline TailPick tail_pick(int64_t M, int64_t N, int64_t K, int used, int64_t kc) {
+  TailPick best{false, 0, 0, 0, 0.0};
+  for (int i = 0; i < kModelRows; ++i) {
+    const ModelRow& r = kModel[i];
+    const CfgEntry& e = kConfigs[r.cfg];
+    const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
+    const int64_t full = tiles / kModelCUs * kModelCUs, tail = tiles - full;
+    if (full == 0 || tail == 0) continue;
+    const double tail_rounds = (double)((tail * used + kModelCUs - 1) / kModelCUs);
+    const double mb = (double)(2 * used + 1) * (double)tail * e.bm * e.bn * 4.0 / 1e6;
+    const double t = r.a_us +
+                     r.g_us * ((double)(full / kModelCUs) * (double)((K + e.bk - 1) / e.bk) +
+                               tail_rounds * (double)((kc + e.bk - 1) / e.bk)) +
+                     kSplitFixedUs + kSplitUsPerMB * mb + kSplitUsPerRound * tail_rounds;
+    if (!best.found || t < best.us) best = TailPick{true, r.variant, r.cfg, full, t};
+  }
+  return best;
+}
+
+// The split count: > 1 splits every tile, 1 does not split, -s splits only the tail tiles
+// into s chunks.
 static inline int select_splits(int64_t M, int64_t N, int64_t K) {
   int best = 1;
   double best_t = 0.0;
@@ -249,6 +287,19 @@ static inline int select_splits(int64_t M, int64_t N, int64_t K) {
     if (i == 0 || t < best_t) {
       best = kSplitChoices[i];
       best_t = t;
+    }
+  }
+  for (int i = 0; i < (int)(sizeof(kSplitChoices) / sizeof(kSplitChoices[0])); ++i) {
+    const int s = kSplitChoices[i];
+    if (s < 2 || K <= 0) continue;
+    int64_t kc = 0;
+    int used = 1;
+    splitk_plan(K, s, &kc, &used);
+    if (used <= 1) continue;
+    const TailPick tp = tail_pick(M, N, K, used, kc);
+    if (tp.found && tp.us < best_t) {
+      best = -s;
+      best_t = tp.us;
     }
   }
   return best;

@@ -73,12 +73,12 @@ enum : int {
 // ------------------------------------------------------------------------------------
 enum : int { kRasterGroupShift = 8, kRasterNoXcdRemap = 1 << 16 };
 
-__device__ inline void tile_coords(int tiles_m, int tiles_n, int flags, int& tm, int& tn) {
+// `bid` is the tile's index in launch order and `nwg` the number of tiles of the product.
+__device__ inline void tile_coords(int bid, int nwg, int tiles_m, int tiles_n, int flags,
+                                   int& tm, int& tn) {
   constexpr int kXcds = 8;
   const int gm_flag = (flags >> kRasterGroupShift) & 0xff;
   const int group_m = gm_flag ? gm_flag : 8;
-  const int nwg = gridDim.x;
-  int bid = blockIdx.x;
   if (!(flags & kRasterNoXcdRemap) && nwg % kXcds == 0)
     bid = (bid % kXcds) * (nwg / kXcds) + bid / kXcds;
   const int per_group = group_m * tiles_n;
@@ -448,18 +448,45 @@ __device__ inline void load_tile(TileCopy<C>& cp, const LoopArgs<C>& g, int kt) 
 // ------------------------------------------------------------------------------------
 // Per-workgroup setup shared by every kernel.
 // ------------------------------------------------------------------------------------
-// Split-K: grid row y multiplies the K range [y*k_chunk, y*k_chunk + k_chunk) into its own
-// M x N partial product at Cmat + y*c_split_stride.  A one-row grid is left untouched.
-template <class PA, class PB, class PC>
-__device__ __forceinline__ void split_k_range(int& K, PA& A, PB& B, int64_t ldb, PC& Cmat,
-                                              int k_chunk, int64_t c_split_stride) {
-  if (gridDim.y > 1) {
-    const int kb = blockIdx.y * k_chunk;
-    K = min(K - kb, k_chunk);
-    A += kb;
-    B += (int64_t)kb * ldb;
-    Cmat += (int64_t)blockIdx.y * c_split_stride;
-  }
+// How a launch divides the product among workgroups.  Tiles 0 .. split_from-1 (in launch
+// order) each run one workgroup over the whole K range into C.  Every later tile runs
+// `chunks` workgroups; chunk y multiplies the K range [y*k_chunk, y*k_chunk + k_chunk)
+// into a partial product that a reduction kernel then sums.  Workgroups: split_from +
+// (tiles - split_from) * chunks, tile-major.
+//   plain launch:  split_from = tiles;
+//   full split-K:  split_from = 0, chunk y of every tile goes to its M x N plane at
+//                  ws + y*plane (rows of N floats);
+//   tail split:    split_from = the tiles of the full rounds of workgroups; only the tiles
+//                  of the last, partly filled round are split, and chunk y of split tile u
+//                  (u = tile - split_from) goes to a packed BM x BN block at
+//                  ws + (y * (tiles - split_from) + u) * BM * BN.
+struct SplitArgs {
+  float* ws;
+  int64_t plane;
+  int k_chunk;
+  int chunks;
+  int split_from;
+  int tiles;
+};
+
+struct SplitWork {
+  int bid;    // the tile's index in launch order
+  int chunk;  // its K chunk, or -1 for the whole K range
+};
+
+// This workgroup's tile and K chunk, with K, A and B moved to the chunk.
+template <class PA, class PB>
+__device__ __forceinline__ SplitWork split_work(const SplitArgs& sp, int& K, PA& A, PB& B,
+                                                int64_t ldb) {
+  const int id = blockIdx.x;
+  if (id < sp.split_from) return SplitWork{id, -1};
+  const int j = id - sp.split_from;
+  const int y = j % sp.chunks;
+  const int kb = y * sp.k_chunk;
+  K = min(K - kb, sp.k_chunk);
+  A += kb;
+  B += (int64_t)kb * ldb;
+  return SplitWork{sp.split_from + j / sp.chunks, y};
 }
 
 // Where this workgroup, wave and lane sit, and the copy arguments of the K-loop.
@@ -470,14 +497,14 @@ struct TilePos {
   LoopArgs<C> g;
 
   __device__ inline void init(int M, int N, int K, const float* A, int64_t lda,
-                              const float* B, int64_t ldb, int flags) {
+                              const float* B, int64_t ldb, int flags, int bid, int nwg) {
     tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     wm = wave / C::WAVES_N;
     wn = wave % C::WAVES_N;
     int tm, tn;
-    tile_coords((M + C::BM - 1) / C::BM, (N + C::BN - 1) / C::BN, flags, tm, tn);
+    tile_coords(bid, nwg, (M + C::BM - 1) / C::BM, (N + C::BN - 1) / C::BN, flags, tm, tn);
     g.A = A;
     g.B = B;
     g.lda = lda;
@@ -498,6 +525,23 @@ struct TilePos {
   // tail included, see the fast path of TileCopy).
   __device__ inline bool unguarded() const { return g.vec_a && g.vec_b; }
 };
+
+// Where a K chunk's partial product goes (see SplitArgs): the output pointer is set so
+// that the epilogue's usual (row * ldc + column) addressing of the tile lands in the
+// chunk's plane or packed block.
+template <class C, class PC>
+__device__ __forceinline__ void split_output(const SplitArgs& sp, const SplitWork& w, int N,
+                                             const TilePos<C>& t, PC& Cmat, int64_t& ldc) {
+  if (w.chunk < 0) return;
+  if (sp.split_from == 0) {
+    Cmat = sp.ws + (int64_t)w.chunk * sp.plane;
+    ldc = N;
+    return;
+  }
+  const int64_t slot = (int64_t)w.chunk * (sp.tiles - sp.split_from) + (w.bid - sp.split_from);
+  Cmat = sp.ws + slot * (C::BM * C::BN) - ((int64_t)t.g.m0 * C::BN + t.g.n0);
+  ldc = C::BN;
+}
 
 template <class C>
 __device__ inline void zero_acc(floatx16 (&acc)[C::FM][C::FN]) {

@@ -24,6 +24,7 @@
 // dispatch and the C ABI.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -55,7 +56,7 @@ using Cfg11 = TileCfg<192, 192, 16, 2, 2>;  // wave 96x96: 16x16 tiles for 3072-
 using Cfg12 = TileCfg<192, 192, 32, 2, 2>;  // wave 96x96, deeper K tile
 
 typedef void (*KernelFn)(int, int, int, const float*, int64_t, const float*, int64_t, float*,
-                         int64_t, int, int, int64_t);
+                         int64_t, int, SplitArgs);
 
 struct CfgEntry {
   int bm, bn, bk, nt;
@@ -154,31 +155,49 @@ static int env_raster_flags() {
   return flags;
 }
 
-// One launch of a GEMM kernel.  splits > 1: grid rows y = 0..splits-1 each multiply the
-// K range [y*k_chunk, ...) into C + y*c_split_stride (the split-K partial products).
-static int launch(int variant, int cfg_id, int64_t M, int64_t N, int64_t K, const float* A,
-                  int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
-                  void* stream, int splits = 1, int k_chunk = 0, int64_t c_split_stride = 0) {
-  const CfgEntry& e = kConfigs[cfg_id];
-  const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
-  if (tiles * e.nt > 0xFFFFFFFFLL) return GEMMF32_ERR_TOO_LARGE;
+// How one launch divides the product (the host side of SplitArgs).  split_from: the first
+// split tile in launch order (0: every tile is split).
+struct SplitPlan {
+  float* ws;
+  int64_t plane;
+  int64_t k_chunk;
+  int chunks;
+  int64_t split_from;
+};
+
+// Kernel flags of a launch with tile configuration e.
+static int launch_flags(const CfgEntry& e, int64_t K, int64_t lda, int64_t ldb) {
   int flags = 0;
   // 16-byte copies address a tile with 32-bit per-thread byte offsets (rows x leading
   // dimension), which must stay below the buffer range; rows need only the 4-byte
   // alignment that validation already demands.
   if (K > 0 && (int64_t)e.bm * lda * 4 <= (int64_t)kBufferRange) flags |= kVecA;
   if (K > 0 && (int64_t)e.bk * ldb * 4 <= (int64_t)kBufferRange) flags |= kVecB;
-  flags |= env_raster_flags();
+  return flags | env_raster_flags();
+}
+
+// One launch of a GEMM kernel: every tile over the whole K range into C, or with `plan`,
+// the tiles from plan->split_from on in plan->chunks K chunks into the workspace.
+static int launch(int variant, int cfg_id, int64_t M, int64_t N, int64_t K, const float* A,
+                  int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
+                  void* stream, const SplitPlan* plan = nullptr) {
+  const CfgEntry& e = kConfigs[cfg_id];
+  const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
+  const int64_t from = plan ? std::min(plan->split_from, tiles) : tiles;
+  const int64_t chunks = plan ? plan->chunks : 1;
+  const int64_t wgs = from + (tiles - from) * chunks;
+  if (wgs * e.nt > 0xFFFFFFFFLL) return GEMMF32_ERR_TOO_LARGE;
+  int flags = launch_flags(e, K, lda, ldb);
   int m = (int)M, n = (int)N, k = (int)K;
-  int kc = splits > 1 ? k_chunk : k;
-  void* args[] = {&m,   &n,     &k,  (void*)&A, &lda, (void*)&B,
-                  &ldb, &C,     &ldc, &flags,   &kc,  &c_split_stride};
+  SplitArgs sp{plan ? plan->ws : nullptr, plan ? plan->plane : 0,
+               plan ? (int)plan->k_chunk : k, (int)chunks, (int)from, (int)tiles};
+  void* args[] = {&m, &n, &k, (void*)&A, &lda, (void*)&B, &ldb, &C, &ldc, &flags, &sp};
   KernelFn fn = variant == GEMMF32_VARIANT_SB    ? e.sb
                 : variant == GEMMF32_VARIANT_MS  ? e.ms
                 : variant == GEMMF32_VARIANT_SB3 ? e.sb3
                                                  : e.db;
-  hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)tiles, (unsigned)splits),
-                                   dim3(e.nt), args, 0, (hipStream_t)stream);
+  hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)wgs), dim3(e.nt), args, 0,
+                                   (hipStream_t)stream);
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
     return GEMMF32_ERR_HIP;
@@ -218,46 +237,88 @@ static int run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, con
 }
 
 
+// The plan of a split-K call with `splits` (> 0: every tile split; < 0: only the tail tiles
+// split into -splits chunks, or every tile when the product has no tail): the chunks, the
+// tile configuration, the first split tile and the workspace floats.  used <= 1: no split.
+struct SplitLayout {
+  int64_t kc;
+  int used;
+  int variant, cfg;
+  int64_t split_from;
+  int64_t need;
+};
+
+static SplitLayout splitk_layout(int64_t M, int64_t N, int64_t K, int splits) {
+  SplitLayout L{0, 1, 0, 0, 0, 0};
+  if (K > 0) splitk_plan(K, splits < 0 ? -splits : splits, &L.kc, &L.used);
+  if (L.used <= 1) return L;
+  const TailPick tp = splits < 0 ? tail_pick(M, N, K, L.used, L.kc) : TailPick{};
+  if (tp.found) {
+    // Full rounds run whole; the split tiles' chunks go to packed tile blocks.
+    const CfgEntry& e = kConfigs[tp.cfg];
+    const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
+    L.variant = tp.variant;
+    L.cfg = tp.cfg;
+    L.split_from = tp.split_from;
+    L.need = (int64_t)L.used * (tiles - tp.split_from) * e.bm * e.bn;
+  } else {
+    // Every tile split: its chunks run side by side in one grid, so the tile is chosen for
+    // `used` times the workgroups of one chunk's product; partial products are M x N planes.
+    const ModelRow& pick = model_pick(M, N, L.kc, 0, L.used);
+    L.variant = pick.variant;
+    L.cfg = pick.cfg;
+    L.need = (int64_t)L.used * M * N;
+  }
+  return L;
+}
+
 static int run_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                       const float* B, int64_t ldb, float* C, int64_t ldc, int splits,
                       float* ws, int64_t ws_floats, void* stream) {
   if (splits == 0 && M >= 0 && N >= 0 && K >= 0) splits = select_splits(M, N, K);
-  if (splits < 1 || splits > kMaxSplits) return GEMMF32_ERR_BAD_CONFIG;
+  if (splits == 0 || splits == -1 || splits < -kMaxSplits || splits > kMaxSplits)
+    return GEMMF32_ERR_BAD_CONFIG;
   int rc = validate(M, N, K, A, lda, B, ldb, C, ldc);
   if (rc != GEMMF32_OK) return rc;
   if (M == 0 || N == 0) return GEMMF32_OK;
-  int64_t kc = 0;
-  int used = 1;
-  if (K > 0) splitk_plan(K, splits, &kc, &used);
-  if (used <= 1) return run(M, N, K, A, lda, B, ldb, C, ldc, GEMMF32_VARIANT_AUTO, -1, stream);
-  const int64_t need = (int64_t)used * M * N;
+  const SplitLayout L = splitk_layout(M, N, K, splits);
+  if (L.used <= 1) return run(M, N, K, A, lda, B, ldb, C, ldc, GEMMF32_VARIANT_AUTO, -1, stream);
   if (ws == nullptr) return GEMMF32_ERR_NULL_PTR;
   if (((uintptr_t)ws & 3u) != 0) return GEMMF32_ERR_MISALIGNED;
-  if (ws_floats < need) return GEMMF32_ERR_BAD_LD;
+  if (ws_floats < L.need) return GEMMF32_ERR_BAD_LD;
   // The workspace must not overlap A, B or C.
-  const uintptr_t w0 = (uintptr_t)ws, w1 = w0 + (uintptr_t)(need * 4);
+  const uintptr_t w0 = (uintptr_t)ws, w1 = w0 + (uintptr_t)(L.need * 4);
   const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)(((M - 1) * lda + K) * 4);
   const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)(((K - 1) * ldb + N) * 4);
   const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)(((M - 1) * ldc + N) * 4);
   if ((w0 < a1 && a0 < w1) || (w0 < b1 && b0 < w1) || (w0 < c1 && c0 < w1))
     return GEMMF32_ERR_ALIAS;
-  // The chunks run side by side in one grid, so the tile is chosen for `used` times the
-  // workgroups of one chunk's product.
-  const ModelRow& pick = model_pick(M, N, kc, 0, used);
-  rc = launch(pick.variant, pick.cfg, M, N, K, A, lda, B, ldb, ws, N, stream, used, (int)kc,
-              M * N);
+  const SplitPlan plan{ws, M * N, L.kc, L.used, L.split_from};
+  rc = launch(L.variant, L.cfg, M, N, K, A, lda, B, ldb, C, ldc, stream, &plan);
   if (rc != GEMMF32_OK) return rc;
-  const bool vec = (N % 4) == 0 && (ldc % 4) == 0 && ((uintptr_t)ws & 15u) == 0 &&
-                   ((uintptr_t)C & 15u) == 0;
-  const int64_t items = vec ? M * (N / 4) : M * N;
-  const int64_t blocks64 = (items + 255) / 256;
-  const unsigned blocks = (unsigned)(blocks64 < 4096 ? blocks64 : 4096);
-  int m = (int)M, n = (int)N;
+  int m = (int)M, n = (int)N, used = L.used;
   const float* p = ws;
-  void* args[] = {&m, &n, &used, (void*)&p, &C, &ldc};
-  const void* fn = vec ? (const void*)&gemm_f32_splitk_reduce<true>
-                       : (const void*)&gemm_f32_splitk_reduce<false>;
-  hipError_t err = hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, (hipStream_t)stream);
+  hipError_t err;
+  if (L.split_from > 0) {
+    const CfgEntry& e = kConfigs[L.cfg];
+    const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
+    int bm = e.bm, bn = e.bn, from = (int)L.split_from, nt = (int)tiles;
+    int flags = env_raster_flags();
+    void* args[] = {&m, &n, &used, (void*)&p, &C, &ldc, &bm, &bn, &from, &nt, &flags};
+    const dim3 grid((unsigned)(tiles - L.split_from), (unsigned)((bm * bn + 255) / 256));
+    err = hipLaunchKernel((const void*)&gemm_f32_splitk_reduce_tiles, grid, dim3(256), args, 0,
+                          (hipStream_t)stream);
+  } else {
+    const bool vec = (N % 4) == 0 && (ldc % 4) == 0 && ((uintptr_t)ws & 15u) == 0 &&
+                     ((uintptr_t)C & 15u) == 0;
+    const int64_t items = vec ? M * (N / 4) : M * N;
+    const int64_t blocks64 = (items + 255) / 256;
+    const unsigned blocks = (unsigned)(blocks64 < 4096 ? blocks64 : 4096);
+    void* args[] = {&m, &n, &used, (void*)&p, &C, &ldc};
+    const void* fn = vec ? (const void*)&gemm_f32_splitk_reduce<true>
+                         : (const void*)&gemm_f32_splitk_reduce<false>;
+    err = hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, (hipStream_t)stream);
+  }
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
     return GEMMF32_ERR_HIP;
@@ -311,12 +372,11 @@ int gemm_f32_splitk_select(int64_t M, int64_t N, int64_t K) {
 int64_t gemm_f32_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits) {
   if (M < 0 || N < 0 || K < 0) return GEMMF32_ERR_NEGATIVE_DIM;
   if (splits == 0) splits = select_splits(M, N, K);
-  if (splits < 1 || splits > kMaxSplits) return GEMMF32_ERR_BAD_CONFIG;
+  if (splits == 0 || splits == -1 || splits < -kMaxSplits || splits > kMaxSplits)
+    return GEMMF32_ERR_BAD_CONFIG;
   if (M == 0 || N == 0 || K == 0) return 0;
-  int64_t kc = 0;
-  int used = 1;
-  splitk_plan(K, splits, &kc, &used);
-  return used <= 1 ? 0 : (int64_t)used * M * N;
+  const SplitLayout L = splitk_layout(M, N, K, splits);
+  return L.used <= 1 ? 0 : L.need;
 }
 
 int gemm_f32_select(int64_t M, int64_t N, int64_t K, int* variant, int* cfg_id) {

@@ -282,13 +282,14 @@ template <class C, int S>
 __global__ void __launch_bounds__(C::NT)
 gemm_f32_ms_kernel(int M, int N, int K, const float* __restrict__ A, int64_t lda,
                    const float* __restrict__ B, int64_t ldb, float* __restrict__ Cmat,
-                   int64_t ldc, int flags, int k_chunk, int64_t c_split_stride) {
+                   int64_t ldc, int flags, SplitArgs sp) {
   using MC = MsCfg<C, S>;
   __shared__ __attribute__((aligned(1024))) float smem[MC::LDS_FLOATS];
 
-  split_k_range(K, A, B, ldb, Cmat, k_chunk, c_split_stride);
+  const SplitWork w = split_work(sp, K, A, B, ldb);
   TilePos<C> t;
-  t.init(M, N, K, A, lda, B, ldb, flags);
+  t.init(M, N, K, A, lda, B, ldb, flags, w.bid, sp.tiles);
+  split_output(sp, w, N, t, Cmat, ldc);
   floatx16 acc[C::FM][C::FN];
   zero_acc<C>(acc);
   const int k_tiles = (K + C::BK - 1) / C::BK;

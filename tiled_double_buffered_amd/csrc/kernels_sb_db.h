@@ -150,16 +150,17 @@ template <class C, int LOOP>
 __global__ void __launch_bounds__(C::NT)
 gemm_f32_tile_kernel(int M, int N, int K, const float* __restrict__ A, int64_t lda,
                      const float* __restrict__ B, int64_t ldb, float* __restrict__ Cmat,
-                     int64_t ldc, int flags, int k_chunk, int64_t c_split_stride) {
+                     int64_t ldc, int flags, SplitArgs sp) {
   static_assert((C::BK / 8) % 2 == 0, "BK/8 rounds must be even for the fragment ping-pong");
   static_assert(LOOP == kLoopSB || LOOP == kLoopDB || LOOP == kLoopSB3, "loop kind");
   constexpr bool DB = LOOP == kLoopDB;
   constexpr bool SPLIT = LOOP == kLoopSB3;
   __shared__ __attribute__((aligned(16))) float smem[(DB ? 2 : 1) * C::SLOT];
 
-  split_k_range(K, A, B, ldb, Cmat, k_chunk, c_split_stride);
+  const SplitWork w = split_work(sp, K, A, B, ldb);
   TilePos<C> t;
-  t.init(M, N, K, A, lda, B, ldb, flags);
+  t.init(M, N, K, A, lda, B, ldb, flags, w.bid, sp.tiles);
+  split_output(sp, w, N, t, Cmat, ldc);
   floatx16 acc[C::FM][C::FN];
   zero_acc<C>(acc);
   TileCopy<C> cp;

@@ -40,4 +40,38 @@ gemm_f32_splitk_reduce(int M, int N, int S, const float* __restrict__ P,
   }
 }
 
+// Tail split: only the tiles split_from .. tiles-1 (in launch order) were split; chunk y
+// of split tile u is a packed bm x bn block at P + (y * U + u) * bm * bn (U split tiles),
+// and the sum P[0] + P[1] + ... + P[S-1] is taken in that order as above.  Workgroup
+// (u, b) sums elements b*256 .. b*256+255 of split tile u, one per thread, its S loads
+// issued ahead of the additions; the tile's place in C comes from the same launch-order
+// -> tile mapping as in the GEMM launch (tile configuration bm x bn, the same flags).
+__global__ void __launch_bounds__(256)
+gemm_f32_splitk_reduce_tiles(int M, int N, int S, const float* __restrict__ P,
+                             float* __restrict__ C, int64_t ldc, int bm, int bn,
+                             int split_from, int tiles, int flags) {
+  const int u = blockIdx.x;
+  const int e = blockIdx.y * 256 + threadIdx.x;
+  const int r = e / bn, c = e % bn;
+  int tm, tn;
+  tile_coords(split_from + u, tiles, (M + bm - 1) / bm, (N + bn - 1) / bn, flags, tm, tn);
+  const int i = tm * bm + r, j = tn * bn + c;
+  if (r >= bm || i >= M || j >= N) return;
+  const int64_t block = (int64_t)bm * bn;
+  const int64_t chunk = (int64_t)(tiles - split_from) * block;
+  const float* p = P + (int64_t)u * block + e;
+  float acc = p[0];
+  int sp = 1;
+  for (; sp + 4 <= S; sp += 4) {
+    const float v0 = p[sp * chunk], v1 = p[(sp + 1) * chunk], v2 = p[(sp + 2) * chunk],
+                v3 = p[(sp + 3) * chunk];
+    acc += v0;
+    acc += v1;
+    acc += v2;
+    acc += v3;
+  }
+  for (; sp < S; ++sp) acc += p[sp * chunk];
+  C[(int64_t)i * ldc + j] = acc;
+}
+
 }  // namespace gemmf32

@@ -53,6 +53,9 @@ SHAPES = [
 SPLIT_SHAPES = [(16, 4096, 4096), (32, 4096, 4096), (64, 4096, 4096), (128, 4096, 4096),
                 (32, 8192, 8192), (64, 8192, 8192), (256, 256, 8192), (512, 512, 8192),
                 (1024, 1024, 1024), (2048, 2048, 2048), (4096, 4096, 4096)]
+# Shapes whose tiles leave the last round of workgroups partly filled (the tail split).
+TAIL_SHAPES = [(1536, 1536, 1536), (1536, 1536, 4096), (2560, 2560, 2560), (1280, 1280, 2048),
+               (5000, 5000, 1000), (1536, 3072, 4096)]
 SPLIT_CHOICES = (1, 2, 4, 8, 16)
 # Skinny shapes measured only to fit the split model.
 SPLIT_TRAIN_SEED = 7
@@ -204,6 +207,38 @@ static inline double split_model_us(int64_t M, int64_t N, int64_t K, int splits)
          kSplitUsPerRound * rounds;
 }}
 
+// Tail split: only the tiles of the last, partly filled round of workgroups are split (the
+// full rounds run whole), priced like a split launch whose overhead covers just those
+// tiles.  The pick with the least modelled time among the configurations whose tiles make
+// at least one full round and a partly filled one; found = false when there is none.
+struct TailPick {{
+  bool found;
+  int variant, cfg;
+  int64_t split_from;
+  double us;
+}};
+
+static inline TailPick tail_pick(int64_t M, int64_t N, int64_t K, int used, int64_t kc) {{
+  TailPick best{{false, 0, 0, 0, 0.0}};
+  for (int i = 0; i < kModelRows; ++i) {{
+    const ModelRow& r = kModel[i];
+    const CfgEntry& e = kConfigs[r.cfg];
+    const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
+    const int64_t full = tiles / kModelCUs * kModelCUs, tail = tiles - full;
+    if (full == 0 || tail == 0) continue;
+    const double tail_rounds = (double)((tail * used + kModelCUs - 1) / kModelCUs);
+    const double mb = (double)(2 * used + 1) * (double)tail * e.bm * e.bn * 4.0 / 1e6;
+    const double t = r.a_us +
+                     r.g_us * ((double)(full / kModelCUs) * (double)((K + e.bk - 1) / e.bk) +
+                               tail_rounds * (double)((kc + e.bk - 1) / e.bk)) +
+                     kSplitFixedUs + kSplitUsPerMB * mb + kSplitUsPerRound * tail_rounds;
+    if (!best.found || t < best.us) best = TailPick{{true, r.variant, r.cfg, full, t}};
+  }}
+  return best;
+}}
+
+// The split count: > 1 splits every tile, 1 does not split, -s splits only the tail tiles
+// into s chunks.
 static inline int select_splits(int64_t M, int64_t N, int64_t K) {{
   int best = 1;
   double best_t = 0.0;
@@ -212,6 +247,19 @@ static inline int select_splits(int64_t M, int64_t N, int64_t K) {{
     if (i == 0 || t < best_t) {{
       best = kSplitChoices[i];
       best_t = t;
+    }}
+  }}
+  for (int i = 0; i < (int)(sizeof(kSplitChoices) / sizeof(kSplitChoices[0])); ++i) {{
+    const int s = kSplitChoices[i];
+    if (s < 2 || K <= 0) continue;
+    int64_t kc = 0;
+    int used = 1;
+    splitk_plan(K, s, &kc, &used);
+    if (used <= 1) continue;
+    const TailPick tp = tail_pick(M, N, K, used, kc);
+    if (tp.found && tp.us < best_t) {{
+      best = -s;
+      best_t = tp.us;
     }}
   }}
   return best;
@@ -389,14 +437,20 @@ def barrier_study(shapes=BARRIER_SHAPES, rounds=2, batches=5, batch_ms=20.0, log
 
 def split_study(shapes=SPLIT_SHAPES, choices=SPLIT_CHOICES, rounds=2, batches=5,
                 batch_ms=20.0, log=print):
-    """Time gemm_f32_splitk for each split count (1 = the plain dispatched product)."""
+    """Time gemm_f32_splitk for each split count (1 = the plain dispatched product; -s = the
+    tail split into s chunks, where the product has a tail)."""
     import torch
 
     out = []
     for (M, N, K) in shapes:
         A, B, C = _operands(M, N, K)
         s_ptr = torch.cuda.current_stream().cuda_stream
-        need = max(tdb.gemm_f32_splitk_workspace(M, N, K, sp) for sp in choices)
+        # a tail split (-s) is timed where the product has a tail, i.e. where it is not
+        # the full split of the same count (the two ask for different workspaces)
+        wsz = tdb.gemm_f32_splitk_workspace
+        counts = list(choices) + [-sp for sp in choices
+                                  if sp > 1 and wsz(M, N, K, -sp) != wsz(M, N, K, sp)]
+        need = max(wsz(M, N, K, sp) for sp in counts)
         ws = torch.empty(max(need, 1), device=A.device)
 
         def caller(sp):
@@ -406,7 +460,7 @@ def split_study(shapes=SPLIT_SHAPES, choices=SPLIT_CHOICES, rounds=2, batches=5,
                 if rc != tdb.OK:
                     raise tdb.GemmError(rc, "gemm_f32_splitk")
             return call
-        us = time_calls({str(sp): caller(sp) for sp in choices}, rounds, batches, batch_ms)
+        us = time_calls({str(sp): caller(sp) for sp in counts}, rounds, batches, batch_ms)
         out.append({"M": M, "N": N, "K": K, "us": us})
         best = min(us, key=us.get)
         log(f"{M}x{N}x{K}: " + ", ".join(f"s{k} {v:.1f}" for k, v in us.items())
@@ -568,19 +622,35 @@ def split_extra_mb(M, N, used):
 
 
 def split_features(M, N, K, splits, model, dims):
-    """(chunks used, modelled GEMM us of the chunks in one grid, [1, extra MB, rounds]) of a
-    split launch; the overhead model is the dot product of fitted constants with the list."""
-    kc, used = split_plan(K, splits)
-    t, _v, c = _model_pick_py(M, N, kc, model, dims, used)
-    bm, bn = dims[c][0], dims[c][1]
-    rounds = -(-(-(-M // bm) * -(-N // bn) * used) // 256)
-    return used, t, [1.0, split_extra_mb(M, N, used), float(rounds)]
+    """(chunks used, modelled GEMM us, [1, extra MB, rounds]) of a split launch; the
+    overhead model is the dot product of fitted constants with the list.  splits < 0: the
+    tail split (full rounds whole, the tail tiles' chunks priced), with the configuration of
+    least modelled GEMM time among those that have a tail; None when none has."""
+    kc, used = split_plan(K, abs(splits))
+    if splits > 0:
+        t, _v, c = _model_pick_py(M, N, kc, model, dims, used)
+        bm, bn = dims[c][0], dims[c][1]
+        rounds = -(-(-(-M // bm) * -(-N // bn) * used) // 256)
+        return used, t, [1.0, split_extra_mb(M, N, used), float(rounds)]
+    best = None
+    for (v, c, a, g, _e) in model:
+        bm, bn, bk = dims[c][:3]
+        tiles = -(-M // bm) * -(-N // bn)
+        full = tiles // 256 * 256
+        rest = tiles - full
+        if full == 0 or rest == 0:
+            continue
+        tr = -(-(rest * used) // 256)
+        t = a + g * (full // 256 * -(-K // bk) + tr * -(-kc // bk))
+        if best is None or t < best[0]:
+            best = (t, [1.0, (2 * used + 1) * rest * bm * bn * 4 / 1e6, float(tr)])
+    return (used, best[0], best[1]) if best else None
 
 
 def fit_split_model(split_results, model, dims):
     """(fixed us, us per extra MB, us per round of workgroups) >= 0 of the split overhead:
-    least squares of what the measured split launches took beyond the modelled GEMM of their
-    chunks."""
+    least squares of what the measured split launches (full and tail) took beyond the
+    modelled GEMM of their chunks."""
     import numpy as np
     from scipy.optimize import nnls
 
@@ -588,10 +658,10 @@ def fit_split_model(split_results, model, dims):
     for r in split_results:
         M, N, K = r["M"], r["N"], r["K"]
         for sp, us in r["us"].items():
-            used, gemm, f = split_features(M, N, K, int(sp), model, dims)
-            if used > 1:
-                X.append(f)
-                y.append(us - gemm)
+            f = split_features(M, N, K, int(sp), model, dims)
+            if f is not None and f[0] > 1:
+                X.append(f[2])
+                y.append(us - f[1])
     coef, _ = nnls(np.array(X), np.array(y))
     return tuple(float(c) for c in coef)
 
@@ -731,7 +801,7 @@ def write_header(results, device, rounds, batches, batch_ms, path=None, split_re
              for (v, c, a, g, e) in model]
     r0, per_mb, per_round = (fit_split_model(split_results, model, dims) if split_results
                              else (3.0, 0.3, 1.0))
-    choices = sorted({int(k) for r in (split_results or []) for k in r["us"]}) or [1]
+    choices = sorted({int(k) for r in (split_results or []) for k in r["us"] if int(k) > 0}) or [1]
     text = HEADER_TEMPLATE.format(device=device, rounds=rounds, batches=batches,
                                   batch_ms=int(batch_ms), rows="\n".join(lines),
                                   split_rows="\n".join(srows), model_rows="\n".join(mrows),
@@ -766,6 +836,9 @@ def main(argv=None) -> int:
     ap.add_argument("--holdout-splitk", type=int, default=0, metavar="N",
                     help="time every split count on N seeded skinny shapes and report how "
                          "far gemm_f32_splitk_select is from the fastest")
+    ap.add_argument("--split-only", default=None, metavar="BASE_JSON",
+                    help="re-measure only the split study; the table and training rows "
+                         "come from an earlier --out file")
     ap.add_argument("--split-json", default=None,
                     help="an earlier --out file whose split study the nearest-row rule of "
                          "--holdout-splitk is measured against")
@@ -814,11 +887,17 @@ def main(argv=None) -> int:
     props = torch.cuda.get_device_properties(0)
     device = f"{props.name} ({getattr(props, 'gcnArchName', '?')})"
     t0 = time.time()
-    results = measure(SHAPES, args.rounds, args.batches, args.batch_ms,
-                      log=lambda *a: print(*a, flush=True))
-    train = measure(train_shapes(), args.rounds, args.batches, args.batch_ms,
-                    log=lambda *a: print(*a, flush=True))
-    splits = split_study(SPLIT_SHAPES + skinny_shapes(SPLIT_TRAIN_COUNT, SPLIT_TRAIN_SEED),
+    if args.split_only:
+        with open(args.split_only) as f:
+            base = json.load(f)
+        results, train = base["results"], base.get("train")
+    else:
+        results = measure(SHAPES, args.rounds, args.batches, args.batch_ms,
+                          log=lambda *a: print(*a, flush=True))
+        train = measure(train_shapes(), args.rounds, args.batches, args.batch_ms,
+                        log=lambda *a: print(*a, flush=True))
+    splits = split_study(SPLIT_SHAPES + TAIL_SHAPES
+                         + skinny_shapes(SPLIT_TRAIN_COUNT, SPLIT_TRAIN_SEED),
                          rounds=args.rounds, batches=args.batches, batch_ms=args.batch_ms,
                          log=lambda *a: print(*a, flush=True))
     data = {"device": device, "rounds": args.rounds, "batches": args.batches,
