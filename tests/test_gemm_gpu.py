@@ -367,6 +367,39 @@ def test_splitk_tail_parity(shape, splits):
     assert torch.equal(C, C2), "tail split is not deterministic"
 
 
+def _split_cases(n=16, seed=4242):
+    """Seeded split-K products.  Half are small (M, N log-uniform in 64..1600, K in
+    64..1200) with full, tail and modelled counts; half are large enough for a full round
+    of tiles plus a tail (M, N in 1000..2200, K in 64..600) with tail and modelled counts."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        if i % 2 == 0:
+            lo, hi, khi, counts = 64.0, 1600.0, 1200.0, [-8, -4, -2, 2, 3, 4, 8, 0]
+        else:
+            lo, hi, khi, counts = 1000.0, 2200.0, 600.0, [-8, -4, -3, -2, 0]
+        M, N = (int(np.exp(rng.uniform(np.log(lo), np.log(hi)))) for _ in range(2))
+        K = int(np.exp(rng.uniform(np.log(64.0), np.log(khi))))
+        cases.append((i, M, N, K, counts[int(rng.integers(len(counts)))]))
+    return cases
+
+
+@pytest.mark.parametrize("case", _split_cases(), ids=lambda c: f"s{c[0]}")
+def test_splitk_random_shapes(case):
+    """Every split mode on seeded ragged shapes, C and the workspace NaN-filled."""
+    i, M, N, K, splits = case
+    _say(f"[splitk-random] {M}x{N}x{K} splits={splits}")
+    A, B = ti.workload_inputs(M, N, K, 8200 + i)
+    C64, Bnd = oracle.gemm_f64(A, B)
+    need = tdb.gemm_f32_splitk_workspace(M, N, K, splits)
+    ws = torch.full((max(need, 1),), float("nan"), device=DEV)
+    C = torch.full((M, N), float("nan"), device=DEV)
+    tdb.matmul_splitk(_dev(A), _dev(B), splits, out=C, workspace=ws)
+    torch.cuda.synchronize()
+    r = _ratio(C, C64, Bnd)
+    assert r <= 1.0, (M, N, K, splits, r)
+
+
 def test_splitk_one_split_equals_plain_and_errors():
     A, B, C64, Bnd = _workload("square_128")
     Ad, Bd = _dev(A), _dev(B)
