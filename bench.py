@@ -62,10 +62,10 @@ METRIC = "FP32 GEMM TFLOP/s and % of MFMA FP32 peak at 1024³/4096³/8192³, 1 G
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_8192.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_double_buffered_amd", "csrc", f)
                   for f in ("gemm_f32.hip", "gemm_common.h", "kernels_sb_db.h",
-                            "kernels_ms.h", "splitk_reduce.h", "dispatch_table.h",
-                            "mfma_peak.h")]
+                            "kernels_ms.h", "kernels_ks.h", "splitk_reduce.h",
+                            "dispatch_table.h", "mfma_peak.h")]
 HEADLINE = "square_8192"
-VARIANT_NAMES = {1: "sb", 2: "db", 3: "ms"}
+VARIANT_NAMES = {1: "sb", 2: "db", 3: "ms", 5: "ks"}
 
 
 def kernel_source_hash() -> str:

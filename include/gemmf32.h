@@ -65,7 +65,7 @@ enum {
                                   K step: the multi-stage asynchronous-copy pipeline the
                                   glossary page names as the CUDA analogue ("Double
                                   Buffering", second paragraph)                         */
-    GEMMF32_VARIANT_SB3 = 4    /* measurement baseline: single-buffered with the A and B
+    GEMMF32_VARIANT_SB3 = 4,   /* measurement baseline: single-buffered with the A and B
                                   copies published by separate barriers, copy A ->
                                   barrier -> copy B -> barrier -> compute -> barrier,
                                   three barriers per K step (the pre-coalescing fence
@@ -73,16 +73,22 @@ enum {
                                   M1 Max", section "Transformation and safety boundary");
                                   only through gemm_f32_ex, never dispatched; its tile
                                   configuration defaults to the single-buffered column  */
+    GEMMF32_VARIANT_KS = 5     /* K split inside a workgroup: four one-wave groups each
+                                  run the double-buffered loop over a quarter of the K
+                                  tiles and add their sums through LDS in a fixed order;
+                                  for few rows against a long K (the skinny regime of
+                                  "Case Study", paragraph on the three regimes).  Only
+                                  configurations that have it (gemm_f32_config_variants) */
 };
 
 /* C = A.B with the variant and tile configuration chosen per shape: the measured pick
  * for a shape in the dispatch table, otherwise the pick of the table's cost model, which
  * weighs each pair's fixed cost against its time per K tile and round of workgroups over
- * the 256 compute units (GEMMF32_VARIANT environment variable "sb", "db" or "ms" forces the variant, for
- * measurement; GEMMF32_RASTER=<group_m>[,noxcd] changes the order in which workgroups walk
- * the output tiles, for every launching entry point, also for measurement only).  The
- * pages' lesson that the faster variant depends on the shape is the reason for the table
- * ("Double Buffering", last two paragraphs). */
+ * the 256 compute units.  The GEMMF32_VARIANT environment variable ("sb", "db", "ms" or
+ * "ks") forces the variant, for measurement; GEMMF32_RASTER=<group_m>[,noxcd] changes the
+ * order in which workgroups walk the output tiles, for every launching entry point, also
+ * for measurement only.  The pages' lesson that the faster variant depends on the shape is
+ * the reason for the table ("Double Buffering", last two paragraphs). */
 int gemm_f32(int64_t M, int64_t N, int64_t K,
              const float *A, int64_t lda,
              const float *B, int64_t ldb,
@@ -117,10 +123,12 @@ int gemm_f32_ms(int64_t M, int64_t N, int64_t K,
                 float *C, int64_t ldc,
                 void *stream);
 
-/* C = A.B with an explicit variant (GEMMF32_VARIANT_SB, _DB, _MS or _SB3; _AUTO = dispatch
- * table) and tile configuration id (0 .. gemm_f32_num_configs()-1; -1 = dispatch table).
- * For measurement and tests: every (variant, configuration) pair computes the same
- * product. */
+/* C = A.B with an explicit variant (GEMMF32_VARIANT_SB, _DB, _MS, _SB3 or _KS; _AUTO =
+ * dispatch table) and tile configuration id (0 .. gemm_f32_num_configs()-1; -1 = dispatch
+ * table).  For measurement and tests: every (variant, configuration) pair computes the
+ * same product.  A configuration without a kernel for the variant
+ * (gemm_f32_config_variants) gives GEMMF32_ERR_BAD_CONFIG; with _AUTO and a forced
+ * configuration that lacks the picked variant, the double-buffered kernel runs. */
 int gemm_f32_ex(int64_t M, int64_t N, int64_t K,
                 const float *A, int64_t lda,
                 const float *B, int64_t ldb,
@@ -188,9 +196,18 @@ int gemm_f32_config_info(int cfg_id, int *BM, int *BN, int *BK, int *threads,
                          int *lds_bytes_sb, int *lds_bytes_db);
 
 /* Multi-stage figures of tile configuration cfg_id: number of LDS stages and LDS bytes per
- * workgroup of the multi-stage kernel.  Output pointers may be NULL.  Returns 0 or
- * GEMMF32_ERR_BAD_CONFIG. */
+ * workgroup of the multi-stage kernel (0 and 0 for a configuration without one).  Output
+ * pointers may be NULL.  Returns 0 or GEMMF32_ERR_BAD_CONFIG. */
 int gemm_f32_config_ms(int cfg_id, int *stages, int *lds_bytes);
+
+/* Variants tile configuration cfg_id has a kernel for: bit v set for GEMMF32_VARIANT_v
+ * (the multi-stage kernel needs B tiles at least 64 wide; the K-split kernel exists for
+ * one-wave configurations).  Returns the mask or GEMMF32_ERR_BAD_CONFIG. */
+int gemm_f32_config_variants(int cfg_id);
+
+/* Wave groups of the K-split kernel of tile configuration cfg_id (1: it has none), or
+ * GEMMF32_ERR_BAD_CONFIG. */
+int gemm_f32_config_ks(int cfg_id);
 
 /* The HIP error code of this thread's last failed launch (0 if none). */
 int gemm_f32_last_hip_error(void);

@@ -27,8 +27,9 @@ VARIANT_SB = 1
 VARIANT_DB = 2
 VARIANT_MS = 3
 VARIANT_SB3 = 4
+VARIANT_KS = 5
 _VARIANTS = {"auto": VARIANT_AUTO, "sb": VARIANT_SB, "db": VARIANT_DB, "ms": VARIANT_MS,
-             "sb3": VARIANT_SB3}
+             "sb3": VARIANT_SB3, "ks": VARIANT_KS}
 
 # Every exported symbol and its C signature (kept in step with include/gemmf32.h).
 _i64, _int, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
@@ -47,6 +48,8 @@ SIGNATURES = {
     "gemm_f32_num_configs": (_int, []),
     "gemm_f32_config_info": (_int, [_int] + [ctypes.POINTER(_int)] * 6),
     "gemm_f32_config_ms": (_int, [_int, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
+    "gemm_f32_config_variants": (_int, [_int]),
+    "gemm_f32_config_ks": (_int, [_int]),
     "gemm_f32_last_hip_error": (_int, []),
     "gemm_f32_strerror": (ctypes.c_char_p, [_int]),
     "gemm_f32_version": (ctypes.c_char_p, []),
@@ -138,6 +141,16 @@ def gemm_f32_config_info(cfg_id):
     rc = load().gemm_f32_config_info(cfg_id, *[ctypes.byref(v) for v in vals])
     keys = ("BM", "BN", "BK", "threads", "lds_bytes_sb", "lds_bytes_db")
     return rc, dict(zip(keys, (v.value for v in vals)))
+
+
+def gemm_f32_config_variants(cfg_id) -> int:
+    """Bit mask of the variants configuration cfg_id has a kernel for (bit v: variant v)."""
+    return load().gemm_f32_config_variants(cfg_id)
+
+
+def gemm_f32_config_ks(cfg_id) -> int:
+    """Wave groups of configuration cfg_id's K-split kernel (1: it has none)."""
+    return load().gemm_f32_config_ks(cfg_id)
 
 
 def gemm_f32_config_ms(cfg_id):

@@ -18,8 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 SOURCES = [os.path.join(CSRC, "gemm_f32.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("gemm_common.h", "kernels_sb_db.h", "kernels_ms.h",
-                                            "splitk_reduce.h", "dispatch_table.h",
-                                            "mfma_peak.h")]
+                                            "kernels_ks.h", "splitk_reduce.h",
+                                            "dispatch_table.h", "mfma_peak.h")]
 DEPS = SOURCES + HEADERS + [os.path.join(INCLUDE, "gemmf32.h")]
 LIB = os.path.join(PKG, "libgemmf32.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
@@ -67,7 +67,8 @@ def device_asm() -> str:
 def kernel_functions(asm: str) -> dict:
     """Map mangled kernel name -> its assembly body (from the label to .Lfunc_end)."""
     out = {}
-    for m in re.finditer(r"^(_Z\S*gemm_f32_(?:tile|ms)_kernel\S*):[ \t]*(?:;.*)?$", asm, re.M):
+    for m in re.finditer(r"^(_Z\S*gemm_f32_(?:tile|ms|ks)_kernel\S*):[ \t]*(?:;.*)?$", asm,
+                         re.M):
         name = m.group(1)
         end = asm.find(f".Lfunc_end", m.end())
         out[name] = asm[m.end():end]
@@ -116,6 +117,7 @@ def resources_table(asm: str) -> str:
     for name, body in sorted(kernel_functions(asm).items()):
         m = re.search(r"TileCfgILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEELi(\d+)E", name)
         kind = "ms%s" % m.group(6) if "_ms_kernel" in name else \
+            "ks%s" % m.group(6) if "_ks_kernel" in name else \
             {"1": "sb", "2": "db", "4": "sb3"}[m.group(6)]
         tile = "%sx%sx%s/%sx%s" % m.groups()[:5]
         d = meta[name]

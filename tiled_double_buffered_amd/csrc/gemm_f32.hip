@@ -31,6 +31,7 @@
 
 #include "gemmf32.h"
 #include "gemm_common.h"
+#include "kernels_ks.h"
 #include "kernels_ms.h"
 #include "kernels_sb_db.h"
 #include "mfma_peak.h"
@@ -54,20 +55,39 @@ using Cfg9 = TileCfg<128, 256, 32, 2, 4>;  // 8 waves of 64x64
 using Cfg10 = TileCfg<32, 128, 32, 1, 4>;  // 4 waves of 32x32 side by side: skinny M
 using Cfg11 = TileCfg<192, 192, 16, 2, 2>;  // wave 96x96: 16x16 tiles for 3072-wide C
 using Cfg12 = TileCfg<192, 192, 32, 2, 2>;  // wave 96x96, deeper K tile
+using Cfg13 = TileCfg<32, 32, 32, 1, 1>;    // one wave: few rows, long K (K-split kernel)
 
 typedef void (*KernelFn)(int, int, int, const float*, int64_t, const float*, int64_t, float*,
                          int64_t, int, SplitArgs);
 
+// ms: the multi-stage kernel, where the configuration has one (its swizzle needs tiles
+// of B at least 64 wide; stages 0 otherwise); ks: the K-split kernel and its wave groups,
+// where it has one (groups 1 otherwise).
 struct CfgEntry {
   int bm, bn, bk, nt;
   int lds_sb, lds_db;
   int ms_stages, lds_ms;
   KernelFn sb, db, ms, sb3;
+  KernelFn ks;
+  int ks_groups;
 };
 
 template <class C>
+constexpr bool has_ms() {
+  return C::BN % 64 == 0;
+}
+
+template <class C>
 constexpr CfgEntry make_entry() {
-  constexpr int S = ms_stages<C>();
+  constexpr int S = has_ms<C>() ? ms_stages<C>() : 0;
+  constexpr int KS = ks_groups<C>();
+  KernelFn ms = nullptr, ks = nullptr;
+  int lds_ms = 0;
+  if constexpr (has_ms<C>()) {
+    ms = &gemm_f32_ms_kernel<C, S>;
+    lds_ms = (int)(MsCfg<C, S>::LDS_FLOATS * sizeof(float));
+  }
+  if constexpr (KS > 1) ks = &gemm_f32_ks_kernel<C, KS>;
   return CfgEntry{C::BM,
                   C::BN,
                   C::BK,
@@ -75,18 +95,20 @@ constexpr CfgEntry make_entry() {
                   (int)(C::SLOT * sizeof(float)),
                   (int)(2 * C::SLOT * sizeof(float)),
                   S,
-                  (int)(MsCfg<C, S>::LDS_FLOATS * sizeof(float)),
+                  lds_ms,
                   &gemm_f32_tile_kernel<C, kLoopSB>,
                   &gemm_f32_tile_kernel<C, kLoopDB>,
-                  &gemm_f32_ms_kernel<C, S>,
-                  &gemm_f32_tile_kernel<C, kLoopSB3>};
+                  ms,
+                  &gemm_f32_tile_kernel<C, kLoopSB3>,
+                  ks,
+                  KS};
 }
 
 static const CfgEntry kConfigs[] = {
     make_entry<Cfg0>(), make_entry<Cfg1>(), make_entry<Cfg2>(), make_entry<Cfg3>(),
     make_entry<Cfg4>(), make_entry<Cfg5>(), make_entry<Cfg6>(), make_entry<Cfg7>(),
     make_entry<Cfg8>(), make_entry<Cfg9>(), make_entry<Cfg10>(), make_entry<Cfg11>(),
-    make_entry<Cfg12>(),
+    make_entry<Cfg12>(), make_entry<Cfg13>(),
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -182,27 +204,47 @@ static int launch(int variant, int cfg_id, int64_t M, int64_t N, int64_t K, cons
                   int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
                   void* stream, const SplitPlan* plan = nullptr) {
   const CfgEntry& e = kConfigs[cfg_id];
+  KernelFn fn = variant == GEMMF32_VARIANT_SB    ? e.sb
+                : variant == GEMMF32_VARIANT_MS  ? e.ms
+                : variant == GEMMF32_VARIANT_SB3 ? e.sb3
+                : variant == GEMMF32_VARIANT_KS  ? e.ks
+                                                 : e.db;
+  // a configuration without this variant's kernel; the K-split kernel divides K itself
+  if (fn == nullptr || (variant == GEMMF32_VARIANT_KS && plan != nullptr))
+    return GEMMF32_ERR_BAD_CONFIG;
+  const int threads = variant == GEMMF32_VARIANT_KS ? e.nt * e.ks_groups : e.nt;
   const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
   const int64_t from = plan ? std::min(plan->split_from, tiles) : tiles;
   const int64_t chunks = plan ? plan->chunks : 1;
   const int64_t wgs = from + (tiles - from) * chunks;
-  if (wgs * e.nt > 0xFFFFFFFFLL) return GEMMF32_ERR_TOO_LARGE;
+  if (wgs * threads > 0xFFFFFFFFLL) return GEMMF32_ERR_TOO_LARGE;
   int flags = launch_flags(e, K, lda, ldb);
   int m = (int)M, n = (int)N, k = (int)K;
   SplitArgs sp{plan ? plan->ws : nullptr, plan ? plan->plane : 0,
                plan ? (int)plan->k_chunk : k, (int)chunks, (int)from, (int)tiles};
   void* args[] = {&m, &n, &k, (void*)&A, &lda, (void*)&B, &ldb, &C, &ldc, &flags, &sp};
-  KernelFn fn = variant == GEMMF32_VARIANT_SB    ? e.sb
-                : variant == GEMMF32_VARIANT_MS  ? e.ms
-                : variant == GEMMF32_VARIANT_SB3 ? e.sb3
-                                                 : e.db;
-  hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)wgs), dim3(e.nt), args, 0,
-                                   (hipStream_t)stream);
+  hipError_t err = hipLaunchKernel((const void*)fn, dim3((unsigned)wgs), dim3(threads), args,
+                                   0, (hipStream_t)stream);
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
     return GEMMF32_ERR_HIP;
   }
   return GEMMF32_OK;
+}
+
+static bool has_variant(int cfg_id, int variant) {
+  const CfgEntry& e = kConfigs[cfg_id];
+  return variant == GEMMF32_VARIANT_MS ? e.ms != nullptr
+         : variant == GEMMF32_VARIANT_KS ? e.ks != nullptr
+                                         : true;
+}
+
+// The first configuration with a kernel for `variant` (the measured tables name one for
+// every variant they timed; this covers a table without the variant).
+static int first_cfg_with(int variant) {
+  for (int c = 0; c < kNumConfigs; ++c)
+    if (has_variant(c, variant)) return c;
+  return 0;
 }
 
 static int env_variant() {
@@ -211,6 +253,7 @@ static int env_variant() {
   if (std::strcmp(v, "sb") == 0) return GEMMF32_VARIANT_SB;
   if (std::strcmp(v, "db") == 0) return GEMMF32_VARIANT_DB;
   if (std::strcmp(v, "ms") == 0) return GEMMF32_VARIANT_MS;
+  if (std::strcmp(v, "ks") == 0) return GEMMF32_VARIANT_KS;
   return GEMMF32_VARIANT_AUTO;
 }
 
@@ -218,9 +261,12 @@ static int run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, con
                int64_t ldb, float* C, int64_t ldc, int variant, int cfg_id, void* stream) {
   if (variant != GEMMF32_VARIANT_AUTO && variant != GEMMF32_VARIANT_SB &&
       variant != GEMMF32_VARIANT_DB && variant != GEMMF32_VARIANT_MS &&
-      variant != GEMMF32_VARIANT_SB3)
+      variant != GEMMF32_VARIANT_SB3 && variant != GEMMF32_VARIANT_KS)
     return GEMMF32_ERR_BAD_CONFIG;
   if (cfg_id < -1 || cfg_id >= kNumConfigs) return GEMMF32_ERR_BAD_CONFIG;
+  if (cfg_id >= 0 && ((variant == GEMMF32_VARIANT_MS && kConfigs[cfg_id].ms == nullptr) ||
+                      (variant == GEMMF32_VARIANT_KS && kConfigs[cfg_id].ks == nullptr)))
+    return GEMMF32_ERR_BAD_CONFIG;
   int rc = validate(M, N, K, A, lda, B, ldb, C, ldc);
   if (rc != GEMMF32_OK) return rc;
   if (M == 0 || N == 0) return GEMMF32_OK;
@@ -228,10 +274,16 @@ static int run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, con
     int v = 0, c = 0;
     select_shape(M, N, K, &v, &c);
     variant = v;
-    if (cfg_id < 0) cfg_id = c;
+    if (cfg_id < 0) {
+      cfg_id = c;
+    } else if ((variant == GEMMF32_VARIANT_MS && kConfigs[cfg_id].ms == nullptr) ||
+               (variant == GEMMF32_VARIANT_KS && kConfigs[cfg_id].ks == nullptr)) {
+      variant = GEMMF32_VARIANT_DB;  // a forced configuration without the picked variant
+    }
   } else if (cfg_id < 0) {
     cfg_id = select_for_variant(M, N, K, variant == GEMMF32_VARIANT_SB3 ? GEMMF32_VARIANT_SB
                                                                         : variant);
+    if (!has_variant(cfg_id, variant)) cfg_id = first_cfg_with(variant);
   }
   return launch(variant, cfg_id, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
@@ -391,9 +443,10 @@ int gemm_f32_select(int64_t M, int64_t N, int64_t K, int* variant, int* cfg_id) 
 int gemm_f32_select_cfg(int64_t M, int64_t N, int64_t K, int variant) {
   if (M < 0 || N < 0 || K < 0) return GEMMF32_ERR_NEGATIVE_DIM;
   if (variant != GEMMF32_VARIANT_SB && variant != GEMMF32_VARIANT_DB &&
-      variant != GEMMF32_VARIANT_MS)
+      variant != GEMMF32_VARIANT_MS && variant != GEMMF32_VARIANT_KS)
     return GEMMF32_ERR_BAD_CONFIG;
-  return select_for_variant(M, N, K, variant);
+  const int c = select_for_variant(M, N, K, variant);
+  return has_variant(c, variant) ? c : first_cfg_with(variant);
 }
 
 int gemm_f32_num_configs(void) { return kNumConfigs; }
@@ -417,6 +470,20 @@ int gemm_f32_config_ms(int cfg_id, int* stages, int* lds_bytes) {
   if (stages) *stages = e.ms_stages;
   if (lds_bytes) *lds_bytes = e.lds_ms;
   return GEMMF32_OK;
+}
+
+int gemm_f32_config_variants(int cfg_id) {
+  if (cfg_id < 0 || cfg_id >= kNumConfigs) return GEMMF32_ERR_BAD_CONFIG;
+  const CfgEntry& e = kConfigs[cfg_id];
+  int mask = (1 << GEMMF32_VARIANT_SB) | (1 << GEMMF32_VARIANT_DB) | (1 << GEMMF32_VARIANT_SB3);
+  if (e.ms != nullptr) mask |= 1 << GEMMF32_VARIANT_MS;
+  if (e.ks != nullptr) mask |= 1 << GEMMF32_VARIANT_KS;
+  return mask;
+}
+
+int gemm_f32_config_ks(int cfg_id) {
+  if (cfg_id < 0 || cfg_id >= kNumConfigs) return GEMMF32_ERR_BAD_CONFIG;
+  return kConfigs[cfg_id].ks_groups;
 }
 
 int gemm_f32_last_hip_error(void) { return g_last_hip_error; }

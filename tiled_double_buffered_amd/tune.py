@@ -30,8 +30,19 @@ import time
 from . import _binding as tdb
 from .build import CSRC
 
-VARIANTS = (tdb.VARIANT_SB, tdb.VARIANT_DB, tdb.VARIANT_MS)
-NAMES = {tdb.VARIANT_SB: "sb", tdb.VARIANT_DB: "db", tdb.VARIANT_MS: "ms"}
+VARIANTS = (tdb.VARIANT_SB, tdb.VARIANT_DB, tdb.VARIANT_MS, tdb.VARIANT_KS)
+NAMES = {tdb.VARIANT_SB: "sb", tdb.VARIANT_DB: "db", tdb.VARIANT_MS: "ms",
+         tdb.VARIANT_KS: "ks"}
+IDS = {v: k for k, v in NAMES.items()}
+
+
+def available_pairs():
+    """(variant, cfg) pairs that have a kernel, in configuration order."""
+    out = []
+    for c in range(tdb.gemm_f32_num_configs()):
+        mask = tdb.gemm_f32_config_variants(c)
+        out += [(v, c) for v in VARIANTS if mask & (1 << v)]
+    return out
 
 SHAPES = [
     # the workloads
@@ -72,8 +83,9 @@ HEADER_TEMPLATE = """// Per-shape dispatch table: (M, N, K) -> variant and tile 
 // other shape takes the pick of the cost model further down, fitted to the same runs.
 //
 // Columns: M, N, K, best variant (1 = single-buffered, 2 = double-buffered, 3 = multi-stage
-// direct-to-LDS), its tile configuration, and the best configuration of each variant.
-// Trailing comments: measured microseconds of the best run of each variant.
+// direct-to-LDS, 5 = K split inside the workgroup), its tile configuration, and the best
+// configuration of the single-buffered, double-buffered and multi-stage variants.
+// Trailing comments: measured microseconds of the best configuration of each variant.
 #pragma once
 
 #include <cmath>
@@ -103,20 +115,22 @@ static inline const DispatchRow* dispatch_exact(int64_t M, int64_t N, int64_t K)
 // are the two the regimes turn on: how many tiles the busiest compute unit multiplies,
 // rounds = ceil(workgroups / 256), and the K tiles per tile, k_tiles = ceil(K / BK).  A
 // launch is modelled as
-//     a + g * rounds * k_tiles   microseconds,
-// a being the fixed cost (launch, first copy, epilogue) and g the time of one K tile of one
-// round.  a and g were fitted per pair by least squares on relative error, both kept
-// >= 0, to the {nfit} shapes measured for this file (the table's {ntable} and {ntrain} seeded
-// shapes outside it).
+//     a + b * rounds + g * rounds * k_tiles   microseconds,
+// a being the fixed cost (launch, first copy, epilogue), g the time of one K tile of one
+// round, and b a cost per round that only the K-split kernel has (each of its rounds ends
+// in a hand-off through LDS; b = 0 elsewhere).  They were fitted per pair by least squares
+// on relative error, all kept >= 0, to the {nfit} shapes measured for this file (the
+// table's {ntable} and {ntrain} seeded shapes outside it).
 struct ModelRow {{
   int variant, cfg;
-  double a_us, g_us;
+  double a_us, b_us, g_us;
 }};
 
 static const ModelRow kModel[] = {{
 {model_rows}
 }};
 constexpr int kModelRows = (int)(sizeof(kModel) / sizeof(kModel[0]));
+constexpr int kVariantKS = 5;
 constexpr int64_t kModelCUs = 256;
 
 // Modelled microseconds of one launch; wg_factor multiplies the workgroup count (the K
@@ -127,7 +141,7 @@ static inline double model_us(const ModelRow& r, int64_t M, int64_t N, int64_t K
   const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn) * wg_factor;
   const int64_t rounds = (tiles + kModelCUs - 1) / kModelCUs;
   const int64_t k_tiles = (K + e.bk - 1) / e.bk;
-  return r.a_us + r.g_us * (double)rounds * (double)k_tiles;
+  return r.a_us + r.b_us * (double)rounds + r.g_us * (double)rounds * (double)k_tiles;
 }}
 
 // The row with the least modelled time (variant 0: any variant), first row on ties.
@@ -138,6 +152,11 @@ static inline const ModelRow& model_pick(int64_t M, int64_t N, int64_t K, int va
   bool found = false;
   for (int i = 0; i < kModelRows; ++i) {{
     if (variant != 0 && kModel[i].variant != variant) continue;
+    // a split-K launch takes neither the K-split kernel (it divides K itself) nor a
+    // one-wave configuration (its plain kernels keep one SIMD of a CU busy)
+    if (wg_factor != 1 &&
+        (kModel[i].variant == kVariantKS || kConfigs[kModel[i].cfg].nt == 64))
+      continue;
     const double t = model_us(kModel[i], M, N, K, wg_factor);
     if (!found || t < best_t) {{
       best = i;
@@ -160,8 +179,8 @@ static inline void select_shape(int64_t M, int64_t N, int64_t K, int* variant, i
 }}
 
 static inline int select_for_variant(int64_t M, int64_t N, int64_t K, int variant) {{
-  if (const DispatchRow* r = dispatch_exact(M, N, K))
-    return variant == 1 ? r->sb_cfg : variant == 3 ? r->ms_cfg : r->db_cfg;
+  const DispatchRow* r = variant != kVariantKS ? dispatch_exact(M, N, K) : nullptr;
+  if (r) return variant == 1 ? r->sb_cfg : variant == 3 ? r->ms_cfg : r->db_cfg;
   return model_pick(M, N, K, variant, 1).cfg;
 }}
 
@@ -223,12 +242,13 @@ static inline TailPick tail_pick(int64_t M, int64_t N, int64_t K, int used, int6
   for (int i = 0; i < kModelRows; ++i) {{
     const ModelRow& r = kModel[i];
     const CfgEntry& e = kConfigs[r.cfg];
+    if (r.variant == kVariantKS || e.nt == 64) continue;  // as in a full split
     const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
     const int64_t full = tiles / kModelCUs * kModelCUs, tail = tiles - full;
     if (full == 0 || tail == 0) continue;
     const double tail_rounds = (double)((tail * used + kModelCUs - 1) / kModelCUs);
     const double mb = (double)(2 * used + 1) * (double)tail * e.bm * e.bn * 4.0 / 1e6;
-    const double t = r.a_us +
+    const double t = r.a_us + r.b_us * ((double)(full / kModelCUs) + tail_rounds) +
                      r.g_us * ((double)(full / kModelCUs) * (double)((K + e.bk - 1) / e.bk) +
                                tail_rounds * (double)((kc + e.bk - 1) / e.bk)) +
                      kSplitFixedUs + kSplitUsPerMB * mb + kSplitUsPerRound * tail_rounds;
@@ -275,8 +295,7 @@ def measure(shapes, rounds=2, batches=5, batch_ms=20.0, log=print):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     s_ptr = stream.cuda_stream
-    ncfg = tdb.gemm_f32_num_configs()
-    pairs = [(v, c) for c in range(ncfg) for v in VARIANTS]
+    pairs = available_pairs()
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
     results = []
@@ -435,6 +454,17 @@ def barrier_study(shapes=BARRIER_SHAPES, rounds=2, batches=5, batch_ms=20.0, log
     return out
 
 
+def _has_tail(M, N, cus=256):
+    """Some configuration a split launch may take (not a one-wave one) cuts M x N into at
+    least one full round of tiles plus a partly filled one."""
+    for c, (bm, bn, _bk, _lds) in config_dims().items():
+        if not _one_wave(c):
+            tiles = -(-M // bm) * -(-N // bn)
+            if tiles >= cus and tiles % cus:
+                return True
+    return False
+
+
 def split_study(shapes=SPLIT_SHAPES, choices=SPLIT_CHOICES, rounds=2, batches=5,
                 batch_ms=20.0, log=print):
     """Time gemm_f32_splitk for each split count (1 = the plain dispatched product; -s = the
@@ -445,11 +475,12 @@ def split_study(shapes=SPLIT_SHAPES, choices=SPLIT_CHOICES, rounds=2, batches=5,
     for (M, N, K) in shapes:
         A, B, C = _operands(M, N, K)
         s_ptr = torch.cuda.current_stream().cuda_stream
-        # a tail split (-s) is timed where the product has a tail, i.e. where it is not
-        # the full split of the same count (the two ask for different workspaces)
+        # a tail split (-s) is timed where some configuration's tiles make a full round
+        # of workgroups and a partly filled one (whichever the model then prefers)
         wsz = tdb.gemm_f32_splitk_workspace
-        counts = list(choices) + [-sp for sp in choices
-                                  if sp > 1 and wsz(M, N, K, -sp) != wsz(M, N, K, sp)]
+        counts = list(choices)
+        if _has_tail(M, N):
+            counts += [-sp for sp in choices if sp > 1]
         need = max(wsz(M, N, K, sp) for sp in counts)
         ws = torch.empty(max(need, 1), device=A.device)
 
@@ -584,27 +615,53 @@ def _fit_pair(xs, ys):
     return min(cands, key=obj)
 
 
+def model_rounds(M, N, cfg_dims, wg_factor=1, cus=256):
+    bm, bn = cfg_dims[0], cfg_dims[1]
+    return -(-(-(-M // bm) * -(-N // bn) * wg_factor) // cus)
+
+
 def fit_model(rows, cfg_dims):
-    """Per (variant, configuration): (variant id, cfg, a_us, g_us, median |relative error|)
-    of the cost model a + g * rounds * k_tiles over the measured rows."""
+    """Per (variant, configuration): (variant id, cfg, a_us, b_us, g_us, median |relative
+    error|) of the cost model a + b * rounds + g * rounds * k_tiles over the measured rows.
+    b is fitted for the K-split kernel only, whose every round of workgroups ends in a
+    hand-off through LDS and a store; it is 0 for the others."""
+    import numpy as np
+    from scipy.optimize import nnls
+
     out = []
-    ids = {"sb": tdb.VARIANT_SB, "db": tdb.VARIANT_DB, "ms": tdb.VARIANT_MS}
+    ids = IDS
     keys = sorted(rows[0]["us"], key=lambda k: (ids[k[:2]], int(k[2:])))
     for key in keys:
         cfg = int(key[2:])
-        xs = [model_features(r["M"], r["N"], r["K"], cfg_dims[cfg][:3]) for r in rows]
-        ys = [r["us"][key] for r in rows]
-        a, g = _fit_pair(xs, ys)
-        err = statistics.median(abs((a + g * x) / y - 1.0) for x, y in zip(xs, ys))
-        out.append((ids[key[:2]], cfg, a, g, err))
+        have = [r for r in rows if key in r["us"]]
+        xs = [model_features(r["M"], r["N"], r["K"], cfg_dims[cfg][:3]) for r in have]
+        rs = [model_rounds(r["M"], r["N"], cfg_dims[cfg][:3]) for r in have]
+        ys = [r["us"][key] for r in have]
+        if ids[key[:2]] == tdb.VARIANT_KS:
+            X = np.array([[1.0 / y, rr / y, x / y] for x, rr, y in zip(xs, rs, ys)])
+            (a, b, g), _ = nnls(X, np.ones(len(ys)))
+            a, b, g = float(a), float(b), float(g)
+        else:
+            (a, g), b = _fit_pair(xs, ys), 0.0
+        err = statistics.median(abs((a + b * rr + g * x) / y - 1.0)
+                                for x, rr, y in zip(xs, rs, ys))
+        out.append((ids[key[:2]], cfg, a, b, g, err))
     return out
 
 
+def _one_wave(cfg):
+    return tdb.gemm_f32_config_info(cfg)[1]["threads"] == 64
+
+
 def _model_pick_py(M, N, K, model, dims, wg_factor=1):
-    """Least modelled (us, variant, cfg) over the fitted rows, as the header computes it."""
+    """Least modelled (us, variant, cfg) over the fitted rows, as the header computes it
+    (a split launch never takes the K-split kernel)."""
     best = None
-    for (v, c, a, g, _e) in model:
-        t = a + g * model_features(M, N, K, dims[c][:3], wg_factor)
+    for (v, c, a, b, g, _e) in model:
+        if wg_factor != 1 and (v == tdb.VARIANT_KS or _one_wave(c)):
+            continue
+        t = (a + b * model_rounds(M, N, dims[c][:3], wg_factor)
+             + g * model_features(M, N, K, dims[c][:3], wg_factor))
         if best is None or t < best[0]:
             best = (t, v, c)
     return best
@@ -633,7 +690,9 @@ def split_features(M, N, K, splits, model, dims):
         rounds = -(-(-(-M // bm) * -(-N // bn) * used) // 256)
         return used, t, [1.0, split_extra_mb(M, N, used), float(rounds)]
     best = None
-    for (v, c, a, g, _e) in model:
+    for (v, c, a, b, g, _e) in model:
+        if v == tdb.VARIANT_KS or _one_wave(c):
+            continue
         bm, bn, bk = dims[c][:3]
         tiles = -(-M // bm) * -(-N // bn)
         full = tiles // 256 * 256
@@ -641,7 +700,7 @@ def split_features(M, N, K, splits, model, dims):
         if full == 0 or rest == 0:
             continue
         tr = -(-(rest * used) // 256)
-        t = a + g * (full // 256 * -(-K // bk) + tr * -(-kc // bk))
+        t = a + b * (full // 256 + tr) + g * (full // 256 * -(-K // bk) + tr * -(-kc // bk))
         if best is None or t < best[0]:
             best = (t, [1.0, (2 * used + 1) * rest * bm * bn * 4 / 1e6, float(tr)])
     return (used, best[0], best[1]) if best else None
@@ -762,16 +821,17 @@ def table_rows(results, dims=None):
     rows = []
     for r in results:
         best = {}
-        for name in ("sb", "db", "ms"):
+        for name in ("sb", "db", "ms", "ks"):
             cands = [(k, v) for k, v in r["us"].items() if k[:2] == name]
             if cands:
                 k, v = _pick(cands, dims)
                 best[name] = (int(k[2:]), v)
         win = _pick([(n + str(c), v) for n, (c, v) in best.items()], dims)[0][:2]
-        vid = {"sb": 1, "db": 2, "ms": 3}[win]
+        vid = IDS[win]
         ms = best.get("ms", best["db"])
+        ks = best.get("ks", (None, None))[1]
         rows.append((r["M"], r["N"], r["K"], vid, best[win][0], best["sb"][0], best["db"][0],
-                     ms[0], best["sb"][1], best["db"][1], ms[1]))
+                     ms[0], best["sb"][1], best["db"][1], ms[1], ks))
     return rows
 
 
@@ -788,17 +848,19 @@ def write_header(results, device, rounds, batches, batch_ms, path=None, split_re
                  train=None):
     path = path or os.path.join(CSRC, "dispatch_table.h")
     lines = []
-    for (m, n, k, v, c, s, d, ms, sb_us, db_us, ms_us) in table_rows(results):
+    for (m, n, k, v, c, s, d, ms, sb_us, db_us, ms_us, ks_us) in table_rows(results):
         lines.append(f"    {{{m}, {n}, {k}, {v}, {c}, {s}, {d}, {ms}}},  // sb {sb_us:.2f} us, "
-                     f"db {db_us:.2f} us, ms {ms_us:.2f} us")
+                     f"db {db_us:.2f} us, ms {ms_us:.2f} us"
+                     + (f", ks {ks_us:.2f} us" if ks_us is not None else ""))
     srows = split_rows(split_results) if split_results else ["    {1024, 1024, 1024, 1},"]
     fit_rows = list(results) + list(train or [])
     dims = config_dims()
     model = fit_model(fit_rows, dims)
     # round as written, so that the split fit sees the model the library will use
-    model = [(v, c, round(a, 4), round(g, 5), e) for (v, c, a, g, e) in model]
-    mrows = [f"    {{{v}, {c}, {a:.4f}, {g:.5f}}},  // median |error| {100 * e:.1f}%"
-             for (v, c, a, g, e) in model]
+    model = [(v, c, round(a, 4), round(b, 4), round(g, 5), e)
+             for (v, c, a, b, g, e) in model]
+    mrows = [f"    {{{v}, {c}, {a:.4f}, {b:.4f}, {g:.5f}}},  // median |error| {100 * e:.1f}%"
+             for (v, c, a, b, g, e) in model]
     r0, per_mb, per_round = (fit_split_model(split_results, model, dims) if split_results
                              else (3.0, 0.3, 1.0))
     choices = sorted({int(k) for r in (split_results or []) for k in r["us"] if int(k) > 0}) or [1]
