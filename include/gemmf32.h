@@ -174,8 +174,18 @@ int64_t gemm_f32_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits);
  * code only.  Negative sizes give GEMMF32_ERR_NEGATIVE_DIM. */
 int gemm_f32_splitk_select(int64_t M, int64_t N, int64_t K);
 
+/* The launches a gemm_f32_splitk call with this shape and split count (0 = the modelled
+ * choice) would make, without launching: *variant and *cfg_id receive the GEMM kernel and
+ * tile configuration, *chunks the number of K chunks of each split tile (1: no split, the
+ * call is the plain gemm_f32 product), *split_from the number of tiles, in launch order,
+ * that run whole over K (0 for a full split; all tiles when *chunks is 1).  Output
+ * pointers may be NULL.  Pure host code.  Returns 0, GEMMF32_ERR_NEGATIVE_DIM, or
+ * GEMMF32_ERR_BAD_CONFIG for a split count gemm_f32_splitk rejects. */
+int gemm_f32_splitk_plan(int64_t M, int64_t N, int64_t K, int splits, int *variant,
+                         int *cfg_id, int *chunks, int64_t *split_from);
+
 /* The dispatch decision for a shape, without launching: *variant receives
- * GEMMF32_VARIANT_SB, _DB or _MS and *cfg_id the tile configuration id.  Either output pointer
+ * GEMMF32_VARIANT_SB, _DB, _MS or _KS and *cfg_id the tile configuration id.  Either output pointer
  * may be NULL.  Pure host code (no GPU needed).  Returns GEMMF32_ERR_NEGATIVE_DIM for
  * negative sizes. */
 int gemm_f32_select(int64_t M, int64_t N, int64_t K, int *variant, int *cfg_id);

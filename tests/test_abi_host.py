@@ -297,6 +297,38 @@ def test_splitk_workspace_sizes():
     assert tdb.gemm_f32_splitk_select(-1, 2, 3) == tdb.ERR_NEGATIVE_DIM
 
 
+@pytest.mark.parametrize("shape", [(16, 4096, 4096), (300, 1000, 4096), (1536, 1536, 1536),
+                                   (4096, 4096, 4096), (7, 1000, 3001), (10, 20, 64),
+                                   (1000, 1300, 257)])
+def test_splitk_plan_agrees_with_the_workspace(shape):
+    """gemm_f32_splitk_plan describes the launch the workspace is sized for: M x N planes per
+    chunk for a full split, packed tile blocks for the split tiles of a tail split, nothing
+    and the plain dispatch when no split results.  A split launch takes neither the K-split
+    kernel nor a one-wave configuration."""
+    M, N, K = shape
+    for splits in (0, 2, 4, 8, 16, -2, -4, -8):
+        rc, p = tdb.gemm_f32_splitk_plan(M, N, K, splits)
+        assert rc == tdb.OK, (shape, splits)
+        _, info = tdb.gemm_f32_config_info(p["cfg"])
+        tiles = -(-M // info["BM"]) * -(-N // info["BN"])
+        need = tdb.gemm_f32_splitk_workspace(M, N, K, splits)
+        if p["chunks"] == 1:
+            assert need == 0 and p["split_from"] == tiles
+            assert (tdb.OK, p["variant"], p["cfg"]) == tdb.gemm_f32_select(M, N, K)
+            continue
+        assert tdb.gemm_f32_config_variants(p["cfg"]) & (1 << p["variant"])
+        assert info["threads"] > 64 and p["variant"] != tdb.VARIANT_KS
+        if p["split_from"] == 0:
+            assert need == p["chunks"] * M * N
+        else:
+            assert (splits or tdb.gemm_f32_splitk_select(M, N, K)) < 0
+            assert 0 < p["split_from"] < tiles
+            assert need == p["chunks"] * (tiles - p["split_from"]) * info["BM"] * info["BN"]
+    assert tdb.gemm_f32_splitk_plan(M, N, K, -1)[0] == tdb.ERR_BAD_CONFIG
+    assert tdb.gemm_f32_splitk_plan(M, N, K, 65)[0] == tdb.ERR_BAD_CONFIG
+    assert tdb.gemm_f32_splitk_plan(-1, N, K, 2)[0] == tdb.ERR_NEGATIVE_DIM
+
+
 def _header_text():
     return open(os.path.join(build.CSRC, "dispatch_table.h")).read()
 

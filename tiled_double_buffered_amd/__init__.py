@@ -12,8 +12,8 @@ from ._binding import (  # noqa: F401
     gemm_f32_config_ks, gemm_f32_config_ms, gemm_f32_config_variants, gemm_f32_db,
     gemm_f32_ex, gemm_f32_last_hip_error, gemm_f32_ms, gemm_f32_num_configs,
     gemm_f32_peak_probe, gemm_f32_sb, gemm_f32_select, gemm_f32_select_cfg, gemm_f32_splitk,
-    gemm_f32_splitk_select, gemm_f32_splitk_workspace, gemm_f32_strerror, gemm_f32_version,
-    load, matmul, matmul_splitk,
+    gemm_f32_splitk_plan, gemm_f32_splitk_select, gemm_f32_splitk_workspace,
+    gemm_f32_strerror, gemm_f32_version, load, matmul, matmul_splitk,
 )
 
 __version__ = "0.1.0"

@@ -43,6 +43,9 @@ SIGNATURES = {
     "gemm_f32_splitk": (_int, _GEMM_ARGS + [_int, _vp, _i64, _vp]),
     "gemm_f32_splitk_workspace": (_i64, [_i64, _i64, _i64, _int]),
     "gemm_f32_splitk_select": (_int, [_i64, _i64, _i64]),
+    "gemm_f32_splitk_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_int),
+                                    ctypes.POINTER(_int), ctypes.POINTER(_int),
+                                    ctypes.POINTER(_i64)]),
     "gemm_f32_select": (_int, [_i64, _i64, _i64, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
     "gemm_f32_select_cfg": (_int, [_i64, _i64, _i64, _int]),
     "gemm_f32_num_configs": (_int, []),
@@ -118,6 +121,16 @@ def gemm_f32_splitk_workspace(M, N, K, splits) -> int:
 
 def gemm_f32_splitk_select(M, N, K) -> int:
     return load().gemm_f32_splitk_select(M, N, K)
+
+
+def gemm_f32_splitk_plan(M, N, K, splits=0):
+    """Returns (rc, dict): the variant and cfg of a split-K call's GEMM launch, its K chunks
+    per split tile (1: no split) and the tiles that run whole over K (split_from)."""
+    v, c, ch, sf = _int(0), _int(0), _int(0), _i64(0)
+    rc = load().gemm_f32_splitk_plan(M, N, K, splits, ctypes.byref(v), ctypes.byref(c),
+                                     ctypes.byref(ch), ctypes.byref(sf))
+    return rc, {"variant": v.value, "cfg": c.value, "chunks": ch.value,
+                "split_from": sf.value}
 
 
 def gemm_f32_select(M, N, K):

@@ -431,6 +431,28 @@ int64_t gemm_f32_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits) {
   return L.used <= 1 ? 0 : L.need;
 }
 
+int gemm_f32_splitk_plan(int64_t M, int64_t N, int64_t K, int splits, int* variant,
+                         int* cfg_id, int* chunks, int64_t* split_from) {
+  if (M < 0 || N < 0 || K < 0) return GEMMF32_ERR_NEGATIVE_DIM;
+  if (splits == 0) splits = select_splits(M, N, K);
+  if (splits == 0 || splits == -1 || splits < -kMaxSplits || splits > kMaxSplits)
+    return GEMMF32_ERR_BAD_CONFIG;
+  const SplitLayout L = splitk_layout(M, N, K, splits);
+  int v = L.variant, c = L.cfg, used = L.used;
+  int64_t from = L.split_from;
+  if (L.used <= 1) {  // the plain product
+    select_shape(M, N, K, &v, &c);
+    used = 1;
+    const CfgEntry& e = kConfigs[c];
+    from = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn);
+  }
+  if (variant) *variant = v;
+  if (cfg_id) *cfg_id = c;
+  if (chunks) *chunks = used;
+  if (split_from) *split_from = from;
+  return GEMMF32_OK;
+}
+
 int gemm_f32_select(int64_t M, int64_t N, int64_t K, int* variant, int* cfg_id) {
   if (M < 0 || N < 0 || K < 0) return GEMMF32_ERR_NEGATIVE_DIM;
   int v = 0, c = 0;
