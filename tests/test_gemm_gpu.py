@@ -68,7 +68,7 @@ SMALL = ["square_128", "ragged_127x193x61", "ragged_513x257x129", "square_1024",
          "rect_256x1024x128", "rect_1024x128x256"]
 
 
-@pytest.mark.parametrize("variant", ["auto", "sb", "db", "ms", "sb3"])
+@pytest.mark.parametrize("variant", ["auto", "sb", "db", "ms", "sb3", "ks"])
 @pytest.mark.parametrize("name", SMALL)
 def test_workload_parity(name, variant):
     _say(f"[parity] {name} {variant}")
