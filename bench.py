@@ -35,6 +35,11 @@ Also:
                                              metric shape (1024^3, 4096^3, 8192^3) plus the
                                              calibration kernel: the program that the
                                              rocprofv3 --pmc passes profile
+  python bench.py --counter-run-skinny       the K-split kernel at 16x4096x4096 and, with
+                                             the same per-wave work, the 64x64x32 DB tile at
+                                             1024^3 (three launches each), plus the
+                                             calibration kernel: the program of the K-split
+                                             kernel's counter passes
   python bench.py --write-traffic FETCH_DIR WRITE_DIR
                                              HBM bytes per launch of the headline kernel from
                                              a FETCH_SIZE pass and a WRITE_SIZE pass of
@@ -236,6 +241,42 @@ def counter_run(calib_mib: int) -> int:
     return 0
 
 
+def counter_run_skinny(calib_mib: int) -> int:
+    """A short program for counter passes of the K-split kernel: three launches at
+    16 x 4096 x 4096 (variant KS, configuration 13) and three of the 64 x 64 x 32 DB tile
+    (configuration 6) at 1024^3, whose four waves each walk the same 32 K tiles of one
+    32 x 32 block."""
+    import torch
+
+    import tdb_inputs as ti
+    import tiled_double_buffered_amd as tdb
+
+    dev = torch.device("cuda:0")
+    if calib_mib > 0:
+        n = calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    s_ptr = torch.cuda.current_stream(dev).cuda_stream
+    for (M, N, K, variant, cfg, seed) in [(16, 4096, 4096, tdb.VARIANT_KS, 13, 7101),
+                                          (1024, 1024, 1024, tdb.VARIANT_DB, 6, 7102)]:
+        a, b = ti.workload_inputs(M, N, K, seed)
+        A, B = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+        C = torch.empty((M, N), device=dev)
+        for _ in range(3):
+            rc = tdb.gemm_f32_ex(M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N,
+                                 variant, cfg, s_ptr)
+            if rc != tdb.OK:
+                raise tdb.GemmError(rc, "gemm_f32_ex")
+        torch.cuda.synchronize()
+        print(f"[counter-run-skinny] {M}x{N}x{K} variant {variant} cfg {cfg} done",
+              file=sys.stderr, flush=True)
+        del A, B, C
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -254,6 +295,7 @@ def main() -> int:
     ap.add_argument("--summarize-counters", metavar="DIR")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--counter-run", action="store_true")
+    ap.add_argument("--counter-run-skinny", action="store_true")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--oracle-table", action="store_true")
     args = ap.parse_args()
@@ -265,6 +307,8 @@ def main() -> int:
         return write_traffic(*args.write_traffic)
     if args.counter_run:
         return counter_run(args.copy_calibration)
+    if args.counter_run_skinny:
+        return counter_run_skinny(args.copy_calibration)
 
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace)
