@@ -44,8 +44,11 @@ enum {
     GEMMF32_ERR_NULL_PTR = -3,      /* NULL pointer for a non-empty operand              */
     GEMMF32_ERR_MISALIGNED = -4,    /* A, B or C not 4-byte aligned                      */
     GEMMF32_ERR_ALIAS = -5,         /* the byte range of C overlaps that of A or B       */
-    GEMMF32_ERR_TOO_LARGE = -6,     /* M, N, K or a leading dimension beyond 2^31 - 1,
-                                       or the grid does not fit one launch              */
+    GEMMF32_ERR_TOO_LARGE = -6,     /* M, N or K beyond 2^31 - 1025; a leading dimension
+                                       beyond 64 times that (about 2^37); an operand or
+                                       workspace whose byte extent ((rows-1)*ld + cols)*4
+                                       passes 2^61 or wraps the address space; or a grid
+                                       that does not fit one launch                     */
     GEMMF32_ERR_BAD_CONFIG = -7,    /* unknown variant or tile configuration id          */
     GEMMF32_ERR_HIP = -8            /* the HIP launch failed                             */
 };
@@ -165,7 +168,9 @@ int gemm_f32_splitk(int64_t M, int64_t N, int64_t K,
                     void *stream);
 
 /* Workspace floats gemm_f32_splitk needs for this shape and split count (0 = the modelled
- * choice; the result is 0 when it will not split), or a negative error code. */
+ * choice; the result is 0 when it will not split), or a negative error code
+ * (GEMMF32_ERR_TOO_LARGE for sizes beyond the limits of gemm_f32 or a workspace of more
+ * than 2^61 bytes). */
 int64_t gemm_f32_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits);
 
 /* The split count for a shape with the least modelled time among 1 (do not split), the
@@ -185,9 +190,13 @@ int gemm_f32_splitk_plan(int64_t M, int64_t N, int64_t K, int splits, int *varia
                          int *cfg_id, int *chunks, int64_t *split_from);
 
 /* The dispatch decision for a shape, without launching: *variant receives
- * GEMMF32_VARIANT_SB, _DB, _MS or _KS and *cfg_id the tile configuration id.  Either output pointer
- * may be NULL.  Pure host code (no GPU needed).  Returns GEMMF32_ERR_NEGATIVE_DIM for
- * negative sizes. */
+ * GEMMF32_VARIANT_SB, _DB, _MS or _KS and *cfg_id the tile configuration id that gemm_f32
+ * would launch for it.  The choice is made per shape because the pages measure the
+ * double-buffered loop winning at one size, losing at another and tying at a third, and
+ * conclude that no one kernel is fastest everywhere ("Double Buffering", last two
+ * paragraphs; "Case Study: The Double-Buffered GEMM", paragraph on the three regimes).
+ * Either output pointer may be NULL.  Pure host code (no GPU needed).  Returns
+ * GEMMF32_ERR_NEGATIVE_DIM for negative sizes. */
 int gemm_f32_select(int64_t M, int64_t N, int64_t K, int *variant, int *cfg_id);
 
 /* Tile configuration id for an explicit variant (SB, DB or MS) and shape, as used by

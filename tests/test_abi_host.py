@@ -74,6 +74,50 @@ def test_validation_errors(fn):
     assert f(4, 4, 1 << 31, PA, 1 << 31, PB, 4, PC, 4) == tdb.ERR_TOO_LARGE
 
 
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_f32_sb", "gemm_f32_db", "gemm_f32_ms"])
+def test_extents_that_overflow_are_rejected(fn):
+    """Byte extents ((rows - 1) * ld + cols) * 4 that pass 2^61 (or overflow int64) are
+    rejected as too large before any alias test: a wrapped extent could otherwise make the
+    overlap test pass an impossible call through to a launch."""
+    f = getattr(tdb, fn)
+    big_ld = 1 << 36
+    # rows * ld far beyond 2^63: A, B and C in turn
+    assert f(1 << 30, 4, 4, PA, big_ld, PB, 4, PC, 4) == tdb.ERR_TOO_LARGE
+    assert f(4, 4, 1 << 30, PA, 1 << 30, PB, big_ld, PC, 4) == tdb.ERR_TOO_LARGE
+    assert f(1 << 30, 4, 4, PA, 4, PB, 4, PC, big_ld) == tdb.ERR_TOO_LARGE
+    # C == A with row strides of 2^32 - 1: the extent, 4 * (2^30 * (2^32 - 1) + 4), wraps
+    # int64 into a negative number, which made the old overlap test miss the alias
+    ld = (1 << 32) - 1
+    assert f((1 << 30) + 1, 4, 4, PA, ld, PB, 4, PA, ld) == tdb.ERR_TOO_LARGE
+    # just past 2^61 bytes without overflowing int64: 2^30 rows of stride 2^29 + 1 floats
+    assert f(1 << 30, 4, 4, PA, (1 << 29) + 1, PB, 4, PC, 4) == tdb.ERR_TOO_LARGE
+    # an extent that fits but wraps the 64-bit address space
+    top = (1 << 64) - 4096
+    assert f(2, 4, 4, top, 1024, PB, 4, PC, 4) == tdb.ERR_TOO_LARGE
+    assert f(2, 1024, 4, PA, 4, PB, 1024, top, 1024) == tdb.ERR_TOO_LARGE
+    # leading dimensions beyond the documented limit (64 * (2^31 - 1025))
+    ld_max = 64 * (2147483647 - 1024)
+    assert f(1, 4, 4, PA, ld_max + 1, PB, 4, PC, 4) == tdb.ERR_TOO_LARGE
+    assert f(4, 4, 4, PA, 4, PB, ld_max + 1, PC, 4) == tdb.ERR_TOO_LARGE
+
+
+def test_splitk_extents_and_workspace_that_overflow_are_rejected():
+    f = tdb.gemm_f32_splitk
+    ld = (1 << 32) - 1
+    assert f((1 << 30) + 1, 4, 4096, PA, ld, PB, 4, PA, ld, 4, PB,
+             1 << 40) == tdb.ERR_TOO_LARGE
+    # the workspace query: 64 * M * N floats passes int64 for the largest M and N
+    big = 2147483647 - 1024
+    assert tdb.gemm_f32_splitk_workspace(big, big, 8192, 64) == tdb.ERR_TOO_LARGE
+    assert tdb.gemm_f32_splitk_workspace(big + 1, 4, 8192, 4) == tdb.ERR_TOO_LARGE
+    # a workspace that fits int64 but wraps the address space
+    M, N, K = 64, 64, 4096
+    need = tdb.gemm_f32_splitk_workspace(M, N, K, 4)
+    assert need > 0
+    top = (1 << 64) - 4096
+    assert f(M, N, K, PA, K, PB, N, PC, N, 4, top, need) == tdb.ERR_TOO_LARGE
+
+
 def test_alias_detection():
     f = tdb.gemm_f32
     M, N, K = 16, 16, 16
@@ -492,3 +536,29 @@ def test_peak_probe_validation_before_launch():
     assert f(4, 16, PA, 0) == tdb.ERR_NULL_PTR
     assert f(4, 16, PA + 2, PR) == tdb.ERR_MISALIGNED
     assert f(4, 16, PA, PR + 4) == tdb.ERR_MISALIGNED
+
+
+def test_binding_rejects_broadcast_and_overlapping_rows():
+    """A view whose rows share storage (an expanded row, or as_strided rows closer than
+    their length) has no leading dimension the library could use: the binding raises
+    instead of passing the row length, which would read or write past the storage.  The
+    checks run before the device check, so CPU tensors exercise them here."""
+    torch = pytest.importorskip("torch")
+    from tiled_double_buffered_amd._binding import _operand
+
+    row = torch.zeros(1, 8)
+    for bad in (row.expand(5, 8),                              # stride 0
+                torch.zeros(64).as_strided((5, 8), (4, 1)),    # rows overlap by half
+                torch.zeros(1, 1).expand(3, 1)):               # a broadcast column
+        with pytest.raises(ValueError, match="row stride"):
+            _operand(bad, "A")
+    # well-formed operands get past the stride checks and stop only at the device check
+    for ok in (torch.zeros(5, 8), torch.zeros(5, 12)[:, :8], torch.zeros(1, 8),
+               torch.zeros(5, 1), row.expand(1, 8)):
+        with pytest.raises(ValueError, match="must live on the GPU"):
+            _operand(ok, "A")
+    # the tensor-level entry points refuse such a view before anything else
+    with pytest.raises(ValueError, match="row stride"):
+        tdb.matmul(row.expand(5, 8), torch.zeros(8, 3), out=torch.zeros(5, 3))
+    with pytest.raises(ValueError, match="row stride"):
+        tdb.matmul_splitk(row.expand(5, 8), torch.zeros(8, 3), out=torch.zeros(5, 3))

@@ -197,13 +197,19 @@ def _operand(t, name):
     import torch
     if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.dim() != 2:
         raise TypeError(f"{name} must be a 2-D float32 tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must live on the GPU (the library takes device pointers)")
     rows, cols = t.shape
     if cols > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must have unit column stride (row-major)")
+    if rows > 1 and t.stride(0) < max(cols, 1):
+        # an expanded (stride 0) or overlapping view: its rows share storage, and passing
+        # the row length as the leading dimension would make the library read or write
+        # past the tensor's storage
+        raise ValueError(f"{name} has row stride {t.stride(0)} < row length {cols}: "
+                         "broadcast or overlapping rows are not supported")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU (the library takes device pointers)")
     ld = t.stride(0) if rows > 1 else max(cols, 1)
-    return t.data_ptr(), max(ld, cols, 1)
+    return t.data_ptr(), ld
 
 
 def matmul(A, B, out=None, variant: str = "auto", cfg_id: int = -1, stream=None):
@@ -248,6 +254,9 @@ def matmul_splitk(A, B, splits=0, out=None, workspace=None, stream=None):
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     elif tuple(out.shape) != (M, N):
         raise ValueError("out has the wrong shape")
+    pa, lda = _operand(A, "A")
+    pb, ldb = _operand(B, "B")
+    pc, ldc = _operand(out, "out")
     need = gemm_f32_splitk_workspace(M, N, K, splits)
     if need < 0:
         raise GemmError(int(need), "gemm_f32_splitk_workspace")
@@ -256,9 +265,6 @@ def matmul_splitk(A, B, splits=0, out=None, workspace=None, stream=None):
     if workspace.dtype != torch.float32 or not workspace.is_cuda or \
             not workspace.is_contiguous():
         raise TypeError("workspace must be a contiguous float32 GPU tensor")
-    pa, lda = _operand(A, "A")
-    pb, ldb = _operand(B, "B")
-    pc, ldc = _operand(out, "out")
     s = (stream if stream is not None else torch.cuda.current_stream(A.device)).cuda_stream
     rc = gemm_f32_splitk(M, N, K, pa, lda, pb, ldb, pc, ldc, splits, workspace.data_ptr(),
                          workspace.numel(), s)

@@ -136,31 +136,66 @@ namespace gemmf32 {
 static thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kMaxDim = 2147483647LL - 1024;  // keeps tile-end arithmetic in int32
+constexpr int64_t kMaxLd = kMaxDim * 64;           // leading dimensions (elements)
+constexpr int64_t kMaxExtent = (int64_t)1 << 61;   // bytes one operand may span
+
+// Byte extent ((rows - 1) * ld + cols) * 4 of a rows x cols operand with row stride ld
+// (rows, cols >= 1), computed without signed overflow.  False when it passes kMaxExtent.
+static bool extent_bytes(int64_t rows, int64_t cols, int64_t ld, int64_t* bytes) {
+  int64_t e;
+  if (__builtin_mul_overflow(rows - 1, ld, &e) || __builtin_add_overflow(e, cols, &e) ||
+      __builtin_mul_overflow(e, (int64_t)4, &e) || e > kMaxExtent)
+    return false;
+  *bytes = e;
+  return true;
+}
+
+// [p, p + bytes) as addresses; false when it wraps around the address space.
+static bool byte_range(const void* p, int64_t bytes, uintptr_t* lo, uintptr_t* hi) {
+  *lo = (uintptr_t)p;
+  if (__builtin_add_overflow(*lo, (uintptr_t)bytes, hi)) return false;
+  return true;
+}
+
+static bool overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
+  return a0 < b1 && b0 < a1;
+}
+
+// Byte ranges of the operands of a validated, non-empty call (A and B only when K > 0).
+struct Extents {
+  uintptr_t a0, a1, b0, b1, c0, c1;
+};
 
 static int validate(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
-                    const float* B, int64_t ldb, const float* C, int64_t ldc) {
+                    const float* B, int64_t ldb, const float* C, int64_t ldc,
+                    Extents* ext = nullptr) {
   if (M < 0 || N < 0 || K < 0) return GEMMF32_ERR_NEGATIVE_DIM;
   const int64_t min_lda = K > 1 ? K : 1;
   const int64_t min_ldb = N > 1 ? N : 1;
   if (lda < min_lda || ldb < min_ldb || ldc < min_ldb) return GEMMF32_ERR_BAD_LD;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMMF32_ERR_TOO_LARGE;
-  if (lda > kMaxDim * 64 || ldb > kMaxDim * 64 || ldc > kMaxDim * 64)
-    return GEMMF32_ERR_TOO_LARGE;
+  if (lda > kMaxLd || ldb > kMaxLd || ldc > kMaxLd) return GEMMF32_ERR_TOO_LARGE;
   if (M == 0 || N == 0) return GEMMF32_OK;
   if (C == nullptr) return GEMMF32_ERR_NULL_PTR;
   if (K > 0 && (A == nullptr || B == nullptr)) return GEMMF32_ERR_NULL_PTR;
   if (((uintptr_t)C & 3u) != 0) return GEMMF32_ERR_MISALIGNED;
   if (K > 0 && ((((uintptr_t)A) & 3u) != 0 || (((uintptr_t)B) & 3u) != 0))
     return GEMMF32_ERR_MISALIGNED;
-  // Byte extents [begin, end) of the three operands; C must be disjoint from A and B.
-  const uintptr_t c0 = (uintptr_t)C;
-  const uintptr_t c1 = c0 + (uintptr_t)(((M - 1) * ldc + N) * 4);
+  // Byte extents [begin, end) of the three operands, each at most kMaxExtent and not
+  // wrapping; C must be disjoint from A and B.
+  Extents x{0, 0, 0, 0, 0, 0};
+  int64_t cb;
+  if (!extent_bytes(M, N, ldc, &cb) || !byte_range(C, cb, &x.c0, &x.c1))
+    return GEMMF32_ERR_TOO_LARGE;
   if (K > 0) {
-    const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)(((M - 1) * lda + K) * 4);
-    const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)(((K - 1) * ldb + N) * 4);
-    if (c0 < a1 && a0 < c1) return GEMMF32_ERR_ALIAS;
-    if (c0 < b1 && b0 < c1) return GEMMF32_ERR_ALIAS;
+    int64_t ab, bb;
+    if (!extent_bytes(M, K, lda, &ab) || !byte_range(A, ab, &x.a0, &x.a1) ||
+        !extent_bytes(K, N, ldb, &bb) || !byte_range(B, bb, &x.b0, &x.b1))
+      return GEMMF32_ERR_TOO_LARGE;
+    if (overlap(x.c0, x.c1, x.a0, x.a1) || overlap(x.c0, x.c1, x.b0, x.b1))
+      return GEMMF32_ERR_ALIAS;
   }
+  if (ext) *ext = x;
   return GEMMF32_OK;
 }
 
@@ -297,8 +332,17 @@ struct SplitLayout {
   int used;
   int variant, cfg;
   int64_t split_from;
-  int64_t need;
+  int64_t need;  // workspace floats; -1 when the workspace would pass kMaxExtent bytes
 };
+
+// a * b * c as workspace floats, or -1 when its byte size would pass kMaxExtent.
+static int64_t checked_product(int64_t a, int64_t b, int64_t c) {
+  int64_t r;
+  if (__builtin_mul_overflow(a, b, &r) || __builtin_mul_overflow(r, c, &r) ||
+      r > kMaxExtent / 4)
+    return -1;
+  return r;
+}
 
 static SplitLayout splitk_layout(int64_t M, int64_t N, int64_t K, int splits) {
   SplitLayout L{0, 1, 0, 0, 0, 0};
@@ -312,14 +356,14 @@ static SplitLayout splitk_layout(int64_t M, int64_t N, int64_t K, int splits) {
     L.variant = tp.variant;
     L.cfg = tp.cfg;
     L.split_from = tp.split_from;
-    L.need = (int64_t)L.used * (tiles - tp.split_from) * e.bm * e.bn;
+    L.need = checked_product(L.used, tiles - tp.split_from, (int64_t)e.bm * e.bn);
   } else {
     // Every tile split: its chunks run side by side in one grid, so the tile is chosen for
     // `used` times the workgroups of one chunk's product; partial products are M x N planes.
     const ModelRow& pick = model_pick(M, N, L.kc, 0, L.used);
     L.variant = pick.variant;
     L.cfg = pick.cfg;
-    L.need = (int64_t)L.used * M * N;
+    L.need = checked_product(L.used, M, N);
   }
   return L;
 }
@@ -330,20 +374,21 @@ static int run_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t l
   if (splits == 0 && M >= 0 && N >= 0 && K >= 0) splits = select_splits(M, N, K);
   if (splits == 0 || splits == -1 || splits < -kMaxSplits || splits > kMaxSplits)
     return GEMMF32_ERR_BAD_CONFIG;
-  int rc = validate(M, N, K, A, lda, B, ldb, C, ldc);
+  Extents x;
+  int rc = validate(M, N, K, A, lda, B, ldb, C, ldc, &x);
   if (rc != GEMMF32_OK) return rc;
   if (M == 0 || N == 0) return GEMMF32_OK;
   const SplitLayout L = splitk_layout(M, N, K, splits);
   if (L.used <= 1) return run(M, N, K, A, lda, B, ldb, C, ldc, GEMMF32_VARIANT_AUTO, -1, stream);
+  if (L.need < 0) return GEMMF32_ERR_TOO_LARGE;
   if (ws == nullptr) return GEMMF32_ERR_NULL_PTR;
   if (((uintptr_t)ws & 3u) != 0) return GEMMF32_ERR_MISALIGNED;
   if (ws_floats < L.need) return GEMMF32_ERR_BAD_LD;
-  // The workspace must not overlap A, B or C.
-  const uintptr_t w0 = (uintptr_t)ws, w1 = w0 + (uintptr_t)(L.need * 4);
-  const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)(((M - 1) * lda + K) * 4);
-  const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)(((K - 1) * ldb + N) * 4);
-  const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)(((M - 1) * ldc + N) * 4);
-  if ((w0 < a1 && a0 < w1) || (w0 < b1 && b0 < w1) || (w0 < c1 && c0 < w1))
+  // The workspace must not overlap A, B or C (K > 0 here: a split needs K chunks).
+  uintptr_t w0, w1;
+  if (!byte_range(ws, L.need * 4, &w0, &w1)) return GEMMF32_ERR_TOO_LARGE;
+  if (overlap(w0, w1, x.a0, x.a1) || overlap(w0, w1, x.b0, x.b1) ||
+      overlap(w0, w1, x.c0, x.c1))
     return GEMMF32_ERR_ALIAS;
   const SplitPlan plan{ws, M * N, L.kc, L.used, L.split_from};
   rc = launch(L.variant, L.cfg, M, N, K, A, lda, B, ldb, C, ldc, stream, &plan);
@@ -427,8 +472,10 @@ int64_t gemm_f32_splitk_workspace(int64_t M, int64_t N, int64_t K, int splits) {
   if (splits == 0 || splits == -1 || splits < -kMaxSplits || splits > kMaxSplits)
     return GEMMF32_ERR_BAD_CONFIG;
   if (M == 0 || N == 0 || K == 0) return 0;
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GEMMF32_ERR_TOO_LARGE;
   const SplitLayout L = splitk_layout(M, N, K, splits);
-  return L.used <= 1 ? 0 : L.need;
+  if (L.used <= 1) return 0;
+  return L.need < 0 ? GEMMF32_ERR_TOO_LARGE : L.need;
 }
 
 int gemm_f32_splitk_plan(int64_t M, int64_t N, int64_t K, int splits, int* variant,
