@@ -50,8 +50,13 @@ enum {
                                        passes 2^61 or wraps the address space; or a grid
                                        that does not fit one launch                     */
     GEMMF32_ERR_BAD_CONFIG = -7,    /* unknown variant or tile configuration id          */
-    GEMMF32_ERR_HIP = -8            /* the HIP launch failed                             */
+    GEMMF32_ERR_HIP = -8,           /* the HIP launch failed                             */
+    GEMMF32_ERR_SCRATCH_LIMIT = -9  /* gemm_f32_splitk_noalloc: the split needs more than
+                                       GEMMF32_SCRATCH_FLOATS floats of scratch         */
 };
+
+/* Floats of the static device scratch array behind gemm_f32_splitk_noalloc (32 MiB). */
+#define GEMMF32_SCRATCH_FLOATS (8 * 1024 * 1024)
 
 /* Variants of the K-loop. */
 enum {
@@ -166,6 +171,32 @@ int gemm_f32_splitk(int64_t M, int64_t N, int64_t K,
                     float *C, int64_t ldc,
                     int splits, float *workspace, int64_t workspace_floats,
                     void *stream);
+
+/* For callers that cannot allocate: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The same product, split and launches as
+ * gemm_f32_splitk, but the partial products go to a scratch array the library holds in
+ * device memory (a file-scope __device__ array of GEMMF32_SCRATCH_FLOATS floats, 32 MiB,
+ * one copy per device, held from the library's first use on that device until the
+ * process ends), so the call itself allocates nothing: no hipMalloc, no hipFree, no
+ * allocating library routine.  The caller still passes A, B and C.
+ *   splits: as for gemm_f32_splitk (0 = the modelled choice of gemm_f32_splitk_select).
+ *   The device is the one `stream` belongs to (the current device for NULL).  Its first
+ *   call on a device looks up the array's device address (hipGetSymbolAddress, with that
+ *   device current) and keeps it.
+ * The array is shared by every call on its device and keeps the last call's partials; each
+ * call overwrites every partial it reads before reading it, so nothing needs clearing.
+ * Calls on one device whose kernels can run at the same time (different streams without
+ * ordering between them) race on the array and give wrong results; calls ordered on one
+ * stream are safe.
+ * Errors: as for gemm_f32_splitk, with GEMMF32_ERR_SCRATCH_LIMIT when the split needs more
+ * than GEMMF32_SCRATCH_FLOATS floats (gemm_f32_splitk_workspace gives the need; pick
+ * fewer splits or use gemm_f32_splitk with a workspace of the caller's), and
+ * GEMMF32_ERR_HIP when the device or the array's address cannot be found. */
+int gemm_f32_splitk_noalloc(int64_t M, int64_t N, int64_t K,
+                            const float *A, int64_t lda,
+                            const float *B, int64_t ldb,
+                            float *C, int64_t ldc,
+                            int splits, void *stream);
 
 /* Workspace floats gemm_f32_splitk needs for this shape and split count (0 = the modelled
  * choice; the result is 0 when it will not split), or a negative error code

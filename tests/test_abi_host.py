@@ -42,7 +42,7 @@ def test_version_and_strerror():
     assert "gfx950" in tdb.gemm_f32_version()
     codes = [tdb.OK, tdb.ERR_NEGATIVE_DIM, tdb.ERR_BAD_LD, tdb.ERR_NULL_PTR,
              tdb.ERR_MISALIGNED, tdb.ERR_ALIAS, tdb.ERR_TOO_LARGE, tdb.ERR_BAD_CONFIG,
-             tdb.ERR_HIP]
+             tdb.ERR_HIP, tdb.ERR_SCRATCH_LIMIT]
     msgs = [tdb.gemm_f32_strerror(c) for c in codes]
     assert len(set(msgs)) == len(codes)
     assert tdb.gemm_f32_strerror(-999) == "unknown error code"
@@ -562,3 +562,25 @@ def test_binding_rejects_broadcast_and_overlapping_rows():
         tdb.matmul(row.expand(5, 8), torch.zeros(8, 3), out=torch.zeros(5, 3))
     with pytest.raises(ValueError, match="row stride"):
         tdb.matmul_splitk(row.expand(5, 8), torch.zeros(8, 3), out=torch.zeros(5, 3))
+
+
+def test_noalloc_split_validation_before_launch():
+    """The allocation-free split entry point validates like gemm_f32_splitk and rejects a
+    split that needs more than its static scratch before any HIP call (no device lookup
+    either: these run without a GPU)."""
+    f = tdb.gemm_f32_splitk_noalloc
+    M, N, K = 64, 256, 4096
+    assert f(M, N, K, PA, K, PB, N, PC, N, -1) == tdb.ERR_BAD_CONFIG
+    assert f(M, N, K, PA, K, PB, N, PC, N, 65) == tdb.ERR_BAD_CONFIG
+    assert f(-1, N, K, PA, K, PB, N, PC, N, 4) == tdb.ERR_NEGATIVE_DIM
+    assert f(M, N, K, PA, K - 1, PB, N, PC, N, 4) == tdb.ERR_BAD_LD
+    assert f(M, N, K, 0, K, PB, N, PC, N, 4) == tdb.ERR_NULL_PTR
+    assert f(M, N, K, PA, K, PB, N, PA, N, 4) == tdb.ERR_ALIAS
+    assert f(0, N, K, 0, K, 0, N, 0, N, 4) == tdb.OK
+    # 8 planes of 4096 x 4096 floats: 128 Mi floats against the 8 Mi of the scratch
+    big = 4096
+    need = tdb.gemm_f32_splitk_workspace(big, big, big, 8)
+    assert need > tdb.SCRATCH_FLOATS == 8 * 1024 * 1024
+    assert f(big, big, big, PA, big, PB, big, PC, big, 8) == tdb.ERR_SCRATCH_LIMIT
+    text = open(HEADER).read()
+    assert re.search(r"#define GEMMF32_SCRATCH_FLOATS \(8 \* 1024 \* 1024\)", text)

@@ -21,6 +21,8 @@ ERR_ALIAS = -5
 ERR_TOO_LARGE = -6
 ERR_BAD_CONFIG = -7
 ERR_HIP = -8
+ERR_SCRATCH_LIMIT = -9
+SCRATCH_FLOATS = 8 * 1024 * 1024  # GEMMF32_SCRATCH_FLOATS
 
 VARIANT_AUTO = 0
 VARIANT_SB = 1
@@ -41,6 +43,7 @@ SIGNATURES = {
     "gemm_f32_ms": (_int, _GEMM_ARGS + [_vp]),
     "gemm_f32_ex": (_int, _GEMM_ARGS + [_int, _int, _vp]),
     "gemm_f32_splitk": (_int, _GEMM_ARGS + [_int, _vp, _i64, _vp]),
+    "gemm_f32_splitk_noalloc": (_int, _GEMM_ARGS + [_int, _vp]),
     "gemm_f32_splitk_workspace": (_i64, [_i64, _i64, _i64, _int]),
     "gemm_f32_splitk_select": (_int, [_i64, _i64, _i64]),
     "gemm_f32_splitk_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_int),
@@ -113,6 +116,10 @@ def gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, splits, workspace, workspac
                     stream=None) -> int:
     return load().gemm_f32_splitk(M, N, K, A, lda, B, ldb, C, ldc, splits, workspace,
                                   workspace_floats, stream)
+
+
+def gemm_f32_splitk_noalloc(M, N, K, A, lda, B, ldb, C, ldc, splits, stream=None) -> int:
+    return load().gemm_f32_splitk_noalloc(M, N, K, A, lda, B, ldb, C, ldc, splits, stream)
 
 
 def gemm_f32_splitk_workspace(M, N, K, splits) -> int:

@@ -25,9 +25,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "gemmf32.h"
 #include "gemm_common.h"
@@ -368,30 +370,14 @@ static SplitLayout splitk_layout(int64_t M, int64_t N, int64_t K, int splits) {
   return L;
 }
 
-static int run_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
-                      const float* B, int64_t ldb, float* C, int64_t ldc, int splits,
-                      float* ws, int64_t ws_floats, void* stream) {
-  if (splits == 0 && M >= 0 && N >= 0 && K >= 0) splits = select_splits(M, N, K);
-  if (splits == 0 || splits == -1 || splits < -kMaxSplits || splits > kMaxSplits)
-    return GEMMF32_ERR_BAD_CONFIG;
-  Extents x;
-  int rc = validate(M, N, K, A, lda, B, ldb, C, ldc, &x);
-  if (rc != GEMMF32_OK) return rc;
-  if (M == 0 || N == 0) return GEMMF32_OK;
-  const SplitLayout L = splitk_layout(M, N, K, splits);
-  if (L.used <= 1) return run(M, N, K, A, lda, B, ldb, C, ldc, GEMMF32_VARIANT_AUTO, -1, stream);
-  if (L.need < 0) return GEMMF32_ERR_TOO_LARGE;
-  if (ws == nullptr) return GEMMF32_ERR_NULL_PTR;
-  if (((uintptr_t)ws & 3u) != 0) return GEMMF32_ERR_MISALIGNED;
-  if (ws_floats < L.need) return GEMMF32_ERR_BAD_LD;
-  // The workspace must not overlap A, B or C (K > 0 here: a split needs K chunks).
-  uintptr_t w0, w1;
-  if (!byte_range(ws, L.need * 4, &w0, &w1)) return GEMMF32_ERR_TOO_LARGE;
-  if (overlap(w0, w1, x.a0, x.a1) || overlap(w0, w1, x.b0, x.b1) ||
-      overlap(w0, w1, x.c0, x.c1))
-    return GEMMF32_ERR_ALIAS;
+// The two launches of a split product whose workspace `ws` holds L.need floats: the GEMM
+// kernel writes every chunk's partial product into it (each element of each partial is
+// stored, so nothing needs clearing first), then a reduction sums the chunks into C.
+static int splitk_launch(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                         const float* B, int64_t ldb, float* C, int64_t ldc,
+                         const SplitLayout& L, float* ws, void* stream) {
   const SplitPlan plan{ws, M * N, L.kc, L.used, L.split_from};
-  rc = launch(L.variant, L.cfg, M, N, K, A, lda, B, ldb, C, ldc, stream, &plan);
+  int rc = launch(L.variant, L.cfg, M, N, K, A, lda, B, ldb, C, ldc, stream, &plan);
   if (rc != GEMMF32_OK) return rc;
   int m = (int)M, n = (int)N, used = L.used;
   const float* p = ws;
@@ -421,6 +407,120 @@ static int run_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t l
     return GEMMF32_ERR_HIP;
   }
   return GEMMF32_OK;
+}
+
+// Validation and layout shared by both split entry points.  Returns GEMMF32_OK with
+// *plain set when the call is an unsplit product (or empty), otherwise the layout in *L.
+static int splitk_prepare(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                          const float* B, int64_t ldb, const float* C, int64_t ldc,
+                          int splits, Extents* x, SplitLayout* L, bool* plain) {
+  if (splits == 0 && M >= 0 && N >= 0 && K >= 0) splits = select_splits(M, N, K);
+  if (splits == 0 || splits == -1 || splits < -kMaxSplits || splits > kMaxSplits)
+    return GEMMF32_ERR_BAD_CONFIG;
+  const int rc = validate(M, N, K, A, lda, B, ldb, C, ldc, x);
+  if (rc != GEMMF32_OK) return rc;
+  *plain = true;
+  if (M == 0 || N == 0) return GEMMF32_OK;
+  *L = splitk_layout(M, N, K, splits);
+  if (L->used <= 1) return GEMMF32_OK;
+  if (L->need < 0) return GEMMF32_ERR_TOO_LARGE;
+  *plain = false;
+  return GEMMF32_OK;
+}
+
+static int run_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                      const float* B, int64_t ldb, float* C, int64_t ldc, int splits,
+                      float* ws, int64_t ws_floats, void* stream) {
+  Extents x;
+  SplitLayout L;
+  bool plain = true;
+  int rc = splitk_prepare(M, N, K, A, lda, B, ldb, C, ldc, splits, &x, &L, &plain);
+  if (rc != GEMMF32_OK) return rc;
+  if (plain) {
+    if (M == 0 || N == 0) return GEMMF32_OK;
+    return run(M, N, K, A, lda, B, ldb, C, ldc, GEMMF32_VARIANT_AUTO, -1, stream);
+  }
+  if (ws == nullptr) return GEMMF32_ERR_NULL_PTR;
+  if (((uintptr_t)ws & 3u) != 0) return GEMMF32_ERR_MISALIGNED;
+  if (ws_floats < L.need) return GEMMF32_ERR_BAD_LD;
+  // The workspace must not overlap A, B or C (K > 0 here: a split needs K chunks).
+  uintptr_t w0, w1;
+  if (!byte_range(ws, L.need * 4, &w0, &w1)) return GEMMF32_ERR_TOO_LARGE;
+  if (overlap(w0, w1, x.a0, x.a1) || overlap(w0, w1, x.b0, x.b1) ||
+      overlap(w0, w1, x.c0, x.c1))
+    return GEMMF32_ERR_ALIAS;
+  return splitk_launch(M, N, K, A, lda, B, ldb, C, ldc, L, ws, stream);
+}
+
+// ------------------------------------------------------------------------------------
+// The static scratch of gemm_f32_splitk_noalloc.  Each device the library runs on holds
+// its own copy of this array from the module's load until the process ends.  Host code
+// never uses the array's name as an address (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and is kept in g_scratch.
+// ------------------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[GEMMF32_SCRATCH_FLOATS];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<float*> g_scratch[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the device `stream` belongs to (the current device
+// for the NULL stream).
+static int scratch_address(void* stream, float** out) {
+  int dev = -1;
+  hipError_t err = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+  if (err != hipSuccess) {
+    g_last_hip_error = (int)err;
+    return GEMMF32_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    g_last_hip_error = (int)hipErrorInvalidDevice;
+    return GEMMF32_ERR_HIP;
+  }
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      int cur = -1;
+      err = hipGetDevice(&cur);
+      if (err == hipSuccess && cur != dev) err = hipSetDevice(dev);
+      void* addr = nullptr;
+      if (err == hipSuccess) err = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (cur >= 0 && cur != dev) {
+        const hipError_t back = hipSetDevice(cur);
+        if (err == hipSuccess) err = back;
+      }
+      if (err != hipSuccess || addr == nullptr) {
+        g_last_hip_error = (int)(err != hipSuccess ? err : hipErrorInvalidSymbol);
+        return GEMMF32_ERR_HIP;
+      }
+      p = static_cast<float*>(addr);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return GEMMF32_OK;
+}
+
+static int run_splitk_noalloc(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                              const float* B, int64_t ldb, float* C, int64_t ldc, int splits,
+                              void* stream) {
+  Extents x;
+  SplitLayout L;
+  bool plain = true;
+  int rc = splitk_prepare(M, N, K, A, lda, B, ldb, C, ldc, splits, &x, &L, &plain);
+  if (rc != GEMMF32_OK) return rc;
+  if (plain) {
+    if (M == 0 || N == 0) return GEMMF32_OK;
+    return run(M, N, K, A, lda, B, ldb, C, ldc, GEMMF32_VARIANT_AUTO, -1, stream);
+  }
+  if (L.need > (int64_t)GEMMF32_SCRATCH_FLOATS) return GEMMF32_ERR_SCRATCH_LIMIT;
+  float* ws = nullptr;
+  rc = scratch_address(stream, &ws);
+  if (rc != GEMMF32_OK) return rc;
+  return splitk_launch(M, N, K, A, lda, B, ldb, C, ldc, L, ws, stream);
 }
 
 }  // namespace gemmf32
@@ -459,6 +559,12 @@ int gemm_f32_splitk(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda
                     float* workspace, int64_t workspace_floats, void* stream) {
   return run_splitk(M, N, K, A, lda, B, ldb, C, ldc, splits, workspace, workspace_floats,
                     stream);
+}
+
+int gemm_f32_splitk_noalloc(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                            const float* B, int64_t ldb, float* C, int64_t ldc, int splits,
+                            void* stream) {
+  return run_splitk_noalloc(M, N, K, A, lda, B, ldb, C, ldc, splits, stream);
 }
 
 int gemm_f32_splitk_select(int64_t M, int64_t N, int64_t K) {
@@ -568,6 +674,7 @@ const char* gemm_f32_strerror(int code) {
     case GEMMF32_ERR_TOO_LARGE: return "dimension or grid too large for one launch";
     case GEMMF32_ERR_BAD_CONFIG: return "unknown variant or tile configuration";
     case GEMMF32_ERR_HIP: return "HIP kernel launch failed";
+    case GEMMF32_ERR_SCRATCH_LIMIT: return "split needs more than the static scratch holds";
     default: return "unknown error code";
   }
 }
