@@ -65,17 +65,15 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_MFMA_TFLOPS = 157.3          # MI355X dense FP32 matrix peak (AMD specification)
 METRIC = "FP32 GEMM TFLOP/s and % of MFMA FP32 peak at 1024³/4096³/8192³, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_8192.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "tiled_double_buffered_amd", "csrc", f)
-                  for f in ("gemm_f32.hip", "gemm_common.h", "kernels_sb_db.h",
-                            "kernels_ms.h", "kernels_ks.h", "splitk_reduce.h",
-                            "dispatch_table.h", "mfma_peak.h")]
 HEADLINE = "square_8192"
 VARIANT_NAMES = {1: "sb", 2: "db", 3: "ms", 5: "ks"}
 
 
 def kernel_source_hash() -> str:
+    """SHA-256 over the library's sources and headers (the files its build compiles)."""
+    from tiled_double_buffered_amd import build
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in build.DEPS:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()

@@ -7,6 +7,7 @@ assembly and per-kernel resource usage for the structural tests.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import re
 import subprocess
@@ -16,9 +17,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-SOURCES = [os.path.join(CSRC, "gemm_f32.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("gemm_common.h", "kernels_sb_db.h", "kernels_ms.h",
-                                            "kernels_ks.h", "splitk_reduce.h",
+MAIN_SOURCE = os.path.join(CSRC, "gemm_f32.hip")
+CFG_SOURCE = os.path.join(CSRC, "cfg_kernels.hip")
+NUM_CONFIGS = 14  # configs.h: kNumConfigs
+SOURCES = [MAIN_SOURCE, CFG_SOURCE]
+HEADERS = [os.path.join(CSRC, f) for f in ("configs.h", "gemm_common.h", "kernels_sb_db.h",
+                                            "kernels_ms.h", "kernels_ks.h", "splitk_reduce.h",
                                             "dispatch_table.h", "mfma_peak.h")]
 DEPS = SOURCES + HEADERS + [os.path.join(INCLUDE, "gemmf32.h")]
 LIB = os.path.join(PKG, "libgemmf32.so")
@@ -37,10 +41,34 @@ def _run(cmd, **kw):
     return subprocess.run(cmd, check=True, **kw)
 
 
+def _units():
+    """(name, source, extra flags) of every translation unit: the host code and reduction
+    kernels, then one unit per tile configuration."""
+    units = [("gemm_f32", MAIN_SOURCE, [])]
+    units += [(f"cfg{i}", CFG_SOURCE, [f"-DGEMMF32_CFG_ID={i}"]) for i in range(NUM_CONFIGS)]
+    return units
+
+
+def _parallel(cmds):
+    jobs = max(1, min(16, os.cpu_count() or 1))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        for f in [ex.submit(_run, c) for c in cmds]:
+            f.result()
+
+
 def build_library() -> str:
-    """Compile libgemmf32.so (always recompiles).  Returns its path."""
+    """Compile libgemmf32.so (always recompiles; the translation units in parallel).
+    Returns its path."""
+    obj_dir = os.path.join(BUILD_DIR, "obj")
+    os.makedirs(obj_dir, exist_ok=True)
+    objs, cmds = [], []
+    for name, src, extra in _units():
+        obj = os.path.join(obj_dir, name + ".o")
+        objs.append(obj)
+        cmds.append([HIPCC, *DEVICE_FLAGS, *extra, "-fPIC", "-c", src, "-o", obj])
+    _parallel(cmds)
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC, *DEVICE_FLAGS, "-fPIC", "-shared", *SOURCES, "-o", tmp])
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", *objs, "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 
@@ -53,15 +81,26 @@ def library_is_stale() -> bool:
 
 
 def device_asm() -> str:
-    """gfx950 assembly of the library's device code (cached under _build/)."""
+    """gfx950 assembly of the library's device code, all translation units (cached under
+    _build/)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    out = os.path.join(BUILD_DIR, "gemm_f32-gfx950.s")
-    if not os.path.exists(out) or os.path.getmtime(out) < max(os.path.getmtime(p) for p in DEPS):
-        tmp = out + ".tmp%d" % os.getpid()
-        _run([HIPCC, *DEVICE_FLAGS, "--cuda-device-only", "-S", *SOURCES, "-o", tmp])
+    newest = max(os.path.getmtime(p) for p in DEPS)
+    outs, cmds = [], []
+    for name, src, extra in _units():
+        out = os.path.join(BUILD_DIR, f"{name}-gfx950.s")
+        outs.append(out)
+        if not os.path.exists(out) or os.path.getmtime(out) < newest:
+            tmp = out + ".tmp%d" % os.getpid()
+            cmds.append(([HIPCC, *DEVICE_FLAGS, *extra, "--cuda-device-only", "-S", src,
+                          "-o", tmp], tmp, out))
+    _parallel([c for c, _, _ in cmds])
+    for _, tmp, out in cmds:
         os.replace(tmp, out)
-    with open(out) as f:
-        return f.read()
+    text = []
+    for out in outs:
+        with open(out) as f:
+            text.append(f.read())
+    return "\n".join(text)
 
 
 def kernel_functions(asm: str) -> dict:

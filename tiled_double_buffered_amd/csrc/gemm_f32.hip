@@ -19,7 +19,9 @@
 //
 // Files: gemm_common.h (tile configurations, copy, micro-kernel, epilogue),
 // kernels_sb_db.h (single- and double-buffered loops), kernels_ms.h (multi-stage
-// direct-to-LDS loop), splitk_reduce.h (split-K reduction), dispatch_table.h (measured
+// direct-to-LDS loop), kernels_ks.h (K split inside the workgroup), configs.h (the
+// configuration list), cfg_kernels.hip (one configuration's kernels, compiled once per
+// configuration), splitk_reduce.h (split-K reduction), dispatch_table.h (measured
 // per-shape choices); this file holds the configuration table, argument validation,
 // dispatch and the C ABI.
 #include <hip/hip_runtime.h>
@@ -32,87 +34,21 @@
 #include <mutex>
 
 #include "gemmf32.h"
+#include "configs.h"
 #include "gemm_common.h"
-#include "kernels_ks.h"
-#include "kernels_ms.h"
-#include "kernels_sb_db.h"
 #include "mfma_peak.h"
 #include "splitk_reduce.h"
 
 namespace gemmf32 {
 
-// ------------------------------------------------------------------------------------
-// Configuration table.  Ids are part of the ABI (gemm_f32_ex, gemm_f32_config_info).
-// ------------------------------------------------------------------------------------
-using Cfg0 = TileCfg<256, 256, 16, 2, 2>;  // wave 128x128 (16 blocks)
-using Cfg1 = TileCfg<256, 256, 32, 2, 2>;  // wave 128x128, deeper K tile
-using Cfg2 = TileCfg<256, 128, 16, 2, 2>;  // wave 128x64
-using Cfg3 = TileCfg<128, 128, 16, 2, 2>;  // wave 64x64
-using Cfg4 = TileCfg<128, 128, 32, 2, 2>;  // wave 64x64, deeper K tile
-using Cfg5 = TileCfg<128, 64, 32, 2, 2>;   // wave 64x32
-using Cfg6 = TileCfg<64, 64, 32, 2, 2>;    // wave 32x32
-using Cfg7 = TileCfg<64, 64, 64, 2, 2>;    // wave 32x32, deeper K tile
-using Cfg8 = TileCfg<256, 256, 32, 2, 4>;  // 8 waves of 128x64: two waves per SIMD
-using Cfg9 = TileCfg<128, 256, 32, 2, 4>;  // 8 waves of 64x64
-using Cfg10 = TileCfg<32, 128, 32, 1, 4>;  // 4 waves of 32x32 side by side: skinny M
-using Cfg11 = TileCfg<192, 192, 16, 2, 2>;  // wave 96x96: 16x16 tiles for 3072-wide C
-using Cfg12 = TileCfg<192, 192, 32, 2, 2>;  // wave 96x96, deeper K tile
-using Cfg13 = TileCfg<32, 32, 32, 1, 1>;    // one wave: few rows, long K (K-split kernel)
-
-typedef void (*KernelFn)(int, int, int, const float*, int64_t, const float*, int64_t, float*,
-                         int64_t, int, SplitArgs);
-
-// ms: the multi-stage kernel, where the configuration has one (its swizzle needs tiles
-// of B at least 64 wide; stages 0 otherwise); ks: the K-split kernel and its wave groups,
-// where it has one (groups 1 otherwise).
-struct CfgEntry {
-  int bm, bn, bk, nt;
-  int lds_sb, lds_db;
-  int ms_stages, lds_ms;
-  KernelFn sb, db, ms, sb3;
-  KernelFn ks;
-  int ks_groups;
-};
-
-template <class C>
-constexpr bool has_ms() {
-  return C::BN % 64 == 0;
-}
-
-template <class C>
-constexpr CfgEntry make_entry() {
-  constexpr int S = has_ms<C>() ? ms_stages<C>() : 0;
-  constexpr int KS = ks_groups<C>();
-  KernelFn ms = nullptr, ks = nullptr;
-  int lds_ms = 0;
-  if constexpr (has_ms<C>()) {
-    ms = &gemm_f32_ms_kernel<C, S>;
-    lds_ms = (int)(MsCfg<C, S>::LDS_FLOATS * sizeof(float));
-  }
-  if constexpr (KS > 1) ks = &gemm_f32_ks_kernel<C, KS>;
-  return CfgEntry{C::BM,
-                  C::BN,
-                  C::BK,
-                  C::NT,
-                  (int)(C::SLOT * sizeof(float)),
-                  (int)(2 * C::SLOT * sizeof(float)),
-                  S,
-                  lds_ms,
-                  &gemm_f32_tile_kernel<C, kLoopSB>,
-                  &gemm_f32_tile_kernel<C, kLoopDB>,
-                  ms,
-                  &gemm_f32_tile_kernel<C, kLoopSB3>,
-                  ks,
-                  KS};
-}
-
+// The table of tile configurations (configs.h); each entry's kernels live in the
+// configuration's own translation unit.
 static const CfgEntry kConfigs[] = {
-    make_entry<Cfg0>(), make_entry<Cfg1>(), make_entry<Cfg2>(), make_entry<Cfg3>(),
-    make_entry<Cfg4>(), make_entry<Cfg5>(), make_entry<Cfg6>(), make_entry<Cfg7>(),
-    make_entry<Cfg8>(), make_entry<Cfg9>(), make_entry<Cfg10>(), make_entry<Cfg11>(),
-    make_entry<Cfg12>(), make_entry<Cfg13>(),
+    cfg_entry_0(),  cfg_entry_1(),  cfg_entry_2(),  cfg_entry_3(),  cfg_entry_4(),
+    cfg_entry_5(),  cfg_entry_6(),  cfg_entry_7(),  cfg_entry_8(),  cfg_entry_9(),
+    cfg_entry_10(), cfg_entry_11(), cfg_entry_12(), cfg_entry_13(),
 };
-constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+static_assert(sizeof(kConfigs) / sizeof(kConfigs[0]) == kNumConfigs, "configuration table");
 
 constexpr int kMaxSplits = 64;
 constexpr int kSplitGranule = 64;  // K chunks are whole K tiles of every configuration
