@@ -18,11 +18,32 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 //   WAVES_M x WAVES_N waves per workgroup; each wave owns a TM x TN sub-tile made of
 //   FM x FN blocks of 32 x 32, one 16-register accumulator per block.
 // LDS layout of one slot (FP32):
-//   As[BM][AS]  A tile with k contiguous, row stride AS = BK + 4 (the pad of 4 words
-//               makes the 16-byte reads of 8 or 16 consecutive rows hit distinct banks)
+//   As[BM][AS]  A tile with k contiguous.  K tiles of 16 (SWZ_A): unpadded rows (AS = BK)
+//               whose 16-byte chunks are XOR-swizzled, chunk c of row r at chunk
+//               c ^ swz_a<BK>(r) (below).  Deeper K tiles: rows padded to AS = BK + 4.
 //   Bs[BK][BS]  B tile with n contiguous, row stride BS = BN + 8 (so the two half-waves,
 //               which read rows 4 apart, land on opposite halves of the 64 banks)
+//
+// A fragment read has 16 lanes read one logical 16-byte chunk of 16 consecutive rows.
+// With padded rows, row r starts on bank group (of 4 banks) r * (BK + 4) / 4 mod 16, an
+// odd multiple of r for BK = 16, 32 and 64, so the 16 rows hit 16 different groups.  The
+// copy's 16-byte stores of 16-row-deep tiles (four 16-float rows per 16 lanes) then wrap
+// onto their own first banks, though: the counters measured 17% of LDS cycles lost to
+// bank conflicts for the 256x256x16 tile, and none for the padded 32- and 64-deep tiles.
+// The swizzle removes them for BK = 16: the 16 lanes of a store cover 64 consecutive
+// words, only permuted inside each row, and each of the rows that start on the same bank
+// group (unpadded, r * 4 mod 16) has its chunk moved by a different amount, so a read's
+// 16 rows still land on 16 different bank groups.  (The swizzle is kept to BK = 16: on the
+// deeper tiles it measured no faster, and the single-buffered 8-wave 128x256x32 tile ran
+// 17% slower with it at 8192^3 though its counters showed no conflicts either way.)
 // ------------------------------------------------------------------------------------
+// Swizzle of A row r: constant over runs of 64/BK rows, stepping through 0 .. BK/4 - 1, so
+// its period is 16 rows for every BK.
+template <int BK>
+__host__ __device__ constexpr int swz_a(int row) {
+  return (row / (64 / BK)) % (BK / 4);
+}
+
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, BK = BK_;
@@ -30,7 +51,8 @@ struct TileCfg {
   static constexpr int NT = WAVES_M * WAVES_N * 64;
   static constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
   static constexpr int FM = TM / 32, FN = TN / 32;
-  static constexpr int AS = BK + 4;
+  static constexpr bool SWZ_A = BK == 16;
+  static constexpr int AS = SWZ_A ? BK : BK + 4;
   static constexpr int BS = BN + 8;
   static constexpr int A_SLOT = BM * AS;
   static constexpr int B_SLOT = BK * BS;
@@ -49,7 +71,7 @@ struct TileCfg {
   static constexpr bool DB_UNROLL = NT <= 256 || FM * FN * 16 <= 64;
 
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
-  static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+  static_assert(BK == 16 || BK == 32 || BK == 64, "A layouts");
   static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "copy must divide");
   static_assert(NT % A_GROUPS_PER_ROW == 0, "copy rows of A");
   // NT a multiple of the B groups per row: every pass of the B copy starts at the same
@@ -245,11 +267,23 @@ struct TileCopy {
     }
   }
 
+  // Where pass i of this thread's A copy goes in a slot (floats); swizzled passes whose
+  // rows differ by whole swizzle periods (16 rows) differ by a constant.
+  __device__ inline int a_store_off(int i) const {
+    const int row = a_row + i * C::A_ROWS_PER_PASS;
+    if constexpr (!C::SWZ_A)
+      return row * C::AS + a_col;
+    else if constexpr (C::A_ROWS_PER_PASS % 16 == 0)
+      return a_row * C::AS + 4 * ((a_col >> 2) ^ swz_a<C::BK>(a_row)) +
+             i * C::A_ROWS_PER_PASS * C::AS;
+    else
+      return row * C::AS + 4 * ((a_col >> 2) ^ swz_a<C::BK>(row));
+  }
   __device__ inline void store_a(float* slot) {
     float* As = slot;
 #pragma unroll
     for (int i = 0; i < C::A_PER_T; ++i)
-      *reinterpret_cast<floatx4*>(As + (a_row + i * C::A_ROWS_PER_PASS) * C::AS + a_col) = ra[i];
+      *reinterpret_cast<floatx4*>(As + a_store_off(i)) = ra[i];
   }
   __device__ inline void store_b(float* slot) {
     float* Bs = slot + C::A_SLOT;
@@ -280,20 +314,26 @@ struct Frag {
   float b[C::FN][4];
 };
 
-// This lane's fragment offsets (in floats) inside an LDS slot.
+// This lane's fragment offsets (in floats) inside an LDS slot.  Round q reads logical
+// chunk 2q + h of its A rows: at float 8q + 4h of a padded row, or, swizzled, at chunk
+// (2q + h) ^ swz = (2q) ^ a_x; the rows of the lane's blocks are 32 apart, whole swizzle
+// periods, so one a_x serves all of them.
 template <class C>
 struct LaneView {
-  int a_off, b_off;
+  int a_off, a_x, b_off;
   __device__ inline void init(int wm, int wn, int lane) {
     const int h = lane >> 5, l32 = lane & 31;
-    a_off = (wm * C::TM + l32) * C::AS + 4 * h;
+    const int row = wm * C::TM + l32;
+    a_off = row * C::AS + (C::SWZ_A ? 0 : 4 * h);
+    a_x = C::SWZ_A ? h ^ swz_a<C::BK>(row) : 0;
     b_off = C::A_SLOT + (4 * h) * C::BS + wn * C::TN + l32;
   }
 };
 
 template <class C>
 __device__ inline void read_frag(const float* slot, const LaneView<C>& lv, int q, Frag<C>& f) {
-  const float* a_ptr = slot + lv.a_off + 8 * q;
+  const float* a_ptr =
+      slot + lv.a_off + (C::SWZ_A ? 4 * ((2 * q) ^ lv.a_x) : 8 * q);
   const float* b_ptr = slot + lv.b_off + 8 * q * C::BS;
 #pragma unroll
   for (int fm = 0; fm < C::FM; ++fm)

@@ -58,10 +58,6 @@ struct MsCfg {
   static_assert(LDS_FLOATS * 4 <= 160 * 1024, "LDS of one CU");
 };
 
-template <class C>
-__device__ __forceinline__ int swz_a(int row) {
-  return (row / (64 / C::BK)) % (C::BK / 4);
-}
 __device__ __forceinline__ int swz_b(int k) { return ((k >> 2) & 1) << 3; }
 
 // The four descriptor words of a raw buffer starting at `base` and `range` bytes long
@@ -107,7 +103,7 @@ struct MsCopy {
       from_a[i] = j < MC::A_CHUNKS;
       if (j < MC::A_CHUNKS) {
         const int row = j * MC::RPC_A + lane / MC::CPR_A;
-        const int c = (lane % MC::CPR_A) ^ swz_a<C>(row);
+        const int c = (lane % MC::CPR_A) ^ swz_a<C::BK>(row);
         off[i] = (uint32_t)(((int64_t)row * lda + 4 * c) * 4);
         lds_off[i] = (uint32_t)j * 1024u;
       } else {
@@ -190,7 +186,7 @@ struct LaneViewMs {
     const int h = lane >> 5, l32 = lane & 31;
     const int row = wm * C::TM + l32;
     a_off = row * C::BK;
-    a_x = h ^ swz_a<C>(row);
+    a_x = h ^ swz_a<C::BK>(row);
 #pragma unroll
     for (int fn = 0; fn < C::FN; ++fn) {
       const int col = wn * C::TN + fn * 32 + l32;
