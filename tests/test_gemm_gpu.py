@@ -91,6 +91,12 @@ def test_every_config_sb_equals_db_and_matches_oracle(cfg):
         A, B = ti.workload_inputs(M, N, K, seed)
         C64, Bnd = oracle.gemm_f64(A, B)
         Ad, Bd = _dev(A), _dev(B)
+        if not _has(cfg, "db"):  # the 16-row configuration: its K-split kernel only
+            Cks = _run(Ad, Bd, "ks", cfg).clone()
+            assert _ratio(Cks, C64, Bnd) <= 1.0
+            assert torch.equal(_run(Ad, Bd, "ks", cfg), Cks), "K-split is not deterministic"
+            assert torch.equal(_run(Ad, Bd, "auto", cfg), Cks), "auto on a K-split-only cfg"
+            continue
         Csb = _run(Ad, Bd, "sb", cfg).clone()
         Cdb = _run(Ad, Bd, "db", cfg).clone()
         Csb3 = _run(Ad, Bd, "sb3", cfg).clone()
@@ -130,6 +136,114 @@ def test_edge_residues(cfg):
             _run(Ad, Bd, v, cfg, out=C)
             r = _ratio(C, C64, Bnd)
             assert r <= 1.0, (cfg, v, M, N, K, r)
+
+
+def _dispatched_pairs():
+    """(variant name, configuration) of every kernel the dispatcher or the explicit SB, DB
+    and MS entry points pick for a workload shape, or for a decode product."""
+    names = {tdb.VARIANT_SB: "sb", tdb.VARIANT_DB: "db", tdb.VARIANT_MS: "ms",
+             tdb.VARIANT_KS: "ks"}
+    pairs = set()
+    shapes = [w[:3] for w in ti.WORKLOADS.values()] + [(16, 4096, 4096), (1, 4096, 4096)]
+    for (M, N, K) in shapes:
+        _, v, c = tdb.gemm_f32_select(M, N, K)
+        pairs.add((names[v], c))
+        for v in (tdb.VARIANT_SB, tdb.VARIANT_DB, tdb.VARIANT_MS):
+            pairs.add((names[v], tdb.gemm_f32_select_cfg(M, N, K, v)))
+    return sorted(pairs, key=lambda p: (p[1], p[0]))
+
+
+@pytest.mark.parametrize("pair", _dispatched_pairs(), ids=lambda p: f"{p[0]}{p[1]}")
+def test_residue_sweep(pair):
+    """Every residue of M in 1 .. 2 BM, of N in 1 .. 2 BN and of K in 1 .. 2 BK (the other
+    two sizes held at ragged values spanning two tiles), C pre-filled with NaN, element by
+    element within the bound.  The oracle runs once per M and N sweep on the largest size:
+    the first m rows (n columns) of that product are the product of the first m rows of A
+    (n columns of B)."""
+    v, cfg = pair
+    _, info = tdb.gemm_f32_config_info(cfg)
+    bm, bn, bk = info["BM"], info["BN"], info["BK"]
+    _say(f"[residues] {v} cfg={cfg} {bm}x{bn}x{bk}")
+    # M sweep
+    N, K = bn + 7, bk + 3
+    A, B = ti.workload_inputs(2 * bm, N, K, 7700 + cfg)
+    C64, Bnd = oracle.gemm_f64(A, B)
+    Ad, Bd = _dev(A), _dev(B)
+    for m in range(1, 2 * bm + 1):
+        C = torch.full((m, N), float("nan"), device=DEV)
+        _run(Ad[:m], Bd, v, cfg, out=C)
+        r = _ratio(C, C64[:m], Bnd[:m])
+        assert r <= 1.0, (v, cfg, "M", m, N, K, r)
+    # N sweep
+    M, K = bm + 5, bk + 3
+    A, B = ti.workload_inputs(M, 2 * bn, K, 7800 + cfg)
+    C64, Bnd = oracle.gemm_f64(A, B)
+    Ad, Bd = _dev(A), _dev(B)
+    for n in range(1, 2 * bn + 1):
+        C = torch.full((M, n), float("nan"), device=DEV)
+        _run(Ad, Bd[:, :n], v, cfg, out=C)
+        r = _ratio(C, C64[:, :n], Bnd[:, :n])
+        assert r <= 1.0, (v, cfg, "N", M, n, K, r)
+    # K sweep (each K its own sums)
+    M, N = bm + 5, bn + 7
+    for k in range(1, 2 * bk + 1):
+        A, B = ti.workload_inputs(M, N, k, 7900 + 100 * cfg + k)
+        C64, Bnd = oracle.gemm_f64(A, B)
+        C = torch.full((M, N), float("nan"), device=DEV)
+        _run(_dev(A), _dev(B), v, cfg, out=C)
+        r = _ratio(C, C64, Bnd)
+        assert r <= 1.0, (v, cfg, "K", M, N, k, r)
+
+
+KS16 = [c for c in range(NCFG) if tdb.gemm_f32_config_variants(c) == 1 << tdb.VARIANT_KS]
+
+
+def _decode_shapes():
+    """Few rows against wide and long operands: every row count 1..17, N and K at and
+    around the 16-column tile and the 64-deep K group (the K range splits over 16 waves in
+    whole groups, so K from 1 to past 16 groups), and a few layer-sized products."""
+    shapes = [(m, 16, 64) for m in range(1, 18)]
+    shapes += [(16, n, 100) for n in (1, 2, 15, 17, 31, 33, 255, 257, 1000)]
+    shapes += [(7, 48, k) for k in (1, 2, 3, 4, 5, 15, 16, 17, 63, 64, 65, 127, 128, 129,
+                                      1023, 1024, 1025, 1087, 2000)]
+    shapes += [(1, 4096, 4096), (8, 4096, 4096), (16, 4096, 4096), (16, 11008, 4096),
+               (16, 4096, 11008), (33, 512, 3000), (5, 4111, 777)]
+    return shapes
+
+
+@pytest.mark.parametrize("cfg", KS16)
+def test_ks16_decode_shapes(cfg):
+    """The 16-row K-split kernel: element by element within the bound on every shape, C
+    pre-filled with NaN, and the same bits on a second run."""
+    for i, (M, N, K) in enumerate(_decode_shapes()):
+        _say(f"[ks16] cfg={cfg} {M}x{N}x{K}")
+        A, B = ti.workload_inputs(M, N, K, 8100 + i)
+        C64, Bnd = oracle.gemm_f64(A, B)
+        Ad, Bd = _dev(A), _dev(B)
+        C = torch.full((M, N), float("nan"), device=DEV)
+        _run(Ad, Bd, "ks", cfg, out=C)
+        r = _ratio(C, C64, Bnd)
+        assert r <= 1.0, (M, N, K, r)
+        assert torch.equal(_run(Ad, Bd, "ks", cfg), C), (M, N, K)
+
+
+@pytest.mark.parametrize("cfg", KS16)
+def test_ks16_matches_the_guarded_loads(cfg):
+    """Row strides too large for the 32-bit buffer offsets take the element-wise loads; the
+    product is the same bit for bit (same instructions, same order), and within the bound."""
+    M, N, K = 9, 70, 300
+    A, B = ti.workload_inputs(M, N, K, 8200)
+    C64, Bnd = oracle.gemm_f64(A, B)
+    fast = _run(_dev(A), _dev(B), "ks", cfg).clone()
+    # A rows 2^26 + 5 floats apart: a 16-row block of A spans more than 4 GiB (2.1 GB in all)
+    lda = (1 << 26) + 5
+    Abig = torch.full(((M - 1) * lda + K,), float("nan"), device=DEV)
+    Abig.as_strided((M, K), (lda, 1)).copy_(torch.from_numpy(A))
+    Av = Abig.as_strided((M, K), (lda, 1))
+    slow = _run(Av, _dev(B), "ks", cfg)
+    assert _ratio(slow, C64, Bnd) <= 1.0
+    assert torch.equal(slow, fast)
+    del Abig, Av
 
 
 def _random_cases(n=60, seed=31337):

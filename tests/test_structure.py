@@ -27,6 +27,11 @@ def kernels():
     assert funcs and set(funcs) <= set(meta)
     out = {}
     for name, body in funcs.items():
+        m16 = re.search(r"Ks16CfgILi(\d+)E", name)
+        if m16:  # the 16-row K-split kernel: a 16 x 16 tile, 16 k per block
+            out[name] = dict(cfg=(16, 16, 16, int(m16.group(1)), 1), kind="ks16", db=False,
+                             ms=False, stages=2, body=body, meta=meta[name])
+            continue
         m = re.search(r"TileCfgILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEE(?:Lb([01])|Li(\d+))E",
                       name)
         assert m, name
@@ -81,6 +86,12 @@ def test_barriers_per_k_step(kernels):
     of the peeled step that copies the last tile."""
     facts = json.load(open(GOLDEN))["barriers_per_k_step"]
     for name, k in kernels.items():
+        if k["kind"] == "ks16":
+            # every wave's K groups pass through its own registers, with no LDS tile shared
+            # between waves: no barrier in any loop, one for the hand-off of the sums
+            assert not any(_count_barriers(ls) for ls in _loop_blocks(k["body"]).values())
+            assert _count_barriers(k["body"].split("\n")) == 1, k["cfg"]
+            continue
         if k["cfg"][3] * k["cfg"][4] == 1 and k["kind"] != "ks":
             # a one-wave workgroup: the compiler drops its barriers (the LDS operations of
             # one wave are performed in order), so the loop shape is all that remains
@@ -123,10 +134,14 @@ def test_no_scratch_and_lds_fits(kernels):
 
 
 def test_fp32_matrix_instruction_only(kernels):
+    """True FP32 matrix instructions only: the 32 x 32 x 2 one, and the 16 x 16 x 4 one in
+    the 16-row K-split kernel (whose 16-row tiles would leave half of a 32-row block idle);
+    no packed FP32 arithmetic."""
     for name, k in kernels.items():
         body = k["body"]
         mfma = re.findall(r"\bv_mfma_\w+", body)
-        assert mfma and set(mfma) == {"v_mfma_f32_32x32x2_f32"}, (k["cfg"], set(mfma))
+        want = "v_mfma_f32_16x16x4_f32" if k["kind"] == "ks16" else "v_mfma_f32_32x32x2_f32"
+        assert mfma and set(mfma) == {want}, (k["cfg"], set(mfma))
         assert not re.search(r"\bv_pk_(fma|mul|add)_f32\b", body), k["cfg"]
 
 
@@ -134,6 +149,10 @@ def test_mfma_count_matches_tile(kernels):
     """One K tile is FM * FN * BK / 2 MFMAs per wave (each MFMA consumes a k pair); every
     kernel holds whole copies of that tile body (loops, unrolled steps, peeled tiles)."""
     for name, k in kernels.items():
+        if k["kind"] == "ks16":  # 4 MFMAs of 16 x 16 x 4 per 16-deep block of a K group
+            n = len(re.findall(r"\bv_mfma_f32_16x16x4_f32\b", k["body"]))
+            assert n > 0 and n % 4 == 0, (k["cfg"], n)
+            continue
         per_tile = _mfma_per_tile(k["cfg"])
         n = len(re.findall(r"\bv_mfma_f32_32x32x2_f32\b", k["body"]))
         assert n > 0 and n % per_tile == 0, (k["cfg"], k["kind"], n, per_tile)
@@ -198,3 +217,35 @@ def test_unguarded_copies_are_buffer_loads_without_vector_address_math(kernels):
             assert not any(t.startswith("v_lshl_add_u64") for t in ins), (k["cfg"], k["kind"])
         seen += 1
     assert seen >= 3
+
+
+def test_lds_poison_build_fills_every_freed_slot():
+    """The LDS-poison debug build (GEMMF32_LDS_POISON=1, the library's test variant) stores
+    NaN into each slot right after the barrier that frees it: in every K-loop of the
+    64 x 64 x 32 four-wave kernels, one extra 16-byte store per 16-byte copy store (the
+    register-staged loops) or per direct-to-LDS copy of the wave (the multi-stage loop),
+    per K tile; the production build has none of them."""
+    cfg = 6  # 64 x 64 x 32, four waves: A and B copies of 2 + 2 groups per thread
+    normal = build.kernel_functions(build.unit_asm(cfg))
+    poison = build.kernel_functions(build.unit_asm(cfg, poison=True))
+    assert set(normal) == set(poison)
+    per_tile_mfma = 16          # one 32 x 32 block per wave, BK / 2 k pairs
+    copies_per_tile = 4         # (64*32 + 32*64) floats: 4 x 16 bytes per thread / 1 KiB per wave
+    seen = 0
+    for name in normal:
+        def loops(body):
+            out = []
+            for ins in _loop_blocks(body).values():
+                if _count_barriers(ins):
+                    mfma = sum(1 for t in ins if t.startswith("v_mfma"))
+                    stores = sum(1 for t in ins if t.startswith("ds_write_b128"))
+                    out.append((mfma // per_tile_mfma, stores))
+            return sorted(out)
+        ln, lp = loops(normal[name]), loops(poison[name])
+        assert len(ln) == len(lp) and ln, name
+        for (tiles, st_n), (tiles_p, st_p) in zip(ln, lp):
+            assert tiles == tiles_p
+            assert st_p - st_n == copies_per_tile * tiles, (name, tiles, st_n, st_p)
+        assert "0x7fc00000" in poison[name] and "0x7fc00000" not in normal[name]
+        seen += 1
+    assert seen == 4  # single-, double-buffered, split-barrier and multi-stage

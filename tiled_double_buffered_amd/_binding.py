@@ -11,6 +11,8 @@ import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgemmf32.so")
+# the LDS-poison debug build of the same source (tests only)
+LIB_POISON_PATH = os.path.join(_PKG, "libgemmf32_lds_poison.so")
 
 OK = 0
 ERR_NEGATIVE_DIM = -1
@@ -74,11 +76,9 @@ class GemmError(RuntimeError):
         super().__init__(f"{what}: {msg} [{code}]" if what else f"{msg} [{code}]")
 
 
-def load(path: str = LIB_PATH):
-    """Load the library (once).  Raises if it is not built."""
-    global _lib
-    if _lib is not None:
-        return _lib
+def open_library(path: str):
+    """A ctypes handle on a build of the library at `path`, every entry point typed.
+    Raises if it is not built."""
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m tiled_double_buffered_amd.build`"
                            " (the GEMM has no fallback path)")
@@ -87,8 +87,15 @@ def load(path: str = LIB_PATH):
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = lib
     return lib
+
+
+def load(path: str = LIB_PATH):
+    """Load the library (once).  Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        _lib = open_library(path)
+    return _lib
 
 
 # ----------------------------------------------------------------------------- raw C ABI

@@ -1,9 +1,15 @@
 """Build the gfx950 library libgemmf32.so in-tree with hipcc, and expose its device
 assembly and per-kernel resource usage for the structural tests.
 
-    python -m tiled_double_buffered_amd.build              # builds the library
+    python -m tiled_double_buffered_amd.build              # builds the library and its
+                                                           # LDS-poison debug variant
     python -m tiled_double_buffered_amd.build --resources  # per-kernel registers, LDS,
                                                            # scratch, barriers per loop
+
+The debug variant libgemmf32_lds_poison.so is the same source built with
+GEMMF32_LDS_POISON=1: every LDS slot is filled with NaN right after the barrier that frees
+it, so a loop that read a slot after that barrier would put NaN into C.  Only the tests
+load it.
 """
 from __future__ import annotations
 
@@ -19,13 +25,14 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 MAIN_SOURCE = os.path.join(CSRC, "gemm_f32.hip")
 CFG_SOURCE = os.path.join(CSRC, "cfg_kernels.hip")
-NUM_CONFIGS = 14  # configs.h: kNumConfigs
+NUM_CONFIGS = 15  # configs.h: kNumConfigs
 SOURCES = [MAIN_SOURCE, CFG_SOURCE]
 HEADERS = [os.path.join(CSRC, f) for f in ("configs.h", "gemm_common.h", "kernels_sb_db.h",
-                                            "kernels_ms.h", "kernels_ks.h", "splitk_reduce.h",
+                                            "kernels_ms.h", "kernels_ks.h", "kernels_ks16.h", "splitk_reduce.h",
                                             "dispatch_table.h", "mfma_peak.h")]
 DEPS = SOURCES + HEADERS + [os.path.join(INCLUDE, "gemmf32.h")]
 LIB = os.path.join(PKG, "libgemmf32.so")
+LIB_POISON = os.path.join(PKG, "libgemmf32_lds_poison.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -56,21 +63,41 @@ def _parallel(cmds):
             f.result()
 
 
-def build_library() -> str:
-    """Compile libgemmf32.so (always recompiles; the translation units in parallel).
-    Returns its path."""
-    obj_dir = os.path.join(BUILD_DIR, "obj")
+def _library_jobs(poison: bool):
+    """(compile commands, objects, link command, temporary output, output) of one build."""
+    obj_dir = os.path.join(BUILD_DIR, "obj_poison" if poison else "obj")
     os.makedirs(obj_dir, exist_ok=True)
+    flags = ["-DGEMMF32_LDS_POISON=1"] if poison else []
+    out = LIB_POISON if poison else LIB
     objs, cmds = [], []
     for name, src, extra in _units():
         obj = os.path.join(obj_dir, name + ".o")
         objs.append(obj)
-        cmds.append([HIPCC, *DEVICE_FLAGS, *extra, "-fPIC", "-c", src, "-o", obj])
+        cmds.append([HIPCC, *DEVICE_FLAGS, *flags, *extra, "-fPIC", "-c", src, "-o", obj])
+    tmp = out + ".tmp%d" % os.getpid()
+    return cmds, [HIPCC, f"--offload-arch={ARCH}", "-shared", *objs, "-o", tmp], tmp, out
+
+
+def build_library(poison: bool = False) -> str:
+    """Compile libgemmf32.so, or with `poison` its LDS-poison debug variant (always
+    recompiles; the translation units in parallel).  Returns its path."""
+    cmds, link, tmp, out = _library_jobs(poison)
     _parallel(cmds)
-    tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    _run(link)
+    os.replace(tmp, out)
+    return out
+
+
+def build_all() -> list:
+    """Both libraries, every translation unit of both in one parallel pool."""
+    jobs = [_library_jobs(False), _library_jobs(True)]
+    _parallel([c for cmds, _, _, _ in jobs for c in cmds])
+    outs = []
+    for _, link, tmp, out in jobs:
+        _run(link)
+        os.replace(tmp, out)
+        outs.append(out)
+    return outs
 
 
 def library_is_stale() -> bool:
@@ -103,10 +130,25 @@ def device_asm() -> str:
     return "\n".join(text)
 
 
+def unit_asm(cfg_id: int, poison: bool = False) -> str:
+    """gfx950 assembly of one configuration's translation unit, optionally the LDS-poison
+    build (cached under _build/)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    out = os.path.join(BUILD_DIR, f"cfg{cfg_id}{'-poison' if poison else ''}-gfx950.s")
+    if not os.path.exists(out) or os.path.getmtime(out) < max(os.path.getmtime(p) for p in DEPS):
+        tmp = out + ".tmp%d" % os.getpid()
+        flags = ["-DGEMMF32_LDS_POISON=1"] if poison else []
+        _run([HIPCC, *DEVICE_FLAGS, *flags, f"-DGEMMF32_CFG_ID={cfg_id}", "--cuda-device-only",
+              "-S", CFG_SOURCE, "-o", tmp])
+        os.replace(tmp, out)
+    with open(out) as f:
+        return f.read()
+
+
 def kernel_functions(asm: str) -> dict:
     """Map mangled kernel name -> its assembly body (from the label to .Lfunc_end)."""
     out = {}
-    for m in re.finditer(r"^(_Z\S*gemm_f32_(?:tile|ms|ks)_kernel\S*):[ \t]*(?:;.*)?$", asm,
+    for m in re.finditer(r"^(_Z\S*gemm_f32_(?:tile|ms|ks|ks16)_kernel\S*):[ \t]*(?:;.*)?$", asm,
                          re.M):
         name = m.group(1)
         end = asm.find(f".Lfunc_end", m.end())
@@ -154,11 +196,16 @@ def resources_table(asm: str) -> str:
     meta = kernel_metadata(asm)
     rows = ["kernel                         vgpr agpr sgpr  lds_B scratch  loops: barriers/MFMAs"]
     for name, body in sorted(kernel_functions(asm).items()):
-        m = re.search(r"TileCfgILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEELi(\d+)E", name)
-        kind = "ms%s" % m.group(6) if "_ms_kernel" in name else \
-            "ks%s" % m.group(6) if "_ks_kernel" in name else \
-            {"1": "sb", "2": "db", "4": "sb3"}[m.group(6)]
-        tile = "%sx%sx%s/%sx%s" % m.groups()[:5]
+        m16 = re.search(r"Ks16CfgILi(\d+)ELi(\d+)E", name)
+        if m16:  # the 16-row K-split kernel: 16 x 16 tile, 16-k blocks per group, W waves
+            kind = "ks%s" % m16.group(1)
+            tile = "16x16x%d/%sx1" % (16 * int(m16.group(2)), m16.group(1))
+        else:
+            m = re.search(r"TileCfgILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEELi(\d+)E", name)
+            kind = "ms%s" % m.group(6) if "_ms_kernel" in name else \
+                "ks%s" % m.group(6) if "_ks_kernel" in name else \
+                {"1": "sb", "2": "db", "4": "sb3"}[m.group(6)]
+            tile = "%sx%sx%s/%sx%s" % m.groups()[:5]
         d = meta[name]
         # unified register file: architected VGPRs first, AGPRs from accum_offset on
         arch = min(d.get("accum_offset", d["next_free_vgpr"]), d["next_free_vgpr"])
@@ -180,8 +227,8 @@ def main(argv=None) -> int:
     if "--resources" in argv:
         print(resources_table(device_asm()))
         return 0
-    path = build_library()
-    print(path)
+    for path in build_all():
+        print(path)
     return 0
 
 

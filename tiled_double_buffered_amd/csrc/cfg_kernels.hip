@@ -5,6 +5,7 @@
 
 #include "configs.h"
 #include "kernels_ks.h"
+#include "kernels_ks16.h"
 #include "kernels_ms.h"
 #include "kernels_sb_db.h"
 
@@ -46,10 +47,26 @@ CfgEntry make_entry() {
                   KS};
 }
 
+// The 16-row decode configuration: the K-split kernel only.
+template <class D>
+CfgEntry make_ks16_entry() {
+  return CfgEntry{D::BM, D::BN, D::KG, 64, 0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr,
+                  &gemm_f32_ks16_kernel<D>, D::WAVES};
+}
+
+template <class T>
+struct EntryOf {
+  static CfgEntry get() { return make_entry<T>(); }
+};
+template <int WAVES, int BLOCKS, bool STRIDED>
+struct EntryOf<Ks16Cfg<WAVES, BLOCKS, STRIDED>> {
+  static CfgEntry get() { return make_ks16_entry<Ks16Cfg<WAVES, BLOCKS, STRIDED>>(); }
+};
+
 #define GEMMF32_CAT2(a, b) a##b
 #define GEMMF32_CAT(a, b) GEMMF32_CAT2(a, b)
 CfgEntry GEMMF32_CAT(cfg_entry_, GEMMF32_CFG_ID)() {
-  return make_entry<typename CfgById<GEMMF32_CFG_ID>::type>();
+  return EntryOf<typename CfgById<GEMMF32_CFG_ID>::type>::get();
 }
 
 }  // namespace gemmf32

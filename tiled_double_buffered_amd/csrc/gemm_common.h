@@ -7,10 +7,23 @@
 
 #include <cstdint>
 
+// Debug builds only (the library's lds-poison variant): every LDS slot or stage is filled
+// with NaN right after the barrier that frees it (see TileCopy::poison).
+#ifndef GEMMF32_LDS_POISON
+#define GEMMF32_LDS_POISON 0
+#endif
+
 namespace gemmf32 {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr bool kLdsPoison = GEMMF32_LDS_POISON != 0;
+
+__device__ __forceinline__ floatx4 nan4() {
+  const float q = __builtin_nanf("");
+  return floatx4{q, q, q, q};
+}
 
 // ------------------------------------------------------------------------------------
 // Tile configuration.
@@ -294,6 +307,25 @@ struct TileCopy {
   __device__ inline void store(float* slot) {
     store_a(slot);
     store_b(slot);
+  }
+
+  // LDS-poison debug mode: overwrite this thread's own part of a slot with NaN.  It is
+  // called right after the barrier that certifies every wave has finished reading the
+  // slot (the double-buffered hand-off, whose one barrier does that double duty: "Case
+  // Study: The Double-Buffered GEMM", paragraph after the code figure), and at the start.
+  // The slot's next tile is stored by the same thread at the same addresses, after this in
+  // program order, so a correct loop never reads the NaN; a wave that read the slot in
+  // between -- before the next tile's barrier -- would carry NaN into C.
+  __device__ inline void poison(float* slot) {
+    if constexpr (kLdsPoison) {
+      float* Bs = slot + C::A_SLOT;
+#pragma unroll
+      for (int i = 0; i < C::A_PER_T; ++i)
+        *reinterpret_cast<floatx4*>(slot + a_store_off(i)) = nan4();
+#pragma unroll
+      for (int i = 0; i < C::B_PER_T; ++i)
+        *reinterpret_cast<floatx4*>(Bs + brow(i) * C::BS + bcol(i)) = nan4();
+    }
   }
 };
 

@@ -46,7 +46,7 @@ namespace gemmf32 {
 static const CfgEntry kConfigs[] = {
     cfg_entry_0(),  cfg_entry_1(),  cfg_entry_2(),  cfg_entry_3(),  cfg_entry_4(),
     cfg_entry_5(),  cfg_entry_6(),  cfg_entry_7(),  cfg_entry_8(),  cfg_entry_9(),
-    cfg_entry_10(), cfg_entry_11(), cfg_entry_12(), cfg_entry_13(),
+    cfg_entry_10(), cfg_entry_11(), cfg_entry_12(), cfg_entry_13(), cfg_entry_14(),
 };
 static_assert(sizeof(kConfigs) / sizeof(kConfigs[0]) == kNumConfigs, "configuration table");
 
@@ -207,9 +207,14 @@ static int launch(int variant, int cfg_id, int64_t M, int64_t N, int64_t K, cons
 
 static bool has_variant(int cfg_id, int variant) {
   const CfgEntry& e = kConfigs[cfg_id];
-  return variant == GEMMF32_VARIANT_MS ? e.ms != nullptr
-         : variant == GEMMF32_VARIANT_KS ? e.ks != nullptr
-                                         : true;
+  switch (variant) {
+    case GEMMF32_VARIANT_SB: return e.sb != nullptr;
+    case GEMMF32_VARIANT_DB: return e.db != nullptr;
+    case GEMMF32_VARIANT_MS: return e.ms != nullptr;
+    case GEMMF32_VARIANT_SB3: return e.sb3 != nullptr;
+    case GEMMF32_VARIANT_KS: return e.ks != nullptr;
+    default: return false;
+  }
 }
 
 // The first configuration with a kernel for `variant` (the measured tables name one for
@@ -237,8 +242,7 @@ static int run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, con
       variant != GEMMF32_VARIANT_SB3 && variant != GEMMF32_VARIANT_KS)
     return GEMMF32_ERR_BAD_CONFIG;
   if (cfg_id < -1 || cfg_id >= kNumConfigs) return GEMMF32_ERR_BAD_CONFIG;
-  if (cfg_id >= 0 && ((variant == GEMMF32_VARIANT_MS && kConfigs[cfg_id].ms == nullptr) ||
-                      (variant == GEMMF32_VARIANT_KS && kConfigs[cfg_id].ks == nullptr)))
+  if (cfg_id >= 0 && variant != GEMMF32_VARIANT_AUTO && !has_variant(cfg_id, variant))
     return GEMMF32_ERR_BAD_CONFIG;
   int rc = validate(M, N, K, A, lda, B, ldb, C, ldc);
   if (rc != GEMMF32_OK) return rc;
@@ -249,9 +253,11 @@ static int run(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, con
     variant = v;
     if (cfg_id < 0) {
       cfg_id = c;
-    } else if ((variant == GEMMF32_VARIANT_MS && kConfigs[cfg_id].ms == nullptr) ||
-               (variant == GEMMF32_VARIANT_KS && kConfigs[cfg_id].ks == nullptr)) {
-      variant = GEMMF32_VARIANT_DB;  // a forced configuration without the picked variant
+    } else if (!has_variant(cfg_id, variant)) {
+      // a forced configuration without the picked variant: its double-buffered kernel, or
+      // its K-split one where it has no other
+      variant = has_variant(cfg_id, GEMMF32_VARIANT_DB) ? GEMMF32_VARIANT_DB
+                                                        : GEMMF32_VARIANT_KS;
     }
   } else if (cfg_id < 0) {
     cfg_id = select_for_variant(M, N, K, variant == GEMMF32_VARIANT_SB3 ? GEMMF32_VARIANT_SB
@@ -585,10 +591,10 @@ int gemm_f32_config_ms(int cfg_id, int* stages, int* lds_bytes) {
 
 int gemm_f32_config_variants(int cfg_id) {
   if (cfg_id < 0 || cfg_id >= kNumConfigs) return GEMMF32_ERR_BAD_CONFIG;
-  const CfgEntry& e = kConfigs[cfg_id];
-  int mask = (1 << GEMMF32_VARIANT_SB) | (1 << GEMMF32_VARIANT_DB) | (1 << GEMMF32_VARIANT_SB3);
-  if (e.ms != nullptr) mask |= 1 << GEMMF32_VARIANT_MS;
-  if (e.ks != nullptr) mask |= 1 << GEMMF32_VARIANT_KS;
+  int mask = 0;
+  for (int v : {GEMMF32_VARIANT_SB, GEMMF32_VARIANT_DB, GEMMF32_VARIANT_MS, GEMMF32_VARIANT_SB3,
+                GEMMF32_VARIANT_KS})
+    if (has_variant(cfg_id, v)) mask |= 1 << v;
   return mask;
 }
 
@@ -615,7 +621,9 @@ const char* gemm_f32_strerror(int code) {
   }
 }
 
-const char* gemm_f32_version(void) { return "gemmf32 0.1.0 gfx950"; }
+const char* gemm_f32_version(void) {
+  return GEMMF32_LDS_POISON ? "gemmf32 0.1.0 gfx950 lds-poison" : "gemmf32 0.1.0 gfx950";
+}
 
 int gemm_f32_peak_probe(int blocks, int iters, float* out, uint64_t* rec, void* stream) {
   if (blocks < 1 || blocks > kPeakMaxBlocks || iters < 0 || iters > kPeakMaxIters)

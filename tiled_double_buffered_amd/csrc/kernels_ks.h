@@ -80,6 +80,7 @@ __device__ __forceinline__ void ks_step(const float* cur, float* nxt, TileCopy<C
   }
   __syncthreads();
   if constexpr (!GUARD) __builtin_amdgcn_sched_barrier(0);
+  have.poison(const_cast<float*>(cur));  // debug builds: tile l's slot is free from here on
   read_frag(nxt, lv, 0, f[0]);
   mfma_round<C, 2>(f[1], acc);
   if constexpr (!GUARD) Sched<C>::db_after_barrier();
@@ -94,6 +95,8 @@ __device__ inline void k_loop_ks(float* smem, TileCopy<C>& cp0, TileCopy<C>& cp1
   Frag<C> f[2];
   float* const s0 = smem;
   float* const s1 = smem + C::SLOT;
+  cp0.poison(s0);  // debug builds: nothing is valid in either slot yet
+  cp0.poison(s1);
   ks_load<C, GUARD, EDGE>(cp0, g, 0, k_tiles);
   cp0.store(s0);
   if (k_tiles > 1) ks_load<C, GUARD, EDGE>(cp1, g, 1, k_tiles);

@@ -161,6 +161,23 @@ struct MsCopy {
   }
 };
 
+// LDS-poison debug mode: overwrite with NaN the 16 bytes this lane's copies write into
+// stage st (lane L of a copy fills bytes 16 L .. 16 L + 15 of the copy's 1 KiB), after the
+// barrier that frees the stage and before the copy that refills it.  The wait makes these
+// stores land before that copy can write the same bytes.
+template <class C, int S>
+__device__ __forceinline__ void ms_poison(float* smem, const MsCopy<C, S>& cp, int lane,
+                                          int st) {
+  if constexpr (kLdsPoison) {
+    using MC = MsCfg<C, S>;
+#pragma unroll
+    for (int i = 0; i < MC::D; ++i)
+      *reinterpret_cast<floatx4*>(smem + st * MC::STAGE + (cp.lds_off[i] + 16 * lane) / 4) =
+          nan4();
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+  }
+}
+
 // Wait until at most N copies of this wave are outstanding and this wave's LDS reads have
 // returned.
 template <int N>
@@ -217,10 +234,10 @@ __device__ inline void read_frag_ms(const float* stage, const LaneViewMs<C, S>& 
 // overwrites.  Near the end the copy index is clamped to the last tile (a harmless
 // duplicate into a stage no later tile uses), so every wait keeps S-2 tiles in flight.
 template <class C, int S, bool EDGE>
-__device__ __forceinline__ void ms_step(const float* smem, const MsCopy<C, S>& cp,
+__device__ __forceinline__ void ms_step(float* smem, const MsCopy<C, S>& cp,
                                         const LaneViewMs<C, S>& lv, int l, int k_tiles,
                                         int st, Frag<C> (&f)[2],
-                                        floatx16 (&acc)[C::FM][C::FN]) {
+                                        floatx16 (&acc)[C::FM][C::FN], int lane) {
   using MC = MsCfg<C, S>;
   constexpr int R = C::BK / 8;
   cp.template issue<EDGE>(min(l + S - 1, k_tiles - 1), st == 0 ? S - 1 : st - 1);
@@ -240,6 +257,7 @@ __device__ __forceinline__ void ms_step(const float* smem, const MsCopy<C, S>& c
   if constexpr (kFence) __builtin_amdgcn_sched_barrier(0);
   ms_wait_tile_barrier<C, S>();
   if constexpr (kFence) __builtin_amdgcn_sched_barrier(0);
+  ms_poison(smem, cp, lane, st);  // debug builds: tile l's stage is free from here on
   read_frag_ms(smem + (st + 1 == S ? 0 : st + 1) * MC::STAGE, lv, 0, f[0]);
   mfma_round<C, 2>(f[1], acc);
   Sched<C>::db_after_barrier();
@@ -251,9 +269,11 @@ __device__ __forceinline__ void ms_step(const float* smem, const MsCopy<C, S>& c
 template <class C, int S, bool EDGE>
 __device__ inline void k_loop_ms(float* smem, const MsCopy<C, S>& cp,
                                  const LaneViewMs<C, S>& lv, int k_tiles,
-                                 floatx16 (&acc)[C::FM][C::FN]) {
+                                 floatx16 (&acc)[C::FM][C::FN], int lane) {
   using MC = MsCfg<C, S>;
   constexpr int R = C::BK / 8;
+#pragma unroll
+  for (int t = 0; t < S; ++t) ms_poison(smem, cp, lane, t);  // debug builds: nothing valid yet
 #pragma unroll
   for (int t = 0; t < S - 1; ++t) cp.template issue<EDGE>(min(t, k_tiles - 1), t);
   ms_wait_tile_barrier<C, S>();
@@ -262,9 +282,11 @@ __device__ inline void k_loop_ms(float* smem, const MsCopy<C, S>& cp,
   int l = 0;
   for (; l + S < k_tiles; l += S) {
 #pragma unroll
-    for (int u = 0; u < S; ++u) ms_step<C, S, EDGE>(smem, cp, lv, l + u, k_tiles, u, f, acc);
+    for (int u = 0; u < S; ++u)
+      ms_step<C, S, EDGE>(smem, cp, lv, l + u, k_tiles, u, f, acc, lane);
   }
-  for (; l + 1 < k_tiles; ++l) ms_step<C, S, EDGE>(smem, cp, lv, l, k_tiles, l % S, f, acc);
+  for (; l + 1 < k_tiles; ++l)
+    ms_step<C, S, EDGE>(smem, cp, lv, l, k_tiles, l % S, f, acc, lane);
   const float* cur = smem + (l % S) * MC::STAGE;  // last tile: nothing left to copy
 #pragma unroll
   for (int q = 0; q + 1 < R; ++q) {
@@ -296,9 +318,9 @@ gemm_f32_ms_kernel(int M, int N, int K, const float* __restrict__ A, int64_t lda
       LaneViewMs<C, S> lv;
       lv.init(t.wm, t.wn, t.lane);
       if (t.m_full && t.n_full)
-        k_loop_ms<C, S, false>(smem, cp, lv, k_tiles, acc);
+        k_loop_ms<C, S, false>(smem, cp, lv, k_tiles, acc, t.lane);
       else
-        k_loop_ms<C, S, true>(smem, cp, lv, k_tiles, acc);
+        k_loop_ms<C, S, true>(smem, cp, lv, k_tiles, acc, t.lane);
     } else {
       // A K tail (its A columns past K must be zeroed, which a direct-to-LDS copy cannot
       // do) or offsets beyond the 32-bit range: the double-buffered loop, with 16-byte

@@ -33,6 +33,7 @@ __device__ __forceinline__ void db_step(const float* cur, float* nxt, TileCopy<C
   }
   __syncthreads();
   if constexpr (!GUARD) __builtin_amdgcn_sched_barrier(0);
+  cp.poison(const_cast<float*>(cur));  // debug builds: tile l's slot is free from here on
   read_frag(nxt, lv, 0, f[0]);
   mfma_round<C, 2>(f[1], acc);
   if constexpr (!GUARD) Sched<C>::db_after_barrier();
@@ -59,6 +60,8 @@ __device__ inline void k_loop_db(float* smem, TileCopy<C>& cp, const LaneView<C>
   Frag<C> f[2];
   float* const s0 = smem;
   float* const s1 = smem + C::SLOT;
+  cp.poison(s0);  // debug builds: nothing is valid in either slot yet
+  cp.poison(s1);
   if (k_tiles == 1)  // prologue: tile 0 into slot 0
     load_tile<C, GUARD, true>(cp, g, 0);
   else
@@ -125,6 +128,7 @@ __device__ __forceinline__ void sb_step(float* smem, TileCopy<C>& cp, const Lane
     Sched<C>::template rounds_with_reads<0>();
   }
   __syncthreads();  // every wave has read tile l: the slot may be overwritten
+  cp.poison(smem);  // debug builds: from here on nobody may read tile l
   mfma_round<C, 0>(f[1], acc);
 }
 
@@ -132,6 +136,7 @@ template <class C, bool GUARD, bool SPLIT = false, bool EDGE = true>
 __device__ inline void k_loop_sb(float* smem, TileCopy<C>& cp, const LaneView<C>& lv,
                                  const LoopArgs<C>& g, int k_tiles,
                                  floatx16 (&acc)[C::FM][C::FN]) {
+  cp.poison(smem);  // debug builds: nothing is valid in the slot yet
   for (int l = 0; l + 1 < k_tiles; ++l)
     sb_step<C, GUARD, SPLIT, false, EDGE>(smem, cp, lv, g, l, acc);
   // the last tile may end past K: its A columns >= K are zeroed
