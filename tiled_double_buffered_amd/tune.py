@@ -58,6 +58,11 @@ SHAPES = [
     (1023, 1023, 1023), (4095, 4095, 4095),
     # skinny shapes (a small batch of rows against a wide layer)
     (16, 4096, 4096), (32, 4096, 4096), (128, 4096, 4096), (32, 8192, 8192),
+    # decode rows (1 to 16) against 4096- and 11008-wide layers, and a small one
+    (1, 4096, 4096), (8, 4096, 4096), (16, 11008, 4096), (16, 4096, 11008),
+    (16, 8192, 8192), (4, 1024, 1024),
+    # one GPU's share of 8192^3 split by rows over eight GPUs
+    (1024, 8192, 8192),
 ]
 
 # Shapes for the split-count table: skinny, tall-K and square.
@@ -111,19 +116,23 @@ static inline const DispatchRow* dispatch_exact(int64_t M, int64_t N, int64_t K)
   return nullptr;
 }}
 
-// Cost model of every (variant, configuration) for shapes outside the table.  The features
-// are the two the regimes turn on: how many tiles the busiest compute unit multiplies,
-// rounds = ceil(workgroups / 256), and the K tiles per tile, k_tiles = ceil(K / BK).  A
-// launch is modelled as
-//     a + b * rounds + g * rounds * k_tiles   microseconds,
+// Cost model of every (variant, configuration) for shapes outside the table.  Its features
+// are what the regimes turn on: how many tiles the busiest compute unit multiplies,
+// rounds = ceil(workgroups / 256), the K tiles per tile, k_tiles = ceil(K / BK), and the
+// whole launch's tile work spread over the 256 compute units, work = workgroups * k_tiles
+// / 256.  A launch is modelled as
+//     a + b * rounds + g * rounds * k_tiles + h * work   microseconds,
 // a being the fixed cost (launch, first copy, epilogue), g the time of one K tile of one
-// round, and b a cost per round that only the K-split kernel has (each of its rounds ends
-// in a hand-off through LDS; b = 0 elsewhere).  They were fitted per pair by least squares
-// on relative error, all kept >= 0, to the {nfit} shapes measured for this file (the
-// table's {ntable} and {ntrain} seeded shapes outside it).
+// round when the compute units run side by side (the matrix cores bound it), h the time of
+// one K tile of work when the memory system that all compute units share bounds it (a
+// product that streams B, where a partly filled round of workgroups is not cheaper per
+// byte), and b a cost per round that only the K-split kernels have (each of their rounds
+// ends in a hand-off through LDS; b = 0 elsewhere).  They were fitted per pair by least
+// squares on relative error, all kept >= 0, to the {nfit} shapes measured for this file
+// (the table's {ntable} and {ntrain} seeded shapes outside it).
 struct ModelRow {{
   int variant, cfg;
-  double a_us, b_us, g_us;
+  double a_us, b_us, g_us, h_us;
 }};
 
 static const ModelRow kModel[] = {{
@@ -141,7 +150,8 @@ static inline double model_us(const ModelRow& r, int64_t M, int64_t N, int64_t K
   const int64_t tiles = ((M + e.bm - 1) / e.bm) * ((N + e.bn - 1) / e.bn) * wg_factor;
   const int64_t rounds = (tiles + kModelCUs - 1) / kModelCUs;
   const int64_t k_tiles = (K + e.bk - 1) / e.bk;
-  return r.a_us + r.b_us * (double)rounds + r.g_us * (double)rounds * (double)k_tiles;
+  return r.a_us + r.b_us * (double)rounds + r.g_us * (double)rounds * (double)k_tiles +
+         r.h_us * (double)tiles * (double)k_tiles / (double)kModelCUs;
 }}
 
 // The row with the least modelled time (variant 0: any variant), first row on ties.
@@ -248,9 +258,11 @@ static inline TailPick tail_pick(int64_t M, int64_t N, int64_t K, int used, int6
     if (full == 0 || tail == 0) continue;
     const double tail_rounds = (double)((tail * used + kModelCUs - 1) / kModelCUs);
     const double mb = (double)(2 * used + 1) * (double)tail * e.bm * e.bn * 4.0 / 1e6;
+    const double kt = (double)((K + e.bk - 1) / e.bk), kct = (double)((kc + e.bk - 1) / e.bk);
     const double t = r.a_us + r.b_us * ((double)(full / kModelCUs) + tail_rounds) +
-                     r.g_us * ((double)(full / kModelCUs) * (double)((K + e.bk - 1) / e.bk) +
-                               tail_rounds * (double)((kc + e.bk - 1) / e.bk)) +
+                     r.g_us * ((double)(full / kModelCUs) * kt + tail_rounds * kct) +
+                     r.h_us * ((double)full * kt + (double)(tail * used) * kct) /
+                         (double)kModelCUs +
                      kSplitFixedUs + kSplitUsPerMB * mb + kSplitUsPerRound * tail_rounds;
     if (!best.found || t < best.us) best = TailPick{{true, r.variant, r.cfg, full, t}};
   }}
@@ -591,61 +603,60 @@ def model_features(M, N, K, cfg_dims, wg_factor=1, cus=256):
     return -(-tiles // cus) * -(-K // bk)
 
 
-def _fit_pair(xs, ys):
-    """a, g >= 0 minimising sum(((a + g*x) / y - 1)**2)."""
-    p = [1.0 / y for y in ys]
-    q = [x / y for x, y in zip(xs, ys)]
-    spp = sum(v * v for v in p)
-    sqq = sum(v * v for v in q)
-    spq = sum(u * v for u, v in zip(p, q))
-    sp, sq = sum(p), sum(q)
-    cands = []
-    det = spp * sqq - spq * spq
-    if det > 1e-12 * spp * max(sqq, 1e-300):
-        a = (sp * sqq - sq * spq) / det
-        g = (spp * sq - spq * sp) / det
-        if a >= 0 and g >= 0:
-            cands.append((a, g))
-    if sqq > 0:
-        cands.append((0.0, sq / sqq))
-    cands.append((sp / spp, 0.0))
-
-    def obj(ag):
-        return sum(((ag[0] + ag[1] * x) / y - 1.0) ** 2 for x, y in zip(xs, ys))
-    return min(cands, key=obj)
-
-
 def model_rounds(M, N, cfg_dims, wg_factor=1, cus=256):
     bm, bn = cfg_dims[0], cfg_dims[1]
     return -(-(-(-M // bm) * -(-N // bn) * wg_factor) // cus)
 
 
+def model_work(M, N, K, cfg_dims, wg_factor=1, cus=256):
+    """workgroups * k_tiles / 256: the launch's tile work spread over every compute unit."""
+    bm, bn, bk = cfg_dims
+    return -(-M // bm) * -(-N // bn) * wg_factor * -(-K // bk) / cus
+
+
+def model_time(row, M, N, K, cfg_dims, wg_factor=1):
+    """a + b * rounds + g * rounds * k_tiles + h * work of one fitted row."""
+    _v, _c, a, b, g, h = row[:6]
+    return (a + b * model_rounds(M, N, cfg_dims, wg_factor)
+            + g * model_features(M, N, K, cfg_dims, wg_factor)
+            + h * model_work(M, N, K, cfg_dims, wg_factor))
+
+
 def fit_model(rows, cfg_dims):
-    """Per (variant, configuration): (variant id, cfg, a_us, b_us, g_us, median |relative
-    error|) of the cost model a + b * rounds + g * rounds * k_tiles over the measured rows.
-    b is fitted for the K-split kernel only, whose every round of workgroups ends in a
-    hand-off through LDS and a store; it is 0 for the others."""
+    """Per (variant, configuration): (variant id, cfg, a_us, b_us, g_us, h_us, median
+    |relative error|) of the cost model a + b * rounds + g * rounds * k_tiles + h * work over
+    the measured rows, by non-negative least squares on relative error.  b is fitted for
+    the K-split kernels only, whose every round of workgroups ends in a hand-off through LDS
+    and a store; it is 0 for the others."""
     import numpy as np
     from scipy.optimize import nnls
 
     out = []
     ids = IDS
-    keys = sorted(rows[0]["us"], key=lambda k: (ids[k[:2]], int(k[2:])))
+    keys = sorted({k for r in rows for k in r["us"]}, key=lambda k: (ids[k[:2]], int(k[2:])))
     for key in keys:
         cfg = int(key[2:])
+        dims = cfg_dims[cfg][:3]
         have = [r for r in rows if key in r["us"]]
-        xs = [model_features(r["M"], r["N"], r["K"], cfg_dims[cfg][:3]) for r in have]
-        rs = [model_rounds(r["M"], r["N"], cfg_dims[cfg][:3]) for r in have]
-        ys = [r["us"][key] for r in have]
-        if ids[key[:2]] == tdb.VARIANT_KS:
-            X = np.array([[1.0 / y, rr / y, x / y] for x, rr, y in zip(xs, rs, ys)])
-            (a, b, g), _ = nnls(X, np.ones(len(ys)))
-            a, b, g = float(a), float(b), float(g)
-        else:
-            (a, g), b = _fit_pair(xs, ys), 0.0
-        err = statistics.median(abs((a + b * rr + g * x) / y - 1.0)
-                                for x, rr, y in zip(xs, rs, ys))
-        out.append((ids[key[:2]], cfg, a, b, g, err))
+        ks = ids[key[:2]] == tdb.VARIANT_KS
+        X, ys = [], []
+        for r in have:
+            y = r["us"][key]
+            f = [1.0, model_rounds(r["M"], r["N"], dims),
+                 model_features(r["M"], r["N"], r["K"], dims),
+                 model_work(r["M"], r["N"], r["K"], dims)]
+            if not ks:
+                f.pop(1)
+            X.append([v / y for v in f])
+            ys.append(y)
+        coef, _ = nnls(np.array(X), np.ones(len(ys)))
+        coef = [float(c) for c in coef]
+        if not ks:
+            coef.insert(1, 0.0)
+        a, b, g, h = coef
+        err = statistics.median(abs(model_time((0, cfg, a, b, g, h), r["M"], r["N"], r["K"],
+                                               dims) / r["us"][key] - 1.0) for r in have)
+        out.append((ids[key[:2]], cfg, a, b, g, h, err))
     return out
 
 
@@ -657,11 +668,11 @@ def _model_pick_py(M, N, K, model, dims, wg_factor=1):
     """Least modelled (us, variant, cfg) over the fitted rows, as the header computes it
     (a split launch never takes the K-split kernel)."""
     best = None
-    for (v, c, a, b, g, _e) in model:
+    for row in model:
+        v, c = row[0], row[1]
         if wg_factor != 1 and (v == tdb.VARIANT_KS or _one_wave(c)):
             continue
-        t = (a + b * model_rounds(M, N, dims[c][:3], wg_factor)
-             + g * model_features(M, N, K, dims[c][:3], wg_factor))
+        t = model_time(row, M, N, K, dims[c][:3], wg_factor)
         if best is None or t < best[0]:
             best = (t, v, c)
     return best
@@ -690,7 +701,7 @@ def split_features(M, N, K, splits, model, dims):
         rounds = -(-(-(-M // bm) * -(-N // bn) * used) // 256)
         return used, t, [1.0, split_extra_mb(M, N, used), float(rounds)]
     best = None
-    for (v, c, a, b, g, _e) in model:
+    for (v, c, a, b, g, h, _e) in model:
         if v == tdb.VARIANT_KS or _one_wave(c):
             continue
         bm, bn, bk = dims[c][:3]
@@ -700,7 +711,9 @@ def split_features(M, N, K, splits, model, dims):
         if full == 0 or rest == 0:
             continue
         tr = -(-(rest * used) // 256)
-        t = a + b * (full // 256 + tr) + g * (full // 256 * -(-K // bk) + tr * -(-kc // bk))
+        kt, kct = -(-K // bk), -(-kc // bk)
+        t = (a + b * (full // 256 + tr) + g * (full // 256 * kt + tr * kct)
+             + h * (full * kt + rest * used * kct) / 256)
         if best is None or t < best[0]:
             best = (t, [1.0, (2 * used + 1) * rest * bm * bn * 4 / 1e6, float(tr)])
     return (used, best[0], best[1]) if best else None
@@ -708,8 +721,10 @@ def split_features(M, N, K, splits, model, dims):
 
 def fit_split_model(split_results, model, dims):
     """(fixed us, us per extra MB, us per round of workgroups) >= 0 of the split overhead:
-    least squares of what the measured split launches (full and tail) took beyond the
-    modelled GEMM of their chunks."""
+    least squares, on error relative to each launch's measured time, of what the measured
+    split launches (full and tail) took beyond the modelled GEMM of their chunks.  Relative
+    error weighs a small product's second launch as much as a large one's extra traffic:
+    the count is chosen by comparing times, whatever their size."""
     import numpy as np
     from scipy.optimize import nnls
 
@@ -719,8 +734,8 @@ def fit_split_model(split_results, model, dims):
         for sp, us in r["us"].items():
             f = split_features(M, N, K, int(sp), model, dims)
             if f is not None and f[0] > 1:
-                X.append(f[2])
-                y.append(us - f[1])
+                X.append([v / us for v in f[2]])
+                y.append((us - f[1]) / us)
     coef, _ = nnls(np.array(X), np.array(y))
     return tuple(float(c) for c in coef)
 
@@ -857,10 +872,11 @@ def write_header(results, device, rounds, batches, batch_ms, path=None, split_re
     dims = config_dims()
     model = fit_model(fit_rows, dims)
     # round as written, so that the split fit sees the model the library will use
-    model = [(v, c, round(a, 4), round(b, 4), round(g, 5), e)
-             for (v, c, a, b, g, e) in model]
-    mrows = [f"    {{{v}, {c}, {a:.4f}, {b:.4f}, {g:.5f}}},  // median |error| {100 * e:.1f}%"
-             for (v, c, a, b, g, e) in model]
+    model = [(v, c, round(a, 4), round(b, 4), round(g, 5), round(h, 5), e)
+             for (v, c, a, b, g, h, e) in model]
+    mrows = [f"    {{{v}, {c}, {a:.4f}, {b:.4f}, {g:.5f}, {h:.5f}}},  "
+             f"// median |error| {100 * e:.1f}%"
+             for (v, c, a, b, g, h, e) in model]
     r0, per_mb, per_round = (fit_split_model(split_results, model, dims) if split_results
                              else (3.0, 0.3, 1.0))
     choices = sorted({int(k) for r in (split_results or []) for k in r["us"] if int(k) > 0}) or [1]
@@ -898,6 +914,9 @@ def main(argv=None) -> int:
     ap.add_argument("--holdout-splitk", type=int, default=0, metavar="N",
                     help="time every split count on N seeded skinny shapes and report how "
                          "far gemm_f32_splitk_select is from the fastest")
+    ap.add_argument("--no-split", action="store_true",
+                    help="measure the table and training shapes only (the split study can "
+                         "follow with --split-only on the --out file)")
     ap.add_argument("--split-only", default=None, metavar="BASE_JSON",
                     help="re-measure only the split study; the table and training rows "
                          "come from an earlier --out file")
@@ -958,10 +977,10 @@ def main(argv=None) -> int:
                           log=lambda *a: print(*a, flush=True))
         train = measure(train_shapes(), args.rounds, args.batches, args.batch_ms,
                         log=lambda *a: print(*a, flush=True))
-    splits = split_study(SPLIT_SHAPES + TAIL_SHAPES
-                         + skinny_shapes(SPLIT_TRAIN_COUNT, SPLIT_TRAIN_SEED),
-                         rounds=args.rounds, batches=args.batches, batch_ms=args.batch_ms,
-                         log=lambda *a: print(*a, flush=True))
+    splits = [] if args.no_split else split_study(
+        SPLIT_SHAPES + TAIL_SHAPES + skinny_shapes(SPLIT_TRAIN_COUNT, SPLIT_TRAIN_SEED),
+        rounds=args.rounds, batches=args.batches, batch_ms=args.batch_ms,
+        log=lambda *a: print(*a, flush=True))
     data = {"device": device, "rounds": args.rounds, "batches": args.batches,
             "batch_ms": args.batch_ms, "library": tdb.gemm_f32_version(),
             "seconds": time.time() - t0, "results": results, "train": train,
