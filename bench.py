@@ -8,7 +8,8 @@ tdb_inputs, resident in HBM before timing starts; C is preallocated.
 
 Prints ONE JSON line:
   value         whole-job TFLOP/s = 2*M*N*K / (host-wall time per step), K timed steps
-                bracketed by torch.cuda.synchronize()
+                bracketed by torch.cuda.synchronize(), after at least 200 ms of untimed
+                launches and the W warm-up steps
   roofline      FP32 MFMA bound: algorithmic FLOP per launch / average launch duration
                 from HIP events on the launch stream, against the 157.3 TFLOP/s peak;
                 `traffic` = HBM bytes per launch from the committed rocprofv3 counter
@@ -16,30 +17,52 @@ Prints ONE JSON line:
   cpu_baseline  the CPU oracle timed on a bounded row sample of the same product
   mfma_ceiling  the matrix-core ceiling at the clock the device sustains (a kernel of
                 nothing but FP32 MFMAs) and the headline's fraction of it
+  telemetry     amd-smi samples of clocks and power taken across a window of >= 1 s in
+                which the GPU runs headline launches without a gap, with their medians
   per_shape     single-buffered, double-buffered, multi-stage and dispatched time for
-                every workload shape, with torch.matmul (FP32, black box) as context
-  parity        the 8192^3 result checked on 4096 seeded positions against the oracle
+                every workload shape, a single- against double-buffered pair on one
+                multi-wave tile, with torch.matmul (FP32, black box) as context; the
+                protocol of the LuisaCompute note by default (4 rotated rounds of 9 batches
+                of >= 40 ms, medians of the per-round medians)
+  parity        the timed 8192^3 output on 4096 seeded positions, and every per-shape
+                variant's output once per round, against the oracle.  Any check above the
+                bound (or one that could not run) sets "parity_ok": false and the exit
+                status to 3: no throughput is published for a wrong product.
 
 Also:
   python bench.py --oracle-table             the CPU oracle's time per workload on all host
                                              threads and on one (no GPU needed)
-  python bench.py --summarize-trace DIR      per-(kernel, grid) average durations from a
-                                             rocprofv3 kernel trace (kernel_trace.csv)
+  python bench.py --summarize-trace DIR      per-(kernel, grid) median, minimum, mean and
+                                             maximum durations from a rocprofv3 kernel trace
+                                             (kernel_trace.csv), and the median without the
+                                             first launches of each group
   python bench.py --summarize-counters DIR   per-(kernel, grid) average counter values
                                              from rocprofv3 --pmc runs (counter_collection.csv)
+  python bench.py --layer-shapes             decode and layer products (1 to 4096 rows
+                                             against 4096- and 11008-wide layers): gemm_f32,
+                                             the 16-row K-split kernel, both split-K entry
+                                             points and torch.matmul, each output checked
+  python bench.py --k-slope                  1024 x 1024 x K for K = 32 .. 2048 on the 1024^3
+                                             kernels: the fixed cost of a launch and the time
+                                             per K tile against the matrix-core time per K tile
   --copy-calibration MIB                     first run one streaming elementwise kernel
                                              (negate) that reads MIB MiB and writes MIB MiB;
                                              its FETCH_SIZE / WRITE_SIZE readings calibrate
                                              the GEMM's HBM byte counts
-  python bench.py --counter-run              a few SB, DB and MS launches per
-                                             metric shape (1024^3, 4096^3, 8192^3) plus the
-                                             calibration kernel: the program that the
-                                             rocprofv3 --pmc passes profile
-  python bench.py --counter-run-skinny       the K-split kernel at 16x4096x4096 and, with
-                                             the same per-wave work, the 64x64x32 DB tile at
-                                             1024^3 (three launches each), plus the
-                                             calibration kernel: the program of the K-split
-                                             kernel's counter passes
+  python bench.py --counter-run              a few SB, DB, MS and dispatched launches per
+                                             metric shape (1024^3, 4096^3, 8192^3), the row
+                                             shard and a decode shape, plus the calibration
+                                             kernel: the program that the rocprofv3 --pmc
+                                             passes profile
+  python bench.py --raster-run               the headline product three times under each
+                                             workgroup order (GEMMF32_RASTER group heights 1
+                                             to 32, with and without the XCD renumbering),
+                                             after the calibration kernel: the program of the
+                                             raster traffic passes; --raster-time times the
+                                             same orders (events, no profiler)
+  python bench.py --write-raster-traffic FETCH_DIR WRITE_DIR TIME_JSON
+                                             HBM bytes and time per workgroup order of the
+                                             headline kernel
   python bench.py --write-traffic FETCH_DIR WRITE_DIR
                                              HBM bytes per launch of the headline kernel from
                                              a FETCH_SIZE pass and a WRITE_SIZE pass of
@@ -67,6 +90,15 @@ METRIC = "FP32 GEMM TFLOP/s and % of MFMA FP32 peak at 1024³/4096³/8192³, 1 G
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_8192.json")
 HEADLINE = "square_8192"
 VARIANT_NAMES = {1: "sb", 2: "db", 3: "ms", 5: "ks"}
+PREWARM_S = 0.2                        # untimed launches before the warm-up steps
+
+# Decode and layer products: a batch of rows against a 4096 x 4096, 4096 x 11008 or
+# 11008 x 4096 weight matrix.  The pages name only the regime ("the regime LLM decode
+# lives in"); the widths are those of a common 7-billion-parameter transformer layer.
+LAYER_SHAPES = [(1, 4096, 4096), (8, 4096, 4096), (16, 4096, 4096), (16, 11008, 4096),
+                (16, 4096, 11008), (128, 4096, 4096), (128, 11008, 4096), (128, 4096, 11008),
+                (512, 4096, 4096), (512, 4096, 11008), (4096, 4096, 4096),
+                (4096, 11008, 4096)]
 
 
 def kernel_source_hash() -> str:
@@ -79,24 +111,44 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def summarize_trace(d: str) -> int:
-    """Average kernel duration per (kernel name, grid size) from rocprofv3's CSV trace."""
+# ------------------------------------------------------------------ profile summaries
+def trace_groups(d: str):
+    """Kernel durations (ns) per (kernel name, grid size), in launch order, from
+    rocprofv3's CSV kernel trace under d."""
     files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
-    if not files:
-        print(f"no kernel_trace.csv under {d}", file=sys.stderr)
-        return 1
     groups = {}
     for fn in files:
         with open(fn) as f:
             for row in csv.DictReader(f):
                 name = row.get("Kernel_Name", "")
                 grid = row.get("Grid_Size", row.get("Grid_Size_X", ""))
-                dur = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
-                groups.setdefault((name, grid), []).append(dur)
-    print(f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}  grid  kernel")
+                start = int(row["Start_Timestamp"])
+                dur = int(row["End_Timestamp"]) - start
+                groups.setdefault((name, grid), []).append((start, dur))
+    return {k: [d for _, d in sorted(v)] for k, v in groups.items()}, bool(files)
+
+
+def steady(durs):
+    """The launches of a group after its first tenth (at least one launch dropped when
+    there are more than two): those ramp the clock up from idle."""
+    skip = max(1, len(durs) // 10) if len(durs) > 2 else 0
+    return durs[skip:]
+
+
+def summarize_trace(d: str) -> int:
+    """Median, minimum, mean and maximum kernel duration per (kernel, grid size) from
+    rocprofv3's CSV trace, and the median of the steady launches (the first tenth of each
+    group dropped)."""
+    groups, found = trace_groups(d)
+    if not found:
+        print(f"no kernel_trace.csv under {d}", file=sys.stderr)
+        return 1
+    print(f"{'calls':>6} {'median_us':>10} {'steady_us':>10} {'min_us':>10} {'mean_us':>10} "
+          f"{'max_us':>10}  grid  kernel")
     for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        print(f"{len(v):6d} {statistics.mean(v)/1e3:10.2f} {min(v)/1e3:10.2f} "
-              f"{max(v)/1e3:10.2f}  {grid}  {name[:150]}")
+        print(f"{len(v):6d} {statistics.median(v)/1e3:10.2f} "
+              f"{statistics.median(steady(v))/1e3:10.2f} {min(v)/1e3:10.2f} "
+              f"{statistics.mean(v)/1e3:10.2f} {max(v)/1e3:10.2f}  {grid}  {name[:150]}")
     return 0
 
 
@@ -142,23 +194,38 @@ def _per_dispatch(rows, counter, match):
     return (statistics.mean(per.values()), len(per)) if per else (None, 0)
 
 
+def _kernel_match(tdb, M, N, K):
+    """(description, predicate on (kernel name, grid size)) for the dispatched kernel of a
+    shape."""
+    _, variant, cfg = tdb.gemm_f32_select(M, N, K)
+    _, info = tdb.gemm_f32_config_info(cfg)
+    threads = info["threads"] * (tdb.gemm_f32_config_ks(cfg) if variant == tdb.VARIANT_KS else 1)
+    grid = str(((M + info["BM"] - 1) // info["BM"]) * ((N + info["BN"] - 1) // info["BN"])
+               * threads)
+    if variant == tdb.VARIANT_KS and tdb.gemm_f32_config_variants(cfg) == 1 << variant:
+        kname, tag, flag = "gemm_f32_ks16_kernel", "Ks16Cfg<", ""
+    else:
+        tag = f"TileCfg<{info['BM']}, {info['BN']}, {info['BK']},"
+        if variant == tdb.VARIANT_MS:
+            kname = "gemm_f32_ms_kernel"
+            flag = ">, %d>" % tdb.gemm_f32_config_ms(cfg)[1]["stages"]
+        elif variant == tdb.VARIANT_KS:
+            kname, flag = "gemm_f32_ks_kernel", ">, %d>" % tdb.gemm_f32_config_ks(cfg)
+        else:
+            kname, flag = "gemm_f32_tile_kernel", ", %d>" % variant  # loop kind = variant id
+    desc = f"{VARIANT_NAMES[variant]} cfg{cfg} {info['BM']}x{info['BN']}x{info['BK']}"
+
+    def match(name, g):
+        return kname in name and tag in name and flag in name and g == grid
+    return desc, match
+
+
 def write_traffic(fetch_dir: str, write_dir: str, calib_mib: int = 512) -> int:
     import tdb_inputs as ti
     import tiled_double_buffered_amd as tdb
 
     M, N, K, _ = ti.WORKLOADS[HEADLINE]
-    _, variant, cfg = tdb.gemm_f32_select(M, N, K)
-    _, info = tdb.gemm_f32_config_info(cfg)
-    grid = str(((M + info["BM"] - 1) // info["BM"]) * ((N + info["BN"] - 1) // info["BN"])
-               * info["threads"])
-    tag = f"TileCfg<{info['BM']}, {info['BN']}, {info['BK']},"
-    if variant == tdb.VARIANT_MS:
-        kname, flag = "gemm_f32_ms_kernel", ">, %d>" % tdb.gemm_f32_config_ms(cfg)[1]["stages"]
-    else:
-        kname, flag = "gemm_f32_tile_kernel", ", %d>" % variant  # loop kind = variant id
-
-    def is_gemm(name, g):
-        return kname in name and tag in name and flag in name and g == grid
+    desc, is_gemm = _kernel_match(tdb, M, N, K)
 
     def is_calib(name, g):
         return "neg" in name.lower() and "gemm" not in name
@@ -179,8 +246,7 @@ def write_traffic(fetch_dir: str, write_dir: str, calib_mib: int = 512) -> int:
     algo = 4.0 * (M * K + K * N + M * N)
     out = {
         "workload": HEADLINE,
-        "kernel": f"{VARIANT_NAMES[variant]} cfg{cfg} "
-                  f"{info['BM']}x{info['BN']}x{info['BK']}",
+        "kernel": desc,
         "kernel_source_sha256": kernel_source_hash(),
         "fetch_kib_per_launch_raw": g_fetch, "write_kib_per_launch_raw": g_write,
         "dispatches": [nf, nw],
@@ -206,75 +272,453 @@ def write_traffic(fetch_dir: str, write_dir: str, calib_mib: int = 512) -> int:
     return 0
 
 
+# ------------------------------------------------------------------ shared helpers
+def _calibration_copy(torch, dev, mib):
+    """One streaming kernel that reads and writes exactly `mib` MiB (torch negate)."""
+    if mib <= 0:
+        return
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _prewarm(torch, fn, seconds=PREWARM_S):
+    """Untimed launches of `fn` for at least `seconds`: the shader clock ramps from idle to
+    its sustained value over some tens of milliseconds of load."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        fn()
+        torch.cuda.synchronize()
+
+
+def _cfg_waves(tdb, cfg):
+    return tdb.gemm_f32_config_info(cfg)[1]["threads"] // 64
+
+
+def _cfg_name(tdb, cfg):
+    _, i = tdb.gemm_f32_config_info(cfg)
+    return f"{i['BM']}x{i['BN']}x{i['BK']}/{i['threads'] // 64} waves"
+
+
+def _pair_cfg(tdb, sb_cfg, db_cfg):
+    """A tile configuration with at least two waves on which the single- and
+    double-buffered loops keep their two and one barriers per K tile: the double-buffered
+    column's, else the single-buffered column's, else 64 x 64 x 32 (four waves).  With one
+    wave the compiler drops every barrier, so such a pair would compare two barrier-free
+    loops."""
+    for c in (db_cfg, sb_cfg):
+        if _cfg_waves(tdb, c) >= 2:
+            return c
+    for c in range(tdb.gemm_f32_num_configs()):
+        _, i = tdb.gemm_f32_config_info(c)
+        if (i["BM"], i["BN"], i["BK"], i["threads"]) == (64, 64, 32, 256):
+            return c
+    raise RuntimeError("no 64x64x32 four-wave configuration")
+
+
+def _timer(torch, stream):
+    """time_call(fn, target_ms, batches) -> (event us median, host-wall us median, event us
+    min, event us max) over `batches` batches of back-to-back launches of >= target_ms."""
+    def time_call(fn, target_ms, batches):
+        fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        one = max(time.perf_counter() - t, 1e-6)
+        reps = int(min(5000, max(3, target_ms * 1e-3 / one)))
+        for _ in range(min(reps, 10)):
+            fn()
+        res = []
+        for _ in range(batches):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            h0 = time.perf_counter()
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            h1 = time.perf_counter()
+            res.append((a.elapsed_time(b) * 1e3 / reps, (h1 - h0) * 1e6 / reps))
+        ev = statistics.median(x[0] for x in res)
+        wall_us = statistics.median(x[1] for x in res)
+        return ev, wall_us, min(x[0] for x in res), max(x[0] for x in res)
+    return time_call
+
+
+class CpuLeg:
+    """The CPU leg of the bench: the oracle (test infrastructure) timed as a baseline and
+    used to check the outputs the bench times.  Nothing the bench measures runs through
+    it."""
+
+    def __init__(self):
+        try:
+            import oracle
+            self.oracle = oracle
+            self.error = None
+        except Exception as exc:  # reported; every check then fails the parity gate
+            self.oracle = None
+            self.error = repr(exc)
+
+    def full_or_sampled(self, torch, dev, ti, m, n, k, seed, a_h, b_h):
+        """A checker C -> max |C - C64| / (1e-5 Bnd + 1e-6): the full output up to 4096^3
+        multiply-adds, else the workload's 4096 seeded positions."""
+        if self.oracle is None:
+            err = self.error
+            return lambda C: {"error": err}
+        o = self.oracle
+        if m * n * k <= 4096 ** 3:
+            c64, bnd = o.gemm_f64(a_h, b_h)
+            return lambda C: o.tolerance_ratio(C.cpu().numpy(), c64, bnd)
+        return self.sampled(torch, dev, ti, m, n, seed, a_h, b_h)
+
+    def sampled(self, torch, dev, ti, m, n, seed, a_h, b_h, count=4096):
+        if self.oracle is None:
+            err = self.error
+            return lambda C: {"error": err}
+        o = self.oracle
+        ri, rj = ti.sample_positions(seed, m, n, count)
+        c64, bnd = o.gemm_f64_sampled(a_h, b_h, ri, rj)
+        ii, jj = torch.from_numpy(ri).to(dev), torch.from_numpy(rj).to(dev)
+        return lambda C: o.tolerance_ratio(C[ii, jj].cpu().numpy(), c64, bnd)
+
+    def baseline(self, A_h, B_h, seconds):
+        """The oracle, untuned, on successive row blocks of the product until `seconds` of
+        CPU time are spent (the block size from a pilot block, so the last one overshoots
+        little)."""
+        o = self.oracle
+        if o is None:
+            return {"error": self.error}
+        M, K = A_h.shape
+        N = B_h.shape[1]
+        threads = o.max_threads()
+        t = time.perf_counter()
+        o.gemm_f64(A_h[:threads], B_h)
+        pilot = time.perf_counter() - t
+        block = int(min(M, max(threads, threads * round(seconds / 8 / pilot))))
+        rows, dt = 0, 0.0
+        while rows < M and dt < seconds:
+            r1 = min(M, rows + block)
+            t = time.perf_counter()
+            o.gemm_f64(A_h[rows:r1], B_h)
+            dt += time.perf_counter() - t
+            rows = r1
+        tflops = 2.0 * rows * N * K / dt / 1e12
+        return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": threads,
+                "kind": "oracle",
+                "sample": f"first {rows} rows of the {M}x{N}x{K} product (C64 and Bnd in FP64, "
+                          f"{dt:.1f} s); full product extrapolates to "
+                          f"{2.0 * M * N * K / (tflops * 1e12):.0f} s",
+                "cpu": _cpu_model()}
+
+
+def _ratio_ok(r) -> bool:
+    """A check passed: a number (not an error record, not NaN) at most 1."""
+    return isinstance(r, float) and r <= 1.0
+
+
+def line_parity_ok(line) -> bool:
+    """The gate on a bench line: the timed headline output passed its check, and every
+    per-shape output of the library (every column but torch.matmul's) carries a recorded
+    ratio of at most 1.  A missing or failed check fails the gate."""
+    if not (isinstance(line.get("parity"), dict) and line["parity"].get("pass") is True):
+        return False
+    for entry in line.get("per_shape", {}).values():
+        for v in ("sb", "db", "ms", "dispatch", "pair_sb", "pair_db"):
+            r = entry.get(v, {}).get("max_err_over_bound")
+            if not _ratio_ok(r):
+                return False
+    return True
+
+
+# ------------------------------------------------------------------ counter programs
 def counter_run(calib_mib: int) -> int:
-    """A short program for counter passes: a few launches of each variant (dispatch-table
-    configurations) at the three metric shapes."""
+    """A short program for counter passes: three launches each of the single-, double-
+    buffered and multi-stage kernels (dispatch-table configurations) and of the dispatched
+    one at the three metric shapes, then the dispatched kernel at the row shard
+    (1024 x 8192 x 8192) and at the decode shape 16 x 4096 x 4096."""
     import torch
 
     import tdb_inputs as ti
     import tiled_double_buffered_amd as tdb
 
     dev = torch.device("cuda:0")
-    if calib_mib > 0:
-        n = calib_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+    _calibration_copy(torch, dev, calib_mib)
     s_ptr = torch.cuda.current_stream(dev).cuda_stream
-    for name in ("square_1024", "square_4096", "square_8192"):
-        M, N, K, seed = ti.WORKLOADS[name]
+    runs = [(name, (tdb.gemm_f32_sb, tdb.gemm_f32_db, tdb.gemm_f32_ms, tdb.gemm_f32))
+            for name in ("square_1024", "square_4096", "square_8192")]
+    runs += [("shard_1024x8192x8192", (tdb.gemm_f32,)), ((16, 4096, 4096, 7101), (tdb.gemm_f32,))]
+    for name, fns in runs:
+        M, N, K, seed = ti.WORKLOADS[name] if isinstance(name, str) else name
         a, b = ti.workload_inputs(M, N, K, seed)
         A, B = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
         C = torch.empty((M, N), device=dev)
-        for fn in (tdb.gemm_f32_sb, tdb.gemm_f32_db, tdb.gemm_f32_ms):
+        for fn in fns:
             for _ in range(3):
                 rc = fn(M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N, s_ptr)
                 if rc != tdb.OK:
                     raise tdb.GemmError(rc, fn.__name__)
         torch.cuda.synchronize()
-        print(f"[counter-run] {name} done", file=sys.stderr, flush=True)
+        print(f"[counter-run] {M}x{N}x{K} done", file=sys.stderr, flush=True)
         del A, B, C
     return 0
 
 
-def counter_run_skinny(calib_mib: int) -> int:
-    """A short program for counter passes of the K-split kernel: three launches at
-    16 x 4096 x 4096 (variant KS, configuration 13) and three of the 64 x 64 x 32 DB tile
-    (configuration 6) at 1024^3, whose four waves each walk the same 32 K tiles of one
-    32 x 32 block."""
+RASTER_SETTINGS = ["8", "1", "2", "4", "16", "32", "8,noxcd", "1,noxcd"]
+
+
+def _headline_operands(torch, dev):
+    import tdb_inputs as ti
+    M, N, K, seed = ti.WORKLOADS[HEADLINE]
+    a, b = ti.workload_inputs(M, N, K, seed)
+    return (M, N, K, torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev),
+            torch.empty((M, N), device=dev))
+
+
+def raster_run(calib_mib: int, timed: bool, args=None) -> int:
+    """The headline product under each workgroup order: three launches per order for the
+    counter passes, or (timed) the per-order time from HIP events."""
     import torch
 
-    import tdb_inputs as ti
     import tiled_double_buffered_amd as tdb
 
     dev = torch.device("cuda:0")
-    if calib_mib > 0:
-        n = calib_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-    s_ptr = torch.cuda.current_stream(dev).cuda_stream
-    for (M, N, K, variant, cfg, seed) in [(16, 4096, 4096, tdb.VARIANT_KS, 13, 7101),
-                                          (1024, 1024, 1024, tdb.VARIANT_DB, 6, 7102)]:
-        a, b = ti.workload_inputs(M, N, K, seed)
-        A, B = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
-        C = torch.empty((M, N), device=dev)
-        for _ in range(3):
-            rc = tdb.gemm_f32_ex(M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N,
-                                 variant, cfg, s_ptr)
-            if rc != tdb.OK:
-                raise tdb.GemmError(rc, "gemm_f32_ex")
-        torch.cuda.synchronize()
-        print(f"[counter-run-skinny] {M}x{N}x{K} variant {variant} cfg {cfg} done",
-              file=sys.stderr, flush=True)
-        del A, B, C
+    _calibration_copy(torch, dev, calib_mib)
+    stream = torch.cuda.current_stream(dev)
+    s_ptr = stream.cuda_stream
+    M, N, K, A, B, C = _headline_operands(torch, dev)
+
+    def step():
+        rc = tdb.gemm_f32(M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N, s_ptr)
+        if rc != tdb.OK:
+            raise tdb.GemmError(rc, "gemm_f32")
+    out = {}
+    time_call = _timer(torch, stream)
+    if timed:
+        _prewarm(torch, step)
+    rounds = args.rounds if (timed and args) else 1
+    for r in range(rounds):
+        order = RASTER_SETTINGS[r % len(RASTER_SETTINGS):] + RASTER_SETTINGS[:r % len(RASTER_SETTINGS)]
+        for setting in (order if timed else RASTER_SETTINGS):
+            os.environ["GEMMF32_RASTER"] = setting  # read by the library at every launch
+            if timed:
+                out.setdefault(setting, []).append(
+                    time_call(step, args.batch_ms, args.batches)[0])
+            else:
+                for _ in range(3):
+                    step()
+                torch.cuda.synchronize()
+            print(f"[raster] {setting} done", file=sys.stderr, flush=True)
+    os.environ.pop("GEMMF32_RASTER", None)
+    if timed:
+        print(json.dumps({s: round(statistics.median(v), 2) for s, v in out.items()}),
+              flush=True)
     return 0
 
 
+def write_raster_traffic(fetch_dir, write_dir, time_json, calib_mib=512) -> int:
+    """Per workgroup order of the headline kernel: calibrated HBM read and write bytes per
+    launch (the order's three dispatches, in launch order) and its time."""
+    import tdb_inputs as ti
+    import tiled_double_buffered_amd as tdb
+
+    M, N, K, _ = ti.WORKLOADS[HEADLINE]
+    desc, is_gemm = _kernel_match(tdb, M, N, K)
+
+    def is_calib(name, g):
+        return "neg" in name.lower() and "gemm" not in name
+
+    def per_dispatch(rows, counter, match):
+        per = {}
+        for r in rows:
+            if r.get("Counter_Name") == counter and match(r.get("Kernel_Name", ""),
+                                                          r.get("Grid_Size", "")):
+                d = int(r["Dispatch_Id"])
+                per[d] = per.get(d, 0.0) + float(r["Counter_Value"])
+        return [per[d] for d in sorted(per)]
+
+    fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    gf, gw = per_dispatch(fr, "FETCH_SIZE", is_gemm), per_dispatch(wr, "WRITE_SIZE", is_gemm)
+    cf, cw = per_dispatch(fr, "FETCH_SIZE", is_calib), per_dispatch(wr, "WRITE_SIZE", is_calib)
+    n = len(RASTER_SETTINGS)
+    if len(gf) != 3 * n or len(gw) != 3 * n or not cf or not cw:
+        print(f"unexpected dispatch counts: {len(gf)} {len(gw)} {len(cf)} {len(cw)}",
+              file=sys.stderr)
+        return 1
+    sf, sw = calib_mib * 1024.0 / cf[0], calib_mib * 1024.0 / cw[0]
+    with open(time_json) as f:
+        times = json.load(f)
+    algo = 4.0 * (M * K + K * N + M * N)
+    print(f"# HBM traffic and time of the headline kernel ({desc}, {M}x{N}x{K}) per "
+          "workgroup order")
+    print(f"# bytes = counter KiB x 1024 x calibration factor (read {sf:.4f}, write {sw:.4f}: "
+          f"{calib_mib} MiB over the negate kernel's readings); algorithmic {algo / 1e9:.3f} GB")
+    print(f"{'GEMMF32_RASTER':>16} {'read_GB':>8} {'write_GB':>9} {'total/algo':>10} "
+          f"{'us':>9}")
+    for i, setting in enumerate(RASTER_SETTINGS):
+        rd = statistics.median(gf[3 * i:3 * i + 3]) * 1024 * sf
+        wt = statistics.median(gw[3 * i:3 * i + 3]) * 1024 * sw
+        print(f"{setting:>16} {rd / 1e9:8.3f} {wt / 1e9:9.3f} {(rd + wt) / algo:10.2f} "
+              f"{times.get(setting, float('nan')):9.1f}")
+    return 0
+
+
+# ------------------------------------------------------------------ other modes
+def _stream_setup():
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("this mode needs a GPU")
+    torch.backends.cuda.matmul.allow_tf32 = False
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    return torch, dev, stream
+
+
+def layer_shapes(args) -> int:
+    """Decode and layer products through every entry point that can run them, each output
+    checked on 4096 seeded positions (one JSON line)."""
+    torch, dev, stream = _stream_setup()
+    import tdb_inputs as ti
+    import tiled_double_buffered_amd as tdb
+
+    s_ptr = stream.cuda_stream
+    time_call = _timer(torch, stream)
+    cpu = CpuLeg()
+    ks16 = [c for c in range(tdb.gemm_f32_num_configs())
+            if tdb.gemm_f32_config_variants(c) == 1 << tdb.VARIANT_KS]
+    rows, ok = [], True
+    for i, (M, N, K) in enumerate(LAYER_SHAPES):
+        seed = 9001 + i
+        a_h, b_h = ti.workload_inputs(M, N, K, seed)
+        A, B = torch.from_numpy(a_h).to(dev), torch.from_numpy(b_h).to(dev)
+        C = torch.zeros((M, N), dtype=torch.float32, device=dev)
+        check = cpu.sampled(torch, dev, ti, M, N, seed, a_h, b_h)
+        pa, pb, pc = A.data_ptr(), B.data_ptr(), C.data_ptr()
+        splits = tdb.gemm_f32_splitk_select(M, N, K)
+        need = tdb.gemm_f32_splitk_workspace(M, N, K, splits)
+        ws = torch.empty(max(need, 1), dtype=torch.float32, device=dev)
+        fns = {"gemm_f32": lambda: tdb.gemm_f32(M, N, K, pa, K, pb, N, pc, N, s_ptr),
+               "splitk": lambda: tdb.gemm_f32_splitk(M, N, K, pa, K, pb, N, pc, N, splits,
+                                                     ws.data_ptr(), ws.numel(), s_ptr)}
+        if need <= tdb.SCRATCH_FLOATS:
+            fns["splitk_noalloc"] = lambda: tdb.gemm_f32_splitk_noalloc(
+                M, N, K, pa, K, pb, N, pc, N, splits, s_ptr)
+        if ks16 and M <= 32:
+            c16 = ks16[0]
+            fns["ks16"] = lambda: tdb.gemm_f32_ex(M, N, K, pa, K, pb, N, pc, N,
+                                                  tdb.VARIANT_KS, c16, s_ptr)
+        fns["torch"] = lambda: torch.matmul(A, B, out=C)
+        _prewarm(torch, fns["gemm_f32"], 0.05)
+        row = {"M": M, "N": N, "K": K, "splits": splits,
+               "b_read_floor_us": round(4.0 * K * N / 8e12 * 1e6, 2)}
+        _, v, c = tdb.gemm_f32_select(M, N, K)
+        row["gemm_f32_kernel"] = f"{VARIANT_NAMES[v]} cfg{c}"
+        times = {name: [] for name in fns}
+        for r in range(args.rounds):
+            names = list(fns)
+            rot = r % len(names)
+            for name in names[rot:] + names[:rot]:
+                times[name].append(time_call(fns[name], args.batch_ms, args.batches)[0])
+        for name, fn in fns.items():
+            row[name] = {"us": round(statistics.median(times[name]), 2)}
+            if name != "torch":
+                C.fill_(float("nan"))
+                rc = fn()
+                torch.cuda.synchronize()
+                ratio = check(C) if rc == tdb.OK else {"error": tdb.gemm_f32_strerror(rc)}
+                row[name]["max_err_over_bound"] = ratio
+                ok = ok and _ratio_ok(ratio)
+        print(f"[layer] {M}x{N}x{K}: " + ", ".join(f"{n} {row[n]['us']} us" for n in fns),
+              file=sys.stderr, flush=True)
+        rows.append(row)
+        del A, B, C, ws
+    print(json.dumps({"layer_shapes": rows, "parity_ok": ok,
+                      "protocol": f"{args.rounds} rotated rounds x {args.batches} batches of "
+                                  f">= {args.batch_ms} ms, event time, medians"}), flush=True)
+    return 0 if ok else 3
+
+
+def k_slope(args) -> int:
+    """Time 1024 x 1024 x K on the dispatched 1024^3 kernel and on the double-buffered
+    kernel of the same tile, K = 32 .. 2048, and fit t = a + b * k_tiles over K >= 128:
+    `a` is what a launch costs besides its K tiles (dispatch, the first tile's latency, the
+    epilogue, the gap to the next launch), `b` the time per K tile, set against the
+    matrix-core time of one K tile at the clock the ceiling probe measures.  Also times a
+    1 x 1 x 1 product, the cost of a launch that does nearly nothing."""
+    torch, dev, stream = _stream_setup()
+    import tdb_inputs as ti
+    import tiled_double_buffered_amd as tdb
+    from tiled_double_buffered_amd import peak
+
+    s_ptr = stream.cuda_stream
+    time_call = _timer(torch, stream)
+    M = N = 1024
+    ks = [32, 64, 128, 256, 512, 1024, 2048]
+    lda = max(ks)
+    a_h, b_h = ti.workload_inputs(M, N, lda, 3101)
+    A = torch.from_numpy(a_h).to(dev)
+    B = torch.from_numpy(b_h).to(dev)
+    C = torch.empty((M, N), device=dev)
+    _, v0, c0 = tdb.gemm_f32_select(M, N, 1024)
+    kernels = [(v0, c0)]
+    if v0 != tdb.VARIANT_DB and tdb.gemm_f32_config_variants(c0) & (1 << tdb.VARIANT_DB):
+        kernels.append((tdb.VARIANT_DB, c0))
+    ceiling = peak.mfma_ceiling(stream=stream)
+    clock = ceiling["clock_ghz"]
+    out = {"M": M, "N": N, "ceiling": ceiling, "kernels": []}
+    for (v, c) in kernels:
+        _, info = tdb.gemm_f32_config_info(c)
+        waves = info["threads"] // 64
+        # Matrix-core time of one K tile of the whole product: each wave's 32 x 32 blocks
+        # take BK / 2 MFMAs of 64 clocks each per K tile, a SIMD runs its waves' MFMAs one
+        # after another, and the tiles spread over 256 compute units in rounds.
+        tiles = (M // info["BM"]) * (N // info["BN"])
+        rounds = -(-tiles // 256)
+        mfma_per_wave = (info["BM"] * info["BN"] // 1024) // waves * info["BK"] // 2
+        waves_per_simd = -(-waves // 4)
+        tile_us = rounds * waves_per_simd * mfma_per_wave * 64 / (clock * 1e3)
+        pts = []
+        for K in ks:
+            def fn(K=K):
+                return tdb.gemm_f32_ex(M, N, K, A.data_ptr(), lda, B.data_ptr(), N,
+                                       C.data_ptr(), N, v, c, s_ptr)
+            _prewarm(torch, fn, 0.05)
+            us = statistics.median(time_call(fn, args.batch_ms, args.batches)[0]
+                                   for _ in range(args.rounds))
+            pts.append((K, K // info["BK"], us))
+            print(f"[k-slope] {VARIANT_NAMES[v]} cfg{c} K={K}: {us:.2f} us", file=sys.stderr,
+                  flush=True)
+        fit = [(kt, us) for K, kt, us in pts if K >= 128]
+        n = len(fit)
+        mx = sum(x for x, _ in fit) / n
+        my = sum(y for _, y in fit) / n
+        b = sum((x - mx) * (y - my) for x, y in fit) / sum((x - mx) ** 2 for x, _ in fit)
+        a = my - b * mx
+        out["kernels"].append({
+            "kernel": f"{VARIANT_NAMES[v]} cfg{c} {_cfg_name(tdb, c)}",
+            "points_us": {str(K): round(us, 3) for K, _, us in pts},
+            "fixed_us": round(a, 3), "per_k_tile_us": round(b, 4),
+            "mfma_per_k_tile_us": round(tile_us, 4),
+            "loop_fraction_of_mfma": round(tile_us / b, 4),
+            "mfma_us_at_k1024": round(tile_us * (1024 // info["BK"]), 3)})
+
+    def tiny():
+        return tdb.gemm_f32_ex(1, 1, 1, A.data_ptr(), 1, B.data_ptr(), 1, C.data_ptr(), 1,
+                               tdb.VARIANT_DB, kernels[0][1] if tdb.gemm_f32_config_variants(
+                                   kernels[0][1]) & (1 << tdb.VARIANT_DB) else 0, s_ptr)
+    out["launch_1x1x1_us"] = round(statistics.median(
+        time_call(tiny, args.batch_ms, args.batches)[0] for _ in range(args.rounds)), 3)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+# ------------------------------------------------------------------ the bench line
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,10 +726,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--per-shape", choices=("all", "metric", "none"), default="all",
                     help="which workload shapes get the SB/DB/dispatch comparison")
-    ap.add_argument("--rounds", type=int, default=2,
+    ap.add_argument("--rounds", type=int, default=4,
                     help="per-shape timing: rounds, each visiting the variants in rotated order")
-    ap.add_argument("--batches", type=int, default=5, help="per-shape timing: batches per round")
-    ap.add_argument("--batch-ms", type=float, default=25.0,
+    ap.add_argument("--batches", type=int, default=9, help="per-shape timing: batches per round")
+    ap.add_argument("--batch-ms", type=float, default=40.0,
                     help="per-shape timing: minimum milliseconds of launches per batch")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
@@ -293,21 +737,26 @@ def main() -> int:
     ap.add_argument("--summarize-counters", metavar="DIR")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--counter-run", action="store_true")
-    ap.add_argument("--counter-run-skinny", action="store_true")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--oracle-table", action="store_true")
+    ap.add_argument("--raster-run", action="store_true")
+    ap.add_argument("--raster-time", action="store_true")
+    ap.add_argument("--write-raster-traffic", nargs=3,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "TIME_JSON"))
+    ap.add_argument("--layer-shapes", action="store_true")
+    ap.add_argument("--k-slope", action="store_true")
     args = ap.parse_args()
 
     if args.oracle_table:
         return oracle_table()
-
     if args.write_traffic:
         return write_traffic(*args.write_traffic)
     if args.counter_run:
         return counter_run(args.copy_calibration)
-    if args.counter_run_skinny:
-        return counter_run_skinny(args.copy_calibration)
-
+    if args.raster_run or args.raster_time:
+        return raster_run(args.copy_calibration, args.raster_time, args)
+    if args.write_raster_traffic:
+        return write_raster_traffic(*args.write_raster_traffic)
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace)
     if args.summarize_counters:
@@ -316,8 +765,11 @@ def main() -> int:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         return 2
+    if args.layer_shapes:
+        return layer_shapes(args)
+    if args.k_slope:
+        return k_slope(args)
 
-    import numpy as np
     import torch
 
     import tdb_inputs as ti
@@ -334,14 +786,10 @@ def main() -> int:
         print(*a, file=sys.stderr, flush=True)
 
     if args.copy_calibration > 0:
-        n = args.copy_calibration * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)  # reads and writes exactly MIB MiB each
-        torch.cuda.synchronize()
+        _calibration_copy(torch, dev, args.copy_calibration)
         log(f"[bench] calibration copy of {args.copy_calibration} MiB done")
-        del src, dst
+
+    cpu = CpuLeg()
 
     # ------------------------------------------------------------------ headline
     M, N, K, seed = ti.WORKLOADS[HEADLINE]
@@ -360,7 +808,9 @@ def main() -> int:
         if rc != tdb.OK:
             raise tdb.GemmError(rc, "gemm_f32")
 
-    log(f"[bench] warmup {args.warmup} steps (variant {variant}, cfg {cfg}) ...")
+    log(f"[bench] {PREWARM_S * 1e3:.0f} ms of untimed launches, then warmup {args.warmup} "
+        f"steps (variant {variant}, cfg {cfg}) ...")
+    _prewarm(torch, step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -381,18 +831,13 @@ def main() -> int:
     log(f"[bench] {HEADLINE}: {ms_per_step:.3f} ms/step wall, {kernel_ms:.3f} ms/launch "
         f"(events) -> {value:.2f} TFLOP/s")
 
-    # parity of the timed output on the workload's seeded positions
-    parity = None
+    # the timed output on the workload's seeded positions
     try:
-        import oracle
-        ri, rj = ti.sample_positions(seed, M, N, 4096)
-        c64, bnd = oracle.gemm_f64_sampled(A_h, B_h, ri, rj)
-        got = C[torch.from_numpy(ri).to(dev), torch.from_numpy(rj).to(dev)].cpu().numpy()
-        r = oracle.tolerance_ratio(got, c64, bnd)
-        parity = {"positions": 4096, "max_err_over_bound": r, "pass": bool(r <= 1.0)}
-        log(f"[bench] parity on 4096 positions: max |C-C64|/(1e-5*Bnd+1e-6) = {r:.3g}")
-    except Exception as exc:  # the oracle is test infrastructure; report, do not fail
-        parity = {"error": repr(exc)}
+        r = cpu.sampled(torch, dev, ti, M, N, seed, A_h, B_h)(C)
+        parity = {"positions": 4096, "max_err_over_bound": r, "pass": _ratio_ok(r)}
+        log(f"[bench] parity on 4096 positions: max |C-C64|/(1e-5*Bnd+1e-6) = {r}")
+    except Exception as exc:
+        parity = {"error": repr(exc), "pass": False}
 
     # traffic from the committed counter summary, if it describes this kernel source
     traffic = None
@@ -422,56 +867,15 @@ def main() -> int:
     except Exception as exc:
         ceiling = {"error": repr(exc)}
 
-    # power, clocks and temperatures while the headline kernel runs (amd-smi, sampled once)
-    telemetry = telemetry_under_load(step, torch)
+    # power, clocks and temperatures while the headline kernel runs without a gap
+    telemetry = telemetry_under_load(step, torch, kernel_ms, ceiling.get("clock_ghz"))
     log(f"[bench] telemetry under load: {telemetry}")
 
     # ------------------------------------------------------------------ per shape
-    def time_call(fn, target_ms=args.batch_ms, batches=args.batches):
-        fn()
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        fn()
-        torch.cuda.synchronize()
-        one = max(time.perf_counter() - t, 1e-6)
-        reps = int(min(5000, max(3, target_ms * 1e-3 / one)))
-        for _ in range(min(reps, 10)):
-            fn()
-        res = []
-        for _ in range(batches):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            h0 = time.perf_counter()
-            a.record(stream)
-            for _ in range(reps):
-                fn()
-            b.record(stream)
-            torch.cuda.synchronize()
-            h1 = time.perf_counter()
-            res.append((a.elapsed_time(b) * 1e3 / reps, (h1 - h0) * 1e6 / reps))
-        ev = statistics.median(x[0] for x in res)
-        wall_us = statistics.median(x[1] for x in res)
-        return ev, wall_us, min(x[0] for x in res), max(x[0] for x in res)
-
-    # the oracle for each per-shape workload, to check every timed variant once per round
-    def shape_checker(name, m, n, k, s, a_h, b_h):
-        try:
-            import oracle
-        except Exception as exc:  # the oracle is test infrastructure; report, do not fail
-            return lambda C: {"error": repr(exc)}
-        if m * n * k <= 4096 ** 3:
-            c64, bnd = oracle.gemm_f64(a_h, b_h)
-            return lambda C: oracle.tolerance_ratio(C.cpu().numpy(), c64, bnd)
-        ri, rj = ti.sample_positions(s, m, n, 4096)
-        c64, bnd = oracle.gemm_f64_sampled(a_h, b_h, ri, rj)
-        ii, jj = torch.from_numpy(ri).to(dev), torch.from_numpy(rj).to(dev)
-        return lambda C: oracle.tolerance_ratio(C[ii, jj].cpu().numpy(), c64, bnd)
-
+    time_call = _timer(torch, stream)
     per_shape = {}
     names = {"all": list(ti.WORKLOADS), "none": [],
              "metric": ["square_1024", "square_4096", "square_8192"]}[args.per_shape]
-    rounds = args.rounds
     for name in names:
         m, n, k, s = ti.WORKLOADS[name]
         if name == HEADLINE:
@@ -481,23 +885,32 @@ def main() -> int:
             a_h, b_h = ti.workload_inputs(m, n, k, s)
             Ad, Bd = torch.from_numpy(a_h).to(dev), torch.from_numpy(b_h).to(dev)
             Cd = torch.zeros((m, n), dtype=torch.float32, device=dev)
-        check = shape_checker(name, m, n, k, s, a_h, b_h)
+        check = cpu.full_or_sampled(torch, dev, ti, m, n, k, s, a_h, b_h)
         pa, pb, pc = Ad.data_ptr(), Bd.data_ptr(), Cd.data_ptr()
+        sb_cfg = tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_SB)
+        db_cfg = tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_DB)
+        pair = _pair_cfg(tdb, sb_cfg, db_cfg)
         fns = {
             "sb": lambda: tdb.gemm_f32_sb(m, n, k, pa, k, pb, n, pc, n, s_ptr),
             "db": lambda: tdb.gemm_f32_db(m, n, k, pa, k, pb, n, pc, n, s_ptr),
             "ms": lambda: tdb.gemm_f32_ms(m, n, k, pa, k, pb, n, pc, n, s_ptr),
             "dispatch": lambda: tdb.gemm_f32(m, n, k, pa, k, pb, n, pc, n, s_ptr),
+            # the same multi-wave tile with two and with one barrier per K tile
+            "pair_sb": lambda: tdb.gemm_f32_ex(m, n, k, pa, k, pb, n, pc, n, tdb.VARIANT_SB,
+                                               pair, s_ptr),
+            "pair_db": lambda: tdb.gemm_f32_ex(m, n, k, pa, k, pb, n, pc, n, tdb.VARIANT_DB,
+                                               pair, s_ptr),
             # context only: the vendor library through torch, timed as a black box
             "torch": lambda: torch.matmul(Ad, Bd, out=Cd),
         }
         order = list(fns)
         samples = {v: [] for v in fns}
         checks = {v: [] for v in fns if v != "torch"}
-        for r in range(rounds):  # rotate the variant order between rounds
+        _prewarm(torch, fns["dispatch"], 0.05)
+        for r in range(args.rounds):  # rotate the variant order between rounds
             rot = r % len(order)
             for v in order[rot:] + order[:rot]:
-                samples[v].append(time_call(fns[v]))
+                samples[v].append(time_call(fns[v], args.batch_ms, args.batches))
             for v in checks:  # every timed variant of the library, once per round
                 Cd.fill_(float("nan"))
                 fns[v]()
@@ -516,20 +929,30 @@ def main() -> int:
             if v in checks:
                 cs = checks[v]
                 entry[v]["max_err_over_bound"] = (max(cs) if all(isinstance(c, float)
-                                                                   for c in cs) else cs[0])
-        entry["sb_cfg"] = tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_SB)
-        entry["db_cfg"] = tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_DB)
+                                                                   for c in cs) else cs)
+        entry["sb_cfg"] = sb_cfg
+        entry["db_cfg"] = db_cfg
         entry["ms_cfg"] = tdb.gemm_f32_select_cfg(m, n, k, tdb.VARIANT_MS)
+        # barriers per K tile of each timed loop: a one-wave workgroup has none (the
+        # compiler drops them), so its SB and DB columns compare barrier-free loops
+        entry["sb_barriers_per_k_tile"] = 2 if _cfg_waves(tdb, sb_cfg) >= 2 else 0
+        entry["db_barriers_per_k_tile"] = 1 if _cfg_waves(tdb, db_cfg) >= 2 else 0
+        entry["pair_cfg"] = pair
+        entry["pair_tile"] = _cfg_name(tdb, pair)
         _, dv, dc = tdb.gemm_f32_select(m, n, k)
         entry["dispatch_choice"] = f"{VARIANT_NAMES[dv]} cfg{dc}"
         entry["db_over_sb_speedup"] = round(entry["sb"]["us"] / entry["db"]["us"], 3)
+        entry["pair_db_over_sb_speedup"] = round(entry["pair_sb"]["us"] /
+                                                 entry["pair_db"]["us"], 3)
         entry["ms_over_db_speedup"] = round(entry["db"]["us"] / entry["ms"]["us"], 3)
         entry["dispatch_over_torch_speedup"] = round(entry["torch"]["us"] /
                                                      entry["dispatch"]["us"], 3)
         per_shape[name] = entry
         log(f"[bench] {name}: sb {entry['sb']['us']} us, db {entry['db']['us']} us, "
             f"ms {entry['ms']['us']} us, dispatch {entry['dispatch']['us']} us "
-            f"({entry['dispatch']['tflops']} TFLOP/s), torch.matmul {entry['torch']['us']} us")
+            f"({entry['dispatch']['tflops']} TFLOP/s), pair on {entry['pair_tile']} "
+            f"sb {entry['pair_sb']['us']} / db {entry['pair_db']['us']} us, "
+            f"torch.matmul {entry['torch']['us']} us")
         if name != HEADLINE:
             del Ad, Bd, Cd
         del check
@@ -538,29 +961,8 @@ def main() -> int:
     cpu_baseline = None
     if args.cpu_seconds > 0:
         try:
-            import oracle
-            threads = oracle.max_threads()
-            # successive row blocks of the product until the time budget is spent; the
-            # block size comes from a pilot block so that the last one overshoots little
-            t = time.perf_counter()
-            oracle.gemm_f64(A_h[:threads], B_h)
-            pilot = time.perf_counter() - t
-            block = int(min(M, max(threads, threads * round(args.cpu_seconds / 8 / pilot))))
-            rows, dt = 0, 0.0
-            while rows < M and dt < args.cpu_seconds:
-                r1 = min(M, rows + block)
-                t = time.perf_counter()
-                oracle.gemm_f64(A_h[rows:r1], B_h)
-                dt += time.perf_counter() - t
-                rows = r1
-            cpu_tflops = 2.0 * rows * N * K / dt / 1e12
-            cpu_baseline = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s",
-                            "cores": threads, "kind": "oracle",
-                            "sample": f"first {rows} rows of the {M}x{N}x{K} product "
-                                      f"(C64 and Bnd in FP64, {dt:.1f} s); full product "
-                                      f"extrapolates to {flop / (cpu_tflops * 1e12):.0f} s",
-                            "cpu": _cpu_model()}
-            log(f"[bench] CPU oracle: {rows} rows in {dt:.1f} s on {threads} threads")
+            cpu_baseline = cpu.baseline(A_h, B_h, args.cpu_seconds)
+            log(f"[bench] CPU oracle: {cpu_baseline.get('sample')}")
         except Exception as exc:
             cpu_baseline = {"error": repr(exc)}
 
@@ -593,16 +995,25 @@ def main() -> int:
         "cpu_baseline": cpu_baseline,
         "metric_shapes": metric_shapes,
         "per_shape": per_shape,
+        "protocol": {"headline": f"{PREWARM_S * 1e3:.0f} ms untimed, {args.warmup} warm-up "
+                                 f"steps, {args.steps} timed steps",
+                     "per_shape": f"{args.rounds} rotated rounds x {args.batches} batches of "
+                                  f">= {args.batch_ms} ms; medians of the per-round medians"},
         "parity": parity,
     }
+    line["parity_ok"] = line_parity_ok(line)
     print(json.dumps(line), flush=True)
+    if not line["parity_ok"]:
+        log("[bench] a timed output failed its oracle check (or the check could not run): "
+            "parity_ok is false")
+        return 3
     return 0
 
 
 def oracle_table() -> int:
     """Time the CPU oracle (C64 and Bnd in FP64) on every workload, in full up to 4096^3
-    and on the 4096 seeded positions at 8192^3, on all host threads and on one thread.
-    Prints one JSON object; needs no GPU."""
+    multiply-adds and on the 4096 seeded positions beyond, on all host threads and on one
+    thread.  Prints one JSON object; needs no GPU."""
     import oracle
     import tdb_inputs as ti
     threads = oracle.max_threads()
@@ -628,43 +1039,76 @@ def oracle_table() -> int:
     return 0
 
 
-def telemetry_under_load(step, torch, timeout_s: float = 20.0) -> dict:
-    """One amd-smi sample of socket power, shader clocks (per XCD) and temperatures, taken
-    while `step` keeps the GPU busy.  amd-smi runs as a child process; nothing is timed
-    meanwhile.  Returns {"error": ...} when amd-smi is missing or fails."""
-    import shutil
+def _amd_smi_sample(exe, timeout_s=10.0):
     import subprocess
-    exe = shutil.which("amd-smi")
-    if exe is None:
-        return {"error": "amd-smi not found"}
     try:
-        proc = subprocess.Popen([exe, "metric", "-g", "0", "-p", "-c", "-t", "--json"],
-                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL)
-    except OSError as exc:
-        return {"error": repr(exc)}
-    t0 = time.perf_counter()
-    while proc.poll() is None and time.perf_counter() - t0 < timeout_s:
-        for _ in range(8):
-            step()
-        torch.cuda.synchronize()
-    try:
-        out, _ = proc.communicate(timeout=5)
-    except subprocess.TimeoutExpired:
-        proc.kill()
-        proc.communicate()
-        return {"error": "amd-smi timed out"}
-    try:
+        out = subprocess.run([exe, "metric", "-g", "0", "-p", "-c", "-t", "--json"],
+                             stdout=subprocess.PIPE, stderr=subprocess.DEVNULL,
+                             timeout=timeout_s, check=False).stdout
         d = json.loads(out)
         g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
         clocks = [v["clk"]["value"] for k, v in sorted(g["clock"].items())
                   if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
         temps = {k: v["value"] for k, v in g.get("temperature", {}).items()
                  if isinstance(v, dict) and "value" in v}
-        return {"socket_power_w": g["power"]["socket_power"]["value"],
-                "gfx_clock_mhz_per_xcd": clocks, "temperature_c": temps,
-                "source": "amd-smi metric -g 0 -p -c -t, sampled during headline launches"}
-    except (ValueError, KeyError, IndexError, TypeError) as exc:
-        return {"error": "unparsed amd-smi output: " + repr(exc)}
+        return {"power_w": g["power"]["socket_power"]["value"], "gfx_mhz": clocks,
+                "temperature_c": temps}
+    except Exception as exc:  # a missing field or a failed call: recorded, not fatal
+        return {"error": repr(exc)}
+
+
+def telemetry_under_load(step, torch, step_ms, probe_clock_ghz, window_s: float = 1.5,
+                         min_samples: int = 4, ahead_s: float = 1.0) -> dict:
+    """amd-smi samples (socket power, shader clock per XCD, temperatures) taken one after
+    another while the headline kernel runs back to back without a gap: before every sample,
+    enough launches are queued to keep the GPU busy for `ahead_s` seconds past it, so no
+    sample falls between launches.  Reports the medians and the median clock against the
+    clock the ceiling probe read from the shader's own counters (flagged when they differ by
+    more than 5%).  amd-smi runs as a child process; nothing is timed meanwhile."""
+    import shutil
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return {"error": "amd-smi not found"}
+    per_s = max(step_ms, 0.01) * 1e-3
+    queued_until = [time.perf_counter()]
+
+    def top_up():
+        now = time.perf_counter()
+        left = max(queued_until[0] - now, 0.0)
+        n = int((ahead_s - left) / per_s) + 1 if left < ahead_s else 0
+        for _ in range(n):
+            step()
+        queued_until[0] = max(queued_until[0], now) + n * per_s
+
+    samples = []
+    t0 = time.perf_counter()
+    top_up()
+    while (time.perf_counter() - t0 < window_s or len(samples) < min_samples) and \
+            len(samples) < 3 * min_samples:
+        samples.append(_amd_smi_sample(exe))
+        top_up()
+    torch.cuda.synchronize()
+    good = [s for s in samples if "error" not in s and s["gfx_mhz"]]
+    if not good:
+        return {"error": "no usable amd-smi sample", "samples": samples}
+    per_xcd = [statistics.median(s["gfx_mhz"][i] for s in good)
+               for i in range(min(len(s["gfx_mhz"]) for s in good))]
+    med = statistics.median(c for s in good for c in s["gfx_mhz"])
+    out = {"samples": len(samples), "usable": len(good),
+           "window_s": round(time.perf_counter() - t0, 2),
+           "socket_power_w_median": statistics.median(s["power_w"] for s in good),
+           "gfx_clock_mhz_median": med,
+           "gfx_clock_mhz_median_per_xcd": per_xcd,
+           "gfx_clock_mhz_range": [min(c for s in good for c in s["gfx_mhz"]),
+                                   max(c for s in good for c in s["gfx_mhz"])],
+           "temperature_c_last": good[-1]["temperature_c"],
+           "source": "amd-smi metric -g 0 -p -c -t, sampled while headline launches queued "
+                     "ahead kept the GPU busy"}
+    if probe_clock_ghz:
+        ratio = med / (probe_clock_ghz * 1e3)
+        out["clock_vs_probe"] = round(ratio, 4)
+        out["clock_consistent_with_probe"] = abs(ratio - 1.0) <= 0.05
+    return out
 
 
 def _cpu_model() -> str:

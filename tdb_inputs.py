@@ -49,6 +49,8 @@ WORKLOADS = {
     "rect_1024x128x256": (1024, 128, 256, 3003),
     "square_4096": (4096, 4096, 4096, 4001),
     "square_8192": (8192, 8192, 8192, 5001),
+    # one GPU's share of the 8192^3 product split by rows over eight GPUs
+    "shard_1024x8192x8192": (1024, 8192, 8192, 6001),
 }
 
 _CHUNK = 1 << 23
