@@ -35,7 +35,9 @@ Also:
   python bench.py --summarize-trace DIR      per-(kernel, grid) median, minimum, mean and
                                              maximum durations from a rocprofv3 kernel trace
                                              (kernel_trace.csv), and the median without the
-                                             first launches of each group
+                                             first launches of each group; with
+                                             --timed-headline LINE_FILE, the headline
+                                             kernel's timed steps of that traced run
   python bench.py --summarize-counters DIR   per-(kernel, grid) average counter values
                                              from rocprofv3 --pmc runs (counter_collection.csv)
   python bench.py --layer-shapes             decode and layer products (1 to 4096 rows
@@ -54,15 +56,17 @@ Also:
                                              shard and a decode shape, plus the calibration
                                              kernel: the program that the rocprofv3 --pmc
                                              passes profile
-  python bench.py --raster-run               the headline product three times under each
-                                             workgroup order (GEMMF32_RASTER group heights 1
-                                             to 32, with and without the XCD renumbering),
-                                             after the calibration kernel: the program of the
-                                             raster traffic passes; --raster-time times the
-                                             same orders (events, no profiler)
+  python bench.py --raster-run               the dispatched products at 8192^3, 4096^3, the
+                                             row shard and 4096x11008x4096, three times under
+                                             each workgroup order (GEMMF32_RASTER group
+                                             heights 1 to 32, with and without the XCD
+                                             renumbering), after the calibration kernel: the
+                                             program of the raster traffic passes;
+                                             --raster-time times the same orders (events, no
+                                             profiler)
   python bench.py --write-raster-traffic FETCH_DIR WRITE_DIR TIME_JSON
-                                             HBM bytes and time per workgroup order of the
-                                             headline kernel
+                                             HBM bytes and time per workgroup order of each
+                                             of those kernels
   python bench.py --write-traffic FETCH_DIR WRITE_DIR
                                              HBM bytes per launch of the headline kernel from
                                              a FETCH_SIZE pass and a WRITE_SIZE pass of
@@ -152,6 +156,38 @@ def summarize_trace(d: str) -> int:
     return 0
 
 
+def summarize_timed_headline(d: str, line_file: str) -> int:
+    """The headline kernel's launches in a kernel trace of a bench run that are that run's
+    timed steps (the line records how many headline launches come before them): their
+    median, minimum and maximum duration, the FLOP rate and peak fraction of the median,
+    and the line's own ms_per_step and roofline fraction beside them."""
+    import tdb_inputs as ti
+    import tiled_double_buffered_amd as tdb
+
+    with open(line_file) as f:
+        line = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    M, N, K = line["config"]["M"], line["config"]["N"], line["config"]["K"]
+    first = line["protocol"]["headline_launches_before_timed"]
+    steps = line["steps"]
+    desc, match = _kernel_match(tdb, M, N, K)
+    groups, found = trace_groups(d)
+    durs = [v for (name, grid), v in groups.items() if match(name, grid)]
+    if not found or len(durs) != 1 or len(durs[0]) < first + steps:
+        print("headline kernel not found once in the trace", file=sys.stderr)
+        return 1
+    timed = durs[0][first:first + steps]
+    med = statistics.median(timed) / 1e3
+    flop = 2.0 * M * N * K
+    print(f"headline kernel {desc}: launches {first} .. {first + steps - 1} of "
+          f"{len(durs[0])} (the timed steps)")
+    print(f"  median {med:.2f} us, min {min(timed) / 1e3:.2f} us, max {max(timed) / 1e3:.2f} us")
+    print(f"  2*M*N*K / median = {flop / (med * 1e-6) / 1e12:.3f} TFLOP/s = "
+          f"{flop / (med * 1e-6) / 1e12 / PEAK_FP32_MFMA_TFLOPS:.4f} of {PEAK_FP32_MFMA_TFLOPS}")
+    print(f"  the run's line: ms_per_step {line['ms_per_step']}, roofline.launch_ms "
+          f"{line['roofline']['launch_ms']}, roofline.frac {line['roofline']['frac']}")
+    return 0
+
+
 def summarize_counters(d: str) -> int:
     """Average counter value per (kernel name, grid size, counter) from rocprofv3 --pmc."""
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -194,10 +230,13 @@ def _per_dispatch(rows, counter, match):
     return (statistics.mean(per.values()), len(per)) if per else (None, 0)
 
 
-def _kernel_match(tdb, M, N, K):
-    """(description, predicate on (kernel name, grid size)) for the dispatched kernel of a
-    shape."""
-    _, variant, cfg = tdb.gemm_f32_select(M, N, K)
+def _kernel_match(tdb, M, N, K, variant=None, cfg=None):
+    """(description, predicate on (kernel name, grid size)) for the kernel that runs a
+    shape: the dispatched one, or that of the given variant (and configuration)."""
+    if variant is None:
+        _, variant, cfg = tdb.gemm_f32_select(M, N, K)
+    elif cfg is None:
+        cfg = tdb.gemm_f32_select_cfg(M, N, K, variant)
     _, info = tdb.gemm_f32_config_info(cfg)
     threads = info["threads"] * (tdb.gemm_f32_config_ks(cfg) if variant == tdb.VARIANT_KS else 1)
     grid = str(((M + info["BM"] - 1) // info["BM"]) * ((N + info["BN"] - 1) // info["BN"])
@@ -212,7 +251,9 @@ def _kernel_match(tdb, M, N, K):
         elif variant == tdb.VARIANT_KS:
             kname, flag = "gemm_f32_ks_kernel", ">, %d>" % tdb.gemm_f32_config_ks(cfg)
         else:
-            kname, flag = "gemm_f32_tile_kernel", ", %d>" % variant  # loop kind = variant id
+            # the loop kind (= variant id) follows the closing ">" of TileCfg<...>: a bare
+            # ", 2>" would also match the last field of a TileCfg ending in "2, 2>"
+            kname, flag = "gemm_f32_tile_kernel", ">, %d>" % variant
     desc = f"{VARIANT_NAMES[variant]} cfg{cfg} {info['BM']}x{info['BN']}x{info['BK']}"
 
     def match(name, g):
@@ -286,13 +327,16 @@ def _calibration_copy(torch, dev, mib):
     del src, dst
 
 
-def _prewarm(torch, fn, seconds=PREWARM_S):
+def _prewarm(torch, fn, seconds=PREWARM_S) -> int:
     """Untimed launches of `fn` for at least `seconds`: the shader clock ramps from idle to
-    its sustained value over some tens of milliseconds of load."""
+    its sustained value over some tens of milliseconds of load.  Returns the launches."""
     t0 = time.perf_counter()
+    n = 0
     while time.perf_counter() - t0 < seconds:
         fn()
+        n += 1
         torch.cuda.synchronize()
+    return n
 
 
 def _cfg_waves(tdb, cfg):
@@ -438,11 +482,35 @@ def line_parity_ok(line) -> bool:
 
 
 # ------------------------------------------------------------------ counter programs
+def _counter_plan(tdb):
+    """The launches of the counter program, as (label, (M, N, K, seed), entry, variant,
+    cfg): entry is an entry point of the library, variant/cfg name the kernel it runs
+    (variant None: the dispatched one).  The last one is a control for the busy-CU figure:
+    the 16-row kernel on half as many 16-column tiles (128 workgroups for 256 CUs)."""
+    import tdb_inputs as ti
+    plan = []
+    for name in ("square_1024", "square_4096", "square_8192"):
+        shape = ti.WORKLOADS[name]
+        plan += [(name, shape, "gemm_f32_sb", tdb.VARIANT_SB, None),
+                 (name, shape, "gemm_f32_db", tdb.VARIANT_DB, None),
+                 (name, shape, "gemm_f32_ms", tdb.VARIANT_MS, None),
+                 (name, shape, "gemm_f32", None, None)]
+    plan.append(("shard_1024x8192x8192", ti.WORKLOADS["shard_1024x8192x8192"], "gemm_f32",
+                 None, None))
+    plan.append(("decode_16x4096x4096", (16, 4096, 4096, 7101), "gemm_f32", None, None))
+    ks16 = [c for c in range(tdb.gemm_f32_num_configs())
+            if tdb.gemm_f32_config_variants(c) == 1 << tdb.VARIANT_KS]
+    plan.append(("control_16x2048x4096", (16, 2048, 4096, 7102), "gemm_f32_ex",
+                 tdb.VARIANT_KS, ks16[0]))
+    return plan
+
+
 def counter_run(calib_mib: int) -> int:
-    """A short program for counter passes: three launches each of the single-, double-
-    buffered and multi-stage kernels (dispatch-table configurations) and of the dispatched
-    one at the three metric shapes, then the dispatched kernel at the row shard
-    (1024 x 8192 x 8192) and at the decode shape 16 x 4096 x 4096."""
+    """A short program for counter passes: three launches of each entry of the counter
+    plan (single-, double-buffered, multi-stage and dispatched kernels at the three metric
+    shapes, the dispatched kernel at the row shard 1024 x 8192 x 8192 and at the decode
+    shape 16 x 4096 x 4096, the 16-row kernel at 16 x 2048 x 4096), after the calibration
+    kernel."""
     import torch
 
     import tdb_inputs as ti
@@ -451,85 +519,210 @@ def counter_run(calib_mib: int) -> int:
     dev = torch.device("cuda:0")
     _calibration_copy(torch, dev, calib_mib)
     s_ptr = torch.cuda.current_stream(dev).cuda_stream
-    runs = [(name, (tdb.gemm_f32_sb, tdb.gemm_f32_db, tdb.gemm_f32_ms, tdb.gemm_f32))
-            for name in ("square_1024", "square_4096", "square_8192")]
-    runs += [("shard_1024x8192x8192", (tdb.gemm_f32,)), ((16, 4096, 4096, 7101), (tdb.gemm_f32,))]
-    for name, fns in runs:
-        M, N, K, seed = ti.WORKLOADS[name] if isinstance(name, str) else name
-        a, b = ti.workload_inputs(M, N, K, seed)
-        A, B = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
-        C = torch.empty((M, N), device=dev)
-        for fn in fns:
-            for _ in range(3):
-                rc = fn(M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N, s_ptr)
-                if rc != tdb.OK:
-                    raise tdb.GemmError(rc, fn.__name__)
+    cached = {}
+    for label, (M, N, K, seed), entry, variant, cfg in _counter_plan(tdb):
+        if cached.get("key") != (M, N, K, seed):
+            cached.clear()
+            a, b = ti.workload_inputs(M, N, K, seed)
+            cached.update(key=(M, N, K, seed), A=torch.from_numpy(a).to(dev),
+                          B=torch.from_numpy(b).to(dev), C=torch.empty((M, N), device=dev))
+        args = (M, N, K, cached["A"].data_ptr(), K, cached["B"].data_ptr(), N,
+                cached["C"].data_ptr(), N)
+        fn = getattr(tdb, entry)
+        for _ in range(3):
+            rc = (fn(*args, variant, cfg, s_ptr) if entry == "gemm_f32_ex"
+                  else fn(*args, s_ptr))
+            if rc != tdb.OK:
+                raise tdb.GemmError(rc, entry)
         torch.cuda.synchronize()
-        print(f"[counter-run] {M}x{N}x{K} done", file=sys.stderr, flush=True)
-        del A, B, C
+        print(f"[counter-run] {label} {entry} done", file=sys.stderr, flush=True)
     return 0
 
 
-RASTER_SETTINGS = ["8", "1", "2", "4", "16", "32", "8,noxcd", "1,noxcd"]
+COUNTER_PASSES = {
+    "mfma": "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_BUSY_CYCLES "
+            "SQ_WAVE_CYCLES GRBM_GUI_ACTIVE",
+    "lds": "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_ANY SQ_ACTIVE_INST_LDS "
+           "SQ_WAIT_INST_LDS SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_ANY SQ_WAVE_CYCLES",
+    "busy": "SQ_BUSY_CU_CYCLES SQ_BUSY_CYCLES SQ_WAVES GRBM_GUI_ACTIVE GRBM_COUNT",
+    "fetch": "FETCH_SIZE",
+    "write": "WRITE_SIZE",
+}
 
 
-def _headline_operands(torch, dev):
+def counter_table(dirs: dict, calib_mib: int = 512) -> int:
+    """One row per entry of the counter plan from the rocprofv3 --pmc passes in `dirs`
+    (keys of COUNTER_PASSES): matrix-core busy share, executed MFMA work against 2 M N K,
+    LDS bank conflicts, wait and LDS-instruction shares of the wave cycles, the mean number
+    of busy compute units, and calibrated HBM bytes against the algorithmic bytes."""
+    import tiled_double_buffered_amd as tdb
+
+    rows = {k: _counter_rows(d) for k, d in dirs.items()}
+
+    def is_calib(name, g):
+        return "neg" in name.lower() and "gemm" not in name
+    c_fetch, _ = _per_dispatch(rows["fetch"], "FETCH_SIZE", is_calib)
+    c_write, _ = _per_dispatch(rows["write"], "WRITE_SIZE", is_calib)
+    if c_fetch is None or c_write is None:
+        print("no calibration kernel in the FETCH_SIZE / WRITE_SIZE passes", file=sys.stderr)
+        return 1
+    sf, sw = calib_mib * 1024.0 / c_fetch, calib_mib * 1024.0 / c_write
+
+    out = [
+        "# rocprofv3 counters of the gemm_f32 kernels: metric shapes 1024^3, 4096^3, 8192^3 "
+        "(single-, double-buffered, multi-stage, dispatched),",
+        "# the row shard 1024x8192x8192 and the decode shape 16x4096x4096 (dispatched), and "
+        "the 16-row kernel at 16x2048x4096 (128 tiles: control)",
+        "#",
+        "# Commands (repo root, MI355X, 1 GPU; one pass per counter set, 3 dispatches of each "
+        "kernel):",
+    ]
+    for k, ctrs in COUNTER_PASSES.items():
+        out.append(f"#   rocprofv3 --pmc {ctrs} -f csv -d <{k.upper()}_DIR> -o run -- "
+                   f"python3 bench.py --counter-run --copy-calibration {calib_mib}")
+    out += [
+        "#   python3 bench.py --counter-table " + " ".join(f"<{k.upper()}_DIR>"
+                                                         for k in COUNTER_PASSES),
+        "#",
+        "# cyc/XCD   GRBM_GUI_ACTIVE / 8 XCDs: cycles of the dispatch under counter "
+        "collection (dispatches run one at a time, so short",
+        "#           kernels carry launch ramp that back-to-back timing overlaps)",
+        "# mfma      SQ_VALU_MFMA_BUSY_CYCLES / (cyc/XCD x 1024 SIMDs)",
+        "# mops/2MNK SQ_INSTS_VALU_MFMA_MOPS_F32 x 512 / (2 M N K): matrix work executed "
+        "over the product's (1.00: no padded MFMAs)",
+        "# lds-conf  SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE",
+        "# wait      SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; lds-inst SQ_ACTIVE_INST_LDS / "
+        "SQ_WAVE_CYCLES",
+        "# busyCU    sum SQ_BUSY_CU_CYCLES (CU-busy cycles, summed over the CUs of each SE) / "
+        "(sum SQ_BUSY_CYCLES / 32 SEs): the mean number",
+        "#           of compute units with waves while the shader engines have waves (the "
+        "numerator of rocprofv3's SIMD_UTILIZATION",
+        "#           over SE-busy cycles); at most 256, and at most the workgroup count when "
+        "one workgroup fills a CU.  The counter's",
+        "#           description says quad-cycles, but rocprofv3's own SIMD_UTILIZATION takes it "
+        "as cycles, and so does this column:",
+        "#           the 8192^3 kernels (1024 or more workgroups for 256 CUs) read 256 on this "
+        "scale",
+        f"# HBM MB    FETCH_SIZE, WRITE_SIZE (KiB) x 1024 x calibration (read {sf:.4f}, write "
+        f"{sw:.4f}: {calib_mib} MiB over the negate kernel's readings)",
+        "# algo MB   4 (MK + KN + MN) bytes",
+        "#",
+        f"{'workload':<22}{'entry':<13}{'kernel':<26}{'grid':>8}{'cyc/XCD':>10}{'mfma':>7}"
+        f"{'mops/2MNK':>10}{'lds-conf':>9}{'wait':>6}{'lds-inst':>9}{'busyCU':>7}"
+        f"{'read MB':>9}{'write MB':>9}{'algo MB':>9}{'hbm/algo':>9}",
+    ]
+
+    def val(kind, ctr, match):
+        v, _ = _per_dispatch(rows[kind], ctr, match)
+        return v
+
+    def fmt(x, spec):
+        return format(x, spec) if x is not None else "-".rjust(len(format(0.0, spec)))
+
+    for label, (M, N, K, _), entry, variant, cfg in _counter_plan(tdb):
+        desc, match = _kernel_match(tdb, M, N, K, variant, cfg)
+        grid = next((g for kind in rows for r in rows[kind]
+                     for g in [r.get("Grid_Size", "")] if match(r.get("Kernel_Name", ""), g)),
+                    "-")
+        gui = val("mfma", "GRBM_GUI_ACTIVE", match)
+        cyc = gui / 8 if gui else None
+        busy = val("mfma", "SQ_VALU_MFMA_BUSY_CYCLES", match)
+        mops = val("mfma", "SQ_INSTS_VALU_MFMA_MOPS_F32", match)
+        conf = val("lds", "SQ_LDS_BANK_CONFLICT", match)
+        idx = val("lds", "SQ_LDS_IDX_ACTIVE", match)
+        wait = val("lds", "SQ_WAIT_INST_ANY", match)
+        ldsi = val("lds", "SQ_ACTIVE_INST_LDS", match)
+        wcyc = val("lds", "SQ_WAVE_CYCLES", match)
+        bcu = val("busy", "SQ_BUSY_CU_CYCLES", match)
+        bse = val("busy", "SQ_BUSY_CYCLES", match)
+        rd = val("fetch", "FETCH_SIZE", match)
+        wr = val("write", "WRITE_SIZE", match)
+        flop = 2.0 * M * N * K
+        algo = 4.0 * (M * K + K * N + M * N)
+        rd_b = rd * 1024 * sf if rd is not None else None
+        wr_b = wr * 1024 * sw if wr is not None else None
+
+        def ratio(a, b, scale=1.0):
+            return a * scale / b if a is not None and b else None
+        out.append(
+            f"{label:<22}{entry:<13}{desc:<26}{grid:>8}{fmt(cyc, '10.0f')}"
+            f"{fmt(ratio(busy, cyc * 1024 if cyc else None), '7.3f')}"
+            f"{fmt(ratio(mops, flop, 512.0), '10.3f')}{fmt(ratio(conf, idx), '9.4f')}"
+            f"{fmt(ratio(wait, wcyc), '6.2f')}{fmt(ratio(ldsi, wcyc), '9.3f')}"
+            f"{fmt(ratio(bcu, bse, 32.0), '7.1f')}"
+            f"{fmt(rd_b / 1e6 if rd_b is not None else None, '9.1f')}"
+            f"{fmt(wr_b / 1e6 if wr_b is not None else None, '9.1f')}{algo / 1e6:9.1f}"
+            f"{fmt(ratio((rd_b or 0) + (wr_b or 0), algo) if rd_b and wr_b else None, '9.2f')}")
+    print("\n".join(out))
+    return 0
+
+
+RASTER_SETTINGS = ["8", "1", "2", "3", "4", "16", "32", "8,noxcd", "4,noxcd", "1,noxcd"]
+# the dispatched kernels of the large shapes: the headline, 4096^3, the row shard and a
+# 4096-token layer product
+RASTER_SHAPES = [("square_8192", None), ("square_4096", None),
+                 ("shard_1024x8192x8192", None), ("layer_4096x11008x4096", (4096, 11008, 4096, 7103))]
+
+
+def _raster_shapes():
     import tdb_inputs as ti
-    M, N, K, seed = ti.WORKLOADS[HEADLINE]
-    a, b = ti.workload_inputs(M, N, K, seed)
-    return (M, N, K, torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev),
-            torch.empty((M, N), device=dev))
+    return [(name, shape or ti.WORKLOADS[name]) for name, shape in RASTER_SHAPES]
 
 
 def raster_run(calib_mib: int, timed: bool, args=None) -> int:
-    """The headline product under each workgroup order: three launches per order for the
-    counter passes, or (timed) the per-order time from HIP events."""
+    """The dispatched product of each raster shape under each workgroup order: three
+    launches per order for the counter passes, or (timed) the per-order time from HIP
+    events, rounds rotating the order of the settings."""
     import torch
 
+    import tdb_inputs as ti
     import tiled_double_buffered_amd as tdb
 
     dev = torch.device("cuda:0")
     _calibration_copy(torch, dev, calib_mib)
     stream = torch.cuda.current_stream(dev)
     s_ptr = stream.cuda_stream
-    M, N, K, A, B, C = _headline_operands(torch, dev)
-
-    def step():
-        rc = tdb.gemm_f32(M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N, s_ptr)
-        if rc != tdb.OK:
-            raise tdb.GemmError(rc, "gemm_f32")
-    out = {}
     time_call = _timer(torch, stream)
+    out = {}
+    for name, (M, N, K, seed) in _raster_shapes():
+        a, b = ti.workload_inputs(M, N, K, seed)
+        A, B = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+        C = torch.empty((M, N), device=dev)
+
+        def step():
+            rc = tdb.gemm_f32(M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N, s_ptr)
+            if rc != tdb.OK:
+                raise tdb.GemmError(rc, "gemm_f32")
+        if timed:
+            _prewarm(torch, step)
+        rounds = args.rounds if (timed and args) else 1
+        times = {}
+        n = len(RASTER_SETTINGS)
+        for r in range(rounds):
+            order = RASTER_SETTINGS[r % n:] + RASTER_SETTINGS[:r % n] if timed else RASTER_SETTINGS
+            for setting in order:
+                os.environ["GEMMF32_RASTER"] = setting  # read by the library at every launch
+                if timed:
+                    times.setdefault(setting, []).append(
+                        time_call(step, args.batch_ms, args.batches)[0])
+                else:
+                    for _ in range(3):
+                        step()
+                    torch.cuda.synchronize()
+            print(f"[raster] {name} round {r} done", file=sys.stderr, flush=True)
+        os.environ.pop("GEMMF32_RASTER", None)
+        out[name] = {st: round(statistics.median(v), 2) for st, v in times.items()}
+        del A, B, C
     if timed:
-        _prewarm(torch, step)
-    rounds = args.rounds if (timed and args) else 1
-    for r in range(rounds):
-        order = RASTER_SETTINGS[r % len(RASTER_SETTINGS):] + RASTER_SETTINGS[:r % len(RASTER_SETTINGS)]
-        for setting in (order if timed else RASTER_SETTINGS):
-            os.environ["GEMMF32_RASTER"] = setting  # read by the library at every launch
-            if timed:
-                out.setdefault(setting, []).append(
-                    time_call(step, args.batch_ms, args.batches)[0])
-            else:
-                for _ in range(3):
-                    step()
-                torch.cuda.synchronize()
-            print(f"[raster] {setting} done", file=sys.stderr, flush=True)
-    os.environ.pop("GEMMF32_RASTER", None)
-    if timed:
-        print(json.dumps({s: round(statistics.median(v), 2) for s, v in out.items()}),
-              flush=True)
+        print(json.dumps(out), flush=True)
     return 0
 
 
 def write_raster_traffic(fetch_dir, write_dir, time_json, calib_mib=512) -> int:
-    """Per workgroup order of the headline kernel: calibrated HBM read and write bytes per
-    launch (the order's three dispatches, in launch order) and its time."""
-    import tdb_inputs as ti
+    """Per raster shape and workgroup order of its dispatched kernel: calibrated HBM read
+    and write bytes per launch (the order's three dispatches, in launch order) and its
+    time."""
     import tiled_double_buffered_amd as tdb
-
-    M, N, K, _ = ti.WORKLOADS[HEADLINE]
-    desc, is_gemm = _kernel_match(tdb, M, N, K)
 
     def is_calib(name, g):
         return "neg" in name.lower() and "gemm" not in name
@@ -544,29 +737,37 @@ def write_raster_traffic(fetch_dir, write_dir, time_json, calib_mib=512) -> int:
         return [per[d] for d in sorted(per)]
 
     fr, wr = _counter_rows(fetch_dir), _counter_rows(write_dir)
-    gf, gw = per_dispatch(fr, "FETCH_SIZE", is_gemm), per_dispatch(wr, "WRITE_SIZE", is_gemm)
     cf, cw = per_dispatch(fr, "FETCH_SIZE", is_calib), per_dispatch(wr, "WRITE_SIZE", is_calib)
-    n = len(RASTER_SETTINGS)
-    if len(gf) != 3 * n or len(gw) != 3 * n or not cf or not cw:
-        print(f"unexpected dispatch counts: {len(gf)} {len(gw)} {len(cf)} {len(cw)}",
-              file=sys.stderr)
+    if not cf or not cw:
+        print("no calibration kernel in the passes", file=sys.stderr)
         return 1
     sf, sw = calib_mib * 1024.0 / cf[0], calib_mib * 1024.0 / cw[0]
     with open(time_json) as f:
-        times = json.load(f)
-    algo = 4.0 * (M * K + K * N + M * N)
-    print(f"# HBM traffic and time of the headline kernel ({desc}, {M}x{N}x{K}) per "
-          "workgroup order")
+        times = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    n = len(RASTER_SETTINGS)
+    print("# HBM traffic and time of the dispatched kernel per workgroup order "
+          "(GEMMF32_RASTER = group height[,noxcd])")
     print(f"# bytes = counter KiB x 1024 x calibration factor (read {sf:.4f}, write {sw:.4f}: "
-          f"{calib_mib} MiB over the negate kernel's readings); algorithmic {algo / 1e9:.3f} GB")
-    print(f"{'GEMMF32_RASTER':>16} {'read_GB':>8} {'write_GB':>9} {'total/algo':>10} "
-          f"{'us':>9}")
-    for i, setting in enumerate(RASTER_SETTINGS):
-        rd = statistics.median(gf[3 * i:3 * i + 3]) * 1024 * sf
-        wt = statistics.median(gw[3 * i:3 * i + 3]) * 1024 * sw
-        print(f"{setting:>16} {rd / 1e9:8.3f} {wt / 1e9:9.3f} {(rd + wt) / algo:10.2f} "
-              f"{times.get(setting, float('nan')):9.1f}")
-    return 0
+          f"{calib_mib} MiB over the negate kernel's readings); us = event time per launch")
+    rc = 0
+    for name, (M, N, K, _) in _raster_shapes():
+        desc, match = _kernel_match(tdb, M, N, K)
+        gf, gw = per_dispatch(fr, "FETCH_SIZE", match), per_dispatch(wr, "WRITE_SIZE", match)
+        if len(gf) != 3 * n or len(gw) != 3 * n:
+            print(f"{name}: unexpected dispatch counts {len(gf)} {len(gw)}", file=sys.stderr)
+            rc = 1
+            continue
+        algo = 4.0 * (M * K + K * N + M * N)
+        print(f"\n{name} ({M}x{N}x{K}), {desc}; algorithmic {algo / 1e9:.3f} GB")
+        print(f"{'GEMMF32_RASTER':>16} {'read_GB':>8} {'write_GB':>9} {'total/algo':>10} "
+              f"{'us':>9}")
+        t = times.get(name, {})
+        for i, setting in enumerate(RASTER_SETTINGS):
+            rd = statistics.median(gf[3 * i:3 * i + 3]) * 1024 * sf
+            wt = statistics.median(gw[3 * i:3 * i + 3]) * 1024 * sw
+            print(f"{setting:>16} {rd / 1e9:8.3f} {wt / 1e9:9.3f} {(rd + wt) / algo:10.2f} "
+                  f"{t.get(setting, float('nan')):9.1f}")
+    return rc
 
 
 # ------------------------------------------------------------------ other modes
@@ -735,8 +936,13 @@ def main() -> int:
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", metavar="DIR")
+    ap.add_argument("--timed-headline", metavar="LINE_FILE",
+                    help="with --summarize-trace: the timed steps of the bench run whose JSON "
+                         "line is in LINE_FILE")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     ap.add_argument("--counter-run", action="store_true")
+    ap.add_argument("--counter-table", nargs=len(COUNTER_PASSES),
+                    metavar=tuple(k.upper() + "_DIR" for k in COUNTER_PASSES))
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--oracle-table", action="store_true")
     ap.add_argument("--raster-run", action="store_true")
@@ -753,10 +959,14 @@ def main() -> int:
         return write_traffic(*args.write_traffic)
     if args.counter_run:
         return counter_run(args.copy_calibration)
+    if args.counter_table:
+        return counter_table(dict(zip(COUNTER_PASSES, args.counter_table)))
     if args.raster_run or args.raster_time:
         return raster_run(args.copy_calibration, args.raster_time, args)
     if args.write_raster_traffic:
         return write_raster_traffic(*args.write_raster_traffic)
+    if args.summarize_trace and args.timed_headline:
+        return summarize_timed_headline(args.summarize_trace, args.timed_headline)
     if args.summarize_trace:
         return summarize_trace(args.summarize_trace)
     if args.summarize_counters:
@@ -810,7 +1020,7 @@ def main() -> int:
 
     log(f"[bench] {PREWARM_S * 1e3:.0f} ms of untimed launches, then warmup {args.warmup} "
         f"steps (variant {variant}, cfg {cfg}) ...")
-    _prewarm(torch, step)
+    untimed = _prewarm(torch, step) + args.warmup
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -997,6 +1207,9 @@ def main() -> int:
         "per_shape": per_shape,
         "protocol": {"headline": f"{PREWARM_S * 1e3:.0f} ms untimed, {args.warmup} warm-up "
                                  f"steps, {args.steps} timed steps",
+                     # in a kernel trace of this run, the timed steps are launches
+                     # untimed .. untimed + steps - 1 of the headline kernel
+                     "headline_launches_before_timed": untimed,
                      "per_shape": f"{args.rounds} rotated rounds x {args.batches} batches of "
                                   f">= {args.batch_ms} ms; medians of the per-round medians"},
         "parity": parity,

@@ -422,11 +422,13 @@ def test_square_3072_full_on_192_tiles():
 
 
 @pytest.mark.slow
-def test_square_8192_sampled():
-    """8192^3 in the launch configuration the benchmark times (dispatcher), checked on the
-    workload's 4096 seeded output positions, plus the same positions for both variants."""
-    M, N, K, seed = ti.WORKLOADS["square_8192"]
-    _say("[parity] square_8192 generating inputs ...")
+@pytest.mark.parametrize("name", ["square_8192", "shard_1024x8192x8192"])
+def test_large_workload_sampled(name):
+    """8192^3, and the one-GPU share of its eight-way row split (1024 x 8192 x 8192), in the
+    launch configuration the benchmark times (dispatcher), checked on the workload's 4096
+    seeded output positions, plus the same positions for the SB, DB and MS variants."""
+    M, N, K, seed = ti.WORKLOADS[name]
+    _say(f"[parity] {name} generating inputs ...")
     A, B = ti.workload_inputs(M, N, K, seed)
     ri, rj = ti.sample_positions(seed, M, N, 4096)
     c64, bnd = oracle.gemm_f64_sampled(A, B, ri, rj)
@@ -437,7 +439,7 @@ def test_square_8192_sampled():
         C = _run(Ad, Bd, v)
         got = C[ii, jj].cpu().numpy()
         r = oracle.tolerance_ratio(got, c64, bnd)
-        _say(f"[parity] square_8192 {v} sampled ratio={r:.3g}")
+        _say(f"[parity] {name} {v} sampled ratio={r:.3g}")
         assert r <= 1.0, v
         assert torch.isfinite(C).all()
         del C

@@ -125,6 +125,34 @@ def test_barriers_per_k_step(kernels):
             assert 1 <= outside <= 3 * len(loops), (k["cfg"], k["kind"], outside)
 
 
+def test_bench_pair_keeps_two_and_one_barriers(kernels):
+    """The single- against double-buffered pair that bench.py reports per workload shape
+    runs on a configuration whose single-buffered loop holds two barriers per K tile and
+    whose double-buffered loop holds one (one-wave workgroups, whose barriers the compiler
+    drops, never form the pair)."""
+    import bench
+    import tdb_inputs as ti
+    import tiled_double_buffered_amd as tdb
+    for name, (M, N, K, _) in ti.WORKLOADS.items():
+        sb = tdb.gemm_f32_select_cfg(M, N, K, tdb.VARIANT_SB)
+        db = tdb.gemm_f32_select_cfg(M, N, K, tdb.VARIANT_DB)
+        c = bench._pair_cfg(tdb, sb, db)
+        _, i = tdb.gemm_f32_config_info(c)
+        assert i["threads"] >= 128, (name, c)
+        per_kind = {}
+        for k in kernels.values():
+            bm, bn, bk, wm, wn = k["cfg"]
+            if (bm, bn, bk) == (i["BM"], i["BN"], i["BK"]) and wm * wn * 64 == i["threads"] \
+                    and k["kind"] in ("sb", "db"):
+                per_tile = _mfma_per_tile(k["cfg"])
+                for ls in _loop_blocks(k["body"]).values():
+                    bars = _count_barriers(ls)
+                    mfma = sum(1 for t in ls if t.startswith("v_mfma"))
+                    if bars:
+                        per_kind.setdefault(k["kind"], set()).add(bars * per_tile // mfma)
+        assert per_kind == {"sb": {2}, "db": {1}}, (name, c, per_kind)
+
+
 def test_no_scratch_and_lds_fits(kernels):
     for name, k in kernels.items():
         meta = k["meta"]
