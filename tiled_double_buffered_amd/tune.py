@@ -513,13 +513,13 @@ def split_study(shapes=SPLIT_SHAPES, choices=SPLIT_CHOICES, rounds=2, batches=5,
 
 
 RASTER_SHAPES = [(4096, 4096, 4096), (8192, 8192, 8192), (6144, 6144, 6144)]
-RASTER_SETTINGS = ["", "1", "2", "3", "4", "16", "32", "8,noxcd", "1,noxcd"]
+RASTER_SETTINGS = ["", "1", "2", "3", "8", "16", "32", "4,noxcd", "8,noxcd", "1,noxcd"]
 
 
 def raster_study(shapes=RASTER_SHAPES, settings=RASTER_SETTINGS, rounds=2, batches=5,
                  batch_ms=20.0, log=print):
     """The dispatched kernel of each shape under different workgroup orders
-    (GEMMF32_RASTER; "" is the built-in default: group 8 with XCD renumbering)."""
+    (GEMMF32_RASTER; "" is the built-in default: group 4 with XCD renumbering)."""
     out = []
     for (M, N, K) in shapes:
         A, B, C = _operands(M, N, K)
