@@ -41,9 +41,10 @@ Also:
   python bench.py --summarize-counters DIR   per-(kernel, grid) average counter values
                                              from rocprofv3 --pmc runs (counter_collection.csv)
   python bench.py --layer-shapes             decode and layer products (1 to 4096 rows
-                                             against 4096- and 11008-wide layers): gemm_f32,
-                                             the 16-row K-split kernel, both split-K entry
-                                             points and torch.matmul, each output checked
+                                             against 4096- to 32000-wide layers): gemm_f32,
+                                             each 16-row K-split configuration, both split-K
+                                             entry points and torch.matmul, each output
+                                             checked
   python bench.py --k-slope                  1024 x 1024 x K for K = 32 .. 2048 on the 1024^3
                                              kernels: the fixed cost of a launch and the time
                                              per K tile against the matrix-core time per K tile
@@ -100,7 +101,8 @@ PREWARM_S = 0.2                        # untimed launches before the warm-up ste
 # 11008 x 4096 weight matrix.  The pages name only the regime ("the regime LLM decode
 # lives in"); the widths are those of a common 7-billion-parameter transformer layer.
 LAYER_SHAPES = [(1, 4096, 4096), (8, 4096, 4096), (16, 4096, 4096), (16, 11008, 4096),
-                (16, 4096, 11008), (128, 4096, 4096), (128, 11008, 4096), (128, 4096, 11008),
+                (16, 4096, 11008), (16, 8192, 8192), (16, 32000, 4096),
+                (128, 4096, 4096), (128, 11008, 4096), (128, 4096, 11008),
                 (512, 4096, 4096), (512, 4096, 11008), (4096, 4096, 4096),
                 (4096, 11008, 4096)]
 
@@ -242,7 +244,10 @@ def _kernel_match(tdb, M, N, K, variant=None, cfg=None):
     grid = str(((M + info["BM"] - 1) // info["BM"]) * ((N + info["BN"] - 1) // info["BN"])
                * threads)
     if variant == tdb.VARIANT_KS and tdb.gemm_f32_config_variants(cfg) == 1 << variant:
-        kname, tag, flag = "gemm_f32_ks16_kernel", "Ks16Cfg<", ""
+        # Ks16Cfg<waves, 16-k blocks per group, strided, 16-column blocks>
+        kname, flag = "gemm_f32_ks16_kernel", ""
+        tag = "Ks16Cfg<%d, %d, false, %d>" % (tdb.gemm_f32_config_ks(cfg), info["BK"] // 16,
+                                               info["BN"] // 16)
     else:
         tag = f"TileCfg<{info['BM']}, {info['BN']}, {info['BK']},"
         if variant == tdb.VARIANT_MS:
@@ -810,10 +815,9 @@ def layer_shapes(args) -> int:
         if need <= tdb.SCRATCH_FLOATS:
             fns["splitk_noalloc"] = lambda: tdb.gemm_f32_splitk_noalloc(
                 M, N, K, pa, K, pb, N, pc, N, splits, s_ptr)
-        if ks16 and M <= 32:
-            c16 = ks16[0]
-            fns["ks16"] = lambda: tdb.gemm_f32_ex(M, N, K, pa, K, pb, N, pc, N,
-                                                  tdb.VARIANT_KS, c16, s_ptr)
+        for c16 in (ks16 if M <= 32 else ()):
+            fns[f"ks16_cfg{c16}"] = lambda c16=c16: tdb.gemm_f32_ex(
+                M, N, K, pa, K, pb, N, pc, N, tdb.VARIANT_KS, c16, s_ptr)
         fns["torch"] = lambda: torch.matmul(A, B, out=C)
         _prewarm(torch, fns["gemm_f32"], 0.05)
         row = {"M": M, "N": N, "K": K, "splits": splits,

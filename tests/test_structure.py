@@ -27,10 +27,11 @@ def kernels():
     assert funcs and set(funcs) <= set(meta)
     out = {}
     for name, body in funcs.items():
-        m16 = re.search(r"Ks16CfgILi(\d+)E", name)
-        if m16:  # the 16-row K-split kernel: a 16 x 16 tile, 16 k per block
-            out[name] = dict(cfg=(16, 16, 16, int(m16.group(1)), 1), kind="ks16", db=False,
-                             ms=False, stages=2, body=body, meta=meta[name])
+        m16 = re.search(r"Ks16CfgILi(\d+)ELi(\d+)ELb[01]ELi(\d+)E", name)
+        if m16:  # the 16-row K-split kernel: a 16 x 16 CB tile, 16 k per block
+            cb = int(m16.group(3))
+            out[name] = dict(cfg=(16, 16 * cb, 16, int(m16.group(1)), 1), kind="ks16",
+                             db=False, ms=False, stages=2, cb=cb, body=body, meta=meta[name])
             continue
         m = re.search(r"TileCfgILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEE(?:Lb([01])|Li(\d+))E",
                       name)
@@ -177,9 +178,9 @@ def test_mfma_count_matches_tile(kernels):
     """One K tile is FM * FN * BK / 2 MFMAs per wave (each MFMA consumes a k pair); every
     kernel holds whole copies of that tile body (loops, unrolled steps, peeled tiles)."""
     for name, k in kernels.items():
-        if k["kind"] == "ks16":  # 4 MFMAs of 16 x 16 x 4 per 16-deep block of a K group
+        if k["kind"] == "ks16":  # 4 MFMAs of 16 x 16 x 4 per 16-deep block and column block
             n = len(re.findall(r"\bv_mfma_f32_16x16x4_f32\b", k["body"]))
-            assert n > 0 and n % 4 == 0, (k["cfg"], n)
+            assert n > 0 and n % (4 * k["cb"]) == 0, (k["cfg"], n)
             continue
         per_tile = _mfma_per_tile(k["cfg"])
         n = len(re.findall(r"\bv_mfma_f32_32x32x2_f32\b", k["body"]))

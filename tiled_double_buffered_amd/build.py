@@ -25,7 +25,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 MAIN_SOURCE = os.path.join(CSRC, "gemm_f32.hip")
 CFG_SOURCE = os.path.join(CSRC, "cfg_kernels.hip")
-NUM_CONFIGS = 15  # configs.h: kNumConfigs
+NUM_CONFIGS = 18  # configs.h: kNumConfigs
 SOURCES = [MAIN_SOURCE, CFG_SOURCE]
 HEADERS = [os.path.join(CSRC, f) for f in ("configs.h", "gemm_common.h", "kernels_sb_db.h",
                                             "kernels_ms.h", "kernels_ks.h", "kernels_ks16.h", "splitk_reduce.h",
@@ -196,10 +196,11 @@ def resources_table(asm: str) -> str:
     meta = kernel_metadata(asm)
     rows = ["kernel                         vgpr agpr sgpr  lds_B scratch  loops: barriers/MFMAs"]
     for name, body in sorted(kernel_functions(asm).items()):
-        m16 = re.search(r"Ks16CfgILi(\d+)ELi(\d+)E", name)
-        if m16:  # the 16-row K-split kernel: 16 x 16 tile, 16-k blocks per group, W waves
+        m16 = re.search(r"Ks16CfgILi(\d+)ELi(\d+)ELb[01]ELi(\d+)E", name)
+        if m16:  # the 16-row K-split kernel: 16 x 16 CB tile, 16-k blocks per group, W waves
             kind = "ks%s" % m16.group(1)
-            tile = "16x16x%d/%sx1" % (16 * int(m16.group(2)), m16.group(1))
+            tile = "16x%dx%d/%sx1" % (16 * int(m16.group(3)), 16 * int(m16.group(2)),
+                                      m16.group(1))
         else:
             m = re.search(r"TileCfgILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEELi(\d+)E", name)
             kind = "ms%s" % m.group(6) if "_ms_kernel" in name else \

@@ -47,7 +47,7 @@ CfgEntry make_entry() {
                   KS};
 }
 
-// The 16-row decode configuration: the K-split kernel only.
+// The 16-row decode configurations: the K-split kernel only.
 template <class D>
 CfgEntry make_ks16_entry() {
   return CfgEntry{D::BM, D::BN, D::KG, 64, 0, 0, 0, 0, nullptr, nullptr, nullptr, nullptr,
@@ -58,9 +58,9 @@ template <class T>
 struct EntryOf {
   static CfgEntry get() { return make_entry<T>(); }
 };
-template <int WAVES, int BLOCKS, bool STRIDED>
-struct EntryOf<Ks16Cfg<WAVES, BLOCKS, STRIDED>> {
-  static CfgEntry get() { return make_ks16_entry<Ks16Cfg<WAVES, BLOCKS, STRIDED>>(); }
+template <int WAVES, int BLOCKS, bool STRIDED, int CB>
+struct EntryOf<Ks16Cfg<WAVES, BLOCKS, STRIDED, CB>> {
+  static CfgEntry get() { return make_ks16_entry<Ks16Cfg<WAVES, BLOCKS, STRIDED, CB>>(); }
 };
 
 #define GEMMF32_CAT2(a, b) a##b

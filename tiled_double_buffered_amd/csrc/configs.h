@@ -26,14 +26,17 @@ template <> struct CfgById<11> { using type = TileCfg<192, 192, 16, 2, 2>; };  /
 template <> struct CfgById<12> { using type = TileCfg<192, 192, 32, 2, 2>; };  // wave 96x96, deeper K tile
 template <> struct CfgById<13> { using type = TileCfg<32, 32, 32, 1, 1>; };    // one wave: few rows, long K (K-split kernel)
 template <> struct CfgById<14> { using type = Ks16Cfg<16, 2>; };               // 16 x 16 tile, 16 waves over K in 32-deep groups: decode rows (K-split only)
-constexpr int kNumConfigs = 15;
+template <> struct CfgById<15> { using type = Ks16Cfg<8, 2, false, 2>; };      // 16 x 32 tile, 8 waves over K: 128-byte rows of B
+template <> struct CfgById<16> { using type = Ks16Cfg<8, 2, false, 4>; };      // 16 x 64 tile, 8 waves over K: wide layers
+template <> struct CfgById<17> { using type = Ks16Cfg<4, 2, false, 2>; };      // 16 x 32 tile, 4 waves over K: several workgroups per CU
+constexpr int kNumConfigs = 18;
 
 typedef void (*KernelFn)(int, int, int, const float*, int64_t, const float*, int64_t, float*,
                          int64_t, int, SplitArgs);
 
 // ms: the multi-stage kernel, where the configuration has one (its swizzle needs tiles
 // of B at least 64 wide; stages 0 otherwise); ks: the K-split kernel and its wave groups,
-// where it has one (groups 1 otherwise).  The 16-row configuration has only a K-split
+// where it has one (groups 1 otherwise).  The 16-row configurations have only a K-split
 // kernel (sb, db and sb3 null, no LDS slots).
 struct CfgEntry {
   int bm, bn, bk, nt;
@@ -50,6 +53,7 @@ GEMMF32_CFG_ENTRY_DECL(3) GEMMF32_CFG_ENTRY_DECL(4) GEMMF32_CFG_ENTRY_DECL(5)
 GEMMF32_CFG_ENTRY_DECL(6) GEMMF32_CFG_ENTRY_DECL(7) GEMMF32_CFG_ENTRY_DECL(8)
 GEMMF32_CFG_ENTRY_DECL(9) GEMMF32_CFG_ENTRY_DECL(10) GEMMF32_CFG_ENTRY_DECL(11)
 GEMMF32_CFG_ENTRY_DECL(12) GEMMF32_CFG_ENTRY_DECL(13) GEMMF32_CFG_ENTRY_DECL(14)
+GEMMF32_CFG_ENTRY_DECL(15) GEMMF32_CFG_ENTRY_DECL(16) GEMMF32_CFG_ENTRY_DECL(17)
 #undef GEMMF32_CFG_ENTRY_DECL
 
 }  // namespace gemmf32

@@ -12,10 +12,12 @@ namespace gemmf32 {
 // GFLOP, so reading B bounds the time.  The 32 x 32 blocks of the other kernels waste half
 // their rows at M = 16, and a 32-column tile gives only 128 tiles at N = 4096.
 //
-// Here a workgroup owns a 16 x 16 tile of C (256 tiles at N = 4096: one per compute unit)
-// and its WAVES waves split the tile's K range: wave w multiplies its contiguous share of
-// the K groups (KG k each) on v_mfma_f32_16x16x4_f32, then the waves' sums meet in LDS and
-// are added in wave order.  Deterministic; no workspace.
+// Here a workgroup owns a 16 x 16 CB tile of C (CB = 1: 256 tiles at N = 4096, one per
+// compute unit) and its WAVES waves split the tile's K range: wave w multiplies its share
+// of the K groups (KG k each) on v_mfma_f32_16x16x4_f32, one accumulator per 16-column
+// block, then the waves' sums meet in LDS and are added in wave order.  Deterministic; no
+// workspace.  Wider tiles (CB = 2, 4) read B in 128- and 256-byte row segments and load
+// each A fragment once for CB blocks; they pay off where N leaves enough tiles.
 //
 // A K group's operands are used by one wave only, so nothing is shared through LDS: each
 // wave loads them straight into the matrix instruction's operand registers, two register
@@ -23,29 +25,30 @@ namespace gemmf32 {
 // next tile into the idle buffer, with registers as the buffers).  For the instruction,
 // lane l supplies A[l mod 16][kk] and B[kk][l mod 16] with kk = l div 16, and register i of
 // lane l receives D[4 (l div 16) + i][l mod 16].  Lane l (r = l mod 16, s = l div 16) reads
-// A[r][k0 + 4s .. 4s + 3] with one 16-byte load per 16 k, and B[k0 + 4s + t][r] for t = 0..3
-// with one 4-byte load each, so that step t of the 16 k consumes its k values
-// k0 + 4s + t: the four steps cover the 16 k once each.
+// A[r][k0 + 4s .. 4s + 3] with one 16-byte load per 16 k, and B[k0 + 4s + t][16c + r] for
+// t = 0..3 and each block c with one 4-byte load each, so that step t of the 16 k consumes
+// its k values k0 + 4s + t: the four steps cover the 16 k once each.
 // ------------------------------------------------------------------------------------
-template <int WAVES_, int BLOCKS_ = 4, bool STRIDED_ = false>
+template <int WAVES_, int BLOCKS_ = 4, bool STRIDED_ = false, int CB_ = 1>
 struct Ks16Cfg {
   static constexpr int WAVES = WAVES_;
   static constexpr int NT = 64 * WAVES;
-  static constexpr int BM = 16, BN = 16;
+  static constexpr int CB = CB_;            // 16-column blocks of the tile
+  static constexpr int BM = 16, BN = 16 * CB;
   static constexpr int BLOCKS = BLOCKS_;    // 16-k blocks per group
   static constexpr int KG = 16 * BLOCKS;    // k per group
   // STRIDED: wave w takes groups w, w + WAVES, w + 2 WAVES, ... (the workgroup walks K in
   // one front); otherwise a contiguous share of the groups
   static constexpr bool STRIDED = STRIDED_;
   static_assert(NT <= 1024, "threads of one workgroup");
-  static_assert(NT >= 256, "the hand-off sums the tile's 256 elements one per thread");
+  static_assert(NT >= 256, "the hand-off sums each 256-element column block with 256 threads");
 };
 
 // One group's operands in this lane's registers.
 template <class D>
 struct Ks16Set {
-  floatx4 a[D::BLOCKS];     // A[r][k0 + 16j + 4s + t], t = 0..3
-  float b[D::BLOCKS][4];    // B[k0 + 16j + 4s + t][r]
+  floatx4 a[D::BLOCKS];            // A[r][k0 + 16j + 4s + t], t = 0..3
+  float b[D::BLOCKS][D::CB][4];    // B[k0 + 16j + 4s + t][16c + r]
 };
 
 template <class D>
@@ -89,22 +92,28 @@ struct Ks16Loader {
       const auto rb = rsrc(B + b_first, range_from(b_bytes, b_first));
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        st.b[j][t] = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rb, (int)b_off[t], 0, 0));
+#pragma unroll
+        for (int c = 0; c < D::CB; ++c)
+          st.b[j][c][t] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(rb, (int)(b_off[t] + 64 * c), 0, 0));
     }
   }
 
   // Element by element, anything outside M x K (A) or K x N (B) reads 0.
   __device__ inline void load_guarded(int g, Ks16Set<D>& st) const {
     const int k0 = g * D::KG;
-    const int row = m0 + r, col = n0 + r;
+    const int row = m0 + r;
 #pragma unroll
     for (int j = 0; j < D::BLOCKS; ++j)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int k = k0 + 16 * j + 4 * s + t;
         st.a[j][t] = (row < M && k < K) ? A[(int64_t)row * lda + k] : 0.0f;
-        st.b[j][t] = (k < K && col < N) ? B[(int64_t)k * ldb + col] : 0.0f;
+#pragma unroll
+        for (int c = 0; c < D::CB; ++c) {
+          const int col = n0 + 16 * c + r;
+          st.b[j][c][t] = (k < K && col < N) ? B[(int64_t)k * ldb + col] : 0.0f;
+        }
       }
   }
 
@@ -121,19 +130,22 @@ struct Ks16Loader {
 };
 
 template <class D>
-__device__ __forceinline__ void ks16_mfma(const Ks16Set<D>& st, floatx4& acc) {
+__device__ __forceinline__ void ks16_mfma(const Ks16Set<D>& st, floatx4 (&acc)[D::CB]) {
 #pragma unroll
   for (int j = 0; j < D::BLOCKS; ++j)
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(st.a[j][t], st.b[j][t], acc, 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < D::CB; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(st.a[j][t], st.b[j][c][t], acc[c], 0, 0,
+                                                      0);
 }
 
 // Groups g0, g0 + gs, ... below g1 of one wave, two register sets in turn; FAST: buffer
 // loads.
 template <class D, bool FAST>
 __device__ inline void ks16_loop(const Ks16Loader<D>& ld, int g0, int g1, int gs,
-                                 floatx4& acc) {
+                                 floatx4 (&acc)[D::CB]) {
   const int tail = ld.K % D::KG ? (ld.K - 1) / D::KG : -1;  // the group to mask, if any
   Ks16Set<D> s0, s1;
   auto load = [&](int g, Ks16Set<D>& st) {
@@ -169,7 +181,7 @@ __global__ void __launch_bounds__(D::NT)
 gemm_f32_ks16_kernel(int M, int N, int K, const float* __restrict__ A, int64_t lda,
                      const float* __restrict__ B, int64_t ldb, float* __restrict__ Cmat,
                      int64_t ldc, int flags, SplitArgs sp) {
-  __shared__ __attribute__((aligned(16))) float red[D::WAVES * 256];
+  __shared__ __attribute__((aligned(16))) float red[D::WAVES * 256 * D::CB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -208,25 +220,34 @@ gemm_f32_ks16_kernel(int M, int N, int K, const float* __restrict__ A, int64_t l
     g1 = (int)((int64_t)groups * (wave + 1) / D::WAVES);
     gs = 1;
   }
-  floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  floatx4 acc[D::CB];
+#pragma unroll
+  for (int c = 0; c < D::CB; ++c) acc[c] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   if ((flags & kVecA) && (flags & kVecB))
     ks16_loop<D, true>(ld, g0, g1, gs, acc);
   else
     ks16_loop<D, false>(ld, g0, g1, gs, acc);
 
-  // Hand-off: register i of lane l of wave w goes to red[w][i][l]; thread t < 256 then adds
-  // element t's WAVES sums in wave order and stores it (row 4 (l div 16) + i, column l mod 16
-  // of the tile, with i = t div 64 and l = t mod 64).
+  // Hand-off: register i of lane l of wave w, column block c, goes to red[w][c][i][l];
+  // then element e (e = tid, tid + NT, ... below 256 CB) is added over the WAVES sums in
+  // wave order and stored: column block c = e div 256, row 4 (l div 16) + i, column
+  // 16 c + l mod 16 of the tile, with i = (e div 64) mod 4 and l = e mod 64.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave * 256 + i * 64 + lane] = acc[i];
+  for (int c = 0; c < D::CB; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wave * D::CB + c) * 256 + i * 64 + lane] = acc[c][i];
   __syncthreads();
-  if (tid < 256) {
-    float sum = red[tid];
 #pragma unroll
-    for (int w = 1; w < D::WAVES; ++w) sum += red[w * 256 + tid];
-    const int l = tid & 63, i = tid >> 6;
-    const int row = ld.m0 + 4 * (l >> 4) + i, col = ld.n0 + (l & 15);
-    if (row < M && col < N) Cmat[(int64_t)row * ldc + col] = sum;
+  for (int e0 = 0; e0 < 256 * D::CB; e0 += D::NT) {
+    const int e = e0 + tid;
+    if (e < 256 * D::CB) {
+      float sum = red[e];
+#pragma unroll
+      for (int w = 1; w < D::WAVES; ++w) sum += red[w * 256 * D::CB + e];
+      const int c = e >> 8, l = e & 63, i = (e >> 6) & 3;
+      const int row = ld.m0 + 4 * (l >> 4) + i, col = ld.n0 + 16 * c + (l & 15);
+      if (row < M && col < N) Cmat[(int64_t)row * ldc + col] = sum;
+    }
   }
 }
 

@@ -16,6 +16,15 @@ shapes outside the table, fit the cost model that picks for every other shape.
     python -m tiled_double_buffered_amd.tune --holdout 40   # dispatcher regret on 40 seeded
                                                             # shapes outside the table
 
+The split-count study times the unsplit product through gemm_f32, that is through the
+dispatch table the library was built with.  After a change of the configurations, measure
+in two steps so that it sees the new table:
+
+    python -m tiled_double_buffered_amd.tune --no-split --out base.json   # GPU
+    python -m tiled_double_buffered_amd.tune --from-json base.json        # header; rebuild
+    python -m tiled_double_buffered_amd.tune --split-only base.json --out full.json   # GPU
+    python -m tiled_double_buffered_amd.tune --from-json full.json        # header; rebuild
+
 Timing does not depend on the values multiplied, so inputs are seeded uniform values.
 """
 from __future__ import annotations
@@ -58,9 +67,9 @@ SHAPES = [
     (1023, 1023, 1023), (4095, 4095, 4095),
     # skinny shapes (a small batch of rows against a wide layer)
     (16, 4096, 4096), (32, 4096, 4096), (128, 4096, 4096), (32, 8192, 8192),
-    # decode rows (1 to 16) against 4096- and 11008-wide layers, and a small one
+    # decode rows (1 to 16) against 4096- to 32000-wide layers, and a small one
     (1, 4096, 4096), (8, 4096, 4096), (16, 11008, 4096), (16, 4096, 11008),
-    (16, 8192, 8192), (4, 1024, 1024),
+    (16, 8192, 8192), (4, 1024, 1024), (16, 32000, 4096),
     # one GPU's share of 8192^3 split by rows over eight GPUs
     (1024, 8192, 8192),
 ]
