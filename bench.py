@@ -108,10 +108,14 @@ LAYER_SHAPES = [(1, 4096, 4096), (8, 4096, 4096), (16, 4096, 4096), (16, 11008, 
 
 
 def kernel_source_hash() -> str:
-    """SHA-256 over the library's sources and headers (the files its build compiles)."""
+    """SHA-256 over the library's sources and headers (the files its build compiles), less
+    the generated dispatch table: that decides which kernel a shape runs, not what any
+    kernel does, and the traffic file names the kernel it was taken on."""
     from tiled_double_buffered_amd import build
     h = hashlib.sha256()
     for p in build.DEPS:
+        if os.path.basename(p) == "dispatch_table.h":
+            continue
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -1053,13 +1057,15 @@ def main() -> int:
     except Exception as exc:
         parity = {"error": repr(exc), "pass": False}
 
-    # traffic from the committed counter summary, if it describes this kernel source
+    # traffic from the committed counter summary, if it was taken on this kernel (same
+    # sources, and the kernel the dispatcher picks for the headline now)
     traffic = None
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("kernel_source_sha256") == kernel_source_hash() and \
-                tr.get("workload") == HEADLINE:
+                tr.get("workload") == HEADLINE and \
+                tr.get("kernel") == _kernel_match(tdb, M, N, K)[0]:
             traffic = tr["hbm_bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         traffic = None

@@ -153,6 +153,18 @@ static inline double model_us(const ModelRow& r, int64_t M, int64_t N, int64_t K
          r.h_us * (double)tiles * (double)k_tiles / (double)kModelCUs;
 }
 
+// Above 16 rows every 16-row tile streams its strip of B again, ceil(M / 16) times in all.
+// How fast that goes depends on how much of it the caches catch, which the model above does
+// not see; measured, the 16-row kernels win above 16 rows while those re-reads stay small
+// and lose by up to 2x beyond (a 208 x 5875 x 8154 product streams 2.5 GB).  So the model
+// offers them above 16 rows only up to this many bytes of B streamed.
+constexpr double kRowTileStreamLimitBytes = 100e6;
+
+static inline bool model_allows(const CfgEntry& e, int64_t M, int64_t N, int64_t K) {
+  if (e.bm != 16 || M <= 16) return true;
+  return (double)((M + 15) / 16) * 4.0 * (double)N * (double)K <= kRowTileStreamLimitBytes;
+}
+
 // The row with the least modelled time (variant 0: any variant), first row on ties.
 static inline const ModelRow& model_pick(int64_t M, int64_t N, int64_t K, int variant,
                                          int64_t wg_factor) {
@@ -161,6 +173,7 @@ static inline const ModelRow& model_pick(int64_t M, int64_t N, int64_t K, int va
   bool found = false;
   for (int i = 0; i < kModelRows; ++i) {
     if (variant != 0 && kModel[i].variant != variant) continue;
+    if (!model_allows(kConfigs[kModel[i].cfg], M, N, K)) continue;
     // a split-K launch takes neither the K-split kernel (it divides K itself) nor a
     // one-wave configuration (its plain kernels keep one SIMD of a CU busy)
     if (wg_factor != 1 &&
@@ -196,15 +209,15 @@ static inline int select_for_variant(int64_t M, int64_t N, int64_t K, int varian
 // Split-K: the number of K chunks (1 = do not split) with the least modelled time among
 // the counts the split study measured.  A split launch costs the GEMM of its chunks, all in
 // one grid (the model above, with the workgroups multiplied by the chunks), plus
-//     3.0735 us (the reduction's launch)
-//   + 0.12906 us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
+//     3.1327 us (the reduction's launch)
+//   + 0.12757 us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
 //     written once and read once by the reduction, and C)
-//   + 0.6413 us per round of workgroups of the split grid (each workgroup's
+//   + 0.5608 us per round of workgroups of the split grid (each workgroup's
 //     first copy and partial-tile store, which short chunks no longer hide),
 // the constants fitted (>= 0, least squares) to the 41 shapes of the split study below.
-constexpr double kSplitFixedUs = 3.0735;
-constexpr double kSplitUsPerMB = 0.12906;
-constexpr double kSplitUsPerRound = 0.6413;
+constexpr double kSplitFixedUs = 3.1327;
+constexpr double kSplitUsPerMB = 0.12757;
+constexpr double kSplitUsPerRound = 0.5608;
 constexpr int kSplitChoices[] = {1, 2, 4, 8, 16};
 
 // The split study: trailing comments hold the measured microseconds of each count.
@@ -214,47 +227,47 @@ struct SplitRow {
 };
 
 static const SplitRow kSplitK[] = {
-    {16, 4096, 4096, 1},  // 1: 16.4, 2: 38.8, 4: 23.0, 8: 17.5, 16: 21.2
-    {32, 4096, 4096, 8},  // 1: 18.4, 2: 39.2, 4: 23.4, 8: 17.4, 16: 21.7
-    {64, 4096, 4096, 4},  // 1: 25.1, 2: 34.8, 4: 21.8, 8: 24.7, 16: 29.4
-    {128, 4096, 4096, 2},  // 1: 41.7, 2: 36.1, 4: 37.9, 8: 39.5, 16: 43.4
-    {32, 8192, 8192, 4},  // 1: 48.4, 2: 73.1, 4: 45.3, 8: 46.8, 16: 53.0
-    {64, 8192, 8192, 2},  // 1: 82.6, 2: 70.2, 4: 75.0, 8: 78.6, 16: 90.3
-    {256, 256, 8192, 16},  // 1: 24.0, 2: 63.0, 4: 34.9, 8: 22.1, 16: 17.1
-    {512, 512, 8192, 4},  // 1: 46.1, 2: 63.7, 4: 35.7, 8: 38.1, 16: 40.3
-    {1024, 1024, 1024, 1},  // 1: 18.0, 2: 24.8, 4: 29.2, 8: 32.8, 16: 40.4
-    {2048, 2048, 2048, 1},  // 1: 117.8, 2: 129.6, 4: 140.5, 8: 158.2, 16: 207.0
-    {4096, 4096, 4096, 1},  // 1: 905.9, 2: 945.9, 4: 997.8, 8: 1128.1, 16: 1293.4, -2: 1067.3, -4: 1081.1, -8: 1123.7, -16: 1175.1
-    {1536, 1536, 1536, -4},  // 1: 68.9, 2: 66.6, 4: 65.2, 8: 78.2, 16: 88.8, -2: 61.8, -4: 57.8, -8: 58.3, -16: 64.5
-    {1536, 1536, 4096, -8},  // 1: 175.2, 2: 155.2, 4: 143.4, 8: 155.2, 16: 177.0, -2: 150.6, -4: 140.1, -8: 137.9, -16: 141.5
-    {2560, 2560, 2560, -8},  // 1: 257.8, 2: 261.3, 4: 272.4, 8: 306.2, 16: 364.7, -2: 248.4, -4: 241.7, -8: 236.5, -16: 243.6
-    {1280, 1280, 2048, 1},  // 1: 62.2, 2: 66.2, 4: 68.0, 8: 71.9, 16: 83.5, -2: 67.1, -4: 62.3, -8: 65.6, -16: 67.2
-    {5000, 5000, 1000, -4},  // 1: 393.9, 2: 448.0, 4: 527.1, 8: 759.6, 16: 1154.5, -2: 391.1, -4: 378.2, -8: 379.9, -16: 385.8
-    {1536, 3072, 4096, -8},  // 1: 290.5, 2: 269.5, 4: 279.9, 8: 310.3, 16: 370.7, -2: 273.7, -4: 269.4, -8: 265.5, -16: 269.1
-    {39, 432, 6224, 16},  // 1: 17.5, 2: 56.2, 4: 31.9, 8: 20.5, 16: 16.2
+    {16, 4096, 4096, 1},  // 1: 16.4, 2: 38.9, 4: 23.0, 8: 17.5, 16: 21.3
+    {32, 4096, 4096, 8},  // 1: 18.5, 2: 39.2, 4: 23.4, 8: 17.2, 16: 21.7
+    {64, 4096, 4096, 4},  // 1: 25.1, 2: 34.9, 4: 21.1, 8: 24.1, 16: 28.9
+    {128, 4096, 4096, 2},  // 1: 39.7, 2: 35.7, 4: 37.3, 8: 39.3, 16: 43.4
+    {32, 8192, 8192, 4},  // 1: 48.1, 2: 73.3, 4: 45.2, 8: 46.4, 16: 52.2
+    {64, 8192, 8192, 2},  // 1: 79.2, 2: 66.6, 4: 70.6, 8: 74.5, 16: 85.3
+    {256, 256, 8192, 16},  // 1: 45.7, 2: 62.8, 4: 34.7, 8: 21.8, 16: 17.1
+    {512, 512, 8192, 4},  // 1: 46.0, 2: 63.4, 4: 35.6, 8: 37.6, 16: 40.3
+    {1024, 1024, 1024, 1},  // 1: 18.0, 2: 24.8, 4: 29.3, 8: 32.9, 16: 40.4
+    {2048, 2048, 2048, 1},  // 1: 117.4, 2: 129.2, 4: 140.0, 8: 157.8, 16: 206.2
+    {4096, 4096, 4096, 1},  // 1: 903.5, 2: 943.8, 4: 996.2, 8: 1124.1, 16: 1291.0, -2: 1064.5, -4: 1076.5, -8: 1119.3, -16: 1170.7
+    {1536, 1536, 1536, -4},  // 1: 68.1, 2: 66.3, 4: 64.7, 8: 77.8, 16: 88.7, -2: 61.4, -4: 57.0, -8: 57.9, -16: 64.1
+    {1536, 1536, 4096, -4},  // 1: 174.0, 2: 153.8, 4: 142.9, 8: 154.5, 16: 174.7, -2: 149.3, -4: 136.5, -8: 136.9, -16: 139.5
+    {2560, 2560, 2560, -8},  // 1: 255.7, 2: 258.3, 4: 267.9, 8: 302.6, 16: 363.5, -2: 242.3, -4: 240.3, -8: 233.3, -16: 241.5
+    {1280, 1280, 2048, -4},  // 1: 61.9, 2: 66.0, 4: 66.0, 8: 71.4, 16: 82.8, -2: 66.6, -4: 61.1, -8: 62.3, -16: 66.5
+    {5000, 5000, 1000, -4},  // 1: 392.8, 2: 442.8, 4: 522.5, 8: 758.3, 16: 1153.5, -2: 381.5, -4: 376.4, -8: 379.9, -16: 385.7
+    {1536, 3072, 4096, -4},  // 1: 289.4, 2: 269.6, 4: 280.2, 8: 310.0, 16: 370.0, -2: 266.9, -4: 265.8, -8: 265.9, -16: 269.6
+    {39, 432, 6224, 16},  // 1: 17.5, 2: 56.1, 4: 31.8, 8: 20.5, 16: 16.2
     {11, 1640, 2822, 1},  // 1: 9.8, 2: 29.1, 4: 18.4, 8: 13.1, 16: 12.2
-    {11, 1486, 1136, 1},  // 1: 5.3, 2: 14.5, 4: 10.9, 8: 9.6, 16: 9.6
-    {66, 326, 1317, 1},  // 1: 5.3, 2: 17.7, 4: 12.1, 8: 9.8, 16: 9.8
-    {63, 4495, 1443, 2},  // 1: 33.3, 2: 18.8, 4: 20.5, 8: 21.0, 16: 22.4
-    {24, 2252, 14173, 8},  // 1: 74.5, 2: 121.4, 4: 64.5, 8: 38.0, 16: 40.0
-    {132, 1012, 15340, 16},  // 1: 85.0, 2: 131.1, 4: 68.9, 8: 65.6, 16: 55.7
-    {10, 5016, 2286, 1},  // 1: 13.9, 2: 24.5, 4: 16.7, 8: 19.6, 16: 16.9
-    {16, 385, 2409, 1},  // 1: 7.0, 2: 24.9, 4: 16.1, 8: 11.8, 16: 11.2
-    {420, 479, 5136, 4},  // 1: 32.0, 2: 48.0, 4: 28.6, 8: 31.2, 16: 34.0
-    {178, 931, 4676, 4},  // 1: 30.6, 2: 44.8, 4: 26.4, 8: 28.8, 16: 33.3
-    {11, 315, 1813, 1},  // 1: 5.9, 2: 20.6, 4: 14.0, 8: 10.6, 16: 10.3
-    {217, 1127, 2447, 4},  // 1: 20.7, 2: 26.6, 4: 18.3, 8: 21.4, 16: 25.5
-    {137, 1231, 2351, 4},  // 1: 20.0, 2: 25.4, 4: 17.7, 8: 20.2, 16: 23.9
-    {378, 2886, 2015, -8},  // 1: 82.2, 2: 56.2, 4: 51.6, 8: 56.7, 16: 69.4, -2: 54.3, -4: 48.2, -8: 45.7, -16: 47.3
-    {130, 1580, 11590, 8},  // 1: 93.7, 2: 102.8, 4: 94.5, 8: 74.4, 16: 77.2
-    {276, 694, 15508, 8},  // 1: 86.7, 2: 132.7, 4: 70.3, 8: 67.8, 16: 73.0
-    {14, 1090, 8356, 16},  // 1: 27.3, 2: 73.7, 4: 39.9, 8: 24.5, 16: 18.6
-    {17, 1394, 1142, 1},  // 1: 5.4, 2: 14.6, 4: 10.9, 8: 9.5, 16: 9.3
-    {205, 3623, 5015, 4},  // 1: 99.9, 2: 83.9, 4: 83.3, 8: 84.2, 16: 90.5
-    {560, 759, 7039, 8},  // 1: 72.7, 2: 64.7, 4: 61.8, 8: 61.6, 16: 63.0
-    {143, 1910, 3628, 2},  // 1: 70.9, 2: 36.3, 4: 36.5, 8: 40.6, 16: 42.1
-    {471, 6763, 3812, -2},  // 1: 220.9, 2: 217.4, 4: 216.8, 8: 238.6, 16: 306.4, -2: 208.2, -4: 212.5, -8: 254.6, -16: 257.9
-    {201, 316, 7161, 8},  // 1: 29.1, 2: 65.7, 4: 35.6, 8: 22.5, 16: 25.0
+    {11, 1486, 1136, 1},  // 1: 5.3, 2: 14.6, 4: 11.0, 8: 9.6, 16: 9.6
+    {66, 326, 1317, 1},  // 1: 5.3, 2: 17.6, 4: 12.1, 8: 9.9, 16: 9.9
+    {63, 4495, 1443, 2},  // 1: 25.8, 2: 18.8, 4: 20.2, 8: 21.0, 16: 22.3
+    {24, 2252, 14173, 8},  // 1: 78.6, 2: 121.3, 4: 64.2, 8: 38.0, 16: 40.2
+    {132, 1012, 15340, 16},  // 1: 85.0, 2: 131.5, 4: 69.2, 8: 65.3, 16: 55.0
+    {10, 5016, 2286, 1},  // 1: 13.9, 2: 24.6, 4: 16.8, 8: 19.8, 16: 17.0
+    {16, 385, 2409, 1},  // 1: 7.0, 2: 24.9, 4: 16.0, 8: 11.8, 16: 11.1
+    {420, 479, 5136, 4},  // 1: 32.0, 2: 48.1, 4: 28.5, 8: 31.3, 16: 34.0
+    {178, 931, 4676, 4},  // 1: 30.6, 2: 44.8, 4: 26.3, 8: 28.9, 16: 33.3
+    {11, 315, 1813, 1},  // 1: 5.9, 2: 20.5, 4: 13.9, 8: 10.6, 16: 10.3
+    {217, 1127, 2447, 4},  // 1: 20.7, 2: 26.6, 4: 18.3, 8: 21.2, 16: 25.5
+    {137, 1231, 2351, 4},  // 1: 20.0, 2: 25.4, 4: 17.6, 8: 19.9, 16: 23.8
+    {378, 2886, 2015, -8},  // 1: 82.3, 2: 55.3, 4: 51.1, 8: 56.6, 16: 69.1, -2: 53.9, -4: 48.0, -8: 45.8, -16: 47.5
+    {130, 1580, 11590, 8},  // 1: 94.2, 2: 103.1, 4: 94.4, 8: 74.3, 16: 76.7
+    {276, 694, 15508, 8},  // 1: 86.6, 2: 132.4, 4: 69.8, 8: 67.5, 16: 72.2
+    {14, 1090, 8356, 16},  // 1: 27.3, 2: 73.4, 4: 39.7, 8: 24.4, 16: 18.6
+    {17, 1394, 1142, 1},  // 1: 5.3, 2: 14.6, 4: 10.9, 8: 9.6, 16: 9.4
+    {205, 3623, 5015, 4},  // 1: 99.8, 2: 83.7, 4: 83.1, 8: 83.6, 16: 90.0
+    {560, 759, 7039, 4},  // 1: 71.7, 2: 64.7, 4: 61.3, 8: 61.4, 16: 62.5
+    {143, 1910, 3628, 2},  // 1: 51.8, 2: 36.3, 4: 36.5, 8: 40.4, 16: 42.3
+    {471, 6763, 3812, -2},  // 1: 220.6, 2: 215.0, 4: 214.5, 8: 237.5, 16: 302.2, -2: 206.0, -4: 211.0, -8: 254.8, -16: 259.2
+    {201, 316, 7161, 8},  // 1: 41.9, 2: 65.5, 4: 35.6, 8: 22.5, 16: 25.1
 };
 
 static inline double model_best_us(int64_t M, int64_t N, int64_t K, int64_t wg_factor) {
