@@ -103,7 +103,10 @@ enum : int {
 // Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin; renumber
 // them so that consecutive ids run on one XCD (which has its own L2), then walk the
 // tiles in column-major groups of `group_m` tile rows so that workgroups close in id
-// share panels of A and B.  Both choices can be changed per launch for measurement (flags
+// share panels of A and B.  The renumbering holds for any number of workgroups: without
+// it, neighbouring tiles of a decode product (16 rows, tiles side by side along N) sit on
+// different XCDs, each fetching the 128-byte lines of B they share, and such products ran
+// up to 2x slower whenever the tile count was not a multiple of 8.  Both choices can be changed per launch for measurement (flags
 // bits 8..15: group_m, 0 = the default 4; bit 16: keep the hardware order of ids).
 // Default 4: on the dispatched kernels at 8192^3, 4096^3, 1024 x 8192 x 8192 and
 // 4096 x 11008 x 4096, group heights 4 and 8 run equally fast (within 0.1%), and 4 makes
@@ -118,8 +121,13 @@ __device__ inline void tile_coords(int bid, int nwg, int tiles_m, int tiles_n, i
   constexpr int kXcds = 8;
   const int gm_flag = (flags >> kRasterGroupShift) & 0xff;
   const int group_m = gm_flag ? gm_flag : 4;
-  if (!(flags & kRasterNoXcdRemap) && nwg % kXcds == 0)
-    bid = (bid % kXcds) * (nwg / kXcds) + bid / kXcds;
+  if (!(flags & kRasterNoXcdRemap)) {
+    // workgroup bid runs on XCD bid mod 8 as its (bid div 8)-th; XCD x runs q or q + 1 of
+    // the nwg workgroups (q = nwg div 8, one more for x < nwg mod 8), so giving it the
+    // consecutive ids from x q + min(x, nwg mod 8) on is a permutation of 0 .. nwg - 1
+    const int q = nwg / kXcds, r = nwg % kXcds, x = bid % kXcds;
+    bid = x * q + min(x, r) + bid / kXcds;
+  }
   const int per_group = group_m * tiles_n;
   const int group = bid / per_group;
   const int first_m = group * group_m;
