@@ -267,29 +267,14 @@ def _model_t(row, M, N, K, dims, wg=1):
     return a + b * rounds + g * rounds * kt + h * tiles * kt / 256.0, tiles
 
 
-def _stream_limit_bytes():
-    text = open(os.path.join(build.CSRC, "dispatch_table.h")).read()
-    return float(re.search(r"kRowTileStreamLimitBytes = ([0-9.eE+-]+);", text).group(1))
-
-
-def _offered(c, M, N, K, dims):
-    """Above 16 rows the 16-row configurations are offered only while the strips of B their
-    row tiles stream, ceil(M / 16) * 4 N K bytes, stay within the header's limit."""
-    if dims[c][0] != 16 or M <= 16:
-        return True
-    return -(-M // 16) * 4.0 * N * K <= _stream_limit_bytes()
-
-
 def _model_pick(M, N, K, rows, dims, variant=0):
     """The cost-model rule, read independently of the C++: least a + b * rounds + g *
     rounds * k_tiles + h * work, rounds = ceil(tiles / 256), work = tiles * k_tiles / 256,
-    over the rows offered at this shape, first row on ties."""
+    first row on ties."""
     best = None
     for row in rows:
         v, c = row[0], row[1]
         if variant and v != variant:
-            continue
-        if not _offered(c, M, N, K, dims):
             continue
         t = _model_t(row, M, N, K, dims)[0]
         if best is None or t < best[0]:
@@ -329,22 +314,6 @@ def test_select_off_table_follows_the_cost_model(shape):
     assert tdb.gemm_f32_select(*shape) == (tdb.OK, *_model_pick(*shape, rows, dims))
     for var in (tdb.VARIANT_SB, tdb.VARIANT_DB, tdb.VARIANT_MS, tdb.VARIANT_KS):
         assert tdb.gemm_f32_select_cfg(*shape, var) == _model_pick(*shape, rows, dims, var)[1]
-
-
-def test_row_tile_streaming_limit():
-    """A 208 x 5875 x 8154 product would stream B 13 times through 16-row tiles (2.5 GB):
-    the model does not offer those kernels; at 16 rows, or with a small B, it does."""
-    dims = {c: (i["BM"], i["BN"], i["BK"]) for c in range(tdb.gemm_f32_num_configs())
-            for i in [tdb.gemm_f32_config_info(c)[1]]}
-    ks16 = [c for c in dims if dims[c][0] == 16]
-    assert ks16 and _stream_limit_bytes() > 0
-    for c in ks16:
-        assert not _offered(c, 208, 5875, 8154, dims)
-        assert _offered(c, 16, 5875, 8154, dims) and _offered(c, 340, 44, 3984, dims)
-    _, v, c = tdb.gemm_f32_select(208, 5875, 8154)
-    assert dims[c][0] != 16
-    for c in ks16:
-        assert tdb.gemm_f32_select_cfg(208, 5875, 8154, tdb.VARIANT_KS) != c
 
 
 def test_under_filled_grids_get_small_tiles():
@@ -489,8 +458,6 @@ def _split_pick(M, N, K, rows, dims, consts, choices):
             v, c = row[0], row[1]
             if wg != 1 and (v == tdb.VARIANT_KS or one_wave(c)):  # never in a split launch
                 continue
-            if not _offered(c, m, n, k, dims):
-                continue
             t, tiles = _model_t(row, m, n, k, dims, wg)
             if best is None or t < best[0]:
                 best = (t, tiles)
@@ -556,10 +523,10 @@ def test_split_count_follows_the_split_model(shape):
 def test_split_model_agrees_with_the_split_study():
     """Over the shapes of the split study (the rows' trailing comments hold the measured
     times of every count, tail splits as negative counts), the modelled count's time over
-    the fastest count's: median at most 1.02, at least 75% of the shapes within 5%, none
-    beyond 1.3.  The misses are mid-sized products (130 to 471 rows) where the cost model
-    of the unsplit kernel is 10-25% off; the worst, 130 x 1580 x 11590, keeps the one-round
-    K-split product at 95 us where 8 chunks take 75 (1.27)."""
+    the fastest count's: median at most 1.02, at least 80% of the shapes within 5%, none
+    beyond 1.25.  The misses are small and mid-sized products where the model of the
+    unsplit kernel is 10-20% off; the worst, 39 x 432 x 6224, splits 16 ways at 1.16x the
+    unsplit time."""
     text = _header_text()
     body = text[text.index("kSplitK[] = {"):]
     body = body[:body.index("};")]
@@ -572,8 +539,8 @@ def test_split_model_agrees_with_the_split_study():
         regrets.append(us[pick] / min(us.values()))
     regrets.sort()
     assert regrets[len(regrets) // 2] <= 1.02, regrets
-    assert sum(r <= 1.05 for r in regrets) >= 0.75 * len(regrets), regrets
-    assert regrets[-1] <= 1.3, regrets
+    assert sum(r <= 1.05 for r in regrets) >= 0.80 * len(regrets), regrets
+    assert regrets[-1] <= 1.25, regrets
 
 
 def test_tail_split_workspace_is_packed_tiles():

@@ -25,40 +25,40 @@ struct DispatchRow {
 };
 
 static const DispatchRow kDispatch[] = {
-    {128, 128, 128, 5, 17, 7, 6, 6},  // sb 4.84 us, db 4.48 us, ms 4.53 us, ks 4.12 us
-    {127, 193, 61, 1, 7, 7, 6, 6},  // sb 4.24 us, db 4.25 us, ms 4.28 us, ks 4.23 us
-    {513, 257, 129, 5, 16, 13, 6, 6},  // sb 6.29 us, db 5.90 us, ms 5.94 us, ks 4.30 us
-    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.71 us, db 18.55 us, ms 17.95 us, ks 23.99 us
-    {256, 1024, 128, 5, 13, 7, 13, 6},  // sb 4.99 us, db 4.60 us, ms 4.79 us, ks 4.20 us
-    {1024, 128, 256, 5, 17, 7, 13, 6},  // sb 7.44 us, db 6.44 us, ms 6.49 us, ks 4.25 us
-    {4096, 4096, 4096, 2, 0, 9, 0, 3},  // sb 965.98 us, db 908.88 us, ms 915.24 us, ks 1196.04 us
-    {8192, 8192, 8192, 2, 0, 4, 0, 3},  // sb 7363.37 us, db 7191.36 us, ms 7188.20 us, ks 9542.48 us
-    {256, 256, 256, 5, 17, 7, 13, 6},  // sb 7.39 us, db 6.41 us, ms 6.44 us, ks 4.27 us
-    {512, 512, 512, 5, 16, 7, 13, 6},  // sb 12.55 us, db 10.23 us, ms 10.11 us, ks 5.73 us
-    {768, 768, 768, 3, 6, 7, 6, 6},  // sb 18.05 us, db 14.50 us, ms 14.08 us, ks 14.43 us
-    {1536, 1536, 1536, 2, 6, 7, 6, 6},  // sb 76.44 us, db 68.60 us, ms 68.71 us, ks 72.13 us
-    {2048, 2048, 2048, 2, 3, 6, 3, 3},  // sb 128.36 us, db 118.02 us, ms 121.21 us, ks 159.02 us
-    {3072, 3072, 3072, 2, 11, 7, 11, 11},  // sb 422.78 us, db 387.03 us, ms 402.36 us, ks 515.01 us
-    {6144, 6144, 6144, 2, 11, 4, 11, 3},  // sb 3175.97 us, db 3050.02 us, ms 3050.39 us, ks 3979.43 us
-    {64, 4096, 4096, 5, 13, 7, 13, 6},  // sb 95.73 us, db 63.76 us, ms 60.80 us, ks 24.96 us
-    {4096, 4096, 512, 2, 2, 9, 2, 3},  // sb 128.32 us, db 122.78 us, ms 124.60 us, ks 201.56 us
-    {2048, 8192, 2048, 2, 0, 9, 0, 8},  // sb 488.51 us, db 459.73 us, ms 466.93 us, ks 623.76 us
-    {4096, 1024, 1024, 2, 3, 7, 3, 3},  // sb 66.89 us, db 61.92 us, ms 63.66 us, ks 88.52 us
-    {1024, 1024, 8192, 3, 6, 7, 6, 6},  // sb 190.96 us, db 129.19 us, ms 121.45 us, ks 151.08 us
-    {1023, 1023, 1023, 3, 6, 7, 6, 6},  // sb 25.24 us, db 21.05 us, ms 20.67 us, ks 27.55 us
-    {4095, 4095, 4095, 2, 0, 9, 0, 0},  // sb 998.93 us, db 918.50 us, ms 921.34 us, ks 1324.24 us
-    {16, 4096, 4096, 5, 14, 7, 6, 6},  // sb 97.40 us, db 70.18 us, ms 69.52 us, ks 16.30 us
-    {32, 4096, 4096, 5, 15, 7, 13, 10},  // sb 98.03 us, db 63.76 us, ms 63.39 us, ks 18.29 us
-    {128, 4096, 4096, 5, 13, 7, 13, 6},  // sb 96.09 us, db 64.61 us, ms 61.33 us, ks 40.60 us
-    {32, 8192, 8192, 5, 13, 7, 13, 10},  // sb 196.30 us, db 129.22 us, ms 124.08 us, ks 48.23 us
-    {1, 4096, 4096, 5, 14, 7, 6, 6},  // sb 96.71 us, db 69.85 us, ms 69.28 us, ks 14.79 us
-    {8, 4096, 4096, 5, 14, 7, 6, 6},  // sb 97.57 us, db 70.13 us, ms 69.43 us, ks 15.27 us
-    {16, 11008, 4096, 5, 16, 7, 13, 6},  // sb 100.36 us, db 70.96 us, ms 69.97 us, ks 31.02 us
-    {16, 4096, 11008, 5, 14, 7, 6, 6},  // sb 261.49 us, db 183.44 us, ms 181.77 us, ks 37.43 us
-    {16, 8192, 8192, 5, 17, 7, 6, 6},  // sb 195.26 us, db 140.69 us, ms 135.87 us, ks 39.91 us
-    {4, 1024, 1024, 5, 14, 7, 6, 6},  // sb 23.33 us, db 19.57 us, ms 19.62 us, ks 4.54 us
-    {16, 32000, 4096, 3, 10, 13, 13, 10},  // sb 154.80 us, db 109.30 us, ms 86.97 us, ks 96.00 us
-    {1024, 8192, 8192, 2, 2, 7, 2, 9},  // sb 1008.51 us, db 905.22 us, ms 922.78 us, ks 1192.77 us
+    {128, 128, 128, 5, 17, 7, 6, 6},  // sb 4.76 us, db 4.52 us, ms 4.55 us, ks 4.06 us
+    {127, 193, 61, 5, 17, 7, 6, 7},  // sb 4.12 us, db 4.14 us, ms 4.16 us, ks 4.06 us
+    {513, 257, 129, 5, 16, 13, 13, 6},  // sb 6.16 us, db 5.81 us, ms 5.97 us, ks 4.14 us
+    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.79 us, db 18.60 us, ms 18.05 us, ks 24.08 us
+    {256, 1024, 128, 5, 17, 13, 13, 6},  // sb 4.97 us, db 4.63 us, ms 4.77 us, ks 4.03 us
+    {1024, 128, 256, 5, 15, 7, 13, 6},  // sb 7.42 us, db 6.42 us, ms 6.47 us, ks 4.01 us
+    {4096, 4096, 4096, 2, 0, 9, 0, 3},  // sb 965.74 us, db 907.13 us, ms 915.79 us, ks 1184.60 us
+    {8192, 8192, 8192, 2, 0, 9, 0, 3},  // sb 7394.38 us, db 7173.85 us, ms 7200.74 us, ks 9478.37 us
+    {256, 256, 256, 5, 17, 7, 13, 6},  // sb 7.40 us, db 6.40 us, ms 6.48 us, ks 4.05 us
+    {512, 512, 512, 5, 16, 7, 13, 6},  // sb 12.52 us, db 10.20 us, ms 10.11 us, ks 5.68 us
+    {768, 768, 768, 3, 6, 7, 6, 6},  // sb 18.04 us, db 14.51 us, ms 14.14 us, ks 14.67 us
+    {1536, 1536, 1536, 2, 6, 7, 6, 6},  // sb 76.62 us, db 68.66 us, ms 68.90 us, ks 72.32 us
+    {2048, 2048, 2048, 2, 3, 6, 3, 3},  // sb 127.98 us, db 117.42 us, ms 121.10 us, ks 158.88 us
+    {3072, 3072, 3072, 2, 11, 7, 11, 11},  // sb 419.44 us, db 385.81 us, ms 401.05 us, ks 509.22 us
+    {6144, 6144, 6144, 2, 11, 4, 11, 3},  // sb 3174.61 us, db 3041.77 us, ms 3057.62 us, ks 3962.03 us
+    {64, 4096, 4096, 5, 16, 7, 13, 6},  // sb 95.13 us, db 63.56 us, ms 60.90 us, ks 24.85 us
+    {4096, 4096, 512, 2, 2, 9, 2, 3},  // sb 128.08 us, db 123.02 us, ms 124.54 us, ks 202.22 us
+    {2048, 8192, 2048, 2, 0, 9, 0, 3},  // sb 488.57 us, db 460.36 us, ms 464.46 us, ks 620.96 us
+    {4096, 1024, 1024, 2, 3, 7, 3, 3},  // sb 66.93 us, db 61.82 us, ms 63.79 us, ks 88.99 us
+    {1024, 1024, 8192, 3, 6, 7, 6, 6},  // sb 190.78 us, db 128.55 us, ms 121.40 us, ks 149.63 us
+    {1023, 1023, 1023, 3, 6, 7, 6, 6},  // sb 25.14 us, db 21.02 us, ms 20.81 us, ks 27.59 us
+    {4095, 4095, 4095, 3, 0, 9, 9, 0},  // sb 1003.93 us, db 916.98 us, ms 921.21 us, ks 1307.13 us
+    {16, 4096, 4096, 5, 14, 7, 6, 6},  // sb 97.38 us, db 70.31 us, ms 69.46 us, ks 15.50 us
+    {32, 4096, 4096, 5, 15, 7, 13, 10},  // sb 97.70 us, db 63.49 us, ms 63.46 us, ks 17.13 us
+    {128, 4096, 4096, 5, 13, 7, 13, 6},  // sb 95.66 us, db 64.22 us, ms 61.30 us, ks 40.28 us
+    {32, 8192, 8192, 5, 13, 7, 13, 10},  // sb 197.15 us, db 128.76 us, ms 124.63 us, ks 48.28 us
+    {1, 4096, 4096, 5, 14, 7, 6, 6},  // sb 96.46 us, db 70.08 us, ms 69.26 us, ks 14.20 us
+    {8, 4096, 4096, 5, 14, 7, 6, 6},  // sb 97.29 us, db 70.31 us, ms 69.44 us, ks 14.57 us
+    {16, 11008, 4096, 5, 16, 7, 13, 6},  // sb 100.25 us, db 70.81 us, ms 70.05 us, ks 30.70 us
+    {16, 4096, 11008, 5, 14, 7, 6, 7},  // sb 262.15 us, db 183.89 us, ms 180.76 us, ks 37.63 us
+    {16, 8192, 8192, 5, 17, 7, 13, 6},  // sb 195.12 us, db 140.28 us, ms 136.04 us, ks 39.60 us
+    {4, 1024, 1024, 5, 14, 7, 6, 6},  // sb 23.37 us, db 19.68 us, ms 19.69 us, ks 4.54 us
+    {16, 32000, 4096, 3, 10, 13, 13, 10},  // sb 154.87 us, db 108.87 us, ms 85.32 us, ks 96.40 us
+    {1024, 8192, 8192, 2, 2, 7, 2, 9},  // sb 1006.13 us, db 901.61 us, ms 919.58 us, ks 1178.68 us
 };
 constexpr int kDispatchRows = (int)(sizeof(kDispatch) / sizeof(kDispatch[0]));
 
@@ -90,52 +90,52 @@ struct ModelRow {
 };
 
 static const ModelRow kModel[] = {
-    {1, 0, 9.9281, 0.0000, 4.01675, 0.39740},  // median |error| 2.6%
-    {1, 1, 10.1421, 0.0000, 7.71133, 0.54964},  // median |error| 1.5%
-    {1, 2, 6.0464, 0.0000, 2.22482, 0.00000},  // median |error| 4.5%
-    {1, 3, 3.9765, 0.0000, 1.21346, 0.00000},  // median |error| 8.7%
-    {1, 4, 4.0922, 0.0000, 2.22598, 0.00000},  // median |error| 4.9%
-    {1, 5, 3.3456, 0.0000, 1.19737, 0.00000},  // median |error| 7.4%
-    {1, 6, 3.0330, 0.0000, 0.65224, 0.00000},  // median |error| 11.0%
-    {1, 7, 3.0580, 0.0000, 1.19515, 0.00000},  // median |error| 8.6%
-    {1, 8, 6.5966, 0.0000, 7.60006, 0.40400},  // median |error| 1.7%
-    {1, 9, 4.3247, 0.0000, 4.06315, 0.00000},  // median |error| 2.5%
-    {1, 10, 3.0957, 0.0000, 0.68083, 0.00000},  // median |error| 13.1%
-    {1, 11, 6.1924, 0.0000, 2.44348, 0.28951},  // median |error| 3.0%
-    {1, 12, 6.7232, 0.0000, 4.56872, 0.40817},  // median |error| 2.0%
-    {1, 13, 4.5780, 0.0000, 0.18851, 0.00000},  // median |error| 22.3%
-    {2, 0, 10.0852, 0.0000, 3.45023, 0.12353},  // median |error| 0.9%
-    {2, 1, 10.3766, 0.0000, 6.90613, 0.24533},  // median |error| 1.0%
-    {2, 2, 6.7344, 0.0000, 1.74021, 0.06564},  // median |error| 1.5%
-    {2, 3, 4.4884, 0.0000, 0.88123, 0.08257},  // median |error| 2.4%
-    {2, 4, 4.6158, 0.0000, 1.74775, 0.07432},  // median |error| 1.5%
-    {2, 5, 4.1019, 0.0000, 0.92273, 0.01650},  // median |error| 2.1%
-    {2, 6, 3.1616, 0.0000, 0.50655, 0.00000},  // median |error| 3.3%
-    {2, 7, 3.1937, 0.0000, 1.05516, 0.00000},  // median |error| 2.9%
-    {2, 8, 7.1824, 0.0000, 7.05075, 0.26023},  // median |error| 0.9%
-    {2, 9, 5.2791, 0.0000, 3.45981, 0.15439},  // median |error| 0.8%
-    {2, 10, 3.1464, 0.0000, 0.54148, 0.00000},  // median |error| 3.9%
-    {2, 11, 7.0375, 0.0000, 1.97715, 0.06783},  // median |error| 0.5%
-    {2, 12, 7.6551, 0.0000, 3.89994, 0.16284},  // median |error| 0.6%
-    {2, 13, 4.4517, 0.0000, 0.17340, 0.00000},  // median |error| 20.1%
-    {3, 0, 10.5682, 0.0000, 3.52960, 0.17267},  // median |error| 1.9%
-    {3, 1, 10.4518, 0.0000, 7.06253, 0.42085},  // median |error| 2.0%
-    {3, 2, 6.7157, 0.0000, 1.78372, 0.08819},  // median |error| 1.7%
-    {3, 3, 4.6112, 0.0000, 0.90753, 0.01718},  // median |error| 2.3%
-    {3, 4, 4.8341, 0.0000, 1.79443, 0.12482},  // median |error| 1.8%
-    {3, 5, 4.1385, 0.0000, 0.92014, 0.08154},  // median |error| 1.7%
-    {3, 6, 3.2057, 0.0000, 0.50231, 0.00000},  // median |error| 3.2%
-    {3, 7, 3.2716, 0.0000, 1.03723, 0.08240},  // median |error| 3.2%
-    {3, 8, 7.6083, 0.0000, 7.02449, 0.27064},  // median |error| 0.8%
-    {3, 9, 5.3482, 0.0000, 3.50292, 0.16839},  // median |error| 1.2%
-    {3, 10, 3.2019, 0.0000, 0.52832, 0.00000},  // median |error| 4.4%
-    {3, 11, 7.2619, 0.0000, 2.02824, 0.08562},  // median |error| 2.5%
-    {3, 12, 7.7497, 0.0000, 4.01336, 0.24822},  // median |error| 2.6%
-    {5, 13, 2.7636, 1.0023, 0.16111, 0.00000},  // median |error| 6.5%
-    {5, 14, 2.9479, 0.5975, 0.04658, 0.02869},  // median |error| 10.7%
-    {5, 15, 2.8145, 0.6020, 0.09744, 0.00000},  // median |error| 11.2%
-    {5, 16, 1.6035, 1.9345, 0.15741, 0.02239},  // median |error| 7.8%
-    {5, 17, 3.2906, 0.1720, 0.10182, 0.00000},  // median |error| 11.8%
+    {1, 0, 9.3915, 0.0000, 4.01728, 0.38009},  // median |error| 2.0%
+    {1, 1, 10.1300, 0.0000, 7.71576, 0.50833},  // median |error| 1.3%
+    {1, 2, 5.7403, 0.0000, 2.21796, 0.00000},  // median |error| 4.3%
+    {1, 3, 3.9902, 0.0000, 1.20930, 0.00000},  // median |error| 8.8%
+    {1, 4, 4.0128, 0.0000, 2.22143, 0.00000},  // median |error| 4.9%
+    {1, 5, 3.4668, 0.0000, 1.19290, 0.00000},  // median |error| 7.2%
+    {1, 6, 3.0817, 0.0000, 0.64546, 0.00000},  // median |error| 11.4%
+    {1, 7, 3.0154, 0.0000, 1.18495, 0.00000},  // median |error| 7.9%
+    {1, 8, 6.7400, 0.0000, 7.60066, 0.37294},  // median |error| 1.5%
+    {1, 9, 4.4994, 0.0000, 4.05955, 0.00000},  // median |error| 2.4%
+    {1, 10, 3.1592, 0.0000, 0.67001, 0.00000},  // median |error| 14.0%
+    {1, 11, 6.4923, 0.0000, 2.43613, 0.28970},  // median |error| 2.9%
+    {1, 12, 6.8563, 0.0000, 4.54440, 0.41346},  // median |error| 1.7%
+    {1, 13, 4.5029, 0.0000, 0.18287, 0.00000},  // median |error| 22.8%
+    {2, 0, 10.3735, 0.0000, 3.45257, 0.10785},  // median |error| 1.2%
+    {2, 1, 10.6782, 0.0000, 6.91691, 0.20482},  // median |error| 1.2%
+    {2, 2, 6.4788, 0.0000, 1.74697, 0.05170},  // median |error| 1.4%
+    {2, 3, 4.4297, 0.0000, 0.88305, 0.07185},  // median |error| 2.4%
+    {2, 4, 4.6388, 0.0000, 1.75081, 0.06255},  // median |error| 1.5%
+    {2, 5, 4.0136, 0.0000, 0.92361, 0.00873},  // median |error| 1.9%
+    {2, 6, 3.1363, 0.0000, 0.50117, 0.00000},  // median |error| 4.0%
+    {2, 7, 3.1396, 0.0000, 1.04871, 0.00000},  // median |error| 3.4%
+    {2, 8, 7.2826, 0.0000, 7.03134, 0.24844},  // median |error| 0.8%
+    {2, 9, 5.2442, 0.0000, 3.46853, 0.13170},  // median |error| 0.8%
+    {2, 10, 3.1852, 0.0000, 0.53280, 0.00000},  // median |error| 4.5%
+    {2, 11, 7.2126, 0.0000, 1.97914, 0.05161},  // median |error| 0.8%
+    {2, 12, 7.7431, 0.0000, 3.90943, 0.12893},  // median |error| 0.7%
+    {2, 13, 4.4277, 0.0000, 0.16737, 0.00000},  // median |error| 18.3%
+    {3, 0, 10.3464, 0.0000, 3.53425, 0.15316},  // median |error| 1.8%
+    {3, 1, 10.8598, 0.0000, 7.07143, 0.39410},  // median |error| 1.8%
+    {3, 2, 6.8939, 0.0000, 1.78449, 0.07958},  // median |error| 1.8%
+    {3, 3, 4.5750, 0.0000, 0.90808, 0.01300},  // median |error| 2.0%
+    {3, 4, 4.6242, 0.0000, 1.80046, 0.11449},  // median |error| 1.6%
+    {3, 5, 4.2278, 0.0000, 0.92066, 0.07597},  // median |error| 1.6%
+    {3, 6, 3.2809, 0.0000, 0.49687, 0.00000},  // median |error| 4.0%
+    {3, 7, 3.2538, 0.0000, 1.04240, 0.07365},  // median |error| 3.3%
+    {3, 8, 7.7592, 0.0000, 7.05088, 0.23420},  // median |error| 1.0%
+    {3, 9, 5.2837, 0.0000, 3.51167, 0.15012},  // median |error| 1.1%
+    {3, 10, 3.2366, 0.0000, 0.52150, 0.00000},  // median |error| 4.6%
+    {3, 11, 7.2551, 0.0000, 2.03094, 0.07740},  // median |error| 2.4%
+    {3, 12, 7.7815, 0.0000, 4.01947, 0.22703},  // median |error| 2.5%
+    {5, 13, 2.7918, 0.9769, 0.15470, 0.00000},  // median |error| 6.6%
+    {5, 14, 2.9068, 0.5996, 0.04711, 0.02438},  // median |error| 8.8%
+    {5, 15, 2.7497, 0.5848, 0.09412, 0.00000},  // median |error| 9.4%
+    {5, 16, 1.4950, 1.9692, 0.15712, 0.01368},  // median |error| 4.8%
+    {5, 17, 3.2329, 0.1463, 0.09917, 0.00000},  // median |error| 9.0%
 };
 constexpr int kModelRows = (int)(sizeof(kModel) / sizeof(kModel[0]));
 constexpr int kVariantKS = 5;
@@ -153,18 +153,6 @@ static inline double model_us(const ModelRow& r, int64_t M, int64_t N, int64_t K
          r.h_us * (double)tiles * (double)k_tiles / (double)kModelCUs;
 }
 
-// Above 16 rows every 16-row tile streams its strip of B again, ceil(M / 16) times in all.
-// How fast that goes depends on how much of it the caches catch, which the model above does
-// not see; measured, the 16-row kernels win above 16 rows while those re-reads stay small
-// and lose by up to 2x beyond (a 208 x 5875 x 8154 product streams 2.5 GB).  So the model
-// offers them above 16 rows only up to this many bytes of B streamed.
-constexpr double kRowTileStreamLimitBytes = 100e6;
-
-static inline bool model_allows(const CfgEntry& e, int64_t M, int64_t N, int64_t K) {
-  if (e.bm != 16 || M <= 16) return true;
-  return (double)((M + 15) / 16) * 4.0 * (double)N * (double)K <= kRowTileStreamLimitBytes;
-}
-
 // The row with the least modelled time (variant 0: any variant), first row on ties.
 static inline const ModelRow& model_pick(int64_t M, int64_t N, int64_t K, int variant,
                                          int64_t wg_factor) {
@@ -173,7 +161,6 @@ static inline const ModelRow& model_pick(int64_t M, int64_t N, int64_t K, int va
   bool found = false;
   for (int i = 0; i < kModelRows; ++i) {
     if (variant != 0 && kModel[i].variant != variant) continue;
-    if (!model_allows(kConfigs[kModel[i].cfg], M, N, K)) continue;
     // a split-K launch takes neither the K-split kernel (it divides K itself) nor a
     // one-wave configuration (its plain kernels keep one SIMD of a CU busy)
     if (wg_factor != 1 &&
@@ -209,15 +196,15 @@ static inline int select_for_variant(int64_t M, int64_t N, int64_t K, int varian
 // Split-K: the number of K chunks (1 = do not split) with the least modelled time among
 // the counts the split study measured.  A split launch costs the GEMM of its chunks, all in
 // one grid (the model above, with the workgroups multiplied by the chunks), plus
-//     3.1327 us (the reduction's launch)
-//   + 0.12757 us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
+//     3.4019 us (the reduction's launch)
+//   + 0.13900 us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
 //     written once and read once by the reduction, and C)
-//   + 0.5608 us per round of workgroups of the split grid (each workgroup's
+//   + 0.3463 us per round of workgroups of the split grid (each workgroup's
 //     first copy and partial-tile store, which short chunks no longer hide),
 // the constants fitted (>= 0, least squares) to the 41 shapes of the split study below.
-constexpr double kSplitFixedUs = 3.1327;
-constexpr double kSplitUsPerMB = 0.12757;
-constexpr double kSplitUsPerRound = 0.5608;
+constexpr double kSplitFixedUs = 3.4019;
+constexpr double kSplitUsPerMB = 0.13900;
+constexpr double kSplitUsPerRound = 0.3463;
 constexpr int kSplitChoices[] = {1, 2, 4, 8, 16};
 
 // The split study: trailing comments hold the measured microseconds of each count.
@@ -227,47 +214,47 @@ struct SplitRow {
 };
 
 static const SplitRow kSplitK[] = {
-    {16, 4096, 4096, 1},  // 1: 16.4, 2: 38.9, 4: 23.0, 8: 17.5, 16: 21.3
-    {32, 4096, 4096, 8},  // 1: 18.5, 2: 39.2, 4: 23.4, 8: 17.2, 16: 21.7
-    {64, 4096, 4096, 4},  // 1: 25.1, 2: 34.9, 4: 21.1, 8: 24.1, 16: 28.9
-    {128, 4096, 4096, 2},  // 1: 39.7, 2: 35.7, 4: 37.3, 8: 39.3, 16: 43.4
-    {32, 8192, 8192, 4},  // 1: 48.1, 2: 73.3, 4: 45.2, 8: 46.4, 16: 52.2
-    {64, 8192, 8192, 2},  // 1: 79.2, 2: 66.6, 4: 70.6, 8: 74.5, 16: 85.3
-    {256, 256, 8192, 16},  // 1: 45.7, 2: 62.8, 4: 34.7, 8: 21.8, 16: 17.1
-    {512, 512, 8192, 4},  // 1: 46.0, 2: 63.4, 4: 35.6, 8: 37.6, 16: 40.3
-    {1024, 1024, 1024, 1},  // 1: 18.0, 2: 24.8, 4: 29.3, 8: 32.9, 16: 40.4
-    {2048, 2048, 2048, 1},  // 1: 117.4, 2: 129.2, 4: 140.0, 8: 157.8, 16: 206.2
-    {4096, 4096, 4096, 1},  // 1: 903.5, 2: 943.8, 4: 996.2, 8: 1124.1, 16: 1291.0, -2: 1064.5, -4: 1076.5, -8: 1119.3, -16: 1170.7
-    {1536, 1536, 1536, -4},  // 1: 68.1, 2: 66.3, 4: 64.7, 8: 77.8, 16: 88.7, -2: 61.4, -4: 57.0, -8: 57.9, -16: 64.1
-    {1536, 1536, 4096, -4},  // 1: 174.0, 2: 153.8, 4: 142.9, 8: 154.5, 16: 174.7, -2: 149.3, -4: 136.5, -8: 136.9, -16: 139.5
-    {2560, 2560, 2560, -8},  // 1: 255.7, 2: 258.3, 4: 267.9, 8: 302.6, 16: 363.5, -2: 242.3, -4: 240.3, -8: 233.3, -16: 241.5
-    {1280, 1280, 2048, -4},  // 1: 61.9, 2: 66.0, 4: 66.0, 8: 71.4, 16: 82.8, -2: 66.6, -4: 61.1, -8: 62.3, -16: 66.5
-    {5000, 5000, 1000, -4},  // 1: 392.8, 2: 442.8, 4: 522.5, 8: 758.3, 16: 1153.5, -2: 381.5, -4: 376.4, -8: 379.9, -16: 385.7
-    {1536, 3072, 4096, -4},  // 1: 289.4, 2: 269.6, 4: 280.2, 8: 310.0, 16: 370.0, -2: 266.9, -4: 265.8, -8: 265.9, -16: 269.6
-    {39, 432, 6224, 16},  // 1: 17.5, 2: 56.1, 4: 31.8, 8: 20.5, 16: 16.2
-    {11, 1640, 2822, 1},  // 1: 9.8, 2: 29.1, 4: 18.4, 8: 13.1, 16: 12.2
-    {11, 1486, 1136, 1},  // 1: 5.3, 2: 14.6, 4: 11.0, 8: 9.6, 16: 9.6
-    {66, 326, 1317, 1},  // 1: 5.3, 2: 17.6, 4: 12.1, 8: 9.9, 16: 9.9
-    {63, 4495, 1443, 2},  // 1: 25.8, 2: 18.8, 4: 20.2, 8: 21.0, 16: 22.3
-    {24, 2252, 14173, 8},  // 1: 78.6, 2: 121.3, 4: 64.2, 8: 38.0, 16: 40.2
-    {132, 1012, 15340, 16},  // 1: 85.0, 2: 131.5, 4: 69.2, 8: 65.3, 16: 55.0
-    {10, 5016, 2286, 1},  // 1: 13.9, 2: 24.6, 4: 16.8, 8: 19.8, 16: 17.0
-    {16, 385, 2409, 1},  // 1: 7.0, 2: 24.9, 4: 16.0, 8: 11.8, 16: 11.1
-    {420, 479, 5136, 4},  // 1: 32.0, 2: 48.1, 4: 28.5, 8: 31.3, 16: 34.0
-    {178, 931, 4676, 4},  // 1: 30.6, 2: 44.8, 4: 26.3, 8: 28.9, 16: 33.3
-    {11, 315, 1813, 1},  // 1: 5.9, 2: 20.5, 4: 13.9, 8: 10.6, 16: 10.3
-    {217, 1127, 2447, 4},  // 1: 20.7, 2: 26.6, 4: 18.3, 8: 21.2, 16: 25.5
-    {137, 1231, 2351, 4},  // 1: 20.0, 2: 25.4, 4: 17.6, 8: 19.9, 16: 23.8
-    {378, 2886, 2015, -8},  // 1: 82.3, 2: 55.3, 4: 51.1, 8: 56.6, 16: 69.1, -2: 53.9, -4: 48.0, -8: 45.8, -16: 47.5
-    {130, 1580, 11590, 8},  // 1: 94.2, 2: 103.1, 4: 94.4, 8: 74.3, 16: 76.7
-    {276, 694, 15508, 8},  // 1: 86.6, 2: 132.4, 4: 69.8, 8: 67.5, 16: 72.2
-    {14, 1090, 8356, 16},  // 1: 27.3, 2: 73.4, 4: 39.7, 8: 24.4, 16: 18.6
-    {17, 1394, 1142, 1},  // 1: 5.3, 2: 14.6, 4: 10.9, 8: 9.6, 16: 9.4
-    {205, 3623, 5015, 4},  // 1: 99.8, 2: 83.7, 4: 83.1, 8: 83.6, 16: 90.0
-    {560, 759, 7039, 4},  // 1: 71.7, 2: 64.7, 4: 61.3, 8: 61.4, 16: 62.5
-    {143, 1910, 3628, 2},  // 1: 51.8, 2: 36.3, 4: 36.5, 8: 40.4, 16: 42.3
-    {471, 6763, 3812, -2},  // 1: 220.6, 2: 215.0, 4: 214.5, 8: 237.5, 16: 302.2, -2: 206.0, -4: 211.0, -8: 254.8, -16: 259.2
-    {201, 316, 7161, 8},  // 1: 41.9, 2: 65.5, 4: 35.6, 8: 22.5, 16: 25.1
+    {16, 4096, 4096, 1},  // 1: 15.4, 2: 38.9, 4: 23.4, 8: 17.6, 16: 21.5
+    {32, 4096, 4096, 1},  // 1: 17.1, 2: 39.3, 4: 23.7, 8: 17.3, 16: 21.7
+    {64, 4096, 4096, 4},  // 1: 24.8, 2: 35.0, 4: 23.0, 8: 23.6, 16: 26.9
+    {128, 4096, 4096, 2},  // 1: 40.9, 2: 36.2, 4: 38.1, 8: 39.6, 16: 43.5
+    {32, 8192, 8192, 4},  // 1: 48.5, 2: 72.9, 4: 45.1, 8: 46.8, 16: 52.6
+    {64, 8192, 8192, 2},  // 1: 83.4, 2: 69.5, 4: 73.9, 8: 77.6, 16: 89.2
+    {256, 256, 8192, 16},  // 1: 24.1, 2: 62.9, 4: 34.8, 8: 22.6, 16: 17.3
+    {512, 512, 8192, 4},  // 1: 46.1, 2: 63.9, 4: 35.9, 8: 38.2, 16: 40.3
+    {1024, 1024, 1024, 1},  // 1: 18.0, 2: 24.8, 4: 29.3, 8: 32.9, 16: 40.2
+    {2048, 2048, 2048, 1},  // 1: 117.7, 2: 129.8, 4: 140.4, 8: 158.6, 16: 207.4
+    {4096, 4096, 4096, 1},  // 1: 905.8, 2: 946.6, 4: 997.8, 8: 1126.6, 16: 1294.8, -2: 1078.3, -4: 1089.6, -8: 1124.2, -16: 1175.2
+    {1536, 1536, 1536, -4},  // 1: 69.1, 2: 66.9, 4: 64.8, 8: 77.4, 16: 89.5, -2: 62.2, -4: 58.2, -8: 58.3, -16: 63.9
+    {1536, 1536, 4096, -8},  // 1: 174.4, 2: 155.7, 4: 143.5, 8: 154.8, 16: 184.7, -2: 151.0, -4: 143.7, -8: 138.4, -16: 142.1
+    {2560, 2560, 2560, -8},  // 1: 258.6, 2: 262.7, 4: 273.9, 8: 308.7, 16: 365.2, -2: 249.5, -4: 243.0, -8: 237.9, -16: 244.3
+    {1280, 1280, 2048, 1},  // 1: 62.1, 2: 66.2, 4: 68.0, 8: 72.2, 16: 82.9, -2: 67.3, -4: 62.4, -8: 64.9, -16: 67.1
+    {5000, 5000, 1000, -8},  // 1: 393.5, 2: 450.3, 4: 528.5, 8: 761.6, 16: 1150.3, -2: 391.2, -4: 391.0, -8: 380.2, -16: 385.4
+    {1536, 3072, 4096, -8},  // 1: 291.8, 2: 270.4, 4: 280.6, 8: 320.8, 16: 372.5, -2: 276.5, -4: 270.2, -8: 266.3, -16: 270.1
+    {39, 432, 6224, 1},  // 1: 13.8, 2: 56.1, 4: 32.0, 8: 20.7, 16: 16.4
+    {11, 1640, 2822, 1},  // 1: 7.5, 2: 29.1, 4: 18.5, 8: 13.1, 16: 12.3
+    {11, 1486, 1136, 1},  // 1: 5.4, 2: 14.5, 4: 10.9, 8: 9.5, 16: 9.6
+    {66, 326, 1317, 1},  // 1: 5.4, 2: 16.8, 4: 12.2, 8: 9.7, 16: 9.9
+    {63, 4495, 1443, 1},  // 1: 17.7, 2: 19.2, 4: 19.1, 8: 19.0, 16: 19.6
+    {24, 2252, 14173, 8},  // 1: 55.4, 2: 121.5, 4: 64.5, 8: 38.1, 16: 40.6
+    {132, 1012, 15340, 16},  // 1: 85.1, 2: 132.1, 4: 69.6, 8: 65.6, 16: 56.0
+    {10, 5016, 2286, 1},  // 1: 10.7, 2: 24.6, 4: 16.9, 8: 19.8, 16: 17.1
+    {16, 385, 2409, 1},  // 1: 7.0, 2: 25.0, 4: 16.0, 8: 12.0, 16: 11.0
+    {420, 479, 5136, 4},  // 1: 32.1, 2: 48.3, 4: 28.6, 8: 31.1, 16: 34.2
+    {178, 931, 4676, 16},  // 1: 29.9, 2: 44.4, 4: 26.4, 8: 28.8, 16: 25.9
+    {11, 315, 1813, 1},  // 1: 6.0, 2: 20.7, 4: 13.9, 8: 10.6, 16: 10.2
+    {217, 1127, 2447, 1},  // 1: 18.4, 2: 26.7, 4: 18.5, 8: 21.4, 16: 23.2
+    {137, 1231, 2351, 1},  // 1: 17.6, 2: 25.4, 4: 17.6, 8: 19.8, 16: 22.4
+    {378, 2886, 2015, -8},  // 1: 56.3, 2: 57.4, 4: 52.7, 8: 56.9, 16: 67.7, -2: 52.3, -4: 47.0, -8: 44.7, -16: 45.7
+    {130, 1580, 11590, 1},  // 1: 65.8, 2: 101.1, 4: 94.1, 8: 74.3, 16: 71.5
+    {276, 694, 15508, 8},  // 1: 88.1, 2: 133.0, 4: 70.0, 8: 68.4, 16: 73.7
+    {14, 1090, 8356, 16},  // 1: 25.0, 2: 73.6, 4: 39.8, 8: 24.4, 16: 18.7
+    {17, 1394, 1142, 1},  // 1: 5.4, 2: 14.5, 4: 11.0, 8: 9.4, 16: 9.3
+    {205, 3623, 5015, 4},  // 1: 87.0, 2: 83.4, 4: 83.2, 8: 84.7, 16: 93.3
+    {560, 759, 7039, 4},  // 1: 73.1, 2: 64.8, 4: 61.4, 8: 61.6, 16: 68.4
+    {143, 1910, 3628, 2},  // 1: 41.6, 2: 35.8, 4: 36.1, 8: 40.2, 16: 38.5
+    {471, 6763, 3812, -8},  // 1: 221.8, 2: 218.7, 4: 217.0, 8: 243.0, 16: 303.0, -2: 210.7, -4: 211.9, -8: 207.0, -16: 208.5
+    {201, 316, 7161, 8},  // 1: 29.7, 2: 64.6, 4: 35.7, 8: 22.5, 16: 24.9
 };
 
 static inline double model_best_us(int64_t M, int64_t N, int64_t K, int64_t wg_factor) {

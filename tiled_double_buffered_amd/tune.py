@@ -163,18 +163,6 @@ static inline double model_us(const ModelRow& r, int64_t M, int64_t N, int64_t K
          r.h_us * (double)tiles * (double)k_tiles / (double)kModelCUs;
 }}
 
-// Above 16 rows every 16-row tile streams its strip of B again, ceil(M / 16) times in all.
-// How fast that goes depends on how much of it the caches catch, which the model above does
-// not see; measured, the 16-row kernels win above 16 rows while those re-reads stay small
-// and lose by up to 2x beyond (a 208 x 5875 x 8154 product streams 2.5 GB).  So the model
-// offers them above 16 rows only up to this many bytes of B streamed.
-constexpr double kRowTileStreamLimitBytes = {stream_limit_mb:.0f}e6;
-
-static inline bool model_allows(const CfgEntry& e, int64_t M, int64_t N, int64_t K) {{
-  if (e.bm != 16 || M <= 16) return true;
-  return (double)((M + 15) / 16) * 4.0 * (double)N * (double)K <= kRowTileStreamLimitBytes;
-}}
-
 // The row with the least modelled time (variant 0: any variant), first row on ties.
 static inline const ModelRow& model_pick(int64_t M, int64_t N, int64_t K, int variant,
                                          int64_t wg_factor) {{
@@ -183,7 +171,6 @@ static inline const ModelRow& model_pick(int64_t M, int64_t N, int64_t K, int va
   bool found = false;
   for (int i = 0; i < kModelRows; ++i) {{
     if (variant != 0 && kModel[i].variant != variant) continue;
-    if (!model_allows(kConfigs[kModel[i].cfg], M, N, K)) continue;
     // a split-K launch takes neither the K-split kernel (it divides K itself) nor a
     // one-wave configuration (its plain kernels keep one SIMD of a CU busy)
     if (wg_factor != 1 &&
@@ -686,17 +673,6 @@ def _one_wave(cfg):
     return tdb.gemm_f32_config_info(cfg)[1]["threads"] == 64
 
 
-# Above 16 rows the 16-row kernels are offered to the model only while the strips of B
-# their row tiles stream, ceil(M / 16) * 4 N K bytes, stay within this (MB).
-ROW_TILE_STREAM_LIMIT_MB = 100.0
-
-
-def model_allows(cfg_dims, M, N, K):
-    if cfg_dims[0] != 16 or M <= 16:
-        return True
-    return -(-M // 16) * 4.0 * N * K <= ROW_TILE_STREAM_LIMIT_MB * 1e6
-
-
 def _model_pick_py(M, N, K, model, dims, wg_factor=1):
     """Least modelled (us, variant, cfg) over the fitted rows, as the header computes it
     (a split launch never takes the K-split kernel)."""
@@ -704,8 +680,6 @@ def _model_pick_py(M, N, K, model, dims, wg_factor=1):
     for row in model:
         v, c = row[0], row[1]
         if wg_factor != 1 and (v == tdb.VARIANT_KS or _one_wave(c)):
-            continue
-        if not model_allows(dims[c], M, N, K):
             continue
         t = model_time(row, M, N, K, dims[c][:3], wg_factor)
         if best is None or t < best[0]:
@@ -922,7 +896,6 @@ def write_header(results, device, rounds, batches, batch_ms, path=None, split_re
                                   ntrain=len(fit_rows) - len(results), split_fixed=r0,
                                   split_us_per_mb=per_mb, split_us_per_round=per_round,
                                   nsplit=len(split_results or []),
-                                  stream_limit_mb=ROW_TILE_STREAM_LIMIT_MB,
                                   split_choices=", ".join(str(c) for c in choices))
     with open(path, "w") as f:
         f.write(text)
