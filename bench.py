@@ -375,7 +375,10 @@ def _pair_cfg(tdb, sb_cfg, db_cfg):
 
 def _timer(torch, stream):
     """time_call(fn, target_ms, batches) -> (event us median, host-wall us median, event us
-    min, event us max) over `batches` batches of back-to-back launches of >= target_ms."""
+    min, event us max, host-issue us median) over `batches` batches of back-to-back launches
+    of >= target_ms.  Host issue is the host's time per call to enqueue the batch, before the
+    synchronization: where it reaches the event time, the host, not the GPU, sets the
+    rate."""
     def time_call(fn, target_ms, batches):
         fn()
         torch.cuda.synchronize()
@@ -396,12 +399,15 @@ def _timer(torch, stream):
             for _ in range(reps):
                 fn()
             b.record(stream)
+            hi = time.perf_counter()
             torch.cuda.synchronize()
             h1 = time.perf_counter()
-            res.append((a.elapsed_time(b) * 1e3 / reps, (h1 - h0) * 1e6 / reps))
+            res.append((a.elapsed_time(b) * 1e3 / reps, (h1 - h0) * 1e6 / reps,
+                        (hi - h0) * 1e6 / reps))
         ev = statistics.median(x[0] for x in res)
         wall_us = statistics.median(x[1] for x in res)
-        return ev, wall_us, min(x[0] for x in res), max(x[0] for x in res)
+        issue_us = statistics.median(x[2] for x in res)
+        return ev, wall_us, min(x[0] for x in res), max(x[0] for x in res), issue_us
     return time_call
 
 
@@ -855,12 +861,16 @@ def layer_shapes(args) -> int:
 
 def k_slope(args) -> int:
     """Time 1024 x 1024 x K on the dispatched 1024^3 kernel and on the double-buffered
-    kernel of the same tile, K = 32 .. 2048, and fit t = a + b * k_tiles over K >= 128:
+    kernel of the same tile, K = 0 .. 2048, and fit t = a + b * k_tiles over K >= 256:
     `a` is what a launch costs besides its K tiles (dispatch, the first tile's latency, the
     epilogue, the gap to the next launch), `b` the time per K tile, set against the
-    matrix-core time of one K tile at the clock the ceiling probe measures.  Also times a
-    1 x 1 x 1 product, the cost of a launch that does nearly nothing."""
+    matrix-core time of one K tile at the clock the ceiling probe measures.  K = 0 launches
+    the same grid with no K tile (the epilogue stores zeros).  Each point also carries the
+    host's time to enqueue one call.  Then the smallest launch (1 x 1 x 0: one workgroup that
+    stores one zero), and the dispatched kernel at K = 0 and 1024 replayed from a captured
+    graph of back-to-back launches, where no per-call host work stands between them."""
     torch, dev, stream = _stream_setup()
+    import numpy as np
     import tdb_inputs as ti
     import tiled_double_buffered_amd as tdb
     from tiled_double_buffered_amd import peak
@@ -868,7 +878,7 @@ def k_slope(args) -> int:
     s_ptr = stream.cuda_stream
     time_call = _timer(torch, stream)
     M = N = 1024
-    ks = [32, 64, 128, 256, 512, 1024, 2048]
+    ks = [0, 32, 64, 128, 256, 512, 1024, 2048]
     lda = max(ks)
     a_h, b_h = ti.workload_inputs(M, N, lda, 3101)
     A = torch.from_numpy(a_h).to(dev)
@@ -881,6 +891,12 @@ def k_slope(args) -> int:
     ceiling = peak.mfma_ceiling(stream=stream)
     clock = ceiling["clock_ghz"]
     out = {"M": M, "N": N, "ceiling": ceiling, "kernels": []}
+
+    def med(fn):
+        """Median over the rounds of (event us, host-issue us)."""
+        xs = [time_call(fn, args.batch_ms, args.batches) for _ in range(args.rounds)]
+        return (statistics.median(x[0] for x in xs), statistics.median(x[4] for x in xs))
+
     for (v, c) in kernels:
         _, info = tdb.gemm_f32_config_info(c)
         waves = info["threads"] // 64
@@ -898,12 +914,11 @@ def k_slope(args) -> int:
                 return tdb.gemm_f32_ex(M, N, K, A.data_ptr(), lda, B.data_ptr(), N,
                                        C.data_ptr(), N, v, c, s_ptr)
             _prewarm(torch, fn, 0.05)
-            us = statistics.median(time_call(fn, args.batch_ms, args.batches)[0]
-                                   for _ in range(args.rounds))
-            pts.append((K, K // info["BK"], us))
-            print(f"[k-slope] {VARIANT_NAMES[v]} cfg{c} K={K}: {us:.2f} us", file=sys.stderr,
-                  flush=True)
-        fit = [(kt, us) for K, kt, us in pts if K >= 128]
+            us, issue = med(fn)
+            pts.append((K, K // info["BK"], us, issue))
+            print(f"[k-slope] {VARIANT_NAMES[v]} cfg{c} K={K}: {us:.2f} us "
+                  f"(host issue {issue:.2f} us)", file=sys.stderr, flush=True)
+        fit = [(kt, us) for K, kt, us, _ in pts if K >= 256]
         n = len(fit)
         mx = sum(x for x, _ in fit) / n
         my = sum(y for _, y in fit) / n
@@ -911,20 +926,74 @@ def k_slope(args) -> int:
         a = my - b * mx
         out["kernels"].append({
             "kernel": f"{VARIANT_NAMES[v]} cfg{c} {_cfg_name(tdb, c)}",
-            "points_us": {str(K): round(us, 3) for K, _, us in pts},
+            "points_us": {str(K): round(us, 3) for K, _, us, _ in pts},
+            "host_issue_us": {str(K): round(iss, 3) for K, _, _, iss in pts},
             "fixed_us": round(a, 3), "per_k_tile_us": round(b, 4),
             "mfma_per_k_tile_us": round(tile_us, 4),
             "loop_fraction_of_mfma": round(tile_us / b, 4),
             "mfma_us_at_k1024": round(tile_us * (1024 // info["BK"]), 3)})
 
     def tiny():
-        return tdb.gemm_f32_ex(1, 1, 1, A.data_ptr(), 1, B.data_ptr(), 1, C.data_ptr(), 1,
-                               tdb.VARIANT_DB, kernels[0][1] if tdb.gemm_f32_config_variants(
-                                   kernels[0][1]) & (1 << tdb.VARIANT_DB) else 0, s_ptr)
-    out["launch_1x1x1_us"] = round(statistics.median(
-        time_call(tiny, args.batch_ms, args.batches)[0] for _ in range(args.rounds)), 3)
+        return tdb.gemm_f32_ex(1, 1, 0, A.data_ptr(), 1, B.data_ptr(), 1, C.data_ptr(), 1,
+                               v0, c0, s_ptr)
+    _prewarm(torch, tiny, 0.05)
+    us, issue = med(tiny)
+    out["launch_1x1x0"] = {"us": round(us, 3), "host_issue_us": round(issue, 3)}
+    print(f"[k-slope] 1x1x0: {us:.2f} us (host issue {issue:.2f} us)", file=sys.stderr,
+          flush=True)
+
+    # The dispatched kernel from a captured graph: `reps` launches recorded once on a side
+    # stream, the graph replayed back to back, event time per launch.
+    reps = 200
+    side = torch.cuda.Stream()
+    graphs = {}
+    for K in (0, 1024):
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(reps):
+                    tdb.gemm_f32_ex(M, N, K, A.data_ptr(), lda, B.data_ptr(), N,
+                                    C.data_ptr(), N, v0, c0, side.cuda_stream)
+        torch.cuda.synchronize()
+        graphs[K] = g
+    graph_us = {}
+    for K, g in graphs.items():
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        per_round = []
+        for _ in range(args.rounds):
+            xs = []
+            for _ in range(args.batches):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                n_rep = 0
+                e0.record(side)
+                with torch.cuda.stream(side):
+                    while True:  # replays until the batch's expected time is covered
+                        g.replay()
+                        n_rep += 1
+                        if n_rep * reps * 0.004 >= args.batch_ms:
+                            break
+                e1.record(side)
+                torch.cuda.synchronize()
+                xs.append(e0.elapsed_time(e1) * 1e3 / (n_rep * reps))
+            per_round.append(statistics.median(xs))
+        graph_us[str(K)] = round(statistics.median(per_round), 3)
+        print(f"[k-slope] graph {VARIANT_NAMES[v0]} cfg{c0} K={K}: {graph_us[str(K)]:.2f} us",
+              file=sys.stderr, flush=True)
+    # the graph-replayed 1024^3 product on 4096 seeded positions against the oracle
+    check = CpuLeg().sampled(torch, dev, ti, M, N, 3102, np.ascontiguousarray(a_h[:, :1024]),
+                             np.ascontiguousarray(b_h[:1024]))
+    C.fill_(float("nan"))
+    graphs[1024].replay()
+    torch.cuda.synchronize()
+    out["graph"] = {"kernel": f"{VARIANT_NAMES[v0]} cfg{c0} {_cfg_name(tdb, c0)}",
+                    "launches_per_graph": reps, "points_us": graph_us,
+                    "k1024_max_err_over_bound": check(C)}
     print(json.dumps(out), flush=True)
-    return 0
+    return 0 if _ratio_ok(out["graph"]["k1024_max_err_over_bound"]) else 3
 
 
 # ------------------------------------------------------------------ the bench line
@@ -1142,6 +1211,7 @@ def main() -> int:
             ev = statistics.median(x[0] for x in xs)  # median of the per-round medians
             wl = statistics.median(x[1] for x in xs)
             entry[v] = {"us": round(ev, 2), "host_wall_us": round(wl, 2),
+                        "host_issue_us": round(statistics.median(x[4] for x in xs), 2),
                         "us_range": [round(min(x[2] for x in xs), 2),
                                      round(max(x[3] for x in xs), 2)],
                         "tflops": round(f / (ev * 1e-6) / 1e12, 2),
