@@ -63,6 +63,8 @@ SHAPES = [
     (2048, 2048, 2048), (3072, 3072, 3072), (6144, 6144, 6144),
     (64, 4096, 4096), (4096, 4096, 512), (2048, 8192, 2048), (4096, 1024, 1024),
     (1024, 1024, 8192),
+    # a few hundred rows against a layer: one round of workgroups
+    (512, 4096, 4096), (512, 4096, 11008),
     # odd sizes: edge tiles, a K tail and leading dimensions that are not multiples of 4
     (1023, 1023, 1023), (4095, 4095, 4095),
     # skinny shapes (a small batch of rows against a wide layer)
