@@ -164,9 +164,11 @@ def summarize_trace(d: str) -> int:
 
 def summarize_timed_headline(d: str, line_file: str) -> int:
     """The headline kernel's launches in a kernel trace of a bench run that are that run's
-    timed steps (the line records how many headline launches come before them): their
-    median, minimum and maximum duration, the FLOP rate and peak fraction of the median,
-    and the line's own ms_per_step and roofline fraction beside them."""
+    timed steps (the line records how many headline launches come before them): their mean,
+    median, minimum and maximum duration, the FLOP rate and peak fraction of the mean and of
+    the median, and the line's own ms_per_step and roofline fraction beside them.  The mean
+    cannot exceed the line's event time per launch: the events span these same launches,
+    which run one after another, and the gaps between them."""
     import tdb_inputs as ti
     import tiled_double_buffered_amd as tdb
 
@@ -183,12 +185,16 @@ def summarize_timed_headline(d: str, line_file: str) -> int:
         return 1
     timed = durs[0][first:first + steps]
     med = statistics.median(timed) / 1e3
+    mean = statistics.mean(timed) / 1e3
     flop = 2.0 * M * N * K
     print(f"headline kernel {desc}: launches {first} .. {first + steps - 1} of "
           f"{len(durs[0])} (the timed steps)")
-    print(f"  median {med:.2f} us, min {min(timed) / 1e3:.2f} us, max {max(timed) / 1e3:.2f} us")
-    print(f"  2*M*N*K / median = {flop / (med * 1e-6) / 1e12:.3f} TFLOP/s = "
-          f"{flop / (med * 1e-6) / 1e12 / PEAK_FP32_MFMA_TFLOPS:.4f} of {PEAK_FP32_MFMA_TFLOPS}")
+    print(f"  mean {mean:.2f} us, median {med:.2f} us, min {min(timed) / 1e3:.2f} us, "
+          f"max {max(timed) / 1e3:.2f} us")
+    for label, us in (("mean", mean), ("median", med)):
+        print(f"  2*M*N*K / {label} = {flop / (us * 1e-6) / 1e12:.3f} TFLOP/s = "
+              f"{flop / (us * 1e-6) / 1e12 / PEAK_FP32_MFMA_TFLOPS:.4f} of "
+              f"{PEAK_FP32_MFMA_TFLOPS}")
     print(f"  the run's line: ms_per_step {line['ms_per_step']}, roofline.launch_ms "
           f"{line['roofline']['launch_ms']}, roofline.frac {line['roofline']['frac']}")
     return 0

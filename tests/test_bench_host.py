@@ -172,7 +172,8 @@ def test_timed_headline_summary_takes_exactly_the_timed_steps(tmp_path):
         assert bench.summarize_timed_headline(str(tmp_path), str(lf)) == 0
     text = out.getvalue()
     assert "launches 7 .. 11 of 32" in text
-    assert "median 7002.00 us, min 7000.00 us, max 7004.00 us" in text
+    assert "mean 7002.00 us, median 7002.00 us, min 7000.00 us, max 7004.00 us" in text
+    assert "2*M*N*K / mean" in text and "2*M*N*K / median" in text
 
 
 def test_counter_table_ratios_from_fake_passes(tmp_path):
