@@ -254,12 +254,13 @@ def _kernel_match(tdb, M, N, K, variant=None, cfg=None):
     grid = str(((M + info["BM"] - 1) // info["BM"]) * ((N + info["BN"] - 1) // info["BN"])
                * threads)
     if variant == tdb.VARIANT_KS and tdb.gemm_f32_config_variants(cfg) == 1 << variant:
-        # Ks16Cfg<waves, 16-k blocks per group, strided, 16-column blocks>
+        # Ks16Cfg<waves, 16-k blocks per group, strided, 16-column blocks>; no two of these
+        # configurations differ in the strided flag alone, so either value matches
         kname, flag = "gemm_f32_ks16_kernel", ""
-        tag = "Ks16Cfg<%d, %d, false, %d>" % (tdb.gemm_f32_config_ks(cfg), info["BK"] // 16,
-                                               info["BN"] // 16)
+        tags = ["Ks16Cfg<%d, %d, %s, %d>" % (tdb.gemm_f32_config_ks(cfg), info["BK"] // 16, st,
+                                              info["BN"] // 16) for st in ("false", "true")]
     else:
-        tag = f"TileCfg<{info['BM']}, {info['BN']}, {info['BK']},"
+        tags = [f"TileCfg<{info['BM']}, {info['BN']}, {info['BK']},"]
         if variant == tdb.VARIANT_MS:
             kname = "gemm_f32_ms_kernel"
             flag = ">, %d>" % tdb.gemm_f32_config_ms(cfg)[1]["stages"]
@@ -272,7 +273,7 @@ def _kernel_match(tdb, M, N, K, variant=None, cfg=None):
     desc = f"{VARIANT_NAMES[variant]} cfg{cfg} {info['BM']}x{info['BN']}x{info['BK']}"
 
     def match(name, g):
-        return kname in name and tag in name and flag in name and g == grid
+        return kname in name and any(t in name for t in tags) and flag in name and g == grid
     return desc, match
 
 

@@ -207,6 +207,16 @@ def test_config_table():
     assert any(tdb.gemm_f32_config_ks(c) > 1 for c in range(n))
 
 
+def test_ks_only_configurations_differ_in_shape():
+    """No two 16-row configurations share waves, K-group depth and tile width (they may
+    differ in how the waves share K, which the ABI does not report): the bench names a
+    traced kernel from those three alone."""
+    keys = [(tdb.gemm_f32_config_ks(c), tdb.gemm_f32_config_info(c)[1]["BK"],
+             tdb.gemm_f32_config_info(c)[1]["BN"])
+            for c in range(tdb.gemm_f32_num_configs()) if _ks_only(c)]
+    assert len(keys) == len(set(keys)), keys
+
+
 def test_ks_only_configuration_rejects_other_variants():
     """Forcing a variant the 16-row configurations have no kernel for fails before launch;
     with the automatic variant they run their K-split kernel (checked on the GPU)."""
@@ -525,7 +535,7 @@ def test_split_model_agrees_with_the_split_study():
     times of every count, tail splits as negative counts), the modelled count's time over
     the fastest count's: median at most 1.02, at least 80% of the shapes within 5%, none
     beyond 1.25.  The misses are small and mid-sized products where the model of the
-    unsplit kernel is 10-20% off; the worst, 178 x 931 x 4676, splits 16 ways at 1.15x the
+    unsplit kernel is 10-20% off; the worst, 64 x 4096 x 4096, stays unsplit at 1.15x the
     time of 4 chunks."""
     text = _header_text()
     body = text[text.index("kSplitK[] = {"):]

@@ -25,7 +25,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 MAIN_SOURCE = os.path.join(CSRC, "gemm_f32.hip")
 CFG_SOURCE = os.path.join(CSRC, "cfg_kernels.hip")
-NUM_CONFIGS = 19  # configs.h: kNumConfigs
+NUM_CONFIGS = 20  # configs.h: kNumConfigs
 SOURCES = [MAIN_SOURCE, CFG_SOURCE]
 HEADERS = [os.path.join(CSRC, f) for f in ("configs.h", "gemm_common.h", "kernels_sb_db.h",
                                             "kernels_ms.h", "kernels_ks.h", "kernels_ks16.h", "splitk_reduce.h",

@@ -30,7 +30,8 @@ template <> struct CfgById<15> { using type = Ks16Cfg<8, 2, false, 2>; };      /
 template <> struct CfgById<16> { using type = Ks16Cfg<8, 2, false, 4>; };      // 16 x 64 tile, 8 waves over K: wide layers
 template <> struct CfgById<17> { using type = Ks16Cfg<4, 2, false, 2>; };      // 16 x 32 tile, 4 waves over K: several workgroups per CU
 template <> struct CfgById<18> { using type = TileCfg<64, 128, 32, 2, 4>; };   // 8 waves of 32x32, two per SIMD: one round of tiles at a few hundred rows
-constexpr int kNumConfigs = 19;
+template <> struct CfgById<19> { using type = Ks16Cfg<4, 2, true>; };         // 16 x 16 tile, 4 waves taking alternate K groups: the workgroup reads B in one front (1-8 rows)
+constexpr int kNumConfigs = 20;
 
 typedef void (*KernelFn)(int, int, int, const float*, int64_t, const float*, int64_t, float*,
                          int64_t, int, SplitArgs);
@@ -55,7 +56,7 @@ GEMMF32_CFG_ENTRY_DECL(6) GEMMF32_CFG_ENTRY_DECL(7) GEMMF32_CFG_ENTRY_DECL(8)
 GEMMF32_CFG_ENTRY_DECL(9) GEMMF32_CFG_ENTRY_DECL(10) GEMMF32_CFG_ENTRY_DECL(11)
 GEMMF32_CFG_ENTRY_DECL(12) GEMMF32_CFG_ENTRY_DECL(13) GEMMF32_CFG_ENTRY_DECL(14)
 GEMMF32_CFG_ENTRY_DECL(15) GEMMF32_CFG_ENTRY_DECL(16) GEMMF32_CFG_ENTRY_DECL(17)
-GEMMF32_CFG_ENTRY_DECL(18)
+GEMMF32_CFG_ENTRY_DECL(18) GEMMF32_CFG_ENTRY_DECL(19)
 #undef GEMMF32_CFG_ENTRY_DECL
 
 }  // namespace gemmf32

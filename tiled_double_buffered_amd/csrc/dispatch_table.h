@@ -25,42 +25,42 @@ struct DispatchRow {
 };
 
 static const DispatchRow kDispatch[] = {
-    {128, 128, 128, 5, 13, 7, 6, 6},  // sb 4.79 us, db 4.53 us, ms 4.55 us, ks 4.10 us
-    {127, 193, 61, 5, 14, 13, 13, 6},  // sb 4.19 us, db 4.25 us, ms 4.29 us, ks 4.11 us
-    {513, 257, 129, 5, 16, 13, 13, 6},  // sb 6.17 us, db 5.82 us, ms 5.97 us, ks 4.18 us
-    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.72 us, db 18.53 us, ms 17.98 us, ks 24.02 us
-    {256, 1024, 128, 5, 17, 7, 13, 6},  // sb 5.06 us, db 4.56 us, ms 4.75 us, ks 4.07 us
-    {1024, 128, 256, 5, 17, 7, 13, 6},  // sb 7.44 us, db 6.42 us, ms 6.51 us, ks 4.03 us
-    {4096, 4096, 4096, 2, 0, 18, 0, 3},  // sb 947.74 us, db 900.41 us, ms 908.38 us, ks 1183.99 us
-    {8192, 8192, 8192, 2, 0, 4, 0, 3},  // sb 7315.52 us, db 7138.96 us, ms 7152.85 us, ks 9456.04 us
-    {256, 256, 256, 5, 17, 7, 13, 6},  // sb 7.41 us, db 6.38 us, ms 6.48 us, ks 3.71 us
-    {512, 512, 512, 5, 16, 7, 13, 6},  // sb 12.52 us, db 10.19 us, ms 10.10 us, ks 5.64 us
-    {768, 768, 768, 3, 6, 7, 6, 6},  // sb 17.99 us, db 14.46 us, ms 14.09 us, ks 14.64 us
-    {1536, 1536, 1536, 2, 6, 7, 6, 6},  // sb 76.45 us, db 68.69 us, ms 68.75 us, ks 70.71 us
-    {2048, 2048, 2048, 2, 3, 6, 3, 18},  // sb 127.55 us, db 117.14 us, ms 119.54 us, ks 158.06 us
-    {3072, 3072, 3072, 2, 11, 7, 11, 11},  // sb 419.15 us, db 383.39 us, ms 399.19 us, ks 510.89 us
-    {6144, 6144, 6144, 2, 11, 4, 11, 3},  // sb 3160.44 us, db 3021.55 us, ms 3039.85 us, ks 3934.46 us
-    {64, 4096, 4096, 5, 16, 7, 13, 6},  // sb 95.68 us, db 63.53 us, ms 61.06 us, ks 24.87 us
-    {4096, 4096, 512, 2, 2, 9, 2, 3},  // sb 127.11 us, db 122.36 us, ms 123.86 us, ks 201.26 us
-    {2048, 8192, 2048, 2, 0, 9, 0, 3},  // sb 485.42 us, db 457.45 us, ms 460.96 us, ks 620.24 us
-    {4096, 1024, 1024, 2, 3, 7, 3, 18},  // sb 66.84 us, db 61.80 us, ms 63.15 us, ks 88.67 us
-    {1024, 1024, 8192, 3, 6, 7, 6, 6},  // sb 190.71 us, db 128.90 us, ms 121.78 us, ks 150.66 us
-    {512, 4096, 4096, 3, 18, 6, 18, 18},  // sb 135.10 us, db 118.95 us, ms 116.43 us, ks 152.02 us
-    {512, 4096, 11008, 3, 18, 6, 18, 18},  // sb 345.00 us, db 314.00 us, ms 307.22 us, ks 391.58 us
-    {1023, 1023, 1023, 3, 6, 7, 6, 6},  // sb 25.15 us, db 20.94 us, ms 20.76 us, ks 27.87 us
-    {4095, 4095, 4095, 3, 0, 9, 0, 0},  // sb 999.86 us, db 913.77 us, ms 913.29 us, ks 1308.75 us
-    {16, 4096, 4096, 5, 14, 7, 6, 6},  // sb 97.71 us, db 70.49 us, ms 69.65 us, ks 15.55 us
-    {32, 4096, 4096, 5, 15, 7, 13, 10},  // sb 98.34 us, db 63.75 us, ms 63.71 us, ks 17.19 us
-    {128, 4096, 4096, 5, 13, 7, 13, 6},  // sb 95.46 us, db 63.82 us, ms 61.04 us, ks 40.15 us
-    {32, 8192, 8192, 5, 13, 7, 13, 10},  // sb 196.58 us, db 128.41 us, ms 124.35 us, ks 48.26 us
-    {1, 4096, 4096, 5, 14, 7, 6, 6},  // sb 97.17 us, db 70.41 us, ms 69.49 us, ks 14.29 us
-    {8, 4096, 4096, 5, 14, 7, 6, 6},  // sb 97.62 us, db 70.55 us, ms 69.63 us, ks 14.65 us
-    {16, 11008, 4096, 5, 16, 7, 13, 6},  // sb 100.02 us, db 70.60 us, ms 69.73 us, ks 30.89 us
-    {16, 4096, 11008, 5, 14, 7, 6, 6},  // sb 262.42 us, db 184.35 us, ms 182.06 us, ks 37.64 us
-    {16, 8192, 8192, 5, 17, 7, 13, 6},  // sb 195.68 us, db 140.39 us, ms 136.27 us, ks 39.77 us
-    {4, 1024, 1024, 5, 14, 7, 6, 6},  // sb 23.37 us, db 19.67 us, ms 19.67 us, ks 4.55 us
-    {16, 32000, 4096, 3, 10, 13, 13, 10},  // sb 154.37 us, db 108.74 us, ms 85.64 us, ks 96.38 us
-    {1024, 8192, 8192, 2, 2, 7, 2, 3},  // sb 1002.50 us, db 899.50 us, ms 912.77 us, ks 1181.05 us
+    {128, 128, 128, 5, 13, 7, 13, 6},  // sb 4.75 us, db 4.49 us, ms 4.55 us, ks 3.96 us
+    {127, 193, 61, 5, 17, 7, 6, 6},  // sb 4.17 us, db 4.20 us, ms 4.27 us, ks 4.11 us
+    {513, 257, 129, 5, 17, 13, 13, 6},  // sb 6.17 us, db 5.82 us, ms 5.96 us, ks 4.27 us
+    {1024, 1024, 1024, 3, 6, 7, 6, 6},  // sb 23.78 us, db 18.57 us, ms 18.04 us, ks 24.14 us
+    {256, 1024, 128, 5, 15, 7, 13, 6},  // sb 5.00 us, db 4.63 us, ms 4.76 us, ks 4.18 us
+    {1024, 128, 256, 5, 17, 7, 13, 6},  // sb 7.43 us, db 6.45 us, ms 6.50 us, ks 4.21 us
+    {4096, 4096, 4096, 2, 0, 9, 0, 3},  // sb 967.42 us, db 906.93 us, ms 916.23 us, ks 1210.85 us
+    {8192, 8192, 8192, 2, 0, 4, 0, 3},  // sb 7394.54 us, db 7196.11 us, ms 7226.13 us, ks 9858.91 us
+    {256, 256, 256, 5, 15, 7, 13, 6},  // sb 7.41 us, db 6.42 us, ms 6.49 us, ks 4.18 us
+    {512, 512, 512, 5, 16, 7, 13, 6},  // sb 12.50 us, db 10.20 us, ms 10.10 us, ks 5.68 us
+    {768, 768, 768, 3, 6, 7, 6, 6},  // sb 18.07 us, db 14.51 us, ms 14.14 us, ks 14.66 us
+    {1536, 1536, 1536, 2, 6, 7, 6, 6},  // sb 76.70 us, db 68.93 us, ms 69.09 us, ks 72.30 us
+    {2048, 2048, 2048, 2, 3, 6, 3, 3},  // sb 129.46 us, db 117.88 us, ms 121.35 us, ks 161.41 us
+    {3072, 3072, 3072, 2, 11, 7, 11, 11},  // sb 426.31 us, db 387.28 us, ms 402.62 us, ks 518.91 us
+    {6144, 6144, 6144, 2, 11, 4, 11, 3},  // sb 3198.57 us, db 3066.33 us, ms 3076.57 us, ks 4079.98 us
+    {64, 4096, 4096, 5, 13, 7, 13, 6},  // sb 95.81 us, db 63.47 us, ms 61.11 us, ks 24.96 us
+    {4096, 4096, 512, 2, 2, 9, 2, 3},  // sb 128.43 us, db 123.53 us, ms 125.12 us, ks 202.91 us
+    {2048, 8192, 2048, 2, 0, 9, 0, 3},  // sb 490.81 us, db 462.32 us, ms 465.90 us, ks 630.07 us
+    {4096, 1024, 1024, 2, 3, 7, 3, 3},  // sb 67.41 us, db 62.15 us, ms 64.09 us, ks 89.46 us
+    {1024, 1024, 8192, 3, 6, 7, 6, 6},  // sb 190.56 us, db 128.89 us, ms 122.53 us, ks 152.49 us
+    {512, 4096, 4096, 3, 18, 6, 18, 18},  // sb 136.55 us, db 120.63 us, ms 118.27 us, ks 155.17 us
+    {512, 4096, 11008, 3, 18, 6, 18, 18},  // sb 349.38 us, db 318.75 us, ms 311.52 us, ks 400.92 us
+    {1023, 1023, 1023, 3, 6, 7, 6, 6},  // sb 25.19 us, db 21.09 us, ms 20.84 us, ks 27.74 us
+    {4095, 4095, 4095, 3, 0, 9, 0, 0},  // sb 1005.53 us, db 921.67 us, ms 921.06 us, ks 1344.13 us
+    {16, 4096, 4096, 5, 19, 7, 6, 6},  // sb 97.31 us, db 70.38 us, ms 69.53 us, ks 15.22 us
+    {32, 4096, 4096, 5, 15, 7, 13, 10},  // sb 97.90 us, db 63.53 us, ms 63.51 us, ks 18.42 us
+    {128, 4096, 4096, 5, 13, 7, 13, 6},  // sb 96.01 us, db 64.41 us, ms 61.64 us, ks 40.93 us
+    {32, 8192, 8192, 5, 13, 7, 13, 10},  // sb 196.54 us, db 128.98 us, ms 124.97 us, ks 48.36 us
+    {1, 4096, 4096, 5, 19, 7, 6, 6},  // sb 96.79 us, db 70.32 us, ms 69.42 us, ks 12.31 us
+    {8, 4096, 4096, 5, 19, 7, 6, 6},  // sb 97.02 us, db 70.29 us, ms 69.44 us, ks 13.91 us
+    {16, 11008, 4096, 5, 16, 7, 6, 6},  // sb 100.10 us, db 71.31 us, ms 70.02 us, ks 30.76 us
+    {16, 4096, 11008, 5, 14, 7, 6, 7},  // sb 262.17 us, db 183.96 us, ms 180.70 us, ks 37.50 us
+    {16, 8192, 8192, 5, 17, 7, 13, 6},  // sb 194.84 us, db 140.12 us, ms 136.44 us, ks 39.66 us
+    {4, 1024, 1024, 5, 19, 7, 6, 6},  // sb 23.30 us, db 19.61 us, ms 19.62 us, ks 4.42 us
+    {16, 32000, 4096, 3, 10, 13, 13, 10},  // sb 154.57 us, db 108.74 us, ms 86.80 us, ks 96.31 us
+    {1024, 8192, 8192, 2, 2, 18, 2, 3},  // sb 1016.33 us, db 908.71 us, ms 922.85 us, ks 1203.24 us
 };
 constexpr int kDispatchRows = (int)(sizeof(kDispatch) / sizeof(kDispatch[0]));
 
@@ -92,55 +92,56 @@ struct ModelRow {
 };
 
 static const ModelRow kModel[] = {
-    {1, 0, 9.3728, 0.0000, 4.02716, 0.35254},  // median |error| 2.0%
-    {1, 1, 10.1124, 0.0000, 7.73141, 0.46750},  // median |error| 1.4%
-    {1, 2, 5.7328, 0.0000, 2.22072, 0.00000},  // median |error| 4.2%
-    {1, 3, 3.9777, 0.0000, 1.21180, 0.00000},  // median |error| 9.0%
-    {1, 4, 4.0103, 0.0000, 2.22303, 0.00000},  // median |error| 5.0%
-    {1, 5, 3.4672, 0.0000, 1.19755, 0.00000},  // median |error| 7.6%
-    {1, 6, 3.1125, 0.0000, 0.63582, 0.00000},  // median |error| 12.6%
-    {1, 7, 3.0355, 0.0000, 1.18089, 0.00000},  // median |error| 7.6%
-    {1, 8, 6.7480, 0.0000, 7.60802, 0.31901},  // median |error| 1.4%
-    {1, 9, 4.5195, 0.0000, 4.05620, 0.00000},  // median |error| 2.3%
-    {1, 10, 3.1991, 0.0000, 0.65901, 0.00000},  // median |error| 13.5%
-    {1, 11, 6.4931, 0.0000, 2.43914, 0.27751},  // median |error| 3.0%
-    {1, 12, 6.8586, 0.0000, 4.55077, 0.38531},  // median |error| 1.7%
-    {1, 13, 4.5417, 0.0000, 0.17999, 0.00000},  // median |error| 20.7%
-    {1, 18, 3.0616, 0.0000, 1.17536, 0.00000},  // median |error| 7.4%
-    {2, 0, 10.3909, 0.0000, 3.45493, 0.08922},  // median |error| 1.1%
-    {2, 1, 10.6935, 0.0000, 6.92182, 0.16154},  // median |error| 1.1%
-    {2, 2, 6.4851, 0.0000, 1.74713, 0.04255},  // median |error| 1.4%
-    {2, 3, 4.4366, 0.0000, 0.88252, 0.06461},  // median |error| 2.5%
-    {2, 4, 4.6436, 0.0000, 1.75111, 0.05179},  // median |error| 1.6%
-    {2, 5, 4.0199, 0.0000, 0.92530, 0.00147},  // median |error| 1.9%
-    {2, 6, 3.1559, 0.0000, 0.49918, 0.00000},  // median |error| 4.3%
-    {2, 7, 3.1606, 0.0000, 1.04411, 0.00000},  // median |error| 3.7%
-    {2, 8, 7.2927, 0.0000, 7.03681, 0.18584},  // median |error| 0.6%
-    {2, 9, 5.2522, 0.0000, 3.46922, 0.11304},  // median |error| 0.8%
-    {2, 10, 3.2135, 0.0000, 0.53034, 0.00000},  // median |error| 5.2%
-    {2, 11, 7.2219, 0.0000, 1.97990, 0.04487},  // median |error| 0.8%
-    {2, 12, 7.7526, 0.0000, 3.91210, 0.10987},  // median |error| 0.7%
-    {2, 13, 4.4355, 0.0000, 0.16450, 0.00000},  // median |error| 18.6%
-    {2, 18, 3.3699, 0.0000, 0.93567, 0.00542},  // median |error| 2.6%
-    {3, 0, 10.3392, 0.0000, 3.54088, 0.12892},  // median |error| 1.8%
-    {3, 1, 10.8395, 0.0000, 7.08836, 0.33020},  // median |error| 2.0%
-    {3, 2, 6.8914, 0.0000, 1.78580, 0.07044},  // median |error| 1.8%
-    {3, 3, 4.5746, 0.0000, 0.90866, 0.00732},  // median |error| 1.9%
-    {3, 4, 4.6235, 0.0000, 1.80187, 0.10390},  // median |error| 1.6%
-    {3, 5, 4.2282, 0.0000, 0.92429, 0.06108},  // median |error| 1.7%
-    {3, 6, 3.2620, 0.0000, 0.49482, 0.00000},  // median |error| 4.5%
-    {3, 7, 3.2399, 0.0000, 1.04965, 0.05124},  // median |error| 3.6%
-    {3, 8, 7.7692, 0.0000, 7.05560, 0.18000},  // median |error| 0.9%
-    {3, 9, 5.2880, 0.0000, 3.51405, 0.12731},  // median |error| 1.0%
-    {3, 10, 3.2503, 0.0000, 0.51917, 0.00000},  // median |error| 4.9%
-    {3, 11, 7.2534, 0.0000, 2.03371, 0.06878},  // median |error| 2.4%
-    {3, 12, 7.7739, 0.0000, 4.02706, 0.19922},  // median |error| 2.7%
-    {3, 18, 3.5252, 0.0000, 0.93274, 0.02597},  // median |error| 2.5%
-    {5, 13, 2.7933, 0.9870, 0.15334, 0.00000},  // median |error| 7.2%
-    {5, 14, 2.8822, 0.6060, 0.04779, 0.02341},  // median |error| 8.8%
-    {5, 15, 2.7821, 0.5928, 0.09326, 0.00000},  // median |error| 8.6%
-    {5, 16, 1.5213, 1.9727, 0.15725, 0.01218},  // median |error| 4.9%
-    {5, 17, 3.2518, 0.1547, 0.09870, 0.00000},  // median |error| 8.8%
+    {1, 0, 9.3632, 0.0000, 4.01241, 0.38787},  // median |error| 2.1%
+    {1, 1, 10.1077, 0.0000, 7.70279, 0.53779},  // median |error| 1.4%
+    {1, 2, 5.7211, 0.0000, 2.21898, 0.00000},  // median |error| 4.4%
+    {1, 3, 3.9682, 0.0000, 1.21321, 0.00000},  // median |error| 8.6%
+    {1, 4, 3.9871, 0.0000, 2.22701, 0.00000},  // median |error| 4.7%
+    {1, 5, 3.4551, 0.0000, 1.20224, 0.00000},  // median |error| 8.1%
+    {1, 6, 3.1436, 0.0000, 0.63944, 0.00000},  // median |error| 11.8%
+    {1, 7, 3.0665, 0.0000, 1.18671, 0.00000},  // median |error| 7.9%
+    {1, 8, 6.7604, 0.0000, 7.57703, 0.41588},  // median |error| 1.5%
+    {1, 9, 4.4797, 0.0000, 4.05831, 0.00000},  // median |error| 2.4%
+    {1, 10, 3.2068, 0.0000, 0.66638, 0.00000},  // median |error| 14.4%
+    {1, 11, 6.4845, 0.0000, 2.43168, 0.29842},  // median |error| 2.8%
+    {1, 12, 6.8461, 0.0000, 4.53739, 0.43049},  // median |error| 1.7%
+    {1, 13, 4.6119, 0.0000, 0.18240, 0.00000},  // median |error| 21.6%
+    {1, 18, 3.0348, 0.0000, 1.18091, 0.00000},  // median |error| 7.2%
+    {2, 0, 10.3640, 0.0000, 3.44435, 0.13208},  // median |error| 1.1%
+    {2, 1, 10.6700, 0.0000, 6.90003, 0.25190},  // median |error| 1.1%
+    {2, 2, 6.4896, 0.0000, 1.74115, 0.06493},  // median |error| 1.4%
+    {2, 3, 4.4481, 0.0000, 0.87960, 0.07593},  // median |error| 2.5%
+    {2, 4, 4.6447, 0.0000, 1.74621, 0.07240},  // median |error| 1.8%
+    {2, 5, 4.0225, 0.0000, 0.92156, 0.01675},  // median |error| 2.0%
+    {2, 6, 3.2018, 0.0000, 0.50229, 0.00000},  // median |error| 3.8%
+    {2, 7, 3.2306, 0.0000, 1.04862, 0.00000},  // median |error| 3.5%
+    {2, 8, 7.2903, 0.0000, 7.01239, 0.29774},  // median |error| 0.6%
+    {2, 9, 5.2468, 0.0000, 3.45879, 0.15948},  // median |error| 0.7%
+    {2, 10, 3.2112, 0.0000, 0.53504, 0.00000},  // median |error| 4.1%
+    {2, 11, 7.2072, 0.0000, 1.97461, 0.06669},  // median |error| 0.6%
+    {2, 12, 7.7324, 0.0000, 3.90146, 0.15705},  // median |error| 0.7%
+    {2, 13, 4.4979, 0.0000, 0.16684, 0.00000},  // median |error| 17.3%
+    {2, 18, 3.3845, 0.0000, 0.93162, 0.02220},  // median |error| 2.5%
+    {3, 0, 10.3181, 0.0000, 3.52999, 0.17236},  // median |error| 1.8%
+    {3, 1, 10.8188, 0.0000, 7.06593, 0.41509},  // median |error| 1.9%
+    {3, 2, 6.8961, 0.0000, 1.77992, 0.09137},  // median |error| 1.7%
+    {3, 3, 4.5854, 0.0000, 0.90573, 0.01793},  // median |error| 2.1%
+    {3, 4, 4.6269, 0.0000, 1.79682, 0.12476},  // median |error| 1.6%
+    {3, 5, 4.2478, 0.0000, 0.92062, 0.07395},  // median |error| 1.6%
+    {3, 6, 3.2849, 0.0000, 0.49831, 0.00000},  // median |error| 3.6%
+    {3, 7, 3.3147, 0.0000, 1.04061, 0.06866},  // median |error| 3.3%
+    {3, 8, 7.7674, 0.0000, 7.03042, 0.28652},  // median |error| 0.9%
+    {3, 9, 5.2823, 0.0000, 3.50331, 0.17726},  // median |error| 1.0%
+    {3, 10, 3.2807, 0.0000, 0.52370, 0.00000},  // median |error| 4.2%
+    {3, 11, 7.2382, 0.0000, 2.02838, 0.08967},  // median |error| 2.2%
+    {3, 12, 7.7546, 0.0000, 4.01655, 0.24488},  // median |error| 2.7%
+    {3, 18, 3.5314, 0.0000, 0.92927, 0.04049},  // median |error| 2.6%
+    {5, 13, 2.8599, 0.9738, 0.15517, 0.00000},  // median |error| 6.7%
+    {5, 14, 3.0424, 0.5866, 0.04514, 0.02661},  // median |error| 8.9%
+    {5, 15, 2.8875, 0.5793, 0.09382, 0.00000},  // median |error| 9.3%
+    {5, 16, 1.6649, 1.9458, 0.15595, 0.01424},  // median |error| 4.7%
+    {5, 17, 3.3774, 0.1541, 0.09836, 0.00000},  // median |error| 9.1%
+    {5, 19, 3.4063, 0.0176, 0.05785, 0.01927},  // median |error| 9.6%
 };
 constexpr int kModelRows = (int)(sizeof(kModel) / sizeof(kModel[0]));
 constexpr int kVariantKS = 5;
@@ -201,15 +202,15 @@ static inline int select_for_variant(int64_t M, int64_t N, int64_t K, int varian
 // Split-K: the number of K chunks (1 = do not split) with the least modelled time among
 // the counts the split study measured.  A split launch costs the GEMM of its chunks, all in
 // one grid (the model above, with the workgroups multiplied by the chunks), plus
-//     3.4594 us (the reduction's launch)
-//   + 0.14133 us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
+//     3.2615 us (the reduction's launch)
+//   + 0.13525 us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
 //     written once and read once by the reduction, and C)
-//   + 0.3726 us per round of workgroups of the split grid (each workgroup's
+//   + 0.4102 us per round of workgroups of the split grid (each workgroup's
 //     first copy and partial-tile store, which short chunks no longer hide),
 // the constants fitted (>= 0, least squares) to the 41 shapes of the split study below.
-constexpr double kSplitFixedUs = 3.4594;
-constexpr double kSplitUsPerMB = 0.14133;
-constexpr double kSplitUsPerRound = 0.3726;
+constexpr double kSplitFixedUs = 3.2615;
+constexpr double kSplitUsPerMB = 0.13525;
+constexpr double kSplitUsPerRound = 0.4102;
 constexpr int kSplitChoices[] = {1, 2, 4, 8, 16};
 
 // The split study: trailing comments hold the measured microseconds of each count.
@@ -219,47 +220,47 @@ struct SplitRow {
 };
 
 static const SplitRow kSplitK[] = {
-    {16, 4096, 4096, 1},  // 1: 15.4, 2: 39.0, 4: 23.1, 8: 17.6, 16: 21.5
-    {32, 4096, 4096, 1},  // 1: 17.0, 2: 39.4, 4: 23.5, 8: 17.3, 16: 21.6
-    {64, 4096, 4096, 4},  // 1: 24.8, 2: 35.1, 4: 21.6, 8: 23.3, 16: 26.9
-    {128, 4096, 4096, 2},  // 1: 41.2, 2: 36.1, 4: 37.2, 8: 39.7, 16: 43.7
-    {32, 8192, 8192, 4},  // 1: 48.8, 2: 73.2, 4: 45.1, 8: 46.9, 16: 52.7
-    {64, 8192, 8192, 2},  // 1: 83.9, 2: 70.9, 4: 74.7, 8: 76.7, 16: 83.8
-    {256, 256, 8192, 16},  // 1: 24.1, 2: 63.2, 4: 34.9, 8: 22.0, 16: 17.3
-    {512, 512, 8192, 4},  // 1: 46.2, 2: 64.3, 4: 36.0, 8: 37.2, 16: 40.9
-    {1024, 1024, 1024, 1},  // 1: 18.1, 2: 24.4, 4: 28.0, 8: 32.8, 16: 39.9
-    {2048, 2048, 2048, 1},  // 1: 118.2, 2: 130.2, 4: 141.0, 8: 159.2, 16: 207.5
-    {4096, 4096, 4096, 1},  // 1: 909.2, 2: 950.8, 4: 1001.5, 8: 1128.0, 16: 1304.3, -2: 1076.7, -4: 1089.7, -8: 1122.8, -16: 1176.0
-    {1536, 1536, 1536, -4},  // 1: 68.9, 2: 67.0, 4: 64.9, 8: 77.6, 16: 89.4, -2: 62.1, -4: 58.3, -8: 58.4, -16: 64.0
-    {1536, 1536, 4096, -8},  // 1: 178.3, 2: 156.0, 4: 143.6, 8: 155.2, 16: 184.5, -2: 151.0, -4: 145.0, -8: 138.3, -16: 143.4
-    {2560, 2560, 2560, -8},  // 1: 258.7, 2: 262.6, 4: 273.9, 8: 307.0, 16: 365.3, -2: 249.2, -4: 243.0, -8: 238.6, -16: 244.2
-    {1280, 1280, 2048, 1},  // 1: 61.9, 2: 66.0, 4: 66.8, 8: 71.9, 16: 82.9, -2: 67.4, -4: 62.2, -8: 64.8, -16: 67.2
-    {5000, 5000, 1000, -8},  // 1: 392.3, 2: 451.2, 4: 527.7, 8: 761.9, 16: 1148.8, -2: 393.5, -4: 390.4, -8: 380.5, -16: 385.9
-    {1536, 3072, 4096, -8},  // 1: 292.8, 2: 269.8, 4: 280.4, 8: 320.8, 16: 372.6, -2: 277.8, -4: 271.6, -8: 266.4, -16: 270.2
-    {39, 432, 6224, 1},  // 1: 13.9, 2: 56.2, 4: 31.9, 8: 20.6, 16: 16.4
-    {11, 1640, 2822, 1},  // 1: 7.5, 2: 29.0, 4: 18.5, 8: 13.2, 16: 12.4
-    {11, 1486, 1136, 1},  // 1: 5.5, 2: 14.6, 4: 11.2, 8: 9.6, 16: 9.7
-    {66, 326, 1317, 1},  // 1: 5.4, 2: 16.9, 4: 12.1, 8: 9.7, 16: 9.7
-    {63, 4495, 1443, 1},  // 1: 17.7, 2: 19.2, 4: 19.4, 8: 19.1, 16: 19.7
-    {24, 2252, 14173, 8},  // 1: 55.1, 2: 121.5, 4: 64.5, 8: 38.2, 16: 40.6
-    {132, 1012, 15340, 16},  // 1: 85.0, 2: 131.8, 4: 69.4, 8: 65.4, 16: 56.3
-    {10, 5016, 2286, 1},  // 1: 10.7, 2: 24.5, 4: 17.0, 8: 19.8, 16: 17.1
-    {16, 385, 2409, 1},  // 1: 7.1, 2: 25.1, 4: 16.1, 8: 11.8, 16: 11.2
-    {420, 479, 5136, 4},  // 1: 32.1, 2: 48.2, 4: 28.6, 8: 30.9, 16: 33.3
-    {178, 931, 4676, 4},  // 1: 30.0, 2: 44.4, 4: 26.3, 8: 28.5, 16: 30.3
-    {11, 315, 1813, 1},  // 1: 6.0, 2: 20.7, 4: 13.9, 8: 10.6, 16: 10.3
-    {217, 1127, 2447, 1},  // 1: 18.5, 2: 26.8, 4: 18.5, 8: 21.4, 16: 22.9
-    {137, 1231, 2351, 1},  // 1: 17.6, 2: 25.4, 4: 17.7, 8: 19.8, 16: 22.4
-    {378, 2886, 2015, -8},  // 1: 56.5, 2: 57.3, 4: 52.5, 8: 56.9, 16: 65.1, -2: 52.3, -4: 46.9, -8: 44.7, -16: 45.6
-    {130, 1580, 11590, 1},  // 1: 65.9, 2: 101.4, 4: 94.4, 8: 74.4, 16: 71.7
-    {276, 694, 15508, 8},  // 1: 88.1, 2: 133.3, 4: 70.4, 8: 68.0, 16: 71.0
-    {14, 1090, 8356, 16},  // 1: 24.9, 2: 73.9, 4: 40.0, 8: 24.5, 16: 18.7
-    {17, 1394, 1142, 1},  // 1: 5.4, 2: 14.6, 4: 11.0, 8: 9.5, 16: 9.3
-    {205, 3623, 5015, 4},  // 1: 87.5, 2: 83.7, 4: 83.3, 8: 84.7, 16: 93.1
-    {560, 759, 7039, 4},  // 1: 73.4, 2: 65.0, 4: 61.6, 8: 61.8, 16: 67.9
-    {143, 1910, 3628, 2},  // 1: 41.7, 2: 36.0, 4: 36.1, 8: 40.3, 16: 38.4
-    {471, 6763, 3812, -2},  // 1: 222.3, 2: 219.0, 4: 217.5, 8: 243.8, 16: 303.1, -2: 210.3, -4: 212.5, -8: 210.8, -16: 212.1
-    {201, 316, 7161, 8},  // 1: 29.7, 2: 64.8, 4: 35.7, 8: 22.6, 16: 24.6
+    {16, 4096, 4096, 1},  // 1: 15.3, 2: 38.8, 4: 22.9, 8: 17.4, 16: 21.4
+    {32, 4096, 4096, 1},  // 1: 17.1, 2: 39.3, 4: 23.4, 8: 17.2, 16: 21.7
+    {64, 4096, 4096, 4},  // 1: 24.9, 2: 34.9, 4: 21.6, 8: 23.1, 16: 26.8
+    {128, 4096, 4096, 2},  // 1: 40.4, 2: 35.9, 4: 36.9, 8: 39.6, 16: 43.3
+    {32, 8192, 8192, 4},  // 1: 48.5, 2: 73.4, 4: 45.1, 8: 46.8, 16: 52.6
+    {64, 8192, 8192, 2},  // 1: 81.1, 2: 68.7, 4: 74.5, 8: 77.3, 16: 82.1
+    {256, 256, 8192, 16},  // 1: 24.1, 2: 63.2, 4: 34.8, 8: 21.8, 16: 17.3
+    {512, 512, 8192, 4},  // 1: 46.1, 2: 63.9, 4: 35.9, 8: 37.2, 16: 40.4
+    {1024, 1024, 1024, 1},  // 1: 18.0, 2: 24.5, 4: 28.0, 8: 32.8, 16: 39.9
+    {2048, 2048, 2048, 1},  // 1: 117.7, 2: 130.2, 4: 141.2, 8: 159.2, 16: 208.2
+    {4096, 4096, 4096, 1},  // 1: 912.6, 2: 955.0, 4: 1005.1, 8: 1131.5, 16: 1295.1, -2: 1078.1, -4: 1093.7, -8: 1125.9, -16: 1179.4
+    {1536, 1536, 1536, -4},  // 1: 68.7, 2: 66.9, 4: 65.1, 8: 77.3, 16: 89.1, -2: 62.0, -4: 57.8, -8: 58.2, -16: 64.0
+    {1536, 1536, 4096, -8},  // 1: 172.0, 2: 155.4, 4: 143.9, 8: 155.2, 16: 184.3, -2: 150.5, -4: 139.5, -8: 137.5, -16: 140.4
+    {2560, 2560, 2560, -8},  // 1: 258.3, 2: 260.8, 4: 272.0, 8: 305.8, 16: 365.5, -2: 245.8, -4: 241.7, -8: 235.5, -16: 241.6
+    {1280, 1280, 2048, -4},  // 1: 62.0, 2: 66.2, 4: 66.6, 8: 71.7, 16: 82.8, -2: 67.1, -4: 61.8, -8: 62.9, -16: 66.9
+    {5000, 5000, 1000, -8},  // 1: 393.3, 2: 447.6, 4: 528.8, 8: 762.9, 16: 1149.9, -2: 389.0, -4: 390.2, -8: 379.6, -16: 385.3
+    {1536, 3072, 4096, -8},  // 1: 291.1, 2: 269.9, 4: 280.3, 8: 320.5, 16: 372.1, -2: 271.6, -4: 267.8, -8: 265.9, -16: 269.8
+    {39, 432, 6224, 1},  // 1: 13.9, 2: 56.1, 4: 32.0, 8: 20.5, 16: 16.4
+    {11, 1640, 2822, 1},  // 1: 7.5, 2: 29.1, 4: 18.4, 8: 13.1, 16: 12.5
+    {11, 1486, 1136, 1},  // 1: 5.3, 2: 14.5, 4: 10.9, 8: 9.6, 16: 9.6
+    {66, 326, 1317, 1},  // 1: 5.4, 2: 17.2, 4: 12.0, 8: 9.9, 16: 9.8
+    {63, 4495, 1443, 1},  // 1: 17.6, 2: 18.8, 4: 19.3, 8: 19.0, 16: 19.8
+    {24, 2252, 14173, 8},  // 1: 55.3, 2: 120.9, 4: 64.1, 8: 38.0, 16: 40.5
+    {132, 1012, 15340, 16},  // 1: 84.7, 2: 131.3, 4: 69.2, 8: 65.5, 16: 56.1
+    {10, 5016, 2286, 1},  // 1: 10.6, 2: 24.4, 4: 16.9, 8: 19.8, 16: 17.1
+    {16, 385, 2409, 1},  // 1: 7.0, 2: 25.0, 4: 15.9, 8: 11.8, 16: 11.0
+    {420, 479, 5136, 4},  // 1: 32.0, 2: 48.2, 4: 28.5, 8: 30.9, 16: 33.3
+    {178, 931, 4676, 4},  // 1: 29.8, 2: 44.3, 4: 26.3, 8: 28.4, 16: 30.2
+    {11, 315, 1813, 1},  // 1: 5.9, 2: 20.6, 4: 13.9, 8: 10.6, 16: 10.2
+    {217, 1127, 2447, 1},  // 1: 18.4, 2: 26.7, 4: 18.5, 8: 21.4, 16: 22.8
+    {137, 1231, 2351, 1},  // 1: 17.6, 2: 25.4, 4: 17.6, 8: 19.8, 16: 22.4
+    {378, 2886, 2015, -8},  // 1: 56.3, 2: 57.2, 4: 52.4, 8: 56.9, 16: 64.9, -2: 52.3, -4: 47.0, -8: 44.5, -16: 45.5
+    {130, 1580, 11590, 1},  // 1: 65.8, 2: 101.0, 4: 94.2, 8: 74.3, 16: 71.5
+    {276, 694, 15508, 8},  // 1: 88.3, 2: 132.5, 4: 70.4, 8: 68.1, 16: 70.7
+    {14, 1090, 8356, 16},  // 1: 25.0, 2: 73.9, 4: 40.1, 8: 24.5, 16: 18.7
+    {17, 1394, 1142, 1},  // 1: 5.4, 2: 14.5, 4: 10.9, 8: 9.5, 16: 9.3
+    {205, 3623, 5015, 4},  // 1: 87.1, 2: 83.5, 4: 83.3, 8: 84.6, 16: 92.8
+    {560, 759, 7039, 4},  // 1: 72.8, 2: 64.8, 4: 61.8, 8: 61.8, 16: 67.4
+    {143, 1910, 3628, 2},  // 1: 41.7, 2: 35.8, 4: 35.9, 8: 40.3, 16: 38.2
+    {471, 6763, 3812, -8},  // 1: 222.6, 2: 217.9, 4: 216.7, 8: 243.6, 16: 302.4, -2: 208.7, -4: 206.6, -8: 203.0, -16: 205.2
+    {201, 316, 7161, 8},  // 1: 29.7, 2: 64.5, 4: 35.7, 8: 22.6, 16: 24.6
 };
 
 static inline double model_best_us(int64_t M, int64_t N, int64_t K, int64_t wg_factor) {

@@ -47,7 +47,7 @@ static const CfgEntry kConfigs[] = {
     cfg_entry_0(),  cfg_entry_1(),  cfg_entry_2(),  cfg_entry_3(),  cfg_entry_4(),
     cfg_entry_5(),  cfg_entry_6(),  cfg_entry_7(),  cfg_entry_8(),  cfg_entry_9(),
     cfg_entry_10(), cfg_entry_11(), cfg_entry_12(), cfg_entry_13(), cfg_entry_14(),
-    cfg_entry_15(), cfg_entry_16(), cfg_entry_17(), cfg_entry_18(),
+    cfg_entry_15(), cfg_entry_16(), cfg_entry_17(), cfg_entry_18(), cfg_entry_19(),
 };
 static_assert(sizeof(kConfigs) / sizeof(kConfigs[0]) == kNumConfigs, "configuration table");
 
