@@ -535,8 +535,8 @@ def test_split_model_agrees_with_the_split_study():
     times of every count, tail splits as negative counts), the modelled count's time over
     the fastest count's: median at most 1.02, at least 80% of the shapes within 5%, none
     beyond 1.25.  The misses are small and mid-sized products where the model of the
-    unsplit kernel is 10-20% off; the worst, 64 x 4096 x 4096, stays unsplit at 1.15x the
-    time of 4 chunks."""
+    unsplit kernel is 10-20% off; the worst, 39 x 432 x 6224, splits 16 ways at 1.18x the
+    unsplit time."""
     text = _header_text()
     body = text[text.index("kSplitK[] = {"):]
     body = body[:body.index("};")]

@@ -84,64 +84,64 @@ static inline const DispatchRow* dispatch_exact(int64_t M, int64_t N, int64_t K)
 // product that streams B, where a partly filled round of workgroups is not cheaper per
 // byte), and b a cost per round that only the K-split kernels have (each of their rounds
 // ends in a hand-off through LDS; b = 0 elsewhere).  They were fitted per pair by least
-// squares on relative error, all kept >= 0, to the 84 shapes measured for this file
-// (the table's 36 and 48 seeded shapes outside it).
+// squares on relative error, all kept >= 0, to the 100 shapes measured for this file
+// (the table's 36 and 64 seeded shapes outside it).
 struct ModelRow {
   int variant, cfg;
   double a_us, b_us, g_us, h_us;
 };
 
 static const ModelRow kModel[] = {
-    {1, 0, 9.3632, 0.0000, 4.01241, 0.38787},  // median |error| 2.1%
-    {1, 1, 10.1077, 0.0000, 7.70279, 0.53779},  // median |error| 1.4%
-    {1, 2, 5.7211, 0.0000, 2.21898, 0.00000},  // median |error| 4.4%
-    {1, 3, 3.9682, 0.0000, 1.21321, 0.00000},  // median |error| 8.6%
-    {1, 4, 3.9871, 0.0000, 2.22701, 0.00000},  // median |error| 4.7%
-    {1, 5, 3.4551, 0.0000, 1.20224, 0.00000},  // median |error| 8.1%
-    {1, 6, 3.1436, 0.0000, 0.63944, 0.00000},  // median |error| 11.8%
-    {1, 7, 3.0665, 0.0000, 1.18671, 0.00000},  // median |error| 7.9%
-    {1, 8, 6.7604, 0.0000, 7.57703, 0.41588},  // median |error| 1.5%
-    {1, 9, 4.4797, 0.0000, 4.05831, 0.00000},  // median |error| 2.4%
-    {1, 10, 3.2068, 0.0000, 0.66638, 0.00000},  // median |error| 14.4%
-    {1, 11, 6.4845, 0.0000, 2.43168, 0.29842},  // median |error| 2.8%
-    {1, 12, 6.8461, 0.0000, 4.53739, 0.43049},  // median |error| 1.7%
-    {1, 13, 4.6119, 0.0000, 0.18240, 0.00000},  // median |error| 21.6%
-    {1, 18, 3.0348, 0.0000, 1.18091, 0.00000},  // median |error| 7.2%
-    {2, 0, 10.3640, 0.0000, 3.44435, 0.13208},  // median |error| 1.1%
-    {2, 1, 10.6700, 0.0000, 6.90003, 0.25190},  // median |error| 1.1%
-    {2, 2, 6.4896, 0.0000, 1.74115, 0.06493},  // median |error| 1.4%
-    {2, 3, 4.4481, 0.0000, 0.87960, 0.07593},  // median |error| 2.5%
-    {2, 4, 4.6447, 0.0000, 1.74621, 0.07240},  // median |error| 1.8%
-    {2, 5, 4.0225, 0.0000, 0.92156, 0.01675},  // median |error| 2.0%
-    {2, 6, 3.2018, 0.0000, 0.50229, 0.00000},  // median |error| 3.8%
-    {2, 7, 3.2306, 0.0000, 1.04862, 0.00000},  // median |error| 3.5%
-    {2, 8, 7.2903, 0.0000, 7.01239, 0.29774},  // median |error| 0.6%
-    {2, 9, 5.2468, 0.0000, 3.45879, 0.15948},  // median |error| 0.7%
-    {2, 10, 3.2112, 0.0000, 0.53504, 0.00000},  // median |error| 4.1%
-    {2, 11, 7.2072, 0.0000, 1.97461, 0.06669},  // median |error| 0.6%
-    {2, 12, 7.7324, 0.0000, 3.90146, 0.15705},  // median |error| 0.7%
-    {2, 13, 4.4979, 0.0000, 0.16684, 0.00000},  // median |error| 17.3%
-    {2, 18, 3.3845, 0.0000, 0.93162, 0.02220},  // median |error| 2.5%
-    {3, 0, 10.3181, 0.0000, 3.52999, 0.17236},  // median |error| 1.8%
-    {3, 1, 10.8188, 0.0000, 7.06593, 0.41509},  // median |error| 1.9%
-    {3, 2, 6.8961, 0.0000, 1.77992, 0.09137},  // median |error| 1.7%
-    {3, 3, 4.5854, 0.0000, 0.90573, 0.01793},  // median |error| 2.1%
-    {3, 4, 4.6269, 0.0000, 1.79682, 0.12476},  // median |error| 1.6%
-    {3, 5, 4.2478, 0.0000, 0.92062, 0.07395},  // median |error| 1.6%
-    {3, 6, 3.2849, 0.0000, 0.49831, 0.00000},  // median |error| 3.6%
-    {3, 7, 3.3147, 0.0000, 1.04061, 0.06866},  // median |error| 3.3%
-    {3, 8, 7.7674, 0.0000, 7.03042, 0.28652},  // median |error| 0.9%
-    {3, 9, 5.2823, 0.0000, 3.50331, 0.17726},  // median |error| 1.0%
-    {3, 10, 3.2807, 0.0000, 0.52370, 0.00000},  // median |error| 4.2%
-    {3, 11, 7.2382, 0.0000, 2.02838, 0.08967},  // median |error| 2.2%
-    {3, 12, 7.7546, 0.0000, 4.01655, 0.24488},  // median |error| 2.7%
-    {3, 18, 3.5314, 0.0000, 0.92927, 0.04049},  // median |error| 2.6%
-    {5, 13, 2.8599, 0.9738, 0.15517, 0.00000},  // median |error| 6.7%
-    {5, 14, 3.0424, 0.5866, 0.04514, 0.02661},  // median |error| 8.9%
-    {5, 15, 2.8875, 0.5793, 0.09382, 0.00000},  // median |error| 9.3%
-    {5, 16, 1.6649, 1.9458, 0.15595, 0.01424},  // median |error| 4.7%
-    {5, 17, 3.3774, 0.1541, 0.09836, 0.00000},  // median |error| 9.1%
-    {5, 19, 3.4063, 0.0176, 0.05785, 0.01927},  // median |error| 9.6%
+    {1, 0, 9.2203, 0.0000, 4.03797, 0.38738},  // median |error| 1.7%
+    {1, 1, 9.9725, 0.0000, 7.74228, 0.53882},  // median |error| 1.1%
+    {1, 2, 5.5399, 0.0000, 2.25173, 0.00000},  // median |error| 3.9%
+    {1, 3, 3.7399, 0.0000, 1.25406, 0.00000},  // median |error| 8.4%
+    {1, 4, 3.8334, 0.0000, 2.27332, 0.00000},  // median |error| 4.1%
+    {1, 5, 3.3143, 0.0000, 1.24246, 0.00000},  // median |error| 11.0%
+    {1, 6, 3.0096, 0.0000, 0.67738, 0.00000},  // median |error| 18.2%
+    {1, 7, 2.9674, 0.0000, 1.23808, 0.00000},  // median |error| 11.7%
+    {1, 8, 6.6011, 0.0000, 7.62774, 0.41470},  // median |error| 1.6%
+    {1, 9, 4.2615, 0.0000, 4.12814, 0.00000},  // median |error| 3.0%
+    {1, 10, 3.0595, 0.0000, 0.71059, 0.00000},  // median |error| 22.1%
+    {1, 11, 6.3532, 0.0000, 2.45476, 0.30036},  // median |error| 2.9%
+    {1, 12, 6.7550, 0.0000, 4.56379, 0.42918},  // median |error| 2.0%
+    {1, 13, 4.6025, 0.0000, 0.19635, 0.00000},  // median |error| 32.1%
+    {1, 18, 2.8593, 0.0000, 1.23321, 0.00000},  // median |error| 10.0%
+    {2, 0, 10.3511, 0.0000, 3.44659, 0.12944},  // median |error| 0.9%
+    {2, 1, 10.6552, 0.0000, 6.90450, 0.24646},  // median |error| 0.9%
+    {2, 2, 6.4776, 0.0000, 1.74350, 0.06060},  // median |error| 1.1%
+    {2, 3, 4.4068, 0.0000, 0.88567, 0.07653},  // median |error| 2.1%
+    {2, 4, 4.6366, 0.0000, 1.74895, 0.06769},  // median |error| 1.4%
+    {2, 5, 4.0199, 0.0000, 0.92256, 0.01512},  // median |error| 1.8%
+    {2, 6, 3.1554, 0.0000, 0.51243, 0.00000},  // median |error| 3.5%
+    {2, 7, 3.2257, 0.0000, 1.05191, 0.00000},  // median |error| 3.4%
+    {2, 8, 7.2823, 0.0000, 7.01500, 0.29217},  // median |error| 0.6%
+    {2, 9, 5.2487, 0.0000, 3.45814, 0.15810},  // median |error| 0.6%
+    {2, 10, 3.1308, 0.0000, 0.55388, 0.00000},  // median |error| 3.6%
+    {2, 11, 7.2206, 0.0000, 1.97200, 0.06581},  // median |error| 0.6%
+    {2, 12, 7.7532, 0.0000, 3.89479, 0.15445},  // median |error| 0.7%
+    {2, 13, 4.4856, 0.0000, 0.17813, 0.00000},  // median |error| 24.4%
+    {2, 18, 3.3221, 0.0000, 0.94747, 0.02045},  // median |error| 2.2%
+    {3, 0, 10.4295, 0.0000, 3.50890, 0.17744},  // median |error| 1.7%
+    {3, 1, 10.9631, 0.0000, 7.01996, 0.42503},  // median |error| 1.9%
+    {3, 2, 6.9414, 0.0000, 1.77249, 0.08127},  // median |error| 1.5%
+    {3, 3, 4.5584, 0.0000, 0.90894, 0.02226},  // median |error| 2.1%
+    {3, 4, 4.6774, 0.0000, 1.78215, 0.12054},  // median |error| 1.5%
+    {3, 5, 4.2530, 0.0000, 0.92014, 0.06539},  // median |error| 1.6%
+    {3, 6, 3.2373, 0.0000, 0.50890, 0.00000},  // median |error| 2.7%
+    {3, 7, 3.3037, 0.0000, 1.04689, 0.06374},  // median |error| 2.8%
+    {3, 8, 7.7447, 0.0000, 7.03791, 0.27933},  // median |error| 0.7%
+    {3, 9, 5.3256, 0.0000, 3.48853, 0.18562},  // median |error| 1.0%
+    {3, 10, 3.1964, 0.0000, 0.54370, 0.00000},  // median |error| 4.1%
+    {3, 11, 7.3337, 0.0000, 2.01058, 0.09299},  // median |error| 2.2%
+    {3, 12, 7.8934, 0.0000, 3.97296, 0.25066},  // median |error| 2.6%
+    {3, 18, 3.4710, 0.0000, 0.94438, 0.03880},  // median |error| 1.6%
+    {5, 13, 2.9086, 0.9064, 0.16087, 0.00000},  // median |error| 6.2%
+    {5, 14, 3.0387, 0.5361, 0.05066, 0.02478},  // median |error| 10.6%
+    {5, 15, 2.9305, 0.5093, 0.10016, 0.00000},  // median |error| 11.5%
+    {5, 16, 1.7820, 1.7977, 0.16374, 0.01693},  // median |error| 6.8%
+    {5, 17, 3.4118, 0.1003, 0.10470, 0.00000},  // median |error| 10.8%
+    {5, 19, 3.3759, 0.0000, 0.05938, 0.02055},  // median |error| 11.5%
 };
 constexpr int kModelRows = (int)(sizeof(kModel) / sizeof(kModel[0]));
 constexpr int kVariantKS = 5;
@@ -202,15 +202,15 @@ static inline int select_for_variant(int64_t M, int64_t N, int64_t K, int varian
 // Split-K: the number of K chunks (1 = do not split) with the least modelled time among
 // the counts the split study measured.  A split launch costs the GEMM of its chunks, all in
 // one grid (the model above, with the workgroups multiplied by the chunks), plus
-//     3.2615 us (the reduction's launch)
-//   + 0.13525 us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
+//     3.2197 us (the reduction's launch)
+//   + 0.13783 us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
 //     written once and read once by the reduction, and C)
-//   + 0.4102 us per round of workgroups of the split grid (each workgroup's
+//   + 0.2955 us per round of workgroups of the split grid (each workgroup's
 //     first copy and partial-tile store, which short chunks no longer hide),
 // the constants fitted (>= 0, least squares) to the 41 shapes of the split study below.
-constexpr double kSplitFixedUs = 3.2615;
-constexpr double kSplitUsPerMB = 0.13525;
-constexpr double kSplitUsPerRound = 0.4102;
+constexpr double kSplitFixedUs = 3.2197;
+constexpr double kSplitUsPerMB = 0.13783;
+constexpr double kSplitUsPerRound = 0.2955;
 constexpr int kSplitChoices[] = {1, 2, 4, 8, 16};
 
 // The split study: trailing comments hold the measured microseconds of each count.

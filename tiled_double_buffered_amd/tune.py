@@ -15,6 +15,12 @@ shapes outside the table, fit the cost model that picks for every other shape.
 
     python -m tiled_double_buffered_amd.tune --holdout 40   # dispatcher regret on 40 seeded
                                                             # shapes outside the table
+    python -m tiled_double_buffered_amd.tune --holdout-decode 16   # ... on decode products
+
+After shapes are added to the table or the training set, --fill measures only the ones an
+earlier --out file lacks and writes the merged file (the split study is kept as it was):
+
+    python -m tiled_double_buffered_amd.tune --fill full.json --out full2.json   # GPU
 
 The split-count study times the unsplit product through gemm_f32, that is through the
 dispatch table the library was built with.  After a change of the configurations, measure
@@ -571,16 +577,40 @@ def holdout_shapes(n, seed=2024, lo=5.0, hi=13.0, max_flop=2.0 * 4096 ** 3, excl
     return out
 
 
+def decode_shapes(n, seed, exclude=()):
+    """n seeded decode products: M uniform in 1..16, N log-uniform in [2**11, 2**15], K
+    log-uniform in [2**10, 2**14]; none of them a row of the table or in `exclude`."""
+    import random
+
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        m = rng.randint(1, 16)
+        n_ = int(round(2.0 ** rng.uniform(11, 15)))
+        k = int(round(2.0 ** rng.uniform(10, 14)))
+        s = (m, n_, k)
+        if s not in SHAPES and s not in exclude and s not in out:
+            out.append(s)
+    return out
+
+
 def train_shapes():
-    """The seeded shapes outside the table that the cost model is also fitted to."""
-    return holdout_shapes(TRAIN_COUNT, TRAIN_SEED)
+    """The seeded shapes outside the table that the cost model is also fitted to: general
+    shapes, and decode products (1-16 rows)."""
+    return (holdout_shapes(TRAIN_COUNT, TRAIN_SEED)
+            + decode_shapes(DECODE_TRAIN_COUNT, DECODE_TRAIN_SEED))
 
 
-def holdout_study(n=40, seed=2024, rounds=2, batches=5, batch_ms=20.0, log=print):
+def holdout_study(n=40, seed=2024, rounds=2, batches=5, batch_ms=20.0, log=print,
+                  decode=False):
     """How far the dispatcher's pick is from the best measured (variant, configuration) on
     shapes it was not tuned on: per shape, the time of the dispatched pair over the time of
-    the fastest pair (1.0 = the dispatcher found the best)."""
-    shapes = holdout_shapes(n, seed, exclude=set(train_shapes()))
+    the fastest pair (1.0 = the dispatcher found the best).  decode: seeded decode products
+    (decode_shapes) instead of general ones."""
+    if decode:
+        shapes = decode_shapes(n, seed, exclude=set(train_shapes()))
+    else:
+        shapes = holdout_shapes(n, seed, exclude=set(train_shapes()))
     results = measure(shapes, rounds, batches, batch_ms, log=log)
     out = []
     for r in results:
@@ -598,13 +628,16 @@ def holdout_study(n=40, seed=2024, rounds=2, batches=5, batch_ms=20.0, log=print
     summary = {"shapes": len(out), "median": statistics.median(regrets),
                "p90": regrets[int(0.9 * (len(regrets) - 1))], "max": regrets[-1],
                "within_5pct": sum(1 for x in regrets if x <= 1.05) / len(regrets)}
-    log("dispatcher regret on held-out shapes: " + json.dumps(summary))
+    log(("dispatcher regret on held-out decode shapes: " if decode else
+         "dispatcher regret on held-out shapes: ") + json.dumps(summary))
     return {"summary": summary, "rows": out}
 
 
 # Shapes measured only to fit the cost model (never table rows).
 TRAIN_SEED = 1
 TRAIN_COUNT = 48
+DECODE_TRAIN_SEED = 3
+DECODE_TRAIN_COUNT = 16
 
 
 def model_features(M, N, K, cfg_dims, wg_factor=1, cus=256):
@@ -621,7 +654,7 @@ def model_rounds(M, N, cfg_dims, wg_factor=1, cus=256):
 
 def model_work(M, N, K, cfg_dims, wg_factor=1, cus=256):
     """workgroups * k_tiles / 256: the launch's tile work spread over every compute unit."""
-    bm, bn, bk = cfg_dims
+    bm, bn, bk = cfg_dims[:3]
     return -(-M // bm) * -(-N // bn) * wg_factor * -(-K // bk) / cus
 
 
@@ -922,6 +955,11 @@ def main(argv=None) -> int:
                     help="time every pair on N seeded shapes outside the table and report "
                          "how far the dispatcher's pick is from the fastest")
     ap.add_argument("--holdout-seed", type=int, default=2024)
+    ap.add_argument("--holdout-decode", type=int, default=0, metavar="N",
+                    help="as --holdout, on N seeded decode products (1-16 rows)")
+    ap.add_argument("--fill", default=None, metavar="BASE_JSON",
+                    help="measure the table and training shapes that an earlier --out file "
+                         "lacks; write the merged file to --out")
     ap.add_argument("--holdout-splitk", type=int, default=0, metavar="N",
                     help="time every split count on N seeded skinny shapes and report how "
                          "far gemm_f32_splitk_select is from the fastest")
@@ -935,7 +973,8 @@ def main(argv=None) -> int:
                     help="an earlier --out file whose split study the nearest-row rule of "
                          "--holdout-splitk is measured against")
     args = ap.parse_args(argv)
-    if args.barrier_study or args.raster_study or args.holdout or args.holdout_splitk:
+    if (args.barrier_study or args.raster_study or args.holdout or args.holdout_splitk
+            or args.holdout_decode):
         import torch
 
         props = torch.cuda.get_device_properties(0)
@@ -954,6 +993,11 @@ def main(argv=None) -> int:
             res["holdout"] = holdout_study(args.holdout, args.holdout_seed, args.rounds,
                                            args.batches, args.batch_ms,
                                            log=lambda *a: print(*a, flush=True))
+        if args.holdout_decode:
+            res["holdout_decode"] = holdout_study(args.holdout_decode, args.holdout_seed,
+                                                  args.rounds, args.batches, args.batch_ms,
+                                                  log=lambda *a: print(*a, flush=True),
+                                                  decode=True)
         if args.holdout_splitk:
             prior = None
             if args.split_json:
@@ -979,6 +1023,24 @@ def main(argv=None) -> int:
     props = torch.cuda.get_device_properties(0)
     device = f"{props.name} ({getattr(props, 'gcnArchName', '?')})"
     t0 = time.time()
+    if args.fill:
+        with open(args.fill) as f:
+            data = json.load(f)
+        have = {(r["M"], r["N"], r["K"]) for r in data["results"] + (data.get("train") or [])}
+        log = lambda *a: print(*a, flush=True)  # noqa: E731
+        data["results"] = data["results"] + measure(
+            [s for s in SHAPES if s not in have], args.rounds, args.batches, args.batch_ms,
+            log=log)
+        train_set = set(train_shapes())
+        data["train"] = [r for r in (data.get("train") or [])
+                         if (r["M"], r["N"], r["K"]) in train_set] + measure(
+            [s for s in train_shapes() if s not in have], args.rounds, args.batches,
+            args.batch_ms, log=log)
+        data["library"] = tdb.gemm_f32_version()
+        if args.out:
+            with open(args.out, "w") as f:
+                json.dump(data, f, indent=1)
+        return 0
     if args.split_only:
         with open(args.split_only) as f:
             base = json.load(f)
