@@ -1028,9 +1028,9 @@ def main(argv=None) -> int:
             data = json.load(f)
         have = {(r["M"], r["N"], r["K"]) for r in data["results"] + (data.get("train") or [])}
         log = lambda *a: print(*a, flush=True)  # noqa: E731
-        data["results"] = data["results"] + measure(
-            [s for s in SHAPES if s not in have], args.rounds, args.batches, args.batch_ms,
-            log=log)
+        data["results"] = [r for r in data["results"] if (r["M"], r["N"], r["K"]) in SHAPES] + \
+            measure([s for s in SHAPES if s not in have], args.rounds, args.batches,
+                    args.batch_ms, log=log)
         train_set = set(train_shapes())
         data["train"] = [r for r in (data.get("train") or [])
                          if (r["M"], r["N"], r["K"]) in train_set] + measure(
