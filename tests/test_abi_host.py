@@ -647,3 +647,51 @@ def test_noalloc_split_validation_before_launch():
     assert f(big, big, big, PA, big, PB, big, PC, big, 8) == tdb.ERR_SCRATCH_LIMIT
     text = open(HEADER).read()
     assert re.search(r"#define GEMMF32_SCRATCH_FLOATS \(8 \* 1024 \* 1024\)", text)
+
+
+def test_seeded_shape_sets_are_disjoint_and_in_range():
+    """The tuner's seeded shape sets: reproducible, inside their stated ranges, none of them
+    a table row, and the held-out sets disjoint from the shapes the model is fitted to."""
+    from tiled_double_buffered_amd import tune
+    train = tune.train_shapes()
+    assert train == tune.train_shapes()
+    assert len(train) == len(set(train)) == tune.TRAIN_COUNT + tune.DECODE_TRAIN_COUNT
+    assert not set(train) & set(tune.SHAPES)
+    dec = tune.decode_shapes(16, 2027, exclude=set(train))
+    assert len(set(dec)) == 16 and not set(dec) & set(train) and not set(dec) & set(tune.SHAPES)
+    for (m, n, k) in dec + tune.decode_shapes(tune.DECODE_TRAIN_COUNT, tune.DECODE_TRAIN_SEED):
+        assert 1 <= m <= 16 and 2 ** 11 - 1 <= n <= 2 ** 15 + 1 and 2 ** 10 - 1 <= k <= 2 ** 14 + 1
+    held = tune.holdout_shapes(40, 2024, exclude=set(train))
+    assert not set(held) & set(train) and not set(held) & set(tune.SHAPES)
+
+
+def test_fill_measures_only_missing_shapes(tmp_path, monkeypatch):
+    """--fill measures the table and training shapes an earlier file lacks, keeps the rows it
+    has (dropping those no longer in the table or the training set) and the split study."""
+    import json
+    from tiled_double_buffered_amd import tune
+    asked = []
+
+    def fake_measure(shapes, *a, **k):
+        asked.append(list(shapes))
+        return [{"M": m, "N": n, "K": kk, "us": {"db0": 1.0}} for (m, n, kk) in shapes]
+
+    monkeypatch.setattr(tune, "measure", fake_measure)
+    keep_t, keep_r = tune.train_shapes()[0], tune.SHAPES[0]
+    base = {"device": "x", "rounds": 2, "batches": 5, "batch_ms": 20.0,
+            "results": [{"M": keep_r[0], "N": keep_r[1], "K": keep_r[2], "us": {"db0": 2.0}},
+                        {"M": 3, "N": 5, "K": 7, "us": {"db0": 2.0}}],
+            "train": [{"M": keep_t[0], "N": keep_t[1], "K": keep_t[2], "us": {"db0": 2.0}},
+                      {"M": 11, "N": 13, "K": 17, "us": {"db0": 2.0}}],
+            "splits": [{"M": 1, "N": 2, "K": 3, "us": {"1": 1.0}}]}
+    src, out = tmp_path / "base.json", tmp_path / "full.json"
+    src.write_text(json.dumps(base))
+    assert tune.main(["--fill", str(src), "--out", str(out)]) == 0
+    got = json.loads(out.read_text())
+    assert asked[0] == [s for s in tune.SHAPES if s != keep_r]
+    assert asked[1] == [s for s in tune.train_shapes() if s != keep_t]
+    res = {(r["M"], r["N"], r["K"]): r["us"]["db0"] for r in got["results"]}
+    tr = {(r["M"], r["N"], r["K"]): r["us"]["db0"] for r in got["train"]}
+    assert set(res) == set(tune.SHAPES) and res[keep_r] == 2.0 and (3, 5, 7) not in res
+    assert set(tr) == set(tune.train_shapes()) and tr[keep_t] == 2.0 and (11, 13, 17) not in tr
+    assert got["splits"] == base["splits"]

@@ -1018,11 +1018,6 @@ def main(argv=None) -> int:
                            data["batch_ms"], split_results=data.get("splits"),
                            train=data.get("train")))
         return 0
-    import torch
-
-    props = torch.cuda.get_device_properties(0)
-    device = f"{props.name} ({getattr(props, 'gcnArchName', '?')})"
-    t0 = time.time()
     if args.fill:
         with open(args.fill) as f:
             data = json.load(f)
@@ -1041,6 +1036,11 @@ def main(argv=None) -> int:
             with open(args.out, "w") as f:
                 json.dump(data, f, indent=1)
         return 0
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    device = f"{props.name} ({getattr(props, 'gcnArchName', '?')})"
+    t0 = time.time()
     if args.split_only:
         with open(args.split_only) as f:
             base = json.load(f)
