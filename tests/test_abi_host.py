@@ -280,11 +280,14 @@ def _model_t(row, M, N, K, dims, wg=1):
 def _model_pick(M, N, K, rows, dims, variant=0):
     """The cost-model rule, read independently of the C++: least a + b * rounds + g *
     rounds * k_tiles + h * work, rounds = ceil(tiles / 256), work = tiles * k_tiles / 256,
-    first row on ties."""
+    first row on ties; for the automatic pick, no multi-stage row where K is not a multiple
+    of its BK (that kernel then runs the double-buffered loop)."""
     best = None
     for row in rows:
         v, c = row[0], row[1]
         if variant and v != variant:
+            continue
+        if not variant and v == tdb.VARIANT_MS and K % dims[c][2] != 0:
             continue
         t = _model_t(row, M, N, K, dims)[0]
         if best is None or t < best[0]:
@@ -535,8 +538,8 @@ def test_split_model_agrees_with_the_split_study():
     times of every count, tail splits as negative counts), the modelled count's time over
     the fastest count's: median at most 1.02, at least 80% of the shapes within 5%, none
     beyond 1.25.  The misses are small and mid-sized products where the model of the
-    unsplit kernel is 10-20% off; the worst, 39 x 432 x 6224, splits 16 ways at 1.18x the
-    unsplit time."""
+    unsplit kernel is 10-20% off; the worst, 178 x 931 x 4676, splits 16 ways at 1.17x the
+    time of 4 chunks."""
     text = _header_text()
     body = text[text.index("kSplitK[] = {"):]
     body = body[:body.index("};")]

@@ -75,6 +75,7 @@ SHAPES = [
     (1023, 1023, 1023), (4095, 4095, 4095),
     # skinny shapes (a small batch of rows against a wide layer)
     (16, 4096, 4096), (32, 4096, 4096), (128, 4096, 4096), (32, 8192, 8192),
+    (128, 11008, 4096), (128, 4096, 11008),
     # decode rows (1 to 16) against 4096- to 32000-wide layers, and a small one
     (1, 4096, 4096), (8, 4096, 4096), (16, 11008, 4096), (16, 4096, 11008),
     (16, 8192, 8192), (4, 1024, 1024), (16, 32000, 4096),
@@ -156,6 +157,7 @@ static const ModelRow kModel[] = {{
 {model_rows}
 }};
 constexpr int kModelRows = (int)(sizeof(kModel) / sizeof(kModel[0]));
+constexpr int kVariantMS = 3;
 constexpr int kVariantKS = 5;
 constexpr int64_t kModelCUs = 256;
 
@@ -179,6 +181,10 @@ static inline const ModelRow& model_pick(int64_t M, int64_t N, int64_t K, int va
   bool found = false;
   for (int i = 0; i < kModelRows; ++i) {{
     if (variant != 0 && kModel[i].variant != variant) continue;
+    // with a K tail the multi-stage kernel runs the double-buffered loop in its larger LDS
+    // allocation, never ahead of the double-buffered kernel: not a candidate then
+    if (variant == 0 && kModel[i].variant == kVariantMS && K % kConfigs[kModel[i].cfg].bk != 0)
+      continue;
     // a split-K launch takes neither the K-split kernel (it divides K itself) nor a
     // one-wave configuration (its plain kernels keep one SIMD of a CU busy)
     if (wg_factor != 1 &&
@@ -710,11 +716,14 @@ def _one_wave(cfg):
 
 def _model_pick_py(M, N, K, model, dims, wg_factor=1):
     """Least modelled (us, variant, cfg) over the fitted rows, as the header computes it
-    (a split launch never takes the K-split kernel)."""
+    (a split launch never takes the K-split kernel; with a K tail the multi-stage kernel
+    runs the double-buffered loop in a larger LDS allocation and is no candidate)."""
     best = None
     for row in model:
         v, c = row[0], row[1]
         if wg_factor != 1 and (v == tdb.VARIANT_KS or _one_wave(c)):
+            continue
+        if v == tdb.VARIANT_MS and K % dims[c][2] != 0:
             continue
         t = model_time(row, M, N, K, dims[c][:3], wg_factor)
         if best is None or t < best[0]:
