@@ -698,3 +698,27 @@ def test_fill_measures_only_missing_shapes(tmp_path, monkeypatch):
     assert set(res) == set(tune.SHAPES) and res[keep_r] == 2.0 and (3, 5, 7) not in res
     assert set(tr) == set(tune.train_shapes()) and tr[keep_t] == 2.0 and (11, 13, 17) not in tr
     assert got["splits"] == base["splits"]
+
+
+def test_no_multistage_pick_on_a_k_tail():
+    """Off the table, the automatic pick never sends a K that is not a multiple of BK to the
+    multi-stage kernel (it would run the double-buffered loop in a larger LDS allocation);
+    an explicit multi-stage request still gets a multi-stage configuration."""
+    import random
+    table = {(m, n, k) for (m, n, k, *_rest) in _dispatch_rows()}
+    rng = random.Random(31)
+    seen_tail = 0
+    for _ in range(400):
+        M, N, K = (int(2 ** rng.uniform(5, 13)) for _ in range(3))
+        if (M, N, K) in table:
+            continue
+        rc, v, c = tdb.gemm_f32_select(M, N, K)
+        assert rc == tdb.OK
+        bk = tdb.gemm_f32_config_info(c)[1]["BK"]
+        if v == tdb.VARIANT_MS:
+            assert K % bk == 0, (M, N, K, c)
+        if K % 16:
+            seen_tail += 1
+            c_ms = tdb.gemm_f32_select_cfg(M, N, K, tdb.VARIANT_MS)
+            assert tdb.gemm_f32_config_variants(c_ms) & (1 << tdb.VARIANT_MS)
+    assert seen_tail > 100
