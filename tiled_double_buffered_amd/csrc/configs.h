@@ -30,7 +30,7 @@ template <> struct CfgById<15> { using type = Ks16Cfg<8, 2, false, 2>; };      /
 template <> struct CfgById<16> { using type = Ks16Cfg<8, 2, false, 4>; };      // 16 x 64 tile, 8 waves over K: wide layers
 template <> struct CfgById<17> { using type = Ks16Cfg<4, 2, false, 2>; };      // 16 x 32 tile, 4 waves over K: several workgroups per CU
 template <> struct CfgById<18> { using type = TileCfg<64, 128, 32, 2, 4>; };   // 8 waves of 32x32, two per SIMD: one round of tiles at a few hundred rows
-template <> struct CfgById<19> { using type = Ks16Cfg<4, 2, true>; };         // 16 x 16 tile, 4 waves taking alternate K groups: the workgroup reads B in one front (1-8 rows)
+template <> struct CfgById<19> { using type = Ks16Cfg<4, 2, true>; };         // 16 x 16 tile, 4 waves taking alternate K groups: the workgroup reads B in one front (few rows, 4096-wide layers)
 constexpr int kNumConfigs = 20;
 
 typedef void (*KernelFn)(int, int, int, const float*, int64_t, const float*, int64_t, float*,
