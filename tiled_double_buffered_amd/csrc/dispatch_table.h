@@ -63,6 +63,11 @@ static const DispatchRow kDispatch[] = {
     {4, 1024, 1024, 5, 19, 7, 6, 6},  // sb 23.36 us, db 19.66 us, ms 19.20 us, ks 4.39 us
     {16, 32000, 4096, 3, 10, 13, 13, 10},  // sb 154.81 us, db 108.84 us, ms 92.27 us, ks 96.62 us
     {1024, 8192, 8192, 2, 2, 7, 2, 18},  // sb 998.21 us, db 906.38 us, ms 912.22 us, ks 1173.89 us
+    {1, 11008, 4096, 5, 14, 7, 13, 6},  // sb 99.87 us, db 70.62 us, ms 67.90 us, ks 30.24 us
+    {1, 4096, 11008, 5, 19, 7, 6, 6},  // sb 255.99 us, db 183.83 us, ms 176.11 us, ks 27.65 us
+    {1, 8192, 8192, 5, 17, 7, 13, 6},  // sb 192.57 us, db 138.39 us, ms 132.17 us, ks 39.47 us
+    {1, 32000, 4096, 3, 10, 13, 13, 10},  // sb 154.25 us, db 107.58 us, ms 92.96 us, ks 94.13 us
+    {4, 4096, 4096, 5, 19, 7, 6, 6},  // sb 97.02 us, db 70.26 us, ms 67.45 us, ks 12.74 us
 };
 constexpr int kDispatchRows = (int)(sizeof(kDispatch) / sizeof(kDispatch[0]));
 
@@ -86,64 +91,64 @@ static inline const DispatchRow* dispatch_exact(int64_t M, int64_t N, int64_t K)
 // product that streams B, where a partly filled round of workgroups is not cheaper per
 // byte), and b a cost per round that only the K-split kernels have (each of their rounds
 // ends in a hand-off through LDS; b = 0 elsewhere).  They were fitted per pair by least
-// squares on relative error, all kept >= 0, to the 102 shapes measured for this file
-// (the table's 38 and 64 seeded shapes outside it).
+// squares on relative error, all kept >= 0, to the 107 shapes measured for this file
+// (the table's 43 and 64 seeded shapes outside it).
 struct ModelRow {
   int variant, cfg;
   double a_us, b_us, g_us, h_us;
 };
 
 static const ModelRow kModel[] = {
-    {1, 0, 9.2182, 0.0000, 4.03652, 0.39016},  // median |error| 1.7%
-    {1, 1, 9.9666, 0.0000, 7.74019, 0.53620},  // median |error| 1.2%
-    {1, 2, 5.5380, 0.0000, 2.25227, 0.00000},  // median |error| 3.9%
-    {1, 3, 3.7170, 0.0000, 1.25553, 0.00000},  // median |error| 7.7%
-    {1, 4, 3.8271, 0.0000, 2.27347, 0.00000},  // median |error| 4.0%
-    {1, 5, 3.2758, 0.0000, 1.24341, 0.00000},  // median |error| 11.0%
-    {1, 6, 3.0023, 0.0000, 0.66875, 0.00000},  // median |error| 19.4%
-    {1, 7, 2.9541, 0.0000, 1.22981, 0.00000},  // median |error| 12.1%
-    {1, 8, 6.5883, 0.0000, 7.62941, 0.39309},  // median |error| 1.6%
-    {1, 9, 4.2804, 0.0000, 4.11953, 0.00000},  // median |error| 3.0%
-    {1, 10, 3.0601, 0.0000, 0.69752, 0.00000},  // median |error| 23.6%
-    {1, 11, 6.3484, 0.0000, 2.45523, 0.29696},  // median |error| 2.7%
-    {1, 12, 6.7525, 0.0000, 4.56221, 0.42643},  // median |error| 1.7%
-    {1, 13, 4.5252, 0.0000, 0.19331, 0.00000},  // median |error| 33.5%
-    {1, 18, 2.8751, 0.0000, 1.22934, 0.00000},  // median |error| 9.5%
-    {2, 0, 10.3337, 0.0000, 3.44825, 0.11746},  // median |error| 0.8%
-    {2, 1, 10.6347, 0.0000, 6.90741, 0.22207},  // median |error| 0.8%
-    {2, 2, 6.4685, 0.0000, 1.74567, 0.05306},  // median |error| 1.1%
-    {2, 3, 4.3925, 0.0000, 0.88450, 0.07659},  // median |error| 2.2%
-    {2, 4, 4.6286, 0.0000, 1.74935, 0.06198},  // median |error| 1.4%
-    {2, 5, 3.9914, 0.0000, 0.92475, 0.00450},  // median |error| 2.0%
-    {2, 6, 3.1261, 0.0000, 0.50706, 0.00000},  // median |error| 3.7%
-    {2, 7, 3.1552, 0.0000, 1.04749, 0.00000},  // median |error| 3.6%
-    {2, 8, 7.2641, 0.0000, 7.01864, 0.25711},  // median |error| 0.5%
-    {2, 9, 5.2391, 0.0000, 3.45821, 0.14386},  // median |error| 0.5%
-    {2, 10, 3.1500, 0.0000, 0.54515, 0.00000},  // median |error| 4.4%
-    {2, 11, 7.2074, 0.0000, 1.97299, 0.05915},  // median |error| 0.5%
-    {2, 12, 7.7475, 0.0000, 3.89610, 0.13634},  // median |error| 0.5%
-    {2, 13, 4.4453, 0.0000, 0.17321, 0.00000},  // median |error| 25.9%
-    {2, 18, 3.3091, 0.0000, 0.94994, 0.00051},  // median |error| 2.5%
-    {3, 0, 10.3930, 0.0000, 3.51358, 0.16128},  // median |error| 1.8%
-    {3, 1, 10.9200, 0.0000, 7.03073, 0.39664},  // median |error| 1.8%
-    {3, 2, 6.9253, 0.0000, 1.77621, 0.07359},  // median |error| 1.4%
-    {3, 3, 4.5405, 0.0000, 0.90909, 0.01929},  // median |error| 2.2%
-    {3, 4, 4.6563, 0.0000, 1.78568, 0.11369},  // median |error| 1.4%
-    {3, 5, 4.2215, 0.0000, 0.92092, 0.06178},  // median |error| 1.5%
-    {3, 6, 3.1932, 0.0000, 0.49889, 0.00000},  // median |error| 4.1%
-    {3, 7, 3.2123, 0.0000, 1.04128, 0.05813},  // median |error| 3.3%
-    {3, 8, 7.7252, 0.0000, 7.04248, 0.24502},  // median |error| 0.6%
-    {3, 9, 5.3094, 0.0000, 3.49069, 0.16851},  // median |error| 0.9%
-    {3, 10, 3.1721, 0.0000, 0.52937, 0.00000},  // median |error| 6.1%
-    {3, 11, 7.3076, 0.0000, 2.01397, 0.08513},  // median |error| 2.3%
-    {3, 12, 7.8646, 0.0000, 3.98035, 0.23555},  // median |error| 2.6%
-    {3, 18, 3.4749, 0.0000, 0.94406, 0.02592},  // median |error| 2.0%
-    {5, 13, 2.8579, 0.9226, 0.15752, 0.00000},  // median |error| 7.1%
-    {5, 14, 2.9383, 0.5421, 0.05174, 0.02371},  // median |error| 10.4%
-    {5, 15, 2.8713, 0.5185, 0.09966, 0.00000},  // median |error| 11.0%
-    {5, 16, 1.6200, 1.8373, 0.16638, 0.01260},  // median |error| 6.6%
-    {5, 17, 3.3595, 0.1017, 0.10431, 0.00000},  // median |error| 10.6%
-    {5, 19, 3.3101, 0.0000, 0.06026, 0.01973},  // median |error| 11.4%
+    {1, 0, 9.2158, 0.0000, 4.03658, 0.39670},  // median |error| 1.7%
+    {1, 1, 9.9696, 0.0000, 7.73859, 0.54805},  // median |error| 1.1%
+    {1, 2, 5.5172, 0.0000, 2.25607, 0.00000},  // median |error| 3.8%
+    {1, 3, 3.6759, 0.0000, 1.26270, 0.00000},  // median |error| 7.2%
+    {1, 4, 3.8023, 0.0000, 2.28078, 0.00000},  // median |error| 3.7%
+    {1, 5, 3.2466, 0.0000, 1.25129, 0.00000},  // median |error| 10.8%
+    {1, 6, 2.9643, 0.0000, 0.67840, 0.00000},  // median |error| 19.4%
+    {1, 7, 2.9295, 0.0000, 1.24135, 0.00000},  // median |error| 13.1%
+    {1, 8, 6.5773, 0.0000, 7.63221, 0.40494},  // median |error| 1.5%
+    {1, 9, 4.2517, 0.0000, 4.12865, 0.00000},  // median |error| 3.1%
+    {1, 10, 3.0176, 0.0000, 0.70893, 0.00000},  // median |error| 24.6%
+    {1, 11, 6.3457, 0.0000, 2.45524, 0.30305},  // median |error| 2.5%
+    {1, 12, 6.7563, 0.0000, 4.56054, 0.43298},  // median |error| 1.6%
+    {1, 13, 4.5144, 0.0000, 0.19718, 0.00000},  // median |error| 35.3%
+    {1, 18, 2.8351, 0.0000, 1.24059, 0.00000},  // median |error| 10.5%
+    {2, 0, 10.3266, 0.0000, 3.44961, 0.11529},  // median |error| 0.7%
+    {2, 1, 10.6272, 0.0000, 6.90987, 0.21794},  // median |error| 0.7%
+    {2, 2, 6.4632, 0.0000, 1.74671, 0.05148},  // median |error| 1.0%
+    {2, 3, 4.3894, 0.0000, 0.88486, 0.07767},  // median |error| 2.1%
+    {2, 4, 4.6245, 0.0000, 1.75071, 0.05992},  // median |error| 1.2%
+    {2, 5, 3.9870, 0.0000, 0.92607, 0.00296},  // median |error| 1.9%
+    {2, 6, 3.1224, 0.0000, 0.50790, 0.00000},  // median |error| 3.7%
+    {2, 7, 3.1530, 0.0000, 1.04853, 0.00000},  // median |error| 3.5%
+    {2, 8, 7.2576, 0.0000, 7.02091, 0.25303},  // median |error| 0.5%
+    {2, 9, 5.2373, 0.0000, 3.45889, 0.14232},  // median |error| 0.5%
+    {2, 10, 3.1369, 0.0000, 0.54827, 0.00000},  // median |error| 4.2%
+    {2, 11, 7.2089, 0.0000, 1.97277, 0.05849},  // median |error| 0.5%
+    {2, 12, 7.7493, 0.0000, 3.89577, 0.13389},  // median |error| 0.5%
+    {2, 13, 4.4367, 0.0000, 0.17631, 0.00000},  // median |error| 27.0%
+    {2, 18, 3.3110, 0.0000, 0.94837, 0.00789},  // median |error| 2.3%
+    {3, 0, 10.3561, 0.0000, 3.52032, 0.15600},  // median |error| 1.8%
+    {3, 1, 10.8666, 0.0000, 7.04727, 0.38331},  // median |error| 2.0%
+    {3, 2, 6.9024, 0.0000, 1.78025, 0.07063},  // median |error| 1.6%
+    {3, 3, 4.5288, 0.0000, 0.91101, 0.01843},  // median |error| 2.3%
+    {3, 4, 4.6383, 0.0000, 1.79127, 0.10820},  // median |error| 1.6%
+    {3, 5, 4.2181, 0.0000, 0.92197, 0.06016},  // median |error| 1.5%
+    {3, 6, 3.1937, 0.0000, 0.49881, 0.00000},  // median |error| 4.0%
+    {3, 7, 3.2232, 0.0000, 1.03592, 0.06087},  // median |error| 3.6%
+    {3, 8, 7.7219, 0.0000, 7.04374, 0.24121},  // median |error| 0.6%
+    {3, 9, 5.2917, 0.0000, 3.49651, 0.16310},  // median |error| 1.0%
+    {3, 10, 3.1687, 0.0000, 0.53028, 0.00000},  // median |error| 5.9%
+    {3, 11, 7.2833, 0.0000, 2.01835, 0.08208},  // median |error| 2.4%
+    {3, 12, 7.8262, 0.0000, 3.99216, 0.22613},  // median |error| 2.9%
+    {3, 18, 3.4730, 0.0000, 0.94459, 0.02560},  // median |error| 1.8%
+    {5, 13, 2.8632, 0.9138, 0.15826, 0.00000},  // median |error| 7.1%
+    {5, 14, 2.9625, 0.5305, 0.05039, 0.02583},  // median |error| 10.4%
+    {5, 15, 2.8759, 0.5092, 0.10059, 0.00000},  // median |error| 11.7%
+    {5, 16, 1.6633, 1.8113, 0.16249, 0.01855},  // median |error| 7.0%
+    {5, 17, 3.3667, 0.0914, 0.10552, 0.00000},  // median |error| 10.6%
+    {5, 19, 3.3011, 0.0000, 0.06077, 0.01946},  // median |error| 11.1%
 };
 constexpr int kModelRows = (int)(sizeof(kModel) / sizeof(kModel[0]));
 constexpr int kVariantMS = 3;
@@ -209,15 +214,15 @@ static inline int select_for_variant(int64_t M, int64_t N, int64_t K, int varian
 // Split-K: the number of K chunks (1 = do not split) with the least modelled time among
 // the counts the split study measured.  A split launch costs the GEMM of its chunks, all in
 // one grid (the model above, with the workgroups multiplied by the chunks), plus
-//     3.3546 us (the reduction's launch)
-//   + 0.13923 us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
+//     3.3486 us (the reduction's launch)
+//   + 0.13897 us per MB of (2 * chunks + 1) * M * N * 4 bytes (partial products,
 //     written once and read once by the reduction, and C)
-//   + 0.2571 us per round of workgroups of the split grid (each workgroup's
+//   + 0.2572 us per round of workgroups of the split grid (each workgroup's
 //     first copy and partial-tile store, which short chunks no longer hide),
 // the constants fitted (>= 0, least squares) to the 41 shapes of the split study below.
-constexpr double kSplitFixedUs = 3.3546;
-constexpr double kSplitUsPerMB = 0.13923;
-constexpr double kSplitUsPerRound = 0.2571;
+constexpr double kSplitFixedUs = 3.3486;
+constexpr double kSplitUsPerMB = 0.13897;
+constexpr double kSplitUsPerRound = 0.2572;
 constexpr int kSplitChoices[] = {1, 2, 4, 8, 16};
 
 // The split study: trailing comments hold the measured microseconds of each count.

@@ -79,6 +79,7 @@ SHAPES = [
     # decode rows (1 to 16) against 4096- to 32000-wide layers, and a small one
     (1, 4096, 4096), (8, 4096, 4096), (16, 11008, 4096), (16, 4096, 11008),
     (16, 8192, 8192), (4, 1024, 1024), (16, 32000, 4096),
+    (1, 11008, 4096), (1, 4096, 11008), (1, 8192, 8192), (1, 32000, 4096), (4, 4096, 4096),
     # one GPU's share of 8192^3 split by rows over eight GPUs
     (1024, 8192, 8192),
 ]
