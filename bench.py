@@ -102,6 +102,7 @@ PREWARM_S = 0.2                        # untimed launches before the warm-up ste
 # lives in"); the widths are those of a common 7-billion-parameter transformer layer.
 LAYER_SHAPES = [(1, 4096, 4096), (8, 4096, 4096), (16, 4096, 4096), (16, 11008, 4096),
                 (16, 4096, 11008), (16, 8192, 8192), (16, 32000, 4096),
+                (1, 4096, 11008), (1, 8192, 8192),
                 (128, 4096, 4096), (128, 11008, 4096), (128, 4096, 11008),
                 (512, 4096, 4096), (512, 4096, 11008), (4096, 4096, 4096),
                 (4096, 11008, 4096)]
